@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Throughput of the QLoRA NF4 linear layer on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+NF4 quantization of the fp32 base weight (block absmax, nearest level, nibble
+packing, 8-bit double quantization of the scales), the forward (on-chip
+restore, base GEMM, fused rank-r term) and the backward (dX through the
+transposed restore, dA, dB).  Inputs are resident in HBM before timing.
+
+Default workload: attention-projection-shaped layer, W 4096 x 4096, 2048
+tokens, r = 16, alpha = 32 (seeded N(0, 0.02) weights; no model is loaded).
+Metric: fwd+bwd algorithmic TFLOP/s = (4 T K N + 6 T r (K + N)) per step /
+step time; the quantization has no flops but its time is inside the step.
+
+Prints ONE JSON line.  Extra fields: per-kernel times from the library's
+hipEvent trace, the roofline of the dominant kernel, the oracle timed on the
+host cores (cpu_baseline), and packed-weight GB/s of the few-token forward.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="skip the few-token packed-weight GB/s section")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget for the oracle timing")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def bf16_dev(bits):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def layer_flops(T, K, N, r):
+    fwd = 2 * T * K * N + 2 * T * r * (K + N)
+    bwd = 2 * T * K * N + 4 * T * r * (K + N)
+    return fwd, bwd
+
+
+def cpu_baseline(inp, lin, budget_s):
+    """The oracle (numpy) on the same workload: quantize + dequant + fwd + bwd."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    from oracle import lora as olora
+    from oracle import nf4 as onf4
+    from oracle.bf16 import bits_to_float
+
+    X, A, B, dY = (bits_to_float(inp[k]) for k in ("X", "A", "B", "dY"))
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        Q = onf4.quantize(inp["W"])
+        W_hat = onf4.dequantize(Q).astype(np.float64)
+        olora.forward(W_hat, X, A, B, lin.alpha, lin.r)
+        olora.backward(W_hat, X, A, B, dY, lin.alpha, lin.r)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start > budget_s or len(times) >= 20:
+            break
+    fwd, bwd = layer_flops(lin.T, lin.d_in, lin.d_out, lin.r)
+    per_step = sum(times) / len(times)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {
+        "value": round((fwd + bwd) / per_step / 1e12, 4),
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"the full {lin.name} step (quantize {lin.d_out}x{lin.d_in}, dequantize, float64 fwd+bwd "
+                   f"at T={lin.T}, r={lin.r}), {len(times)} repetitions, {per_step:.3f} s each; "
+                   f"host threads available {len(os.sched_getaffinity(0))}"),
+    }
+
+
+def decode_section(steps, warmup):
+    """Packed-weight GB/s of the few-token forward (8192 <-> 28672, r=64),
+    rotating 5 copies of each weight (> 512 MB) so the 256 MB MALL cannot hold them."""
+    import numpy as np
+    import torch
+    import nf4_bit_quantized_amd as q
+    import workloads
+
+    out = {}
+    copies = 5
+    for T in (1, 4, 16):
+        for lin in workloads.decode_70b(T):
+            if T == 1:
+                pass
+            inp = workloads.layer_inputs(lin.d_out, lin.d_in, T, lin.r, lin.seed, with_dy=False)
+            W = torch.from_numpy(inp["W"]).cuda()
+            pk, cd, cs = q.qlora_quantize_nf4(W)
+            del W
+            reps = [(pk.clone(), cd.clone(), cs.clone()) for _ in range(copies)]
+            X, A, B = (bf16_dev(inp[k]) for k in ("X", "A", "B"))
+            Y = torch.empty((T, lin.d_out), dtype=torch.bfloat16, device="cuda")
+            U = torch.empty((T, lin.r), dtype=torch.float32, device="cuda")
+            ws = torch.empty(max(1, q.qlora_fwd_workspace_bytes(lin.d_out, lin.d_in, T, lin.r)),
+                             dtype=torch.uint8, device="cuda")
+            for i in range(warmup):
+                p = reps[i % copies]
+                q.qlora_linear_fwd(p[0], p[1], p[2], X, A, B, lin.alpha, Y=Y, U_out=U, workspace=ws)
+            torch.cuda.synchronize()
+            q.qlora_trace_read(reset=True)
+            q.qlora_trace_enable(True)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(steps):
+                p = reps[i % copies]
+                q.qlora_linear_fwd(p[0], p[1], p[2], X, A, B, lin.alpha, Y=Y, U_out=U, workspace=ws)
+            e1.record()
+            torch.cuda.synchronize()
+            q.qlora_trace_enable(False)
+            kt = q.qlora_trace_read(reset=True)
+            call_ms = e0.elapsed_time(e1) / steps
+            packed_bytes = pk.numel() + cd.numel() + cs.numel() * 4
+            dec_n, dec_ms = kt.get("decode_partial", (1, float("nan")))
+            dec_avg = dec_ms / max(dec_n, 1)
+            out[lin.name] = {
+                "T": T, "d_out": lin.d_out, "d_in": lin.d_in,
+                "packed_weight_bytes": packed_bytes,
+                "call_us": round(call_ms * 1e3, 2),
+                "packed_GBps_call": round(packed_bytes / (call_ms * 1e-3) / 1e9, 1),
+                "decode_kernel_us": round(dec_avg * 1e3, 2),
+                "packed_GBps_kernel": round(packed_bytes / (dec_avg * 1e-3) / 1e9, 1),
+                "frac_hbm_kernel": round(packed_bytes / (dec_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            }
+            log("decode", lin.name, out[lin.name])
+            del reps, pk, cd, cs
+            torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer's multi-GPU sharding is described in DESIGN.md, not built).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import nf4_bit_quantized_amd as q
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    (lin,) = workloads.attn_4096()
+    T, K, N, r, alpha = lin.T, lin.d_in, lin.d_out, lin.r, lin.alpha
+    log(f"workload {lin}")
+    inp = workloads.layer_inputs(N, K, T, r, lin.seed)
+
+    W = torch.from_numpy(inp["W"]).cuda()
+    X, A, B, dY = (bf16_dev(inp[k]) for k in ("X", "A", "B", "dY"))
+    n_p, n_c, n_k = q.qlora_nf4_sizes(N, K)
+    packed = torch.empty((N, K // 2), dtype=torch.uint8, device="cuda")
+    codes = torch.empty(n_c, dtype=torch.uint8, device="cuda")
+    consts = torch.empty(n_k // 4, dtype=torch.float32, device="cuda")
+    Y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+    U = torch.empty((T, r), dtype=torch.float32, device="cuda")
+    dX = torch.empty((T, K), dtype=torch.bfloat16, device="cuda")
+    dA = torch.empty((r, K), dtype=torch.float32, device="cuda")
+    dB = torch.empty((N, r), dtype=torch.float32, device="cuda")
+    wsf = torch.empty(max(1, q.qlora_fwd_workspace_bytes(N, K, T, r)), dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(max(1, q.qlora_bwd_workspace_bytes(N, K, T, r)), dtype=torch.uint8, device="cuda")
+
+    def step():
+        q.qlora_quantize_nf4(W, packed, codes, consts)
+        q.qlora_linear_fwd(packed, codes, consts, X, A, B, alpha, Y=Y, U_out=U, workspace=wsf)
+        q.qlora_linear_bwd(packed, codes, consts, X, A, B, alpha, dY, U_in=U, dX=dX, dA=dA, dB=dB, workspace=wsb)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps, with the library's per-kernel hipEvents on
+    q.qlora_trace_read(reset=True)
+    q.qlora_trace_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    q.qlora_trace_enable(False)
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    kt = q.qlora_trace_read(reset=True)
+
+    fwd_f, bwd_f = layer_flops(T, K, N, r)
+    value = (fwd_f + bwd_f) / (ms_per_step * 1e-3) / 1e12
+
+    kernels = {name: {"launches": n, "avg_us": round(ms / n * 1e3, 2), "share": None}
+               for name, (n, ms) in kt.items()}
+    total_k = sum(ms for (_, ms) in kt.values())
+    for name, (n, ms) in kt.items():
+        kernels[name]["share"] = round(ms / total_k, 4) if total_k > 0 else None
+    # algorithmic work per launch of the two big kernels
+    kernel_flops = {"fwd_gemm": 2 * T * K * N + 2 * T * r * N, "dx_gemm": 2 * T * N * K + 2 * T * r * K}
+    dom = max(kernel_flops, key=lambda k: kt.get(k, (1, 0.0))[1])
+    dn, dms = kt.get(dom, (1, float("nan")))
+    dom_avg_s = dms / dn * 1e-3
+    achieved = kernel_flops[dom] / dom_avg_s / 1e12
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "avg_launch_us": round(dom_avg_s * 1e6, 2), "flops_per_launch": kernel_flops[dom]}
+    qn, qms = kt.get("nf4_quantize", (1, float("nan")))
+    q_bytes = N * K * 4 + N * K // 2 + n_c + n_k
+    quant = {"avg_us": round(qms / qn * 1e3, 2), "bytes": q_bytes,
+             "GBps": round(q_bytes / (qms / qn * 1e-3) / 1e9, 1),
+             "frac_hbm": round(q_bytes / (qms / qn * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+
+    result = {
+        "metric": "QLoRA linear fwd+bwd TFLOP/s & packed-weight GB/s; % of MI355X roofline",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded PCG64: W ~ N(0, 0.02) fp32, X, dY ~ N(0, 1) bf16, A ~ N(0, 1/r), B ~ N(0, 0.01))",
+        "config": {"workload": "attention-projection QLoRA linear: W 4096x4096 NF4 (block 64, 8-bit scale "
+                               "codes per 256 blocks), 2048 tokens, r=16, alpha=32; step = quantize + fwd + bwd",
+                   "d_out": N, "d_in": K, "tokens": T, "r": r, "alpha": alpha},
+        "roofline": roofline,
+        "kernels": kernels,
+        "quantize": quant,
+        "step_flops": fwd_f + bwd_f,
+    }
+    if not args.no_decode:
+        result["decode_packed_weight"] = decode_section(steps=max(20, args.steps), warmup=5)
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host ...")
+        result["cpu_baseline"] = cpu_baseline(inp, lin, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

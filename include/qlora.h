@@ -1,0 +1,193 @@
+/*
+ * qlora.h -- C ABI of the MI355X (gfx950) QLoRA linear-layer library.
+ *
+ * The layer: a frozen weight W (d_out x d_in) stored as blockwise NF4 with
+ * double-quantized scales, plus a trainable rank-r adapter (A, B):
+ *     forward   Y  = X W_hat^T + s (X A^T) B^T,          s = fl32(alpha / r)
+ *     backward  dX = dY W_hat + s (dY B) A,  dA = s (dY B)^T X,  dB = s dY^T (X A^T)
+ * where W_hat is the restored (dequantized, bf16) weight and no gradient is
+ * ever formed for W.
+ *
+ * Sources (page titles and sections):
+ *   "QLoRA技术从入门到精通" §2(3) NF4 grid; §3(1) offline quantization
+ *       (blocks, absmax scale, normalize, nearest level, 4-bit index, 8-bit
+ *       quantization of the scales); §3(2) forward (restore to 16 bit, two
+ *       branches, alpha / r); §3(3) backward (frozen base, only A and B).
+ *   "LoRA 与 QLoRA：把大模型微调拆成可负担的工程" §2 (h = W x + (alpha/r) B A x,
+ *       shapes of A and B), §8 (bf16 compute, bias none).
+ *   "【X 长文】LoRA 与 QLoRA：用一块 GPU 微调大模型", quantization section
+ *       (64-value blocks, NF4 levels with an exact 0, about 4.13 bits per
+ *       weight with 8-bit scales) and QLoRA section (gradient passes through
+ *       the restored weight to A and B).
+ *   "7、QLoRA 量化微调" §7.1 (16 ascending level indices; group storage).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All matrices are dense and row-major.  bf16 tensors cross the ABI as
+ *   uint16_t bit patterns.  Shapes (T = tokens, K = d_in, N = d_out):
+ *     W [N][K] fp32, X [T][K], Y [T][N], A [r][K], B [N][r], dY [T][N],
+ *     dX [T][K] (bf16); U [T][r], dA [r][K], dB [N][r] (fp32).
+ * - Stored weight format (written by qlora_quantize_nf4):
+ *     packed [N][K/2] uint8: 4-bit level indices, element 2j of the flattened
+ *            weight in the HIGH nibble of byte j, element 2j+1 in the low one;
+ *     codes  [N*K/64] uint8: 8-bit code of each 64-weight block's absmax scale;
+ *     consts [ceil(N*K/64/256)] fp32: per group of 256 consecutive block
+ *            scales, the group's largest scale c_g.
+ *   Block b is restored with s'_b = fl32(fl32(code_b) * fl32(c_g / 255)) and
+ *   each weight as bf16_rne(fl32(T[q] * s'_b)).
+ * - Device pointers: every tensor argument is device memory owned by the
+ *   caller (the library never allocates, frees or retains device memory and
+ *   keeps no state between calls).  Descriptors and output-size pointers are
+ *   host memory.
+ * - stream: a hipStream_t passed as void* (NULL = the null stream).  Every
+ *   compute call only enqueues work on that stream and returns without
+ *   synchronizing; outputs are valid once the stream has reached that point.
+ * - Errors: functions return QLORA_OK (0) or a negative QLORA_ERR_* code.
+ *   Arguments are validated on the host before anything is enqueued, so a
+ *   call that fails validation has no side effect.  QLORA_ERR_HIP reports a
+ *   failed launch (hipGetLastError after enqueueing).
+ * - Inputs must be finite; results for NaN/Inf inputs are unspecified.
+ * - Hot-path preconditions: blocksize == 64, dq_blocksize == 256,
+ *   d_in % 64 == 0, d_out % 64 == 0, 0 <= r <= 128, T >= 0 (T == 0 is a
+ *   no-op).  r == 0 means the base branch only.
+ */
+#ifndef QLORA_NF4_H
+#define QLORA_NF4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  QLORA_OK = 0,
+  QLORA_ERR_NULL = -1,        /* a required pointer is NULL */
+  QLORA_ERR_SHAPE = -2,       /* a size is out of range or not a multiple it must be */
+  QLORA_ERR_UNSUPPORTED = -3, /* a format parameter the library does not implement */
+  QLORA_ERR_WORKSPACE = -4,   /* workspace is NULL or smaller than the size query returned */
+  QLORA_ERR_HIP = -5          /* the HIP runtime reported an error while enqueueing */
+};
+
+/* Descriptor of the stored base weight. */
+typedef struct qlora_nf4_desc {
+  int64_t d_out;        /* N: rows of W */
+  int64_t d_in;         /* K: columns of W */
+  int32_t blocksize;    /* weights per absmax block; must be 64 */
+  int32_t dq_blocksize; /* block scales per second-level group; must be 256 */
+} qlora_nf4_desc;
+
+/* Human-readable name of a status code.  Never NULL; static storage. */
+const char* qlora_status_string(int status);
+
+/*
+ * The library's NF4 level table and decision thresholds (host copy).
+ * levels[16]: ascending, levels[0] = -1, levels[7] = 0, levels[15] = +1; the
+ *   medians of 7 equal-probability slices of the lower half of N(0,1) and of
+ *   8 slices of the upper half, each half scaled by its largest magnitude
+ *   ("QLoRA技术从入门到精通" §2(3); "【X 长文】..." NF4 paragraph).
+ * thresholds[15]: thresholds[k] is the largest float32 that is not closer to
+ *   levels[k+1] than to levels[k]; the index of a normalized value x is the
+ *   number of thresholds it exceeds (nearest level, ties to the lower index).
+ * Either pointer may be NULL.  Host only; never touches the GPU.
+ */
+int qlora_nf4_levels(float* levels, float* thresholds);
+
+/*
+ * Sizes in bytes of the three stored-weight buffers for descriptor d.
+ * Host only.  Errors: NULL (d or any out pointer), SHAPE, UNSUPPORTED.
+ */
+int qlora_nf4_sizes(const qlora_nf4_desc* d, size_t* packed_bytes, size_t* codes_bytes,
+                    size_t* consts_bytes);
+
+/*
+ * Offline quantization of W (fp32 [N][K], device) into packed / codes /
+ * consts (device, sizes from qlora_nf4_sizes) -- "QLoRA技术从入门到精通" §3(1):
+ * per 64-weight block absmax scale s_b, x = fl32(w / s_b) (IEEE division),
+ * nearest NF4 level (ties to the lower index; an all-zero block gives index 7),
+ * two indices per byte; then per group of 256 block scales c_g = max s_b and
+ * code_b = rint_half_even(fl32(fl32(s_b / c_g) * 255)) (0 when c_g == 0).
+ * Indices use the exact s_b.  Results are bit-exact and deterministic.
+ * Errors: NULL, SHAPE, UNSUPPORTED, HIP.
+ */
+int qlora_quantize_nf4(const qlora_nf4_desc* d, const float* W, uint8_t* packed, uint8_t* codes,
+                       float* consts, void* stream);
+
+/*
+ * Workspace (device bytes) qlora_linear_fwd needs for T tokens and rank r.
+ * Host only.  Errors: NULL, SHAPE, UNSUPPORTED.
+ */
+int qlora_fwd_workspace_bytes(const qlora_nf4_desc* d, int64_t T, int32_t r, size_t* bytes);
+
+/*
+ * Forward of the layer -- "QLoRA技术从入门到精通" §3(2); "LoRA 与 QLoRA：..." §2:
+ *   U = X A^T (fp32 [T][r]),  Y = bf16( X W_hat^T + s U B^T ),  s = fl32(alpha/r).
+ * W_hat is restored tile by tile on chip and never written to memory.
+ * X [T][K], A [r][K], B [N][r], Y [T][N] are bf16 bits (device).  U_out
+ * (fp32 [T][r], device) receives U for the backward pass; may be NULL.
+ * A and B may be NULL only when r == 0; X and Y only when T == 0.
+ * workspace: device scratch of at
+ * least qlora_fwd_workspace_bytes (may be NULL if that size is 0); its
+ * contents on entry are ignored.  Y must not alias any input.
+ * Accuracy: fp32 accumulation of bf16 products; deterministic (no atomics).
+ * Errors: NULL, SHAPE, UNSUPPORTED, WORKSPACE, HIP.
+ */
+int qlora_linear_fwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes,
+                     const float* consts, int64_t T, const uint16_t* X, int32_t r, float alpha,
+                     const uint16_t* A, const uint16_t* B, uint16_t* Y, float* U_out,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace (device bytes) qlora_linear_bwd needs for T tokens and rank r.
+ * Host only.  Errors: NULL, SHAPE, UNSUPPORTED.
+ */
+int qlora_bwd_workspace_bytes(const qlora_nf4_desc* d, int64_t T, int32_t r, size_t* bytes);
+
+/*
+ * Backward of the layer -- "QLoRA技术从入门到精通" §3(3); "【X 长文】..." QLoRA
+ * section (the gradient reaches A and B through the restored weight; the base
+ * weight is frozen, so no dW exists):
+ *   G  = dY B
+ *   dX = bf16( dY W_hat + s G A )        (skipped when dX == NULL)
+ *   dA = s G^T X        fp32 [r][K], overwritten (not accumulated)
+ *   dB = s dY^T U       fp32 [N][r], overwritten (not accumulated)
+ * U_in: fp32 [T][r] saved by the forward; NULL recomputes U = X A^T.
+ * dA and dB are required when r > 0 and ignored when r == 0; X and dY may
+ * be NULL only when T == 0 (then dA and dB are set to zero).
+ * workspace: at least qlora_bwd_workspace_bytes.  Outputs must not alias inputs.
+ * Deterministic (no atomics).  Errors: NULL, SHAPE, UNSUPPORTED, WORKSPACE, HIP.
+ */
+int qlora_linear_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes,
+                     const float* consts, int64_t T, const uint16_t* X, int32_t r, float alpha,
+                     const uint16_t* A, const uint16_t* B, const float* U_in, const uint16_t* dY,
+                     uint16_t* dX, float* dA, float* dB, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/*
+ * Per-kernel timing (measurement support; not an operation of the layer).
+ * qlora_trace_enable(1) makes every subsequent kernel launch of the library
+ * record a hipEvent before and after it on the launch stream (event objects
+ * are created on first use and reused; no device memory is allocated);
+ * qlora_trace_enable(0) (the default) records nothing.
+ * qlora_trace_read waits for the recorded events, adds their elapsed times to
+ * per-kernel totals and writes up to max_stats entries {name, launches,
+ * total_ms} (name: static string) for the kernels launched so far; *count
+ * receives the number of kernels with launches.  reset != 0 clears the
+ * totals afterwards.  Errors: NULL (count, or stats with max_stats > 0), HIP.
+ * Not thread-safe with respect to concurrent compute calls on other threads.
+ */
+typedef struct qlora_kernel_stat {
+  const char* name;
+  int64_t launches;
+  double total_ms;
+} qlora_kernel_stat;
+
+int qlora_trace_enable(int enable);
+int qlora_trace_read(qlora_kernel_stat* stats, int max_stats, int* count, int reset);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_NF4_H */

@@ -1,0 +1,267 @@
+"""Python binding of the MI355X QLoRA NF4 linear-layer library.
+
+Argument marshalling only: each function here has the name of a C entry point
+declared in ``include/qlora.h``, checks and converts its arguments (torch
+tensors on the GPU, the current stream), allocates missing outputs and
+workspace with torch, and calls the entry point through ctypes.  Every step of
+the layer runs in the library's HIP kernels.  If the library is not built, or
+no GPU is present when a compute call is made, an error is raised: there is no
+fallback implementation.
+"""
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqlora_nf4.so")
+
+QLORA_OK = 0
+QLORA_ERR_NULL = -1
+QLORA_ERR_SHAPE = -2
+QLORA_ERR_UNSUPPORTED = -3
+QLORA_ERR_WORKSPACE = -4
+QLORA_ERR_HIP = -5
+
+# Every exported symbol of include/qlora.h
+EXPORTED = (
+    "qlora_status_string",
+    "qlora_nf4_levels",
+    "qlora_nf4_sizes",
+    "qlora_quantize_nf4",
+    "qlora_fwd_workspace_bytes",
+    "qlora_linear_fwd",
+    "qlora_bwd_workspace_bytes",
+    "qlora_linear_bwd",
+    "qlora_trace_enable",
+    "qlora_trace_read",
+)
+
+
+class QloraError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({qlora_status_string(status)})")
+
+
+class KernelStat(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char_p), ("launches", ctypes.c_int64), ("total_ms", ctypes.c_double)]
+
+
+class Nf4Desc(ctypes.Structure):
+    _fields_ = [("d_out", ctypes.c_int64), ("d_in", ctypes.c_int64),
+                ("blocksize", ctypes.c_int32), ("dq_blocksize", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the built library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"HIP library not built: {LIB_PATH} missing "
+                           "(run python -m nf4_bit_quantized_amd.build)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, sz, i64, i32, f32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+    dp = ctypes.POINTER(Nf4Desc)
+    L.qlora_status_string.argtypes = [ctypes.c_int]
+    L.qlora_status_string.restype = ctypes.c_char_p
+    L.qlora_nf4_levels.argtypes = [vp, vp]
+    L.qlora_nf4_sizes.argtypes = [dp, ctypes.POINTER(sz), ctypes.POINTER(sz), ctypes.POINTER(sz)]
+    L.qlora_quantize_nf4.argtypes = [dp, vp, vp, vp, vp, vp]
+    L.qlora_fwd_workspace_bytes.argtypes = [dp, i64, i32, ctypes.POINTER(sz)]
+    L.qlora_bwd_workspace_bytes.argtypes = [dp, i64, i32, ctypes.POINTER(sz)]
+    L.qlora_linear_fwd.argtypes = [dp, vp, vp, vp, i64, vp, i32, f32, vp, vp, vp, vp, vp, sz, vp]
+    L.qlora_linear_bwd.argtypes = [dp, vp, vp, vp, i64, vp, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.qlora_trace_enable.argtypes = [ctypes.c_int]
+    L.qlora_trace_read.argtypes = [ctypes.POINTER(KernelStat), ctypes.c_int, ctypes.POINTER(ctypes.c_int),
+                                   ctypes.c_int]
+    for name in EXPORTED[1:]:
+        getattr(L, name).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(status: int, where: str):
+    if status != QLORA_OK:
+        raise QloraError(status, where)
+
+
+def _desc(d_out: int, d_in: int, blocksize: int = 64, dq_blocksize: int = 256) -> Nf4Desc:
+    return Nf4Desc(int(d_out), int(d_in), int(blocksize), int(dq_blocksize))
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _need_cuda(*tensors, dtype=None, name=""):
+    import torch
+    for t in tensors:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name}: tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError(f"{name}: tensors must be contiguous")
+
+
+# ---------------------------------------------------------------------------
+# Host-only queries
+# ---------------------------------------------------------------------------
+
+def qlora_status_string(status: int) -> str:
+    return lib().qlora_status_string(int(status)).decode()
+
+
+def qlora_nf4_levels():
+    """(levels float32[16], thresholds float32[15]) as numpy arrays."""
+    import numpy as np
+    lv = (ctypes.c_float * 16)()
+    th = (ctypes.c_float * 15)()
+    _check(lib().qlora_nf4_levels(ctypes.cast(lv, ctypes.c_void_p), ctypes.cast(th, ctypes.c_void_p)),
+           "qlora_nf4_levels")
+    return np.frombuffer(lv, dtype=np.float32).copy(), np.frombuffer(th, dtype=np.float32).copy()
+
+
+def qlora_nf4_sizes(d_out: int, d_in: int, blocksize: int = 64, dq_blocksize: int = 256) -> Tuple[int, int, int]:
+    d = _desc(d_out, d_in, blocksize, dq_blocksize)
+    a, b, c = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().qlora_nf4_sizes(ctypes.byref(d), ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)),
+           "qlora_nf4_sizes")
+    return a.value, b.value, c.value
+
+
+def qlora_fwd_workspace_bytes(d_out: int, d_in: int, T: int, r: int) -> int:
+    d = _desc(d_out, d_in)
+    n = ctypes.c_size_t()
+    _check(lib().qlora_fwd_workspace_bytes(ctypes.byref(d), int(T), int(r), ctypes.byref(n)),
+           "qlora_fwd_workspace_bytes")
+    return n.value
+
+
+def qlora_bwd_workspace_bytes(d_out: int, d_in: int, T: int, r: int) -> int:
+    d = _desc(d_out, d_in)
+    n = ctypes.c_size_t()
+    _check(lib().qlora_bwd_workspace_bytes(ctypes.byref(d), int(T), int(r), ctypes.byref(n)),
+           "qlora_bwd_workspace_bytes")
+    return n.value
+
+
+# ---------------------------------------------------------------------------
+# Compute calls (enqueue on the current torch stream; no synchronization)
+# ---------------------------------------------------------------------------
+
+def _workspace(nbytes: int, device, workspace=None):
+    import torch
+    if nbytes == 0:
+        return workspace
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError("workspace too small")
+        return workspace
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def qlora_quantize_nf4(W, packed=None, codes=None, consts=None, stream=None):
+    """Quantize fp32 W [d_out][d_in] (GPU) -> (packed uint8 [d_out][d_in/2],
+    codes uint8 [nb], consts float32 [ng])."""
+    import torch
+    _need_cuda(W, name="qlora_quantize_nf4")
+    if W.dtype != torch.float32 or W.dim() != 2:
+        raise ValueError("W must be a 2-D float32 tensor")
+    d_out, d_in = W.shape
+    n_p, n_c, n_k = qlora_nf4_sizes(d_out, d_in)
+    if packed is None:
+        packed = torch.empty((d_out, d_in // 2), dtype=torch.uint8, device=W.device)
+    if codes is None:
+        codes = torch.empty(n_c, dtype=torch.uint8, device=W.device)
+    if consts is None:
+        consts = torch.empty(n_k // 4, dtype=torch.float32, device=W.device)
+    _need_cuda(packed, codes, consts, name="qlora_quantize_nf4")
+    d = _desc(d_out, d_in)
+    _check(lib().qlora_quantize_nf4(ctypes.byref(d), _ptr(W), _ptr(packed), _ptr(codes), _ptr(consts),
+                                    _stream(stream)), "qlora_quantize_nf4")
+    return packed, codes, consts
+
+
+def qlora_linear_fwd(packed, codes, consts, X, A, B, alpha: float, Y=None, U_out=None,
+                     want_u: bool = True, workspace=None, stream=None):
+    """Forward: returns (Y bf16 [T][d_out], U fp32 [T][r] or None).
+
+    ``packed`` [d_out][d_in/2] fixes the layer shape; X bf16 [T][d_in],
+    A bf16 [r][d_in], B bf16 [d_out][r] (A, B may be None for r = 0).
+    """
+    import torch
+    d_out, d_in = packed.shape[0], packed.shape[1] * 2
+    T = X.shape[0]
+    r = 0 if A is None else A.shape[0]
+    _need_cuda(packed, codes, consts, X, A, B, Y, U_out, name="qlora_linear_fwd")
+    for t, nm in ((X, "X"), (A, "A"), (B, "B")):
+        if t is not None and t.dtype != torch.bfloat16:
+            raise ValueError(f"{nm} must be bfloat16")
+    if Y is None:
+        Y = torch.empty((T, d_out), dtype=torch.bfloat16, device=X.device)
+    if U_out is None and want_u and r > 0:
+        U_out = torch.empty((T, r), dtype=torch.float32, device=X.device)
+    nbytes = qlora_fwd_workspace_bytes(d_out, d_in, T, r)
+    ws = _workspace(nbytes, X.device, workspace)
+    d = _desc(d_out, d_in)
+    _check(lib().qlora_linear_fwd(ctypes.byref(d), _ptr(packed), _ptr(codes), _ptr(consts), T, _ptr(X), r,
+                                  float(alpha), _ptr(A), _ptr(B), _ptr(Y), _ptr(U_out), _ptr(ws), nbytes,
+                                  _stream(stream)), "qlora_linear_fwd")
+    return Y, U_out
+
+
+def qlora_linear_bwd(packed, codes, consts, X, A, B, alpha: float, dY, U_in=None, dX=None, dA=None, dB=None,
+                     want_dx: bool = True, workspace=None, stream=None):
+    """Backward: returns (dX bf16 [T][d_in] or None, dA fp32 [r][d_in], dB fp32 [d_out][r])."""
+    import torch
+    d_out, d_in = packed.shape[0], packed.shape[1] * 2
+    T = X.shape[0]
+    r = 0 if A is None else A.shape[0]
+    _need_cuda(packed, codes, consts, X, A, B, dY, U_in, dX, dA, dB, name="qlora_linear_bwd")
+    for t, nm in ((X, "X"), (A, "A"), (B, "B"), (dY, "dY")):
+        if t is not None and t.dtype != torch.bfloat16:
+            raise ValueError(f"{nm} must be bfloat16")
+    if dX is None and want_dx:
+        dX = torch.empty((T, d_in), dtype=torch.bfloat16, device=X.device)
+    if r > 0:
+        if dA is None:
+            dA = torch.empty((r, d_in), dtype=torch.float32, device=X.device)
+        if dB is None:
+            dB = torch.empty((d_out, r), dtype=torch.float32, device=X.device)
+    nbytes = qlora_bwd_workspace_bytes(d_out, d_in, T, r)
+    ws = _workspace(nbytes, X.device, workspace)
+    d = _desc(d_out, d_in)
+    _check(lib().qlora_linear_bwd(ctypes.byref(d), _ptr(packed), _ptr(codes), _ptr(consts), T, _ptr(X), r,
+                                  float(alpha), _ptr(A), _ptr(B), _ptr(U_in), _ptr(dY), _ptr(dX), _ptr(dA),
+                                  _ptr(dB), _ptr(ws), nbytes, _stream(stream)), "qlora_linear_bwd")
+    return dX, dA, dB
+
+
+# ---------------------------------------------------------------------------
+# Per-kernel timing (hipEvents recorded by the library around its launches)
+# ---------------------------------------------------------------------------
+
+def qlora_trace_enable(enable: bool = True) -> None:
+    _check(lib().qlora_trace_enable(1 if enable else 0), "qlora_trace_enable")
+
+
+def qlora_trace_read(reset: bool = True) -> dict:
+    """{kernel name: (launches, total_ms)} for the launches recorded so far."""
+    stats = (KernelStat * 32)()
+    n = ctypes.c_int()
+    _check(lib().qlora_trace_read(stats, 32, ctypes.byref(n), 1 if reset else 0), "qlora_trace_read")
+    return {stats[i].name.decode(): (int(stats[i].launches), float(stats[i].total_ms))
+            for i in range(min(n.value, 32))}

@@ -1,0 +1,124 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, reports sizes, and rejects bad arguments on the host before
+anything is enqueued.  No compute call reaches the device here."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import nf4_bit_quantized_amd as q
+from oracle import nf4 as onf4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlora.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(q.LIB_PATH), reason="library not built")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qlora_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_what_binding_lists():
+    assert _declared() == sorted(q.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = q.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+    out = os.popen(f"nm -D --defined-only {q.LIB_PATH}").read()
+    for name in _declared():
+        assert re.search(rf"\bT {name}\b", out), name
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, -5):
+        assert isinstance(q.qlora_status_string(code), str) and q.qlora_status_string(code)
+    assert q.qlora_status_string(-99) == "unknown status"
+
+
+def test_library_table_is_bit_identical_to_oracle_table():
+    levels, thr = q.qlora_nf4_levels()
+    np.testing.assert_array_equal(levels.view(np.uint32), onf4.nf4_levels().view(np.uint32))
+
+
+def test_library_thresholds_reproduce_oracle_nearest_level():
+    levels, thr = q.qlora_nf4_levels()
+    T = onf4.nf4_levels()
+    for k in range(15):
+        at = np.array([thr[k]], np.float32)
+        above = np.nextafter(at, np.float32(np.inf))
+        assert onf4._nearest_level(at, T)[0] == k
+        assert onf4._nearest_level(above, T)[0] == k + 1
+
+
+def test_sizes():
+    p, c, k = q.qlora_nf4_sizes(4096, 4096)
+    assert p == 4096 * 4096 // 2 and c == 4096 * 4096 // 64 and k == 4 * (4096 * 4096 // 64 // 256)
+    p, c, k = q.qlora_nf4_sizes(64, 320)          # 320 blocks -> 2 groups (partial last group)
+    assert (p, c, k) == (64 * 160, 320, 8)
+    bits = (8 * p + 8 * c + 8 * k) / (64 * 320)
+    assert abs(bits - onf4.storage_bits_per_weight(64 * 320)) < 1e-12
+
+
+def _err(fn, *a):
+    with pytest.raises(q.QloraError) as e:
+        fn(*a)
+    return e.value.status
+
+
+def test_bad_descriptor_rejected():
+    assert _err(q.qlora_nf4_sizes, 100, 64) == q.QLORA_ERR_SHAPE
+    assert _err(q.qlora_nf4_sizes, 64, 0) == q.QLORA_ERR_SHAPE
+    assert _err(q.qlora_nf4_sizes, 64, 64, 128) == q.QLORA_ERR_UNSUPPORTED
+    assert _err(q.qlora_nf4_sizes, 64, 64, 64, 0) == q.QLORA_ERR_UNSUPPORTED
+    assert _err(q.qlora_fwd_workspace_bytes, 64, 64, 4, 129) == q.QLORA_ERR_SHAPE
+    assert _err(q.qlora_fwd_workspace_bytes, 64, 64, -1, 4) == q.QLORA_ERR_SHAPE
+
+
+def _raw_fwd(desc, packed, codes, consts, T, X, r, A, B, Y, ws, wsb):
+    L = q.lib()
+    return L.qlora_linear_fwd(ctypes.byref(desc), packed, codes, consts, T, X, r, ctypes.c_float(2.0), A, B, Y,
+                              None, ws, wsb, None)
+
+
+def test_validation_happens_before_any_launch():
+    # fake, aligned, never-dereferenced addresses: every call below must fail on the host
+    fake = 0x10000
+    d = q._desc(64, 64)
+    L = q.lib()
+    assert L.qlora_quantize_nf4(None, fake, fake, fake, fake, None) == q.QLORA_ERR_NULL
+    assert L.qlora_quantize_nf4(ctypes.byref(d), None, fake, fake, fake, None) == q.QLORA_ERR_NULL
+    assert L.qlora_quantize_nf4(ctypes.byref(d), fake + 4, fake, fake, fake, None) == q.QLORA_ERR_UNSUPPORTED
+    bad = q._desc(64, 96)
+    assert L.qlora_quantize_nf4(ctypes.byref(bad), fake, fake, fake, fake, None) == q.QLORA_ERR_SHAPE
+    # forward: missing adapter, missing output, missing / short workspace
+    assert _raw_fwd(d, fake, fake, fake, 8, fake, 4, None, fake, fake, fake, 1 << 20) == q.QLORA_ERR_NULL
+    assert _raw_fwd(d, fake, fake, fake, 8, fake, 4, fake, fake, None, fake, 1 << 20) == q.QLORA_ERR_NULL
+    need = q.qlora_fwd_workspace_bytes(64, 64, 8, 4)
+    assert need > 0
+    assert _raw_fwd(d, fake, fake, fake, 8, fake, 4, fake, fake, fake, None, need) == q.QLORA_ERR_WORKSPACE
+    assert _raw_fwd(d, fake, fake, fake, 8, fake, 4, fake, fake, fake, fake, need - 1) == q.QLORA_ERR_WORKSPACE
+    assert _raw_fwd(d, fake, fake, fake, 8, fake + 8, 4, fake, fake, fake, fake, need) == q.QLORA_ERR_UNSUPPORTED
+    # backward: dA / dB required when r > 0
+    nb = q.qlora_bwd_workspace_bytes(64, 64, 8, 4)
+    r = L.qlora_linear_bwd(ctypes.byref(d), fake, fake, fake, 8, fake, 4, ctypes.c_float(1.0), fake, fake, None,
+                           fake, fake, None, fake, fake, nb, None)
+    assert r == q.QLORA_ERR_NULL
+    r = L.qlora_linear_bwd(ctypes.byref(d), fake, fake, fake, 8, fake, 4, ctypes.c_float(1.0), fake, fake, None,
+                           fake, fake, fake, fake, None, nb, None)
+    assert r == q.QLORA_ERR_WORKSPACE
+
+
+def test_workspace_sizes_grow_with_tokens_and_rank():
+    a = q.qlora_bwd_workspace_bytes(4096, 4096, 2048, 16)
+    b = q.qlora_bwd_workspace_bytes(4096, 4096, 4096, 64)
+    assert 0 < a < b
+    assert q.qlora_fwd_workspace_bytes(4096, 4096, 2048, 0) == 0          # base-only, no decode: nothing
+    assert q.qlora_bwd_workspace_bytes(4096, 4096, 0, 16) == 0

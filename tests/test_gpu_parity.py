@@ -1,0 +1,228 @@
+"""GPU parity: the HIP path through the C ABI against the oracle, element by
+element, on seeded inputs.  Integer/byte outputs are bit-exact; floating-point
+outputs are within the stated bar (TOL, normwise max relative error)."""
+
+import numpy as np
+import pytest
+
+import workloads
+from gpu_helpers import (TOL, assert_quant_bit_exact, gpu_layer, normwise_err, oracle_layer, say,
+                         dev_bf16, dev_f32, host_bf16_to_f64)
+from oracle import nf4 as onf4
+
+pytestmark = pytest.mark.gpu
+
+
+# --------------------------------------------------------------------------
+# Quantization: bit-exact indices, packed bytes, scale codes, constants
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d_out,d_in", [(256, 256), (64, 320), (128, 192), (4096, 4096)])
+def test_quantize_bit_exact(d_out, d_in):
+    import nf4_bit_quantized_amd as q
+    import torch
+    say(f"quantize {d_out}x{d_in}")
+    inp = workloads.layer_inputs(d_out, d_in, 1, 1, seed=0, with_dy=False)
+    Q = onf4.quantize(inp["W"])
+    packed, codes, consts = q.qlora_quantize_nf4(dev_f32(inp["W"]))
+    torch.cuda.synchronize()
+    assert_quant_bit_exact({"packed_h": packed.cpu().numpy(), "codes_h": codes.cpu().numpy(),
+                            "consts_h": consts.cpu().numpy()}, Q)
+
+
+def test_quantize_threshold_sweep_bit_exact():
+    """Every NF4 decision threshold and its 40 float32 neighbours on each side,
+    in blocks holding a +-1 so that the block scale is 1 and x = w exactly;
+    plus all-zero blocks and a ragged last group."""
+    import nf4_bit_quantized_amd as q
+    import torch
+    _, thr = q.qlora_nf4_levels()
+    vals = []
+    for k in range(15):
+        c = np.float32(thr[k])
+        vals.append(c)
+        for d in (np.float32(np.inf), np.float32(-np.inf)):
+            v = c
+            for _ in range(40):
+                v = np.nextafter(v, d, dtype=np.float32)
+                vals.append(v)
+    vals += list(onf4.nf4_levels())
+    vals = np.array(vals, np.float32)
+    per = 63
+    nblk = -(-vals.size // per)
+    W = np.zeros((nblk, 64), np.float32)
+    for b in range(nblk):
+        chunk = vals[b * per:(b + 1) * per]
+        W[b, 0] = 1.0 if b % 2 == 0 else -1.0
+        W[b, 1:1 + chunk.size] = chunk
+    W = np.concatenate([W.reshape(-1), np.zeros(64 * 5, np.float32)])     # zero blocks at the end
+    pad = (-W.size) % (64 * 64)
+    W = np.concatenate([W, np.full(pad, 0.01, np.float32)]).reshape(64, -1)
+    say(f"threshold sweep W {W.shape}")
+    Q = onf4.quantize(W)
+    packed, codes, consts = q.qlora_quantize_nf4(dev_f32(W))
+    torch.cuda.synchronize()
+    assert_quant_bit_exact({"packed_h": packed.cpu().numpy(), "codes_h": codes.cpu().numpy(),
+                            "consts_h": consts.cpu().numpy()}, Q)
+
+
+def test_quantize_deterministic():
+    import nf4_bit_quantized_amd as q
+    import torch
+    inp = workloads.layer_inputs(512, 1024, 1, 1, seed=3, with_dy=False)
+    W = dev_f32(inp["W"])
+    a = [t.clone() for t in q.qlora_quantize_nf4(W)]
+    b = q.qlora_quantize_nf4(W)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+# --------------------------------------------------------------------------
+# Forward / backward parity
+# --------------------------------------------------------------------------
+
+CASES = [
+    # (d_out, d_in, T, r, alpha, seed)
+    (256, 256, 16, 8, 16.0, 0),       # parity workload: W 256x256, 16 tokens, r=8, alpha=16, seed 0
+    (256, 256, 1, 8, 16.0, 1),
+    (192, 320, 4, 3, 5.0, 2),         # ragged everything, odd rank
+    (128, 256, 17, 16, 32.0, 3),      # first tiled-GEMM size
+    (320, 192, 100, 1, 2.0, 4),
+    (256, 384, 150, 64, 16.0, 5),
+    (448, 256, 64, 128, 64.0, 6),
+    (256, 256, 40, 0, 0.0, 7),        # base branch only
+]
+
+
+@pytest.mark.parametrize("d_out,d_in,T,r,alpha,seed", CASES)
+def test_fwd_bwd_parity(d_out, d_in, T, r, alpha, seed):
+    say(f"fwd/bwd d_out={d_out} d_in={d_in} T={T} r={r} alpha={alpha} seed={seed}")
+    inp = workloads.layer_inputs(d_out, d_in, T, r, seed)
+    o = oracle_layer(inp, r, alpha)
+    g = gpu_layer(inp, r, alpha)
+    assert_quant_bit_exact(g, o["Q"])
+    errs = {"Y": normwise_err(g["Y"], o["Y"]), "dX": normwise_err(g["dX"], o["dX"])}
+    if r > 0:
+        errs.update(U=normwise_err(g["U"], o["U"]), dA=normwise_err(g["dA"], o["dA"]),
+                    dB=normwise_err(g["dB"], o["dB"]))
+    say("  errors", {k: f"{v:.2e}" for k, v in errs.items()})
+    for k, v in errs.items():
+        assert v <= TOL, (k, v)
+
+
+def test_bwd_recomputes_u_when_not_saved():
+    inp = workloads.layer_inputs(256, 320, 33, 8, seed=8)
+    a = gpu_layer(inp, 8, 16.0, pass_u=True)
+    b = gpu_layer(inp, 8, 16.0, pass_u=False)
+    for k in ("dX", "dA", "dB"):
+        np.testing.assert_array_equal(a[k], b[k])
+
+
+def test_attention_shaped_layer_full_size():
+    """W 4096x4096, 2048 tokens, r=16, alpha=32: every output against the oracle."""
+    (lin,) = workloads.attn_4096()
+    say(f"full-size {lin}")
+    inp = workloads.layer_inputs(lin.d_out, lin.d_in, lin.T, lin.r, lin.seed)
+    o = oracle_layer(inp, lin.r, lin.alpha)
+    g = gpu_layer(inp, lin.r, lin.alpha)
+    assert_quant_bit_exact(g, o["Q"])
+    for k in ("Y", "U", "dX", "dA", "dB"):
+        e = normwise_err(g[k], o[k])
+        say(f"  {k} err {e:.2e}")
+        assert e <= TOL, (k, e)
+
+
+# --------------------------------------------------------------------------
+# Special cases the pages fix
+# --------------------------------------------------------------------------
+
+def test_b_zero_equals_base_path_bit_identical():
+    """B = 0: the adapter adds nothing -- Y equals the r = 0 result exactly,
+    dA = 0 exactly, dB != 0 (A != 0, so B receives a gradient)."""
+    import nf4_bit_quantized_amd as q
+    import torch
+    for T in (8, 64):
+        inp = workloads.layer_inputs(256, 192, T, 8, seed=9)
+        W = dev_f32(inp["W"])
+        packed, codes, consts = q.qlora_quantize_nf4(W)
+        X, A, dY = dev_bf16(inp["X"]), dev_bf16(inp["A"]), dev_bf16(inp["dY"])
+        B0 = torch.zeros((256, 8), dtype=torch.bfloat16, device="cuda")
+        Y, U = q.qlora_linear_fwd(packed, codes, consts, X, A, B0, 16.0)
+        Yb, _ = q.qlora_linear_fwd(packed, codes, consts, X, None, None, 0.0)
+        dX, dA, dB = q.qlora_linear_bwd(packed, codes, consts, X, A, B0, 16.0, dY, U_in=U)
+        dXb, _, _ = q.qlora_linear_bwd(packed, codes, consts, X, None, None, 0.0, dY)
+        torch.cuda.synchronize()
+        assert torch.equal(Y.float(), Yb.float()), T
+        assert torch.all(dA == 0)
+        assert dB.abs().max().item() > 0
+        assert torch.equal(dX.float(), dXb.float())
+
+
+def test_sales_tables_bit_exact():
+    """The rank-1 and rank-2 sales tables through the layer: W = 0, alpha = r,
+    X = identity, so Y = (B A)^T exactly (small integers are exact in bf16)."""
+    import nf4_bit_quantized_amd as q
+    import torch
+    tables = {
+        1: ([[10, 20, 30]], [[1, 2, 2, 1]], [[10, 20, 20, 10], [20, 40, 40, 20], [30, 60, 60, 30]]),
+        2: ([[10, 20, 30], [1, 0, 2]], [[1, 2, 2, 1], [0, 0, 5, 5]],
+            [[10, 20, 25, 15], [20, 40, 40, 20], [30, 60, 70, 40]]),
+    }
+    for T in (16, 64):                        # few-token path and tiled path
+        for r, (cols, rows, want) in tables.items():
+            W = torch.zeros((64, 64), dtype=torch.float32, device="cuda")
+            packed, codes, consts = q.qlora_quantize_nf4(W)
+            B = torch.zeros((64, r), dtype=torch.float32)
+            A = torch.zeros((r, 64), dtype=torch.float32)
+            for i in range(r):
+                B[:3, i] = torch.tensor(cols[i], dtype=torch.float32)
+                A[i, :4] = torch.tensor(rows[i], dtype=torch.float32)
+            X = torch.zeros((T, 64), dtype=torch.float32)
+            X[:min(T, 64), :min(T, 64)] = torch.eye(min(T, 64))
+            Y, _ = q.qlora_linear_fwd(packed, codes, consts, X.bfloat16().cuda(), A.bfloat16().cuda(),
+                                      B.bfloat16().cuda(), float(r))
+            torch.cuda.synchronize()
+            got = Y.float().cpu().numpy().T[:3, :4]
+            np.testing.assert_array_equal(got, np.array(want, np.float32))
+            assert np.linalg.matrix_rank(got) == r
+
+
+def test_merge_matches_two_branch_result():
+    """Y from the layer equals X (W_hat + s B A)^T computed by the oracle."""
+    from oracle import lora as olora
+    from oracle.bf16 import bits_to_float
+    inp = workloads.layer_inputs(256, 256, 48, 16, seed=10)
+    g = gpu_layer(inp, 16, 32.0, do_bwd=False)
+    W_hat = onf4.dequantize(onf4.quantize(inp["W"]))
+    Wm = olora.merged_weight(W_hat, bits_to_float(inp["A"]), bits_to_float(inp["B"]), 32.0, 16)
+    want = bits_to_float(inp["X"]) @ Wm.T
+    assert normwise_err(g["Y"], want) <= TOL
+
+
+def test_deterministic_fwd_bwd():
+    inp = workloads.layer_inputs(256, 512, 80, 16, seed=11)
+    a = gpu_layer(inp, 16, 32.0)
+    b = gpu_layer(inp, 16, 32.0)
+    for k in ("Y", "U", "dX", "dA", "dB"):
+        np.testing.assert_array_equal(a[k], b[k])
+    a = gpu_layer(workloads.layer_inputs(256, 512, 8, 16, seed=11), 16, 32.0)
+    b = gpu_layer(workloads.layer_inputs(256, 512, 8, 16, seed=11), 16, 32.0)
+    for k in ("Y", "U", "dX", "dA", "dB"):
+        np.testing.assert_array_equal(a[k], b[k])
+
+
+def test_zero_tokens_is_a_no_op():
+    import nf4_bit_quantized_amd as q
+    import torch
+    inp = workloads.layer_inputs(128, 128, 0, 4, seed=12)
+    packed, codes, consts = q.qlora_quantize_nf4(dev_f32(inp["W"]))
+    X = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda")
+    dY = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda")
+    A, B = dev_bf16(inp["A"]), dev_bf16(inp["B"])
+    Y, U = q.qlora_linear_fwd(packed, codes, consts, X, A, B, 8.0)
+    dA = torch.full((4, 128), 7.0, device="cuda")
+    dB = torch.full((128, 4), 7.0, device="cuda")
+    q.qlora_linear_bwd(packed, codes, consts, X, A, B, 8.0, dY, dA=dA, dB=dB)
+    torch.cuda.synchronize()
+    assert Y.shape == (0, 128) and torch.all(dA == 0) and torch.all(dB == 0)
