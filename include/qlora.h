@@ -46,6 +46,8 @@
  *   Arguments are validated on the host before anything is enqueued, so a
  *   call that fails validation has no side effect.  QLORA_ERR_HIP reports a
  *   failed launch (hipGetLastError after enqueueing).
+ * - W, packed, X, dY and A must be 16-byte aligned (QLORA_ERR_UNSUPPORTED
+ *   otherwise); other pointers need only their element alignment.
  * - Inputs must be finite; results for NaN/Inf inputs are unspecified.
  * - Hot-path preconditions: blocksize == 64, dq_blocksize == 256,
  *   d_in % 64 == 0, d_out % 64 == 0, 0 <= r <= 128, T >= 0 (T == 0 is a
@@ -177,6 +179,16 @@ int qlora_linear_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8
  * totals afterwards.  Errors: NULL (count, or stats with max_stats > 0), HIP.
  * Not thread-safe with respect to concurrent compute calls on other threads.
  */
+/*
+ * qlora_trace_select: like qlora_trace_enable, but only the kernels whose bit
+ * is set in kernel_mask are bracketed (bit k = the kernel named by
+ * qlora_trace_kernel_name(k)), so a caller can time the big kernels without
+ * adding events between all the small ones.  qlora_trace_kernel_name returns
+ * a static name, or NULL for k outside the library's kernel list.
+ */
+int qlora_trace_select(uint32_t kernel_mask);
+const char* qlora_trace_kernel_name(int kernel);
+
 typedef struct qlora_kernel_stat {
   const char* name;
   int64_t launches;

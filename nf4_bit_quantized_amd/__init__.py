@@ -34,6 +34,8 @@ EXPORTED = (
     "qlora_bwd_workspace_bytes",
     "qlora_linear_bwd",
     "qlora_trace_enable",
+    "qlora_trace_select",
+    "qlora_trace_kernel_name",
     "qlora_trace_read",
 )
 
@@ -77,10 +79,13 @@ def lib() -> ctypes.CDLL:
     L.qlora_linear_fwd.argtypes = [dp, vp, vp, vp, i64, vp, i32, f32, vp, vp, vp, vp, vp, sz, vp]
     L.qlora_linear_bwd.argtypes = [dp, vp, vp, vp, i64, vp, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.qlora_trace_enable.argtypes = [ctypes.c_int]
+    L.qlora_trace_select.argtypes = [ctypes.c_uint32]
+    L.qlora_trace_kernel_name.argtypes = [ctypes.c_int]
     L.qlora_trace_read.argtypes = [ctypes.POINTER(KernelStat), ctypes.c_int, ctypes.POINTER(ctypes.c_int),
                                    ctypes.c_int]
     for name in EXPORTED[1:]:
         getattr(L, name).restype = ctypes.c_int
+    L.qlora_trace_kernel_name.restype = ctypes.c_char_p
     _lib = L
     return L
 
@@ -256,6 +261,25 @@ def qlora_linear_bwd(packed, codes, consts, X, A, B, alpha: float, dY, U_in=None
 
 def qlora_trace_enable(enable: bool = True) -> None:
     _check(lib().qlora_trace_enable(1 if enable else 0), "qlora_trace_enable")
+
+
+def qlora_trace_kernel_name(kernel: int):
+    n = lib().qlora_trace_kernel_name(int(kernel))
+    return None if n is None else n.decode()
+
+
+def qlora_trace_select(names) -> None:
+    """Bracket only the named kernels (names as reported by qlora_trace_read)."""
+    mask = 0
+    k = 0
+    while True:
+        n = qlora_trace_kernel_name(k)
+        if n is None:
+            break
+        if n in names:
+            mask |= 1 << k
+        k += 1
+    _check(lib().qlora_trace_select(mask), "qlora_trace_select")
 
 
 def qlora_trace_read(reset: bool = True) -> dict:

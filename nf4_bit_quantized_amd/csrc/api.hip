@@ -4,6 +4,7 @@
 // include/qlora.h.
 #include <cstring>
 
+#include "fused.hpp"
 #include "gemm.hpp"
 #include "trace.hpp"
 #include "../../include/qlora.h"
@@ -293,7 +294,7 @@ int qlora_linear_fwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8
   if (!packed || !codes || !consts) return QLORA_ERR_NULL;
   if (T > 0 && (!X || !Y)) return QLORA_ERR_NULL;
   if (r > 0 && (!A || !B)) return QLORA_ERR_NULL;
-  if (!aligned16(packed) || !aligned16(X)) return QLORA_ERR_UNSUPPORTED;
+  if (!aligned16(packed) || !aligned16(X) || !aligned16(A)) return QLORA_ERR_UNSUPPORTED;
   const size_t need = plan_fwd(d, T, r, nullptr).bytes;
   if (need > 0 && (!workspace || workspace_bytes < need)) return QLORA_ERR_WORKSPACE;
   if (T == 0) return QLORA_OK;
@@ -313,10 +314,13 @@ int qlora_linear_fwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8
                           B, Y, s_));
     return QLORA_OK;
   }
-  GemmParams p = gemm_one(op_bf16_k(X, K, T, K), op_nf4(OP_NF4_K, packed, codes, consts, K, N, K), T, N);
-  if (r > 0) add_tail(p, op_bf16_k(w.Us, hilo_ld(r), T, 2 * (int64_t)r), op_bf16_k(B, r, N, 2 * (int64_t)r, r));
-  out_bf16(p, Y, N);
-  HIP_TRY(launch_gemm(p, s_, KID_FWD_GEMM));
+  FusedParams fp{};
+  fp.A = X; fp.lda = K;
+  fp.packed = packed; fp.codes = codes; fp.consts = consts; fp.Kw = K;
+  fp.M = T; fp.N = N; fp.K0 = K;
+  fp.At = w.Us; fp.ldat = hilo_ld(r); fp.Bt = B; fp.ldbt = r; fp.r = r;
+  fp.C = Y; fp.ldc = N;
+  HIP_TRY(launch_fused(fp, false, s_, KID_FWD_GEMM));
   return QLORA_OK;
 }
 
@@ -330,7 +334,7 @@ int qlora_linear_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8
   if (!packed || !codes || !consts) return QLORA_ERR_NULL;
   if (T > 0 && (!X || !dY)) return QLORA_ERR_NULL;
   if (r > 0 && (!A || !B || !dA || !dB)) return QLORA_ERR_NULL;
-  if (!aligned16(packed) || !aligned16(X) || !aligned16(dY)) return QLORA_ERR_UNSUPPORTED;
+  if (!aligned16(packed) || !aligned16(X) || !aligned16(dY) || !aligned16(A)) return QLORA_ERR_UNSUPPORTED;
   const size_t need = plan_bwd(d, T, r, nullptr).bytes;
   if (need > 0 && (!workspace || workspace_bytes < need)) return QLORA_ERR_WORKSPACE;
 
@@ -362,11 +366,14 @@ int qlora_linear_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8
     HIP_TRY(launch_reduce_lowrank(w.g_part, w.sg.nsplit, T * r, T, r, s, nullptr, w.Gs, ldh, s_));
   }
   if (dX) {
-    // dX = dY W_hat + (s G) A: restore W transposed, tail over the 2r hi/lo columns
-    GemmParams px = gemm_one(op_bf16_k(dY, N, T, N), op_nf4(OP_NF4_T, packed, codes, consts, K, K, N), T, K);
-    if (r > 0) add_tail(px, op_bf16_k(w.Gs, ldh, T, 2 * (int64_t)r), op_bf16_t(A, K, K, 2 * (int64_t)r, r));
-    out_bf16(px, dX, K);
-    HIP_TRY(launch_gemm(px, s_, KID_DX_GEMM));
+    // dX = dY W_hat + (s G) A: the contraction runs over d_out, the rows of W
+    FusedParams fp{};
+    fp.A = dY; fp.lda = N;
+    fp.packed = packed; fp.codes = codes; fp.consts = consts; fp.Kw = K;
+    fp.M = T; fp.N = K; fp.K0 = N;
+    fp.At = w.Gs; fp.ldat = ldh; fp.Bt = A; fp.ldbt = K; fp.r = r;
+    fp.C = dX; fp.ldc = K;
+    HIP_TRY(launch_fused(fp, true, s_, KID_DX_GEMM));
   }
   if (r > 0) {
     // dA = (s G)^T X: rows j of the hi/lo pair, contraction over tokens

@@ -1,0 +1,498 @@
+// The two large products of the layer with the NF4 restore fused in:
+//   forward  Y  = bf16( X W_hat^T + [sU_hi | sU_lo] [B | B]^T )
+//   backward dX = bf16( dY W_hat  + [sG_hi | sG_lo] [A ; A] )
+//
+// "QLoRA技术从入门到精通" §3(2) restores the 4-bit weight at compute time
+// (table value times the block's stored scale, to a 16-bit float) and
+// discards it; "【X 长文】..." (storage and compute paragraph) restores each
+// 64-weight block to bf16 just before it enters the product.  Here every
+// 64-weight block is restored once per workgroup into an LDS bf16 tile and fed
+// to v_mfma_f32_32x32x16_bf16; the restored weight never reaches memory.
+//
+// Restore without table lookups in LDS: a thread that restores one block first
+// builds, in registers, the 16 values bf16(T[i] * s') of that block (16 fp32
+// products, 8 pack-converts) split into a high-byte table and a low-byte table
+// of four registers each; each 4-bit index is then resolved with v_perm_b32
+// byte selects (three per byte table per four indices), so a packed word of 8
+// indices costs about 29 VALU instructions and no memory access.  The values
+// are exactly bf16_rne(fl32(T[q] * s')).
+//
+// Tiling (gfx950: 256 CUs, 4 SIMDs each, 160 KB LDS, LDS reads ~128 B/clk):
+// 256 threads = 4 waves in a 2 x 2 grid, workgroup tile 256 x BN (BN = 256 or
+// 128), wave tile 128 x (BN/2) of 32 x 32 MFMA tiles, contraction step 64.
+// Two LDS stages: while the waves multiply stage t, the next step's operands
+// are already in registers (issued before the MFMAs) and are restored/written
+// into the other stage after them; one barrier per step.  Rows of
+// contraction-contiguous LDS tiles are padded to 144 B so that sixteen-byte
+// fragment reads of 8 consecutive rows hit distinct banks.
+//
+// dX contracts over d_out, the row index of the packed weight.  The restored
+// tile is stored row-major ([n][k], rows padded to 544/288 B) exactly as it
+// comes from memory, and the MFMA B fragments (8 consecutive n at one k) are
+// read with ds_read_b64_tr_b16: within each 16-lane group, source lane s
+// points at row kb + s/4, columns c0 + 4*(s%4), and lane i receives the four
+// rows kb..kb+3 of column c0 + i.
+//
+// The LoRA term runs as extra contraction steps over the 2r columns of a
+// hi/lo bf16 split of s*U (forward) or s*G (dX), so it is accumulated in fp32
+// with the base product before the single rounding of the output.
+//
+// Output: the fp32 tile is converted to bf16 into LDS and stored with
+// coalesced 16-byte writes.  Workgroups are ordered so that the tiles a single
+// XCD (round-robin by workgroup id) works on form a compact block (two tile
+// rows), keeping the operands they share in that XCD's L2.
+#include "fused.hpp"
+#include "trace.hpp"
+
+namespace qlora {
+namespace {
+
+constexpr int BK = 64;
+constexpr int LDK = BK + 8;  // contraction-contiguous LDS row: 72 bf16 = 144 B
+
+// Workgroup barrier that orders LDS only: waits for this wave's LDS operations,
+// then s_barrier.  (__syncthreads() also waits for every outstanding global
+// load, which would drain the producers' prefetch at each step.)  The asm is a
+// compiler memory barrier, so no LDS access moves across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// High-byte and low-byte tables of the 16 restored values of one block.
+struct RestoreTab {
+  uint32_t h[4], l[4];
+};
+
+__device__ __forceinline__ RestoreTab make_tab(const Nf4Table& tab, float sc) {
+  uint32_t w[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) w[j] = pack_bf16x2(tab.level[2 * j] * sc, tab.level[2 * j + 1] * sc);
+  RestoreTab t;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    t.h[i] = perm(w[2 * i + 1], w[2 * i], 0x07050301u);
+    t.l[i] = perm(w[2 * i + 1], w[2 * i], 0x06040200u);
+  }
+  return t;
+}
+
+// n holds four 4-bit indices, one per byte; returns the high and low bytes of
+// their restored bf16 values, one per byte.
+__device__ __forceinline__ void lookup4(uint32_t n, const RestoreTab& t, uint32_t& H, uint32_t& L) {
+  const uint32_t sl = n & 0x07070707u;
+  const uint32_t s2 = ((n >> 1) & 0x04040404u) | 0x03020100u;
+  H = perm(perm(t.h[3], t.h[2], sl), perm(t.h[1], t.h[0], sl), s2);
+  L = perm(perm(t.l[3], t.l[2], sl), perm(t.l[1], t.l[0], sl), s2);
+}
+
+// One packed word (8 indices, element 2j in the high nibble of byte j) ->
+// four words of bf16 pairs in element order.
+__device__ __forceinline__ void restore8(uint32_t w, const RestoreTab& t, uint32_t* out) {
+  uint32_t HE, LE, HO, LO;
+  lookup4((w >> 4) & 0x0F0F0F0Fu, t, HE, LE);
+  lookup4(w & 0x0F0F0F0Fu, t, HO, LO);
+  const uint32_t e01 = perm(HE, LE, 0x05010400u), e23 = perm(HE, LE, 0x07030602u);
+  const uint32_t o01 = perm(HO, LO, 0x05010400u), o23 = perm(HO, LO, 0x07030602u);
+  out[0] = perm(o01, e01, 0x05040100u);
+  out[1] = perm(o01, e01, 0x07060302u);
+  out[2] = perm(o23, e23, 0x05040100u);
+  out[3] = perm(o23, e23, 0x07060302u);
+}
+
+typedef uint16_t u16x4_t __attribute__((ext_vector_type(4)));
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+template <int BN, bool BT>
+struct Geometry {
+  static constexpr int BM = 256;
+  static constexpr int TM = 4;              // 32-row MFMA tiles per wave (wave rows 128)
+  static constexpr int TN = BN / 64;        // 32-col MFMA tiles per wave
+  static constexpr int A_ELEMS = BM * LDK;
+  // B tile: [BN][LDK] (contraction-contiguous) or [64][BN + 16] (column-contiguous)
+  static constexpr int LDB_T = BN + 16;
+  static constexpr int B_ELEMS = BT ? BK * LDB_T : BN * LDK;
+  static constexpr int STAGE = A_ELEMS + B_ELEMS;
+  static constexpr int LDC = BN + 8;        // epilogue bf16 tile row
+  static constexpr int LDS_ELEMS = (2 * STAGE > BM * LDC) ? 2 * STAGE : BM * LDC;
+};
+
+// ---------------------------------------------------------------------------
+// Producers: global -> registers (issued early), registers -> LDS (after the MFMAs)
+//
+// Main-loop loads are buffer loads whose per-thread byte offsets are computed
+// once; the contraction step advances through the scalar offset.  Rows beyond
+// the output (A rows >= M, weight rows/columns beyond the output columns) are
+// clamped to a valid address instead of masked: they only feed output rows or
+// columns that are never stored.
+// ---------------------------------------------------------------------------
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+template <int BN>
+struct StepRegs {
+  u32x4_t a[8];          // A: eight 16-byte chunks (rows tid/8 + 32i, columns (tid%8)*8 .. +8)
+  uint32_t w[BN / 32];   // packed weight words (8 indices each)
+  uint32_t code4;        // the aligned dword holding the block's 8-bit scale code
+  uint32_t code_shift;   // bit position of the code inside code4
+  float cg;
+};
+
+struct Cursor {
+  __amdgpu_buffer_rsrc_t ra, rw, rc, rk;
+  uint32_t aoff[8];  // byte offsets of the thread's A chunks at step 0
+  uint32_t woff;     // byte offset of the thread's packed words at step 0
+  uint32_t coff;     // block index of the thread's weights at step 0
+  uint32_t wstep;    // bytes the packed words advance per step
+  uint32_t cstep;    // blocks the block index advances per step
+  uint32_t nk;       // contraction steps
+  uint32_t rot;      // this workgroup starts its contraction at step rot (see fused_body)
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, int64_t bytes) {
+  const int32_t n = bytes > 0x7FFFFFF0LL ? 0x7FFFFFF0 : (int32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, n, 0x00020000);
+}
+
+// Producer-local thread index: producer waves are waves 4..7 of the workgroup.
+__device__ __forceinline__ int ptid() { return (int)threadIdx.x - 256; }
+
+template <int BN, bool BT>
+__device__ __forceinline__ void w_coords(int64_t n0, int& lrow, int& lcol) {
+  const int tid = ptid();
+  if (!BT) {
+    // forward: BN rows of 64 weights; one row (BN = 256) or half a row (BN = 128) per thread
+    if (BN == 256) { lrow = tid; lcol = 0; }
+    else { lrow = tid >> 1; lcol = (tid & 1) * 32; }
+  } else {
+    // dX: 64 rows (contraction) of BN columns; four threads per row
+    lrow = tid >> 2;
+    lcol = (tid & 3) * (BN / 4);
+  }
+}
+
+template <int BN, bool BT>
+__device__ __forceinline__ Cursor make_cursor(const FusedParams& P, int64_t m0, int64_t n0) {
+  const int tid = ptid();
+  Cursor c;
+  c.ra = rsrc(P.A, P.M * P.lda * 2);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    int64_t row = m0 + (tid >> 3) + 32 * i;
+    row = row < P.M ? row : P.M - 1;
+    c.aoff[i] = (uint32_t)((row * P.lda + (tid & 7) * 8) * 2);
+  }
+  const int64_t Nw = BT ? P.K0 : P.N;  // rows of the stored weight
+  c.rw = rsrc(P.packed, Nw * P.Kw / 2);
+  c.rc = rsrc(P.codes, Nw * P.Kw / 64);
+  c.rk = rsrc(P.consts, ((Nw * P.Kw / 64 + 255) / 256) * 4);
+  int lrow, lcol;
+  w_coords<BN, BT>(n0, lrow, lcol);
+  if (!BT) {
+    int64_t n = n0 + lrow;
+    n = n < P.N ? n : P.N - 1;
+    c.woff = (uint32_t)(n * (P.Kw / 2) + lcol / 2);
+    c.coff = (uint32_t)(n * (P.Kw / 64));
+    c.wstep = BK / 2;
+    c.cstep = 1;
+  } else {
+    int64_t k = n0 + lcol;
+    k = k < P.N ? k : 0;
+    c.woff = (uint32_t)(lrow * (P.Kw / 2) + k / 2);
+    c.coff = (uint32_t)(lrow * (P.Kw / 64) + k / 64);
+    c.wstep = (uint32_t)(BK * (P.Kw / 2));
+    c.cstep = (uint32_t)(BK * (P.Kw / 64));
+  }
+  return c;
+}
+
+template <int BN>
+__device__ __forceinline__ void fetch(StepRegs<BN>& f, const Cursor& c, uint32_t step) {
+  uint32_t kt = step + c.rot;
+  kt = kt >= c.nk ? kt - c.nk : kt;
+  const uint32_t sa = kt * (BK * 2);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f.a[i] = __builtin_amdgcn_raw_buffer_load_b128(c.ra, c.aoff[i], sa, 0);
+  const uint32_t sw = kt * c.wstep;
+  const u32x4_t w0 = __builtin_amdgcn_raw_buffer_load_b128(c.rw, c.woff, sw, 0);
+  f.w[0] = w0.x; f.w[1] = w0.y; f.w[2] = w0.z; f.w[3] = w0.w;
+  if (BN == 256) {
+    const u32x4_t w1 = __builtin_amdgcn_raw_buffer_load_b128(c.rw, c.woff + 16, sw, 0);
+    f.w[4] = w1.x; f.w[5] = w1.y; f.w[6] = w1.z; f.w[7] = w1.w;
+  }
+  const uint32_t blk = c.coff + kt * c.cstep;
+  // the codes array holds N*K/64 bytes, a multiple of 4, so the aligned dword is in range
+  f.code4 = __builtin_amdgcn_raw_buffer_load_b32(c.rc, blk & ~3u, 0, 0);
+  f.code_shift = (blk & 3u) * 8u;
+  f.cg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(c.rk, (blk >> 8) * 4, 0, 0));
+}
+
+// Keeps the scheduler from hoisting work on prefetched registers above the
+// point of use: an early use of a late load would wait for every load issued
+// before it (loads complete in order) and drain the prefetch.
+template <int BN>
+__device__ __forceinline__ void pin(StepRegs<BN>& f) {
+  asm volatile("" : "+v"(f.code4), "+v"(f.cg));
+#pragma unroll
+  for (int i = 0; i < BN / 32; ++i) asm volatile("" : "+v"(f.w[i]));
+}
+
+template <int BN, bool BT>
+__device__ __forceinline__ void store_step(StepRegs<BN>& f, const Nf4Table& tab, uint16_t* __restrict__ As,
+                                           uint16_t* __restrict__ Bs, int64_t n0) {
+  pin<BN>(f);
+  const int tid = ptid();
+  const int kc = (tid & 7) * 8;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    *reinterpret_cast<u32x4_t*>(As + ((tid >> 3) + 32 * i) * LDK + kc) = f.a[i];
+  int lrow, lcol;
+  w_coords<BN, BT>(n0, lrow, lcol);
+  const RestoreTab t = make_tab(tab, restored_scale((f.code4 >> f.code_shift) & 0xFFu, f.cg));
+  uint16_t* dst = BT ? Bs + lrow * Geometry<BN, BT>::LDB_T + lcol : Bs + lrow * LDK + lcol;
+#pragma unroll
+  for (int i = 0; i < BN / 32; i += 2) {
+    uint32_t o[8];
+    restore8(f.w[i], t, o);
+    restore8(f.w[i + 1], t, o + 4);
+    *reinterpret_cast<uint4*>(dst + i * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<uint4*>(dst + i * 8 + 8) = make_uint4(o[4], o[5], o[6], o[7]);
+  }
+}
+
+// Tail A operand (the hi/lo pair of s*U or s*G, [M][ldat], zero past 2r):
+// plain loads with row clamping; the tail runs once per tile.
+__device__ __forceinline__ void tail_a_store(const uint16_t* __restrict__ At, int64_t ldat, int64_t M, int64_t m0,
+                                             int64_t k0, uint16_t* __restrict__ As) {
+  const int tid = ptid();
+  const int kc = (tid & 7) * 8;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    int64_t row = m0 + (tid >> 3) + 32 * i;
+    row = row < M ? row : M - 1;
+    *reinterpret_cast<uint4*>(As + ((tid >> 3) + 32 * i) * LDK + kc) =
+        *reinterpret_cast<const uint4*>(At + row * ldat + k0 + kc);
+  }
+}
+
+// LoRA tail B operand (bf16, small): forward Bop[n][kk] = B[n][kk % r],
+// dX Bop[kk][k] = A[kk % r][k].  Columns kk >= 2r meet zeros in the tail A
+// operand, so they need no masking.  Written straight to LDS.
+template <int BN, bool BT>
+__device__ __forceinline__ void tail_b_store(const uint16_t* __restrict__ Bt, int64_t ldbt, int r, int64_t cols,
+                                             int64_t n0, int64_t kt, uint16_t* __restrict__ Bs) {
+  const int tid = ptid();
+  if (!BT) {
+    for (int c = tid; c < BN * 8; c += 256) {
+      const int lrow = c >> 3, kc = (c & 7) * 8;
+      int64_t n = n0 + lrow;
+      n = n < cols ? n : cols - 1;
+      const uint32_t kk = (uint32_t)(kt * BK + kc);
+      uint4 v;
+      if ((r & 7) == 0) {
+        v = *reinterpret_cast<const uint4*>(Bt + n * ldbt + kk % (uint32_t)r);
+      } else {
+        uint16_t e[8];
+        for (int q = 0; q < 8; ++q) e[q] = Bt[n * ldbt + (kk + q) % (uint32_t)r];
+        v = make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16));
+      }
+      *reinterpret_cast<uint4*>(Bs + lrow * LDK + kc) = v;
+    }
+  } else {
+    constexpr int LDB_T = Geometry<BN, BT>::LDB_T;
+    for (int c = tid; c < BK * (BN / 8); c += 256) {
+      const int lrow = c / (BN / 8), lc = (c % (BN / 8)) * 8;
+      const int64_t kk = kt * BK + lrow;
+      int64_t col = n0 + lc;
+      col = col < cols ? col : 0;
+      *reinterpret_cast<uint4*>(Bs + lrow * LDB_T + lc) =
+          *reinterpret_cast<const uint4*>(Bt + (int64_t)((uint32_t)kk % (uint32_t)r) * ldbt + col);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// MFMA on one LDS stage
+// ---------------------------------------------------------------------------
+
+template <int BN, bool BT>
+__device__ __forceinline__ void mma_stage(const uint16_t* __restrict__ As, const uint16_t* __restrict__ Bs,
+                                          f32x16_t (&acc)[4][BN / 64]) {
+  constexpr int TM = 4, TN = BN / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int ks = 0; ks < BK / 16; ++ks) {
+    bf16x8_t a[TM], b[TN];
+    const int kofs = ks * 16 + (lane >> 5) * 8;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      a[i] = *reinterpret_cast<const bf16x8_t*>(As + ((wm * TM + i) * 32 + (lane & 31)) * LDK + kofs);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      if (!BT) {
+        b[j] = *reinterpret_cast<const bf16x8_t*>(Bs + ((wn * TN + j) * 32 + (lane & 31)) * LDK + kofs);
+      } else {
+        constexpr int LDB_T = Geometry<BN, BT>::LDB_T;
+        const int s = lane & 15;
+        const int col = (wn * TN + j) * 32 + ((lane >> 4) & 1) * 16 + 4 * (s & 3);
+        const int row = kofs + (s >> 2);
+        typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
+        const lds_u16_t* base = (const lds_u16_t*)Bs;
+        const u16x4_t lo = __builtin_bit_cast(
+            u16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(base + row * LDB_T + col)));
+        const u16x4_t hi = __builtin_bit_cast(
+            u16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(base + (row + 4) * LDB_T + col)));
+        typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
+        const u16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        b[j] = __builtin_bit_cast(bf16x8_t, v);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The kernel body
+// ---------------------------------------------------------------------------
+
+template <int BN, bool BT>
+__device__ __forceinline__ void fused_body(const FusedParams& P) {
+  using G = Geometry<BN, BT>;
+  constexpr int TM = G::TM, TN = G::TN;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[G::LDS_ELEMS];
+
+  // tile order: chunks of consecutive tiles go to one XCD; inside the order,
+  // groups of two tile rows are walked column by column.
+  const int64_t ntiles = (int64_t)P.mt * P.nt;
+  const int64_t chunk = (ntiles + 7) / 8;
+  const int64_t order = (int64_t)(blockIdx.x % 8) * chunk + blockIdx.x / 8;
+  if (order >= ntiles) return;
+  const int gm = P.group_m;
+  const int64_t group = order / ((int64_t)gm * P.nt);
+  const int64_t first_m = group * gm;
+  const int64_t rows_in_group = (P.mt - first_m) < gm ? (P.mt - first_m) : gm;
+  const int64_t in_group = order - group * gm * P.nt;
+  const int64_t tm = first_m + in_group % rows_in_group;
+  const int64_t tn = in_group / rows_in_group;
+  const int64_t m0 = tm * G::BM, n0 = tn * BN;
+
+  uint16_t* stage0 = lds;
+  uint16_t* stage1 = lds + G::STAGE;
+  const uint32_t nk = (uint32_t)(P.K0 / BK);
+  const uint32_t ntail = P.r > 0 ? (uint32_t)((2 * (int64_t)P.r + BK - 1) / BK) : 0;
+
+  // Waves 0-3 multiply (consumers), waves 4-7 load and restore (producers);
+  // two waves per SIMD, so one's VALU/memory work overlaps the other's MFMAs.
+  // Both roles pass the same sequence of barriers: 1 + nk + 2*ntail + 1.
+  if (threadIdx.x < 256) {
+    f32x16_t acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+    lds_barrier();
+    for (uint32_t h = 0; h < nk; ++h) {
+      uint16_t* st = (h & 1) ? stage1 : stage0;
+      mma_stage<BN, BT>(st, st + G::A_ELEMS, acc);
+      lds_barrier();
+    }
+    for (uint32_t t = 0; t < ntail; ++t) {
+      lds_barrier();
+      mma_stage<BN, BT>(stage0, stage0 + G::A_ELEMS, acc);
+      lds_barrier();
+    }
+    // epilogue: bf16 tile into LDS
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col = (wn * TN + j) * 32 + (lane & 31);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = (wm * TM + i) * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          lds[row * G::LDC + col] = f32_to_bf16_bits(acc[i][j][v]);
+        }
+      }
+    lds_barrier();
+  } else {
+    Cursor cur = make_cursor<BN, BT>(P, m0, n0);
+    // Workgroups that run together on one XCD would otherwise walk the
+    // contraction in lockstep, all reading the same column block of every
+    // operand row at once (rows are a power-of-two apart, so those requests
+    // pile onto few L2 channels).  Each tile starts at its own step instead;
+    // the sum order per tile is fixed, so results stay deterministic.
+    cur.nk = nk;
+    cur.rot = (uint32_t)((order * 5) % nk);
+    // three register sets: set i%3 holds step i; at half-step h the producers
+    // issue the loads of step h+3 into the set freed by step h, then restore
+    // step h+1 into LDS stage (h+1)%2, so every load has two steps in flight.
+    StepRegs<BN> f0, f1, f2;
+    const uint32_t last = nk - 1;
+    fetch<BN>(f0, cur, 0);
+    fetch<BN>(f1, cur, 1 < nk ? 1 : last);
+    fetch<BN>(f2, cur, 2 < nk ? 2 : last);
+    store_step<BN, BT>(f0, P.tab, stage0, stage0 + G::A_ELEMS, n0);
+    lds_barrier();
+    auto half = [&](StepRegs<BN>& into, StepRegs<BN>& from, uint16_t* st, uint32_t h) {
+      fetch<BN>(into, cur, h + 3 < nk ? h + 3 : last);
+      if (h + 1 < nk) store_step<BN, BT>(from, P.tab, st, st + G::A_ELEMS, n0);
+      lds_barrier();
+    };
+    for (uint32_t h = 0; h < nk; h += 6) {
+      half(f0, f1, stage1, h);
+      if (h + 1 < nk) half(f1, f2, stage0, h + 1);
+      if (h + 2 < nk) half(f2, f0, stage1, h + 2);
+      if (h + 3 < nk) half(f0, f1, stage0, h + 3);
+      if (h + 4 < nk) half(f1, f2, stage1, h + 4);
+      if (h + 5 < nk) half(f2, f0, stage0, h + 5);
+    }
+    // rank-r term: contraction over the hi/lo columns (zero-padded to a multiple of 64)
+    for (uint32_t t = 0; t < ntail; ++t) {
+      tail_a_store(P.At, P.ldat, P.M, m0, (int64_t)t * BK, stage0);
+      tail_b_store<BN, BT>(P.Bt, P.ldbt, P.r, P.N, n0, t, stage0 + G::A_ELEMS);
+      lds_barrier();
+      lds_barrier();
+    }
+    lds_barrier();
+  }
+
+  // coalesced 16-byte stores of the bf16 tile, all eight waves
+  for (int c = threadIdx.x; c < G::BM * (BN / 8); c += 512) {
+    const int row = c / (BN / 8), cc = (c % (BN / 8)) * 8;
+    const int64_t gr = m0 + row, gc = n0 + cc;
+    if (gr < P.M && gc < P.N)
+      *reinterpret_cast<uint4*>(P.C + gr * P.ldc + gc) = *reinterpret_cast<const uint4*>(lds + row * G::LDC + cc);
+  }
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(512) void k_qlora_fwd_gemm(FusedParams P) { fused_body<128, false>(P); }
+__global__ __launch_bounds__(512) void k_qlora_dx_gemm(FusedParams P) { fused_body<128, true>(P); }
+
+hipError_t launch_fused(FusedParams P, bool dx, hipStream_t stream, int kernel_id) {
+  constexpr int bn = 128;
+  P.mt = (int32_t)((P.M + 255) / 256);
+  P.nt = (int32_t)((P.N + bn - 1) / bn);
+  P.group_m = 2;
+  P.tab = nf4_table();
+  const int64_t ntiles = (int64_t)P.mt * P.nt;
+  const unsigned grid = (unsigned)(((ntiles + 7) / 8) * 8);
+  TraceScope ts(kernel_id, stream);
+  if (!dx) hipLaunchKernelGGL(k_qlora_fwd_gemm, dim3(grid), dim3(512), 0, stream, P);
+  else hipLaunchKernelGGL(k_qlora_dx_gemm, dim3(grid), dim3(512), 0, stream, P);
+  return hipGetLastError();
+}
+
+}  // namespace qlora

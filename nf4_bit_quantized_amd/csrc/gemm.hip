@@ -265,16 +265,6 @@ __device__ __forceinline__ void gemm_body(const GemmParams& P, const Nf4Table& t
   }
 }
 
-// Forward base product X W_hat^T (+ LoRA tail): restore along k.
-__global__ __launch_bounds__(256) void k_qlora_fwd_gemm(GemmParams P, Nf4Table tab) {
-  gemm_body<128, 128, 2, 2, OP_BF16_K, OP_NF4_K>(P, tab);
-}
-
-// dX = dY W_hat (+ LoRA tail): restore and transpose.
-__global__ __launch_bounds__(256) void k_qlora_dx_gemm(GemmParams P, Nf4Table tab) {
-  gemm_body<128, 128, 2, 2, OP_BF16_K, OP_NF4_T>(P, tab);
-}
-
 // Adapter products and anything else: operand kinds read at run time.
 template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(256) void k_lowrank_gemm(GemmParams P, Nf4Table tab) {
@@ -303,19 +293,12 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t stream, int kernel_id) {
   gemm_tile_shape(cfg, &bm, &bn);
   const dim3 grid((unsigned)((p.N + bn - 1) / bn), (unsigned)((p.M + bm - 1) / bm), (unsigned)p.nsplit);
   const Nf4Table& tab = nf4_table();
-  const int ka = p.seg[0].a.kind, kb = p.seg[0].b.kind;
   TraceScope ts(kernel_id, stream);
-  if (cfg == 0 && ka == OP_BF16_K && kb == OP_NF4_K) {
-    hipLaunchKernelGGL(k_qlora_fwd_gemm, grid, dim3(256), 0, stream, p, tab);
-  } else if (cfg == 0 && ka == OP_BF16_K && kb == OP_NF4_T) {
-    hipLaunchKernelGGL(k_qlora_dx_gemm, grid, dim3(256), 0, stream, p, tab);
-  } else {
-    switch (cfg) {
-      case 0: hipLaunchKernelGGL((k_lowrank_gemm<128, 128, 2, 2>), grid, dim3(256), 0, stream, p, tab); break;
-      case 1: hipLaunchKernelGGL((k_lowrank_gemm<32, 128, 1, 4>), grid, dim3(256), 0, stream, p, tab); break;
-      case 2: hipLaunchKernelGGL((k_lowrank_gemm<128, 32, 4, 1>), grid, dim3(256), 0, stream, p, tab); break;
-      default: hipLaunchKernelGGL((k_lowrank_gemm<64, 64, 2, 2>), grid, dim3(256), 0, stream, p, tab); break;
-    }
+  switch (cfg) {
+    case 0: hipLaunchKernelGGL((k_lowrank_gemm<128, 128, 2, 2>), grid, dim3(256), 0, stream, p, tab); break;
+    case 1: hipLaunchKernelGGL((k_lowrank_gemm<32, 128, 1, 4>), grid, dim3(256), 0, stream, p, tab); break;
+    case 2: hipLaunchKernelGGL((k_lowrank_gemm<128, 32, 4, 1>), grid, dim3(256), 0, stream, p, tab); break;
+    default: hipLaunchKernelGGL((k_lowrank_gemm<64, 64, 2, 2>), grid, dim3(256), 0, stream, p, tab); break;
   }
   return hipGetLastError();
 }

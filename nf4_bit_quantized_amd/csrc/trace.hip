@@ -18,7 +18,7 @@ struct Pending {
 };
 
 std::mutex g_mu;
-bool g_enabled = false;
+uint32_t g_mask = 0;  // bit k set: launches of kernel k are bracketed
 std::vector<Pending> g_pending;
 std::vector<hipEvent_t> g_pool;
 int64_t g_launches[KID_COUNT] = {};
@@ -39,7 +39,7 @@ hipEvent_t take_event() {
 
 TraceScope::TraceScope(int kid, hipStream_t stream) : kid_(kid), stream_(stream) {
   std::lock_guard<std::mutex> lk(g_mu);
-  if (!g_enabled) return;
+  if (!((g_mask >> kid) & 1u)) return;
   start_ = take_event();
   stop_ = take_event();
   if (!start_ || !stop_) return;
@@ -58,8 +58,18 @@ using namespace qlora;
 
 extern "C" int qlora_trace_enable(int enable) {
   std::lock_guard<std::mutex> lk(g_mu);
-  g_enabled = enable != 0;
+  g_mask = enable ? 0xFFFFFFFFu : 0u;
   return QLORA_OK;
+}
+
+extern "C" int qlora_trace_select(uint32_t kernel_mask) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_mask = kernel_mask;
+  return QLORA_OK;
+}
+
+extern "C" const char* qlora_trace_kernel_name(int kernel) {
+  return (kernel >= 0 && kernel < KID_COUNT) ? kNames[kernel] : nullptr;
 }
 
 extern "C" int qlora_trace_read(qlora_kernel_stat* stats, int max_stats, int* count, int reset) {

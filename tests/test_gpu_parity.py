@@ -226,3 +226,25 @@ def test_zero_tokens_is_a_no_op():
     q.qlora_linear_bwd(packed, codes, consts, X, A, B, 8.0, dY, dA=dA, dB=dB)
     torch.cuda.synchronize()
     assert Y.shape == (0, 128) and torch.all(dA == 0) and torch.all(dB == 0)
+
+
+def test_restore_is_bit_exact_through_identity():
+    """With X = I (forward, r = 0) every output is one restored weight, so Y
+    must equal W_hat^T bit for bit; with dY = I the same holds for dX = W_hat.
+    Covers the tiled forward, the transposed-restore dX and the few-token path."""
+    import nf4_bit_quantized_amd as q
+    import torch
+    d_out, d_in = 320, 256
+    inp = workloads.layer_inputs(d_out, d_in, 1, 1, seed=13, with_dy=False)
+    W_hat = onf4.dequantize(onf4.quantize(inp["W"]))            # float32, bf16-valued
+    packed, codes, consts = q.qlora_quantize_nf4(dev_f32(inp["W"]))
+    eye_k = torch.eye(d_in, dtype=torch.bfloat16, device="cuda")
+    Y, _ = q.qlora_linear_fwd(packed, codes, consts, eye_k, None, None, 0.0)
+    eye_n = torch.eye(d_out, dtype=torch.bfloat16, device="cuda")
+    dX, _, _ = q.qlora_linear_bwd(packed, codes, consts, torch.zeros((d_out, d_in), dtype=torch.bfloat16,
+                                                                      device="cuda"), None, None, 0.0, eye_n)
+    Y16, _ = q.qlora_linear_fwd(packed, codes, consts, eye_k[:16].contiguous(), None, None, 0.0)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(Y.float().cpu().numpy(), W_hat.T)
+    np.testing.assert_array_equal(dX.float().cpu().numpy(), W_hat)
+    np.testing.assert_array_equal(Y16.float().cpu().numpy(), W_hat.T[:16])
