@@ -2,10 +2,11 @@
 // planning and the sequence of launches on the caller's stream.  The
 // declarations, with argument meaning and error behaviour, are in
 // include/qlora.h.
+#include <algorithm>
 #include <cstring>
 
 #include "fused.hpp"
-#include "gemm.hpp"
+#include "skinny.hpp"
 #include "trace.hpp"
 #include "../../include/qlora.h"
 
@@ -16,15 +17,7 @@ hipError_t launch_decode(const uint8_t* packed, const uint8_t* codes, const floa
                          const uint16_t* X, int64_t T, int64_t N, int64_t K, int64_t kchunk,
                          int nsplit, float* Ppart, const float* U, int r, float s,
                          const uint16_t* B, uint16_t* Y, hipStream_t stream);
-hipError_t launch_reduce_lowrank(const float* P, int nsplit, int64_t split_stride, int64_t T, int r,
-                                 float s, float* V, uint16_t* Hs, int64_t ldh, hipStream_t stream);
-hipError_t launch_reduce_colpairs(const float* P, int nsplit, int64_t split_stride, int64_t M, int r,
-                                  float* out, hipStream_t stream);
-hipError_t launch_reduce_rowpairs(const float* P, int nsplit, int64_t split_stride, int r, int64_t K,
-                                  float* out, hipStream_t stream);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
-int gemm_tile_config(int64_t M, int64_t N);
-void gemm_tile_shape(int cfg, int* bm, int* bn);
 }  // namespace qlora
 
 using namespace qlora;
@@ -51,28 +44,6 @@ int check_layer(const qlora_nf4_desc* d, int64_t T, int32_t r) {
   if (st) return st;
   if (T < 0 || r < 0 || r > kMaxRank) return QLORA_ERR_SHAPE;
   return QLORA_OK;
-}
-
-// Split of a partial-sum contraction over grid.z.
-struct Split {
-  int nsplit;
-  int tps;  // 64-wide contraction tiles per split
-};
-
-Split plan_split(int64_t M, int64_t N, int64_t kdim) {
-  int bm, bn;
-  gemm_tile_shape(gemm_tile_config(M, N), &bm, &bn);
-  const int64_t tiles = cdiv(M, bm) * cdiv(N, bn);
-  const int64_t kt = cdiv(kdim, 64);
-  int64_t ns = cdiv(kTargetWorkgroups, tiles);
-  const int64_t cap = kt / 2 > 1 ? kt / 2 : 1;
-  if (ns > cap) ns = cap;
-  if (ns < 1) ns = 1;
-  const int64_t tps = cdiv(kt, ns) > 0 ? cdiv(kt, ns) : 1;
-  Split s;
-  s.tps = (int)tps;
-  s.nsplit = (int)(kt > 0 ? cdiv(kt, tps) : 1);
-  return s;
 }
 
 struct DecodePlan {
@@ -105,10 +76,15 @@ struct Carve {
   }
 };
 
+// Scratch for the split-contraction partials of one rank-r product.
+size_t skinny_part_bytes(int64_t mrows, int64_t clen, int64_t cols) {
+  const int ns = skinny_splits(mrows, clen, (int)cols);
+  return ns > 1 ? (size_t)ns * mrows * cols * 4 : 0;
+}
+
 struct FwdWs {
-  Split su;
   DecodePlan dp;
-  float* u_part = nullptr;
+  float* part = nullptr;
   float* U = nullptr;
   uint16_t* Us = nullptr;
   float* dec = nullptr;
@@ -120,8 +96,7 @@ FwdWs plan_fwd(const qlora_nf4_desc* d, int64_t T, int32_t r, void* ws) {
   Carve c(ws);
   const int64_t N = d->d_out, K = d->d_in;
   if (r > 0 && T > 0) {
-    w.su = plan_split(T, r, K);
-    w.u_part = static_cast<float*>(c.take((size_t)w.su.nsplit * T * r * 4));
+    w.part = static_cast<float*>(c.take(skinny_part_bytes(T, K, r)));
     w.U = static_cast<float*>(c.take((size_t)T * r * 4));
     w.Us = static_cast<uint16_t*>(c.take((size_t)T * hilo_ld(r) * 2));
   }
@@ -134,14 +109,10 @@ FwdWs plan_fwd(const qlora_nf4_desc* d, int64_t T, int32_t r, void* ws) {
 }
 
 struct BwdWs {
-  Split su, sg, sda, sdb;
-  float* u_part = nullptr;
+  float* part = nullptr;  // shared by the rank-r products (they run one after another)
   float* U = nullptr;
   uint16_t* Us = nullptr;
-  float* g_part = nullptr;
   uint16_t* Gs = nullptr;
-  float* da_part = nullptr;
-  float* db_part = nullptr;
   size_t bytes = 0;
 };
 
@@ -151,61 +122,33 @@ BwdWs plan_bwd(const qlora_nf4_desc* d, int64_t T, int32_t r, void* ws) {
   const int64_t N = d->d_out, K = d->d_in;
   if (r > 0 && T > 0) {
     const int64_t ldh = hilo_ld(r);
-    w.su = plan_split(T, r, K);
-    w.sg = plan_split(T, r, N);
-    w.sda = plan_split(2 * (int64_t)r, K, T);
-    w.sdb = plan_split(N, 2 * (int64_t)r, T);
-    w.u_part = static_cast<float*>(c.take((size_t)w.su.nsplit * T * r * 4));
+    size_t part = skinny_part_bytes(T, K, r);
+    part = std::max(part, skinny_part_bytes(T, N, r));
+    part = std::max(part, skinny_part_bytes(K, T, 2 * (int64_t)r));
+    part = std::max(part, skinny_part_bytes(N, T, 2 * (int64_t)r));
+    w.part = static_cast<float*>(c.take(part));
     w.U = static_cast<float*>(c.take((size_t)T * r * 4));
     w.Us = static_cast<uint16_t*>(c.take((size_t)T * ldh * 2));
-    w.g_part = static_cast<float*>(c.take((size_t)w.sg.nsplit * T * r * 4));
     w.Gs = static_cast<uint16_t*>(c.take((size_t)T * ldh * 2));
-    w.da_part = static_cast<float*>(c.take((size_t)w.sda.nsplit * 2 * r * K * 4));
-    w.db_part = static_cast<float*>(c.take((size_t)w.sdb.nsplit * N * 2 * r * 4));
   }
   w.bytes = c.off;
   return w;
 }
 
-Operand op_bf16_k(const uint16_t* p, int64_t ld, int64_t rows, int64_t kdim, int32_t kk_mod = 0) {
-  Operand o{};
-  o.kind = OP_BF16_K; o.p = p; o.ld = ld; o.rows = rows; o.kdim = kdim; o.kk_mod = kk_mod;
-  return o;
-}
-Operand op_bf16_t(const uint16_t* p, int64_t ld, int64_t rows, int64_t kdim, int32_t kk_mod = 0) {
-  Operand o{};
-  o.kind = OP_BF16_T; o.p = p; o.ld = ld; o.rows = rows; o.kdim = kdim; o.kk_mod = kk_mod;
-  return o;
-}
-Operand op_nf4(int kind, const uint8_t* packed, const uint8_t* codes, const float* consts, int64_t K,
-               int64_t rows, int64_t kdim) {
-  Operand o{};
-  o.kind = kind; o.p = packed; o.codes = codes; o.consts = consts; o.ld = K; o.rows = rows; o.kdim = kdim;
-  return o;
+bool vec_ok(const void* p, int64_t ld) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0 && (ld & 7) == 0; }
+
+SkinnyParams skinny(const uint16_t* P, int64_t ldp, bool p_contig, int64_t mrows, int64_t clen, int r, float s,
+                    int qcols, int out_mode, float* part) {
+  SkinnyParams S{};
+  S.P = P; S.ldp = ldp; S.p_contig = p_contig; S.pvec = vec_ok(P, ldp);
+  S.mrows = mrows; S.clen = clen; S.r = r; S.s = s; S.qcols = qcols; S.out_mode = out_mode;
+  S.nsplit = skinny_splits(mrows, clen, qcols);
+  S.Pout = part;
+  return S;
 }
 
-GemmParams gemm_one(const Operand& a, const Operand& b, int64_t M, int64_t N) {
-  GemmParams p{};
-  p.seg[0].a = a; p.seg[0].b = b; p.seg[0].ktiles = cdiv(a.kdim, 64);
-  p.nseg = 1; p.M = M; p.N = N; p.nsplit = 1;
-  p.tiles_per_split = (int)p.seg[0].ktiles;
-  return p;
-}
-
-void add_tail(GemmParams& p, const Operand& a, const Operand& b) {
-  p.seg[1].a = a; p.seg[1].b = b; p.seg[1].ktiles = cdiv(a.kdim, 64);
-  p.nseg = 2;
-  p.tiles_per_split = (int)(p.seg[0].ktiles + p.seg[1].ktiles);
-}
-
-void out_bf16(GemmParams& p, uint16_t* out, int64_t ldo) {
-  p.out_kind = OUT_BF16; p.out = out; p.ldo = ldo;
-}
-
-void out_partial(GemmParams& p, float* out, int64_t ldo, const Split& s) {
-  p.out_kind = OUT_F32; p.out = out; p.ldo = ldo;
-  p.split_stride = p.M * ldo;
-  p.nsplit = s.nsplit; p.tiles_per_split = s.tps;
+void skinny_q(SkinnyParams& S, const uint16_t* Q, int64_t ldq, int64_t qrows, int q_mode) {
+  S.Q = Q; S.ldq = ldq; S.qrows = qrows; S.q_mode = q_mode; S.qvec = vec_ok(Q, ldq);
 }
 
 #define HIP_TRY(expr)                          \
@@ -214,12 +157,12 @@ void out_partial(GemmParams& p, float* out, int64_t ldo, const Split& s) {
   } while (0)
 
 // U = X A^T (fp32 into U), and the hi/lo bf16 pair of s*U into Us.
-int lora_down(const uint16_t* X, const uint16_t* A, int64_t T, int64_t K, int32_t r, float s,
-              const Split& su, float* u_part, float* U, uint16_t* Us, hipStream_t st) {
-  GemmParams p = gemm_one(op_bf16_k(X, K, T, K), op_bf16_k(A, K, r, K), T, r);
-  out_partial(p, u_part, r, su);
-  HIP_TRY(launch_gemm(p, st, KID_LORA_DOWN));
-  HIP_TRY(launch_reduce_lowrank(u_part, su.nsplit, (int64_t)T * r, T, r, s, U, Us, hilo_ld(r), st));
+int lora_down(const uint16_t* X, const uint16_t* A, int64_t T, int64_t K, int32_t r, float s, float* part,
+              float* U, uint16_t* Us, hipStream_t st) {
+  SkinnyParams S = skinny(X, K, true, T, K, r, s, r, OUT_ROWS_HILO, part);
+  skinny_q(S, A, K, r, Q_CONTIG);
+  S.Vout = U; S.Hout = Us; S.ldh = hilo_ld(r);
+  HIP_TRY(launch_skinny(S, st, KID_LORA_DOWN));
   return QLORA_OK;
 }
 
@@ -306,7 +249,7 @@ int qlora_linear_fwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8
   float* U = U_out ? U_out : w.U;
 
   if (r > 0) {
-    const int e = lora_down(X, A, T, K, r, s, w.su, w.u_part, U, w.Us, s_);
+    const int e = lora_down(X, A, T, K, r, s, w.part, U, w.Us, s_);
     if (e) return e;
   }
   if (T <= kDecodeMaxT) {
@@ -352,18 +295,11 @@ int qlora_linear_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8
   const int64_t ldh = hilo_ld(r);
 
   if (r > 0) {
-    // hi/lo of s*U (recomputing U when it was not saved)
-    if (U_in) {
-      HIP_TRY(launch_reduce_lowrank(U_in, 1, 0, T, r, s, nullptr, w.Us, ldh, s_));
-    } else {
-      const int e = lora_down(X, A, T, K, r, s, w.su, w.u_part, w.U, w.Us, s_);
-      if (e) return e;
-    }
-    // G = dY B  ->  hi/lo of s*G
-    GemmParams pg = gemm_one(op_bf16_k(dY, N, T, N), op_bf16_t(B, r, r, N), T, r);
-    out_partial(pg, w.g_part, r, w.sg);
-    HIP_TRY(launch_gemm(pg, s_, KID_LORA_G));
-    HIP_TRY(launch_reduce_lowrank(w.g_part, w.sg.nsplit, T * r, T, r, s, nullptr, w.Gs, ldh, s_));
+    // G = dY B -> hi/lo of s*G (feeds the dX tail and dA)
+    SkinnyParams S = skinny(dY, N, true, T, N, r, s, r, OUT_ROWS_HILO, w.part);
+    skinny_q(S, B, r, r, Q_STRIDED);
+    S.Hout = w.Gs; S.ldh = ldh;
+    HIP_TRY(launch_skinny(S, s_, KID_LORA_G));
   }
   if (dX) {
     // dX = dY W_hat + (s G) A: the contraction runs over d_out, the rows of W
@@ -376,16 +312,22 @@ int qlora_linear_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8
     HIP_TRY(launch_fused(fp, true, s_, KID_DX_GEMM));
   }
   if (r > 0) {
-    // dA = (s G)^T X: rows j of the hi/lo pair, contraction over tokens
-    GemmParams pa = gemm_one(op_bf16_t(w.Gs, ldh, 2 * (int64_t)r, T), op_bf16_t(X, K, K, T), 2 * (int64_t)r, K);
-    out_partial(pa, w.da_part, K, w.sda);
-    HIP_TRY(launch_gemm(pa, s_, KID_LORA_DA));
-    HIP_TRY(launch_reduce_rowpairs(w.da_part, w.sda.nsplit, 2 * (int64_t)r * K, r, K, dA, s_));
-    // dB = dY^T (s U): columns j of the hi/lo pair, contraction over tokens
-    GemmParams pb = gemm_one(op_bf16_t(dY, N, N, T), op_bf16_t(w.Us, ldh, 2 * (int64_t)r, T), N, 2 * (int64_t)r);
-    out_partial(pb, w.db_part, 2 * (int64_t)r, w.sdb);
-    HIP_TRY(launch_gemm(pb, s_, KID_LORA_DB));
-    HIP_TRY(launch_reduce_colpairs(w.db_part, w.sdb.nsplit, N * 2 * (int64_t)r, N, r, dB, s_));
+    // dA = (s G)^T X over the hi/lo columns, pairs summed: dA [r][d_in]
+    SkinnyParams Sa = skinny(X, K, false, K, T, r, s, 2 * r, OUT_PAIRS_T, w.part);
+    skinny_q(Sa, w.Gs, ldh, 2 * (int64_t)r, Q_STRIDED);
+    Sa.Fout = dA;
+    HIP_TRY(launch_skinny(Sa, s_, KID_LORA_DA));
+    // dB = dY^T (s U) over the hi/lo columns, pairs summed: dB [d_out][r]
+    SkinnyParams Sb = skinny(dY, N, false, N, T, r, s, 2 * r, OUT_PAIRS, w.part);
+    if (U_in) {
+      Sb.q_mode = Q_HILO; Sb.V = U_in; Sb.ldv = r;
+    } else {
+      const int e = lora_down(X, A, T, K, r, s, w.part, w.U, w.Us, s_);
+      if (e) return e;
+      skinny_q(Sb, w.Us, ldh, 2 * (int64_t)r, Q_STRIDED);
+    }
+    Sb.Fout = dB;
+    HIP_TRY(launch_skinny(Sb, s_, KID_LORA_DB));
   }
   return QLORA_OK;
 }
