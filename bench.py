@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the few-token packed-weight GB/s section")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget for the oracle timing")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after the JSON line, fill then copy a buffer of this many MiB (known HBM bytes "
+                         "for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
 
 
@@ -267,6 +270,15 @@ def main():
         log("timing the oracle on the host ...")
         result["cpu_baseline"] = cpu_baseline(inp, lin, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+    if args.copy_calibration > 0:
+        nbytes = args.copy_calibration << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        src.fill_(1)      # writes nbytes, reads none
+        dst.copy_(src)    # reads nbytes, writes nbytes
+        torch.cuda.synchronize()
+        log(f"copy calibration: fill + copy of {nbytes} bytes")
 
 
 if __name__ == "__main__":

@@ -21,6 +21,32 @@ struct Nf4Table {
 
 const Nf4Table& nf4_table();
 
+// Decision tables of the quantization kernel (built on the host from the
+// thresholds above, passed by value).  A normalized value y is first
+// estimated as y' = x * rcp(s), within a few ulp of fl32(x / s).  The top 16
+// bits of y' select a bucket: index 0 holds |y'| < 2^-6, index i >= 1 the
+// bf16 interval starting at bits 0x3C7F + i; the sign picks one of two rows.
+// Every bucket, widened by a relative 2^-19 on both sides, contains at most one
+// threshold; kidx is the number of thresholds below it, so the level index is
+// kidx + [fl32(x / s) > thr[kidx]], and that one comparison is made exactly
+// as x > s * mid[kidx] in double precision (mid[k] is the midpoint between
+// thr[k] and the next float32 above it; s * mid is exact in double, and
+// x / s never equals mid, so no tie can occur).  mid[15] = +inf.
+constexpr int kLutSide = 770;
+struct QuantLut {
+  uint8_t kidx[2 * kLutSide + 4];  // [sign][bucket], padded to whole words
+  double mid[16];
+};
+
+// The table above; ok is false if some widened bucket held two thresholds.
+const QuantLut& quant_lut(bool* ok);
+
+// Workgroup barrier that orders LDS only: waits for this wave's LDS
+// operations, then s_barrier.  (__syncthreads() also waits for every
+// outstanding global load, which would drain loads issued ahead.)  The asm is
+// a compiler memory barrier, so no LDS access moves across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Two fp32 -> packed bf16x2 (round to nearest even; low half = a).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   f32x2_t v = {a, b};

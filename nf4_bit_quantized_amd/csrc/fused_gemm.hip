@@ -50,11 +50,6 @@ namespace {
 constexpr int BK = 64;
 constexpr int LDK = BK + 8;  // contraction-contiguous LDS row: 72 bf16 = 144 B
 
-// Workgroup barrier that orders LDS only: waits for this wave's LDS operations,
-// then s_barrier.  (__syncthreads() also waits for every outstanding global
-// load, which would drain the producers' prefetch at each step.)  The asm is a
-// compiler memory barrier, so no LDS access moves across it.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
   return __builtin_amdgcn_perm(hi, lo, sel);
@@ -427,13 +422,13 @@ __device__ __forceinline__ void fused_body(const FusedParams& P) {
     lds_barrier();
   } else {
     Cursor cur = make_cursor<BN, BT>(P, m0, n0);
-    // Workgroups that run together on one XCD would otherwise walk the
-    // contraction in lockstep, all reading the same column block of every
-    // operand row at once (rows are a power-of-two apart, so those requests
-    // pile onto few L2 channels).  Each tile starts at its own step instead;
-    // the sum order per tile is fixed, so results stay deterministic.
+    // Tiles of one tile row share their A rows and walk the contraction in
+    // lockstep, so those rows are read once into L2 and hit there.  Different
+    // tile rows start at different steps: rows a power of two apart would
+    // otherwise send the same column block of every row to few L2 channels
+    // at once.  The sum order per tile is fixed, so results stay deterministic.
     cur.nk = nk;
-    cur.rot = (uint32_t)((order * 5) % nk);
+    cur.rot = (uint32_t)((tm * 5) % nk);
     // three register sets: set i%3 holds step i; at half-step h the producers
     // issue the loads of step h+3 into the set freed by step h, then restore
     // step h+1 into LDS stage (h+1)%2, so every load has two steps in flight.

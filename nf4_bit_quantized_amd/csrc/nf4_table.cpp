@@ -19,6 +19,7 @@
 // float32 input.
 #include <algorithm>
 #include <cmath>
+#include <cstring>
 #include <vector>
 
 #include "common.hpp"
@@ -68,11 +69,57 @@ Nf4Table build_table() {
   return t;
 }
 
+// Bucket tables of the quantization kernel (layout and use: QuantLut).
+QuantLut build_lut(const Nf4Table& t, bool* ok) {
+  QuantLut L{};
+  *ok = true;
+  auto bf16_value = [](uint32_t hi16) {
+    const uint32_t bits = hi16 << 16;
+    float f;
+    std::memcpy(&f, &bits, 4);
+    return (double)f;
+  };
+  const double widen = std::ldexp(1.0, -19), floor_abs = std::ldexp(1.0, -140);
+  for (int sign = 0; sign < 2; ++sign) {
+    for (int idx = 0; idx < kLutSide; ++idx) {
+      double mlo, mhi;
+      if (idx == 0) {
+        mlo = 0.0;
+        mhi = std::ldexp(1.0, -6);
+      } else {
+        mlo = bf16_value(0x3C7Fu + (uint32_t)idx);
+        mhi = bf16_value(0x3C7Fu + (uint32_t)idx + 1);
+      }
+      double lo = sign ? -mhi : mlo, hi = sign ? -mlo : mhi;
+      lo -= std::fabs(lo) * widen + floor_abs;
+      hi += std::fabs(hi) * widen + floor_abs;
+      int below = 0, inside = 0;
+      for (int k = 0; k < 15; ++k) {
+        if ((double)t.thr[k] < lo) ++below;
+        else if ((double)t.thr[k] <= hi) ++inside;
+      }
+      if (inside > 1) *ok = false;
+      L.kidx[sign * kLutSide + idx] = (uint8_t)below;
+    }
+  }
+  for (int k = 0; k < 15; ++k)
+    L.mid[k] = ((double)t.thr[k] + (double)std::nextafter(t.thr[k], INFINITY)) * 0.5;  // exact
+  L.mid[15] = INFINITY;
+  return L;
+}
+
 }  // namespace
 
 const Nf4Table& nf4_table() {
   static const Nf4Table table = build_table();
   return table;
+}
+
+const QuantLut& quant_lut(bool* ok) {
+  static bool good = false;
+  static const QuantLut lut = build_lut(nf4_table(), &good);
+  *ok = good;
+  return lut;
 }
 
 }  // namespace qlora

@@ -13,21 +13,49 @@
 // 256 threads; thread t loads float4 number i*256 + t (i = 0..15) of the
 // group, so each load instruction is a fully coalesced 4 KiB row; a float4
 // belongs to block i*16 + t/16, shared by 16 consecutive lanes, whose absmax
-// is reduced with four xor-shuffles inside those 16 lanes.  Results are
-// bit-exact: IEEE division for x = w / s and for s / c_g, comparisons against
-// exact thresholds, rint for the codes.  No floating-point contraction.
+// is reduced with four xor-shuffles inside those 16 lanes.  All sixteen loads
+// are issued first; float4 i is quantized and stored as soon as it arrives,
+// so the arithmetic of early rows overlaps the loads of later ones.
+//
+// The index of x = fl32(w / s) is found without the division: a bucket of
+// the estimate w * rcp(s) names the one threshold that can matter, and that
+// comparison is made exactly in double precision (QuantLut in common.hpp).
+// Weights whose block scale is below 2^-64 or above 2^64 are first scaled by
+// 2^64 or 2^-64 (exact for every value that can reach a threshold), so the
+// reciprocal stays a normal float.  Results are bit-exact: the scale codes use
+// IEEE division for s / c_g and rint.  No floating-point contraction.
 #pragma clang fp contract(off)
+
+#include <type_traits>
 
 #include "common.hpp"
 #include "trace.hpp"
 
 namespace qlora {
 
+// Max over the 16 lanes of a DPP row, left in every lane: swap neighbours,
+// swap pairs, mirror the half-rows, mirror the row.
+__device__ __forceinline__ float row_max16(float m) {
+  auto dpp = [](float v, auto ctrl) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), decltype(ctrl)::value,
+                                                              0xF, 0xF, false));
+  };
+  m = fmaxf(m, dpp(m, std::integral_constant<int, 0xB1>{}));   // quad_perm [1,0,3,2]
+  m = fmaxf(m, dpp(m, std::integral_constant<int, 0x4E>{}));   // quad_perm [2,3,0,1]
+  m = fmaxf(m, dpp(m, std::integral_constant<int, 0x141>{}));  // row_half_mirror
+  m = fmaxf(m, dpp(m, std::integral_constant<int, 0x140>{}));  // row_mirror
+  return m;
+}
+
 __global__ __launch_bounds__(256) void k_nf4_quantize(const float* __restrict__ W,
                                                       uint8_t* __restrict__ packed,
                                                       uint8_t* __restrict__ codes,
                                                       float* __restrict__ consts, int64_t nb,
-                                                      Nf4Table tab) {
+                                                      QuantLut lut) {
+  constexpr int kLutWords = (2 * kLutSide + 4) / 4;
+  static_assert(kLutWords <= 512, "two words per thread");
+  __shared__ uint32_t sh_lut[512];
+  __shared__ double sh_mid[16];
   __shared__ float sh_scale[256];
   __shared__ float sh_wmax[4];
 
@@ -36,32 +64,57 @@ __global__ __launch_bounds__(256) void k_nf4_quantize(const float* __restrict__ 
   const int64_t blk0 = g * 256;
   const int nblk = (int)((nb - blk0) < 256 ? (nb - blk0) : 256);
   typedef float f4_t __attribute__((ext_vector_type(4)));
-  const f4_t* src = reinterpret_cast<const f4_t*>(W) + blk0 * 16;
 
+  // decision tables: read before the weights, written to LDS after them
+  const uint32_t* lw = reinterpret_cast<const uint32_t*>(lut.kidx);
+  const uint32_t lut_a = lw[t];
+  const uint32_t lut_b = lw[t + 256 < kLutWords ? t + 256 : kLutWords - 1];
+  const double mid = lut.mid[t & 15];
+
+  // the group's weights through a buffer resource sized to its blocks, so the
+  // float4s of a ragged last group past the end read as zero
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(W) + blk0 * 64, (short)0, nblk * 256, 0x00020000);
   f4_t v[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int b = i * 16 + (t >> 4);
-    if (b < nblk) {
-      v[i] = __builtin_nontemporal_load(src + i * 256 + t);
-    } else {
-      v[i] = f4_t{0.f, 0.f, 0.f, 0.f};
-    }
-  }
+  for (int i = 0; i < 16; ++i)
+    v[i] = __builtin_bit_cast(f4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (i * 256 + t) * 16, 0, 0));
+  sh_lut[t] = lut_a;
+  sh_lut[t + 256] = lut_b;
+  sh_mid[t & 15] = mid;   // 16 threads write each entry, all the same value
+  lds_barrier();
+  const uint8_t* kidx = reinterpret_cast<const uint8_t*>(sh_lut);
 
-  // absmax of each block: 4 values per lane, then 16 lanes
-  float s[16];
+  // per float4: block absmax (4 values per lane, then 16 lanes), indices,
+  // two packed bytes stored as one uint16 (element 2j in the high nibble)
+  uint16_t* dst = reinterpret_cast<uint16_t*>(packed) + blk0 * 16;
   float tmax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
+    const int b = i * 16 + (t >> 4);
     float m = fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w)));
-    m = fmaxf(m, __shfl_xor(m, 8, 16));
-    m = fmaxf(m, __shfl_xor(m, 4, 16));
-    m = fmaxf(m, __shfl_xor(m, 2, 16));
-    m = fmaxf(m, __shfl_xor(m, 1, 16));
-    s[i] = m;
+    m = row_max16(m);
     tmax = fmaxf(tmax, m);
-    if ((t & 15) == 0) sh_scale[i * 16 + (t >> 4)] = m;
+    if ((t & 15) == 0) sh_scale[b] = m;
+
+    const float pre = m < 0x1p-64f ? 0x1p64f : (m > 0x1p64f ? 0x1p-64f : 1.0f);
+    const float rs = m > 0.0f ? __builtin_amdgcn_rcpf(m * pre) : 0.0f;
+    const double sd = (double)m;
+    const float x[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+    uint32_t q[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float ya = (x[e] * pre) * rs;
+      const uint32_t bits = __builtin_bit_cast(uint32_t, ya);
+      int key = (int)((bits >> 16) & 0x7FFFu) - 0x3C7F;
+      key = key < 0 ? 0 : (key > kLutSide - 1 ? kLutSide - 1 : key);
+      key += (int)(bits >> 31) * kLutSide;
+      const uint32_t k = kidx[key];
+      q[e] = k + ((double)x[e] > sd * sh_mid[k] ? 1u : 0u);
+    }
+    const uint32_t b0 = (q[0] << 4) | q[1];
+    const uint32_t b1 = (q[2] << 4) | q[3];
+    if (b < nblk) dst[i * 256 + t] = (uint16_t)(b0 | (b1 << 8));
   }
 
   // group constant c_g = max block scale (all 256 blocks of the group)
@@ -83,38 +136,18 @@ __global__ __launch_bounds__(256) void k_nf4_quantize(const float* __restrict__ 
     codes[blk0 + t] = (uint8_t)code;
   }
   if (t == 0) consts[g] = cg;
-
-  // indices: x = w / s, q = #{k : x > thr[k]}; two nibbles per byte, element
-  // 2j in the high nibble; a float4 yields two bytes stored as one uint16.
-  uint16_t* dst = reinterpret_cast<uint16_t*>(packed) + blk0 * 16;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int b = i * 16 + (t >> 4);
-    if (b >= nblk) continue;
-    const float sb = s[i];
-    float x[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-    uint32_t q[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float xn = sb > 0.0f ? x[e] / sb : 0.0f;
-      uint32_t c = 0;
-#pragma unroll
-      for (int k = 0; k < 15; ++k) c += (xn > tab.thr[k]) ? 1u : 0u;
-      q[e] = c;
-    }
-    const uint32_t b0 = (q[0] << 4) | q[1];
-    const uint32_t b1 = (q[2] << 4) | q[3];
-    dst[i * 256 + t] = (uint16_t)(b0 | (b1 << 8));
-  }
 }
 
 hipError_t launch_nf4_quantize(const float* W, uint8_t* packed, uint8_t* codes, float* consts,
                                int64_t numel, hipStream_t stream) {
+  bool ok = false;
+  const QuantLut& lut = quant_lut(&ok);
+  if (!ok) return hipErrorInvalidValue;
   const int64_t nb = numel / 64;
   const int64_t ng = (nb + 255) / 256;
   TraceScope ts(KID_QUANTIZE, stream);
   hipLaunchKernelGGL(k_nf4_quantize, dim3((unsigned)ng), dim3(256), 0, stream, W, packed, codes,
-                     consts, nb, nf4_table());
+                     consts, nb, lut);
   return hipGetLastError();
 }
 

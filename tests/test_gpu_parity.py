@@ -66,6 +66,74 @@ def test_quantize_threshold_sweep_bit_exact():
                             "consts_h": consts.cpu().numpy()}, Q)
 
 
+def _sweep_blocks(scale, thr, per=63, width=40):
+    """Blocks whose absmax is exactly +-scale, holding the float32 neighbours of
+    thr[k] * scale for every threshold k (so that fl32(w / scale) walks across
+    each decision point)."""
+    scale = np.float32(scale)
+    vals = []
+    for k in range(15):
+        c = np.float32(np.float64(thr[k]) * np.float64(scale))
+        vals.append(c)
+        for d in (np.float32(np.inf), np.float32(-np.inf)):
+            v = c
+            for _ in range(width):
+                v = np.nextafter(v, d, dtype=np.float32)
+                vals.append(v)
+    vals = np.array(vals, np.float32)
+    vals = vals[np.abs(vals) <= scale]
+    nblk = -(-vals.size // per)
+    W = np.zeros((nblk, 64), np.float32)
+    for b in range(nblk):
+        chunk = vals[b * per:(b + 1) * per]
+        W[b, 0] = scale if b % 2 == 0 else -scale
+        W[b, 1:1 + chunk.size] = chunk
+    return W.reshape(-1)
+
+
+@pytest.mark.parametrize("scales", [
+    (0.0123, 0.3, 7.25, 1.0e-3, 2.0 ** -20),
+    (1.0e-20, 3.0e-30, 1.0e-38, 1.0e-39, 5.0e-42),     # tiny, down to subnormal block scales
+    (1.0e20, 3.0e30, 1.0e38, 3.3e38),                   # huge block scales
+])
+def test_quantize_threshold_sweep_scaled_bit_exact(scales):
+    """The threshold sweep at block scales other than 1, across the float32
+    range (subnormal to near the largest finite), with random mantissas."""
+    import nf4_bit_quantized_amd as q
+    import torch
+    _, thr = q.qlora_nf4_levels()
+    parts = [_sweep_blocks(sc, thr) for sc in scales]
+    W = np.concatenate(parts)
+    pad = (-W.size) % (64 * 64)
+    W = np.concatenate([W, np.zeros(pad, np.float32)]).reshape(64, -1)
+    say(f"scaled threshold sweep {scales} W {W.shape}")
+    Q = onf4.quantize(W)
+    packed, codes, consts = q.qlora_quantize_nf4(dev_f32(W))
+    torch.cuda.synchronize()
+    assert_quant_bit_exact({"packed_h": packed.cpu().numpy(), "codes_h": codes.cpu().numpy(),
+                            "consts_h": consts.cpu().numpy()}, Q)
+
+
+def test_quantize_random_magnitudes_bit_exact():
+    """Normal weights with each block scaled by 10^u, u uniform in [-44, 38]:
+    block scales from subnormal to near the largest float32, mixed in groups."""
+    import nf4_bit_quantized_amd as q
+    import torch
+    rng = np.random.default_rng(11)
+    nblk = 64 * 64 * 4
+    W = rng.standard_normal((nblk, 64)).astype(np.float32)
+    mag = np.power(10.0, rng.uniform(-44.0, 38.0, size=(nblk, 1)))
+    W = (W.astype(np.float64) * mag / 4.0).astype(np.float32)
+    W = W.reshape(256, -1)
+    assert np.all(np.isfinite(W))
+    say(f"random magnitudes W {W.shape}")
+    Q = onf4.quantize(W)
+    packed, codes, consts = q.qlora_quantize_nf4(dev_f32(W))
+    torch.cuda.synchronize()
+    assert_quant_bit_exact({"packed_h": packed.cpu().numpy(), "codes_h": codes.cpu().numpy(),
+                            "consts_h": consts.cpu().numpy()}, Q)
+
+
 def test_quantize_deterministic():
     import nf4_bit_quantized_amd as q
     import torch
