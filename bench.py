@@ -29,6 +29,36 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 
+# HBM bytes per launch of the two large kernels on the attention-shaped step,
+# from two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE,
+# KiB per dispatch, averaged over the dispatches of each kernel), scaled by
+# what the same counters read for a plain 256 MiB fill and copy in the same
+# runs (--copy-calibration 256): the copy's FETCH_SIZE reads 131087.1 KiB for
+# 262144 KiB moved (scale 1.99977), the fill's WRITE_SIZE reads exactly
+# 262144 KiB (scale 1).  Valid only for the kernel sources they were taken
+# on (sha256 of the files below); reported as null once those change.
+TRAFFIC_SOURCES = ("fused_gemm.hip", "fused.hpp", "common.hpp")
+TRAFFIC = {
+    "sha256": "58b6e97966b4b7a47b71986af4b00aaa10e04428de53960fa43ec0ee896e73de",
+    "fetch_scale": 262144.0 / 131087.1,
+    "write_scale": 1.0,
+    "fwd_gemm": {"fetch_kib": 36021.1, "write_kib": 24576.0},
+    "dx_gemm": {"fetch_kib": 35846.9, "write_kib": 16384.0},
+}
+
+
+def traffic_bytes(kernel):
+    """Measured HBM bytes per launch of `kernel`, or None if its sources changed."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, "nf4_bit_quantized_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != TRAFFIC["sha256"] or kernel not in TRAFFIC:
+        return None
+    t = TRAFFIC[kernel]
+    return int(round((t["fetch_kib"] * TRAFFIC["fetch_scale"] + t["write_kib"] * TRAFFIC["write_scale"]) * 1024))
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -232,7 +262,7 @@ def main():
     dom_avg_s = dms / dn * 1e-3
     achieved = kernel_flops[dom] / dom_avg_s / 1e12
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": traffic_bytes(dom),
                 "avg_launch_us": round(dom_avg_s * 1e6, 2), "flops_per_launch": kernel_flops[dom]}
     qn, qms = kt_all.get("nf4_quantize", (1, float("nan")))
     q_bytes = N * K * 4 + N * K // 2 + n_c + n_k
