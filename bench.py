@@ -153,7 +153,7 @@ def decode_section(steps, warmup):
                 q.qlora_linear_fwd(p[0], p[1], p[2], X, A, B, lin.alpha, Y=Y, U_out=U, workspace=ws)
             torch.cuda.synchronize()
             q.qlora_trace_read(reset=True)
-            q.qlora_trace_select({"decode_partial"})
+            q.qlora_trace_select({"decode"})
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             for i in range(steps):
@@ -165,7 +165,7 @@ def decode_section(steps, warmup):
             kt = q.qlora_trace_read(reset=True)
             call_ms = e0.elapsed_time(e1) / steps
             packed_bytes = pk.numel() + cd.numel() + cs.numel() * 4
-            dec_n, dec_ms = kt.get("decode_partial", (1, float("nan")))
+            dec_n, dec_ms = kt.get("decode", (1, float("nan")))
             dec_avg = dec_ms / max(dec_n, 1)
             out[lin.name] = {
                 "T": T, "d_out": lin.d_out, "d_in": lin.d_in,

@@ -13,10 +13,10 @@
 namespace qlora {
 hipError_t launch_nf4_quantize(const float* W, uint8_t* packed, uint8_t* codes, float* consts,
                                int64_t numel, hipStream_t stream);
-hipError_t launch_decode(const uint8_t* packed, const uint8_t* codes, const float* consts,
-                         const uint16_t* X, int64_t T, int64_t N, int64_t K, int64_t kchunk,
-                         int nsplit, float* Ppart, const float* U, int r, float s,
-                         const uint16_t* B, uint16_t* Y, hipStream_t stream);
+int decode_splits(int64_t N, int64_t K);
+hipError_t launch_decode(const uint8_t* packed, const uint8_t* codes, const float* consts, const uint16_t* X,
+                         int64_t T, int64_t N, int64_t K, const uint16_t* Us, int64_t ldh, const uint16_t* B,
+                         int r, int nsplit, float* part, uint16_t* Y, hipStream_t stream);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
 }  // namespace qlora
 
@@ -26,7 +26,6 @@ namespace {
 
 constexpr int64_t kDecodeMaxT = 16;
 constexpr int kMaxRank = 128;
-constexpr int kTargetWorkgroups = 1024;
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -44,22 +43,6 @@ int check_layer(const qlora_nf4_desc* d, int64_t T, int32_t r) {
   if (st) return st;
   if (T < 0 || r < 0 || r > kMaxRank) return QLORA_ERR_SHAPE;
   return QLORA_OK;
-}
-
-struct DecodePlan {
-  int nsplit;
-  int64_t kchunk;
-};
-
-DecodePlan plan_decode(int64_t N, int64_t K) {
-  const int64_t groups = cdiv(N, 128);
-  int64_t ns = cdiv(kTargetWorkgroups, groups);
-  if (ns > K / 64) ns = K / 64;
-  if (ns < 1) ns = 1;
-  DecodePlan p;
-  p.kchunk = cdiv(cdiv(K, ns), 64) * 64;
-  p.nsplit = (int)cdiv(K, p.kchunk);
-  return p;
 }
 
 int64_t hilo_ld(int32_t r) { return cdiv(2 * (int64_t)r, 64) * 64; }
@@ -83,7 +66,7 @@ size_t skinny_part_bytes(int64_t mrows, int64_t clen, int64_t cols) {
 }
 
 struct FwdWs {
-  DecodePlan dp;
+  int nsplit = 1;  // contraction slices of the few-token kernel
   float* part = nullptr;
   float* U = nullptr;
   uint16_t* Us = nullptr;
@@ -101,8 +84,8 @@ FwdWs plan_fwd(const qlora_nf4_desc* d, int64_t T, int32_t r, void* ws) {
     w.Us = static_cast<uint16_t*>(c.take((size_t)T * hilo_ld(r) * 2));
   }
   if (T > 0 && T <= kDecodeMaxT) {
-    w.dp = plan_decode(N, K);
-    w.dec = static_cast<float*>(c.take((size_t)w.dp.nsplit * T * N * 4));
+    w.nsplit = decode_splits(N, K);
+    if (w.nsplit > 1) w.dec = static_cast<float*>(c.take((size_t)w.nsplit * T * N * 4));
   }
   w.bytes = c.off;
   return w;
@@ -253,8 +236,7 @@ int qlora_linear_fwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8
     if (e) return e;
   }
   if (T <= kDecodeMaxT) {
-    HIP_TRY(launch_decode(packed, codes, consts, X, T, N, K, w.dp.kchunk, w.dp.nsplit, w.dec, U, r, s,
-                          B, Y, s_));
+    HIP_TRY(launch_decode(packed, codes, consts, X, T, N, K, w.Us, hilo_ld(r), B, r, w.nsplit, w.dec, Y, s_));
     return QLORA_OK;
   }
   FusedParams fp{};

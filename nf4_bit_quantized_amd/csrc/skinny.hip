@@ -205,33 +205,36 @@ __global__ __launch_bounds__(256) void k_skinny(SkinnyParams S) {
     for (int j = 0; j < JT; ++j) acc[a][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // contraction chunks of this workgroup: split z of S.nsplit; wave w takes
-  // chunks cb + w, cb + w + 4, ... (at most NCH), all loaded before any is used
+  // chunks cb + w, cb + w + 4, ...
   const int64_t nchunks = (S.clen + CH - 1) / CH;
   const int64_t per = (nchunks + S.nsplit - 1) / S.nsplit;
   const int64_t cb = (int64_t)z * per;
   const int64_t ce = cb + per < nchunks ? cb + per : nchunks;
-  ChunkRegs<J> R[NCH];
+  // rounds of WAVES * NCH chunks: every chunk of a round is loaded before any is used
+  for (int64_t base = cb; base < ce; base += (int64_t)WAVES * NCH) {
+    ChunkRegs<J> R[NCH];
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const int64_t ch = cb + wave + (int64_t)WAVES * i;
-    if (ch < ce) load_chunk<J, P_CONTIG, Q_MODE>(R[i], S, m0, ch * CH);
-  }
-#pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const int64_t ch = cb + wave + (int64_t)WAVES * i;
-    if (ch >= ce) break;
-    stage_chunk<J, P_CONTIG, Q_MODE>(R[i], S, Ps, Qs);
-    wave_lds_sync();
-    bf16x8_t pa[2];
-#pragma unroll
-    for (int a = 0; a < 2; ++a) pa[a] = frag<MT, P_CONTIG>(Ps, 16 * a);
-#pragma unroll
-    for (int j = 0; j < JT; ++j) {
-      const bf16x8_t qb = frag<J, Q_MODE == Q_CONTIG>(Qs, 16 * j);
-#pragma unroll
-      for (int a = 0; a < 2; ++a) acc[a][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[a], qb, acc[a][j], 0, 0, 0);
+    for (int i = 0; i < NCH; ++i) {
+      const int64_t ch = base + wave + (int64_t)WAVES * i;
+      if (ch < ce) load_chunk<J, P_CONTIG, Q_MODE>(R[i], S, m0, ch * CH);
     }
-    wave_lds_sync();  // fragments read before the slice is overwritten
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int64_t ch = base + wave + (int64_t)WAVES * i;
+      if (ch >= ce) break;
+      stage_chunk<J, P_CONTIG, Q_MODE>(R[i], S, Ps, Qs);
+      wave_lds_sync();
+      bf16x8_t pa[2];
+#pragma unroll
+      for (int a = 0; a < 2; ++a) pa[a] = frag<MT, P_CONTIG>(Ps, 16 * a);
+#pragma unroll
+      for (int j = 0; j < JT; ++j) {
+        const bf16x8_t qb = frag<J, Q_MODE == Q_CONTIG>(Qs, 16 * j);
+#pragma unroll
+        for (int a = 0; a < 2; ++a) acc[a][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[a], qb, acc[a][j], 0, 0, 0);
+      }
+      wave_lds_sync();  // fragments read before the slice is overwritten
+    }
   }
 
   // add the four waves' tiles: C[m][j] in fp32, [MT][J]
@@ -337,14 +340,15 @@ void launch_pq(const SkinnyParams& S, int J, dim3 grid, hipStream_t stream) {
 int skinny_width(int cols) { return cols <= 32 ? 32 : cols <= 64 ? 64 : cols <= 128 ? 128 : 256; }
 
 int skinny_splits(int64_t mrows, int64_t clen, int cols) {
-  const int J = skinny_width(cols);
-  const int64_t nch = chunks_per_wave(J);
+  (void)cols;
   const int64_t tiles = (mrows + MT - 1) / MT;
   const int64_t chunks = (clen + CH - 1) / CH;
-  int64_t ns = (chunks + WAVES * nch - 1) / (WAVES * nch);     // every chunk loaded up front
-  const int64_t want = (512 + tiles - 1) / tiles;               // and enough workgroups in flight
-  const int64_t cap = (chunks + WAVES - 1) / WAVES;             // at least one chunk per wave
-  if (ns < want) ns = want < cap ? want : cap;
+  // about 512 workgroups in flight, at least one chunk per wave, and at most
+  // 32 partials per output (they are summed by one thread each)
+  int64_t ns = (512 + tiles - 1) / tiles;
+  int64_t cap = (chunks + WAVES - 1) / WAVES;
+  if (cap > 32) cap = 32;
+  if (ns > cap) ns = cap;
   return (int)(ns < 1 ? 1 : ns);
 }
 

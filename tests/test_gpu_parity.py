@@ -160,6 +160,9 @@ CASES = [
     (256, 384, 150, 64, 16.0, 5),
     (448, 256, 64, 128, 64.0, 6),
     (256, 256, 40, 0, 0.0, 7),        # base branch only
+    (256, 512, 7, 16, 32.0, 8),       # few-token path, 5..8 tokens
+    (128, 448, 12, 8, 16.0, 9),       # few-token path, code runs not 4-byte aligned (K/64 = 7)
+    (192, 1024, 16, 64, 16.0, 10),    # few-token path, two stages per contraction slice
 ]
 
 
@@ -299,7 +302,10 @@ def test_zero_tokens_is_a_no_op():
 def test_restore_is_bit_exact_through_identity():
     """With X = I (forward, r = 0) every output is one restored weight, so Y
     must equal W_hat^T bit for bit; with dY = I the same holds for dX = W_hat.
-    Covers the tiled forward, the transposed-restore dX and the few-token path."""
+    Covers the tiled forward and the transposed-restore dX.  The few-token
+    path applies the block scale to the product of bf16(T[q]) instead of
+    rounding T[q] * s' to bf16 first, so there each restored weight must lie
+    within two bf16 rounding steps (relative 2^-7) of W_hat, zeros exact."""
     import nf4_bit_quantized_amd as q
     import torch
     d_out, d_in = 320, 256
@@ -315,4 +321,72 @@ def test_restore_is_bit_exact_through_identity():
     torch.cuda.synchronize()
     np.testing.assert_array_equal(Y.float().cpu().numpy(), W_hat.T)
     np.testing.assert_array_equal(dX.float().cpu().numpy(), W_hat)
-    np.testing.assert_array_equal(Y16.float().cpu().numpy(), W_hat.T[:16])
+    got16, ref16 = Y16.float().cpu().numpy(), W_hat.T[:16]
+    assert np.all(np.abs(got16 - ref16) <= np.float32(2.0 ** -7) * np.abs(ref16))
+
+
+# --------------------------------------------------------------------------
+# Full-size decode shapes: 8192 <-> 28672, T in {1, 4, 16}, r = 64, alpha = 16
+# --------------------------------------------------------------------------
+
+def _oracle_rows(W, rows, K):
+    """Restored rows of W (float64) and their packed bytes, codes and group
+    constants, from the oracle quantizing only the 256-block groups that cover
+    each row (groups start at multiples of 16384 weights, so they match the
+    full-tensor quantization exactly)."""
+    out = {}
+    flat = W.reshape(-1)
+    for n in rows:
+        a, b = n * K, (n + 1) * K
+        g0, g1 = a // 16384, -(-b // 16384)
+        seg = flat[g0 * 16384: min(g1 * 16384, flat.size)]
+        Q = onf4.quantize(seg.reshape(1, -1))
+        Wh = onf4.dequantize(Q).reshape(-1)
+        lo = a - g0 * 16384
+        out[n] = {
+            "w": Wh[lo: lo + K].astype(np.float64),
+            "packed": Q.packed.reshape(-1)[lo // 2: (lo + K) // 2],
+            "codes": Q.codes[lo // 64: (lo + K) // 64],
+            "consts": (g0, Q.consts),
+        }
+    return out
+
+
+@pytest.mark.parametrize("d_out,d_in", [(28672, 8192), (8192, 28672)])
+def test_decode_full_size_sampled(d_out, d_in):
+    """The few-token forward at the decode shapes, T = 1, 4, 16: sampled output
+    columns against the oracle (normwise 2e-2), and the sampled rows' packed
+    bytes, codes and group constants bit-exact."""
+    import nf4_bit_quantized_amd as q
+    import torch
+    from oracle.bf16 import bits_to_float
+    r, alpha = 64, 16.0
+    say(f"decode full size {d_out}x{d_in}: drawing inputs")
+    inp = workloads.layer_inputs(d_out, d_in, 16, r, seed=3, with_dy=False)
+    rng = np.random.default_rng(7)
+    rows = sorted(rng.choice(d_out, size=48, replace=False).tolist())
+    ref = _oracle_rows(inp["W"], rows, d_in)
+    packed, codes, consts = q.qlora_quantize_nf4(dev_f32(inp["W"]))
+    pk = packed.view(-1)
+    cd = codes.view(-1)
+    for n in rows:
+        assert np.array_equal(pk[n * d_in // 2:(n + 1) * d_in // 2].cpu().numpy(), ref[n]["packed"]), n
+        assert np.array_equal(cd[n * d_in // 64:(n + 1) * d_in // 64].cpu().numpy(), ref[n]["codes"]), n
+        g0, cs = ref[n]["consts"]
+        assert np.array_equal(consts[g0:g0 + cs.size].cpu().numpy().view(np.uint32), cs.view(np.uint32)), n
+    X = bits_to_float(inp["X"]).astype(np.float64)
+    A = bits_to_float(inp["A"]).astype(np.float64)
+    B = bits_to_float(inp["B"]).astype(np.float64)
+    s = float(np.float32(alpha / r))
+    Wrows = np.stack([ref[n]["w"] for n in rows])                      # [rows][K]
+    for T in (1, 4, 16):
+        say(f"  T={T}")
+        Xg = dev_bf16(inp["X"][:T])
+        Y, _ = q.qlora_linear_fwd(packed, codes, consts, Xg, dev_bf16(inp["A"]), dev_bf16(inp["B"]), alpha)
+        torch.cuda.synchronize()
+        got = Y.float().cpu().numpy()[:, rows].astype(np.float64)
+        U = X[:T] @ A.T
+        want = X[:T] @ Wrows.T + s * (U @ B[rows].T)
+        err = np.max(np.abs(got - want)) / np.max(np.abs(want))
+        say(f"    normwise error {err:.2e}")
+        assert err <= TOL, (T, err)
