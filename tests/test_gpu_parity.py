@@ -390,3 +390,73 @@ def test_decode_full_size_sampled(d_out, d_in):
         err = np.max(np.abs(got - want)) / np.max(np.abs(want))
         say(f"    normwise error {err:.2e}")
         assert err <= TOL, (T, err)
+
+
+# --------------------------------------------------------------------------
+# Full-size training shapes: the MLP set (4096 <-> 11008) and the 65B-class
+# projections (8192 x 8192, 8192 <-> 22016), 4096 tokens, r = 64, alpha = 16
+# --------------------------------------------------------------------------
+
+def _restore_subset(Q, rows=None, cols=None):
+    """Oracle restored weight (float64) for whole rows or whole columns, with
+    the same arithmetic as oracle.nf4.dequantize: bf16(fl32(T[q] * s'))."""
+    from oracle.bf16 import round_to_bf16
+    N, K = Q.shape
+    levels = onf4.nf4_levels()
+    q = Q.q.reshape(N, K)
+    s = onf4.restored_scales(Q).reshape(N, K // 64)
+    if rows is not None:
+        qq, ss = q[rows], np.repeat(s[rows], 64, axis=1)
+    else:
+        qq, ss = q[:, cols], s[:, np.asarray(cols) // 64]
+    return round_to_bf16((levels[qq] * ss).astype(np.float32)).astype(np.float64)
+
+
+@pytest.mark.parametrize("d_out,d_in", [(11008, 4096), (4096, 11008), (8192, 8192), (22016, 8192), (8192, 22016)])
+def test_training_shapes_full_size_sampled(d_out, d_in):
+    """Quantize bit-exact over the whole weight; forward and backward at the
+    full size with sampled outputs against the oracle: Y and dB on 32 sampled
+    output rows, dX and dA on 32 sampled input columns (normwise 2e-2)."""
+    import nf4_bit_quantized_amd as q
+    import torch
+    from oracle.bf16 import bits_to_float
+    T, r, alpha = 4096, 64, 16.0
+    say(f"training shape {d_out}x{d_in}, T={T}: drawing inputs")
+    inp = workloads.layer_inputs(d_out, d_in, T, r, seed=100 + d_out % 97)
+    Q = onf4.quantize(inp["W"])
+    packed, codes, consts = q.qlora_quantize_nf4(dev_f32(inp["W"]))
+    torch.cuda.synchronize()
+    assert_quant_bit_exact({"packed_h": packed.cpu().numpy(), "codes_h": codes.cpu().numpy(),
+                            "consts_h": consts.cpu().numpy()}, Q)
+    say("  quantize bit-exact")
+    Xg, Ag, Bg, dYg = (dev_bf16(inp[k]) for k in ("X", "A", "B", "dY"))
+    Y, U = q.qlora_linear_fwd(packed, codes, consts, Xg, Ag, Bg, alpha)
+    dX, dA, dB = q.qlora_linear_bwd(packed, codes, consts, Xg, Ag, Bg, alpha, dYg, U_in=U)
+    torch.cuda.synchronize()
+
+    rng = np.random.default_rng(d_out * 7 + d_in)
+    rows = np.sort(rng.choice(d_out, size=32, replace=False))
+    cols = np.sort(rng.choice(d_in, size=32, replace=False))
+    X, A, B, dY = (bits_to_float(inp[k]) for k in ("X", "A", "B", "dY"))
+    s = float(np.float32(alpha / r))
+    Uo = X @ A.T                                   # [T][r]
+    Go = dY @ B                                    # [T][r]
+    W_rows = _restore_subset(Q, rows=rows)         # [32][K]
+    W_cols = _restore_subset(Q, cols=cols)         # [N][32]
+    want = {
+        "Y": X @ W_rows.T + s * (Uo @ B[rows].T),          # Y[:, rows]
+        "dB": s * (dY[:, rows].T @ Uo),                     # dB[rows, :]
+        "dX": dY @ W_cols + s * (Go @ A[:, cols]),           # dX[:, cols]
+        "dA": s * (Go.T @ X[:, cols]),                       # dA[:, cols]
+    }
+    ri, ci = torch.as_tensor(rows, device="cuda"), torch.as_tensor(cols, device="cuda")
+    got = {
+        "Y": Y.index_select(1, ri).float().cpu().numpy().astype(np.float64),
+        "dB": dB.index_select(0, ri).cpu().numpy().astype(np.float64),
+        "dX": dX.index_select(1, ci).float().cpu().numpy().astype(np.float64),
+        "dA": dA.index_select(1, ci).cpu().numpy().astype(np.float64),
+    }
+    errs = {k: float(np.max(np.abs(got[k] - want[k])) / np.max(np.abs(want[k]))) for k in want}
+    say("  errors", {k: f"{v:.2e}" for k, v in errs.items()})
+    for k, v in errs.items():
+        assert v <= TOL, (k, v)
