@@ -92,7 +92,8 @@ FwdWs plan_fwd(const qlora_nf4_desc* d, int64_t T, int32_t r, void* ws) {
 }
 
 struct BwdWs {
-  float* part = nullptr;  // shared by the rank-r products (they run one after another)
+  float* part = nullptr;   // shared by the rank-r products that run one after another
+  float* part2 = nullptr;  // dB's partials (it runs in the same launch as dA)
   float* U = nullptr;
   uint16_t* Us = nullptr;
   uint16_t* Gs = nullptr;
@@ -108,8 +109,8 @@ BwdWs plan_bwd(const qlora_nf4_desc* d, int64_t T, int32_t r, void* ws) {
     size_t part = skinny_part_bytes(T, K, r);
     part = std::max(part, skinny_part_bytes(T, N, r));
     part = std::max(part, skinny_part_bytes(K, T, 2 * (int64_t)r));
-    part = std::max(part, skinny_part_bytes(N, T, 2 * (int64_t)r));
     w.part = static_cast<float*>(c.take(part));
+    w.part2 = static_cast<float*>(c.take(skinny_part_bytes(N, T, 2 * (int64_t)r)));
     w.U = static_cast<float*>(c.take((size_t)T * r * 4));
     w.Us = static_cast<uint16_t*>(c.take((size_t)T * ldh * 2));
     w.Gs = static_cast<uint16_t*>(c.take((size_t)T * ldh * 2));
@@ -277,10 +278,17 @@ int qlora_linear_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8
   const int64_t ldh = hilo_ld(r);
 
   if (r > 0) {
-    // G = dY B -> hi/lo of s*G (feeds the dX tail and dA)
+    // U = X A^T when the forward's U is not given (its hi/lo pair feeds dB)
+    if (!U_in) {
+      const int e = lora_down(X, A, T, K, r, s, w.part, w.U, w.Us, s_);
+      if (e) return e;
+    }
+    // G = dY B -> hi/lo of s*G (feeds the dX tail and dA); the same launch
+    // turns the given U into the hi/lo pair of s*U
     SkinnyParams S = skinny(dY, N, true, T, N, r, s, r, OUT_ROWS_HILO, w.part);
     skinny_q(S, B, r, r, Q_STRIDED);
     S.Hout = w.Gs; S.ldh = ldh;
+    if (U_in) { S.Uc = U_in; S.Ucs = w.Us; }
     HIP_TRY(launch_skinny(S, s_, KID_LORA_G));
   }
   if (dX) {
@@ -294,22 +302,15 @@ int qlora_linear_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8
     HIP_TRY(launch_fused(fp, true, s_, KID_DX_GEMM));
   }
   if (r > 0) {
-    // dA = (s G)^T X over the hi/lo columns, pairs summed: dA [r][d_in]
+    // one launch for both adapter gradients, contractions over the hi/lo columns:
+    // dA = (s G)^T X -> [r][d_in]; dB = dY^T (s U) -> [d_out][r]
     SkinnyParams Sa = skinny(X, K, false, K, T, r, s, 2 * r, OUT_PAIRS_T, w.part);
     skinny_q(Sa, w.Gs, ldh, 2 * (int64_t)r, Q_STRIDED);
     Sa.Fout = dA;
-    HIP_TRY(launch_skinny(Sa, s_, KID_LORA_DA));
-    // dB = dY^T (s U) over the hi/lo columns, pairs summed: dB [d_out][r]
-    SkinnyParams Sb = skinny(dY, N, false, N, T, r, s, 2 * r, OUT_PAIRS, w.part);
-    if (U_in) {
-      Sb.q_mode = Q_HILO; Sb.V = U_in; Sb.ldv = r;
-    } else {
-      const int e = lora_down(X, A, T, K, r, s, w.part, w.U, w.Us, s_);
-      if (e) return e;
-      skinny_q(Sb, w.Us, ldh, 2 * (int64_t)r, Q_STRIDED);
-    }
+    SkinnyParams Sb = skinny(dY, N, false, N, T, r, s, 2 * r, OUT_PAIRS, w.part2);
+    skinny_q(Sb, w.Us, ldh, 2 * (int64_t)r, Q_STRIDED);
     Sb.Fout = dB;
-    HIP_TRY(launch_skinny(Sb, s_, KID_LORA_DB));
+    HIP_TRY(launch_skinny_pair(Sa, Sb, s_, KID_LORA_DA));
   }
   return QLORA_OK;
 }

@@ -23,6 +23,8 @@
 // bf16 hi/lo pair while staging: Qop[j][c] = hi(s V[c][j]) for j < r and
 // lo(s V[c][j-r]) for r <= j < 2r, so the product carries about 16 bits of
 // the fp32 value.
+#include <algorithm>
+
 #include "skinny.hpp"
 #include "trace.hpp"
 
@@ -185,7 +187,9 @@ __device__ __forceinline__ bf16x8_t frag(const uint16_t* __restrict__ t, int row
 
 
 template <int J, bool P_CONTIG, int Q_MODE>
-__global__ __launch_bounds__(256) void k_skinny(SkinnyParams S) {
+__global__ __launch_bounds__(256) void k_skinny(SkinnyBatch SB) {
+  const SkinnyParams& S = SB.p[blockIdx.z];
+  if ((int64_t)blockIdx.x * MT >= S.mrows || (int)blockIdx.y >= S.nsplit) return;
   constexpr int JT = J / 16;
   constexpr int NCH = chunks_per_wave(J);
   using L = Slice<J>;
@@ -282,6 +286,22 @@ __global__ __launch_bounds__(256) void k_skinny(SkinnyParams S) {
       }
     }
   }
+  if (S.Ucs && S.nsplit == 1) {
+    // hi/lo pair of s * Uc for this workgroup's rows, zero-padded to ldh
+    // (with split contractions the sum kernel does this)
+    for (int i = threadIdx.x; i < MT * S.ldh; i += 256) {
+      const int64_t m = m0 + i / S.ldh;
+      const int c = (int)(i % S.ldh);
+      if (m >= S.mrows) continue;
+      uint16_t h = 0;
+      if (c < 2 * S.r) {
+        uint16_t hi, lo;
+        split_bf16(S.s * S.Uc[m * S.r + (c < S.r ? c : c - S.r)], hi, lo);
+        h = c < S.r ? hi : lo;
+      }
+      S.Ucs[m * S.ldh + c] = h;
+    }
+  }
   if (S.out_mode == OUT_ROWS_HILO) {
     // zero the padding columns [2r, ldh) of the hi/lo pair
     const int padw = (int)(S.ldh - 2 * S.r);
@@ -293,9 +313,10 @@ __global__ __launch_bounds__(256) void k_skinny(SkinnyParams S) {
 }
 
 // Fixed-order sum of split partials, then the same outputs as the kernel above.
-__global__ __launch_bounds__(256) void k_skinny_sum(SkinnyParams S) {
+__global__ __launch_bounds__(256) void k_skinny_sum(SkinnyBatch SB) {
+  const SkinnyParams& S = SB.p[blockIdx.z];
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= S.mrows * S.ocols) return;
+  if (S.nsplit == 1 || idx >= S.mrows * S.ocols) return;
   const int64_t m = idx / S.ocols;
   const int col = (int)(idx - m * S.ocols);
   auto part = [&](int c) {
@@ -313,6 +334,15 @@ __global__ __launch_bounds__(256) void k_skinny_sum(SkinnyParams S) {
       S.Hout[m * S.ldh + S.r + col] = lo;
     }
     for (int64_t c = 2 * S.r + col; c < S.ldh; c += S.ocols) S.Hout[m * S.ldh + c] = 0;
+    if (S.Ucs) {
+      if (col < S.r) {
+        uint16_t hi, lo;
+        split_bf16(S.s * S.Uc[m * S.r + col], hi, lo);
+        S.Ucs[m * S.ldh + col] = hi;
+        S.Ucs[m * S.ldh + S.r + col] = lo;
+      }
+      for (int64_t c = 2 * S.r + col; c < S.ldh; c += S.ocols) S.Ucs[m * S.ldh + c] = 0;
+    }
   } else if (col < S.r) {
     const float t = part(col) + part(col + S.r);
     if (S.out_mode == OUT_PAIRS) S.Fout[m * S.r + col] = t;
@@ -321,12 +351,12 @@ __global__ __launch_bounds__(256) void k_skinny_sum(SkinnyParams S) {
 }
 
 template <int J, bool P_CONTIG, int Q_MODE>
-void launch_j(const SkinnyParams& S, dim3 grid, hipStream_t stream) {
+void launch_j(const SkinnyBatch& S, dim3 grid, hipStream_t stream) {
   hipLaunchKernelGGL((k_skinny<J, P_CONTIG, Q_MODE>), grid, dim3(256), 0, stream, S);
 }
 
 template <bool P_CONTIG, int Q_MODE>
-void launch_pq(const SkinnyParams& S, int J, dim3 grid, hipStream_t stream) {
+void launch_pq(const SkinnyBatch& S, int J, dim3 grid, hipStream_t stream) {
   switch (J) {
     case 32: launch_j<32, P_CONTIG, Q_MODE>(S, grid, stream); break;
     case 64: launch_j<64, P_CONTIG, Q_MODE>(S, grid, stream); break;
@@ -352,31 +382,61 @@ int skinny_splits(int64_t mrows, int64_t clen, int cols) {
   return (int)(ns < 1 ? 1 : ns);
 }
 
-hipError_t launch_skinny(SkinnyParams S, hipStream_t stream, int kernel_id) {
-  const int J = skinny_width(S.qcols);
-  const dim3 grid((unsigned)((S.mrows + MT - 1) / MT), (unsigned)S.nsplit);
-  const int final_mode = S.out_mode;
-  if (S.nsplit > 1) S.out_mode = OUT_PARTIAL;
-  S.ocols = S.qcols;
+namespace {
+
+hipError_t launch_batch(SkinnyBatch B, hipStream_t stream, int kernel_id) {
+  const int J = skinny_width(B.p[0].qcols);
+  int64_t tiles = 0, ns = 1, outs = 0;
+  for (int i = 0; i < B.n; ++i) {
+    SkinnyParams& S = B.p[i];
+    S.ocols = S.qcols;
+    tiles = std::max(tiles, (S.mrows + MT - 1) / MT);
+    ns = std::max<int64_t>(ns, S.nsplit);
+    if (S.nsplit > 1) outs = std::max(outs, S.mrows * S.ocols);
+  }
+  // the kernel writes partials whenever it runs split; the sum kernel finishes
+  SkinnyBatch K = B;
+  for (int i = 0; i < B.n; ++i)
+    if (K.p[i].nsplit > 1) K.p[i].out_mode = OUT_PARTIAL;
+  const bool p_contig = B.p[0].p_contig;
+  const int q_mode = B.p[0].q_mode;
   {
     TraceScope ts(kernel_id, stream);
-    if (S.p_contig) {
-      if (S.q_mode == Q_CONTIG) launch_pq<true, Q_CONTIG>(S, J, grid, stream);
-      else if (S.q_mode == Q_STRIDED) launch_pq<true, Q_STRIDED>(S, J, grid, stream);
-      else launch_pq<true, Q_HILO>(S, J, grid, stream);
+    const dim3 grid((unsigned)tiles, (unsigned)ns, (unsigned)B.n);
+    if (p_contig) {
+      if (q_mode == Q_CONTIG) launch_pq<true, Q_CONTIG>(K, J, grid, stream);
+      else if (q_mode == Q_STRIDED) launch_pq<true, Q_STRIDED>(K, J, grid, stream);
+      else launch_pq<true, Q_HILO>(K, J, grid, stream);
     } else {
-      if (S.q_mode == Q_CONTIG) launch_pq<false, Q_CONTIG>(S, J, grid, stream);
-      else if (S.q_mode == Q_STRIDED) launch_pq<false, Q_STRIDED>(S, J, grid, stream);
-      else launch_pq<false, Q_HILO>(S, J, grid, stream);
+      if (q_mode == Q_CONTIG) launch_pq<false, Q_CONTIG>(K, J, grid, stream);
+      else if (q_mode == Q_STRIDED) launch_pq<false, Q_STRIDED>(K, J, grid, stream);
+      else launch_pq<false, Q_HILO>(K, J, grid, stream);
     }
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || S.nsplit == 1) return e;
-  S.out_mode = final_mode;
-  const int64_t n = S.mrows * S.ocols;
+  if (e != hipSuccess || outs == 0) return e;
   TraceScope ts(KID_REDUCE, stream);
-  hipLaunchKernelGGL(k_skinny_sum, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, S);
+  hipLaunchKernelGGL(k_skinny_sum, dim3((unsigned)((outs + 255) / 256), 1, (unsigned)B.n), dim3(256), 0, stream, B);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_skinny(SkinnyParams S, hipStream_t stream, int kernel_id) {
+  SkinnyBatch B{};
+  B.p[0] = S;
+  B.n = 1;
+  return launch_batch(B, stream, kernel_id);
+}
+
+hipError_t launch_skinny_pair(SkinnyParams S0, SkinnyParams S1, hipStream_t stream, int kernel_id) {
+  if (S0.p_contig != S1.p_contig || S0.q_mode != S1.q_mode || skinny_width(S0.qcols) != skinny_width(S1.qcols))
+    return hipErrorInvalidValue;
+  SkinnyBatch B{};
+  B.p[0] = S0;
+  B.p[1] = S1;
+  B.n = 2;
+  return launch_batch(B, stream, kernel_id);
 }
 
 }  // namespace qlora

@@ -43,10 +43,22 @@ struct SkinnyParams {
   uint16_t* Hout;
   int64_t ldh;
   float* Fout;
+  // optional (OUT_ROWS_HILO products of r columns): Ucs[m][..] = hi/lo pair
+  // of s * Uc[m][0..r) for the same rows m, zero-padded to ldh
+  const float* Uc;
+  uint16_t* Ucs;
+};
+
+// Up to two independent products in one launch (blockIdx.z picks one).
+struct SkinnyBatch {
+  SkinnyParams p[2];
+  int n;
 };
 
 int skinny_width(int cols);
 int skinny_splits(int64_t mrows, int64_t clen, int cols);
 hipError_t launch_skinny(SkinnyParams S, hipStream_t stream, int kernel_id);
+// Two products with the same operand modes and width (P strided, Q strided).
+hipError_t launch_skinny_pair(SkinnyParams S0, SkinnyParams S1, hipStream_t stream, int kernel_id);
 
 }  // namespace qlora

@@ -283,6 +283,32 @@ def test_deterministic_fwd_bwd():
         np.testing.assert_array_equal(a[k], b[k])
 
 
+def test_workspace_reuse_across_calls():
+    """One workspace shared by forward and backward calls of several sizes
+    (its contents left over from the previous call) gives the same outputs as
+    a fresh workspace, bit for bit."""
+    import nf4_bit_quantized_amd as q
+    import torch
+    shapes = [(256, 384, 150, 64), (448, 256, 64, 16), (4096, 1024, 600, 16), (256, 256, 16, 8)]
+    size = max(max(q.qlora_fwd_workspace_bytes(n, k, t, r), q.qlora_bwd_workspace_bytes(n, k, t, r))
+               for (n, k, t, r) in shapes)
+    ws = torch.full((size,), 0x5A, dtype=torch.uint8, device="cuda")   # stale contents
+    for rep in range(2):
+        for (n, k, t, r) in shapes:
+            say(f"workspace reuse {n}x{k} T={t} r={r} pass {rep}")
+            inp = workloads.layer_inputs(n, k, t, r, seed=21)
+            packed, codes, consts = q.qlora_quantize_nf4(dev_f32(inp["W"]))
+            X, A, B, dY = (dev_bf16(inp[key]) for key in ("X", "A", "B", "dY"))
+            Y1, U1 = q.qlora_linear_fwd(packed, codes, consts, X, A, B, 16.0, workspace=ws)
+            g1 = q.qlora_linear_bwd(packed, codes, consts, X, A, B, 16.0, dY, U_in=U1, workspace=ws)
+            Y2, U2 = q.qlora_linear_fwd(packed, codes, consts, X, A, B, 16.0)
+            g2 = q.qlora_linear_bwd(packed, codes, consts, X, A, B, 16.0, dY, U_in=U2)
+            torch.cuda.synchronize()
+            assert torch.equal(Y1, Y2) and torch.equal(U1, U2)
+            for a, b in zip(g1, g2):
+                assert torch.equal(a, b)
+
+
 def test_zero_tokens_is_a_no_op():
     import nf4_bit_quantized_amd as q
     import torch
