@@ -58,6 +58,7 @@ __global__ __launch_bounds__(256) void k_nf4_quantize(const float* __restrict__ 
   __shared__ double sh_mid[16];
   __shared__ float sh_scale[256];
   __shared__ float sh_wmax[4];
+  __shared__ __attribute__((aligned(16))) uint16_t sh_packed[16 * 256];  // the group's packed bytes
 
   const int t = threadIdx.x;
   const int64_t g = blockIdx.x;
@@ -86,8 +87,8 @@ __global__ __launch_bounds__(256) void k_nf4_quantize(const float* __restrict__ 
   const uint8_t* kidx = reinterpret_cast<const uint8_t*>(sh_lut);
 
   // per float4: block absmax (4 values per lane, then 16 lanes), indices,
-  // two packed bytes stored as one uint16 (element 2j in the high nibble)
-  uint16_t* dst = reinterpret_cast<uint16_t*>(packed) + blk0 * 16;
+  // two packed bytes as one uint16 (element 2j in the high nibble), staged in
+  // LDS and written out below as 16-byte stores
   float tmax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -114,7 +115,7 @@ __global__ __launch_bounds__(256) void k_nf4_quantize(const float* __restrict__ 
     }
     const uint32_t b0 = (q[0] << 4) | q[1];
     const uint32_t b1 = (q[2] << 4) | q[3];
-    if (b < nblk) dst[i * 256 + t] = (uint16_t)(b0 | (b1 << 8));
+    sh_packed[i * 256 + t] = (uint16_t)(b0 | (b1 << 8));
   }
 
   // group constant c_g = max block scale (all 256 blocks of the group)
@@ -136,6 +137,12 @@ __global__ __launch_bounds__(256) void k_nf4_quantize(const float* __restrict__ 
     codes[blk0 + t] = (uint8_t)code;
   }
   if (t == 0) consts[g] = cg;
+
+  // the group's packed bytes (nblk * 32 of them) as 16-byte stores
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  u32x4_t* dst = reinterpret_cast<u32x4_t*>(packed + blk0 * 32);
+  const u32x4_t* srcp = reinterpret_cast<const u32x4_t*>(sh_packed);
+  for (int c = t; c < nblk * 2; c += 256) dst[c] = srcp[c];
 }
 
 hipError_t launch_nf4_quantize(const float* W, uint8_t* packed, uint8_t* codes, float* consts,
