@@ -313,23 +313,40 @@ __global__ __launch_bounds__(256) void k_skinny(SkinnyBatch SB) {
 }
 
 // Fixed-order sum of split partials, then the same outputs as the kernel above.
-__global__ __launch_bounds__(256) void k_skinny_sum(SkinnyBatch SB) {
+// TPO threads share one output: thread j adds splits j, j + TPO, ... in order,
+// then the TPO sums are added in order (deterministic).  With pairs of
+// columns (OUT_PAIRS / OUT_PAIRS_T) a workgroup covers whole rows.
+__global__ __launch_bounds__(256) void k_skinny_sum(SkinnyBatch SB, int tpo) {
   const SkinnyParams& S = SB.p[blockIdx.z];
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (S.nsplit == 1 || idx >= S.mrows * S.ocols) return;
+  if (S.nsplit == 1) return;
+  __shared__ float part[256];
+  __shared__ float tot[256];
+  const int per_wg = 256 / tpo;
+  const int64_t o0 = (int64_t)blockIdx.x * per_wg;
+  const int64_t nout = S.mrows * S.ocols;
+  if (o0 >= nout) return;
+  const int tid = threadIdx.x, o = tid / tpo, j = tid % tpo;
+  float v = 0.0f;
+  if (o0 + o < nout)
+    for (int z = j; z < S.nsplit; z += tpo) v += S.Pout[(int64_t)z * nout + o0 + o];
+  part[tid] = v;
+  __syncthreads();
+  if (tid < per_wg) {
+    float t = 0.0f;
+    for (int jj = 0; jj < tpo; ++jj) t += part[tid * tpo + jj];
+    tot[tid] = t;
+  }
+  __syncthreads();
+  if (tid >= per_wg || o0 + tid >= nout) return;
+  const int64_t idx = o0 + tid;
   const int64_t m = idx / S.ocols;
   const int col = (int)(idx - m * S.ocols);
-  auto part = [&](int c) {
-    float v = 0.0f;
-    for (int z = 0; z < S.nsplit; ++z) v += S.Pout[(int64_t)z * S.mrows * S.ocols + m * S.ocols + c];
-    return v;
-  };
   if (S.out_mode == OUT_ROWS_HILO) {
     if (col < S.r) {
-      const float v = part(col);
-      if (S.Vout) S.Vout[m * S.r + col] = v;
+      const float v2 = tot[tid];
+      if (S.Vout) S.Vout[m * S.r + col] = v2;
       uint16_t hi, lo;
-      split_bf16(S.s * v, hi, lo);
+      split_bf16(S.s * v2, hi, lo);
       S.Hout[m * S.ldh + col] = hi;
       S.Hout[m * S.ldh + S.r + col] = lo;
     }
@@ -344,7 +361,7 @@ __global__ __launch_bounds__(256) void k_skinny_sum(SkinnyBatch SB) {
       for (int64_t c = 2 * S.r + col; c < S.ldh; c += S.ocols) S.Ucs[m * S.ldh + c] = 0;
     }
   } else if (col < S.r) {
-    const float t = part(col) + part(col + S.r);
+    const float t = tot[tid] + tot[tid + S.r];   // the row's column col + r is in this workgroup
     if (S.out_mode == OUT_PAIRS) S.Fout[m * S.r + col] = t;
     else S.Fout[(int64_t)col * S.mrows + m] = t;
   }
@@ -373,11 +390,11 @@ int skinny_splits(int64_t mrows, int64_t clen, int cols) {
   (void)cols;
   const int64_t tiles = (mrows + MT - 1) / MT;
   const int64_t chunks = (clen + CH - 1) / CH;
-  // about 512 workgroups in flight, at least one chunk per wave, and at most
-  // 32 partials per output (they are summed by one thread each)
+  // about 512 workgroups in flight, at least one chunk per wave, at most 256
+  // partials per output
   int64_t ns = (512 + tiles - 1) / tiles;
   int64_t cap = (chunks + WAVES - 1) / WAVES;
-  if (cap > 32) cap = 32;
+  if (cap > 256) cap = 256;
   if (ns > cap) ns = cap;
   return (int)(ns < 1 ? 1 : ns);
 }
@@ -415,8 +432,17 @@ hipError_t launch_batch(SkinnyBatch B, hipStream_t stream, int kernel_id) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || outs == 0) return e;
+  // threads per output: about 4 splits each, at most 16, and whole rows per
+  // workgroup when columns are summed in pairs
+  int tpo = 1;
+  while (tpo < 16 && tpo * 4 < ns) tpo *= 2;
+  for (int i = 0; i < B.n; ++i)
+    if (B.p[i].out_mode != OUT_ROWS_HILO)
+      while (tpo > 1 && (256 / tpo) % B.p[i].ocols != 0) tpo /= 2;
+  const int64_t per_wg = 256 / tpo;
   TraceScope ts(KID_REDUCE, stream);
-  hipLaunchKernelGGL(k_skinny_sum, dim3((unsigned)((outs + 255) / 256), 1, (unsigned)B.n), dim3(256), 0, stream, B);
+  hipLaunchKernelGGL(k_skinny_sum, dim3((unsigned)((outs + per_wg - 1) / per_wg), 1, (unsigned)B.n), dim3(256), 0,
+                     stream, B, tpo);
   return hipGetLastError();
 }
 
