@@ -70,8 +70,16 @@ __device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) 
 }
 
 // Restored scale of a 64-weight block: fl32(fl32(code) * fl32(c_g / 255)).
+// The quotient is formed without a division: q = c_g * fl32(1/255) is within
+// an ulp, and one residual step r = c_g - 255 q (exact in an FMA),
+// q + r * fl32(1/255) rounds to the correctly rounded quotient for every
+// finite c_g >= 0 (checked over all such floats).  c_g = inf or NaN leaves r
+// NaN; q is then the IEEE quotient itself.
 __device__ __forceinline__ float restored_scale(uint32_t code, float c_g) {
-  const float step = c_g / 255.0f;  // IEEE-rounded division
+  constexpr float inv = 1.0f / 255.0f;
+  const float q = c_g * inv;
+  const float r = __builtin_fmaf(-q, 255.0f, c_g);
+  const float step = r == r ? __builtin_fmaf(r, inv, q) : q;
   return (float)code * step;
 }
 

@@ -17,21 +17,34 @@
 // indices costs about 29 VALU instructions and no memory access.  The values
 // are exactly bf16_rne(fl32(T[q] * s')).
 //
-// Tiling (gfx950: 256 CUs, 4 SIMDs each, 160 KB LDS, LDS reads ~128 B/clk):
-// 256 threads = 4 waves in a 2 x 2 grid, workgroup tile 256 x BN (BN = 256 or
-// 128), wave tile 128 x (BN/2) of 32 x 32 MFMA tiles, contraction step 64.
-// Two LDS stages: while the waves multiply stage t, the next step's operands
-// are already in registers (issued before the MFMAs) and are restored/written
-// into the other stage after them; one barrier per step.  Rows of
-// contraction-contiguous LDS tiles are padded to 144 B so that sixteen-byte
-// fragment reads of 8 consecutive rows hit distinct banks.
+// Tiling (gfx950: 256 CUs, 4 SIMDs each, 160 KB LDS; measured per CU: LDS
+// reads ~240 B/clk, global loads ~55 B/clk): 512 threads.  Waves 0-3 multiply
+// (2 x 2 grid, wave tile 128 x 64 of 32 x 32 MFMA tiles, workgroup tile
+// 256 x 128, contraction step 64); waves 4-7 restore weights.  One barrier per
+// step.
+//
+// The activation operand (X or dY) goes from global memory straight to LDS
+// (buffer_load_dwordx4 ... lds): the multiplying waves issue those copies for
+// step t+2 between their MFMAs of step t, two per sixteen-wide contraction
+// slice, so the per-CU load path (~55 B/clk) is never hit by a burst and no
+// VGPR or VALU work is spent on it.  Three A stages (t, t+1 landing, t+2 being
+// issued); before the barrier that ends step t each wave waits until its
+// copies for step t+1 have landed.  A tiles are 256 rows of 128 B without
+// padding; sixteen-byte chunk c of row R sits at position
+// c ^ (R & 7) ^ ((R >> 3) & 1), so a fragment read (16 lanes per LDS cycle: 16
+// consecutive rows, one chunk) touches 16 distinct 16-byte bank groups.
+//
+// The restoring waves load the packed words, codes and group constants of step
+// t+3 into registers and restore step t+1 into one of two B stages while step t
+// is multiplied.  Forward B rows are contraction-contiguous and padded to
+// 144 B, which is conflict-free for the same fragment reads.
 //
 // dX contracts over d_out, the row index of the packed weight.  The restored
-// tile is stored row-major ([n][k], rows padded to 544/288 B) exactly as it
-// comes from memory, and the MFMA B fragments (8 consecutive n at one k) are
-// read with ds_read_b64_tr_b16: within each 16-lane group, source lane s
-// points at row kb + s/4, columns c0 + 4*(s%4), and lane i receives the four
-// rows kb..kb+3 of column c0 + i.
+// tile is stored row-major ([k][n], rows padded to 288 B) exactly as it comes
+// from memory, and the MFMA B fragments (8 consecutive k at one n) are read
+// with ds_read_b64_tr_b16: within each 16-lane group, source lane s points at
+// row kb + s/4, columns c0 + 4*(s%4), and lane i receives the four rows
+// kb..kb+3 of column c0 + i.
 //
 // The LoRA term runs as extra contraction steps over the 2r columns of a
 // hi/lo bf16 split of s*U (forward) or s*G (dX), so it is accumulated in fp32
@@ -105,30 +118,77 @@ struct Geometry {
   static constexpr int BM = 256;
   static constexpr int TM = 4;              // 32-row MFMA tiles per wave (wave rows 128)
   static constexpr int TN = BN / 64;        // 32-col MFMA tiles per wave
-  static constexpr int A_ELEMS = BM * LDK;
+  static constexpr int A_BYTES = BM * BK * 2;  // one A stage: 256 rows of 128 B
   // B tile: [BN][LDK] (contraction-contiguous) or [64][BN + 16] (column-contiguous)
   static constexpr int LDB_T = BN + 16;
   static constexpr int B_ELEMS = BT ? BK * LDB_T : BN * LDK;
-  static constexpr int STAGE = A_ELEMS + B_ELEMS;
-  static constexpr int LDC = BN + 8;        // epilogue bf16 tile row
-  static constexpr int LDS_ELEMS = (2 * STAGE > BM * LDC) ? 2 * STAGE : BM * LDC;
+  static constexpr int B_BYTES = B_ELEMS * 2;
+  static constexpr int B_OFF = 3 * A_BYTES;    // the two B stages follow the three A stages
+  static constexpr int LDC = BN + 8;           // epilogue bf16 tile row
+  static constexpr int MAIN_BYTES = B_OFF + 2 * B_BYTES;
+  static constexpr int LDS_BYTES = MAIN_BYTES > BM * LDC * 2 ? MAIN_BYTES : BM * LDC * 2;
 };
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, int64_t bytes) {
+  const int32_t n = bytes > 0x7FFFFFF0LL ? 0x7FFFFFF0 : (int32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, n, 0x00020000);
+}
+
 // ---------------------------------------------------------------------------
-// Producers: global -> registers (issued early), registers -> LDS (after the MFMAs)
+// A operand: global -> LDS copies issued by the multiplying waves
 //
-// Main-loop loads are buffer loads whose per-thread byte offsets are computed
-// once; the contraction step advances through the scalar offset.  Rows beyond
-// the output (A rows >= M, weight rows/columns beyond the output columns) are
-// clamped to a valid address instead of masked: they only feed output rows or
-// columns that are never stored.
+// Multiplying wave cw copies rows 64cw .. 64cw+63 of each A stage with eight
+// 1 KB copies; copy j covers rows 64cw + 8j .. +7, lane l lands at byte 16l of
+// it, i.e. row 64cw + 8j + l/8, position l%8, and so fetches chunk
+// (l%8) ^ (l/8) ^ (j%2) of that row (the swizzle above).  Rows beyond the
+// output are clamped to the last row: they only feed output rows never stored.
 // ---------------------------------------------------------------------------
 
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+struct ACopy {
+  __amdgpu_buffer_rsrc_t r;
+  uint32_t voff[8];  // per-lane byte offsets at contraction column 0
+};
+
+__device__ __forceinline__ ACopy make_acopy(const uint16_t* A, int64_t ld, int64_t M, int64_t m0, int cw, int lane) {
+  ACopy c;
+  c.r = rsrc(A, M * ld * 2);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    int64_t row = m0 + 64 * cw + 8 * j + (lane >> 3);
+    row = row < M ? row : M - 1;
+    const int chunk = (lane & 7) ^ (lane >> 3) ^ (j & 1);
+    c.voff[j] = (uint32_t)(row * ld * 2 + chunk * 16);
+  }
+  return c;
+}
+
+// Copy j of this wave's rows for the contraction columns starting at byte col_bytes.
+__device__ __forceinline__ void a_copy(const ACopy& c, uint32_t col_bytes, uint8_t* stage, int cw, int j) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(c.r, (lds_void_t*)(stage + (64 * cw + 8 * j) * 128), 16, c.voff[j],
+                                           col_bytes, 0, 0);
+}
+
+// Wait until at most n of this wave's global loads (here: its A copies) are in flight.
+template <int N>
+__device__ __forceinline__ void wait_copies() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// ---------------------------------------------------------------------------
+// Restoring waves: packed words, codes, group constants -> registers (issued
+// early), restored bf16 -> LDS
+//
+// Main-loop loads are buffer loads whose per-thread byte offsets are computed
+// once; the contraction step advances through the scalar offset.  Weight
+// rows/columns beyond the output are clamped to a valid address instead of
+// masked: they only feed output columns that are never stored.
+// ---------------------------------------------------------------------------
 
 template <int BN>
 struct StepRegs {
-  u32x4_t a[8];          // A: eight 16-byte chunks (rows tid/8 + 32i, columns (tid%8)*8 .. +8)
   uint32_t w[BN / 32];   // packed weight words (8 indices each)
   uint32_t code4;        // the aligned dword holding the block's 8-bit scale code
   uint32_t code_shift;   // bit position of the code inside code4
@@ -136,8 +196,7 @@ struct StepRegs {
 };
 
 struct Cursor {
-  __amdgpu_buffer_rsrc_t ra, rw, rc, rk;
-  uint32_t aoff[8];  // byte offsets of the thread's A chunks at step 0
+  __amdgpu_buffer_rsrc_t rw, rc, rk;
   uint32_t woff;     // byte offset of the thread's packed words at step 0
   uint32_t coff;     // block index of the thread's weights at step 0
   uint32_t wstep;    // bytes the packed words advance per step
@@ -146,16 +205,11 @@ struct Cursor {
   uint32_t rot;      // this workgroup starts its contraction at step rot (see fused_body)
 };
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, int64_t bytes) {
-  const int32_t n = bytes > 0x7FFFFFF0LL ? 0x7FFFFFF0 : (int32_t)bytes;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, n, 0x00020000);
-}
-
-// Producer-local thread index: producer waves are waves 4..7 of the workgroup.
+// Restoring-wave thread index: those are waves 4..7 of the workgroup.
 __device__ __forceinline__ int ptid() { return (int)threadIdx.x - 256; }
 
 template <int BN, bool BT>
-__device__ __forceinline__ void w_coords(int64_t n0, int& lrow, int& lcol) {
+__device__ __forceinline__ void w_coords(int& lrow, int& lcol) {
   const int tid = ptid();
   if (!BT) {
     // forward: BN rows of 64 weights; one row (BN = 256) or half a row (BN = 128) per thread
@@ -169,22 +223,14 @@ __device__ __forceinline__ void w_coords(int64_t n0, int& lrow, int& lcol) {
 }
 
 template <int BN, bool BT>
-__device__ __forceinline__ Cursor make_cursor(const FusedParams& P, int64_t m0, int64_t n0) {
-  const int tid = ptid();
+__device__ __forceinline__ Cursor make_cursor(const FusedParams& P, int64_t n0) {
   Cursor c;
-  c.ra = rsrc(P.A, P.M * P.lda * 2);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    int64_t row = m0 + (tid >> 3) + 32 * i;
-    row = row < P.M ? row : P.M - 1;
-    c.aoff[i] = (uint32_t)((row * P.lda + (tid & 7) * 8) * 2);
-  }
   const int64_t Nw = BT ? P.K0 : P.N;  // rows of the stored weight
   c.rw = rsrc(P.packed, Nw * P.Kw / 2);
   c.rc = rsrc(P.codes, Nw * P.Kw / 64);
   c.rk = rsrc(P.consts, ((Nw * P.Kw / 64 + 255) / 256) * 4);
   int lrow, lcol;
-  w_coords<BN, BT>(n0, lrow, lcol);
+  w_coords<BN, BT>(lrow, lcol);
   if (!BT) {
     int64_t n = n0 + lrow;
     n = n < P.N ? n : P.N - 1;
@@ -203,13 +249,15 @@ __device__ __forceinline__ Cursor make_cursor(const FusedParams& P, int64_t m0, 
   return c;
 }
 
+// contraction step -> stored column block (the workgroup's rotated order)
+__device__ __forceinline__ uint32_t rotated(uint32_t step, uint32_t rot, uint32_t nk) {
+  const uint32_t kt = step + rot;
+  return kt >= nk ? kt - nk : kt;
+}
+
 template <int BN>
 __device__ __forceinline__ void fetch(StepRegs<BN>& f, const Cursor& c, uint32_t step) {
-  uint32_t kt = step + c.rot;
-  kt = kt >= c.nk ? kt - c.nk : kt;
-  const uint32_t sa = kt * (BK * 2);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) f.a[i] = __builtin_amdgcn_raw_buffer_load_b128(c.ra, c.aoff[i], sa, 0);
+  const uint32_t kt = rotated(step, c.rot, c.nk);
   const uint32_t sw = kt * c.wstep;
   const u32x4_t w0 = __builtin_amdgcn_raw_buffer_load_b128(c.rw, c.woff, sw, 0);
   f.w[0] = w0.x; f.w[1] = w0.y; f.w[2] = w0.z; f.w[3] = w0.w;
@@ -235,16 +283,10 @@ __device__ __forceinline__ void pin(StepRegs<BN>& f) {
 }
 
 template <int BN, bool BT>
-__device__ __forceinline__ void store_step(StepRegs<BN>& f, const Nf4Table& tab, uint16_t* __restrict__ As,
-                                           uint16_t* __restrict__ Bs, int64_t n0) {
+__device__ __forceinline__ void restore_step(StepRegs<BN>& f, const Nf4Table& tab, uint16_t* __restrict__ Bs) {
   pin<BN>(f);
-  const int tid = ptid();
-  const int kc = (tid & 7) * 8;
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    *reinterpret_cast<u32x4_t*>(As + ((tid >> 3) + 32 * i) * LDK + kc) = f.a[i];
   int lrow, lcol;
-  w_coords<BN, BT>(n0, lrow, lcol);
+  w_coords<BN, BT>(lrow, lcol);
   const RestoreTab t = make_tab(tab, restored_scale((f.code4 >> f.code_shift) & 0xFFu, f.cg));
   uint16_t* dst = BT ? Bs + lrow * Geometry<BN, BT>::LDB_T + lcol : Bs + lrow * LDK + lcol;
 #pragma unroll
@@ -254,21 +296,6 @@ __device__ __forceinline__ void store_step(StepRegs<BN>& f, const Nf4Table& tab,
     restore8(f.w[i + 1], t, o + 4);
     *reinterpret_cast<uint4*>(dst + i * 8) = make_uint4(o[0], o[1], o[2], o[3]);
     *reinterpret_cast<uint4*>(dst + i * 8 + 8) = make_uint4(o[4], o[5], o[6], o[7]);
-  }
-}
-
-// Tail A operand (the hi/lo pair of s*U or s*G, [M][ldat], zero past 2r):
-// plain loads with row clamping; the tail runs once per tile.
-__device__ __forceinline__ void tail_a_store(const uint16_t* __restrict__ At, int64_t ldat, int64_t M, int64_t m0,
-                                             int64_t k0, uint16_t* __restrict__ As) {
-  const int tid = ptid();
-  const int kc = (tid & 7) * 8;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    int64_t row = m0 + (tid >> 3) + 32 * i;
-    row = row < M ? row : M - 1;
-    *reinterpret_cast<uint4*>(As + ((tid >> 3) + 32 * i) * LDK + kc) =
-        *reinterpret_cast<const uint4*>(At + row * ldat + k0 + kc);
   }
 }
 
@@ -309,48 +336,52 @@ __device__ __forceinline__ void tail_b_store(const uint16_t* __restrict__ Bt, in
 }
 
 // ---------------------------------------------------------------------------
-// MFMA on one LDS stage
+// MFMA fragments of one sixteen-wide contraction slice, and their products
 // ---------------------------------------------------------------------------
 
+template <int BN>
+struct Frags {
+  bf16x8_t a[4];
+  bf16x8_t b[BN / 64];
+};
+
 template <int BN, bool BT>
-__device__ __forceinline__ void mma_stage(const uint16_t* __restrict__ As, const uint16_t* __restrict__ Bs,
-                                          f32x16_t (&acc)[4][BN / 64]) {
+__device__ __forceinline__ void load_frags(Frags<BN>& f, const uint8_t* __restrict__ As,
+                                           const uint16_t* __restrict__ Bs, uint32_t arow, uint32_t apos, int ks) {
   constexpr int TM = 4, TN = BN / 64;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 1;
+  const int kofs = ks * 16 + (lane >> 5) * 8;
 #pragma unroll
-  for (int ks = 0; ks < BK / 16; ++ks) {
-    bf16x8_t a[TM], b[TN];
-    const int kofs = ks * 16 + (lane >> 5) * 8;
+  for (int i = 0; i < TM; ++i) f.a[i] = *reinterpret_cast<const bf16x8_t*>(As + arow + i * 4096 + apos);
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
-      a[i] = *reinterpret_cast<const bf16x8_t*>(As + ((wm * TM + i) * 32 + (lane & 31)) * LDK + kofs);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      if (!BT) {
-        b[j] = *reinterpret_cast<const bf16x8_t*>(Bs + ((wn * TN + j) * 32 + (lane & 31)) * LDK + kofs);
-      } else {
-        constexpr int LDB_T = Geometry<BN, BT>::LDB_T;
-        const int s = lane & 15;
-        const int col = (wn * TN + j) * 32 + ((lane >> 4) & 1) * 16 + 4 * (s & 3);
-        const int row = kofs + (s >> 2);
-        typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
-        const lds_u16_t* base = (const lds_u16_t*)Bs;
-        const u16x4_t lo = __builtin_bit_cast(
-            u16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(base + row * LDB_T + col)));
-        const u16x4_t hi = __builtin_bit_cast(
-            u16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(base + (row + 4) * LDB_T + col)));
-        typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
-        const u16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        b[j] = __builtin_bit_cast(bf16x8_t, v);
-      }
+  for (int j = 0; j < TN; ++j) {
+    if (!BT) {
+      f.b[j] = *reinterpret_cast<const bf16x8_t*>(Bs + ((wn * TN + j) * 32 + (lane & 31)) * LDK + kofs);
+    } else {
+      constexpr int LDB_T = Geometry<BN, BT>::LDB_T;
+      const int s = lane & 15;
+      const int col = (wn * TN + j) * 32 + ((lane >> 4) & 1) * 16 + 4 * (s & 3);
+      const int row = kofs + (s >> 2);
+      typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
+      const lds_u16_t* base = (const lds_u16_t*)Bs;
+      const u16x4_t lo = __builtin_bit_cast(
+          u16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(base + row * LDB_T + col)));
+      const u16x4_t hi = __builtin_bit_cast(
+          u16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(base + (row + 4) * LDB_T + col)));
+      typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
+      const u16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      f.b[j] = __builtin_bit_cast(bf16x8_t, v);
     }
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
   }
+}
+
+template <int BN>
+__device__ __forceinline__ void mma_frags(const Frags<BN>& f, f32x16_t (&acc)[4][BN / 64]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < BN / 64; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -361,7 +392,7 @@ template <int BN, bool BT>
 __device__ __forceinline__ void fused_body(const FusedParams& P) {
   using G = Geometry<BN, BT>;
   constexpr int TM = G::TM, TN = G::TN;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[G::LDS_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[G::LDS_BYTES];
 
   // tile order: chunks of consecutive tiles go to one XCD; inside the order,
   // groups of two tile rows are walked column by column.
@@ -378,15 +409,30 @@ __device__ __forceinline__ void fused_body(const FusedParams& P) {
   const int64_t tn = in_group / rows_in_group;
   const int64_t m0 = tm * G::BM, n0 = tn * BN;
 
-  uint16_t* stage0 = lds;
-  uint16_t* stage1 = lds + G::STAGE;
   const uint32_t nk = (uint32_t)(P.K0 / BK);
   const uint32_t ntail = P.r > 0 ? (uint32_t)((2 * (int64_t)P.r + BK - 1) / BK) : 0;
+  const uint32_t nsteps = nk + ntail;
+  // Tiles of one tile row share their A rows and walk the contraction in
+  // lockstep, so those rows are read once into L2 and hit there.  Different
+  // tile rows start at different steps: rows a power of two apart would
+  // otherwise send the same column block of every row to few L2 channels
+  // at once.  The sum order per tile is fixed, so results stay deterministic.
+  const uint32_t rot = (uint32_t)((tm * 5) % nk);
+  auto a_stage = [&](uint32_t s) { return lds + (s % 3) * G::A_BYTES; };
+  auto b_stage = [&](uint32_t s) { return reinterpret_cast<uint16_t*>(lds + G::B_OFF + (s & 1) * G::B_BYTES); };
 
-  // Waves 0-3 multiply (consumers), waves 4-7 load and restore (producers);
-  // two waves per SIMD, so one's VALU/memory work overlaps the other's MFMAs.
-  // Both roles pass the same sequence of barriers: 1 + nk + 2*ntail + 1.
+  // Both roles pass the same sequence of barriers: 1 + nsteps, then 1.
   if (threadIdx.x < 256) {
+    const int lane = threadIdx.x & 63;
+    const int cw = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int wm = cw >> 1;
+    // fragment addresses: row wm*128 + i*32 + lane%32, chunk 2ks + lane/32
+    const uint32_t arow = (uint32_t)((wm * 128 + (lane & 31)) * 128);
+    const int x = (lane & 7) ^ ((lane >> 3) & 1);
+    uint32_t apos[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) apos[ks] = (uint32_t)(((2 * ks + (lane >> 5)) ^ x) * 16);
+
     f32x16_t acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -394,20 +440,71 @@ __device__ __forceinline__ void fused_body(const FusedParams& P) {
       for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    // A copies, issued in step order: steps < nk read the rotated column block
+    // of X / dY, step nk + t the hi/lo columns 64t .. 64t+63.
+    ACopy cp = make_acopy(P.A, P.lda, P.M, m0, cw, lane);
+    auto col_of = [&](uint32_t c) { return c < nk ? rotated(c, rot, nk) * (BK * 2) : (c - nk) * (BK * 2); };
+    for (uint32_t c = 0; c < 2 && c < nsteps; ++c) {
+      if (c == nk) cp = make_acopy(P.At, P.ldat, P.M, m0, cw, lane);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) a_copy(cp, col_of(c), a_stage(c), cw, j);
+    }
+    if (nsteps > 1) wait_copies<8>();
+    else wait_copies<0>();
     lds_barrier();
-    for (uint32_t h = 0; h < nk; ++h) {
-      uint16_t* st = (h & 1) ? stage1 : stage0;
-      mma_stage<BN, BT>(st, st + G::A_ELEMS, acc);
+
+    // Step s: slices 0-2 are multiplied while the next slice's fragments are
+    // read; the barrier follows; slice 3 is multiplied after it, while the
+    // first fragments of step s+1 are read.  Step s+2's eight copies go out
+    // two per slice, so six of them are in flight at the barrier that ends
+    // step s, by when every copy of step s+1 has landed.  In the last two
+    // steps the copies repeat the last step's columns into the stage no one
+    // reads (and the last fragment reads fetch a stage no one multiplies), so
+    // the loop body has no branch and its order can be fixed: each slice
+    // issues the next slice's reads first, then its eight MFMAs with the two
+    // copies between them.
+    constexpr int kReads = BT ? 8 : 6;  // LDS read instructions per slice
+    auto order_slice = [] {
+      __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);  // LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);       // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);       // copy
+      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    };
+    const uint32_t last_col = col_of(nsteps - 1);
+    Frags<BN> cur, nxt;
+    load_frags<BN, BT>(cur, a_stage(0), b_stage(0), arow, apos[0], 0);
+    for (uint32_t s = 0; s < nsteps; ++s) {
+      const uint32_t c = s + 2;
+      if (c == nk && c < nsteps) cp = make_acopy(P.At, P.ldat, P.M, m0, cw, lane);
+      const uint32_t col = c < nsteps ? col_of(c) : last_col;
+      uint8_t* dst = a_stage(c);
+      const uint8_t* As = a_stage(s);
+      const uint16_t* Bs = b_stage(s);
+#pragma unroll
+      for (int ks = 0; ks < 3; ++ks) {
+        load_frags<BN, BT>(nxt, As, Bs, arow, apos[ks + 1], ks + 1);
+        a_copy(cp, col, dst, cw, 2 * ks);
+        a_copy(cp, col, dst, cw, 2 * ks + 1);
+        mma_frags<BN>(cur, acc);
+        order_slice();
+        cur = nxt;
+      }
+      wait_copies<6>();
       lds_barrier();
+      load_frags<BN, BT>(nxt, a_stage(s + 1), b_stage(s + 1), arow, apos[0], 0);
+      a_copy(cp, col, dst, cw, 6);
+      a_copy(cp, col, dst, cw, 7);
+      mma_frags<BN>(cur, acc);
+      order_slice();
+      cur = nxt;
     }
-    for (uint32_t t = 0; t < ntail; ++t) {
-      lds_barrier();
-      mma_stage<BN, BT>(stage0, stage0 + G::A_ELEMS, acc);
-      lds_barrier();
-    }
-    // epilogue: bf16 tile into LDS
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    wait_copies<0>();
+    // epilogue: bf16 tile into LDS (over the A stages, no longer read)
+    uint16_t* ct = reinterpret_cast<uint16_t*>(lds);
+    const int wn = cw & 1;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -416,58 +513,55 @@ __device__ __forceinline__ void fused_body(const FusedParams& P) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int row = (wm * TM + i) * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-          lds[row * G::LDC + col] = f32_to_bf16_bits(acc[i][j][v]);
+          ct[row * G::LDC + col] = f32_to_bf16_bits(acc[i][j][v]);
         }
       }
     lds_barrier();
   } else {
-    Cursor cur = make_cursor<BN, BT>(P, m0, n0);
-    // Tiles of one tile row share their A rows and walk the contraction in
-    // lockstep, so those rows are read once into L2 and hit there.  Different
-    // tile rows start at different steps: rows a power of two apart would
-    // otherwise send the same column block of every row to few L2 channels
-    // at once.  The sum order per tile is fixed, so results stay deterministic.
+    Cursor cur = make_cursor<BN, BT>(P, n0);
     cur.nk = nk;
-    cur.rot = (uint32_t)((tm * 5) % nk);
-    // three register sets: set i%3 holds step i; at half-step h the producers
-    // issue the loads of step h+3 into the set freed by step h, then restore
-    // step h+1 into LDS stage (h+1)%2, so every load has two steps in flight.
+    cur.rot = rot;
+    auto tail_b = [&](uint32_t s) { tail_b_store<BN, BT>(P.Bt, P.ldbt, P.r, P.N, n0, s - nk, b_stage(s)); };
+    // three register sets: set i%3 holds step i; in the period of step h the
+    // restoring waves issue the loads of step h+3 into the set freed by step
+    // h, then restore step h+1 into B stage (h+1)%2, so every load has two
+    // steps in flight.
     StepRegs<BN> f0, f1, f2;
     const uint32_t last = nk - 1;
     fetch<BN>(f0, cur, 0);
     fetch<BN>(f1, cur, 1 < nk ? 1 : last);
     fetch<BN>(f2, cur, 2 < nk ? 2 : last);
-    store_step<BN, BT>(f0, P.tab, stage0, stage0 + G::A_ELEMS, n0);
+    restore_step<BN, BT>(f0, P.tab, b_stage(0));
     lds_barrier();
-    auto half = [&](StepRegs<BN>& into, StepRegs<BN>& from, uint16_t* st, uint32_t h) {
+    auto period = [&](StepRegs<BN>& into, StepRegs<BN>& from, uint32_t h) {
       fetch<BN>(into, cur, h + 3 < nk ? h + 3 : last);
-      if (h + 1 < nk) store_step<BN, BT>(from, P.tab, st, st + G::A_ELEMS, n0);
+      restore_step<BN, BT>(from, P.tab, b_stage(h + 1));
       lds_barrier();
     };
-    for (uint32_t h = 0; h < nk; h += 6) {
-      half(f0, f1, stage1, h);
-      if (h + 1 < nk) half(f1, f2, stage0, h + 1);
-      if (h + 2 < nk) half(f2, f0, stage1, h + 2);
-      if (h + 3 < nk) half(f0, f1, stage0, h + 3);
-      if (h + 4 < nk) half(f1, f2, stage1, h + 4);
-      if (h + 5 < nk) half(f2, f0, stage0, h + 5);
+    // periods h = 0 .. nk-2 restore main steps 1 .. nk-1
+    for (uint32_t h = 0; h + 1 < nk; h += 6) {
+      period(f0, f1, h);
+      if (h + 2 < nk) period(f1, f2, h + 1);
+      if (h + 3 < nk) period(f2, f0, h + 2);
+      if (h + 4 < nk) period(f0, f1, h + 3);
+      if (h + 5 < nk) period(f1, f2, h + 4);
+      if (h + 6 < nk) period(f2, f0, h + 5);
     }
-    // rank-r term: contraction over the hi/lo columns (zero-padded to a multiple of 64)
-    for (uint32_t t = 0; t < ntail; ++t) {
-      tail_a_store(P.At, P.ldat, P.M, m0, (int64_t)t * BK, stage0);
-      tail_b_store<BN, BT>(P.Bt, P.ldbt, P.r, P.N, n0, t, stage0 + G::A_ELEMS);
-      lds_barrier();
+    // period nk-1 and the tail periods: the rank-r term's B operand
+    for (uint32_t h = nk - 1; h < nsteps; ++h) {
+      if (h + 1 < nsteps) tail_b(h + 1);
       lds_barrier();
     }
     lds_barrier();
   }
 
   // coalesced 16-byte stores of the bf16 tile, all eight waves
+  const uint16_t* ct = reinterpret_cast<const uint16_t*>(lds);
   for (int c = threadIdx.x; c < G::BM * (BN / 8); c += 512) {
     const int row = c / (BN / 8), cc = (c % (BN / 8)) * 8;
     const int64_t gr = m0 + row, gc = n0 + cc;
     if (gr < P.M && gc < P.N)
-      *reinterpret_cast<uint4*>(P.C + gr * P.ldc + gc) = *reinterpret_cast<const uint4*>(lds + row * G::LDC + cc);
+      *reinterpret_cast<uint4*>(P.C + gr * P.ldc + gc) = *reinterpret_cast<const uint4*>(ct + row * G::LDC + cc);
   }
 }
 
@@ -478,6 +572,10 @@ __global__ __launch_bounds__(512) void k_qlora_dx_gemm(FusedParams P) { fused_bo
 
 hipError_t launch_fused(FusedParams P, bool dx, hipStream_t stream, int kernel_id) {
   constexpr int bn = 128;
+  // buffer offsets are 32-bit and the ranges are capped below 2 GiB
+  if (P.M * P.lda * 2 > 0x7FFFFFF0LL || (P.r > 0 && P.M * P.ldat * 2 > 0x7FFFFFF0LL) ||
+      (dx ? P.K0 : P.N) * P.Kw / 2 > 0x7FFFFFF0LL)
+    return hipErrorInvalidValue;
   P.mt = (int32_t)((P.M + 255) / 256);
   P.nt = (int32_t)((P.N + bn - 1) / bn);
   P.group_m = 2;
