@@ -46,7 +46,7 @@
  *   Arguments are validated on the host before anything is enqueued, so a
  *   call that fails validation has no side effect.  QLORA_ERR_HIP reports a
  *   failed launch (hipGetLastError after enqueueing).
- * - W, packed, X, dY and A must be 16-byte aligned (QLORA_ERR_UNSUPPORTED
+ * - W, packed, X, dY, A and B must be 16-byte aligned (QLORA_ERR_UNSUPPORTED
  *   otherwise); other pointers need only their element alignment.
  * - Inputs must be finite; results for NaN/Inf inputs are unspecified.
  * - Hot-path preconditions: blocksize == 64, dq_blocksize == 256,

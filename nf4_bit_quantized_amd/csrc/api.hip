@@ -6,6 +6,7 @@
 #include <cstring>
 
 #include "fused.hpp"
+#include "lora_stream.hpp"
 #include "skinny.hpp"
 #include "trace.hpp"
 #include "../../include/qlora.h"
@@ -79,7 +80,7 @@ FwdWs plan_fwd(const qlora_nf4_desc* d, int64_t T, int32_t r, void* ws) {
   Carve c(ws);
   const int64_t N = d->d_out, K = d->d_in;
   if (r > 0 && T > 0) {
-    w.part = static_cast<float*>(c.take(skinny_part_bytes(T, K, r)));
+    if (!lora_rows_ok(T, r)) w.part = static_cast<float*>(c.take(skinny_part_bytes(T, K, r)));
     w.U = static_cast<float*>(c.take((size_t)T * r * 4));
     w.Us = static_cast<uint16_t*>(c.take((size_t)T * hilo_ld(r) * 2));
   }
@@ -106,11 +107,15 @@ BwdWs plan_bwd(const qlora_nf4_desc* d, int64_t T, int32_t r, void* ws) {
   const int64_t N = d->d_out, K = d->d_in;
   if (r > 0 && T > 0) {
     const int64_t ldh = hilo_ld(r);
-    size_t part = skinny_part_bytes(T, K, r);
-    part = std::max(part, skinny_part_bytes(T, N, r));
-    part = std::max(part, skinny_part_bytes(K, T, 2 * (int64_t)r));
+    // split-contraction partials, only for the products the streaming kernels do not take
+    size_t part = 0, part2 = 0;
+    if (!lora_rows_ok(T, r)) part = std::max(skinny_part_bytes(T, K, r), skinny_part_bytes(T, N, r));
+    if (!lora_stream_ok(r)) {
+      part = std::max(part, skinny_part_bytes(K, T, 2 * (int64_t)r));
+      part2 = skinny_part_bytes(N, T, 2 * (int64_t)r);
+    }
     w.part = static_cast<float*>(c.take(part));
-    w.part2 = static_cast<float*>(c.take(skinny_part_bytes(N, T, 2 * (int64_t)r)));
+    w.part2 = static_cast<float*>(c.take(part2));
     w.U = static_cast<float*>(c.take((size_t)T * r * 4));
     w.Us = static_cast<uint16_t*>(c.take((size_t)T * ldh * 2));
     w.Gs = static_cast<uint16_t*>(c.take((size_t)T * ldh * 2));
@@ -143,6 +148,14 @@ void skinny_q(SkinnyParams& S, const uint16_t* Q, int64_t ldq, int64_t qrows, in
 // U = X A^T (fp32 into U), and the hi/lo bf16 pair of s*U into Us.
 int lora_down(const uint16_t* X, const uint16_t* A, int64_t T, int64_t K, int32_t r, float s, float* part,
               float* U, uint16_t* Us, hipStream_t st) {
+  if (lora_rows_ok(T, r)) {
+    RowsParams R{};
+    R.P = X; R.ldp = K; R.M = T; R.D = K;
+    R.Q = A; R.ldq = K; R.q_strided = 0; R.r = r; R.s = s;
+    R.Vout = U; R.Hout = Us; R.ldh = hilo_ld(r);
+    HIP_TRY(launch_lora_rows(R, st, KID_LORA_DOWN));
+    return QLORA_OK;
+  }
   SkinnyParams S = skinny(X, K, true, T, K, r, s, r, OUT_ROWS_HILO, part);
   skinny_q(S, A, K, r, Q_CONTIG);
   S.Vout = U; S.Hout = Us; S.ldh = hilo_ld(r);
@@ -221,7 +234,7 @@ int qlora_linear_fwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8
   if (!packed || !codes || !consts) return QLORA_ERR_NULL;
   if (T > 0 && (!X || !Y)) return QLORA_ERR_NULL;
   if (r > 0 && (!A || !B)) return QLORA_ERR_NULL;
-  if (!aligned16(packed) || !aligned16(X) || !aligned16(A)) return QLORA_ERR_UNSUPPORTED;
+  if (!aligned16(packed) || !aligned16(X) || !aligned16(A) || !aligned16(B)) return QLORA_ERR_UNSUPPORTED;
   const size_t need = plan_fwd(d, T, r, nullptr).bytes;
   if (need > 0 && (!workspace || workspace_bytes < need)) return QLORA_ERR_WORKSPACE;
   if (T == 0) return QLORA_OK;
@@ -260,7 +273,8 @@ int qlora_linear_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8
   if (!packed || !codes || !consts) return QLORA_ERR_NULL;
   if (T > 0 && (!X || !dY)) return QLORA_ERR_NULL;
   if (r > 0 && (!A || !B || !dA || !dB)) return QLORA_ERR_NULL;
-  if (!aligned16(packed) || !aligned16(X) || !aligned16(dY) || !aligned16(A)) return QLORA_ERR_UNSUPPORTED;
+  if (!aligned16(packed) || !aligned16(X) || !aligned16(dY) || !aligned16(A) || !aligned16(B))
+    return QLORA_ERR_UNSUPPORTED;
   const size_t need = plan_bwd(d, T, r, nullptr).bytes;
   if (need > 0 && (!workspace || workspace_bytes < need)) return QLORA_ERR_WORKSPACE;
 
@@ -285,11 +299,20 @@ int qlora_linear_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8
     }
     // G = dY B -> hi/lo of s*G (feeds the dX tail and dA); the same launch
     // turns the given U into the hi/lo pair of s*U
-    SkinnyParams S = skinny(dY, N, true, T, N, r, s, r, OUT_ROWS_HILO, w.part);
-    skinny_q(S, B, r, r, Q_STRIDED);
-    S.Hout = w.Gs; S.ldh = ldh;
-    if (U_in) { S.Uc = U_in; S.Ucs = w.Us; }
-    HIP_TRY(launch_skinny(S, s_, KID_LORA_G));
+    if (lora_rows_ok(T, r)) {
+      RowsParams R{};
+      R.P = dY; R.ldp = N; R.M = T; R.D = N;
+      R.Q = B; R.ldq = r; R.q_strided = 1; R.r = r; R.s = s;
+      R.Hout = w.Gs; R.ldh = ldh;
+      if (U_in) { R.Uc = U_in; R.Ucs = w.Us; }
+      HIP_TRY(launch_lora_rows(R, s_, KID_LORA_G));
+    } else {
+      SkinnyParams S = skinny(dY, N, true, T, N, r, s, r, OUT_ROWS_HILO, w.part);
+      skinny_q(S, B, r, r, Q_STRIDED);
+      S.Hout = w.Gs; S.ldh = ldh;
+      if (U_in) { S.Uc = U_in; S.Ucs = w.Us; }
+      HIP_TRY(launch_skinny(S, s_, KID_LORA_G));
+    }
   }
   if (dX) {
     // dX = dY W_hat + (s G) A: the contraction runs over d_out, the rows of W
@@ -304,13 +327,21 @@ int qlora_linear_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8
   if (r > 0) {
     // one launch for both adapter gradients, contractions over the hi/lo columns:
     // dA = (s G)^T X -> [r][d_in]; dB = dY^T (s U) -> [d_out][r]
-    SkinnyParams Sa = skinny(X, K, false, K, T, r, s, 2 * r, OUT_PAIRS_T, w.part);
-    skinny_q(Sa, w.Gs, ldh, 2 * (int64_t)r, Q_STRIDED);
-    Sa.Fout = dA;
-    SkinnyParams Sb = skinny(dY, N, false, N, T, r, s, 2 * r, OUT_PAIRS, w.part2);
-    skinny_q(Sb, w.Us, ldh, 2 * (int64_t)r, Q_STRIDED);
-    Sb.Fout = dB;
-    HIP_TRY(launch_skinny_pair(Sa, Sb, s_, KID_LORA_DA));
+    if (lora_stream_ok(r)) {
+      ColsBatch C{};
+      C.p[0] = ColsParams{X, K, K, w.Gs, ldh, T, r, 1, dA};
+      C.p[1] = ColsParams{dY, N, N, w.Us, ldh, T, r, 0, dB};
+      C.n = 2;
+      HIP_TRY(launch_lora_cols(C, s_, KID_LORA_DA));
+    } else {
+      SkinnyParams Sa = skinny(X, K, false, K, T, r, s, 2 * r, OUT_PAIRS_T, w.part);
+      skinny_q(Sa, w.Gs, ldh, 2 * (int64_t)r, Q_STRIDED);
+      Sa.Fout = dA;
+      SkinnyParams Sb = skinny(dY, N, false, N, T, r, s, 2 * r, OUT_PAIRS, w.part2);
+      skinny_q(Sb, w.Us, ldh, 2 * (int64_t)r, Q_STRIDED);
+      Sb.Fout = dB;
+      HIP_TRY(launch_skinny_pair(Sa, Sb, s_, KID_LORA_DA));
+    }
   }
   return QLORA_OK;
 }

@@ -163,6 +163,11 @@ CASES = [
     (256, 512, 7, 16, 32.0, 8),       # few-token path, 5..8 tokens
     (128, 448, 12, 8, 16.0, 9),       # few-token path, code runs not 4-byte aligned (K/64 = 7)
     (192, 1024, 16, 64, 16.0, 10),    # few-token path, two stages per contraction slice
+    # streaming adapter products (many tokens): ragged token counts, contractions
+    # ending in half a 128-chunk, ranks 8 / 24 / 64
+    (192, 320, 523, 8, 16.0, 11),
+    (256, 192, 600, 24, 8.0, 12),
+    (320, 448, 1031, 64, 16.0, 13),
 ]
 
 
@@ -182,8 +187,10 @@ def test_fwd_bwd_parity(d_out, d_in, T, r, alpha, seed):
         assert v <= TOL, (k, v)
 
 
-def test_bwd_recomputes_u_when_not_saved():
-    inp = workloads.layer_inputs(256, 320, 33, 8, seed=8)
+@pytest.mark.parametrize("T", [33, 700])
+def test_bwd_recomputes_u_when_not_saved(T):
+    # 33 tokens: split-contraction adapter kernels; 700: streaming ones
+    inp = workloads.layer_inputs(256, 320, T, 8, seed=8)
     a = gpu_layer(inp, 8, 16.0, pass_u=True)
     b = gpu_layer(inp, 8, 16.0, pass_u=False)
     for k in ("dX", "dA", "dB"):
