@@ -421,7 +421,7 @@ __device__ __forceinline__ void fused_body(const FusedParams& P) {
   auto a_stage = [&](uint32_t s) { return lds + (s % 3) * G::A_BYTES; };
   auto b_stage = [&](uint32_t s) { return reinterpret_cast<uint16_t*>(lds + G::B_OFF + (s & 1) * G::B_BYTES); };
 
-  // Both roles pass the same sequence of barriers: 1 + nsteps, then 1.
+  // Both roles pass the same sequence of barriers: 1 + nsteps, then 2.
   if (threadIdx.x < 256) {
     const int lane = threadIdx.x & 63;
     const int cw = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -501,7 +501,10 @@ __device__ __forceinline__ void fused_body(const FusedParams& P) {
       order_slice();
       cur = nxt;
     }
+    // the last copies (into stages no one reads) land before anyone writes
+    // the output tile over the A stages: every wave's own, then a barrier
     wait_copies<0>();
+    lds_barrier();
     // epilogue: bf16 tile into LDS (over the A stages, no longer read)
     uint16_t* ct = reinterpret_cast<uint16_t*>(lds);
     const int wn = cw & 1;
@@ -552,7 +555,8 @@ __device__ __forceinline__ void fused_body(const FusedParams& P) {
       if (h + 1 < nsteps) tail_b(h + 1);
       lds_barrier();
     }
-    lds_barrier();
+    lds_barrier();  // the multiplying waves' last copies have landed
+    lds_barrier();  // the output tile is in LDS
   }
 
   // coalesced 16-byte stores of the bf16 tile, all eight waves
