@@ -136,8 +136,6 @@ def decode_section(steps, warmup):
     copies = 5
     for T in (1, 4, 16):
         for lin in workloads.decode_70b(T):
-            if T == 1:
-                pass
             inp = workloads.layer_inputs(lin.d_out, lin.d_in, T, lin.r, lin.seed, with_dy=False)
             W = torch.from_numpy(inp["W"]).cuda()
             pk, cd, cs = q.qlora_quantize_nf4(W)

@@ -47,7 +47,10 @@
  *   call that fails validation has no side effect.  QLORA_ERR_HIP reports a
  *   failed launch (hipGetLastError after enqueueing).
  * - W, packed, X, dY, A and B must be 16-byte aligned (QLORA_ERR_UNSUPPORTED
- *   otherwise); other pointers need only their element alignment.
+ *   otherwise); other pointers need only their element alignment.  A forward
+ *   call with at most 16 tokens takes the weight-streaming kernel when codes
+ *   is 16-byte aligned and K/64 is at most about 2000, else the tiled kernel
+ *   (same results within the accuracy stated below).
  * - Inputs must be finite; results for NaN/Inf inputs are unspecified.
  * - Hot-path preconditions: blocksize == 64, dq_blocksize == 256,
  *   d_in % 64 == 0, d_out % 64 == 0, 0 <= r <= 128, T >= 0 (T == 0 is a

@@ -14,10 +14,10 @@
 namespace qlora {
 hipError_t launch_nf4_quantize(const float* W, uint8_t* packed, uint8_t* codes, float* consts,
                                int64_t numel, hipStream_t stream);
-int decode_splits(int64_t N, int64_t K);
+bool decode_supported(int64_t N, int64_t K);
 hipError_t launch_decode(const uint8_t* packed, const uint8_t* codes, const float* consts, const uint16_t* X,
                          int64_t T, int64_t N, int64_t K, const uint16_t* Us, int64_t ldh, const uint16_t* B,
-                         int r, int nsplit, float* part, uint16_t* Y, hipStream_t stream);
+                         int r, uint16_t* Y, hipStream_t stream);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
 }  // namespace qlora
 
@@ -67,11 +67,9 @@ size_t skinny_part_bytes(int64_t mrows, int64_t clen, int64_t cols) {
 }
 
 struct FwdWs {
-  int nsplit = 1;  // contraction slices of the few-token kernel
   float* part = nullptr;
   float* U = nullptr;
   uint16_t* Us = nullptr;
-  float* dec = nullptr;
   size_t bytes = 0;
 };
 
@@ -83,10 +81,6 @@ FwdWs plan_fwd(const qlora_nf4_desc* d, int64_t T, int32_t r, void* ws) {
     if (!lora_rows_ok(T, r)) w.part = static_cast<float*>(c.take(skinny_part_bytes(T, K, r)));
     w.U = static_cast<float*>(c.take((size_t)T * r * 4));
     w.Us = static_cast<uint16_t*>(c.take((size_t)T * hilo_ld(r) * 2));
-  }
-  if (T > 0 && T <= kDecodeMaxT) {
-    w.nsplit = decode_splits(N, K);
-    if (w.nsplit > 1) w.dec = static_cast<float*>(c.take((size_t)w.nsplit * T * N * 4));
   }
   w.bytes = c.off;
   return w;
@@ -249,8 +243,8 @@ int qlora_linear_fwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8
     const int e = lora_down(X, A, T, K, r, s, w.part, U, w.Us, s_);
     if (e) return e;
   }
-  if (T <= kDecodeMaxT) {
-    HIP_TRY(launch_decode(packed, codes, consts, X, T, N, K, w.Us, hilo_ld(r), B, r, w.nsplit, w.dec, Y, s_));
+  if (T <= kDecodeMaxT && decode_supported(N, K) && aligned16(codes)) {
+    HIP_TRY(launch_decode(packed, codes, consts, X, T, N, K, w.Us, hilo_ld(r), B, r, Y, s_));
     return QLORA_OK;
   }
   FusedParams fp{};

@@ -4,35 +4,42 @@
 // nibbles and scale codes from HBM ("QLoRA技术从入门到精通" §3(2): the 4-bit
 // weight is restored block by block at compute time and discarded).
 //
-// Workgroup: 4 waves, 64 weight rows, one slice of the contraction, walked in
-// stages of 8 blocks (512 weights per row).  A stage is loaded with long runs
-// per row -- each load instruction covers 4 rows x 256 bytes of packed data,
-// one token row of X (1 KB) or the 8 scale codes of 16 rows -- into registers
-// two or three stages ahead of use (fewer tokens, fewer X registers, deeper),
-// written to one of two LDS buffers one stage ahead,
-// and multiplied from LDS.  (Spreading each load instruction over 32 rows of
-// 32 bytes, the MFMA operand layout, reads HBM at about half the rate.)
+// Work split: the rows are cut into 16-row tiles and every workgroup owns a
+// run of NTW consecutive tiles over the whole contraction (NTW = N/16/256
+// rounded up, so the weight shapes of a transformer give every CU the same
+// share and no partial sums leave the workgroup).  The workgroup's DW waves
+// split the contraction into chunks of 128 weights (wave w: chunks w, w+DW, ...)
+// and add their tiles in LDS in a fixed order at the end.
 //
-// Restore: a packed byte holding levels (q_hi, q_lo) is looked up in a
-// 256-entry LDS table of the pairs bf16(T[q_hi]), bf16(T[q_lo]) in element
-// order.  The block scale is applied to the MFMA result instead: the four
-// v_mfma_f32_32x32x16_bf16 of one block of 32 rows cover exactly that block's
-// 64 weights of each row, so their sum is multiplied by the row's restored
-// scale s' = fl32(code) * fl32(c_g / 255) and added to an fp32 accumulator.
+// Loads: per tile, one 16-byte load per lane covers 16 rows x 64 contiguous
+// bytes of a chunk; it goes to registers, and is issued again for the wave's
+// next chunk as soon as the tile has been restored, so a wave keeps about one
+// chunk per tile in flight while it computes.  The chunk's X rows (256 bytes
+// each) come densely from L2, one 16-byte load per lane per 4 token rows, and
+// reach the MFMA layout through the wave's LDS slot.  The workgroup's scale
+// codes (one contiguous run) and the ratios c_g / 255 of their groups are
+// copied to LDS once, while the table is built, so the loop reads a chunk's two
+// codes with one LDS read.
+//
+// MFMA v_mfma_f32_16x16x32_bf16, A = X (16 token rows), B = restored weights
+// (16 rows): lane l holds row l%16 and contraction slots 8(l/16) .. +7.  One
+// MFMA covers half a 64-weight block (32 weights), so the block's two MFMA
+// results form the block's own sum, which is multiplied by the row's restored
+// scale s' = fl32(code) * fl32(c_g / 255) and added to the fp32 accumulator.
 // (This differs from rounding T[q] * s' to bf16 by at most one bf16 rounding
-// of each weight.)  fl32(c_g / 255) is computed once per row and group, into
-// an LDS table, before the stages start.  MFMA operands: X is the 32 x 16 A
-// operand (token rows >= T read a zero row), the restored weight the 16 x 32
-// B operand; in MFMA j of a block, lane group g supplies weights 32g+8j..+8.
-// Wave w multiplies blocks 2w and 2w+1 of every stage for all 64 rows.
+// of each weight.)  The loaded 16 bytes of lane group g are bytes 16g.. of the
+// row chunk; a 4 x 4 transpose of the four dwords across the lane groups
+// (v_permlane32_swap, v_permlane16_swap) gives group g dword 4j + g for half
+// block j, i.e. contraction slots 64(j/2) + 32(j%2) + 8g.
 //
-// Rank-r term: the workgroups of the first contraction slice add
-// s (X A^T) B^T through the same MFMA, over the 2r hi/lo columns of s U
-// (zero-padded to a multiple of 64), as the dense kernels do.
+// Restore: a packed byte (levels q_hi, q_lo) indexes a 256-entry table of the
+// pairs bf16(T[q_hi]), bf16(T[q_lo]) in element order.  Each lane has a private
+// copy of the table in its own LDS bank (entry v of lane L at dword 64v + L,
+// 64 KB at LDS offset 0), so the 64 lanes of a lookup never conflict, and the
+// address (v << 8) | 4L is one v_perm_b32 of the packed dword and 4L.
 //
-// The four waves' sums are added in LDS in a fixed order.  One slice: bf16 Y
-// is written directly; several slices: fp32 partials, summed in slice order by
-// k_decode_reduce.
+// Rank-r term: added per tile after the sum, s (X A^T) B^T through the same
+// MFMA over the 2r hi/lo columns of s U (zero-padded to a multiple of 64).
 #include "common.hpp"
 #include "trace.hpp"
 
@@ -40,58 +47,24 @@ namespace qlora {
 
 namespace {
 
-constexpr int ROWS = 64;        // weight rows per workgroup (two 32-row MFMA tiles)
-constexpr int WAVES = 4;
-constexpr int SB = 8;           // blocks per stage
-constexpr int MAXG = 5;         // groups of 256 blocks a row can touch inside one slice
-constexpr int WLD = SB * 32 + 16;       // LDS row of packed bytes (256 + 16 pad)
-constexpr int XLD = SB * 64 * 2 + 16;   // LDS row of X bytes (1024 + 16 pad)
-constexpr int XROWS = 17;               // 16 token rows + one zero row
+constexpr int LUT_DWORDS = 256 * 64;      // 64 KB
+constexpr int CODES_BYTES = 32 * 1024;    // the workgroup's scale codes and group ratios
+constexpr uint32_t kOob = 0x80000000u;    // buffer offset past every range used here: loads read zero
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 struct DecodeParams {
   const uint8_t* packed;
   const uint8_t* codes;
   const float* consts;
-  const uint16_t* X;
+  const uint16_t* X;   // [T][K]
   int64_t T, N, K;
   const uint16_t* Us;  // hi/lo pair of s*U, [T][ldh], zero past 2r (unused when r == 0)
   int64_t ldh;
   const uint16_t* B;   // [N][r]
   int r;
-  int nsplit;
-  int64_t per;         // blocks per contraction slice (a multiple of SB)
-  uint16_t* Y;         // [T][N] (one slice)
-  float* part;         // [nsplit][T][N] (several slices)
+  uint16_t* Y;         // [T][N]
   float level[16];
-};
-
-// One stage's loads for one wave: packed bytes of 16 rows (4 per load), XR
-// token rows of X (rows >= T read as zero), the stage's scale codes of 16 rows.
-template <int XR>
-struct StageRegs {
-  u32x4_t w[4];
-  u32x4_t x[XR];
-  u32x2_t code;
-};
-
-struct Cursor {
-  __amdgpu_buffer_rsrc_t rw, rx, rc;
-  uint32_t woff;       // this lane's packed-byte offset for stage 0, load 0
-  uint32_t wrow_step;  // bytes between the loads' row groups (4 rows)
-  uint32_t xoff;       // this lane's X byte offset for stage 0, token row = wave
-  uint32_t xrow_step;  // bytes between the token rows a wave loads (4 rows apart)
-  uint32_t coff;       // this lane's code offset for stage 0
-};
-
-struct Smem {
-  uint8_t w[2][ROWS * WLD];       // packed bytes, [row][256 B]
-  uint8_t x[2][XROWS * XLD];      // X, [token][1 KB]; row 16 stays zero
-  uint8_t code[2][ROWS * SB];     // scale codes, [row][block]
-  float ratio[ROWS][MAXG];        // fl32(c_g / 255) of the row's groups in this slice
-  uint32_t lut[256];
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, int64_t bytes) {
@@ -99,273 +72,364 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, int64_t by
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, n, 0x00020000);
 }
 
-// CODES4: the rows' code runs start on 4-byte boundaries (K % 256 == 0), so a
-// stage's 8 codes of a row are one 8-byte load; otherwise eight byte loads.
-template <bool CODES4, int XR>
-__device__ __forceinline__ void load_stage(StageRegs<XR>& R, const Cursor& c, uint32_t blk0) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    R.w[i] = __builtin_amdgcn_raw_buffer_load_b128(c.rw, c.woff + i * c.wrow_step, blk0 * 32u, 0);
-#pragma unroll
-  for (int i = 0; i < XR; ++i)
-    R.x[i] = __builtin_amdgcn_raw_buffer_load_b128(c.rx, c.xoff + i * c.xrow_step, blk0 * 128u, 0);
-  if (CODES4) {
-    R.code = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(c.rc, c.coff, blk0, 0));
-  } else {
-    uint32_t b[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) b[q] = __builtin_amdgcn_raw_buffer_load_b8(c.rc, c.coff + q, blk0, 0);
-    R.code = u32x2_t{b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24), b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24)};
-  }
-}
+// One chunk's loads of one wave: X (XQ loads of 4 token rows x 256 bytes) and
+// the packed 16 bytes of each tile.
+template <int NTW, int XQ>
+struct ChunkRegs {
+  u32x4_t x[XQ];
+  u32x4_t w[NTW];
+};
 
-// Registers -> LDS buffer: this wave's 16 rows of packed bytes, its XR token
-// rows of X (wave, wave + 4, ...) and the codes of its 16 rows.
-template <int XR>
-__device__ __forceinline__ void store_stage(const StageRegs<XR>& R, Smem& sm, int buf, int wave, int lane) {
-  // load i holds rows wave*16 + 4i + lane/16, bytes (lane%16)*16
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = wave * 16 + 4 * i + (lane >> 4);
-    *reinterpret_cast<u32x4_t*>(&sm.w[buf][row * WLD + (lane & 15) * 16]) = R.w[i];
-  }
-#pragma unroll
-  for (int i = 0; i < XR; ++i) {
-    const int t = wave + 4 * i;
-    *reinterpret_cast<u32x4_t*>(&sm.x[buf][t * XLD + lane * 16]) = R.x[i];
-  }
-  if (lane < 16) *reinterpret_cast<u32x2_t*>(&sm.code[buf][(wave * 16 + lane) * SB]) = R.code;
-}
-
-__device__ __forceinline__ bf16x8_t lookup8(uint32_t d, const uint32_t* __restrict__ lut) {
+// Four table lookups of the bytes of packed dword d -> 8 restored bf16 in element order.
+__device__ __forceinline__ bf16x8_t lookup8(uint32_t d, uint32_t lanebase) {
+  typedef __attribute__((address_space(3))) const uint32_t lds_cu32_t;
   u32x4_t o;
-  o.x = lut[d & 0xFFu];
-  o.y = lut[(d >> 8) & 0xFFu];
-  o.z = lut[(d >> 16) & 0xFFu];
-  o.w = lut[d >> 24];
+  o.x = *reinterpret_cast<lds_cu32_t*>((uintptr_t)__builtin_amdgcn_perm(d, lanebase, 0x0C0C0400u));
+  o.y = *reinterpret_cast<lds_cu32_t*>((uintptr_t)__builtin_amdgcn_perm(d, lanebase, 0x0C0C0500u));
+  o.z = *reinterpret_cast<lds_cu32_t*>((uintptr_t)__builtin_amdgcn_perm(d, lanebase, 0x0C0C0600u));
+  o.w = *reinterpret_cast<lds_cu32_t*>((uintptr_t)__builtin_amdgcn_perm(d, lanebase, 0x0C0C0700u));
   return __builtin_bit_cast(bf16x8_t, o);
 }
 
-// XR: token rows of X each wave stages (X holds up to 4 * XR tokens);
-// DEPTH: stages loaded ahead of use (register sets: DEPTH + 1).
-template <bool CODES4, int XR, int DEPTH>
-__global__ __launch_bounds__(256) void k_decode(DecodeParams P) {
-  __shared__ __attribute__((aligned(16))) Smem sm;
+// 4 x 4 transpose of dwords across the four 16-lane groups: afterwards group
+// g's register j holds what group j's register g held.
+__device__ __forceinline__ void transpose4(uint32_t& a, uint32_t& b, uint32_t& c, uint32_t& d) {
+  const auto p = __builtin_amdgcn_permlane32_swap(a, c, false, false);
+  const auto q = __builtin_amdgcn_permlane32_swap(b, d, false, false);
+  const auto s = __builtin_amdgcn_permlane16_swap(p[0], q[0], false, false);
+  const auto t = __builtin_amdgcn_permlane16_swap(p[1], q[1], false, false);
+  a = s[0]; b = s[1]; c = t[0]; d = t[1];
+}
+
+__device__ __forceinline__ f32x4_t mfma(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// DW: waves per workgroup (8 or 16).  NTW: 16-row tiles per workgroup.  XQ: X
+// loads per chunk (1 for T <= 4, else 4).  CODES2: K/64 is even, so a chunk's
+// two codes are one aligned 2-byte LDS read and its two blocks (an even block
+// index and the next) never straddle a group of 256 blocks.
+template <int DW, int NTW, int XQ, bool CODES2>
+__global__ __launch_bounds__(DW * 64) void k_decode(DecodeParams P) {
+  constexpr int DT = DW * 64;
+  // chunks in flight per wave besides the reissued tiles (registers: 128 per
+  // lane with 16 waves, 256 with 8)
+  constexpr int PD = DW == 16 ? (NTW <= 2 ? 2 : 1) : (NTW <= 2 ? 3 : (NTW <= 5 ? 2 : 1));
+  constexpr int XSW = XQ * 1024;          // a wave's X slot: 4 XQ token rows x 256 bytes
+  constexpr int RED = 8 * NTW * 1024;     // eight waves' partial tiles, after the loop
+  constexpr int REGION = CODES_BYTES + DW * XSW > RED ? CODES_BYTES + DW * XSW : RED;
+  // the table must sit at LDS offset 0 (its addresses are formed without a base):
+  // this is the kernel's only LDS variable
+  __shared__ __attribute__((aligned(16))) uint32_t lds[LUT_DWORDS + REGION / 4];
+  uint32_t* lut = lds;
+  uint8_t* aux = reinterpret_cast<uint8_t*>(lds + LUT_DWORDS);
+  float* red = reinterpret_cast<float*>(aux);  // [wave][tile][v][lane]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nl = lane & 31, g = lane >> 5;
-  const int64_t n0 = (int64_t)blockIdx.x * ROWS;
-  const int z = blockIdx.y;
-  const int64_t nbk = P.K / 64;
-  const int64_t kb = (int64_t)z * P.per;
-  const int64_t ke = kb + P.per < nbk ? kb + P.per : nbk;
-  const int nst = kb < ke ? (int)((ke - kb + SB - 1) / SB) : 0;
+  const int i16 = lane & 15, g = lane >> 4;
+  const uint32_t lanebase = (uint32_t)lane * 4u;
+  // every byte offset below fits 32 bits: the packed weight is below 2 GiB
+  const int T = (int)P.T, K = (int)P.K;
+  const int ntiles = (int)(P.N / 16);
+  const int nt0 = (int)blockIdx.x * NTW;
+  const int nbk = K / 64;
+  const int nch = (K + 127) / 128;
+  const int nmine = nch > wave ? (nch - wave + DW - 1) / DW : 0;
+  const int iters = (nmine + PD - 1) / PD * PD;
 
-  // byte table, zero X rows, per-row ratios c_g / 255 of the groups this slice touches
-  sm.lut[tid] = pack_bf16x2(P.level[tid >> 4], P.level[tid & 15]);
-  for (int i = tid; i < XLD / 4; i += 256) {
-    reinterpret_cast<uint32_t*>(&sm.x[0][16 * XLD])[i] = 0u;
-    reinterpret_cast<uint32_t*>(&sm.x[1][16 * XLD])[i] = 0u;
-  }
-  const int64_t ngroups = (P.N * nbk + 255) / 256;
-  for (int i = tid; i < ROWS * MAXG; i += 256) {
-    const int row = i / MAXG, k = i % MAXG;
-    const int64_t gi = (((n0 + row) * nbk + kb) >> 8) + k;
-    sm.ratio[row][k] = gi < ngroups ? P.consts[gi] / 255.0f : 0.0f;
-  }
+  const __amdgpu_buffer_rsrc_t rw = rsrc(P.packed, P.N * P.K / 2);
+  const __amdgpu_buffer_rsrc_t rx = rsrc(P.X, P.T * P.K * 2);
+  const __amdgpu_buffer_rsrc_t rc = rsrc(P.codes, P.N * nbk);
+  const __amdgpu_buffer_rsrc_t rk = rsrc(P.consts, ((P.N * nbk + 255) / 256) * 4);
 
-  Cursor c;
-  c.rw = rsrc(P.packed, P.N * P.K / 2);
-  c.rx = rsrc(P.X, P.T * P.K * 2);
-  c.rc = rsrc(P.codes, P.N * nbk);
-  c.woff = (uint32_t)((n0 + wave * 16 + (lane >> 4)) * (P.K / 2) + (lane & 15) * 16);
-  c.wrow_step = (uint32_t)(4 * (P.K / 2));
-  c.xoff = (uint32_t)((int64_t)wave * P.K * 2 + lane * 16);  // token rows >= T lie past the end: zero
-  c.xrow_step = (uint32_t)(4 * P.K * 2);
-  c.coff = (uint32_t)((n0 + wave * 16 + (lane & 15)) * nbk);
-
-  float acc[2][8];
+  // the workgroup's codes: rows nt0*16 .. are one contiguous, 16-byte aligned
+  // run of 16*NTW*nbk bytes in memory (rows past N read zero); in LDS each row
+  // starts at a multiple of rs bytes, rs/4 odd, so that 16 consecutive rows
+  // read at one column fall in distinct banks.  Then the ratios c_g / 255 of
+  // the groups of 256 blocks the run spans.
+  const uint32_t cfirst = (uint32_t)nt0 * 16u * (uint32_t)nbk;
+  const uint32_t cbytes = 16u * NTW * (uint32_t)nbk;
+  const uint32_t rs = 4u * (((uint32_t)(nbk + 3) >> 2) | 1u);
+  const uint32_t g_lo = cfirst >> 8;
+  const uint32_t ngr = ((cfirst + cbytes - 1u) >> 8) - g_lo + 1u;
+  float* ratio = reinterpret_cast<float*>(aux + ((16u * NTW * rs + 15u) & ~15u));
+  constexpr int CQ = CODES_BYTES / 16 / DT;
+  u32x4_t cv[CQ];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int v = 0; v < 8; ++v) acc[i][v] = 0.0f;
+  for (int q = 0; q < CQ; ++q) {
+    const uint32_t o = (uint32_t)(tid + q * DT) * 16u;
+    cv[q] = __builtin_amdgcn_raw_buffer_load_b128(rc, o < cbytes ? cfirst + o : kOob, 0, 0);
+  }
+  const float cg = __builtin_bit_cast(
+      float, __builtin_amdgcn_raw_buffer_load_b32(rk, (uint32_t)tid < ngr ? (g_lo + (uint32_t)tid) * 4u : kOob, 0, 0));
 
-  // stage s covers blocks kb + s*SB ...; loads outside [0, nst) repeat an end stage
-  auto blk_of = [&](int s) {
-    const int j = s < 0 ? 0 : (s < nst ? s : nst - 1);
-    return (uint32_t)(kb + (int64_t)SB * j);
+  // this lane's row of tile i is n0 + 16 i
+  const uint32_t n0 = (uint32_t)nt0 * 16u + (uint32_t)i16;
+  const uint32_t wbase = n0 * (uint32_t)(K / 2) + 16u * (uint32_t)g;  // packed byte of tile 0, chunk 0
+  const uint32_t wtile = 16u * (uint32_t)(K / 2);                      // packed bytes per tile
+  // X load q: lane l holds piece l%16 (16 bytes) of token row 4q + l/16 of the chunk
+  const int xp = lane & 15;
+  const uint32_t xbase = (uint32_t)g * (uint32_t)(K * 2) + 16u * (uint32_t)xp;
+  // X slot: piece p of token row t at piece position p ^ t (conflict-free reads);
+  // with one load per chunk only rows 0..3 exist, and lanes of rows >= 4 read
+  // row i16 % 4 (MFMA rows are independent and token rows >= T are never stored)
+  uint8_t* xs = aux + CODES_BYTES + wave * XSW;
+  const int xrow = XQ == 1 ? (i16 & 3) : i16;
+
+  auto issue_x = [&](ChunkRegs<NTW, XQ>& R, int k) {
+    const int ch = wave + DW * k;
+    const bool in = ch < nch && ch * 128 + 8 * xp < K;
+#pragma unroll
+    for (int q = 0; q < XQ; ++q) {
+      const bool tin = in && 4 * q + g < T;
+      R.x[q] = __builtin_amdgcn_raw_buffer_load_b128(
+          rx, tin ? xbase + (uint32_t)(4 * q) * (uint32_t)(K * 2) + (uint32_t)ch * 256u : kOob, 0, 0);
+    }
   };
-  auto compute = [&](int buf, uint32_t blk0) {
+  auto issue_w = [&](ChunkRegs<NTW, XQ>& R, int i, int k) {
+    const int ch = wave + DW * k;
+    const bool in = ch < nch && ch * 64 + 16 * g < K / 2 && nt0 + i < ntiles;
+    R.w[i] = __builtin_amdgcn_raw_buffer_load_b128(
+        rw, in ? wbase + (uint32_t)i * wtile + (uint32_t)ch * 64u : kOob, 0, 0);
+  };
+
+  // the first chunks' loads go out before the table is built
+  ChunkRegs<NTW, XQ> R[PD];
 #pragma unroll
-    for (int bb = 0; bb < 2; ++bb) {
-      const int b = 2 * wave + bb;                  // block inside the stage
-      const uint32_t blk = blk0 + (uint32_t)b;      // block inside the row
-      const bool live = blk < (uint32_t)ke;         // blocks past the slice count zero
-      const int t = nl < P.T ? nl : 16;  // rows 4*XR .. 15 are never written: T <= 4*XR
-      bf16x8_t xf[4];
+  for (int sp = 0; sp < PD; ++sp) {
+    issue_x(R[sp], sp);
+#pragma unroll
+    for (int i = 0; i < NTW; ++i) issue_w(R[sp], i, sp);
+  }
+
+  // byte table: entry v = (bf16(T[v >> 4]), bf16(T[v & 15])), one copy per
+  // lane bank; a wave writes whole entries, so the levels are read with scalar
+  // loads (a vector load here would make the waits below drain the loads
+  // already in flight)
+  for (int v = wave; v < 256; v += DW)
+    lut[v * 64 + lane] = pack_bf16x2(P.level[v >> 4], P.level[v & 15]);
+#pragma unroll
+  for (int q = 0; q < CQ; ++q) {
+    const uint32_t o = (uint32_t)(tid + q * DT) * 16u;
+    if (o < cbytes) {
+      uint32_t row = o / (uint32_t)nbk, col = o - row * (uint32_t)nbk;
+      const uint32_t w4[4] = {cv[q].x, cv[q].y, cv[q].z, cv[q].w};
+      if ((nbk & 3) == 0) {  // dwords never straddle rows
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          *reinterpret_cast<uint32_t*>(aux + row * rs + col) = w4[d];
+          col += 4u;
+          if (col >= (uint32_t)nbk) { col -= (uint32_t)nbk; ++row; }
+        }
+      } else {
+#pragma unroll
+        for (int b = 0; b < 16; ++b) {
+          aux[row * rs + col] = (uint8_t)(w4[b >> 2] >> (8 * (b & 3)));
+          if (++col == (uint32_t)nbk) { col = 0u; ++row; }
+        }
+      }
+    }
+  }
+  if ((uint32_t)tid < ngr) ratio[tid] = restored_scale(1u, cg);  // fl32(c_g / 255)
+
+  f32x4_t acc[NTW];
+#pragma unroll
+  for (int i = 0; i < NTW; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  __syncthreads();  // the table, codes and ratios are in place
+
+  for (int k = 0; k < iters; k += PD) {
+#pragma unroll
+    for (int sp = 0; sp < PD; ++sp) {
+      const int ch = wave + DW * (k + sp);
+      const bool chin = ch < nch;
+      const int chc = chin ? ch : 0;
+      // X through the wave's slot into the MFMA layout; the slot's reads of the
+      // previous chunk precede these writes in the wave's LDS order
+#pragma unroll
+      for (int q = 0; q < XQ; ++q) {
+        const int t = 4 * q + g;
+        *reinterpret_cast<u32x4_t*>(xs + t * 256 + ((xp ^ t) & 15) * 16) = R[sp].x[q];
+      }
+      bf16x8_t xa[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        xf[j] = *reinterpret_cast<const bf16x8_t*>(&sm.x[buf][t * XLD + (64 * b + 32 * g + 8 * j) * 2]);
+        xa[j] = *reinterpret_cast<const bf16x8_t*>(xs + xrow * 256 + (((4 * j + g) ^ xrow) & 15) * 16);
+      issue_x(R[sp], k + sp + PD);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int row = 32 * i + nl;
-        const u32x4_t wv = *reinterpret_cast<const u32x4_t*>(&sm.w[buf][row * WLD + 32 * b + 16 * g]);
-        const uint32_t code = sm.code[buf][row * SB + b];
-        const int64_t rb = (n0 + row) * nbk;
-        int gk = (int)(((rb + blk) >> 8) - ((rb + kb) >> 8));
-        gk = gk < MAXG ? gk : MAXG - 1;
-        const float sc = live ? (float)code * sm.ratio[row][gk] : 0.0f;
-        f32x16_t cblk = {};
+      for (int i = 0; i < NTW; ++i) {
+        uint32_t d0 = R[sp].w[i].x, d1 = R[sp].w[i].y, d2 = R[sp].w[i].z, d3 = R[sp].w[i].w;
+        transpose4(d0, d1, d2, d3);  // dj: half block j of this lane group
+        // s' = fl32(code) * fl32(c_g / 255) of the chunk's two blocks of this
+        // lane's row (zero for a chunk past the row's end, whose weights read zero)
+        const uint32_t row = (uint32_t)(16 * i + i16);
+        const uint32_t cl = row * rs + (uint32_t)(2 * chc);                     // code byte in LDS
+        const uint32_t gb = cfirst + row * (uint32_t)nbk + (uint32_t)(2 * chc);  // its block index
+        float s0, s1;
+        if (CODES2) {
+          const uint32_t c2 = *reinterpret_cast<const uint16_t*>(aux + cl);
+          const float rt = ratio[(gb >> 8) - g_lo];
+          s0 = (float)(c2 & 0xFFu) * rt;
+          s1 = (float)(c2 >> 8) * rt;
+        } else {
+          const bool two = 2 * chc + 1 < nbk;
+          s0 = (float)aux[cl] * ratio[(gb >> 8) - g_lo];
+          s1 = two ? (float)aux[cl + 1u] * ratio[((gb + 1u) >> 8) - g_lo] : 0.f;
+        }
+        s0 = chin ? s0 : 0.f;
+        s1 = chin ? s1 : 0.f;
+        f32x4_t c = mfma(xa[0], lookup8(d0, lanebase), f32x4_t{0.f, 0.f, 0.f, 0.f});
+        c = mfma(xa[1], lookup8(d1, lanebase), c);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          cblk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf[j], lookup8(wv[j], sm.lut), cblk, 0, 0, 0);
+        for (int v = 0; v < 4; ++v) acc[i][v] = fmaf(s0, c[v], acc[i][v]);
+        c = mfma(xa[2], lookup8(d2, lanebase), f32x4_t{0.f, 0.f, 0.f, 0.f});
+        c = mfma(xa[3], lookup8(d3, lanebase), c);
 #pragma unroll
-        for (int v = 0; v < 8; ++v) acc[i][v] = fmaf(sc, cblk[v], acc[i][v]);
+        for (int v = 0; v < 4; ++v) acc[i][v] = fmaf(s1, c[v], acc[i][v]);
+        // the tile's next load, into the registers just consumed (issued once
+        // they are free, so the loop carries no register copies, which would
+        // wait for the load), and kept here by the scheduling barriers
+        __builtin_amdgcn_sched_barrier(0);
+        issue_w(R[sp], i, k + sp + PD);
+        __builtin_amdgcn_sched_barrier(0);
       }
-    }
-  };
-
-  if (nst > 0) {
-    // Stage x lives in register set x mod (DEPTH + 1): loaded at step x - DEPTH,
-    // written to LDS buffer x & 1 at step x - 1, multiplied at step x.  The
-    // first period only loads (its stores and multiplies are skipped by uniform
-    // tests), so the sets live in the same registers from the first load on.
-    StageRegs<XR> R[DEPTH + 1];
-    int s = -(DEPTH + 1);
-    for (; s + DEPTH + 1 <= nst; s += DEPTH + 1) {
-#pragma unroll
-      for (int d = 0; d <= DEPTH; ++d) {
-        const int st = s + d;  // stage multiplied in this step
-        load_stage<CODES4, XR>(R[(d + DEPTH) % (DEPTH + 1)], c, blk_of(st + DEPTH));
-        asm volatile("" ::: "memory");  // keep the loads in stage order (waits count in issue order)
-        if (st + 1 >= 0) store_stage(R[(d + 1) % (DEPTH + 1)], sm, (st + 1) & 1, wave, lane);
-        if (st >= 0) compute(st & 1, blk_of(st));
-        lds_barrier();
-      }
-    }
-    // the last stages: stage s is in LDS, stages s+1 .. s+DEPTH-1 in R[1 ..]
-#pragma unroll
-    for (int d = 0; d < DEPTH; ++d) {
-      const int st = s + d;
-      if (st < nst) {
-        if (d + 1 < DEPTH && st + 1 < nst) store_stage(R[d + 1], sm, (st + 1) & 1, wave, lane);
-        compute(st & 1, blk_of(st));
-      }
-      lds_barrier();
     }
   }
-  __syncthreads();
 
-  // rank-r term (first slice only): wave i adds it for tile i
-  if (P.r > 0 && z == 0 && wave < 2) {
-    const int i = wave;
-    const int64_t n = n0 + 32 * i + nl;
-    const __amdgpu_buffer_rsrc_t ru = rsrc(P.Us, P.T * P.ldh * 2);
-    f32x16_t ct = {};
+  // wave w < NTW finishes tile w; its rank-r operands are fetched before the
+  // partial tiles are added (r a multiple of 8 and 2r <= 128: A = hi/lo
+  // columns of s U, token rows >= T read zero; B = B[n][j % r])
+  const bool fin = wave < NTW && nt0 + wave < ntiles;
+  const int64_t n = (int64_t)n0 + 16 * wave;
+  const bool tok = i16 < T;
+  constexpr int MJ = 4;
+  const bool pre = P.r > 0 && (P.r & 7) == 0 && P.ldh <= 32 * MJ;
+  const __amdgpu_buffer_rsrc_t ru = rsrc(P.Us, P.T * P.ldh * 2);
+  u32x4_t ua[MJ], ub[MJ];
+  if (fin && pre) {
 #pragma unroll
-    for (int v = 0; v < 8; ++v) ct[v] = acc[i][v];
-    for (int64_t kk = 0; kk < P.ldh; kk += 16) {
-      const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(ru, (uint32_t)(((int64_t)nl * P.ldh + kk + 8 * g) * 2), 0, 0);
-      const uint32_t j0 = (uint32_t)((kk + 8 * g) % P.r);
-      u32x4_t b;
-      if ((P.r & 7) == 0) {
-        b = *reinterpret_cast<const u32x4_t*>(P.B + n * P.r + j0);
-      } else {
-        uint16_t e[8];
-        for (int q = 0; q < 8; ++q) e[q] = P.B[n * P.r + (j0 + q) % (uint32_t)P.r];
-        b = u32x4_t{e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16), e[4] | ((uint32_t)e[5] << 16),
-                    e[6] | ((uint32_t)e[7] << 16)};
+    for (int q = 0; q < MJ; ++q) {
+      if (32 * q < P.ldh) {
+        ua[q] = __builtin_amdgcn_raw_buffer_load_b128(
+            ru, tok ? (uint32_t)((i16 * P.ldh + 32 * q + 8 * g) * 2) : kOob, 0, 0);
+        ub[q] = *reinterpret_cast<const u32x4_t*>(P.B + n * P.r + (32 * q + 8 * g) % P.r);
       }
-      ct = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
-                                                    ct, 0, 0, 0);
     }
-#pragma unroll
-    for (int v = 0; v < 8; ++v) acc[i][v] = ct[v];
   }
 
-  // add the four waves' sums (in the packed-byte buffers, free by now); lane
-  // l, value v of tile i holds token 8(v/4) + 4(l/32) + v%4 of row 32i + l%32
-  float* red = reinterpret_cast<float*>(&sm.w[0][0]);  // [wave][tile][v][lane], 16 KB
-  static_assert(sizeof(sm.w) >= WAVES * 2 * 8 * 64 * 4, "reduction fits in the packed-byte buffers");
+  // add the waves' tiles in a fixed order: (w + (w + 8)) for w < 8, then
+  // w = 0 .. 7; lane l, value v holds token 4(l/16) + v of row l%16
+  __syncthreads();  // every wave is done with the codes and its X slot
+  if (DW == 16 && wave >= 8) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < NTW; ++i)
 #pragma unroll
-    for (int v = 0; v < 8; ++v) red[((wave * 2 + i) * 8 + v) * 64 + lane] = acc[i][v];
+      for (int v = 0; v < 4; ++v) red[(((wave - 8) * NTW + i) * 4 + v) * 64 + lane] = acc[i][v];
+  }
+  if (DW == 16) __syncthreads();
+  if (wave < 8) {
+#pragma unroll
+    for (int i = 0; i < NTW; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        float* r = &red[((wave * NTW + i) * 4 + v) * 64 + lane];
+        *r = DW == 16 ? acc[i][v] + *r : acc[i][v];
+      }
+  }
   __syncthreads();
-  for (int o = tid; o < 16 * ROWS; o += 256) {
-    const int t = o / ROWS, row = o % ROWS;
-    if (t >= P.T) break;
-    const int i = row >> 5, l = (row & 31) + 32 * ((t >> 2) & 1), v = 4 * (t >> 3) + (t & 3);
-    float sum = red[(i * 8 + v) * 64 + l];
+  if (!fin) return;
+  f32x4_t c;
 #pragma unroll
-    for (int w = 1; w < WAVES; ++w) sum += red[((w * 2 + i) * 8 + v) * 64 + l];
-    const int64_t n = n0 + row;
-    if (P.nsplit == 1) P.Y[t * P.N + n] = f32_to_bf16_bits(sum);
-    else P.part[((int64_t)z * P.T + t) * P.N + n] = sum;
+  for (int v = 0; v < 4; ++v) {
+    float sum = red[((0 * NTW + wave) * 4 + v) * 64 + lane];
+#pragma unroll
+    for (int w = 1; w < 8; ++w) sum += red[((w * NTW + wave) * 4 + v) * 64 + lane];
+    c[v] = sum;
+  }
+  if (pre) {
+#pragma unroll
+    for (int q = 0; q < MJ; ++q)
+      if (32 * q < P.ldh) c = mfma(__builtin_bit_cast(bf16x8_t, ua[q]), __builtin_bit_cast(bf16x8_t, ub[q]), c);
+  } else if (P.r > 0) {
+    for (int64_t jj = 0; jj < P.ldh; jj += 32) {
+      const uint32_t uo = tok ? (uint32_t)((i16 * P.ldh + jj + 8 * g) * 2) : kOob;
+      const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(ru, uo, 0, 0);
+      const uint32_t j0 = (uint32_t)((jj + 8 * g) % P.r);
+      uint16_t e[8];
+      for (int q = 0; q < 8; ++q) e[q] = P.B[n * P.r + (j0 + q) % (uint32_t)P.r];
+      const u32x4_t b = {e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16), e[4] | ((uint32_t)e[5] << 16),
+                         e[6] | ((uint32_t)e[7] << 16)};
+      c = mfma(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c);
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int t = 4 * g + v;
+    if (t < T) P.Y[t * P.N + n] = f32_to_bf16_bits(c[v]);
   }
 }
 
-// Y = bf16(sum over slices of the partials), slices added in order.
-__global__ __launch_bounds__(256) void k_decode_reduce(const float* __restrict__ part, int nsplit, int64_t total,
-                                                       uint16_t* __restrict__ Y) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= total) return;
-  float sum = part[idx];
-  for (int z = 1; z < nsplit; ++z) sum += part[(int64_t)z * total + idx];
-  Y[idx] = f32_to_bf16_bits(sum);
+// 16 waves where their 128 registers per lane hold the loop, else 8
+template <int NTW>
+void launch_ntw(const DecodeParams& P, bool c2, unsigned grid, hipStream_t stream) {
+  const dim3 g(grid);
+  if (c2 && P.T <= 4) {
+    if constexpr (NTW <= 7) hipLaunchKernelGGL((k_decode<16, NTW, 1, true>), g, dim3(1024), 0, stream, P);
+    else hipLaunchKernelGGL((k_decode<8, NTW, 1, true>), g, dim3(512), 0, stream, P);
+  } else if (c2) {
+    if constexpr (NTW <= 6) hipLaunchKernelGGL((k_decode<16, NTW, 4, true>), g, dim3(1024), 0, stream, P);
+    else hipLaunchKernelGGL((k_decode<8, NTW, 4, true>), g, dim3(512), 0, stream, P);
+  } else if (P.T <= 4) {
+    hipLaunchKernelGGL((k_decode<8, NTW, 1, false>), g, dim3(512), 0, stream, P);
+  } else {
+    hipLaunchKernelGGL((k_decode<8, NTW, 4, false>), g, dim3(512), 0, stream, P);
+  }
 }
 
 }  // namespace
 
-// Contraction slices for an N x K weight: about 448 workgroups, whole stages
-// per slice, at most 3 * 256 + SB blocks per slice (so a row touches at most
-// MAXG groups of 256 blocks inside one slice).
-int decode_splits(int64_t N, int64_t K) {
-  const int64_t tiles = N / ROWS;
-  const int64_t nbk = K / 64;
-  const int64_t nst = (nbk + SB - 1) / SB;
-  int64_t ns = (448 + tiles - 1) / tiles;
-  if (ns > nst) ns = nst;
-  const int64_t min_ns = (nbk + 3 * 256 - 1) / (3 * 256);
-  if (ns < min_ns) ns = min_ns;
-  return (int)(ns < 1 ? 1 : ns);
+// The workgroup's codes must fit their LDS region with at least one 16-row tile.
+bool decode_supported(int64_t N, int64_t K) {
+  if (N % 16 != 0 || K % 64 != 0 || N * K / 2 > 0x7FFFFFF0LL) return false;
+  const int64_t rs = 4 * (((K / 64 + 3) / 4) | 1);
+  return ((16 * rs + 15) & ~15LL) + 4 * (16 * (K / 64) / 256 + 2) <= CODES_BYTES;
 }
 
 hipError_t launch_decode(const uint8_t* packed, const uint8_t* codes, const float* consts, const uint16_t* X,
                          int64_t T, int64_t N, int64_t K, const uint16_t* Us, int64_t ldh, const uint16_t* B,
-                         int r, int nsplit, float* part, uint16_t* Y, hipStream_t stream) {
+                         int r, uint16_t* Y, hipStream_t stream) {
+  // byte offsets into the packed weight, codes and X are 32-bit
+  if (T < 1 || T > 16 || N % 16 != 0 || K % 64 != 0 || N * K / 2 > 0x7FFFFFF0LL) return hipErrorInvalidValue;
   DecodeParams P;
   P.packed = packed; P.codes = codes; P.consts = consts; P.X = X;
   P.T = T; P.N = N; P.K = K;
   P.Us = Us; P.ldh = ldh; P.B = B; P.r = r;
-  P.nsplit = nsplit;
-  const int64_t nst = (K / 64 + SB - 1) / SB;
-  P.per = (nst + nsplit - 1) / nsplit * SB;
-  P.Y = Y; P.part = part;
+  P.Y = Y;
   const Nf4Table& tab = nf4_table();
   for (int i = 0; i < 16; ++i) P.level[i] = tab.level[i];
-  const dim3 grid((unsigned)(N / ROWS), (unsigned)nsplit);
-  {
-    TraceScope ts(KID_DECODE, stream);
-    const bool c4 = (K / 64) % 4 == 0;
-    if (T <= 4) {
-      if (c4) hipLaunchKernelGGL((k_decode<true, 1, 3>), grid, dim3(256), 0, stream, P);
-      else hipLaunchKernelGGL((k_decode<false, 1, 3>), grid, dim3(256), 0, stream, P);
-    } else if (T <= 8) {
-      if (c4) hipLaunchKernelGGL((k_decode<true, 2, 3>), grid, dim3(256), 0, stream, P);
-      else hipLaunchKernelGGL((k_decode<false, 2, 3>), grid, dim3(256), 0, stream, P);
-    } else {
-      if (c4) hipLaunchKernelGGL((k_decode<true, 4, 2>), grid, dim3(256), 0, stream, P);
-      else hipLaunchKernelGGL((k_decode<false, 4, 2>), grid, dim3(256), 0, stream, P);
-    }
+  // tiles per workgroup: the 16-row tiles spread over the 256 CUs (at most 8 each)
+  const int64_t ntiles = N / 16;
+  int64_t ntw = (ntiles + 255) / 256;
+  if (ntw > 8) ntw = 8;
+  // the workgroup's codes and group ratios must fit their LDS region, and the
+  // group count one load per thread
+  const int64_t rs = 4 * (((K / 64 + 3) / 4) | 1);  // LDS row stride of the codes
+  auto aux_need = [&](int64_t t) { return ((16 * t * rs + 15) & ~15LL) + 4 * (16 * t * (K / 64) / 256 + 2); };
+  while (ntw > 1 && aux_need(ntw) > CODES_BYTES) --ntw;
+  if (aux_need(ntw) > CODES_BYTES) return hipErrorInvalidValue;
+  const unsigned grid = (unsigned)((ntiles + ntw - 1) / ntw);
+  const bool c2 = (K / 64) % 2 == 0;
+  TraceScope ts(KID_DECODE, stream);
+  switch (ntw) {
+    case 1: launch_ntw<1>(P, c2, grid, stream); break;
+    case 2: launch_ntw<2>(P, c2, grid, stream); break;
+    case 3: launch_ntw<3>(P, c2, grid, stream); break;
+    case 4: launch_ntw<4>(P, c2, grid, stream); break;
+    case 5: launch_ntw<5>(P, c2, grid, stream); break;
+    case 6: launch_ntw<6>(P, c2, grid, stream); break;
+    case 7: launch_ntw<7>(P, c2, grid, stream); break;
+    default: launch_ntw<8>(P, c2, grid, stream); break;
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || nsplit == 1) return e;
-  const int64_t total = T * N;
-  TraceScope ts(KID_DECODE_EPILOGUE, stream);
-  hipLaunchKernelGGL(k_decode_reduce, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, part, nsplit,
-                     total, Y);
   return hipGetLastError();
 }
 

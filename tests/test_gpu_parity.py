@@ -168,6 +168,12 @@ CASES = [
     (192, 320, 523, 8, 16.0, 11),
     (256, 192, 600, 24, 8.0, 12),
     (320, 448, 1031, 64, 16.0, 13),
+    # few-token path with several 16-row tiles per workgroup (N/16 above 256)
+    (4160, 256, 2, 16, 16.0, 14),     # 2 tiles per workgroup
+    (8320, 192, 9, 24, 8.0, 15),      # 3 tiles, the last workgroup 1; K/64 odd
+    (16448, 256, 3, 8, 16.0, 16),     # 5 tiles, the last workgroup 3
+    (20608, 256, 6, 16, 16.0, 18),    # 6 tiles, the last workgroup 4
+    (28736, 128, 16, 64, 16.0, 17),   # 8 tiles, the last workgroup 4
 ]
 
 
@@ -314,6 +320,27 @@ def test_workspace_reuse_across_calls():
             assert torch.equal(Y1, Y2) and torch.equal(U1, U2)
             for a, b in zip(g1, g2):
                 assert torch.equal(a, b)
+
+
+def test_few_tokens_with_unaligned_codes():
+    """Codes off a 16-byte boundary: the few-token forward runs the tiled kernel
+    instead of the weight-streaming one; both results match the oracle."""
+    import nf4_bit_quantized_amd as q
+    import torch
+    for T in (1, 4):
+        inp = workloads.layer_inputs(256, 320, T, 8, seed=21)
+        o = oracle_layer(inp, 8, 16.0, do_bwd=False)
+        packed, codes, consts = q.qlora_quantize_nf4(dev_f32(inp["W"]))
+        buf = torch.zeros(codes.numel() + 16, dtype=torch.uint8, device="cuda")
+        shifted = buf[1:1 + codes.numel()]
+        shifted.copy_(codes)
+        X, A, B = dev_bf16(inp["X"]), dev_bf16(inp["A"]), dev_bf16(inp["B"])
+        for c in (codes, shifted):
+            Y, _ = q.qlora_linear_fwd(packed, c, consts, X, A, B, 16.0)
+            torch.cuda.synchronize()
+            e = normwise_err(host_bf16_to_f64(Y), o["Y"])
+            say(f"  T={T} codes offset {c.data_ptr() % 16}: Y err {e:.2e}")
+            assert e <= TOL, (T, e)
 
 
 def test_zero_tokens_is_a_no_op():
