@@ -39,11 +39,11 @@ BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 # on (sha256 of the files below); reported as null once those change.
 TRAFFIC_SOURCES = ("fused_gemm.hip", "fused.hpp", "common.hpp")
 TRAFFIC = {
-    "sha256": "58b6e97966b4b7a47b71986af4b00aaa10e04428de53960fa43ec0ee896e73de",
-    "fetch_scale": 262144.0 / 131087.1,
+    "sha256": "66ddabd1afb18b2b54db223d7afd3e297befcf8e427ec22ce50ff0066ac17d4a",
+    "fetch_scale": 262144.0 / 131087.8,
     "write_scale": 1.0,
-    "fwd_gemm": {"fetch_kib": 36021.1, "write_kib": 24576.0},
-    "dx_gemm": {"fetch_kib": 35846.9, "write_kib": 16384.0},
+    "fwd_gemm": {"fetch_kib": 36002.9, "write_kib": 16384.0},
+    "dx_gemm": {"fetch_kib": 35834.1, "write_kib": 16384.0},
 }
 
 

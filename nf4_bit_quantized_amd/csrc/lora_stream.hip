@@ -20,6 +20,7 @@
 // column) l % 16 and contraction slots 8(l/16) .. +7.
 #include <algorithm>
 
+#include "dma.hpp"
 #include "lora_stream.hpp"
 #include "trace.hpp"
 
@@ -27,47 +28,18 @@ namespace qlora {
 namespace {
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void_t;
+using dma::lds_void_t;
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
 
-// A buffer offset no range here reaches (ranges are capped below 2^31): loads read zero.
-constexpr uint32_t kOob = 0x80000000u;
-
-// Buffer resource (base, stride 0, byte range capped below 2^31) as four
-// dwords, for the copies below.
-typedef int v4i_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ v4i_t rsrc(const void* p, int64_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(p);
-  const int32_t n = bytes > 0x7FFFFFF0LL ? 0x7FFFFFF0 : (int32_t)bytes;
-  return v4i_t{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xFFFFu), n, 0x00020000};
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-__device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-
-// 16-byte copy of global memory (buffer offset voff) to LDS: lane l lands at
-// LDS byte address dst + 16 l.  Written as inline asm so that the compiler does not track the
-// copy as an LDS store: its own bookkeeping would wait for every copy in
-// flight before each LDS read it cannot prove disjoint (draining the
-// prefetch); the kernels below wait for exactly the copies they read instead.
-// No other code in this file uses M0 (checked in the generated code).
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void copy16(v4i_t r, uint32_t voff, uint32_t dst) {
-  const uint32_t l = __builtin_amdgcn_readfirstlane(dst);
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(l), "v"(voff), "s"(r)
-               : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-// LDS byte address of a __shared__ array (apply to the array itself).
-#define LDS_ADDR(arr) ((uint32_t)reinterpret_cast<uintptr_t>((lds_void_t*)(arr)))
+using dma::copy16;
+using dma::kOob;
+using dma::rsrc;
+using dma::v4i_t;
+using dma::wait_lds;
+using dma::wait_vm;
 
 // MFMA fragment from a row-major LDS tile [rows][ld] whose rows run along the
 // contraction: lane l (i = l % 16) receives rows kb .. kb+7 of column c0 + i.

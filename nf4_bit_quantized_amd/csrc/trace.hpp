@@ -15,7 +15,6 @@ enum KernelId : int {
   KID_LORA_DA,
   KID_LORA_DB,
   KID_DECODE,
-  KID_DECODE_EPILOGUE,
   KID_REDUCE,
   KID_FILL,
   KID_COUNT
