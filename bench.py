@@ -37,13 +37,13 @@ BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 # 262144 KiB moved (scale 1.99977), the fill's WRITE_SIZE reads exactly
 # 262144 KiB (scale 1).  Valid only for the kernel sources they were taken
 # on (sha256 of the files below); reported as null once those change.
-TRAFFIC_SOURCES = ("fused_gemm.hip", "fused.hpp", "common.hpp")
+TRAFFIC_SOURCES = ("fused_gemm.hip", "fused.hpp", "restore.hpp", "common.hpp")
 TRAFFIC = {
-    "sha256": "66ddabd1afb18b2b54db223d7afd3e297befcf8e427ec22ce50ff0066ac17d4a",
-    "fetch_scale": 262144.0 / 131087.8,
+    "sha256": "fa74709fa9816fc29523a15d118faad93b04a283106e375e976b664830d8fc1a",
+    "fetch_scale": 262144.0 / 131090.1,
     "write_scale": 1.0,
-    "fwd_gemm": {"fetch_kib": 36002.9, "write_kib": 16384.0},
-    "dx_gemm": {"fetch_kib": 35834.1, "write_kib": 16384.0},
+    "fwd_gemm": {"fetch_kib": 36003.0, "write_kib": 16384.0},
+    "dx_gemm": {"fetch_kib": 35833.9, "write_kib": 16384.0},
 }
 
 
@@ -180,6 +180,48 @@ def decode_section(steps, warmup):
     return out
 
 
+def export_section(lin, steps):
+    """HBM GB/s of the restored-weight export and of the merge, on the step's
+    weight (rotating 8 copies of the packed weight and of the output, 336 MB,
+    so the 256 MB MALL cannot hold them)."""
+    import torch
+    import nf4_bit_quantized_amd as q
+    import workloads
+
+    N, K, r = lin.d_out, lin.d_in, lin.r
+    inp = workloads.layer_inputs(N, K, 1, r, lin.seed)
+    W = torch.from_numpy(inp["W"]).cuda()
+    pk, cd, cs = q.qlora_quantize_nf4(W)
+    del W
+    copies = 8
+    reps = [(pk.clone(), cd.clone(), cs.clone()) for _ in range(copies)]
+    outs = [torch.empty((N, K), dtype=torch.bfloat16, device="cuda") for _ in range(copies)]
+    A, B = bf16_dev(inp["A"]), bf16_dev(inp["B"])
+    weight_bytes = pk.numel() + cd.numel() + cs.numel() * 4
+    out = {}
+    for name, call, extra in (
+            ("dequantize", lambda p, o: q.qlora_dequantize_nf4(p[0], p[1], p[2], W_hat=o), 0),
+            ("merge", lambda p, o: q.qlora_merge_lora(p[0], p[1], p[2], A, B, lin.alpha, W_merged=o),
+             A.numel() * 2 + B.numel() * 2)):
+        for i in range(copies):
+            call(reps[i], outs[i])
+        torch.cuda.synchronize()
+        q.qlora_trace_read(reset=True)
+        q.qlora_trace_select({"export"})
+        for i in range(steps):
+            call(reps[i % copies], outs[i % copies])
+        torch.cuda.synchronize()
+        q.qlora_trace_enable(False)
+        n, ms = q.qlora_trace_read(reset=True).get("export", (1, float("nan")))
+        avg = ms / max(n, 1)
+        nbytes = weight_bytes + N * K * 2 + extra
+        out[name] = {"d_out": N, "d_in": K, "r": r if name == "merge" else 0, "bytes": nbytes,
+                     "kernel_us": round(avg * 1e3, 2), "GBps": round(nbytes / (avg * 1e-3) / 1e9, 1),
+                     "frac_hbm": round(nbytes / (avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+        log("export", name, out[name])
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -294,6 +336,7 @@ def main():
     }
     if not args.no_decode:
         result["decode_packed_weight"] = decode_section(steps=max(20, args.steps), warmup=5)
+        result["export_bf16"] = export_section(lin, steps=max(20, args.steps))
     if not args.no_cpu_baseline:
         log("timing the oracle on the host ...")
         result["cpu_baseline"] = cpu_baseline(inp, lin, args.cpu_seconds)

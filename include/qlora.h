@@ -170,6 +170,33 @@ int qlora_linear_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8
                      void* stream);
 
 /*
+ * Export of the restored weight -- "QLoRA技术从入门到精通" §3(2) (the 4-bit
+ * weight restored to a 16-bit float, table value times the block's scale):
+ *   W_hat[N][K] = bf16_rne(fl32(T[q] * s'))   (bf16 bits, device)
+ * Bit-identical to the weight the fused products restore on chip.  packed,
+ * codes, consts as produced by qlora_quantize_nf4; W_hat must be 16-byte
+ * aligned and must not alias the inputs.
+ * Errors: NULL, SHAPE, UNSUPPORTED, HIP.
+ */
+int qlora_dequantize_nf4(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes,
+                         const float* consts, uint16_t* W_hat, void* stream);
+
+/*
+ * The adapter merged into the restored weight -- "LoRA 与 QLoRA：把大模型微调拆成
+ * 可负担的工程" §3 (W + (alpha/r) B A after training); "【X 长文】LoRA 与 QLoRA：
+ * 用一块 GPU 微调大模型", QLoRA section (with a 4-bit base, the merge goes into
+ * the restored 16-bit weight, not into the 4-bit one):
+ *   W_merged[N][K] = bf16_rne( fl32( W_hat + fl32(s * (B A)) ) ),  s = fl32(alpha / r)
+ * A [r][K] and B [N][r] are bf16 bits (device, 16-byte aligned); B A is
+ * accumulated in fp32 (MFMA order).  r = 0 gives W_hat exactly.  1 <= r <= 128
+ * otherwise.  The 4-bit arrays are not modified.
+ * Errors: NULL, SHAPE, UNSUPPORTED, HIP.
+ */
+int qlora_merge_lora(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes,
+                     const float* consts, int32_t r, float alpha, const uint16_t* A, const uint16_t* B,
+                     uint16_t* W_merged, void* stream);
+
+/*
  * Per-kernel timing (measurement support; not an operation of the layer).
  * qlora_trace_enable(1) makes every subsequent kernel launch of the library
  * record a hipEvent before and after it on the launch stream (event objects

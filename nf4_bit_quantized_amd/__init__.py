@@ -33,6 +33,8 @@ EXPORTED = (
     "qlora_linear_fwd",
     "qlora_bwd_workspace_bytes",
     "qlora_linear_bwd",
+    "qlora_dequantize_nf4",
+    "qlora_merge_lora",
     "qlora_trace_enable",
     "qlora_trace_select",
     "qlora_trace_kernel_name",
@@ -78,6 +80,8 @@ def lib() -> ctypes.CDLL:
     L.qlora_bwd_workspace_bytes.argtypes = [dp, i64, i32, ctypes.POINTER(sz)]
     L.qlora_linear_fwd.argtypes = [dp, vp, vp, vp, i64, vp, i32, f32, vp, vp, vp, vp, vp, sz, vp]
     L.qlora_linear_bwd.argtypes = [dp, vp, vp, vp, i64, vp, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.qlora_dequantize_nf4.argtypes = [dp, vp, vp, vp, vp, vp]
+    L.qlora_merge_lora.argtypes = [dp, vp, vp, vp, i32, f32, vp, vp, vp, vp]
     L.qlora_trace_enable.argtypes = [ctypes.c_int]
     L.qlora_trace_select.argtypes = [ctypes.c_uint32]
     L.qlora_trace_kernel_name.argtypes = [ctypes.c_int]
@@ -253,6 +257,38 @@ def qlora_linear_bwd(packed, codes, consts, X, A, B, alpha: float, dY, U_in=None
                                   float(alpha), _ptr(A), _ptr(B), _ptr(U_in), _ptr(dY), _ptr(dX), _ptr(dA),
                                   _ptr(dB), _ptr(ws), nbytes, _stream(stream)), "qlora_linear_bwd")
     return dX, dA, dB
+
+
+def qlora_dequantize_nf4(packed, codes, consts, W_hat=None, stream=None):
+    """Restored weight: bf16 [d_out][d_in], bit-identical to what the fused
+    products restore on chip."""
+    import torch
+    d_out, d_in = packed.shape[0], packed.shape[1] * 2
+    _need_cuda(packed, codes, consts, W_hat, name="qlora_dequantize_nf4")
+    if W_hat is None:
+        W_hat = torch.empty((d_out, d_in), dtype=torch.bfloat16, device=packed.device)
+    d = _desc(d_out, d_in)
+    _check(lib().qlora_dequantize_nf4(ctypes.byref(d), _ptr(packed), _ptr(codes), _ptr(consts), _ptr(W_hat),
+                                      _stream(stream)), "qlora_dequantize_nf4")
+    return W_hat
+
+
+def qlora_merge_lora(packed, codes, consts, A, B, alpha: float, W_merged=None, stream=None):
+    """The adapter merged into the restored weight: bf16 [d_out][d_in] =
+    bf16(W_hat + (alpha / r) B A); A bf16 [r][d_in], B bf16 [d_out][r]."""
+    import torch
+    d_out, d_in = packed.shape[0], packed.shape[1] * 2
+    r = A.shape[0]
+    _need_cuda(packed, codes, consts, A, B, W_merged, name="qlora_merge_lora")
+    for t, nm in ((A, "A"), (B, "B")):
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{nm} must be bfloat16")
+    if W_merged is None:
+        W_merged = torch.empty((d_out, d_in), dtype=torch.bfloat16, device=packed.device)
+    d = _desc(d_out, d_in)
+    _check(lib().qlora_merge_lora(ctypes.byref(d), _ptr(packed), _ptr(codes), _ptr(consts), int(r), float(alpha),
+                                  _ptr(A), _ptr(B), _ptr(W_merged), _stream(stream)), "qlora_merge_lora")
+    return W_merged
 
 
 # ---------------------------------------------------------------------------

@@ -19,6 +19,8 @@ hipError_t launch_decode(const uint8_t* packed, const uint8_t* codes, const floa
                          int64_t T, int64_t N, int64_t K, const uint16_t* Us, int64_t ldh, const uint16_t* B,
                          int r, uint16_t* Y, hipStream_t stream);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
+hipError_t launch_export(const uint8_t* packed, const uint8_t* codes, const float* consts, int64_t N, int64_t K,
+                         int r, float s, const uint16_t* A, const uint16_t* B, uint16_t* W, hipStream_t stream);
 }  // namespace qlora
 
 using namespace qlora;
@@ -200,6 +202,24 @@ int qlora_quantize_nf4(const qlora_nf4_desc* d, const float* W, uint8_t* packed,
   if (!W || !packed || !codes || !consts) return QLORA_ERR_NULL;
   if (!aligned16(W) || !aligned16(packed)) return QLORA_ERR_UNSUPPORTED;
   HIP_TRY(launch_nf4_quantize(W, packed, codes, consts, d->d_out * d->d_in, (hipStream_t)stream));
+  return QLORA_OK;
+}
+
+int qlora_dequantize_nf4(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes,
+                         const float* consts, uint16_t* W_hat, void* stream) {
+  return qlora_merge_lora(d, packed, codes, consts, 0, 0.0f, nullptr, nullptr, W_hat, stream);
+}
+
+int qlora_merge_lora(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes,
+                     const float* consts, int32_t r, float alpha, const uint16_t* A, const uint16_t* B,
+                     uint16_t* W_merged, void* stream) {
+  const int st = check_layer(d, 0, r);
+  if (st) return st;
+  if (!packed || !codes || !consts || !W_merged) return QLORA_ERR_NULL;
+  if (r > 0 && (!A || !B)) return QLORA_ERR_NULL;
+  if (!aligned16(W_merged) || (r > 0 && (!aligned16(A) || !aligned16(B)))) return QLORA_ERR_UNSUPPORTED;
+  const float s = r > 0 ? alpha / (float)r : 0.0f;
+  HIP_TRY(launch_export(packed, codes, consts, d->d_out, d->d_in, r, s, A, B, W_merged, (hipStream_t)stream));
   return QLORA_OK;
 }
 

@@ -1,0 +1,204 @@
+// Export of the restored weight, and of the weight with the adapter merged in.
+//
+// "QLoRA技术从入门到精通" §3(2): the 4-bit weight is restored to a 16-bit float
+// (table value times the block's restored scale).  "LoRA 与 QLoRA：把大模型微调
+// 拆成可负担的工程" §3: after training the update can be merged into the
+// weight, W + (alpha / r) B A.  "【X 长文】LoRA 与 QLoRA：用一块 GPU 微调大模型",
+// QLoRA section: with a 4-bit base the trained A and B cannot be added to the
+// 4-bit weight; they are merged into the restored 16-bit weight.
+//
+//   dequantize:  W_out = W_hat = bf16_rne(fl32(T[q] * s'))       (bit-exact)
+//   merge:       W_out = bf16_rne( fl32( W_hat + fl32(s * (B A)) ) ),  s = fl32(alpha / r)
+//
+// Dequantize: a flat pass, four 16-weight pairs of packed words per thread
+// (a pair shares one block and its table), all loads issued before any
+// restore, 32-byte stores.
+//
+// Merge: one workgroup per 64 x 128 tile of W (rows x columns), 256 threads. the tile's rank-r term runs on v_mfma_f32_16x16x32_bf16.  Wave w
+// takes rows 16w .. 16w+15.  Operand A is rows of B ([N][r]; lane l: row
+// l % 16, j = 8(l/16) ..); operand B is the tile's columns of A ([r][K]),
+// copied to LDS once and read with ds_read_b64_tr_b16 (within a 16-lane
+// group, source lane s points at row kb + s/4, columns c0 + 4(s%4); lane i
+// receives rows kb .. kb+3 of column c0 + i).  r is padded to a multiple of 32
+// with zeros.  s times the fp32 result is written to an LDS tile.
+//
+// Then every thread restores two pairs of packed words of the tile (8
+// weights each, the restore of the fused products; the two words of a pair
+// share a block and its table), adds the LDS term when merging, rounds once
+// to bf16 and writes 32 bytes; a row's 8 pairs are 8 consecutive threads, so
+// loads and stores are coalesced.  The A tile is sized to the rank (dynamic
+// LDS), so short ranks leave room for more workgroups per CU.
+#include "common.hpp"
+#include "restore.hpp"
+#include "trace.hpp"
+
+namespace qlora {
+
+namespace {
+
+constexpr int TR = 64, TC = 128;  // tile rows (weight rows) and columns
+constexpr int LDA = TC + 16;      // bf16 row of the A tile in LDS
+constexpr int LDD = TC + 4;       // fp32 row of the rank-r term in LDS
+constexpr int MAX_R = 128;
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x4_t __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
+
+struct ExportParams {
+  const uint8_t* packed;
+  const uint8_t* codes;
+  const float* consts;
+  int64_t N, K;
+  const uint16_t* A;  // [r][K] bf16 (merge only)
+  const uint16_t* B;  // [N][r] bf16 (merge only)
+  int r;
+  float s;
+  uint16_t* W;        // [N][K] bf16 out
+  Nf4Table tab;
+};
+
+template <bool MERGE>
+__global__ __launch_bounds__(256) void k_export(ExportParams P) {
+  static_assert(MERGE, "the tile kernel serves the merge; k_dequant the plain export");
+  // dynamic LDS (merge only): D [TR][LDD] fp32, then the A tile [rpad][LDA] bf16
+  extern __shared__ __attribute__((aligned(16))) float dyn[];
+  float* D = dyn;
+  uint16_t* At = reinterpret_cast<uint16_t*>(dyn + TR * LDD);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t i0 = (int64_t)blockIdx.y * TR, k0 = (int64_t)blockIdx.x * TC;
+
+  if (MERGE) {
+    const int rpad = (P.r + 31) & ~31;
+    // A[j][k0 .. k0+127], zero for j >= r or columns past K
+    for (int c = tid; c < rpad * (TC / 8); c += 256) {
+      const int j = c / (TC / 8), cc = (c % (TC / 8)) * 8;
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (j < P.r && k0 + cc < P.K) v = *reinterpret_cast<const u32x4_t*>(P.A + (int64_t)j * P.K + k0 + cc);
+      *reinterpret_cast<u32x4_t*>(At + j * LDA + cc) = v;
+    }
+    __syncthreads();
+    const int i16 = lane & 15, g = lane >> 4;
+    const int64_t brow = i0 + 16 * wave + i16;
+    f32x4_t acc[TC / 16];
+#pragma unroll
+    for (int ct = 0; ct < TC / 16; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const lds_u16_t* at = (const lds_u16_t*)At;
+    for (int js = 0; js < rpad; js += 32) {
+      u16x8_t a;
+      if ((P.r & 7) == 0) {
+        const int j0 = js + 8 * g;
+        a = j0 < P.r ? *reinterpret_cast<const u16x8_t*>(P.B + brow * P.r + j0) : u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int jj = js + 8 * g + q;
+          a[q] = jj < P.r ? P.B[brow * P.r + jj] : (uint16_t)0;
+        }
+      }
+      const int row = js + 8 * g + (i16 >> 2);
+#pragma unroll
+      for (int ct = 0; ct < TC / 16; ++ct) {
+        const int col = 16 * ct + 4 * (i16 & 3);
+        const u16x4_t lo = __builtin_bit_cast(
+            u16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(at + row * LDA + col)));
+        const u16x4_t hi = __builtin_bit_cast(
+            u16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(at + (row + 4) * LDA + col)));
+        const u16x8_t b = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                          __builtin_bit_cast(bf16x8_t, b), acc[ct], 0, 0, 0);
+      }
+    }
+    // C layout: lane l, value v holds row 4(l/16) + v, column l % 16 of the tile
+#pragma unroll
+    for (int ct = 0; ct < TC / 16; ++ct)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) D[(16 * wave + 4 * g + v) * LDD + 16 * ct + i16] = P.s * acc[ct][v];
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int d = tid + 256 * q;
+    const int row = d >> 3, cp = (d & 7) * 2;  // words cp, cp + 1 of the row (one block)
+    const int64_t n = i0 + row, kc = k0 + 8 * cp;
+    if (n >= P.N || kc >= P.K) continue;
+    const int64_t e0 = n * P.K + kc;  // element index of the pair's first weight
+    const uint2 w = *reinterpret_cast<const uint2*>(P.packed + e0 / 2);
+    const int64_t blk = e0 / 64;
+    const RestoreTab t = make_tab(P.tab, restored_scale(P.codes[blk], P.consts[blk >> 8]));
+    uint32_t o[8];
+    restore8(w.x, t, o);
+    restore8(w.y, t, o + 4);
+    if (MERGE) {
+      const float* dr = D + row * LDD + 8 * cp;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        o[e] = pack_bf16x2(bf16_bits_to_f32(o[e] & 0xFFFFu) + dr[2 * e], bf16_bits_to_f32(o[e] >> 16) + dr[2 * e + 1]);
+    }
+    uint4* dst = reinterpret_cast<uint4*>(P.W + e0);
+    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+  }
+}
+
+// Dequantize only: pairs p = 16-weight runs in element order (packed bytes
+// 8p .. 8p+7, block p / 4).
+constexpr int DQ_PER = 4;
+__global__ __launch_bounds__(256) void k_dequant(ExportParams P) {
+  const int64_t npairs = P.N * P.K / 16;
+  const int64_t p0 = ((int64_t)blockIdx.x * 256 * DQ_PER) + threadIdx.x;
+  uint2 w[DQ_PER];
+  uint32_t code[DQ_PER];
+  float cg[DQ_PER];
+#pragma unroll
+  for (int q = 0; q < DQ_PER; ++q) {
+    const int64_t p = p0 + 256 * q;
+    const int64_t pc = p < npairs ? p : npairs - 1;
+    w[q] = *reinterpret_cast<const uint2*>(P.packed + 8 * pc);
+    code[q] = P.codes[pc >> 2];
+    cg[q] = P.consts[pc >> 10];
+  }
+#pragma unroll
+  for (int q = 0; q < DQ_PER; ++q) {
+    const int64_t p = p0 + 256 * q;
+    if (p >= npairs) break;
+    const RestoreTab t = make_tab(P.tab, restored_scale(code[q], cg[q]));
+    uint32_t o[8];
+    restore8(w[q].x, t, o);
+    restore8(w[q].y, t, o + 4);
+    uint4* dst = reinterpret_cast<uint4*>(P.W + 16 * p);
+    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_export(const uint8_t* packed, const uint8_t* codes, const float* consts, int64_t N, int64_t K,
+                         int r, float s, const uint16_t* A, const uint16_t* B, uint16_t* W, hipStream_t stream) {
+  if (N % TR != 0 || K % 64 != 0 || r < 0 || r > MAX_R) return hipErrorInvalidValue;
+  ExportParams P;
+  P.packed = packed; P.codes = codes; P.consts = consts;
+  P.N = N; P.K = K;
+  P.A = A; P.B = B; P.r = r; P.s = s;
+  P.W = W;
+  P.tab = nf4_table();
+  const dim3 grid((unsigned)((K + TC - 1) / TC), (unsigned)(N / TR));
+  TraceScope ts(KID_EXPORT, stream);
+  if (r > 0) {
+    const size_t lds = (size_t)TR * LDD * 4 + (size_t)((r + 31) & ~31) * LDA * 2;
+    hipLaunchKernelGGL(k_export<true>, grid, dim3(256), lds, stream, P);
+  } else {
+    const int64_t npairs = N * K / 16;
+    const unsigned g = (unsigned)((npairs + 256 * DQ_PER - 1) / (256 * DQ_PER));
+    hipLaunchKernelGGL(k_dequant, dim3(g), dim3(256), 0, stream, P);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace qlora

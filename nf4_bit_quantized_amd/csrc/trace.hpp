@@ -17,6 +17,7 @@ enum KernelId : int {
   KID_DECODE,
   KID_REDUCE,
   KID_FILL,
+  KID_EXPORT,
   KID_COUNT
 };
 

@@ -116,6 +116,22 @@ def test_validation_happens_before_any_launch():
     assert r == q.QLORA_ERR_WORKSPACE
 
 
+def test_export_validation_happens_before_any_launch():
+    fake = 0x10000
+    d = q._desc(64, 64)
+    L = q.lib()
+    f = ctypes.c_float(2.0)
+    assert L.qlora_dequantize_nf4(None, fake, fake, fake, fake, None) == q.QLORA_ERR_NULL
+    assert L.qlora_dequantize_nf4(ctypes.byref(d), fake, fake, fake, None, None) == q.QLORA_ERR_NULL
+    assert L.qlora_dequantize_nf4(ctypes.byref(d), fake, fake, fake, fake + 2, None) == q.QLORA_ERR_UNSUPPORTED
+    assert L.qlora_dequantize_nf4(ctypes.byref(q._desc(64, 96)), fake, fake, fake, fake, None) == q.QLORA_ERR_SHAPE
+    assert L.qlora_merge_lora(ctypes.byref(d), fake, fake, fake, 4, f, None, fake, fake, None) == q.QLORA_ERR_NULL
+    assert L.qlora_merge_lora(ctypes.byref(d), fake, fake, fake, 4, f, fake, None, fake, None) == q.QLORA_ERR_NULL
+    assert L.qlora_merge_lora(ctypes.byref(d), fake, fake, fake, 129, f, fake, fake, fake, None) == q.QLORA_ERR_SHAPE
+    assert L.qlora_merge_lora(ctypes.byref(d), fake, fake, fake, 4, f, fake + 8, fake, fake, None) == \
+        q.QLORA_ERR_UNSUPPORTED
+
+
 def test_workspace_sizes_grow_with_tokens_and_rank():
     a = q.qlora_bwd_workspace_bytes(4096, 4096, 2048, 16)
     b = q.qlora_bwd_workspace_bytes(4096, 4096, 4096, 64)

@@ -9,6 +9,7 @@ import workloads
 from gpu_helpers import (TOL, assert_quant_bit_exact, gpu_layer, normwise_err, oracle_layer, say,
                          dev_bf16, dev_f32, host_bf16_to_f64)
 from oracle import nf4 as onf4
+from oracle.bf16 import bits_to_float, float_to_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -282,6 +283,53 @@ def test_merge_matches_two_branch_result():
     Wm = olora.merged_weight(W_hat, bits_to_float(inp["A"]), bits_to_float(inp["B"]), 32.0, 16)
     want = bits_to_float(inp["X"]) @ Wm.T
     assert normwise_err(g["Y"], want) <= TOL
+
+
+@pytest.mark.parametrize("d_out,d_in", [(64, 64), (192, 320), (256, 4160), (1024, 1024)])
+def test_dequantize_export_bit_exact(d_out, d_in):
+    """The exported restored weight equals the oracle's bf16(T[q] s') bit for
+    bit ([入门到精通] §3(2)); shapes include a last column tile of 64."""
+    import nf4_bit_quantized_amd as q
+    import torch
+    say(f"dequantize export {d_out}x{d_in}")
+    inp = workloads.layer_inputs(d_out, d_in, 1, 1, seed=30)
+    packed, codes, consts = q.qlora_quantize_nf4(dev_f32(inp["W"]))
+    W_hat = q.qlora_dequantize_nf4(packed, codes, consts)
+    torch.cuda.synchronize()
+    got = W_hat.view(torch.int16).cpu().numpy().view(np.uint16)
+    want = float_to_bits(onf4.dequantize(onf4.quantize(inp["W"])))
+    np.testing.assert_array_equal(got, want)
+
+
+@pytest.mark.parametrize("d_out,d_in,r,alpha", [(128, 128, 8, 16.0), (192, 320, 3, 5.0), (256, 4160, 64, 16.0),
+                                                (512, 256, 128, 32.0)])
+def test_merge_export_matches_oracle(d_out, d_in, r, alpha):
+    """bf16(W_hat + s B A) ([工程] §3; [X长文] QLoRA section: merged into the
+    restored 16-bit weight): every element within one bf16 step of the
+    oracle's float64 value rounded to bf16; r = 0 and B = 0 give W_hat exactly."""
+    import nf4_bit_quantized_amd as q
+    import torch
+    from oracle import lora as olora
+    say(f"merge export {d_out}x{d_in} r={r}")
+    inp = workloads.layer_inputs(d_out, d_in, 1, r, seed=31)
+    packed, codes, consts = q.qlora_quantize_nf4(dev_f32(inp["W"]))
+    A, B = dev_bf16(inp["A"]), dev_bf16(inp["B"])
+    Wm = q.qlora_merge_lora(packed, codes, consts, A, B, alpha)
+    Wh = q.qlora_dequantize_nf4(packed, codes, consts)
+    W0 = q.qlora_merge_lora(packed, codes, consts, A, torch.zeros_like(B), alpha)
+    torch.cuda.synchronize()
+    assert torch.equal(W0.view(torch.int16), Wh.view(torch.int16))
+    W_hat = onf4.dequantize(onf4.quantize(inp["W"]))
+    want = olora.merged_weight(W_hat, bits_to_float(inp["A"]), bits_to_float(inp["B"]), alpha, r)
+    got = host_bf16_to_f64(Wm)
+    # one bf16 step at the value's magnitude (8 significant bits), plus the
+    # fp32 rounding of the two terms (which matters only where they cancel)
+    step = np.exp2(np.floor(np.log2(np.maximum(np.abs(want), 1e-30))) - 7)
+    tol = step + 2.0 ** -20 * (np.abs(W_hat) + np.abs(want - W_hat))
+    worst = float(np.max(np.abs(got - want) / tol))
+    say(f"  worst error {worst:.3f} of the bound")
+    assert worst <= 1.0
+    assert not torch.equal(Wm.view(torch.int16), Wh.view(torch.int16))
 
 
 def test_deterministic_fwd_bwd():
