@@ -81,7 +81,20 @@ typedef struct qlora_nf4_desc {
   int64_t d_in;         /* K: columns of W */
   int32_t blocksize;    /* weights per absmax block; must be 64 */
   int32_t dq_blocksize; /* block scales per second-level group; must be 256 */
+  int32_t table;        /* level table: QLORA_TABLE_NF4 (0) or QLORA_TABLE_UNIFORM (1) */
 } qlora_nf4_desc;
+
+/*
+ * Level tables.  QLORA_TABLE_NF4: the NF4 table (qlora_nf4_levels).
+ * QLORA_TABLE_UNIFORM: 16 equally spaced levels -1 + 2i/15 on [-1, 1]
+ * ("7、QLoRA 量化微调" §7.1, with its worked example: 0.27 in a group of
+ * absmax 1.52 -> index 9 -> 0.304); it has no zero level.  Everything else
+ * (blocks, scale codes, packing, kernels) is the same.  The table is not
+ * stored with the quantized weight: every call on a weight must pass the desc
+ * it was quantized with.  Any other value: QLORA_ERR_UNSUPPORTED.
+ */
+#define QLORA_TABLE_NF4 0
+#define QLORA_TABLE_UNIFORM 1
 
 /* Human-readable name of a status code.  Never NULL; static storage. */
 const char* qlora_status_string(int status);
@@ -98,6 +111,12 @@ const char* qlora_status_string(int status);
  * Either pointer may be NULL.  Host only; never touches the GPU.
  */
 int qlora_nf4_levels(float* levels, float* thresholds);
+
+/*
+ * The same for either level table (QLORA_TABLE_NF4 or QLORA_TABLE_UNIFORM);
+ * the thresholds follow the same rule.  Errors: UNSUPPORTED for another table.
+ */
+int qlora_table_levels(int32_t table, float* levels, float* thresholds);
 
 /*
  * Sizes in bytes of the three stored-weight buffers for descriptor d.

@@ -27,6 +27,7 @@ QLORA_ERR_HIP = -5
 EXPORTED = (
     "qlora_status_string",
     "qlora_nf4_levels",
+    "qlora_table_levels",
     "qlora_nf4_sizes",
     "qlora_quantize_nf4",
     "qlora_fwd_workspace_bytes",
@@ -54,7 +55,12 @@ class KernelStat(ctypes.Structure):
 
 class Nf4Desc(ctypes.Structure):
     _fields_ = [("d_out", ctypes.c_int64), ("d_in", ctypes.c_int64),
-                ("blocksize", ctypes.c_int32), ("dq_blocksize", ctypes.c_int32)]
+                ("blocksize", ctypes.c_int32), ("dq_blocksize", ctypes.c_int32), ("table", ctypes.c_int32)]
+
+
+# level tables (qlora_nf4_desc.table)
+TABLE_NF4 = 0
+TABLE_UNIFORM = 1
 
 
 _lib = None
@@ -74,6 +80,7 @@ def lib() -> ctypes.CDLL:
     L.qlora_status_string.argtypes = [ctypes.c_int]
     L.qlora_status_string.restype = ctypes.c_char_p
     L.qlora_nf4_levels.argtypes = [vp, vp]
+    L.qlora_table_levels.argtypes = [i32, vp, vp]
     L.qlora_nf4_sizes.argtypes = [dp, ctypes.POINTER(sz), ctypes.POINTER(sz), ctypes.POINTER(sz)]
     L.qlora_quantize_nf4.argtypes = [dp, vp, vp, vp, vp, vp]
     L.qlora_fwd_workspace_bytes.argtypes = [dp, i64, i32, ctypes.POINTER(sz)]
@@ -99,8 +106,8 @@ def _check(status: int, where: str):
         raise QloraError(status, where)
 
 
-def _desc(d_out: int, d_in: int, blocksize: int = 64, dq_blocksize: int = 256) -> Nf4Desc:
-    return Nf4Desc(int(d_out), int(d_in), int(blocksize), int(dq_blocksize))
+def _desc(d_out: int, d_in: int, blocksize: int = 64, dq_blocksize: int = 256, table: int = TABLE_NF4) -> Nf4Desc:
+    return Nf4Desc(int(d_out), int(d_in), int(blocksize), int(dq_blocksize), int(table))
 
 
 def _ptr(t) -> Optional[int]:
@@ -143,6 +150,16 @@ def qlora_nf4_levels():
     return np.frombuffer(lv, dtype=np.float32).copy(), np.frombuffer(th, dtype=np.float32).copy()
 
 
+def qlora_table_levels(table: int = TABLE_NF4):
+    """(levels float32[16], thresholds float32[15]) of level table `table`."""
+    import numpy as np
+    lv = (ctypes.c_float * 16)()
+    th = (ctypes.c_float * 15)()
+    _check(lib().qlora_table_levels(int(table), ctypes.cast(lv, ctypes.c_void_p), ctypes.cast(th, ctypes.c_void_p)),
+           "qlora_table_levels")
+    return np.frombuffer(lv, dtype=np.float32).copy(), np.frombuffer(th, dtype=np.float32).copy()
+
+
 def qlora_nf4_sizes(d_out: int, d_in: int, blocksize: int = 64, dq_blocksize: int = 256) -> Tuple[int, int, int]:
     d = _desc(d_out, d_in, blocksize, dq_blocksize)
     a, b, c = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
@@ -182,7 +199,7 @@ def _workspace(nbytes: int, device, workspace=None):
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
-def qlora_quantize_nf4(W, packed=None, codes=None, consts=None, stream=None):
+def qlora_quantize_nf4(W, packed=None, codes=None, consts=None, stream=None, table: int = TABLE_NF4):
     """Quantize fp32 W [d_out][d_in] (GPU) -> (packed uint8 [d_out][d_in/2],
     codes uint8 [nb], consts float32 [ng])."""
     import torch
@@ -198,14 +215,14 @@ def qlora_quantize_nf4(W, packed=None, codes=None, consts=None, stream=None):
     if consts is None:
         consts = torch.empty(n_k // 4, dtype=torch.float32, device=W.device)
     _need_cuda(packed, codes, consts, name="qlora_quantize_nf4")
-    d = _desc(d_out, d_in)
+    d = _desc(d_out, d_in, table=table)
     _check(lib().qlora_quantize_nf4(ctypes.byref(d), _ptr(W), _ptr(packed), _ptr(codes), _ptr(consts),
                                     _stream(stream)), "qlora_quantize_nf4")
     return packed, codes, consts
 
 
 def qlora_linear_fwd(packed, codes, consts, X, A, B, alpha: float, Y=None, U_out=None,
-                     want_u: bool = True, workspace=None, stream=None):
+                     want_u: bool = True, workspace=None, stream=None, table: int = TABLE_NF4):
     """Forward: returns (Y bf16 [T][d_out], U fp32 [T][r] or None).
 
     ``packed`` [d_out][d_in/2] fixes the layer shape; X bf16 [T][d_in],
@@ -225,7 +242,7 @@ def qlora_linear_fwd(packed, codes, consts, X, A, B, alpha: float, Y=None, U_out
         U_out = torch.empty((T, r), dtype=torch.float32, device=X.device)
     nbytes = qlora_fwd_workspace_bytes(d_out, d_in, T, r)
     ws = _workspace(nbytes, X.device, workspace)
-    d = _desc(d_out, d_in)
+    d = _desc(d_out, d_in, table=table)
     _check(lib().qlora_linear_fwd(ctypes.byref(d), _ptr(packed), _ptr(codes), _ptr(consts), T, _ptr(X), r,
                                   float(alpha), _ptr(A), _ptr(B), _ptr(Y), _ptr(U_out), _ptr(ws), nbytes,
                                   _stream(stream)), "qlora_linear_fwd")
@@ -233,7 +250,7 @@ def qlora_linear_fwd(packed, codes, consts, X, A, B, alpha: float, Y=None, U_out
 
 
 def qlora_linear_bwd(packed, codes, consts, X, A, B, alpha: float, dY, U_in=None, dX=None, dA=None, dB=None,
-                     want_dx: bool = True, workspace=None, stream=None):
+                     want_dx: bool = True, workspace=None, stream=None, table: int = TABLE_NF4):
     """Backward: returns (dX bf16 [T][d_in] or None, dA fp32 [r][d_in], dB fp32 [d_out][r])."""
     import torch
     d_out, d_in = packed.shape[0], packed.shape[1] * 2
@@ -252,14 +269,14 @@ def qlora_linear_bwd(packed, codes, consts, X, A, B, alpha: float, dY, U_in=None
             dB = torch.empty((d_out, r), dtype=torch.float32, device=X.device)
     nbytes = qlora_bwd_workspace_bytes(d_out, d_in, T, r)
     ws = _workspace(nbytes, X.device, workspace)
-    d = _desc(d_out, d_in)
+    d = _desc(d_out, d_in, table=table)
     _check(lib().qlora_linear_bwd(ctypes.byref(d), _ptr(packed), _ptr(codes), _ptr(consts), T, _ptr(X), r,
                                   float(alpha), _ptr(A), _ptr(B), _ptr(U_in), _ptr(dY), _ptr(dX), _ptr(dA),
                                   _ptr(dB), _ptr(ws), nbytes, _stream(stream)), "qlora_linear_bwd")
     return dX, dA, dB
 
 
-def qlora_dequantize_nf4(packed, codes, consts, W_hat=None, stream=None):
+def qlora_dequantize_nf4(packed, codes, consts, W_hat=None, stream=None, table: int = TABLE_NF4):
     """Restored weight: bf16 [d_out][d_in], bit-identical to what the fused
     products restore on chip."""
     import torch
@@ -267,13 +284,14 @@ def qlora_dequantize_nf4(packed, codes, consts, W_hat=None, stream=None):
     _need_cuda(packed, codes, consts, W_hat, name="qlora_dequantize_nf4")
     if W_hat is None:
         W_hat = torch.empty((d_out, d_in), dtype=torch.bfloat16, device=packed.device)
-    d = _desc(d_out, d_in)
+    d = _desc(d_out, d_in, table=table)
     _check(lib().qlora_dequantize_nf4(ctypes.byref(d), _ptr(packed), _ptr(codes), _ptr(consts), _ptr(W_hat),
                                       _stream(stream)), "qlora_dequantize_nf4")
     return W_hat
 
 
-def qlora_merge_lora(packed, codes, consts, A, B, alpha: float, W_merged=None, stream=None):
+def qlora_merge_lora(packed, codes, consts, A, B, alpha: float, W_merged=None, stream=None,
+                     table: int = TABLE_NF4):
     """The adapter merged into the restored weight: bf16 [d_out][d_in] =
     bf16(W_hat + (alpha / r) B A); A bf16 [r][d_in], B bf16 [d_out][r]."""
     import torch
@@ -285,7 +303,7 @@ def qlora_merge_lora(packed, codes, consts, A, B, alpha: float, W_merged=None, s
             raise ValueError(f"{nm} must be bfloat16")
     if W_merged is None:
         W_merged = torch.empty((d_out, d_in), dtype=torch.bfloat16, device=packed.device)
-    d = _desc(d_out, d_in)
+    d = _desc(d_out, d_in, table=table)
     _check(lib().qlora_merge_lora(ctypes.byref(d), _ptr(packed), _ptr(codes), _ptr(consts), int(r), float(alpha),
                                   _ptr(A), _ptr(B), _ptr(W_merged), _stream(stream)), "qlora_merge_lora")
     return W_merged

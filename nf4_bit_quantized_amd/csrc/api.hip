@@ -13,14 +13,15 @@
 
 namespace qlora {
 hipError_t launch_nf4_quantize(const float* W, uint8_t* packed, uint8_t* codes, float* consts,
-                               int64_t numel, hipStream_t stream);
+                               int64_t numel, int table, hipStream_t stream);
 bool decode_supported(int64_t N, int64_t K);
 hipError_t launch_decode(const uint8_t* packed, const uint8_t* codes, const float* consts, const uint16_t* X,
                          int64_t T, int64_t N, int64_t K, const uint16_t* Us, int64_t ldh, const uint16_t* B,
-                         int r, uint16_t* Y, hipStream_t stream);
+                         int r, uint16_t* Y, int table, hipStream_t stream);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
 hipError_t launch_export(const uint8_t* packed, const uint8_t* codes, const float* consts, int64_t N, int64_t K,
-                         int r, float s, const uint16_t* A, const uint16_t* B, uint16_t* W, hipStream_t stream);
+                         int r, float s, const uint16_t* A, const uint16_t* B, uint16_t* W, int table,
+                         hipStream_t stream);
 }  // namespace qlora
 
 using namespace qlora;
@@ -37,6 +38,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 int check_desc(const qlora_nf4_desc* d) {
   if (!d) return QLORA_ERR_NULL;
   if (d->blocksize != 64 || d->dq_blocksize != 256) return QLORA_ERR_UNSUPPORTED;
+  if (d->table != QLORA_TABLE_NF4 && d->table != QLORA_TABLE_UNIFORM) return QLORA_ERR_UNSUPPORTED;
   if (d->d_out <= 0 || d->d_in <= 0 || d->d_out % 64 != 0 || d->d_in % 64 != 0) return QLORA_ERR_SHAPE;
   return QLORA_OK;
 }
@@ -175,8 +177,11 @@ const char* qlora_status_string(int status) {
   }
 }
 
-int qlora_nf4_levels(float* levels, float* thresholds) {
-  const Nf4Table& t = nf4_table();
+int qlora_nf4_levels(float* levels, float* thresholds) { return qlora_table_levels(QLORA_TABLE_NF4, levels, thresholds); }
+
+int qlora_table_levels(int32_t table, float* levels, float* thresholds) {
+  if (table != QLORA_TABLE_NF4 && table != QLORA_TABLE_UNIFORM) return QLORA_ERR_UNSUPPORTED;
+  const Nf4Table& t = level_table(table);
   if (levels) std::memcpy(levels, t.level, sizeof(t.level));
   if (thresholds) std::memcpy(thresholds, t.thr, sizeof(t.thr));
   return QLORA_OK;
@@ -201,7 +206,7 @@ int qlora_quantize_nf4(const qlora_nf4_desc* d, const float* W, uint8_t* packed,
   if (st) return st;
   if (!W || !packed || !codes || !consts) return QLORA_ERR_NULL;
   if (!aligned16(W) || !aligned16(packed)) return QLORA_ERR_UNSUPPORTED;
-  HIP_TRY(launch_nf4_quantize(W, packed, codes, consts, d->d_out * d->d_in, (hipStream_t)stream));
+  HIP_TRY(launch_nf4_quantize(W, packed, codes, consts, d->d_out * d->d_in, d->table, (hipStream_t)stream));
   return QLORA_OK;
 }
 
@@ -219,7 +224,8 @@ int qlora_merge_lora(const qlora_nf4_desc* d, const uint8_t* packed, const uint8
   if (r > 0 && (!A || !B)) return QLORA_ERR_NULL;
   if (!aligned16(W_merged) || (r > 0 && (!aligned16(A) || !aligned16(B)))) return QLORA_ERR_UNSUPPORTED;
   const float s = r > 0 ? alpha / (float)r : 0.0f;
-  HIP_TRY(launch_export(packed, codes, consts, d->d_out, d->d_in, r, s, A, B, W_merged, (hipStream_t)stream));
+  HIP_TRY(launch_export(packed, codes, consts, d->d_out, d->d_in, r, s, A, B, W_merged, d->table,
+                        (hipStream_t)stream));
   return QLORA_OK;
 }
 
@@ -264,12 +270,12 @@ int qlora_linear_fwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8
     if (e) return e;
   }
   if (T <= kDecodeMaxT && decode_supported(N, K) && aligned16(codes)) {
-    HIP_TRY(launch_decode(packed, codes, consts, X, T, N, K, w.Us, hilo_ld(r), B, r, Y, s_));
+    HIP_TRY(launch_decode(packed, codes, consts, X, T, N, K, w.Us, hilo_ld(r), B, r, Y, d->table, s_));
     return QLORA_OK;
   }
   FusedParams fp{};
   fp.A = X; fp.lda = K;
-  fp.packed = packed; fp.codes = codes; fp.consts = consts; fp.Kw = K;
+  fp.packed = packed; fp.codes = codes; fp.consts = consts; fp.Kw = K; fp.table = d->table;
   fp.M = T; fp.N = N; fp.K0 = K;
   fp.At = w.Us; fp.ldat = hilo_ld(r); fp.Bt = B; fp.ldbt = r; fp.r = r;
   fp.C = Y; fp.ldc = N;
@@ -332,7 +338,7 @@ int qlora_linear_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8
     // dX = dY W_hat + (s G) A: the contraction runs over d_out, the rows of W
     FusedParams fp{};
     fp.A = dY; fp.lda = N;
-    fp.packed = packed; fp.codes = codes; fp.consts = consts; fp.Kw = K;
+    fp.packed = packed; fp.codes = codes; fp.consts = consts; fp.Kw = K; fp.table = d->table;
     fp.M = T; fp.N = K; fp.K0 = N;
     fp.At = w.Gs; fp.ldat = ldh; fp.Bt = A; fp.ldbt = K; fp.r = r;
     fp.C = dX; fp.ldc = K;

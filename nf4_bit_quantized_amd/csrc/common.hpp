@@ -21,6 +21,12 @@ struct Nf4Table {
 
 const Nf4Table& nf4_table();
 
+// Level tables a quantized weight can use (the choice is not stored with it;
+// every call on the weight passes the same one).
+constexpr int kTableNf4 = 0;      // the NF4 table above
+constexpr int kTableUniform = 1;  // 16 equally spaced levels -1 + 2i/15
+const Nf4Table& level_table(int table);
+
 // Decision tables of the quantization kernel (built on the host from the
 // thresholds above, passed by value).  A normalized value y is first
 // estimated as y' = x * rcp(s), within a few ulp of fl32(x / s).  The top 16
@@ -38,8 +44,10 @@ struct QuantLut {
   double mid[16];
 };
 
-// The table above; ok is false if some widened bucket held two thresholds.
+// The table above (NF4, or that of level table `table`); ok is false if some
+// widened bucket held two thresholds.
 const QuantLut& quant_lut(bool* ok);
+const QuantLut& quant_lut(int table, bool* ok);
 
 // Workgroup barrier that orders LDS only: waits for this wave's LDS
 // operations, then s_barrier.  (__syncthreads() also waits for every

@@ -397,7 +397,7 @@ bool decode_supported(int64_t N, int64_t K) {
 
 hipError_t launch_decode(const uint8_t* packed, const uint8_t* codes, const float* consts, const uint16_t* X,
                          int64_t T, int64_t N, int64_t K, const uint16_t* Us, int64_t ldh, const uint16_t* B,
-                         int r, uint16_t* Y, hipStream_t stream) {
+                         int r, uint16_t* Y, int table, hipStream_t stream) {
   // byte offsets into the packed weight, codes and X are 32-bit
   if (T < 1 || T > 16 || N % 16 != 0 || K % 64 != 0 || N * K / 2 > 0x7FFFFFF0LL) return hipErrorInvalidValue;
   DecodeParams P;
@@ -405,7 +405,7 @@ hipError_t launch_decode(const uint8_t* packed, const uint8_t* codes, const floa
   P.T = T; P.N = N; P.K = K;
   P.Us = Us; P.ldh = ldh; P.B = B; P.r = r;
   P.Y = Y;
-  const Nf4Table& tab = nf4_table();
+  const Nf4Table& tab = level_table(table);
   for (int i = 0; i < 16; ++i) P.level[i] = tab.level[i];
   // tiles per workgroup: the 16-row tiles spread over the 256 CUs (at most 8 each)
   const int64_t ntiles = N / 16;

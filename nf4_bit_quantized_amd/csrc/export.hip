@@ -180,14 +180,15 @@ __global__ __launch_bounds__(256) void k_dequant(ExportParams P) {
 }  // namespace
 
 hipError_t launch_export(const uint8_t* packed, const uint8_t* codes, const float* consts, int64_t N, int64_t K,
-                         int r, float s, const uint16_t* A, const uint16_t* B, uint16_t* W, hipStream_t stream) {
+                         int r, float s, const uint16_t* A, const uint16_t* B, uint16_t* W, int table,
+                         hipStream_t stream) {
   if (N % TR != 0 || K % 64 != 0 || r < 0 || r > MAX_R) return hipErrorInvalidValue;
   ExportParams P;
   P.packed = packed; P.codes = codes; P.consts = consts;
   P.N = N; P.K = K;
   P.A = A; P.B = B; P.r = r; P.s = s;
   P.W = W;
-  P.tab = nf4_table();
+  P.tab = level_table(table);
   const dim3 grid((unsigned)((K + TC - 1) / TC), (unsigned)(N / TR));
   TraceScope ts(KID_EXPORT, stream);
   if (r > 0) {

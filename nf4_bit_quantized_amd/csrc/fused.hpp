@@ -22,8 +22,9 @@ struct FusedParams {
   int32_t r;               // rank (0: no tail)
   uint16_t* C;             // bf16 output [M][ldc]
   int64_t ldc;
+  int32_t table;           // level table (kTableNf4 / kTableUniform)
   int32_t mt, nt, group_m; // filled by the launcher
-  Nf4Table tab;            // filled by the launcher
+  Nf4Table tab;            // filled by the launcher from table
 };
 
 hipError_t launch_fused(FusedParams P, bool dx, hipStream_t stream, int kernel_id);

@@ -539,7 +539,7 @@ hipError_t launch_fused(FusedParams P, bool dx, hipStream_t stream, int kernel_i
   P.mt = (int32_t)((P.M + 255) / 256);
   P.nt = (int32_t)((P.N + bn - 1) / bn);
   P.group_m = 2;
-  P.tab = nf4_table();
+  P.tab = level_table(P.table);
   const int64_t ntiles = (int64_t)P.mt * P.nt;
   const unsigned grid = (unsigned)(((ntiles + 7) / 8) * 8);
   TraceScope ts(kernel_id, stream);

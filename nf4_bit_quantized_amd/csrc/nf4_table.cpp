@@ -12,6 +12,10 @@
 // complementary error function of the C library, in double precision, and
 // the levels are rounded to float32 once.
 //
+// The uniform table ("7、QLoRA 量化微调" §7.1): 16 equally spaced levels
+// -1 + 2i/15 on [-1, 1] (computed in double, rounded to float32 once); it has
+// no zero level.  Same thresholds rule.
+//
 // Thresholds: thr[k] is the largest float32 x with |x - T[k]| <= |x - T[k+1]|,
 // i.e. the exact midpoint (T[k] + T[k+1]) / 2 (exact in double) rounded toward
 // minus infinity to float32.  Counting the thresholds that a normalized value
@@ -45,6 +49,23 @@ double normal_quantile(double p) {
   return x;
 }
 
+// thr[k] from the levels: the exact midpoint, rounded toward minus infinity
+void set_thresholds(Nf4Table& t) {
+  for (int k = 0; k < 15; ++k) {
+    const double m = ((double)t.level[k] + (double)t.level[k + 1]) * 0.5;  // exact
+    float f = (float)m;
+    if ((double)f > m) f = std::nextafter(f, -INFINITY);
+    t.thr[k] = f;
+  }
+}
+
+Nf4Table build_uniform_table() {
+  Nf4Table t;
+  for (int i = 0; i < 16; ++i) t.level[i] = (float)(-1.0 + 2.0 * i / 15.0);
+  set_thresholds(t);
+  return t;
+}
+
 Nf4Table build_table() {
   std::vector<double> neg, pos;
   for (int j = 0; j < 7; ++j) neg.push_back(normal_quantile((j + 0.5) / 14.0));
@@ -60,12 +81,7 @@ Nf4Table build_table() {
 
   Nf4Table t;
   for (int i = 0; i < 16; ++i) t.level[i] = (float)lv[i];
-  for (int k = 0; k < 15; ++k) {
-    const double m = ((double)t.level[k] + (double)t.level[k + 1]) * 0.5;  // exact
-    float f = (float)m;
-    if ((double)f > m) f = std::nextafter(f, -INFINITY);
-    t.thr[k] = f;
-  }
+  set_thresholds(t);
   return t;
 }
 
@@ -115,11 +131,23 @@ const Nf4Table& nf4_table() {
   return table;
 }
 
-const QuantLut& quant_lut(bool* ok) {
-  static bool good = false;
-  static const QuantLut lut = build_lut(nf4_table(), &good);
-  *ok = good;
-  return lut;
+const Nf4Table& level_table(int table) {
+  static const Nf4Table uniform = build_uniform_table();
+  return table == kTableUniform ? uniform : nf4_table();
+}
+
+const QuantLut& quant_lut(bool* ok) { return quant_lut(kTableNf4, ok); }
+
+const QuantLut& quant_lut(int table, bool* ok) {
+  static bool good_nf4 = false, good_uniform = false;
+  static const QuantLut lut_nf4 = build_lut(nf4_table(), &good_nf4);
+  static const QuantLut lut_uniform = build_lut(level_table(kTableUniform), &good_uniform);
+  if (table == kTableUniform) {
+    *ok = good_uniform;
+    return lut_uniform;
+  }
+  *ok = good_nf4;
+  return lut_nf4;
 }
 
 }  // namespace qlora

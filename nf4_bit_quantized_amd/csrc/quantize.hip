@@ -146,9 +146,9 @@ __global__ __launch_bounds__(256) void k_nf4_quantize(const float* __restrict__ 
 }
 
 hipError_t launch_nf4_quantize(const float* W, uint8_t* packed, uint8_t* codes, float* consts,
-                               int64_t numel, hipStream_t stream) {
+                               int64_t numel, int table, hipStream_t stream) {
   bool ok = false;
-  const QuantLut& lut = quant_lut(&ok);
+  const QuantLut& lut = quant_lut(table, &ok);
   if (!ok) return hipErrorInvalidValue;
   const int64_t nb = numel / 64;
   const int64_t ng = (nb + 255) / 256;

@@ -47,11 +47,12 @@ def oracle_quantized(W):
     return onf4.quantize(W)
 
 
-def oracle_layer(inp, r, alpha, Q=None, do_bwd=True):
-    """Oracle forward (+backward) on a workloads.layer_inputs dict."""
+def oracle_layer(inp, r, alpha, Q=None, do_bwd=True, levels=None):
+    """Oracle forward (+backward) on a workloads.layer_inputs dict (levels:
+    None for the NF4 table, else the table's 16 levels)."""
     if Q is None:
-        Q = onf4.quantize(inp["W"])
-    W_hat = onf4.dequantize(Q).astype(np.float64)
+        Q = onf4.quantize(inp["W"], levels=levels)
+    W_hat = onf4.dequantize(Q, levels=levels).astype(np.float64)
     X = bits_to_float(inp["X"])
     A = bits_to_float(inp["A"]) if r > 0 else None
     B = bits_to_float(inp["B"]) if r > 0 else None
@@ -64,21 +65,21 @@ def oracle_layer(inp, r, alpha, Q=None, do_bwd=True):
     return out
 
 
-def gpu_layer(inp, r, alpha, do_bwd=True, pass_u=True):
+def gpu_layer(inp, r, alpha, do_bwd=True, pass_u=True, table=0):
     """Quantize + forward (+ backward) through the C ABI; returns host arrays."""
     import torch
     import nf4_bit_quantized_amd as q
     W = dev_f32(inp["W"])
-    packed, codes, consts = q.qlora_quantize_nf4(W)
+    packed, codes, consts = q.qlora_quantize_nf4(W, table=table)
     X = dev_bf16(inp["X"])
     A = dev_bf16(inp["A"]) if r > 0 else None
     B = dev_bf16(inp["B"]) if r > 0 else None
-    Y, U = q.qlora_linear_fwd(packed, codes, consts, X, A, B, alpha)
+    Y, U = q.qlora_linear_fwd(packed, codes, consts, X, A, B, alpha, table=table)
     out = {"packed": packed, "codes": codes, "consts": consts}
     if do_bwd:
         dY = dev_bf16(inp["dY"])
         dX, dA, dB = q.qlora_linear_bwd(packed, codes, consts, X, A, B, alpha, dY,
-                                        U_in=U if pass_u else None)
+                                        U_in=U if pass_u else None, table=table)
     torch.cuda.synchronize()
     out["Y"] = host_bf16_to_f64(Y)
     out["U"] = U.cpu().numpy().astype(np.float64) if U is not None else None
@@ -96,3 +97,28 @@ def assert_quant_bit_exact(g, Q):
     np.testing.assert_array_equal(g["packed_h"], Q.packed)
     np.testing.assert_array_equal(g["codes_h"], Q.codes)
     np.testing.assert_array_equal(g["consts_h"].view(np.uint32), Q.consts.view(np.uint32))
+
+
+def sweep_blocks(scale, thr, per=63, width=40):
+    """Blocks whose absmax is exactly +-scale, holding the float32 neighbours of
+    thr[k] * scale for every threshold k (so that fl32(w / scale) walks across
+    each decision point)."""
+    scale = np.float32(scale)
+    vals = []
+    for k in range(15):
+        c = np.float32(np.float64(thr[k]) * np.float64(scale))
+        vals.append(c)
+        for d in (np.float32(np.inf), np.float32(-np.inf)):
+            v = c
+            for _ in range(width):
+                v = np.nextafter(v, d, dtype=np.float32)
+                vals.append(v)
+    vals = np.array(vals, np.float32)
+    vals = vals[np.abs(vals) <= scale]
+    nblk = -(-vals.size // per)
+    W = np.zeros((nblk, 64), np.float32)
+    for b in range(nblk):
+        chunk = vals[b * per:(b + 1) * per]
+        W[b, 0] = scale if b % 2 == 0 else -scale
+        W[b, 1:1 + chunk.size] = chunk
+    return W.reshape(-1)

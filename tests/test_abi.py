@@ -58,6 +58,29 @@ def test_library_thresholds_reproduce_oracle_nearest_level():
         assert onf4._nearest_level(above, T)[0] == k + 1
 
 
+def test_uniform_table_is_the_oracles():
+    levels, thr = q.qlora_table_levels(q.TABLE_UNIFORM)
+    U = onf4.uniform_levels()
+    np.testing.assert_array_equal(levels.view(np.uint32), U.view(np.uint32))
+    for k in range(15):
+        at = np.array([thr[k]], np.float32)
+        above = np.nextafter(at, np.float32(np.inf))
+        assert onf4._nearest_level(at, U)[0] == k
+        assert onf4._nearest_level(above, U)[0] == k + 1
+    # the NF4 table through the same call
+    levels, _ = q.qlora_table_levels(q.TABLE_NF4)
+    np.testing.assert_array_equal(levels.view(np.uint32), onf4.nf4_levels().view(np.uint32))
+
+
+def test_unknown_table_rejected():
+    L = q.lib()
+    assert L.qlora_table_levels(2, None, None) == q.QLORA_ERR_UNSUPPORTED
+    d = q._desc(64, 64, table=2)
+    a, b, c = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    assert L.qlora_nf4_sizes(ctypes.byref(d), ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)) == \
+        q.QLORA_ERR_UNSUPPORTED
+
+
 def test_sizes():
     p, c, k = q.qlora_nf4_sizes(4096, 4096)
     assert p == 4096 * 4096 // 2 and c == 4096 * 4096 // 64 and k == 4 * (4096 * 4096 // 64 // 256)

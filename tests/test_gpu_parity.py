@@ -7,7 +7,7 @@ import pytest
 
 import workloads
 from gpu_helpers import (TOL, assert_quant_bit_exact, gpu_layer, normwise_err, oracle_layer, say,
-                         dev_bf16, dev_f32, host_bf16_to_f64)
+                         dev_bf16, dev_f32, host_bf16_to_f64, sweep_blocks)
 from oracle import nf4 as onf4
 from oracle.bf16 import bits_to_float, float_to_bits
 
@@ -67,31 +67,6 @@ def test_quantize_threshold_sweep_bit_exact():
                             "consts_h": consts.cpu().numpy()}, Q)
 
 
-def _sweep_blocks(scale, thr, per=63, width=40):
-    """Blocks whose absmax is exactly +-scale, holding the float32 neighbours of
-    thr[k] * scale for every threshold k (so that fl32(w / scale) walks across
-    each decision point)."""
-    scale = np.float32(scale)
-    vals = []
-    for k in range(15):
-        c = np.float32(np.float64(thr[k]) * np.float64(scale))
-        vals.append(c)
-        for d in (np.float32(np.inf), np.float32(-np.inf)):
-            v = c
-            for _ in range(width):
-                v = np.nextafter(v, d, dtype=np.float32)
-                vals.append(v)
-    vals = np.array(vals, np.float32)
-    vals = vals[np.abs(vals) <= scale]
-    nblk = -(-vals.size // per)
-    W = np.zeros((nblk, 64), np.float32)
-    for b in range(nblk):
-        chunk = vals[b * per:(b + 1) * per]
-        W[b, 0] = scale if b % 2 == 0 else -scale
-        W[b, 1:1 + chunk.size] = chunk
-    return W.reshape(-1)
-
-
 @pytest.mark.parametrize("scales", [
     (0.0123, 0.3, 7.25, 1.0e-3, 2.0 ** -20),
     (1.0e-20, 3.0e-30, 1.0e-38, 1.0e-39, 5.0e-42),     # tiny, down to subnormal block scales
@@ -103,7 +78,7 @@ def test_quantize_threshold_sweep_scaled_bit_exact(scales):
     import nf4_bit_quantized_amd as q
     import torch
     _, thr = q.qlora_nf4_levels()
-    parts = [_sweep_blocks(sc, thr) for sc in scales]
+    parts = [sweep_blocks(sc, thr) for sc in scales]
     W = np.concatenate(parts)
     pad = (-W.size) % (64 * 64)
     W = np.concatenate([W, np.zeros(pad, np.float32)]).reshape(64, -1)
