@@ -222,6 +222,42 @@ def export_section(lin, steps):
     return out
 
 
+def quantize16_section(lin, steps):
+    """Quantization of the attention-shaped weight handed over as bf16 and as
+    fp16 (2 bytes in per weight instead of 4), rotating 8 copies of the
+    weight (268 MB) so the 256 MB MALL cannot hold them."""
+    import torch
+    import nf4_bit_quantized_amd as q
+    import workloads
+
+    N, K = lin.d_out, lin.d_in
+    W = workloads.layer_inputs(N, K, 1, 1, lin.seed, with_dy=False)["W"]
+    copies = 8
+    out = {}
+    for name, dt in (("bf16", torch.bfloat16), ("fp16", torch.float16)):
+        w16 = torch.from_numpy(W).cuda().to(dt)
+        reps = [w16.clone() for _ in range(copies)]
+        del w16
+        bufs = [q.qlora_quantize_nf4(reps[i]) for i in range(copies)]
+        torch.cuda.synchronize()
+        q.qlora_trace_read(reset=True)
+        q.qlora_trace_select({"nf4_quantize"})
+        for i in range(steps):
+            q.qlora_quantize_nf4(reps[i % copies], *bufs[i % copies])
+        torch.cuda.synchronize()
+        q.qlora_trace_enable(False)
+        n, ms = q.qlora_trace_read(reset=True).get("nf4_quantize", (1, float("nan")))
+        avg = ms / max(n, 1)
+        pk, cd, cs = bufs[0]
+        nbytes = N * K * 2 + pk.numel() + cd.numel() + cs.numel() * 4
+        out[name] = {"d_out": N, "d_in": K, "bytes": nbytes, "kernel_us": round(avg * 1e3, 2),
+                     "GBps": round(nbytes / (avg * 1e-3) / 1e9, 1),
+                     "frac_hbm": round(nbytes / (avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+        log("quantize16", name, out[name])
+        del reps, bufs
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -337,6 +373,7 @@ def main():
     if not args.no_decode:
         result["decode_packed_weight"] = decode_section(steps=max(20, args.steps), warmup=5)
         result["export_bf16"] = export_section(lin, steps=max(20, args.steps))
+        result["quantize_16bit_weight"] = quantize16_section(lin, steps=max(20, args.steps))
     if not args.no_cpu_baseline:
         log("timing the oracle on the host ...")
         result["cpu_baseline"] = cpu_baseline(inp, lin, args.cpu_seconds)

@@ -139,6 +139,22 @@ int qlora_quantize_nf4(const qlora_nf4_desc* d, const float* W, uint8_t* packed,
                        float* consts, void* stream);
 
 /*
+ * The same quantization of a base weight held in a 16-bit format
+ * ("QLoRA技术从入门到精通" §3(1): the FP16 base model is converted offline to
+ * the 4-bit form).  w_format: QLORA_W_F32 (W is float*, the call above),
+ * QLORA_W_BF16 or QLORA_W_F16 (W is [N][K] uint16 bit patterns).  Each value
+ * is widened exactly to fp32 and then quantized as above, so the outputs are
+ * bit-identical to qlora_quantize_nf4 on the widened weight.  W and packed
+ * 16-byte aligned.  Errors: NULL, SHAPE, UNSUPPORTED (unknown w_format,
+ * alignment), HIP.
+ */
+#define QLORA_W_F32 0
+#define QLORA_W_BF16 1
+#define QLORA_W_F16 2
+int qlora_quantize_nf4_typed(const qlora_nf4_desc* d, const void* W, int32_t w_format, uint8_t* packed,
+                             uint8_t* codes, float* consts, void* stream);
+
+/*
  * Workspace (device bytes) qlora_linear_fwd needs for T tokens and rank r.
  * Host only.  Errors: NULL, SHAPE, UNSUPPORTED.
  */

@@ -23,6 +23,11 @@ QLORA_ERR_UNSUPPORTED = -3
 QLORA_ERR_WORKSPACE = -4
 QLORA_ERR_HIP = -5
 
+# element formats of the weight handed to quantization
+QLORA_W_F32 = 0
+QLORA_W_BF16 = 1
+QLORA_W_F16 = 2
+
 # Every exported symbol of include/qlora.h
 EXPORTED = (
     "qlora_status_string",
@@ -30,6 +35,7 @@ EXPORTED = (
     "qlora_table_levels",
     "qlora_nf4_sizes",
     "qlora_quantize_nf4",
+    "qlora_quantize_nf4_typed",
     "qlora_fwd_workspace_bytes",
     "qlora_linear_fwd",
     "qlora_bwd_workspace_bytes",
@@ -83,6 +89,7 @@ def lib() -> ctypes.CDLL:
     L.qlora_table_levels.argtypes = [i32, vp, vp]
     L.qlora_nf4_sizes.argtypes = [dp, ctypes.POINTER(sz), ctypes.POINTER(sz), ctypes.POINTER(sz)]
     L.qlora_quantize_nf4.argtypes = [dp, vp, vp, vp, vp, vp]
+    L.qlora_quantize_nf4_typed.argtypes = [dp, vp, i32, vp, vp, vp, vp]
     L.qlora_fwd_workspace_bytes.argtypes = [dp, i64, i32, ctypes.POINTER(sz)]
     L.qlora_bwd_workspace_bytes.argtypes = [dp, i64, i32, ctypes.POINTER(sz)]
     L.qlora_linear_fwd.argtypes = [dp, vp, vp, vp, i64, vp, i32, f32, vp, vp, vp, vp, vp, sz, vp]
@@ -200,12 +207,14 @@ def _workspace(nbytes: int, device, workspace=None):
 
 
 def qlora_quantize_nf4(W, packed=None, codes=None, consts=None, stream=None, table: int = TABLE_NF4):
-    """Quantize fp32 W [d_out][d_in] (GPU) -> (packed uint8 [d_out][d_in/2],
-    codes uint8 [nb], consts float32 [ng])."""
+    """Quantize W [d_out][d_in] (GPU; float32, bfloat16 or float16) ->
+    (packed uint8 [d_out][d_in/2], codes uint8 [nb], consts float32 [ng]).
+    A 16-bit W is widened exactly to fp32 inside the kernel."""
     import torch
     _need_cuda(W, name="qlora_quantize_nf4")
-    if W.dtype != torch.float32 or W.dim() != 2:
-        raise ValueError("W must be a 2-D float32 tensor")
+    fmts = {torch.float32: QLORA_W_F32, torch.bfloat16: QLORA_W_BF16, torch.float16: QLORA_W_F16}
+    if W.dtype not in fmts or W.dim() != 2:
+        raise ValueError("W must be a 2-D float32, bfloat16 or float16 tensor")
     d_out, d_in = W.shape
     n_p, n_c, n_k = qlora_nf4_sizes(d_out, d_in)
     if packed is None:
@@ -216,8 +225,12 @@ def qlora_quantize_nf4(W, packed=None, codes=None, consts=None, stream=None, tab
         consts = torch.empty(n_k // 4, dtype=torch.float32, device=W.device)
     _need_cuda(packed, codes, consts, name="qlora_quantize_nf4")
     d = _desc(d_out, d_in, table=table)
-    _check(lib().qlora_quantize_nf4(ctypes.byref(d), _ptr(W), _ptr(packed), _ptr(codes), _ptr(consts),
-                                    _stream(stream)), "qlora_quantize_nf4")
+    if W.dtype == torch.float32:
+        _check(lib().qlora_quantize_nf4(ctypes.byref(d), _ptr(W), _ptr(packed), _ptr(codes), _ptr(consts),
+                                        _stream(stream)), "qlora_quantize_nf4")
+    else:
+        _check(lib().qlora_quantize_nf4_typed(ctypes.byref(d), _ptr(W), fmts[W.dtype], _ptr(packed), _ptr(codes),
+                                              _ptr(consts), _stream(stream)), "qlora_quantize_nf4_typed")
     return packed, codes, consts
 
 

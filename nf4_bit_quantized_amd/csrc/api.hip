@@ -12,7 +12,7 @@
 #include "../../include/qlora.h"
 
 namespace qlora {
-hipError_t launch_nf4_quantize(const float* W, uint8_t* packed, uint8_t* codes, float* consts,
+hipError_t launch_nf4_quantize(const void* W, int wformat, uint8_t* packed, uint8_t* codes, float* consts,
                                int64_t numel, int table, hipStream_t stream);
 bool decode_supported(int64_t N, int64_t K);
 hipError_t launch_decode(const uint8_t* packed, const uint8_t* codes, const float* consts, const uint16_t* X,
@@ -202,11 +202,20 @@ int qlora_nf4_sizes(const qlora_nf4_desc* d, size_t* packed_bytes, size_t* codes
 
 int qlora_quantize_nf4(const qlora_nf4_desc* d, const float* W, uint8_t* packed, uint8_t* codes,
                        float* consts, void* stream) {
+  return qlora_quantize_nf4_typed(d, W, QLORA_W_F32, packed, codes, consts, stream);
+}
+
+int qlora_quantize_nf4_typed(const qlora_nf4_desc* d, const void* W, int32_t w_format, uint8_t* packed,
+                             uint8_t* codes, float* consts, void* stream) {
   const int st = check_desc(d);
   if (st) return st;
   if (!W || !packed || !codes || !consts) return QLORA_ERR_NULL;
+  static_assert(QLORA_W_F32 == kWeightF32 && QLORA_W_BF16 == kWeightBf16 && QLORA_W_F16 == kWeightF16,
+                "weight formats");
+  if (w_format != QLORA_W_F32 && w_format != QLORA_W_BF16 && w_format != QLORA_W_F16) return QLORA_ERR_UNSUPPORTED;
   if (!aligned16(W) || !aligned16(packed)) return QLORA_ERR_UNSUPPORTED;
-  HIP_TRY(launch_nf4_quantize(W, packed, codes, consts, d->d_out * d->d_in, d->table, (hipStream_t)stream));
+  HIP_TRY(launch_nf4_quantize(W, w_format, packed, codes, consts, d->d_out * d->d_in, d->table,
+                              (hipStream_t)stream));
   return QLORA_OK;
 }
 

@@ -27,6 +27,11 @@ constexpr int kTableNf4 = 0;      // the NF4 table above
 constexpr int kTableUniform = 1;  // 16 equally spaced levels -1 + 2i/15
 const Nf4Table& level_table(int table);
 
+// Element formats of the fp weight handed to the quantization kernel.
+constexpr int kWeightF32 = 0;
+constexpr int kWeightBf16 = 1;
+constexpr int kWeightF16 = 2;
+
 // Decision tables of the quantization kernel (built on the host from the
 // thresholds above, passed by value).  A normalized value y is first
 // estimated as y' = x * rcp(s), within a few ulp of fl32(x / s).  The top 16

@@ -9,9 +9,14 @@
 // (its largest scale), unsigned 8-bit codes linear on [0, c_g] rounded half
 // to even.  Indices use the exact block scale.
 //
+// The base weight may also arrive as bf16 or fp16 (the pages quantize an FP16
+// model offline): each value is widened exactly to fp32 on load, after which
+// the steps are the same, so the result equals quantizing the widened weight.
+//
 // One workgroup = one second-level group = 256 blocks = 16384 weights.
 // 256 threads; thread t loads float4 number i*256 + t (i = 0..15) of the
-// group, so each load instruction is a fully coalesced 4 KiB row; a float4
+// group (four 16-bit values, 8 bytes, for a 16-bit weight), so each load
+// instruction is a fully coalesced 4 KiB (2 KiB) row; a float4
 // belongs to block i*16 + t/16, shared by 16 consecutive lanes, whose absmax
 // is reduced with four xor-shuffles inside those 16 lanes.  All sixteen loads
 // are issued first; float4 i is quantized and stored as soon as it arrives,
@@ -47,7 +52,8 @@ __device__ __forceinline__ float row_max16(float m) {
   return m;
 }
 
-__global__ __launch_bounds__(256) void k_nf4_quantize(const float* __restrict__ W,
+template <int WF>
+__global__ __launch_bounds__(256) void k_nf4_quantize(const void* __restrict__ W,
                                                       uint8_t* __restrict__ packed,
                                                       uint8_t* __restrict__ codes,
                                                       float* __restrict__ consts, int64_t nb,
@@ -65,6 +71,7 @@ __global__ __launch_bounds__(256) void k_nf4_quantize(const float* __restrict__ 
   const int64_t blk0 = g * 256;
   const int nblk = (int)((nb - blk0) < 256 ? (nb - blk0) : 256);
   typedef float f4_t __attribute__((ext_vector_type(4)));
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
   // decision tables: read before the weights, written to LDS after them
   const uint32_t* lw = reinterpret_cast<const uint32_t*>(lut.kidx);
@@ -74,12 +81,29 @@ __global__ __launch_bounds__(256) void k_nf4_quantize(const float* __restrict__ 
 
   // the group's weights through a buffer resource sized to its blocks, so the
   // float4s of a ragged last group past the end read as zero
+  constexpr int EB = WF == kWeightF32 ? 4 : 2;  // bytes per weight
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(W) + blk0 * 64, (short)0, nblk * 256, 0x00020000);
+      const_cast<char*>(static_cast<const char*>(W)) + blk0 * 64 * EB, (short)0, nblk * 64 * EB, 0x00020000);
   f4_t v[16];
+  if constexpr (WF == kWeightF32) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
-    v[i] = __builtin_bit_cast(f4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (i * 256 + t) * 16, 0, 0));
+    for (int i = 0; i < 16; ++i)
+      v[i] = __builtin_bit_cast(f4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (i * 256 + t) * 16, 0, 0));
+  } else {
+    u32x2_t h[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) h[i] = __builtin_amdgcn_raw_buffer_load_b64(rsrc, (i * 256 + t) * 8, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t u[4] = {h[i].x & 0xFFFFu, h[i].x >> 16, h[i].y & 0xFFFFu, h[i].y >> 16};
+      float f[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        f[e] = WF == kWeightBf16 ? __builtin_bit_cast(float, u[e] << 16)
+                                 : (float)__builtin_bit_cast(_Float16, (uint16_t)u[e]);
+      v[i] = f4_t{f[0], f[1], f[2], f[3]};
+    }
+  }
   sh_lut[t] = lut_a;
   sh_lut[t + 256] = lut_b;
   sh_mid[t & 15] = mid;   // 16 threads write each entry, all the same value
@@ -145,7 +169,7 @@ __global__ __launch_bounds__(256) void k_nf4_quantize(const float* __restrict__ 
   for (int c = t; c < nblk * 2; c += 256) dst[c] = srcp[c];
 }
 
-hipError_t launch_nf4_quantize(const float* W, uint8_t* packed, uint8_t* codes, float* consts,
+hipError_t launch_nf4_quantize(const void* W, int wformat, uint8_t* packed, uint8_t* codes, float* consts,
                                int64_t numel, int table, hipStream_t stream) {
   bool ok = false;
   const QuantLut& lut = quant_lut(table, &ok);
@@ -153,8 +177,17 @@ hipError_t launch_nf4_quantize(const float* W, uint8_t* packed, uint8_t* codes, 
   const int64_t nb = numel / 64;
   const int64_t ng = (nb + 255) / 256;
   TraceScope ts(KID_QUANTIZE, stream);
-  hipLaunchKernelGGL(k_nf4_quantize, dim3((unsigned)ng), dim3(256), 0, stream, W, packed, codes,
-                     consts, nb, lut);
+  if (wformat == kWeightF32)
+    hipLaunchKernelGGL(k_nf4_quantize<kWeightF32>, dim3((unsigned)ng), dim3(256), 0, stream, W, packed, codes,
+                       consts, nb, lut);
+  else if (wformat == kWeightBf16)
+    hipLaunchKernelGGL(k_nf4_quantize<kWeightBf16>, dim3((unsigned)ng), dim3(256), 0, stream, W, packed, codes,
+                       consts, nb, lut);
+  else if (wformat == kWeightF16)
+    hipLaunchKernelGGL(k_nf4_quantize<kWeightF16>, dim3((unsigned)ng), dim3(256), 0, stream, W, packed, codes,
+                       consts, nb, lut);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

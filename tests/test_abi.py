@@ -155,6 +155,20 @@ def test_export_validation_happens_before_any_launch():
         q.QLORA_ERR_UNSUPPORTED
 
 
+def test_typed_quantize_validation_happens_before_any_launch():
+    fake = 0x10000
+    d = q._desc(64, 64)
+    L = q.lib()
+    assert L.qlora_quantize_nf4_typed(ctypes.byref(d), fake, 3, fake, fake, fake, None) == q.QLORA_ERR_UNSUPPORTED
+    assert L.qlora_quantize_nf4_typed(ctypes.byref(d), fake, -1, fake, fake, fake, None) == q.QLORA_ERR_UNSUPPORTED
+    assert L.qlora_quantize_nf4_typed(ctypes.byref(d), None, q.QLORA_W_BF16, fake, fake, fake, None) == \
+        q.QLORA_ERR_NULL
+    assert L.qlora_quantize_nf4_typed(ctypes.byref(d), fake + 2, q.QLORA_W_F16, fake, fake, fake, None) == \
+        q.QLORA_ERR_UNSUPPORTED
+    assert L.qlora_quantize_nf4_typed(ctypes.byref(q._desc(64, 96)), fake, q.QLORA_W_BF16, fake, fake, fake,
+                                      None) == q.QLORA_ERR_SHAPE
+
+
 def test_workspace_sizes_grow_with_tokens_and_rank():
     a = q.qlora_bwd_workspace_bytes(4096, 4096, 2048, 16)
     b = q.qlora_bwd_workspace_bytes(4096, 4096, 4096, 64)

@@ -40,7 +40,8 @@ class Linear:
     seed: int
 
 
-def _bf16_bits(x: np.ndarray) -> np.ndarray:
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 values -> uint16 bf16 bit patterns (torch's round to nearest even)."""
     import torch
     t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
     return t.view(torch.int16).numpy().view(np.uint16).copy()
@@ -51,12 +52,12 @@ def layer_inputs(d_out: int, d_in: int, T: int, r: int, seed: int, with_dy: bool
     rng = np.random.Generator(np.random.PCG64(seed))
     out = {}
     out["W"] = (rng.standard_normal((d_out, d_in), dtype=np.float32) * np.float32(W_STD)).astype(np.float32)
-    out["X"] = _bf16_bits(rng.standard_normal((T, d_in), dtype=np.float32))
+    out["X"] = bf16_bits(rng.standard_normal((T, d_in), dtype=np.float32))
     a_std = np.float32(1.0 / r) if r > 0 else np.float32(0.0)
-    out["A"] = _bf16_bits(rng.standard_normal((r, d_in), dtype=np.float32) * a_std)
-    out["B"] = _bf16_bits(rng.standard_normal((d_out, r), dtype=np.float32) * np.float32(0.01))
+    out["A"] = bf16_bits(rng.standard_normal((r, d_in), dtype=np.float32) * a_std)
+    out["B"] = bf16_bits(rng.standard_normal((d_out, r), dtype=np.float32) * np.float32(0.01))
     if with_dy:
-        out["dY"] = _bf16_bits(rng.standard_normal((T, d_out), dtype=np.float32))
+        out["dY"] = bf16_bits(rng.standard_normal((T, d_out), dtype=np.float32))
     return out
 
 
