@@ -14,6 +14,7 @@ describe, step by step and in the pages' order:
   4-bit indices, nibble packing, double quantization of the scales, dequant.
 * ``oracle.lora`` -- the two-branch forward, the frozen-base backward, merge.
 * ``oracle.bf16`` -- the oracle's own bfloat16 round-to-nearest-even.
+* ``oracle.optim`` -- the AdamW update of the adapter parameters.
 
 Page keys used in citations (titles of the pages the method is read from):
 
@@ -27,7 +28,7 @@ is pinned by at least one ``-m "not gpu"`` test against something other than
 itself, except where the docstring says "parity unpinned".
 """
 
-from . import bf16, lora, nf4  # noqa: F401
+from . import bf16, lora, nf4, optim  # noqa: F401
 from .nf4 import (  # noqa: F401
     nf4_levels,
     uniform_levels,
