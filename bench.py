@@ -258,6 +258,41 @@ def quantize16_section(lin, steps):
     return out
 
 
+def adamw_section(steps):
+    """The AdamW update over every adapter of the 65B-class stack (8 layers x
+    q, k, v, o 8192x8192, gate/up 8192->22016, down 22016->8192, r = 64) laid
+    out in one fp32 arena: about 80M parameters, 30 bytes each per step."""
+    import torch
+    import nf4_bit_quantized_amd as q
+    import workloads
+
+    n = sum(l.r * (l.d_in + l.d_out) for l in workloads.stack_65b())
+    g = torch.Generator(device="cuda").manual_seed(0)
+    P = torch.randn(n, device="cuda", generator=g) * 0.02
+    G = torch.randn(n, device="cuda", generator=g) * 1e-3
+    M = torch.zeros(n, device="cuda")
+    V = torch.zeros(n, device="cuda")
+    P16 = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    for t in range(1, 4):
+        q.qlora_adamw_step(P, G, M, V, t, 1e-4, weight_decay=0.01, param_bf16=P16)
+    torch.cuda.synchronize()
+    q.qlora_trace_read(reset=True)
+    q.qlora_trace_select({"adamw"})
+    for t in range(4, 4 + steps):
+        q.qlora_adamw_step(P, G, M, V, t, 1e-4, weight_decay=0.01, param_bf16=P16)
+    torch.cuda.synchronize()
+    q.qlora_trace_enable(False)
+    k, ms = q.qlora_trace_read(reset=True).get("adamw", (1, float("nan")))
+    avg = ms / max(k, 1)
+    nbytes = 30 * n
+    out = {"params": n, "bytes": nbytes, "kernel_us": round(avg * 1e3, 2),
+           "GBps": round(nbytes / (avg * 1e-3) / 1e9, 1),
+           "frac_hbm": round(nbytes / (avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    log("adamw", out)
+    del P, G, M, V, P16
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -374,6 +409,7 @@ def main():
         result["decode_packed_weight"] = decode_section(steps=max(20, args.steps), warmup=5)
         result["export_bf16"] = export_section(lin, steps=max(20, args.steps))
         result["quantize_16bit_weight"] = quantize16_section(lin, steps=max(20, args.steps))
+        result["adamw_65b_adapters"] = adamw_section(steps=max(20, args.steps))
     if not args.no_cpu_baseline:
         log("timing the oracle on the host ...")
         result["cpu_baseline"] = cpu_baseline(inp, lin, args.cpu_seconds)

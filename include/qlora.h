@@ -205,6 +205,22 @@ int qlora_linear_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8
                      void* stream);
 
 /*
+ * The backward above for gradient accumulation over micro-batches ("LoRA 与
+ * QLoRA：..." §10: gradient accumulation simulates a larger effective batch):
+ * identical, except that the adapter gradients are added to what dA and dB
+ * hold on entry,
+ *   dA += s G^T X,   dB += s dY^T U,
+ * each element read, added once in fp32 and written (deterministic; the sum
+ * over the micro-batch is formed first, then added).  T == 0 leaves dA and dB
+ * unchanged.  dX is written as by qlora_linear_bwd.  Same errors.
+ */
+int qlora_linear_bwd_accumulate(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes,
+                                const float* consts, int64_t T, const uint16_t* X, int32_t r, float alpha,
+                                const uint16_t* A, const uint16_t* B, const float* U_in, const uint16_t* dY,
+                                uint16_t* dX, float* dA, float* dB, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/*
  * Export of the restored weight -- "QLoRA技术从入门到精通" §3(2) (the 4-bit
  * weight restored to a 16-bit float, table value times the block's scale):
  *   W_hat[N][K] = bf16_rne(fl32(T[q] * s'))   (bf16 bits, device)
@@ -244,6 +260,42 @@ int qlora_merge_lora(const qlora_nf4_desc* d, const uint8_t* packed, const uint8
  * totals afterwards.  Errors: NULL (count, or stats with max_stats > 0), HIP.
  * Not thread-safe with respect to concurrent compute calls on other threads.
  */
+/*
+ * AdamW update of the adapter parameters ("QLoRA技术从入门到精通" §3(3):
+ * after the backward pass the optimizer updates only A and B, never the
+ * quantized base weight).  The arithmetic is the published AdamW method
+ * (Loshchilov and Hutter, decoupled weight decay), per element in fp32 with
+ * the fp32 hyperparameters as given; the factors below that depend on them
+ * (1 - beta, 1 - lr * weight_decay, the bias corrections) are formed in double
+ * on the host and rounded to fp32 once:
+ *   g = grad * grad_scale;  p *= 1 - lr * weight_decay
+ *   m = beta1 m + (1 - beta1) g;  v = beta2 v + (1 - beta2) g^2
+ *   p -= (lr / (1 - beta1^step)) * m / (sqrt(v) / sqrt(1 - beta2^step) + eps)
+ *   param_bf16 = bf16_rne(p)        (skipped when param_bf16 == NULL)
+ * param, grad, exp_avg (m), exp_avg_sq (v): fp32 [n], device, 16-byte
+ * aligned, updated in place (grad is read only); param_bf16: uint16 [n]
+ * bf16 bits, 8-byte aligned.  Lay out every adapter of a model in one arena
+ * to update them all in one call; with gradient accumulation, grad_scale =
+ * 1 / (number of micro-batches) averages them.  The paged placement of the
+ * optimizer state is not part of this call.  No buffer may alias another.
+ * n == 0 does nothing (the buffers may then be NULL).
+ * Errors: NULL (h; param, grad, exp_avg or exp_avg_sq when n > 0), SHAPE (n < 0),
+ * UNSUPPORTED (step < 1, beta outside [0, 1), eps < 0, non-finite
+ * hyperparameters, alignment), HIP.
+ */
+typedef struct qlora_adamw_hparams {
+  float lr;
+  float beta1;
+  float beta2;
+  float eps;
+  float weight_decay;
+  float grad_scale;
+  int64_t step;  /* 1 for the first update */
+} qlora_adamw_hparams;
+
+int qlora_adamw_step(const qlora_adamw_hparams* h, int64_t n, float* param, const float* grad, float* exp_avg,
+                     float* exp_avg_sq, uint16_t* param_bf16, void* stream);
+
 /*
  * qlora_trace_select: like qlora_trace_enable, but only the kernels whose bit
  * is set in kernel_mask are bracketed (bit k = the kernel named by

@@ -40,8 +40,10 @@ EXPORTED = (
     "qlora_linear_fwd",
     "qlora_bwd_workspace_bytes",
     "qlora_linear_bwd",
+    "qlora_linear_bwd_accumulate",
     "qlora_dequantize_nf4",
     "qlora_merge_lora",
+    "qlora_adamw_step",
     "qlora_trace_enable",
     "qlora_trace_select",
     "qlora_trace_kernel_name",
@@ -62,6 +64,12 @@ class KernelStat(ctypes.Structure):
 class Nf4Desc(ctypes.Structure):
     _fields_ = [("d_out", ctypes.c_int64), ("d_in", ctypes.c_int64),
                 ("blocksize", ctypes.c_int32), ("dq_blocksize", ctypes.c_int32), ("table", ctypes.c_int32)]
+
+
+class AdamwHparams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float), ("grad_scale", ctypes.c_float),
+                ("step", ctypes.c_int64)]
 
 
 # level tables (qlora_nf4_desc.table)
@@ -94,8 +102,10 @@ def lib() -> ctypes.CDLL:
     L.qlora_bwd_workspace_bytes.argtypes = [dp, i64, i32, ctypes.POINTER(sz)]
     L.qlora_linear_fwd.argtypes = [dp, vp, vp, vp, i64, vp, i32, f32, vp, vp, vp, vp, vp, sz, vp]
     L.qlora_linear_bwd.argtypes = [dp, vp, vp, vp, i64, vp, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.qlora_linear_bwd_accumulate.argtypes = L.qlora_linear_bwd.argtypes
     L.qlora_dequantize_nf4.argtypes = [dp, vp, vp, vp, vp, vp]
     L.qlora_merge_lora.argtypes = [dp, vp, vp, vp, i32, f32, vp, vp, vp, vp]
+    L.qlora_adamw_step.argtypes = [ctypes.POINTER(AdamwHparams), i64, vp, vp, vp, vp, vp, vp]
     L.qlora_trace_enable.argtypes = [ctypes.c_int]
     L.qlora_trace_select.argtypes = [ctypes.c_uint32]
     L.qlora_trace_kernel_name.argtypes = [ctypes.c_int]
@@ -263,8 +273,12 @@ def qlora_linear_fwd(packed, codes, consts, X, A, B, alpha: float, Y=None, U_out
 
 
 def qlora_linear_bwd(packed, codes, consts, X, A, B, alpha: float, dY, U_in=None, dX=None, dA=None, dB=None,
-                     want_dx: bool = True, workspace=None, stream=None, table: int = TABLE_NF4):
-    """Backward: returns (dX bf16 [T][d_in] or None, dA fp32 [r][d_in], dB fp32 [d_out][r])."""
+                     want_dx: bool = True, workspace=None, stream=None, table: int = TABLE_NF4,
+                     accumulate: bool = False):
+    """Backward: returns (dX bf16 [T][d_in] or None, dA fp32 [r][d_in], dB fp32 [d_out][r]).
+
+    accumulate=True adds the adapter gradients to the given dA and dB
+    (qlora_linear_bwd_accumulate) instead of overwriting them."""
     import torch
     d_out, d_in = packed.shape[0], packed.shape[1] * 2
     T = X.shape[0]
@@ -276,16 +290,22 @@ def qlora_linear_bwd(packed, codes, consts, X, A, B, alpha: float, dY, U_in=None
     if dX is None and want_dx:
         dX = torch.empty((T, d_in), dtype=torch.bfloat16, device=X.device)
     if r > 0:
+        if accumulate and (dA is None or dB is None):
+            raise ValueError("accumulate=True needs the dA and dB to add to")
         if dA is None:
             dA = torch.empty((r, d_in), dtype=torch.float32, device=X.device)
         if dB is None:
             dB = torch.empty((d_out, r), dtype=torch.float32, device=X.device)
+        for t, nm, shape in ((dA, "dA", (r, d_in)), (dB, "dB", (d_out, r))):
+            if t.dtype != torch.float32 or tuple(t.shape) != shape or not t.is_contiguous():
+                raise ValueError(f"{nm} must be a contiguous float32 tensor of shape {shape}")
     nbytes = qlora_bwd_workspace_bytes(d_out, d_in, T, r)
     ws = _workspace(nbytes, X.device, workspace)
     d = _desc(d_out, d_in, table=table)
-    _check(lib().qlora_linear_bwd(ctypes.byref(d), _ptr(packed), _ptr(codes), _ptr(consts), T, _ptr(X), r,
-                                  float(alpha), _ptr(A), _ptr(B), _ptr(U_in), _ptr(dY), _ptr(dX), _ptr(dA),
-                                  _ptr(dB), _ptr(ws), nbytes, _stream(stream)), "qlora_linear_bwd")
+    name = "qlora_linear_bwd_accumulate" if accumulate else "qlora_linear_bwd"
+    _check(getattr(lib(), name)(ctypes.byref(d), _ptr(packed), _ptr(codes), _ptr(consts), T, _ptr(X), r,
+                                float(alpha), _ptr(A), _ptr(B), _ptr(U_in), _ptr(dY), _ptr(dX), _ptr(dA),
+                                _ptr(dB), _ptr(ws), nbytes, _stream(stream)), name)
     return dX, dA, dB
 
 
@@ -325,6 +345,28 @@ def qlora_merge_lora(packed, codes, consts, A, B, alpha: float, W_merged=None, s
 # ---------------------------------------------------------------------------
 # Per-kernel timing (hipEvents recorded by the library around its launches)
 # ---------------------------------------------------------------------------
+
+def qlora_adamw_step(param, grad, exp_avg, exp_avg_sq, step: int, lr: float, betas=(0.9, 0.999),
+                     eps: float = 1e-8, weight_decay: float = 0.0, grad_scale: float = 1.0, param_bf16=None,
+                     stream=None):
+    """AdamW update in place of fp32 param / exp_avg / exp_avg_sq (same size,
+    contiguous, on the GPU) from fp32 grad; param_bf16 (bf16, same size) if
+    given receives the rounded parameters.  Returns param_bf16."""
+    import torch
+    _need_cuda(param, grad, exp_avg, exp_avg_sq, param_bf16, name="qlora_adamw_step")
+    n = param.numel()
+    for t, nm in ((param, "param"), (grad, "grad"), (exp_avg, "exp_avg"), (exp_avg_sq, "exp_avg_sq")):
+        if t.dtype != torch.float32 or t.numel() != n or not t.is_contiguous():
+            raise ValueError(f"{nm} must be a contiguous float32 tensor of {n} elements")
+    if param_bf16 is not None and (param_bf16.dtype != torch.bfloat16 or param_bf16.numel() != n
+                                   or not param_bf16.is_contiguous()):
+        raise ValueError(f"param_bf16 must be a contiguous bfloat16 tensor of {n} elements")
+    h = AdamwHparams(float(lr), float(betas[0]), float(betas[1]), float(eps), float(weight_decay),
+                     float(grad_scale), int(step))
+    _check(lib().qlora_adamw_step(ctypes.byref(h), n, _ptr(param), _ptr(grad), _ptr(exp_avg), _ptr(exp_avg_sq),
+                                  _ptr(param_bf16), _stream(stream)), "qlora_adamw_step")
+    return param_bf16
+
 
 def qlora_trace_enable(enable: bool = True) -> None:
     _check(lib().qlora_trace_enable(1 if enable else 0), "qlora_trace_enable")

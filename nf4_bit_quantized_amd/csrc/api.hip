@@ -7,6 +7,9 @@
 
 #include "fused.hpp"
 #include "lora_stream.hpp"
+#include <cmath>
+
+#include "adamw.hpp"
 #include "skinny.hpp"
 #include "trace.hpp"
 #include "../../include/qlora.h"
@@ -292,11 +295,11 @@ int qlora_linear_fwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8
   return QLORA_OK;
 }
 
-int qlora_linear_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes,
-                     const float* consts, int64_t T, const uint16_t* X, int32_t r, float alpha,
-                     const uint16_t* A, const uint16_t* B, const float* U_in, const uint16_t* dY,
-                     uint16_t* dX, float* dA, float* dB, void* workspace, size_t workspace_bytes,
-                     void* stream) {
+namespace {
+int linear_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes, const float* consts, int64_t T,
+               const uint16_t* X, int32_t r, float alpha, const uint16_t* A, const uint16_t* B, const float* U_in,
+               const uint16_t* dY, uint16_t* dX, float* dA, float* dB, void* workspace, size_t workspace_bytes,
+               void* stream, int accumulate) {
   const int st = check_layer(d, T, r);
   if (st) return st;
   if (!packed || !codes || !consts) return QLORA_ERR_NULL;
@@ -310,7 +313,7 @@ int qlora_linear_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8
   hipStream_t s_ = (hipStream_t)stream;
   const int64_t N = d->d_out, K = d->d_in;
   if (T == 0) {
-    if (r > 0) {
+    if (r > 0 && !accumulate) {
       HIP_TRY(launch_fill_zero(dA, (int64_t)r * K, s_));
       HIP_TRY(launch_fill_zero(dB, N * r, s_));
     }
@@ -358,20 +361,71 @@ int qlora_linear_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8
     // dA = (s G)^T X -> [r][d_in]; dB = dY^T (s U) -> [d_out][r]
     if (lora_stream_ok(r)) {
       ColsBatch C{};
-      C.p[0] = ColsParams{X, K, K, w.Gs, ldh, T, r, 1, dA};
-      C.p[1] = ColsParams{dY, N, N, w.Us, ldh, T, r, 0, dB};
+      C.p[0] = ColsParams{X, K, K, w.Gs, ldh, T, r, 1, dA, accumulate};
+      C.p[1] = ColsParams{dY, N, N, w.Us, ldh, T, r, 0, dB, accumulate};
       C.n = 2;
       HIP_TRY(launch_lora_cols(C, s_, KID_LORA_DA));
     } else {
       SkinnyParams Sa = skinny(X, K, false, K, T, r, s, 2 * r, OUT_PAIRS_T, w.part);
       skinny_q(Sa, w.Gs, ldh, 2 * (int64_t)r, Q_STRIDED);
       Sa.Fout = dA;
+      Sa.accumulate = accumulate;
       SkinnyParams Sb = skinny(dY, N, false, N, T, r, s, 2 * r, OUT_PAIRS, w.part2);
       skinny_q(Sb, w.Us, ldh, 2 * (int64_t)r, Q_STRIDED);
       Sb.Fout = dB;
+      Sb.accumulate = accumulate;
       HIP_TRY(launch_skinny_pair(Sa, Sb, s_, KID_LORA_DA));
     }
   }
+  return QLORA_OK;
+}
+}  // namespace
+
+int qlora_linear_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes,
+                     const float* consts, int64_t T, const uint16_t* X, int32_t r, float alpha,
+                     const uint16_t* A, const uint16_t* B, const float* U_in, const uint16_t* dY,
+                     uint16_t* dX, float* dA, float* dB, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  return linear_bwd(d, packed, codes, consts, T, X, r, alpha, A, B, U_in, dY, dX, dA, dB, workspace,
+                    workspace_bytes, stream, 0);
+}
+
+int qlora_linear_bwd_accumulate(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes,
+                                const float* consts, int64_t T, const uint16_t* X, int32_t r, float alpha,
+                                const uint16_t* A, const uint16_t* B, const float* U_in, const uint16_t* dY,
+                                uint16_t* dX, float* dA, float* dB, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  return linear_bwd(d, packed, codes, consts, T, X, r, alpha, A, B, U_in, dY, dX, dA, dB, workspace,
+                    workspace_bytes, stream, 1);
+}
+
+int qlora_adamw_step(const qlora_adamw_hparams* h, int64_t n, float* param, const float* grad, float* exp_avg,
+                     float* exp_avg_sq, uint16_t* param_bf16, void* stream) {
+  if (!h) return QLORA_ERR_NULL;
+  if (n < 0) return QLORA_ERR_SHAPE;
+  const float hp[6] = {h->lr, h->beta1, h->beta2, h->eps, h->weight_decay, h->grad_scale};
+  for (float x : hp)
+    if (!std::isfinite(x)) return QLORA_ERR_UNSUPPORTED;
+  if (h->step < 1 || !(h->beta1 >= 0.0f && h->beta1 < 1.0f) || !(h->beta2 >= 0.0f && h->beta2 < 1.0f) ||
+      h->eps < 0.0f)
+    return QLORA_ERR_UNSUPPORTED;
+  if (n == 0) return QLORA_OK;
+  if (!param || !grad || !exp_avg || !exp_avg_sq) return QLORA_ERR_NULL;
+  if (!aligned16(param) || !aligned16(grad) || !aligned16(exp_avg) || !aligned16(exp_avg_sq) ||
+      (param_bf16 && ((uintptr_t)param_bf16 & 7) != 0))
+    return QLORA_ERR_UNSUPPORTED;
+  const double t = (double)h->step;
+  const double bc1 = 1.0 - std::pow((double)h->beta1, t), bc2 = 1.0 - std::pow((double)h->beta2, t);
+  AdamwParams P{};
+  P.p = param; P.g = grad; P.m = exp_avg; P.v = exp_avg_sq; P.p16 = param_bf16; P.n = n;
+  P.decay = (float)(1.0 - (double)h->lr * (double)h->weight_decay);
+  P.gscale = h->grad_scale;
+  P.beta1 = h->beta1; P.one_minus_beta1 = (float)(1.0 - (double)h->beta1);
+  P.beta2 = h->beta2; P.one_minus_beta2 = (float)(1.0 - (double)h->beta2);
+  P.step_size = (float)((double)h->lr / bc1);
+  P.inv_sqrt_bc2 = (float)(1.0 / std::sqrt(bc2));
+  P.eps = h->eps;
+  HIP_TRY(launch_adamw(P, (hipStream_t)stream));
   return QLORA_OK;
 }
 

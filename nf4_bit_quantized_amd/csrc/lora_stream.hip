@@ -311,8 +311,8 @@ __global__ __launch_bounds__(256) void k_lora_cols(ColsBatch B) {
              red[(3 * 32 + mm) * J2 + jj];
     };
     const float t = col(j) + col(j + r);
-    if (p.transposed_out) p.Fout[(int64_t)j * p.D + m] = t;
-    else p.Fout[m * r + j] = t;
+    float* dst = p.transposed_out ? p.Fout + (int64_t)j * p.D + m : p.Fout + m * r + j;
+    *dst = p.accumulate ? *dst + t : t;
   }
 }
 

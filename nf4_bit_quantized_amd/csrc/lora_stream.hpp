@@ -36,6 +36,7 @@ struct ColsParams {
   int32_t r;          // a multiple of 8, at most 64 (the same for both products of a batch)
   int32_t transposed_out;
   float* Fout;
+  int32_t accumulate;  // 1: Fout += result (gradient accumulation), 0: Fout = result
 };
 
 struct ColsBatch {

@@ -281,8 +281,8 @@ __global__ __launch_bounds__(256) void k_skinny(SkinnyBatch SB) {
       // pair sums of the hi/lo columns: out[m][col] (dB) or out[col][m] (dA)
       if (col < S.r) {
         const float t = v + red[row * J + col + S.r];
-        if (S.out_mode == OUT_PAIRS) S.Fout[m * S.r + col] = t;
-        else S.Fout[(int64_t)col * S.mrows + m] = t;
+        float* dst = S.out_mode == OUT_PAIRS ? S.Fout + m * S.r + col : S.Fout + (int64_t)col * S.mrows + m;
+        *dst = S.accumulate ? *dst + t : t;
       }
     }
   }
@@ -362,8 +362,8 @@ __global__ __launch_bounds__(256) void k_skinny_sum(SkinnyBatch SB, int tpo) {
     }
   } else if (col < S.r) {
     const float t = tot[tid] + tot[tid + S.r];   // the row's column col + r is in this workgroup
-    if (S.out_mode == OUT_PAIRS) S.Fout[m * S.r + col] = t;
-    else S.Fout[(int64_t)col * S.mrows + m] = t;
+    float* dst = S.out_mode == OUT_PAIRS ? S.Fout + m * S.r + col : S.Fout + (int64_t)col * S.mrows + m;
+    *dst = S.accumulate ? *dst + t : t;
   }
 }
 

@@ -43,6 +43,7 @@ struct SkinnyParams {
   uint16_t* Hout;
   int64_t ldh;
   float* Fout;
+  int32_t accumulate; // OUT_PAIRS / OUT_PAIRS_T: 1 adds the result to Fout, 0 overwrites it
   // optional (OUT_ROWS_HILO products of r columns): Ucs[m][..] = hi/lo pair
   // of s * Uc[m][0..r) for the same rows m, zero-padded to ldh
   const float* Uc;

@@ -18,6 +18,7 @@ enum KernelId : int {
   KID_REDUCE,
   KID_FILL,
   KID_EXPORT,
+  KID_ADAMW,
   KID_COUNT
 };
 

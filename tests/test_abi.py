@@ -169,6 +169,28 @@ def test_typed_quantize_validation_happens_before_any_launch():
                                       None) == q.QLORA_ERR_SHAPE
 
 
+def test_adamw_validation_happens_before_any_launch():
+    fake = 0x10000
+    L = q.lib()
+    ok = q.AdamwHparams(1e-3, 0.9, 0.999, 1e-8, 0.01, 1.0, 1)
+    assert L.qlora_adamw_step(None, 8, fake, fake, fake, fake, None, None) == q.QLORA_ERR_NULL
+    assert L.qlora_adamw_step(ctypes.byref(ok), 8, fake, None, fake, fake, None, None) == q.QLORA_ERR_NULL
+    assert L.qlora_adamw_step(ctypes.byref(ok), 0, None, None, None, None, None, None) == q.QLORA_OK
+    assert L.qlora_adamw_step(ctypes.byref(ok), -1, fake, fake, fake, fake, None, None) == q.QLORA_ERR_SHAPE
+    for bad in (q.AdamwHparams(1e-3, 0.9, 0.999, 1e-8, 0.01, 1.0, 0),        # step 0
+                q.AdamwHparams(1e-3, 1.0, 0.999, 1e-8, 0.01, 1.0, 1),        # beta1 = 1
+                q.AdamwHparams(1e-3, 0.9, -0.1, 1e-8, 0.01, 1.0, 1),         # beta2 < 0
+                q.AdamwHparams(1e-3, 0.9, 0.999, -1.0, 0.01, 1.0, 1),        # eps < 0
+                q.AdamwHparams(float("nan"), 0.9, 0.999, 1e-8, 0.01, 1.0, 1)):
+        assert L.qlora_adamw_step(ctypes.byref(bad), 8, fake, fake, fake, fake, None, None) == \
+            q.QLORA_ERR_UNSUPPORTED
+    assert L.qlora_adamw_step(ctypes.byref(ok), 8, fake + 4, fake, fake, fake, None, None) == \
+        q.QLORA_ERR_UNSUPPORTED
+    assert L.qlora_adamw_step(ctypes.byref(ok), 8, fake, fake, fake, fake, fake + 2, None) == \
+        q.QLORA_ERR_UNSUPPORTED
+    assert ctypes.sizeof(q.AdamwHparams) == 32
+
+
 def test_workspace_sizes_grow_with_tokens_and_rank():
     a = q.qlora_bwd_workspace_bytes(4096, 4096, 2048, 16)
     b = q.qlora_bwd_workspace_bytes(4096, 4096, 4096, 64)
