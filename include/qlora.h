@@ -30,8 +30,10 @@
  * - Stored weight format (written by qlora_quantize_nf4):
  *     packed [N][K/2] uint8: 4-bit level indices, element 2j of the flattened
  *            weight in the HIGH nibble of byte j, element 2j+1 in the low one;
- *     codes  [N*K/64] uint8: 8-bit code of each 64-weight block's absmax scale;
- *     consts [ceil(N*K/64/256)] fp32: per group of 256 consecutive block
+ *     codes  [N*K/bs] uint8: 8-bit code of each block's absmax scale, a block
+ *            being bs consecutive weights of the flattened weight (bs =
+ *            desc.blocksize: 64, 128 or 256; blocks may span rows);
+ *     consts [ceil(N*K/bs/256)] fp32: per group of 256 consecutive block
  *            scales, the group's largest scale c_g.
  *   Block b is restored with s'_b = fl32(fl32(code_b) * fl32(c_g / 255)) and
  *   each weight as bf16_rne(fl32(T[q] * s'_b)).
@@ -49,10 +51,11 @@
  * - W, packed, X, dY, A and B must be 16-byte aligned (QLORA_ERR_UNSUPPORTED
  *   otherwise); other pointers need only their element alignment.  A forward
  *   call with at most 16 tokens takes the weight-streaming kernel when codes
- *   is 16-byte aligned and K/64 is at most about 2000, else the tiled kernel
- *   (same results within the accuracy stated below).
+ *   is 16-byte aligned, K is a multiple of the block size and K/bs is at
+ *   most about 2000, else the tiled kernel (same results within the accuracy
+ *   stated below).
  * - Inputs must be finite; results for NaN/Inf inputs are unspecified.
- * - Hot-path preconditions: blocksize == 64, dq_blocksize == 256,
+ * - Hot-path preconditions: blocksize 64 (also 128 or 256), dq_blocksize == 256,
  *   d_in % 64 == 0, d_out % 64 == 0, 0 <= r <= 128, T >= 0 (T == 0 is a
  *   no-op).  r == 0 means the base branch only.
  */
@@ -79,7 +82,8 @@ enum {
 typedef struct qlora_nf4_desc {
   int64_t d_out;        /* N: rows of W */
   int64_t d_in;         /* K: columns of W */
-  int32_t blocksize;    /* weights per absmax block; must be 64 */
+  int32_t blocksize;    /* weights per absmax block: 64, 128 or 256 ("QLoRA技术从入门到精通"
+                           §3(1): blocks of e.g. 64 or 256 values) */
   int32_t dq_blocksize; /* block scales per second-level group; must be 256 */
   int32_t table;        /* level table: QLORA_TABLE_NF4 (0) or QLORA_TABLE_UNIFORM (1) */
 } qlora_nf4_desc;
@@ -128,7 +132,7 @@ int qlora_nf4_sizes(const qlora_nf4_desc* d, size_t* packed_bytes, size_t* codes
 /*
  * Offline quantization of W (fp32 [N][K], device) into packed / codes /
  * consts (device, sizes from qlora_nf4_sizes) -- "QLoRA技术从入门到精通" §3(1):
- * per 64-weight block absmax scale s_b, x = fl32(w / s_b) (IEEE division),
+ * per block (desc.blocksize weights) absmax scale s_b, x = fl32(w / s_b) (IEEE division),
  * nearest NF4 level (ties to the lower index; an all-zero block gives index 7),
  * two indices per byte; then per group of 256 block scales c_g = max s_b and
  * code_b = rint_half_even(fl32(fl32(s_b / c_g) * 255)) (0 when c_g == 0).

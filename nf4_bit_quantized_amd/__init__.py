@@ -127,6 +127,17 @@ def _desc(d_out: int, d_in: int, blocksize: int = 64, dq_blocksize: int = 256, t
     return Nf4Desc(int(d_out), int(d_in), int(blocksize), int(dq_blocksize), int(table))
 
 
+def _stored_desc(packed, codes, table: int) -> Nf4Desc:
+    """Descriptor of a stored weight; its block size follows from the length of
+    its codes array (one code per block)."""
+    d_out, d_in = packed.shape[0], packed.shape[1] * 2
+    nb = codes.numel()
+    if nb <= 0 or (d_out * d_in) % nb != 0 or (d_out * d_in) // nb not in (64, 128, 256):
+        raise ValueError(f"codes holds {nb} entries: not one per block of 64, 128 or 256 weights "
+                         f"of a {d_out}x{d_in} weight")
+    return _desc(d_out, d_in, (d_out * d_in) // nb, table=table)
+
+
 def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
@@ -216,9 +227,11 @@ def _workspace(nbytes: int, device, workspace=None):
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
-def qlora_quantize_nf4(W, packed=None, codes=None, consts=None, stream=None, table: int = TABLE_NF4):
+def qlora_quantize_nf4(W, packed=None, codes=None, consts=None, stream=None, table: int = TABLE_NF4,
+                       blocksize: int = 64):
     """Quantize W [d_out][d_in] (GPU; float32, bfloat16 or float16) ->
-    (packed uint8 [d_out][d_in/2], codes uint8 [nb], consts float32 [ng]).
+    (packed uint8 [d_out][d_in/2], codes uint8 [nb], consts float32 [ng]),
+    nb = d_out * d_in / blocksize (64, 128 or 256 weights per absmax block).
     A 16-bit W is widened exactly to fp32 inside the kernel."""
     import torch
     _need_cuda(W, name="qlora_quantize_nf4")
@@ -226,7 +239,7 @@ def qlora_quantize_nf4(W, packed=None, codes=None, consts=None, stream=None, tab
     if W.dtype not in fmts or W.dim() != 2:
         raise ValueError("W must be a 2-D float32, bfloat16 or float16 tensor")
     d_out, d_in = W.shape
-    n_p, n_c, n_k = qlora_nf4_sizes(d_out, d_in)
+    n_p, n_c, n_k = qlora_nf4_sizes(d_out, d_in, blocksize)
     if packed is None:
         packed = torch.empty((d_out, d_in // 2), dtype=torch.uint8, device=W.device)
     if codes is None:
@@ -234,7 +247,11 @@ def qlora_quantize_nf4(W, packed=None, codes=None, consts=None, stream=None, tab
     if consts is None:
         consts = torch.empty(n_k // 4, dtype=torch.float32, device=W.device)
     _need_cuda(packed, codes, consts, name="qlora_quantize_nf4")
-    d = _desc(d_out, d_in, table=table)
+    for t, nm, n, dt in ((packed, "packed", n_p, torch.uint8), (codes, "codes", n_c, torch.uint8),
+                         (consts, "consts", n_k // 4, torch.float32)):
+        if t.dtype != dt or t.numel() != n or not t.is_contiguous():
+            raise ValueError(f"{nm} must be a contiguous {dt} tensor of {n} elements")
+    d = _desc(d_out, d_in, blocksize, table=table)
     if W.dtype == torch.float32:
         _check(lib().qlora_quantize_nf4(ctypes.byref(d), _ptr(W), _ptr(packed), _ptr(codes), _ptr(consts),
                                         _stream(stream)), "qlora_quantize_nf4")
@@ -265,7 +282,7 @@ def qlora_linear_fwd(packed, codes, consts, X, A, B, alpha: float, Y=None, U_out
         U_out = torch.empty((T, r), dtype=torch.float32, device=X.device)
     nbytes = qlora_fwd_workspace_bytes(d_out, d_in, T, r)
     ws = _workspace(nbytes, X.device, workspace)
-    d = _desc(d_out, d_in, table=table)
+    d = _stored_desc(packed, codes, table)
     _check(lib().qlora_linear_fwd(ctypes.byref(d), _ptr(packed), _ptr(codes), _ptr(consts), T, _ptr(X), r,
                                   float(alpha), _ptr(A), _ptr(B), _ptr(Y), _ptr(U_out), _ptr(ws), nbytes,
                                   _stream(stream)), "qlora_linear_fwd")
@@ -301,7 +318,7 @@ def qlora_linear_bwd(packed, codes, consts, X, A, B, alpha: float, dY, U_in=None
                 raise ValueError(f"{nm} must be a contiguous float32 tensor of shape {shape}")
     nbytes = qlora_bwd_workspace_bytes(d_out, d_in, T, r)
     ws = _workspace(nbytes, X.device, workspace)
-    d = _desc(d_out, d_in, table=table)
+    d = _stored_desc(packed, codes, table)
     name = "qlora_linear_bwd_accumulate" if accumulate else "qlora_linear_bwd"
     _check(getattr(lib(), name)(ctypes.byref(d), _ptr(packed), _ptr(codes), _ptr(consts), T, _ptr(X), r,
                                 float(alpha), _ptr(A), _ptr(B), _ptr(U_in), _ptr(dY), _ptr(dX), _ptr(dA),
@@ -317,7 +334,7 @@ def qlora_dequantize_nf4(packed, codes, consts, W_hat=None, stream=None, table: 
     _need_cuda(packed, codes, consts, W_hat, name="qlora_dequantize_nf4")
     if W_hat is None:
         W_hat = torch.empty((d_out, d_in), dtype=torch.bfloat16, device=packed.device)
-    d = _desc(d_out, d_in, table=table)
+    d = _stored_desc(packed, codes, table)
     _check(lib().qlora_dequantize_nf4(ctypes.byref(d), _ptr(packed), _ptr(codes), _ptr(consts), _ptr(W_hat),
                                       _stream(stream)), "qlora_dequantize_nf4")
     return W_hat
@@ -336,7 +353,7 @@ def qlora_merge_lora(packed, codes, consts, A, B, alpha: float, W_merged=None, s
             raise ValueError(f"{nm} must be bfloat16")
     if W_merged is None:
         W_merged = torch.empty((d_out, d_in), dtype=torch.bfloat16, device=packed.device)
-    d = _desc(d_out, d_in, table=table)
+    d = _stored_desc(packed, codes, table)
     _check(lib().qlora_merge_lora(ctypes.byref(d), _ptr(packed), _ptr(codes), _ptr(consts), int(r), float(alpha),
                                   _ptr(A), _ptr(B), _ptr(W_merged), _stream(stream)), "qlora_merge_lora")
     return W_merged

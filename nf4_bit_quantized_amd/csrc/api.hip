@@ -16,15 +16,15 @@
 
 namespace qlora {
 hipError_t launch_nf4_quantize(const void* W, int wformat, uint8_t* packed, uint8_t* codes, float* consts,
-                               int64_t numel, int table, hipStream_t stream);
-bool decode_supported(int64_t N, int64_t K);
+                               int64_t numel, int blocksize, int table, hipStream_t stream);
+bool decode_supported(int64_t N, int64_t K, int bshift);
 hipError_t launch_decode(const uint8_t* packed, const uint8_t* codes, const float* consts, const uint16_t* X,
                          int64_t T, int64_t N, int64_t K, const uint16_t* Us, int64_t ldh, const uint16_t* B,
-                         int r, uint16_t* Y, int table, hipStream_t stream);
+                         int r, uint16_t* Y, int table, int bshift, hipStream_t stream);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
 hipError_t launch_export(const uint8_t* packed, const uint8_t* codes, const float* consts, int64_t N, int64_t K,
                          int r, float s, const uint16_t* A, const uint16_t* B, uint16_t* W, int table,
-                         hipStream_t stream);
+                         int bshift, hipStream_t stream);
 }  // namespace qlora
 
 using namespace qlora;
@@ -38,9 +38,13 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+// log2(blocksize / 64): 64-weight chunk index -> block index
+int block_shift(const qlora_nf4_desc* d) { return d->blocksize == 256 ? 2 : (d->blocksize == 128 ? 1 : 0); }
+
 int check_desc(const qlora_nf4_desc* d) {
   if (!d) return QLORA_ERR_NULL;
-  if (d->blocksize != 64 || d->dq_blocksize != 256) return QLORA_ERR_UNSUPPORTED;
+  if ((d->blocksize != 64 && d->blocksize != 128 && d->blocksize != 256) || d->dq_blocksize != 256)
+    return QLORA_ERR_UNSUPPORTED;
   if (d->table != QLORA_TABLE_NF4 && d->table != QLORA_TABLE_UNIFORM) return QLORA_ERR_UNSUPPORTED;
   if (d->d_out <= 0 || d->d_in <= 0 || d->d_out % 64 != 0 || d->d_in % 64 != 0) return QLORA_ERR_SHAPE;
   return QLORA_OK;
@@ -196,7 +200,7 @@ int qlora_nf4_sizes(const qlora_nf4_desc* d, size_t* packed_bytes, size_t* codes
   const int st = check_desc(d);
   if (st) return st;
   const int64_t numel = d->d_out * d->d_in;
-  const int64_t nb = numel / 64;
+  const int64_t nb = numel / d->blocksize;
   *packed_bytes = (size_t)(numel / 2);
   *codes_bytes = (size_t)nb;
   *consts_bytes = (size_t)cdiv(nb, 256) * 4;
@@ -217,7 +221,7 @@ int qlora_quantize_nf4_typed(const qlora_nf4_desc* d, const void* W, int32_t w_f
                 "weight formats");
   if (w_format != QLORA_W_F32 && w_format != QLORA_W_BF16 && w_format != QLORA_W_F16) return QLORA_ERR_UNSUPPORTED;
   if (!aligned16(W) || !aligned16(packed)) return QLORA_ERR_UNSUPPORTED;
-  HIP_TRY(launch_nf4_quantize(W, w_format, packed, codes, consts, d->d_out * d->d_in, d->table,
+  HIP_TRY(launch_nf4_quantize(W, w_format, packed, codes, consts, d->d_out * d->d_in, d->blocksize, d->table,
                               (hipStream_t)stream));
   return QLORA_OK;
 }
@@ -236,7 +240,7 @@ int qlora_merge_lora(const qlora_nf4_desc* d, const uint8_t* packed, const uint8
   if (r > 0 && (!A || !B)) return QLORA_ERR_NULL;
   if (!aligned16(W_merged) || (r > 0 && (!aligned16(A) || !aligned16(B)))) return QLORA_ERR_UNSUPPORTED;
   const float s = r > 0 ? alpha / (float)r : 0.0f;
-  HIP_TRY(launch_export(packed, codes, consts, d->d_out, d->d_in, r, s, A, B, W_merged, d->table,
+  HIP_TRY(launch_export(packed, codes, consts, d->d_out, d->d_in, r, s, A, B, W_merged, d->table, block_shift(d),
                         (hipStream_t)stream));
   return QLORA_OK;
 }
@@ -281,13 +285,14 @@ int qlora_linear_fwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8
     const int e = lora_down(X, A, T, K, r, s, w.part, U, w.Us, s_);
     if (e) return e;
   }
-  if (T <= kDecodeMaxT && decode_supported(N, K) && aligned16(codes)) {
-    HIP_TRY(launch_decode(packed, codes, consts, X, T, N, K, w.Us, hilo_ld(r), B, r, Y, d->table, s_));
+  if (T <= kDecodeMaxT && decode_supported(N, K, block_shift(d)) && aligned16(codes)) {
+    HIP_TRY(launch_decode(packed, codes, consts, X, T, N, K, w.Us, hilo_ld(r), B, r, Y, d->table, block_shift(d),
+                          s_));
     return QLORA_OK;
   }
   FusedParams fp{};
   fp.A = X; fp.lda = K;
-  fp.packed = packed; fp.codes = codes; fp.consts = consts; fp.Kw = K; fp.table = d->table;
+  fp.packed = packed; fp.codes = codes; fp.consts = consts; fp.Kw = K; fp.table = d->table; fp.bshift = block_shift(d);
   fp.M = T; fp.N = N; fp.K0 = K;
   fp.At = w.Us; fp.ldat = hilo_ld(r); fp.Bt = B; fp.ldbt = r; fp.r = r;
   fp.C = Y; fp.ldc = N;
@@ -350,7 +355,7 @@ int linear_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* co
     // dX = dY W_hat + (s G) A: the contraction runs over d_out, the rows of W
     FusedParams fp{};
     fp.A = dY; fp.lda = N;
-    fp.packed = packed; fp.codes = codes; fp.consts = consts; fp.Kw = K; fp.table = d->table;
+    fp.packed = packed; fp.codes = codes; fp.consts = consts; fp.Kw = K; fp.table = d->table; fp.bshift = block_shift(d);
     fp.M = T; fp.N = K; fp.K0 = N;
     fp.At = w.Gs; fp.ldat = ldh; fp.Bt = A; fp.ldbt = K; fp.r = r;
     fp.C = dX; fp.ldc = K;

@@ -64,6 +64,7 @@ struct DecodeParams {
   const uint16_t* B;   // [N][r]
   int r;
   uint16_t* Y;         // [T][N]
+  int bshift;          // log2(weights per absmax block / 64); K is a multiple of the block
   float level[16];
 };
 
@@ -133,24 +134,25 @@ __global__ __launch_bounds__(DW * 64) void k_decode(DecodeParams P) {
   const int T = (int)P.T, K = (int)P.K;
   const int ntiles = (int)(P.N / 16);
   const int nt0 = (int)blockIdx.x * NTW;
-  const int nbk = K / 64;
+  const int nbk = K / 64;             // 64-weight halves of chunks per row
+  const int nbc = nbk >> P.bshift;    // scale codes per row
   const int nch = (K + 127) / 128;
   const int nmine = nch > wave ? (nch - wave + DW - 1) / DW : 0;
   const int iters = (nmine + PD - 1) / PD * PD;
 
   const __amdgpu_buffer_rsrc_t rw = rsrc(P.packed, P.N * P.K / 2);
   const __amdgpu_buffer_rsrc_t rx = rsrc(P.X, P.T * P.K * 2);
-  const __amdgpu_buffer_rsrc_t rc = rsrc(P.codes, P.N * nbk);
-  const __amdgpu_buffer_rsrc_t rk = rsrc(P.consts, ((P.N * nbk + 255) / 256) * 4);
+  const __amdgpu_buffer_rsrc_t rc = rsrc(P.codes, P.N * nbc);
+  const __amdgpu_buffer_rsrc_t rk = rsrc(P.consts, ((P.N * nbc + 255) / 256) * 4);
 
   // the workgroup's codes: rows nt0*16 .. are one contiguous, 16-byte aligned
-  // run of 16*NTW*nbk bytes in memory (rows past N read zero); in LDS each row
+  // run of 16*NTW*nbc bytes in memory (rows past N read zero); in LDS each row
   // starts at a multiple of rs bytes, rs/4 odd, so that 16 consecutive rows
   // read at one column fall in distinct banks.  Then the ratios c_g / 255 of
   // the groups of 256 blocks the run spans.
-  const uint32_t cfirst = (uint32_t)nt0 * 16u * (uint32_t)nbk;
-  const uint32_t cbytes = 16u * NTW * (uint32_t)nbk;
-  const uint32_t rs = 4u * (((uint32_t)(nbk + 3) >> 2) | 1u);
+  const uint32_t cfirst = (uint32_t)nt0 * 16u * (uint32_t)nbc;
+  const uint32_t cbytes = 16u * NTW * (uint32_t)nbc;
+  const uint32_t rs = 4u * (((uint32_t)(nbc + 3) >> 2) | 1u);
   const uint32_t g_lo = cfirst >> 8;
   const uint32_t ngr = ((cfirst + cbytes - 1u) >> 8) - g_lo + 1u;
   float* ratio = reinterpret_cast<float*>(aux + ((16u * NTW * rs + 15u) & ~15u));
@@ -213,20 +215,20 @@ __global__ __launch_bounds__(DW * 64) void k_decode(DecodeParams P) {
   for (int q = 0; q < CQ; ++q) {
     const uint32_t o = (uint32_t)(tid + q * DT) * 16u;
     if (o < cbytes) {
-      uint32_t row = o / (uint32_t)nbk, col = o - row * (uint32_t)nbk;
+      uint32_t row = o / (uint32_t)nbc, col = o - row * (uint32_t)nbc;
       const uint32_t w4[4] = {cv[q].x, cv[q].y, cv[q].z, cv[q].w};
-      if ((nbk & 3) == 0) {  // dwords never straddle rows
+      if ((nbc & 3) == 0) {  // dwords never straddle rows
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
           *reinterpret_cast<uint32_t*>(aux + row * rs + col) = w4[d];
           col += 4u;
-          if (col >= (uint32_t)nbk) { col -= (uint32_t)nbk; ++row; }
+          if (col >= (uint32_t)nbc) { col -= (uint32_t)nbc; ++row; }
         }
       } else {
 #pragma unroll
         for (int b = 0; b < 16; ++b) {
           aux[row * rs + col] = (uint8_t)(w4[b >> 2] >> (8 * (b & 3)));
-          if (++col == (uint32_t)nbk) { col = 0u; ++row; }
+          if (++col == (uint32_t)nbc) { col = 0u; ++row; }
         }
       }
     }
@@ -263,18 +265,20 @@ __global__ __launch_bounds__(DW * 64) void k_decode(DecodeParams P) {
         // s' = fl32(code) * fl32(c_g / 255) of the chunk's two blocks of this
         // lane's row (zero for a chunk past the row's end, whose weights read zero)
         const uint32_t row = (uint32_t)(16 * i + i16);
-        const uint32_t cl = row * rs + (uint32_t)(2 * chc);                     // code byte in LDS
-        const uint32_t gb = cfirst + row * (uint32_t)nbk + (uint32_t)(2 * chc);  // its block index
         float s0, s1;
-        if (CODES2) {
+        if (CODES2) {  // 64-weight blocks, an even count per row
+          const uint32_t cl = row * rs + (uint32_t)(2 * chc);                     // code byte in LDS
+          const uint32_t gb = cfirst + row * (uint32_t)nbc + (uint32_t)(2 * chc);  // its block index
           const uint32_t c2 = *reinterpret_cast<const uint16_t*>(aux + cl);
           const float rt = ratio[(gb >> 8) - g_lo];
           s0 = (float)(c2 & 0xFFu) * rt;
           s1 = (float)(c2 >> 8) * rt;
-        } else {
+        } else {  // the two halves' blocks (one and the same when blocks hold 128 or 256 weights)
           const bool two = 2 * chc + 1 < nbk;
-          s0 = (float)aux[cl] * ratio[(gb >> 8) - g_lo];
-          s1 = two ? (float)aux[cl + 1u] * ratio[((gb + 1u) >> 8) - g_lo] : 0.f;
+          const uint32_t b0 = (uint32_t)(2 * chc) >> P.bshift, b1 = (uint32_t)(2 * chc + 1) >> P.bshift;
+          const uint32_t gb0 = cfirst + row * (uint32_t)nbc + b0, gb1 = cfirst + row * (uint32_t)nbc + b1;
+          s0 = (float)aux[row * rs + b0] * ratio[(gb0 >> 8) - g_lo];
+          s1 = two ? (float)aux[row * rs + b1] * ratio[(gb1 >> 8) - g_lo] : 0.f;
         }
         s0 = chin ? s0 : 0.f;
         s1 = chin ? s1 : 0.f;
@@ -388,23 +392,26 @@ void launch_ntw(const DecodeParams& P, bool c2, unsigned grid, hipStream_t strea
 
 }  // namespace
 
-// The workgroup's codes must fit their LDS region with at least one 16-row tile.
-bool decode_supported(int64_t N, int64_t K) {
-  if (N % 16 != 0 || K % 64 != 0 || N * K / 2 > 0x7FFFFFF0LL) return false;
-  const int64_t rs = 4 * (((K / 64 + 3) / 4) | 1);
-  return ((16 * rs + 15) & ~15LL) + 4 * (16 * (K / 64) / 256 + 2) <= CODES_BYTES;
+// Rows hold whole blocks, and the workgroup's codes must fit their LDS region
+// with at least one 16-row tile.
+bool decode_supported(int64_t N, int64_t K, int bshift) {
+  if (N % 16 != 0 || K % (64 << bshift) != 0 || N * K / 2 > 0x7FFFFFF0LL) return false;
+  const int64_t nbc = (K / 64) >> bshift;
+  const int64_t rs = 4 * (((nbc + 3) / 4) | 1);
+  return ((16 * rs + 15) & ~15LL) + 4 * (16 * nbc / 256 + 2) <= CODES_BYTES;
 }
 
 hipError_t launch_decode(const uint8_t* packed, const uint8_t* codes, const float* consts, const uint16_t* X,
                          int64_t T, int64_t N, int64_t K, const uint16_t* Us, int64_t ldh, const uint16_t* B,
-                         int r, uint16_t* Y, int table, hipStream_t stream) {
+                         int r, uint16_t* Y, int table, int bshift, hipStream_t stream) {
   // byte offsets into the packed weight, codes and X are 32-bit
-  if (T < 1 || T > 16 || N % 16 != 0 || K % 64 != 0 || N * K / 2 > 0x7FFFFFF0LL) return hipErrorInvalidValue;
+  if (T < 1 || T > 16 || bshift < 0 || bshift > 2 || !decode_supported(N, K, bshift)) return hipErrorInvalidValue;
   DecodeParams P;
   P.packed = packed; P.codes = codes; P.consts = consts; P.X = X;
   P.T = T; P.N = N; P.K = K;
   P.Us = Us; P.ldh = ldh; P.B = B; P.r = r;
   P.Y = Y;
+  P.bshift = bshift;
   const Nf4Table& tab = level_table(table);
   for (int i = 0; i < 16; ++i) P.level[i] = tab.level[i];
   // tiles per workgroup: the 16-row tiles spread over the 256 CUs (at most 8 each)
@@ -413,12 +420,13 @@ hipError_t launch_decode(const uint8_t* packed, const uint8_t* codes, const floa
   if (ntw > 8) ntw = 8;
   // the workgroup's codes and group ratios must fit their LDS region, and the
   // group count one load per thread
-  const int64_t rs = 4 * (((K / 64 + 3) / 4) | 1);  // LDS row stride of the codes
-  auto aux_need = [&](int64_t t) { return ((16 * t * rs + 15) & ~15LL) + 4 * (16 * t * (K / 64) / 256 + 2); };
+  const int64_t nbc = (K / 64) >> bshift;             // scale codes per row
+  const int64_t rs = 4 * (((nbc + 3) / 4) | 1);      // LDS row stride of the codes
+  auto aux_need = [&](int64_t t) { return ((16 * t * rs + 15) & ~15LL) + 4 * (16 * t * nbc / 256 + 2); };
   while (ntw > 1 && aux_need(ntw) > CODES_BYTES) --ntw;
   if (aux_need(ntw) > CODES_BYTES) return hipErrorInvalidValue;
   const unsigned grid = (unsigned)((ntiles + ntw - 1) / ntw);
-  const bool c2 = (K / 64) % 2 == 0;
+  const bool c2 = bshift == 0 && (K / 64) % 2 == 0;
   TraceScope ts(KID_DECODE, stream);
   switch (ntw) {
     case 1: launch_ntw<1>(P, c2, grid, stream); break;

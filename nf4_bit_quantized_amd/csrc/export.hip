@@ -59,6 +59,7 @@ struct ExportParams {
   float s;
   uint16_t* W;        // [N][K] bf16 out
   Nf4Table tab;
+  int bshift;         // log2(weights per absmax block / 64)
 };
 
 template <bool MERGE>
@@ -129,7 +130,7 @@ __global__ __launch_bounds__(256) void k_export(ExportParams P) {
     if (n >= P.N || kc >= P.K) continue;
     const int64_t e0 = n * P.K + kc;  // element index of the pair's first weight
     const uint2 w = *reinterpret_cast<const uint2*>(P.packed + e0 / 2);
-    const int64_t blk = e0 / 64;
+    const int64_t blk = (e0 / 64) >> P.bshift;
     const RestoreTab t = make_tab(P.tab, restored_scale(P.codes[blk], P.consts[blk >> 8]));
     uint32_t o[8];
     restore8(w.x, t, o);
@@ -147,7 +148,7 @@ __global__ __launch_bounds__(256) void k_export(ExportParams P) {
 }
 
 // Dequantize only: pairs p = 16-weight runs in element order (packed bytes
-// 8p .. 8p+7, block p / 4).
+// 8p .. 8p+7, block 16p / blocksize).
 constexpr int DQ_PER = 4;
 __global__ __launch_bounds__(256) void k_dequant(ExportParams P) {
   const int64_t npairs = P.N * P.K / 16;
@@ -160,8 +161,9 @@ __global__ __launch_bounds__(256) void k_dequant(ExportParams P) {
     const int64_t p = p0 + 256 * q;
     const int64_t pc = p < npairs ? p : npairs - 1;
     w[q] = *reinterpret_cast<const uint2*>(P.packed + 8 * pc);
-    code[q] = P.codes[pc >> 2];
-    cg[q] = P.consts[pc >> 10];
+    const int64_t blk = pc >> (2 + P.bshift);
+    code[q] = P.codes[blk];
+    cg[q] = P.consts[blk >> 8];
   }
 #pragma unroll
   for (int q = 0; q < DQ_PER; ++q) {
@@ -181,14 +183,15 @@ __global__ __launch_bounds__(256) void k_dequant(ExportParams P) {
 
 hipError_t launch_export(const uint8_t* packed, const uint8_t* codes, const float* consts, int64_t N, int64_t K,
                          int r, float s, const uint16_t* A, const uint16_t* B, uint16_t* W, int table,
-                         hipStream_t stream) {
-  if (N % TR != 0 || K % 64 != 0 || r < 0 || r > MAX_R) return hipErrorInvalidValue;
+                         int bshift, hipStream_t stream) {
+  if (N % TR != 0 || K % 64 != 0 || r < 0 || r > MAX_R || bshift < 0 || bshift > 2) return hipErrorInvalidValue;
   ExportParams P;
   P.packed = packed; P.codes = codes; P.consts = consts;
   P.N = N; P.K = K;
   P.A = A; P.B = B; P.r = r; P.s = s;
   P.W = W;
   P.tab = level_table(table);
+  P.bshift = bshift;
   const dim3 grid((unsigned)((K + TC - 1) / TC), (unsigned)(N / TR));
   TraceScope ts(KID_EXPORT, stream);
   if (r > 0) {

@@ -23,6 +23,7 @@ struct FusedParams {
   uint16_t* C;             // bf16 output [M][ldc]
   int64_t ldc;
   int32_t table;           // level table (kTableNf4 / kTableUniform)
+  int32_t bshift;          // log2(weights per absmax block / 64)
   int32_t mt, nt, group_m; // filled by the launcher
   Nf4Table tab;            // filled by the launcher from table
 };

@@ -154,11 +154,12 @@ struct StepRegs {
 struct Cursor {
   __amdgpu_buffer_rsrc_t rw, rc, rk;
   uint32_t woff;     // byte offset of the thread's packed words at step 0
-  uint32_t coff;     // block index of the thread's weights at step 0
+  uint32_t coff;     // 64-weight chunk index of the thread's weights at step 0
   uint32_t wstep;    // bytes the packed words advance per step
-  uint32_t cstep;    // blocks the block index advances per step
+  uint32_t cstep;    // chunks the chunk index advances per step
   uint32_t nk;       // contraction steps
   uint32_t rot;      // this workgroup starts its contraction at step rot (see fused_body)
+  uint32_t bshift;   // 64-weight chunk index >> bshift = absmax block index
 };
 
 // Restoring-wave thread index: those are waves 4..7 of the workgroup.
@@ -183,8 +184,10 @@ __device__ __forceinline__ Cursor make_cursor(const FusedParams& P, int64_t n0) 
   Cursor c;
   const int64_t Nw = BT ? P.K0 : P.N;  // rows of the stored weight
   c.rw = rsrc(P.packed, Nw * P.Kw / 2);
-  c.rc = rsrc(P.codes, Nw * P.Kw / 64);
-  c.rk = rsrc(P.consts, ((Nw * P.Kw / 64 + 255) / 256) * 4);
+  const int64_t nblocks = (Nw * P.Kw / 64) >> P.bshift;
+  c.rc = rsrc(P.codes, nblocks);
+  c.rk = rsrc(P.consts, ((nblocks + 255) / 256) * 4);
+  c.bshift = (uint32_t)P.bshift;
   int lrow, lcol;
   w_coords<BN, BT>(lrow, lcol);
   if (!BT) {
@@ -221,8 +224,8 @@ __device__ __forceinline__ void fetch(StepRegs<BN>& f, const Cursor& c, uint32_t
     const u32x4_t w1 = __builtin_amdgcn_raw_buffer_load_b128(c.rw, c.woff + 16, sw, 0);
     f.w[4] = w1.x; f.w[5] = w1.y; f.w[6] = w1.z; f.w[7] = w1.w;
   }
-  const uint32_t blk = c.coff + kt * c.cstep;
-  // the codes array holds N*K/64 bytes, a multiple of 4, so the aligned dword is in range
+  const uint32_t blk = (c.coff + kt * c.cstep) >> c.bshift;
+  // the codes array holds N*K/blocksize bytes, a multiple of 4, so the aligned dword is in range
   f.code4 = __builtin_amdgcn_raw_buffer_load_b32(c.rc, blk & ~3u, 0, 0);
   f.code_shift = (blk & 3u) * 8u;
   f.cg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(c.rk, (blk >> 8) * 4, 0, 0));

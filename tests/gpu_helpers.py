@@ -65,12 +65,12 @@ def oracle_layer(inp, r, alpha, Q=None, do_bwd=True, levels=None):
     return out
 
 
-def gpu_layer(inp, r, alpha, do_bwd=True, pass_u=True, table=0):
+def gpu_layer(inp, r, alpha, do_bwd=True, pass_u=True, table=0, blocksize=64):
     """Quantize + forward (+ backward) through the C ABI; returns host arrays."""
     import torch
     import nf4_bit_quantized_amd as q
     W = dev_f32(inp["W"])
-    packed, codes, consts = q.qlora_quantize_nf4(W, table=table)
+    packed, codes, consts = q.qlora_quantize_nf4(W, table=table, blocksize=blocksize)
     X = dev_bf16(inp["X"])
     A = dev_bf16(inp["A"]) if r > 0 else None
     B = dev_bf16(inp["B"]) if r > 0 else None
@@ -99,7 +99,7 @@ def assert_quant_bit_exact(g, Q):
     np.testing.assert_array_equal(g["consts_h"].view(np.uint32), Q.consts.view(np.uint32))
 
 
-def sweep_blocks(scale, thr, per=63, width=40):
+def sweep_blocks(scale, thr, per=63, width=40, bs=64):
     """Blocks whose absmax is exactly +-scale, holding the float32 neighbours of
     thr[k] * scale for every threshold k (so that fl32(w / scale) walks across
     each decision point)."""
@@ -116,7 +116,7 @@ def sweep_blocks(scale, thr, per=63, width=40):
     vals = np.array(vals, np.float32)
     vals = vals[np.abs(vals) <= scale]
     nblk = -(-vals.size // per)
-    W = np.zeros((nblk, 64), np.float32)
+    W = np.zeros((nblk, bs), np.float32)
     for b in range(nblk):
         chunk = vals[b * per:(b + 1) * per]
         W[b, 0] = scale if b % 2 == 0 else -scale

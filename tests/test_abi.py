@@ -99,7 +99,11 @@ def _err(fn, *a):
 def test_bad_descriptor_rejected():
     assert _err(q.qlora_nf4_sizes, 100, 64) == q.QLORA_ERR_SHAPE
     assert _err(q.qlora_nf4_sizes, 64, 0) == q.QLORA_ERR_SHAPE
-    assert _err(q.qlora_nf4_sizes, 64, 64, 128) == q.QLORA_ERR_UNSUPPORTED
+    assert _err(q.qlora_nf4_sizes, 64, 64, 32) == q.QLORA_ERR_UNSUPPORTED
+    assert _err(q.qlora_nf4_sizes, 64, 64, 512) == q.QLORA_ERR_UNSUPPORTED
+    # blocks of 128 and 256 weights: one code per block, one constant per 256 codes
+    assert q.qlora_nf4_sizes(4096, 4096, 128) == (4096 * 2048, 4096 * 4096 // 128, 4 * 4096 * 4096 // 128 // 256)
+    assert q.qlora_nf4_sizes(64, 192, 256) == (64 * 96, 48, 4)
     assert _err(q.qlora_nf4_sizes, 64, 64, 64, 0) == q.QLORA_ERR_UNSUPPORTED
     assert _err(q.qlora_fwd_workspace_bytes, 64, 64, 4, 129) == q.QLORA_ERR_SHAPE
     assert _err(q.qlora_fwd_workspace_bytes, 64, 64, -1, 4) == q.QLORA_ERR_SHAPE
