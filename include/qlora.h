@@ -36,7 +36,9 @@
  *     consts [ceil(N*K/bs/256)] fp32: per group of 256 consecutive block
  *            scales, the group's largest scale c_g.
  *   Block b is restored with s'_b = fl32(fl32(code_b) * fl32(c_g / 255)) and
- *   each weight as bf16_rne(fl32(T[q] * s'_b)).
+ *   each weight as bf16_rne(fl32(T[q] * s'_b)).  With dq_blocksize == 0 there
+ *   are no codes: consts [N*K/bs] holds each block's fp32 absmax s_b, and
+ *   s'_b = s_b.
  * - Device pointers: every tensor argument is device memory owned by the
  *   caller (the library never allocates, frees or retains device memory and
  *   keeps no state between calls).  Descriptors and output-size pointers are
@@ -55,7 +57,7 @@
  *   most about 2000, else the tiled kernel (same results within the accuracy
  *   stated below).
  * - Inputs must be finite; results for NaN/Inf inputs are unspecified.
- * - Hot-path preconditions: blocksize 64 (also 128 or 256), dq_blocksize == 256,
+ * - Hot-path preconditions: blocksize 64 (also 128 or 256), dq_blocksize 256 (also 0),
  *   d_in % 64 == 0, d_out % 64 == 0, 0 <= r <= 128, T >= 0 (T == 0 is a
  *   no-op).  r == 0 means the base branch only.
  */
@@ -84,7 +86,9 @@ typedef struct qlora_nf4_desc {
   int64_t d_in;         /* K: columns of W */
   int32_t blocksize;    /* weights per absmax block: 64, 128 or 256 ("QLoRA技术从入门到精通"
                            §3(1): blocks of e.g. 64 or 256 values) */
-  int32_t dq_blocksize; /* block scales per second-level group; must be 256 */
+  int32_t dq_blocksize; /* block scales per second-level group: 256, or 0 for no second level
+                           (the fp32 block scales are kept: consts holds one per block, codes is
+                           empty and may be NULL; "7、QLoRA 量化微调" §7.1, 4.5 bits per weight) */
   int32_t table;        /* level table: QLORA_TABLE_NF4 (0) or QLORA_TABLE_UNIFORM (1) */
 } qlora_nf4_desc;
 

@@ -127,15 +127,21 @@ def _desc(d_out: int, d_in: int, blocksize: int = 64, dq_blocksize: int = 256, t
     return Nf4Desc(int(d_out), int(d_in), int(blocksize), int(dq_blocksize), int(table))
 
 
-def _stored_desc(packed, codes, table: int) -> Nf4Desc:
-    """Descriptor of a stored weight; its block size follows from the length of
-    its codes array (one code per block)."""
+def _stored_desc(packed, codes, consts, table: int) -> Nf4Desc:
+    """Descriptor of a stored weight.  Its block size follows from the length
+    of its codes array (one code per block); an empty codes array means no
+    second level, and consts then holds one fp32 scale per block."""
     d_out, d_in = packed.shape[0], packed.shape[1] * 2
-    nb = codes.numel()
+    dq = codes is not None and codes.numel() > 0
+    nb = codes.numel() if dq else consts.numel()
     if nb <= 0 or (d_out * d_in) % nb != 0 or (d_out * d_in) // nb not in (64, 128, 256):
-        raise ValueError(f"codes holds {nb} entries: not one per block of 64, 128 or 256 weights "
-                         f"of a {d_out}x{d_in} weight")
-    return _desc(d_out, d_in, (d_out * d_in) // nb, table=table)
+        raise ValueError(f"{'codes' if dq else 'consts'} holds {nb} entries: not one per block of 64, 128 or "
+                         f"256 weights of a {d_out}x{d_in} weight")
+    bs = (d_out * d_in) // nb
+    want_k = -(-nb // 256) if dq else nb
+    if consts.numel() != want_k:
+        raise ValueError(f"consts holds {consts.numel()} entries, expected {want_k}")
+    return _desc(d_out, d_in, bs, 256 if dq else 0, table=table)
 
 
 def _ptr(t) -> Optional[int]:
@@ -228,18 +234,20 @@ def _workspace(nbytes: int, device, workspace=None):
 
 
 def qlora_quantize_nf4(W, packed=None, codes=None, consts=None, stream=None, table: int = TABLE_NF4,
-                       blocksize: int = 64):
+                       blocksize: int = 64, double_quant: bool = True):
     """Quantize W [d_out][d_in] (GPU; float32, bfloat16 or float16) ->
     (packed uint8 [d_out][d_in/2], codes uint8 [nb], consts float32 [ng]),
     nb = d_out * d_in / blocksize (64, 128 or 256 weights per absmax block).
-    A 16-bit W is widened exactly to fp32 inside the kernel."""
+    double_quant=False keeps the fp32 block scales: codes is empty and consts
+    holds the nb scales.  A 16-bit W is widened exactly to fp32 in the kernel."""
     import torch
     _need_cuda(W, name="qlora_quantize_nf4")
     fmts = {torch.float32: QLORA_W_F32, torch.bfloat16: QLORA_W_BF16, torch.float16: QLORA_W_F16}
     if W.dtype not in fmts or W.dim() != 2:
         raise ValueError("W must be a 2-D float32, bfloat16 or float16 tensor")
     d_out, d_in = W.shape
-    n_p, n_c, n_k = qlora_nf4_sizes(d_out, d_in, blocksize)
+    dqb = 256 if double_quant else 0
+    n_p, n_c, n_k = qlora_nf4_sizes(d_out, d_in, blocksize, dqb)
     if packed is None:
         packed = torch.empty((d_out, d_in // 2), dtype=torch.uint8, device=W.device)
     if codes is None:
@@ -251,7 +259,7 @@ def qlora_quantize_nf4(W, packed=None, codes=None, consts=None, stream=None, tab
                          (consts, "consts", n_k // 4, torch.float32)):
         if t.dtype != dt or t.numel() != n or not t.is_contiguous():
             raise ValueError(f"{nm} must be a contiguous {dt} tensor of {n} elements")
-    d = _desc(d_out, d_in, blocksize, table=table)
+    d = _desc(d_out, d_in, blocksize, dqb, table=table)
     if W.dtype == torch.float32:
         _check(lib().qlora_quantize_nf4(ctypes.byref(d), _ptr(W), _ptr(packed), _ptr(codes), _ptr(consts),
                                         _stream(stream)), "qlora_quantize_nf4")
@@ -282,7 +290,7 @@ def qlora_linear_fwd(packed, codes, consts, X, A, B, alpha: float, Y=None, U_out
         U_out = torch.empty((T, r), dtype=torch.float32, device=X.device)
     nbytes = qlora_fwd_workspace_bytes(d_out, d_in, T, r)
     ws = _workspace(nbytes, X.device, workspace)
-    d = _stored_desc(packed, codes, table)
+    d = _stored_desc(packed, codes, consts, table)
     _check(lib().qlora_linear_fwd(ctypes.byref(d), _ptr(packed), _ptr(codes), _ptr(consts), T, _ptr(X), r,
                                   float(alpha), _ptr(A), _ptr(B), _ptr(Y), _ptr(U_out), _ptr(ws), nbytes,
                                   _stream(stream)), "qlora_linear_fwd")
@@ -318,7 +326,7 @@ def qlora_linear_bwd(packed, codes, consts, X, A, B, alpha: float, dY, U_in=None
                 raise ValueError(f"{nm} must be a contiguous float32 tensor of shape {shape}")
     nbytes = qlora_bwd_workspace_bytes(d_out, d_in, T, r)
     ws = _workspace(nbytes, X.device, workspace)
-    d = _stored_desc(packed, codes, table)
+    d = _stored_desc(packed, codes, consts, table)
     name = "qlora_linear_bwd_accumulate" if accumulate else "qlora_linear_bwd"
     _check(getattr(lib(), name)(ctypes.byref(d), _ptr(packed), _ptr(codes), _ptr(consts), T, _ptr(X), r,
                                 float(alpha), _ptr(A), _ptr(B), _ptr(U_in), _ptr(dY), _ptr(dX), _ptr(dA),
@@ -334,7 +342,7 @@ def qlora_dequantize_nf4(packed, codes, consts, W_hat=None, stream=None, table: 
     _need_cuda(packed, codes, consts, W_hat, name="qlora_dequantize_nf4")
     if W_hat is None:
         W_hat = torch.empty((d_out, d_in), dtype=torch.bfloat16, device=packed.device)
-    d = _stored_desc(packed, codes, table)
+    d = _stored_desc(packed, codes, consts, table)
     _check(lib().qlora_dequantize_nf4(ctypes.byref(d), _ptr(packed), _ptr(codes), _ptr(consts), _ptr(W_hat),
                                       _stream(stream)), "qlora_dequantize_nf4")
     return W_hat
@@ -353,7 +361,7 @@ def qlora_merge_lora(packed, codes, consts, A, B, alpha: float, W_merged=None, s
             raise ValueError(f"{nm} must be bfloat16")
     if W_merged is None:
         W_merged = torch.empty((d_out, d_in), dtype=torch.bfloat16, device=packed.device)
-    d = _stored_desc(packed, codes, table)
+    d = _stored_desc(packed, codes, consts, table)
     _check(lib().qlora_merge_lora(ctypes.byref(d), _ptr(packed), _ptr(codes), _ptr(consts), int(r), float(alpha),
                                   _ptr(A), _ptr(B), _ptr(W_merged), _stream(stream)), "qlora_merge_lora")
     return W_merged

@@ -16,7 +16,7 @@
 
 namespace qlora {
 hipError_t launch_nf4_quantize(const void* W, int wformat, uint8_t* packed, uint8_t* codes, float* consts,
-                               int64_t numel, int blocksize, int table, hipStream_t stream);
+                               int64_t numel, int blocksize, int dq, int table, hipStream_t stream);
 bool decode_supported(int64_t N, int64_t K, int bshift);
 hipError_t launch_decode(const uint8_t* packed, const uint8_t* codes, const float* consts, const uint16_t* X,
                          int64_t T, int64_t N, int64_t K, const uint16_t* Us, int64_t ldh, const uint16_t* B,
@@ -24,7 +24,7 @@ hipError_t launch_decode(const uint8_t* packed, const uint8_t* codes, const floa
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
 hipError_t launch_export(const uint8_t* packed, const uint8_t* codes, const float* consts, int64_t N, int64_t K,
                          int r, float s, const uint16_t* A, const uint16_t* B, uint16_t* W, int table,
-                         int bshift, hipStream_t stream);
+                         int bshift, int dq, hipStream_t stream);
 }  // namespace qlora
 
 using namespace qlora;
@@ -43,7 +43,8 @@ int block_shift(const qlora_nf4_desc* d) { return d->blocksize == 256 ? 2 : (d->
 
 int check_desc(const qlora_nf4_desc* d) {
   if (!d) return QLORA_ERR_NULL;
-  if ((d->blocksize != 64 && d->blocksize != 128 && d->blocksize != 256) || d->dq_blocksize != 256)
+  if ((d->blocksize != 64 && d->blocksize != 128 && d->blocksize != 256) ||
+      (d->dq_blocksize != 256 && d->dq_blocksize != 0))
     return QLORA_ERR_UNSUPPORTED;
   if (d->table != QLORA_TABLE_NF4 && d->table != QLORA_TABLE_UNIFORM) return QLORA_ERR_UNSUPPORTED;
   if (d->d_out <= 0 || d->d_in <= 0 || d->d_out % 64 != 0 || d->d_in % 64 != 0) return QLORA_ERR_SHAPE;
@@ -202,8 +203,9 @@ int qlora_nf4_sizes(const qlora_nf4_desc* d, size_t* packed_bytes, size_t* codes
   const int64_t numel = d->d_out * d->d_in;
   const int64_t nb = numel / d->blocksize;
   *packed_bytes = (size_t)(numel / 2);
-  *codes_bytes = (size_t)nb;
-  *consts_bytes = (size_t)cdiv(nb, 256) * 4;
+  const bool dq = d->dq_blocksize != 0;
+  *codes_bytes = dq ? (size_t)nb : 0;
+  *consts_bytes = dq ? (size_t)cdiv(nb, 256) * 4 : (size_t)nb * 4;
   return QLORA_OK;
 }
 
@@ -216,13 +218,13 @@ int qlora_quantize_nf4_typed(const qlora_nf4_desc* d, const void* W, int32_t w_f
                              uint8_t* codes, float* consts, void* stream) {
   const int st = check_desc(d);
   if (st) return st;
-  if (!W || !packed || !codes || !consts) return QLORA_ERR_NULL;
+  if (!W || !packed || (!codes && d->dq_blocksize) || !consts) return QLORA_ERR_NULL;
   static_assert(QLORA_W_F32 == kWeightF32 && QLORA_W_BF16 == kWeightBf16 && QLORA_W_F16 == kWeightF16,
                 "weight formats");
   if (w_format != QLORA_W_F32 && w_format != QLORA_W_BF16 && w_format != QLORA_W_F16) return QLORA_ERR_UNSUPPORTED;
   if (!aligned16(W) || !aligned16(packed)) return QLORA_ERR_UNSUPPORTED;
-  HIP_TRY(launch_nf4_quantize(W, w_format, packed, codes, consts, d->d_out * d->d_in, d->blocksize, d->table,
-                              (hipStream_t)stream));
+  HIP_TRY(launch_nf4_quantize(W, w_format, packed, codes, consts, d->d_out * d->d_in, d->blocksize,
+                              d->dq_blocksize != 0, d->table, (hipStream_t)stream));
   return QLORA_OK;
 }
 
@@ -236,12 +238,12 @@ int qlora_merge_lora(const qlora_nf4_desc* d, const uint8_t* packed, const uint8
                      uint16_t* W_merged, void* stream) {
   const int st = check_layer(d, 0, r);
   if (st) return st;
-  if (!packed || !codes || !consts || !W_merged) return QLORA_ERR_NULL;
+  if (!packed || (!codes && d->dq_blocksize) || !consts || !W_merged) return QLORA_ERR_NULL;
   if (r > 0 && (!A || !B)) return QLORA_ERR_NULL;
   if (!aligned16(W_merged) || (r > 0 && (!aligned16(A) || !aligned16(B)))) return QLORA_ERR_UNSUPPORTED;
   const float s = r > 0 ? alpha / (float)r : 0.0f;
   HIP_TRY(launch_export(packed, codes, consts, d->d_out, d->d_in, r, s, A, B, W_merged, d->table, block_shift(d),
-                        (hipStream_t)stream));
+                        d->dq_blocksize != 0, (hipStream_t)stream));
   return QLORA_OK;
 }
 
@@ -267,7 +269,7 @@ int qlora_linear_fwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8
                      void* workspace, size_t workspace_bytes, void* stream) {
   const int st = check_layer(d, T, r);
   if (st) return st;
-  if (!packed || !codes || !consts) return QLORA_ERR_NULL;
+  if (!packed || (!codes && d->dq_blocksize) || !consts) return QLORA_ERR_NULL;
   if (T > 0 && (!X || !Y)) return QLORA_ERR_NULL;
   if (r > 0 && (!A || !B)) return QLORA_ERR_NULL;
   if (!aligned16(packed) || !aligned16(X) || !aligned16(A) || !aligned16(B)) return QLORA_ERR_UNSUPPORTED;
@@ -285,7 +287,8 @@ int qlora_linear_fwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8
     const int e = lora_down(X, A, T, K, r, s, w.part, U, w.Us, s_);
     if (e) return e;
   }
-  if (T <= kDecodeMaxT && decode_supported(N, K, block_shift(d)) && aligned16(codes)) {
+  // the few-token kernel stages 8-bit codes; fp32 block scales take the tiled kernel
+  if (T <= kDecodeMaxT && d->dq_blocksize != 0 && decode_supported(N, K, block_shift(d)) && aligned16(codes)) {
     HIP_TRY(launch_decode(packed, codes, consts, X, T, N, K, w.Us, hilo_ld(r), B, r, Y, d->table, block_shift(d),
                           s_));
     return QLORA_OK;
@@ -293,6 +296,7 @@ int qlora_linear_fwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8
   FusedParams fp{};
   fp.A = X; fp.lda = K;
   fp.packed = packed; fp.codes = codes; fp.consts = consts; fp.Kw = K; fp.table = d->table; fp.bshift = block_shift(d);
+  fp.dq = d->dq_blocksize != 0;
   fp.M = T; fp.N = N; fp.K0 = K;
   fp.At = w.Us; fp.ldat = hilo_ld(r); fp.Bt = B; fp.ldbt = r; fp.r = r;
   fp.C = Y; fp.ldc = N;
@@ -307,7 +311,7 @@ int linear_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* co
                void* stream, int accumulate) {
   const int st = check_layer(d, T, r);
   if (st) return st;
-  if (!packed || !codes || !consts) return QLORA_ERR_NULL;
+  if (!packed || (!codes && d->dq_blocksize) || !consts) return QLORA_ERR_NULL;
   if (T > 0 && (!X || !dY)) return QLORA_ERR_NULL;
   if (r > 0 && (!A || !B || !dA || !dB)) return QLORA_ERR_NULL;
   if (!aligned16(packed) || !aligned16(X) || !aligned16(dY) || !aligned16(A) || !aligned16(B))
@@ -356,6 +360,7 @@ int linear_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* co
     FusedParams fp{};
     fp.A = dY; fp.lda = N;
     fp.packed = packed; fp.codes = codes; fp.consts = consts; fp.Kw = K; fp.table = d->table; fp.bshift = block_shift(d);
+    fp.dq = d->dq_blocksize != 0;
     fp.M = T; fp.N = K; fp.K0 = N;
     fp.At = w.Gs; fp.ldat = ldh; fp.Bt = A; fp.ldbt = K; fp.r = r;
     fp.C = dX; fp.ldc = K;

@@ -60,6 +60,7 @@ struct ExportParams {
   uint16_t* W;        // [N][K] bf16 out
   Nf4Table tab;
   int bshift;         // log2(weights per absmax block / 64)
+  int dq;             // 1: codes + group constants; 0: consts holds the fp32 block scales
 };
 
 template <bool MERGE>
@@ -131,7 +132,7 @@ __global__ __launch_bounds__(256) void k_export(ExportParams P) {
     const int64_t e0 = n * P.K + kc;  // element index of the pair's first weight
     const uint2 w = *reinterpret_cast<const uint2*>(P.packed + e0 / 2);
     const int64_t blk = (e0 / 64) >> P.bshift;
-    const RestoreTab t = make_tab(P.tab, restored_scale(P.codes[blk], P.consts[blk >> 8]));
+    const RestoreTab t = make_tab(P.tab, P.dq ? restored_scale(P.codes[blk], P.consts[blk >> 8]) : P.consts[blk]);
     uint32_t o[8];
     restore8(w.x, t, o);
     restore8(w.y, t, o + 4);
@@ -162,14 +163,14 @@ __global__ __launch_bounds__(256) void k_dequant(ExportParams P) {
     const int64_t pc = p < npairs ? p : npairs - 1;
     w[q] = *reinterpret_cast<const uint2*>(P.packed + 8 * pc);
     const int64_t blk = pc >> (2 + P.bshift);
-    code[q] = P.codes[blk];
-    cg[q] = P.consts[blk >> 8];
+    code[q] = P.dq ? P.codes[blk] : 0u;
+    cg[q] = P.consts[P.dq ? blk >> 8 : blk];
   }
 #pragma unroll
   for (int q = 0; q < DQ_PER; ++q) {
     const int64_t p = p0 + 256 * q;
     if (p >= npairs) break;
-    const RestoreTab t = make_tab(P.tab, restored_scale(code[q], cg[q]));
+    const RestoreTab t = make_tab(P.tab, P.dq ? restored_scale(code[q], cg[q]) : cg[q]);
     uint32_t o[8];
     restore8(w[q].x, t, o);
     restore8(w[q].y, t, o + 4);
@@ -183,7 +184,7 @@ __global__ __launch_bounds__(256) void k_dequant(ExportParams P) {
 
 hipError_t launch_export(const uint8_t* packed, const uint8_t* codes, const float* consts, int64_t N, int64_t K,
                          int r, float s, const uint16_t* A, const uint16_t* B, uint16_t* W, int table,
-                         int bshift, hipStream_t stream) {
+                         int bshift, int dq, hipStream_t stream) {
   if (N % TR != 0 || K % 64 != 0 || r < 0 || r > MAX_R || bshift < 0 || bshift > 2) return hipErrorInvalidValue;
   ExportParams P;
   P.packed = packed; P.codes = codes; P.consts = consts;
@@ -192,6 +193,7 @@ hipError_t launch_export(const uint8_t* packed, const uint8_t* codes, const floa
   P.W = W;
   P.tab = level_table(table);
   P.bshift = bshift;
+  P.dq = dq;
   const dim3 grid((unsigned)((K + TC - 1) / TC), (unsigned)(N / TR));
   TraceScope ts(KID_EXPORT, stream);
   if (r > 0) {

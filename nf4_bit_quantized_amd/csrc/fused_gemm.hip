@@ -160,6 +160,7 @@ struct Cursor {
   uint32_t nk;       // contraction steps
   uint32_t rot;      // this workgroup starts its contraction at step rot (see fused_body)
   uint32_t bshift;   // 64-weight chunk index >> bshift = absmax block index
+  uint32_t dq;       // 1: codes + group constants; 0: fp32 block scales in consts
 };
 
 // Restoring-wave thread index: those are waves 4..7 of the workgroup.
@@ -185,9 +186,10 @@ __device__ __forceinline__ Cursor make_cursor(const FusedParams& P, int64_t n0) 
   const int64_t Nw = BT ? P.K0 : P.N;  // rows of the stored weight
   c.rw = rsrc(P.packed, Nw * P.Kw / 2);
   const int64_t nblocks = (Nw * P.Kw / 64) >> P.bshift;
-  c.rc = rsrc(P.codes, nblocks);
-  c.rk = rsrc(P.consts, ((nblocks + 255) / 256) * 4);
+  c.rc = rsrc(P.codes, P.dq ? nblocks : 0);
+  c.rk = rsrc(P.consts, P.dq ? ((nblocks + 255) / 256) * 4 : nblocks * 4);
   c.bshift = (uint32_t)P.bshift;
+  c.dq = (uint32_t)P.dq;
   int lrow, lcol;
   w_coords<BN, BT>(lrow, lcol);
   if (!BT) {
@@ -225,10 +227,11 @@ __device__ __forceinline__ void fetch(StepRegs<BN>& f, const Cursor& c, uint32_t
     f.w[4] = w1.x; f.w[5] = w1.y; f.w[6] = w1.z; f.w[7] = w1.w;
   }
   const uint32_t blk = (c.coff + kt * c.cstep) >> c.bshift;
-  // the codes array holds N*K/blocksize bytes, a multiple of 4, so the aligned dword is in range
+  // the codes array holds N*K/blocksize bytes, a multiple of 4, so the aligned dword is in range;
+  // without the second level the code load reads zero (empty range) and cg is the block's scale
   f.code4 = __builtin_amdgcn_raw_buffer_load_b32(c.rc, blk & ~3u, 0, 0);
   f.code_shift = (blk & 3u) * 8u;
-  f.cg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(c.rk, (blk >> 8) * 4, 0, 0));
+  f.cg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(c.rk, (c.dq ? blk >> 8 : blk) * 4, 0, 0));
 }
 
 // Keeps the scheduler from hoisting work on prefetched registers above the
@@ -242,11 +245,12 @@ __device__ __forceinline__ void pin(StepRegs<BN>& f) {
 }
 
 template <int BN, bool BT>
-__device__ __forceinline__ void restore_step(StepRegs<BN>& f, const Nf4Table& tab, uint16_t* __restrict__ Bs) {
+__device__ __forceinline__ void restore_step(StepRegs<BN>& f, const Nf4Table& tab, int dq,
+                                             uint16_t* __restrict__ Bs) {
   pin<BN>(f);
   int lrow, lcol;
   w_coords<BN, BT>(lrow, lcol);
-  const RestoreTab t = make_tab(tab, restored_scale((f.code4 >> f.code_shift) & 0xFFu, f.cg));
+  const RestoreTab t = make_tab(tab, dq ? restored_scale((f.code4 >> f.code_shift) & 0xFFu, f.cg) : f.cg);
   uint16_t* dst = BT ? Bs + lrow * Geometry<BN, BT>::LDB_T + lcol : Bs + lrow * LDK + lcol;
 #pragma unroll
   for (int i = 0; i < BN / 32; i += 2) {
@@ -493,11 +497,11 @@ __device__ __forceinline__ void fused_body(const FusedParams& P) {
     fetch<BN>(f0, cur, 0);
     fetch<BN>(f1, cur, 1 < nk ? 1 : last);
     fetch<BN>(f2, cur, 2 < nk ? 2 : last);
-    restore_step<BN, BT>(f0, P.tab, b_stage(0));
+    restore_step<BN, BT>(f0, P.tab, P.dq, b_stage(0));
     lds_barrier();
     auto period = [&](StepRegs<BN>& into, StepRegs<BN>& from, uint32_t h) {
       fetch<BN>(into, cur, h + 3 < nk ? h + 3 : last);
-      restore_step<BN, BT>(from, P.tab, b_stage(h + 1));
+      restore_step<BN, BT>(from, P.tab, P.dq, b_stage(h + 1));
       lds_barrier();
     };
     // periods h = 0 .. nk-2 restore main steps 1 .. nk-1

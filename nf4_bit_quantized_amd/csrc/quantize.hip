@@ -62,7 +62,7 @@ __global__ __launch_bounds__(256) void k_nf4_quantize(const void* __restrict__ W
                                                       uint8_t* __restrict__ packed,
                                                       uint8_t* __restrict__ codes,
                                                       float* __restrict__ consts, int64_t nb,
-                                                      QuantLut lut) {
+                                                      QuantLut lut, int dq) {
   static_assert(BS == 64 || BS == 128 || BS == 256, "block size");
   constexpr int NPASS = BS / 64;
   constexpr int LPB = BS / 4;  // lanes per block
@@ -166,7 +166,9 @@ __global__ __launch_bounds__(256) void k_nf4_quantize(const void* __restrict__ W
   __syncthreads();
   const float cg = fmaxf(fmaxf(sh_wmax[0], sh_wmax[1]), fmaxf(sh_wmax[2], sh_wmax[3]));
 
-  if (t < nblk) {
+  if (!dq) {  // no second level: the fp32 block scales themselves
+    if (t < nblk) consts[blk0 + t] = sh_scale[t];
+  } else if (t < nblk) {
     uint32_t code = 0;
     if (cg > 0.0f) {
       const float ratio = sh_scale[t] / cg;
@@ -177,7 +179,7 @@ __global__ __launch_bounds__(256) void k_nf4_quantize(const void* __restrict__ W
     }
     codes[blk0 + t] = (uint8_t)code;
   }
-  if (t == 0) consts[g] = cg;
+  if (dq && t == 0) consts[g] = cg;
 
   // the group's packed bytes (nblk * BS / 2 of them) as 16-byte stores
   typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -187,7 +189,7 @@ __global__ __launch_bounds__(256) void k_nf4_quantize(const void* __restrict__ W
 }
 
 hipError_t launch_nf4_quantize(const void* W, int wformat, uint8_t* packed, uint8_t* codes, float* consts,
-                               int64_t numel, int blocksize, int table, hipStream_t stream) {
+                               int64_t numel, int blocksize, int dq, int table, hipStream_t stream) {
   bool ok = false;
   const QuantLut& lut = quant_lut(table, &ok);
   if (!ok) return hipErrorInvalidValue;
@@ -199,7 +201,7 @@ hipError_t launch_nf4_quantize(const void* W, int wformat, uint8_t* packed, uint
   TraceScope ts(KID_QUANTIZE, stream);
   const dim3 grid((unsigned)ng), block(256);
 #define QLORA_QUANT_LAUNCH(WFV, BSV) \
-  hipLaunchKernelGGL((k_nf4_quantize<WFV, BSV>), grid, block, 0, stream, W, packed, codes, consts, nb, lut)
+  hipLaunchKernelGGL((k_nf4_quantize<WFV, BSV>), grid, block, 0, stream, W, packed, codes, consts, nb, lut, dq)
 #define QLORA_QUANT_BS(WFV)                \
   if (blocksize == 64) QLORA_QUANT_LAUNCH(WFV, 64);   \
   else if (blocksize == 128) QLORA_QUANT_LAUNCH(WFV, 128); \

@@ -104,7 +104,7 @@ def test_bad_descriptor_rejected():
     # blocks of 128 and 256 weights: one code per block, one constant per 256 codes
     assert q.qlora_nf4_sizes(4096, 4096, 128) == (4096 * 2048, 4096 * 4096 // 128, 4 * 4096 * 4096 // 128 // 256)
     assert q.qlora_nf4_sizes(64, 192, 256) == (64 * 96, 48, 4)
-    assert _err(q.qlora_nf4_sizes, 64, 64, 64, 0) == q.QLORA_ERR_UNSUPPORTED
+    assert _err(q.qlora_nf4_sizes, 64, 64, 64, 64) == q.QLORA_ERR_UNSUPPORTED
     assert _err(q.qlora_fwd_workspace_bytes, 64, 64, 4, 129) == q.QLORA_ERR_SHAPE
     assert _err(q.qlora_fwd_workspace_bytes, 64, 64, -1, 4) == q.QLORA_ERR_SHAPE
 
@@ -193,6 +193,16 @@ def test_adamw_validation_happens_before_any_launch():
     assert L.qlora_adamw_step(ctypes.byref(ok), 8, fake, fake, fake, fake, fake + 2, None) == \
         q.QLORA_ERR_UNSUPPORTED
     assert ctypes.sizeof(q.AdamwHparams) == 32
+
+
+def test_fp32_scale_format_sizes():
+    """No second level ("7、QLoRA 量化微调" §7.1, extended calculation: 64 weights
+    sharing one fp32 scale cost 4.5 bits each): no codes, one fp32 scale per block."""
+    n_p, n_c, n_k = q.qlora_nf4_sizes(4096, 4096, 64, 0)
+    assert n_c == 0 and n_k == 4 * 4096 * 4096 // 64
+    assert (n_p + n_c + n_k) * 8 / (4096 * 4096) == 4.5
+    assert q.qlora_nf4_sizes(64, 320, 256, 0) == (64 * 160, 0, 4 * 64 * 320 // 256)
+    assert _err(q.qlora_nf4_sizes, 64, 64, 64, 128) == q.QLORA_ERR_UNSUPPORTED
 
 
 def test_workspace_sizes_grow_with_tokens_and_rank():
