@@ -171,3 +171,94 @@ def test_trainable_parameter_count():
     B = np.zeros((d, r))
     assert A.size + B.size == 65536
     assert round(100 * (A.size + B.size) / (d * d), 2) == 0.39
+
+
+# --------------------------------------------------------------------------
+# LoRA dropout on the adapter input ([LoRA-QLoRA-工程] §4.3)
+# --------------------------------------------------------------------------
+
+def _drop_case(p=0.25, seed=21):
+    import workloads
+    rng = np.random.default_rng(seed)
+    T, K, N, r = 5, 16, 12, 3
+    W = rng.standard_normal((N, K))
+    X = rng.standard_normal((T, K))
+    A = rng.standard_normal((r, K))
+    B = rng.standard_normal((N, r))
+    dY = rng.standard_normal((T, N))
+    keep = workloads.dropout_keep_bits(T, K, p, seed)
+    return W, X, A, B, dY, keep, r
+
+
+def test_dropout_keep_bit_order():
+    bits = np.array([[0b00000101, 0b10000000]], np.uint8)
+    k = lora.unpack_keep(bits, 16)
+    assert list(np.flatnonzero(k[0])) == [0, 2, 15]
+
+
+def test_dropout_p0_all_kept_is_the_plain_layer():
+    from oracle.bf16 import round_to_bf16
+    W, X, A, B, dY, _, r = _drop_case()
+    X = round_to_bf16(X.astype(np.float32)).astype(np.float64)      # exact bf16 inputs
+    keep = np.full((X.shape[0], X.shape[1] // 8), 0xFF, np.uint8)
+    Y0, U0 = lora.forward(W, X, A, B, 4.0, r)
+    Y1, U1 = lora.forward_dropout(W, X, A, B, 4.0, r, keep, 0.0)
+    np.testing.assert_array_equal(Y0, Y1)
+    np.testing.assert_array_equal(U0, U1)
+    for a, b in zip(lora.backward(W, X, A, B, dY, 4.0, r), lora.backward_dropout(W, X, A, B, dY, 4.0, r, keep, 0.0)):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_dropout_all_dropped_leaves_the_base_branch():
+    W, X, A, B, dY, _, r = _drop_case()
+    keep = np.zeros((X.shape[0], X.shape[1] // 8), np.uint8)
+    Y, U = lora.forward_dropout(W, X, A, B, 4.0, r, keep, 0.5)
+    assert not U.any()
+    np.testing.assert_array_equal(Y, X @ W.T)
+    dX, dA, dB = lora.backward_dropout(W, X, A, B, dY, 4.0, r, keep, 0.5)
+    np.testing.assert_array_equal(dX, dY @ W)
+    assert not dA.any() and not dB.any()
+
+
+def _autograd_dropout(W, X, A, B, dY, keep_bool, c, s):
+    import torch
+    t = lambda a: torch.tensor(a, dtype=torch.float64, requires_grad=True)
+    Xt, At, Bt = t(X), t(A), t(B)
+    M = torch.tensor(keep_bool, dtype=torch.float64)
+    Y = Xt @ torch.tensor(W).T + s * ((Xt * M * c) @ At.T) @ Bt.T
+    (Y * torch.tensor(dY)).sum().backward()
+    return Xt.grad.numpy(), At.grad.numpy(), Bt.grad.numpy()
+
+
+def test_dropout_backward_matches_torch_autograd_float64():
+    W, X, A, B, dY, keep, r = _drop_case()
+    alpha, p = 6.0, 0.25
+    want = _autograd_dropout(W, X, A, B, dY, lora.unpack_keep(keep, X.shape[1]), lora.dropout_factor(p),
+                             lora.lora_scale(alpha, r))
+    got = lora.backward_dropout(W, X, A, B, dY, alpha, r, keep, p, round_bf16=False)
+    for g, w in zip(got, want):
+        np.testing.assert_allclose(g, w, rtol=1e-12, atol=1e-12)
+
+
+def test_dropout_planted_mistake_fails_autograd():
+    # the adapter's share of dX without the mask (a plausible slip) differs from autograd
+    W, X, A, B, dY, keep, r = _drop_case()
+    alpha, p = 6.0, 0.25
+    want = _autograd_dropout(W, X, A, B, dY, lora.unpack_keep(keep, X.shape[1]), lora.dropout_factor(p),
+                             lora.lora_scale(alpha, r))[0]
+    s = lora.lora_scale(alpha, r)
+    unmasked = dY @ W + s * ((dY @ B) @ A) * lora.dropout_factor(p)
+    assert not np.allclose(unmasked, want, rtol=1e-6)
+
+
+def test_dropped_input_rounding():
+    # kept values are bf16(fl32(x * c)), c = fl32(1 / (1 - p)); checked against
+    # torch's own float32 product and float32 -> bfloat16 conversion
+    import torch
+    X = np.array([[1.0, 3.0, -0.7, 2.5, 0.1, 0.2, 0.3, 0.4]])
+    keep = np.array([[0b11111011]], np.uint8)
+    Xd = lora.dropped_input(X, keep, 0.1)
+    c = torch.tensor(1.0, dtype=torch.float32) / (torch.tensor(1.0, dtype=torch.float32) - torch.tensor(0.1, dtype=torch.float32))
+    want = (torch.tensor(X[0], dtype=torch.float32) * c).to(torch.bfloat16).to(torch.float64).numpy()
+    want[2] = 0.0
+    np.testing.assert_array_equal(Xd[0], want)

@@ -61,6 +61,14 @@ def layer_inputs(d_out: int, d_in: int, T: int, r: int, seed: int, with_dy: bool
     return out
 
 
+def dropout_keep_bits(T: int, d_in: int, p: float, seed: int) -> np.ndarray:
+    """Seeded LoRA-dropout keep mask: each element kept with probability 1 - p,
+    packed 8 per byte ([T][d_in / 8] uint8, bit j of byte i keeps element 8i + j)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    keep = rng.random((T, d_in)) >= p
+    return np.packbits(keep, axis=1, bitorder="little")
+
+
 def bf16_bits_to_float(bits: np.ndarray) -> np.ndarray:
     """uint16 bf16 bit patterns -> float32 values (exact widening)."""
     b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
