@@ -258,6 +258,55 @@ def quantize16_section(lin, steps):
     return out
 
 
+def dropout_section(lin, steps):
+    """The attention-shaped step with LoRA dropout on the adapter input at the
+    pages' rate (p = 0.05, seeded keep mask), beside the same step without it:
+    step time, and the two dropout kernels' own time."""
+    import torch
+    import nf4_bit_quantized_amd as q
+    import workloads
+
+    N, K, T, r, alpha, p = lin.d_out, lin.d_in, lin.T, lin.r, lin.alpha, 0.05
+    inp = workloads.layer_inputs(N, K, T, r, lin.seed)
+    X, A, B, dY = (bf16_dev(inp[k]) for k in ("X", "A", "B", "dY"))
+    keep = torch.from_numpy(workloads.dropout_keep_bits(T, K, p, lin.seed)).cuda()
+    packed, codes, consts = q.qlora_quantize_nf4(torch.from_numpy(inp["W"]).cuda())
+    Y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+    U = torch.empty((T, r), dtype=torch.float32, device="cuda")
+    dX = torch.empty((T, K), dtype=torch.bfloat16, device="cuda")
+    dA = torch.empty((r, K), dtype=torch.float32, device="cuda")
+    dB = torch.empty((N, r), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(q.qlora_bwd_workspace_bytes(N, K, T, r), q.qlora_fwd_workspace_bytes(N, K, T, r))
+                     + T * K * 2 + 256, dtype=torch.uint8, device="cuda")
+    out = {"p": p}
+    for name, kw in (("plain", {}), ("dropout", {"keep": keep, "p": p})):
+        def step():
+            q.qlora_linear_fwd(packed, codes, consts, X, A, B, alpha, Y=Y, U_out=U, workspace=ws, **kw)
+            q.qlora_linear_bwd(packed, codes, consts, X, A, B, alpha, dY, U_in=U, dX=dX, dA=dA, dB=dB, workspace=ws,
+                               **kw)
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name + "_fwd_bwd_ms"] = round(e0.elapsed_time(e1) / steps, 4)
+    q.qlora_trace_read(reset=True)
+    q.qlora_trace_select({"dropout"})
+    for _ in range(steps):
+        q.qlora_linear_bwd(packed, codes, consts, X, A, B, alpha, dY, U_in=U, dX=dX, dA=dA, dB=dB, workspace=ws,
+                           keep=keep, p=p)
+    torch.cuda.synchronize()
+    q.qlora_trace_enable(False)
+    n, ms = q.qlora_trace_read(reset=True).get("dropout", (1, float("nan")))
+    out["dropout_kernels_us_per_bwd"] = round(ms / max(n, 1) * 2 * 1e3, 2)   # two launches per backward
+    log("dropout", out)
+    return out
+
+
 def adamw_section(steps):
     """The AdamW update over every adapter of the 65B-class stack (8 layers x
     q, k, v, o 8192x8192, gate/up 8192->22016, down 22016->8192, r = 64) laid
@@ -410,6 +459,7 @@ def main():
         result["export_bf16"] = export_section(lin, steps=max(20, args.steps))
         result["quantize_16bit_weight"] = quantize16_section(lin, steps=max(20, args.steps))
         result["adamw_65b_adapters"] = adamw_section(steps=max(20, args.steps))
+        result["lora_dropout_attn4096"] = dropout_section(lin, steps=max(20, args.steps))
     if not args.no_cpu_baseline:
         log("timing the oracle on the host ...")
         result["cpu_baseline"] = cpu_baseline(inp, lin, args.cpu_seconds)

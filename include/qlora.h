@@ -269,6 +269,36 @@ int qlora_merge_lora(const qlora_nf4_desc* d, const uint8_t* packed, const uint8
  * Not thread-safe with respect to concurrent compute calls on other threads.
  */
 /*
+ * LoRA dropout on the adapter's input ("LoRA 与 QLoRA：..." §4.3; its §8
+ * configuration uses lora_dropout 0.05).  The base branch takes X unchanged;
+ * the adapter takes X_d = bf16_rne(fl32(x * c)) where kept and 0 where
+ * dropped, c = fl32(1 / fl32(1 - p)):
+ *   forward   U = X_d A^T,  Y = bf16(X W_hat^T + s U B^T)
+ *   backward  dX = bf16(bf16(dY W_hat) + keep * c * (s G A)),  dA = s G^T X_d,
+ *             dB = s dY^T U          (G = dY B; U as saved by the forward)
+ * keep: the mask, an input (the random draw is the caller's): device,
+ * [T][K/8] bytes, bit j of byte i (least significant first) keeps element
+ * 8i + j of the row.  p in [0, 1).  The adapter's share of dX is added to the
+ * rounded base share, so dX is rounded twice (once more than without
+ * dropout).  Workspace: qlora_dropout_workspace_bytes (backward = 0 or 1);
+ * its first T*K*2 bytes (rounded up to 256) hold X_d.  accumulate != 0 adds
+ * to dA and dB as qlora_linear_bwd_accumulate does.  Other arguments as in
+ * qlora_linear_fwd / qlora_linear_bwd.  r == 0 or T == 0: the plain call.
+ * Errors: as those calls, and NULL (keep when T > 0 and r > 0),
+ * UNSUPPORTED (p outside [0, 1)).
+ */
+int qlora_dropout_workspace_bytes(const qlora_nf4_desc* d, int64_t T, int32_t r, int32_t backward, size_t* bytes);
+int qlora_linear_fwd_dropout(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes,
+                             const float* consts, int64_t T, const uint16_t* X, int32_t r, float alpha,
+                             const uint16_t* A, const uint16_t* B, const uint8_t* keep, float p, uint16_t* Y,
+                             float* U_out, void* workspace, size_t workspace_bytes, void* stream);
+int qlora_linear_bwd_dropout(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes,
+                             const float* consts, int64_t T, const uint16_t* X, int32_t r, float alpha,
+                             const uint16_t* A, const uint16_t* B, const float* U_in, const uint16_t* dY,
+                             const uint8_t* keep, float p, uint16_t* dX, float* dA, float* dB, int32_t accumulate,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * AdamW update of the adapter parameters ("QLoRA技术从入门到精通" §3(3):
  * after the backward pass the optimizer updates only A and B, never the
  * quantized base weight).  The arithmetic is the published AdamW method

@@ -41,6 +41,9 @@ EXPORTED = (
     "qlora_bwd_workspace_bytes",
     "qlora_linear_bwd",
     "qlora_linear_bwd_accumulate",
+    "qlora_dropout_workspace_bytes",
+    "qlora_linear_fwd_dropout",
+    "qlora_linear_bwd_dropout",
     "qlora_dequantize_nf4",
     "qlora_merge_lora",
     "qlora_adamw_step",
@@ -103,6 +106,10 @@ def lib() -> ctypes.CDLL:
     L.qlora_linear_fwd.argtypes = [dp, vp, vp, vp, i64, vp, i32, f32, vp, vp, vp, vp, vp, sz, vp]
     L.qlora_linear_bwd.argtypes = [dp, vp, vp, vp, i64, vp, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.qlora_linear_bwd_accumulate.argtypes = L.qlora_linear_bwd.argtypes
+    L.qlora_dropout_workspace_bytes.argtypes = [dp, i64, i32, i32, ctypes.POINTER(sz)]
+    L.qlora_linear_fwd_dropout.argtypes = [dp, vp, vp, vp, i64, vp, i32, f32, vp, vp, vp, f32, vp, vp, vp, sz, vp]
+    L.qlora_linear_bwd_dropout.argtypes = [dp, vp, vp, vp, i64, vp, i32, f32, vp, vp, vp, vp, vp, f32, vp, vp, vp,
+                                           i32, vp, sz, vp]
     L.qlora_dequantize_nf4.argtypes = [dp, vp, vp, vp, vp, vp]
     L.qlora_merge_lora.argtypes = [dp, vp, vp, vp, i32, f32, vp, vp, vp, vp]
     L.qlora_adamw_step.argtypes = [ctypes.POINTER(AdamwHparams), i64, vp, vp, vp, vp, vp, vp]
@@ -270,11 +277,14 @@ def qlora_quantize_nf4(W, packed=None, codes=None, consts=None, stream=None, tab
 
 
 def qlora_linear_fwd(packed, codes, consts, X, A, B, alpha: float, Y=None, U_out=None,
-                     want_u: bool = True, workspace=None, stream=None, table: int = TABLE_NF4):
+                     want_u: bool = True, workspace=None, stream=None, table: int = TABLE_NF4,
+                     keep=None, p: float = 0.0):
     """Forward: returns (Y bf16 [T][d_out], U fp32 [T][r] or None).
 
     ``packed`` [d_out][d_in/2] fixes the layer shape; X bf16 [T][d_in],
     A bf16 [r][d_in], B bf16 [d_out][r] (A, B may be None for r = 0).
+    keep (uint8 [T][d_in/8] keep bits) applies LoRA dropout with rate p to
+    the adapter's input (qlora_linear_fwd_dropout).
     """
     import torch
     d_out, d_in = packed.shape[0], packed.shape[1] * 2
@@ -288,22 +298,46 @@ def qlora_linear_fwd(packed, codes, consts, X, A, B, alpha: float, Y=None, U_out
         Y = torch.empty((T, d_out), dtype=torch.bfloat16, device=X.device)
     if U_out is None and want_u and r > 0:
         U_out = torch.empty((T, r), dtype=torch.float32, device=X.device)
+    d = _stored_desc(packed, codes, consts, table)
+    if keep is not None:
+        _check_keep(keep, T, d_in)
+        nbytes = _dropout_ws(d, T, r, 0)
+        ws = _workspace(nbytes, X.device, workspace)
+        _check(lib().qlora_linear_fwd_dropout(ctypes.byref(d), _ptr(packed), _ptr(codes), _ptr(consts), T, _ptr(X),
+                                              r, float(alpha), _ptr(A), _ptr(B), _ptr(keep), float(p), _ptr(Y),
+                                              _ptr(U_out), _ptr(ws), nbytes, _stream(stream)),
+               "qlora_linear_fwd_dropout")
+        return Y, U_out
     nbytes = qlora_fwd_workspace_bytes(d_out, d_in, T, r)
     ws = _workspace(nbytes, X.device, workspace)
-    d = _stored_desc(packed, codes, consts, table)
     _check(lib().qlora_linear_fwd(ctypes.byref(d), _ptr(packed), _ptr(codes), _ptr(consts), T, _ptr(X), r,
                                   float(alpha), _ptr(A), _ptr(B), _ptr(Y), _ptr(U_out), _ptr(ws), nbytes,
                                   _stream(stream)), "qlora_linear_fwd")
     return Y, U_out
 
 
+def _check_keep(keep, T: int, d_in: int):
+    import torch
+    if keep.dtype != torch.uint8 or tuple(keep.shape) != (T, d_in // 8) or not keep.is_contiguous():
+        raise ValueError(f"keep must be a contiguous uint8 tensor of shape {(T, d_in // 8)}")
+    _need_cuda(keep, name="keep")
+
+
+def _dropout_ws(d, T: int, r: int, backward: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().qlora_dropout_workspace_bytes(ctypes.byref(d), int(T), int(r), int(backward), ctypes.byref(n)),
+           "qlora_dropout_workspace_bytes")
+    return n.value
+
+
 def qlora_linear_bwd(packed, codes, consts, X, A, B, alpha: float, dY, U_in=None, dX=None, dA=None, dB=None,
                      want_dx: bool = True, workspace=None, stream=None, table: int = TABLE_NF4,
-                     accumulate: bool = False):
+                     accumulate: bool = False, keep=None, p: float = 0.0):
     """Backward: returns (dX bf16 [T][d_in] or None, dA fp32 [r][d_in], dB fp32 [d_out][r]).
 
     accumulate=True adds the adapter gradients to the given dA and dB
-    (qlora_linear_bwd_accumulate) instead of overwriting them."""
+    (qlora_linear_bwd_accumulate) instead of overwriting them; keep / p as in
+    qlora_linear_fwd (qlora_linear_bwd_dropout; pass the forward's U)."""
     import torch
     d_out, d_in = packed.shape[0], packed.shape[1] * 2
     T = X.shape[0]
@@ -324,9 +358,18 @@ def qlora_linear_bwd(packed, codes, consts, X, A, B, alpha: float, dY, U_in=None
         for t, nm, shape in ((dA, "dA", (r, d_in)), (dB, "dB", (d_out, r))):
             if t.dtype != torch.float32 or tuple(t.shape) != shape or not t.is_contiguous():
                 raise ValueError(f"{nm} must be a contiguous float32 tensor of shape {shape}")
+    d = _stored_desc(packed, codes, consts, table)
+    if keep is not None:
+        _check_keep(keep, T, d_in)
+        nbytes = _dropout_ws(d, T, r, 1)
+        ws = _workspace(nbytes, X.device, workspace)
+        _check(lib().qlora_linear_bwd_dropout(ctypes.byref(d), _ptr(packed), _ptr(codes), _ptr(consts), T, _ptr(X),
+                                              r, float(alpha), _ptr(A), _ptr(B), _ptr(U_in), _ptr(dY), _ptr(keep),
+                                              float(p), _ptr(dX), _ptr(dA), _ptr(dB), 1 if accumulate else 0,
+                                              _ptr(ws), nbytes, _stream(stream)), "qlora_linear_bwd_dropout")
+        return dX, dA, dB
     nbytes = qlora_bwd_workspace_bytes(d_out, d_in, T, r)
     ws = _workspace(nbytes, X.device, workspace)
-    d = _stored_desc(packed, codes, consts, table)
     name = "qlora_linear_bwd_accumulate" if accumulate else "qlora_linear_bwd"
     _check(getattr(lib(), name)(ctypes.byref(d), _ptr(packed), _ptr(codes), _ptr(consts), T, _ptr(X), r,
                                 float(alpha), _ptr(A), _ptr(B), _ptr(U_in), _ptr(dY), _ptr(dX), _ptr(dA),

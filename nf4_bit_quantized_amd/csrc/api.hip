@@ -10,6 +10,7 @@
 #include <cmath>
 
 #include "adamw.hpp"
+#include "dropout.hpp"
 #include "skinny.hpp"
 #include "trace.hpp"
 #include "../../include/qlora.h"
@@ -263,10 +264,11 @@ int qlora_bwd_workspace_bytes(const qlora_nf4_desc* d, int64_t T, int32_t r, siz
   return QLORA_OK;
 }
 
-int qlora_linear_fwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes,
-                     const float* consts, int64_t T, const uint16_t* X, int32_t r, float alpha,
-                     const uint16_t* A, const uint16_t* B, uint16_t* Y, float* U_out,
-                     void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+// Xa: the adapter's input (X itself, or X with dropout applied)
+int linear_fwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes, const float* consts, int64_t T,
+               const uint16_t* X, const uint16_t* Xa, int32_t r, float alpha, const uint16_t* A, const uint16_t* B,
+               uint16_t* Y, float* U_out, void* workspace, size_t workspace_bytes, void* stream) {
   const int st = check_layer(d, T, r);
   if (st) return st;
   if (!packed || (!codes && d->dq_blocksize) || !consts) return QLORA_ERR_NULL;
@@ -284,7 +286,7 @@ int qlora_linear_fwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8
   float* U = U_out ? U_out : w.U;
 
   if (r > 0) {
-    const int e = lora_down(X, A, T, K, r, s, w.part, U, w.Us, s_);
+    const int e = lora_down(Xa, A, T, K, r, s, w.part, U, w.Us, s_);
     if (e) return e;
   }
   // the few-token kernel stages 8-bit codes; fp32 block scales take the tiled kernel
@@ -303,12 +305,22 @@ int qlora_linear_fwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8
   HIP_TRY(launch_fused(fp, false, s_, KID_FWD_GEMM));
   return QLORA_OK;
 }
+}  // namespace
+
+int qlora_linear_fwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes,
+                     const float* consts, int64_t T, const uint16_t* X, int32_t r, float alpha,
+                     const uint16_t* A, const uint16_t* B, uint16_t* Y, float* U_out,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  return linear_fwd(d, packed, codes, consts, T, X, X, r, alpha, A, B, Y, U_out, workspace, workspace_bytes, stream);
+}
 
 namespace {
+// Xa: the adapter's input (X, or X with dropout applied); keep (optional):
+// the dropout mask, whose factor c scales the adapter's share of dX
 int linear_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes, const float* consts, int64_t T,
-               const uint16_t* X, int32_t r, float alpha, const uint16_t* A, const uint16_t* B, const float* U_in,
-               const uint16_t* dY, uint16_t* dX, float* dA, float* dB, void* workspace, size_t workspace_bytes,
-               void* stream, int accumulate) {
+               const uint16_t* X, const uint16_t* Xa, const uint8_t* keep, float c, int32_t r, float alpha,
+               const uint16_t* A, const uint16_t* B, const float* U_in, const uint16_t* dY, uint16_t* dX, float* dA,
+               float* dB, void* workspace, size_t workspace_bytes, void* stream, int accumulate) {
   const int st = check_layer(d, T, r);
   if (st) return st;
   if (!packed || (!codes && d->dq_blocksize) || !consts) return QLORA_ERR_NULL;
@@ -335,7 +347,7 @@ int linear_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* co
   if (r > 0) {
     // U = X A^T when the forward's U is not given (its hi/lo pair feeds dB)
     if (!U_in) {
-      const int e = lora_down(X, A, T, K, r, s, w.part, w.U, w.Us, s_);
+      const int e = lora_down(Xa, A, T, K, r, s, w.part, w.U, w.Us, s_);
       if (e) return e;
     }
     // G = dY B -> hi/lo of s*G (feeds the dX tail and dA); the same launch
@@ -362,21 +374,27 @@ int linear_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* co
     fp.packed = packed; fp.codes = codes; fp.consts = consts; fp.Kw = K; fp.table = d->table; fp.bshift = block_shift(d);
     fp.dq = d->dq_blocksize != 0;
     fp.M = T; fp.N = K; fp.K0 = N;
-    fp.At = w.Gs; fp.ldat = ldh; fp.Bt = A; fp.ldbt = K; fp.r = r;
+    fp.At = w.Gs; fp.ldat = ldh; fp.Bt = A; fp.ldbt = K;
+    fp.r = keep ? 0 : r;  // with dropout the adapter's share is added after, through the mask
     fp.C = dX; fp.ldc = K;
     HIP_TRY(launch_fused(fp, true, s_, KID_DX_GEMM));
+    if (keep && r > 0) {
+      DropoutDxParams Dp{};
+      Dp.dX = dX; Dp.Gs = w.Gs; Dp.ldh = ldh; Dp.A = A; Dp.keep = keep; Dp.c = c; Dp.T = T; Dp.K = K; Dp.r = r;
+      HIP_TRY(launch_dropout_dx_add(Dp, s_));
+    }
   }
   if (r > 0) {
     // one launch for both adapter gradients, contractions over the hi/lo columns:
     // dA = (s G)^T X -> [r][d_in]; dB = dY^T (s U) -> [d_out][r]
     if (lora_stream_ok(r)) {
       ColsBatch C{};
-      C.p[0] = ColsParams{X, K, K, w.Gs, ldh, T, r, 1, dA, accumulate};
+      C.p[0] = ColsParams{Xa, K, K, w.Gs, ldh, T, r, 1, dA, accumulate};
       C.p[1] = ColsParams{dY, N, N, w.Us, ldh, T, r, 0, dB, accumulate};
       C.n = 2;
       HIP_TRY(launch_lora_cols(C, s_, KID_LORA_DA));
     } else {
-      SkinnyParams Sa = skinny(X, K, false, K, T, r, s, 2 * r, OUT_PAIRS_T, w.part);
+      SkinnyParams Sa = skinny(Xa, K, false, K, T, r, s, 2 * r, OUT_PAIRS_T, w.part);
       skinny_q(Sa, w.Gs, ldh, 2 * (int64_t)r, Q_STRIDED);
       Sa.Fout = dA;
       Sa.accumulate = accumulate;
@@ -396,7 +414,7 @@ int qlora_linear_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8
                      const uint16_t* A, const uint16_t* B, const float* U_in, const uint16_t* dY,
                      uint16_t* dX, float* dA, float* dB, void* workspace, size_t workspace_bytes,
                      void* stream) {
-  return linear_bwd(d, packed, codes, consts, T, X, r, alpha, A, B, U_in, dY, dX, dA, dB, workspace,
+  return linear_bwd(d, packed, codes, consts, T, X, X, nullptr, 1.0f, r, alpha, A, B, U_in, dY, dX, dA, dB, workspace,
                     workspace_bytes, stream, 0);
 }
 
@@ -405,8 +423,77 @@ int qlora_linear_bwd_accumulate(const qlora_nf4_desc* d, const uint8_t* packed, 
                                 const uint16_t* A, const uint16_t* B, const float* U_in, const uint16_t* dY,
                                 uint16_t* dX, float* dA, float* dB, void* workspace, size_t workspace_bytes,
                                 void* stream) {
-  return linear_bwd(d, packed, codes, consts, T, X, r, alpha, A, B, U_in, dY, dX, dA, dB, workspace,
+  return linear_bwd(d, packed, codes, consts, T, X, X, nullptr, 1.0f, r, alpha, A, B, U_in, dY, dX, dA, dB, workspace,
                     workspace_bytes, stream, 1);
+}
+
+namespace {
+// X with dropout applied, at the start of the workspace; the rest is the
+// plain call's workspace
+size_t dropout_xd_bytes(const qlora_nf4_desc* d, int64_t T) { return ((size_t)(T * d->d_in * 2) + 255) & ~(size_t)255; }
+
+int check_dropout(const qlora_nf4_desc* d, int64_t T, int32_t r, const uint8_t* keep, float p) {
+  if (!(p >= 0.0f && p < 1.0f)) return QLORA_ERR_UNSUPPORTED;
+  if (T > 0 && r > 0 && !keep) return QLORA_ERR_NULL;
+  return QLORA_OK;
+}
+
+float dropout_factor(float p) { return 1.0f / (1.0f - p); }
+}  // namespace
+
+int qlora_dropout_workspace_bytes(const qlora_nf4_desc* d, int64_t T, int32_t r, int32_t backward, size_t* bytes) {
+  if (!bytes) return QLORA_ERR_NULL;
+  const int st = check_layer(d, T, r);
+  if (st) return st;
+  *bytes = dropout_xd_bytes(d, T) + (backward ? plan_bwd(d, T, r, nullptr).bytes : plan_fwd(d, T, r, nullptr).bytes);
+  return QLORA_OK;
+}
+
+int qlora_linear_fwd_dropout(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes,
+                             const float* consts, int64_t T, const uint16_t* X, int32_t r, float alpha,
+                             const uint16_t* A, const uint16_t* B, const uint8_t* keep, float p, uint16_t* Y,
+                             float* U_out, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_layer(d, T, r);
+  if (st) return st;
+  if ((st = check_dropout(d, T, r, keep, p))) return st;
+  if (r == 0 || T == 0)
+    return linear_fwd(d, packed, codes, consts, T, X, X, r, alpha, A, B, Y, U_out, workspace, workspace_bytes,
+                      stream);
+  if (!X) return QLORA_ERR_NULL;
+  if (!aligned16(X)) return QLORA_ERR_UNSUPPORTED;
+  const size_t xd = dropout_xd_bytes(d, T);
+  if (!workspace || workspace_bytes < xd + plan_fwd(d, T, r, nullptr).bytes) return QLORA_ERR_WORKSPACE;
+  uint16_t* Xd = static_cast<uint16_t*>(workspace);
+  // validate everything else before the first launch
+  if (!packed || (!codes && d->dq_blocksize) || !consts || !Y || !A || !B) return QLORA_ERR_NULL;
+  if (!aligned16(packed) || !aligned16(A) || !aligned16(B)) return QLORA_ERR_UNSUPPORTED;
+  HIP_TRY(launch_dropout_input(X, keep, dropout_factor(p), T, d->d_in, Xd, (hipStream_t)stream));
+  return linear_fwd(d, packed, codes, consts, T, X, Xd, r, alpha, A, B, Y, U_out, static_cast<char*>(workspace) + xd,
+                    workspace_bytes - xd, stream);
+}
+
+int qlora_linear_bwd_dropout(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes,
+                             const float* consts, int64_t T, const uint16_t* X, int32_t r, float alpha,
+                             const uint16_t* A, const uint16_t* B, const float* U_in, const uint16_t* dY,
+                             const uint8_t* keep, float p, uint16_t* dX, float* dA, float* dB, int32_t accumulate,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_layer(d, T, r);
+  if (st) return st;
+  if ((st = check_dropout(d, T, r, keep, p))) return st;
+  if (r == 0 || T == 0)
+    return linear_bwd(d, packed, codes, consts, T, X, X, nullptr, 1.0f, r, alpha, A, B, U_in, dY, dX, dA, dB,
+                      workspace, workspace_bytes, stream, accumulate != 0);
+  if (!X || !dY || !A || !B || !dA || !dB || !packed || (!codes && d->dq_blocksize) || !consts)
+    return QLORA_ERR_NULL;
+  if (!aligned16(X) || !aligned16(dY) || !aligned16(A) || !aligned16(B) || !aligned16(packed))
+    return QLORA_ERR_UNSUPPORTED;
+  const size_t xd = dropout_xd_bytes(d, T);
+  if (!workspace || workspace_bytes < xd + plan_bwd(d, T, r, nullptr).bytes) return QLORA_ERR_WORKSPACE;
+  uint16_t* Xd = static_cast<uint16_t*>(workspace);
+  const float c = dropout_factor(p);
+  HIP_TRY(launch_dropout_input(X, keep, c, T, d->d_in, Xd, (hipStream_t)stream));
+  return linear_bwd(d, packed, codes, consts, T, X, Xd, keep, c, r, alpha, A, B, U_in, dY, dX, dA, dB,
+                    static_cast<char*>(workspace) + xd, workspace_bytes - xd, stream, accumulate != 0);
 }
 
 int qlora_adamw_step(const qlora_adamw_hparams* h, int64_t n, float* param, const float* grad, float* exp_avg,

@@ -19,6 +19,7 @@ enum KernelId : int {
   KID_FILL,
   KID_EXPORT,
   KID_ADAMW,
+  KID_DROPOUT,
   KID_COUNT
 };
 

@@ -205,6 +205,30 @@ def test_fp32_scale_format_sizes():
     assert _err(q.qlora_nf4_sizes, 64, 64, 64, 128) == q.QLORA_ERR_UNSUPPORTED
 
 
+def test_dropout_validation_happens_before_any_launch():
+    fake = 0x10000
+    d = q._desc(64, 64)
+    L = q.lib()
+    f = ctypes.c_float
+    big = 1 << 30
+    # p outside [0, 1)
+    for p in (-0.1, 1.0, float("nan")):
+        assert L.qlora_linear_fwd_dropout(ctypes.byref(d), fake, fake, fake, 4, fake, 8, f(16.0), fake, fake, fake,
+                                          f(p), fake, None, fake, big, None) == q.QLORA_ERR_UNSUPPORTED
+    # no mask
+    assert L.qlora_linear_fwd_dropout(ctypes.byref(d), fake, fake, fake, 4, fake, 8, f(16.0), fake, fake, None,
+                                      f(0.1), fake, None, fake, big, None) == q.QLORA_ERR_NULL
+    assert L.qlora_linear_bwd_dropout(ctypes.byref(d), fake, fake, fake, 4, fake, 8, f(16.0), fake, fake, None, fake,
+                                      None, f(0.1), fake, fake, fake, 0, fake, big, None) == q.QLORA_ERR_NULL
+    # workspace below the query
+    n = ctypes.c_size_t()
+    assert L.qlora_dropout_workspace_bytes(ctypes.byref(d), 4, 8, 1, ctypes.byref(n)) == q.QLORA_OK
+    assert n.value >= 4 * 64 * 2
+    assert L.qlora_linear_bwd_dropout(ctypes.byref(d), fake, fake, fake, 4, fake, 8, f(16.0), fake, fake, None, fake,
+                                      fake, f(0.1), fake, fake, fake, 0, fake, n.value - 1, None) == \
+        q.QLORA_ERR_WORKSPACE
+
+
 def test_workspace_sizes_grow_with_tokens_and_rank():
     a = q.qlora_bwd_workspace_bytes(4096, 4096, 2048, 16)
     b = q.qlora_bwd_workspace_bytes(4096, 4096, 4096, 64)
