@@ -92,8 +92,8 @@ hipError_t launch_adamw(const AdamwParams& P, hipStream_t stream) {
   const int64_t per = (int64_t)kThreads * kRuns;
   const int64_t blocks = n4 > 0 ? (n4 + per - 1) / per : 1;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  TraceScope ts(KID_ADAMW, stream);
-  hipLaunchKernelGGL(k_adamw, dim3((unsigned)blocks), dim3(kThreads), 0, stream, P);
+  KernelEvents ev(KID_ADAMW);
+  hipExtLaunchKernelGGL(k_adamw, dim3((unsigned)blocks), dim3(kThreads), 0, stream, ev.start(), ev.stop(), 0, P);
   return hipGetLastError();
 }
 

@@ -377,16 +377,18 @@ __global__ __launch_bounds__(DW * 64) void k_decode(DecodeParams P) {
 template <int NTW>
 void launch_ntw(const DecodeParams& P, bool c2, unsigned grid, hipStream_t stream) {
   const dim3 g(grid);
+  KernelEvents ev(KID_DECODE);
+  const hipEvent_t e0 = ev.start(), e1 = ev.stop();
   if (c2 && P.T <= 4) {
-    if constexpr (NTW <= 7) hipLaunchKernelGGL((k_decode<16, NTW, 1, true>), g, dim3(1024), 0, stream, P);
-    else hipLaunchKernelGGL((k_decode<8, NTW, 1, true>), g, dim3(512), 0, stream, P);
+    if constexpr (NTW <= 7) hipExtLaunchKernelGGL((k_decode<16, NTW, 1, true>), g, dim3(1024), 0, stream, e0, e1, 0, P);
+    else hipExtLaunchKernelGGL((k_decode<8, NTW, 1, true>), g, dim3(512), 0, stream, e0, e1, 0, P);
   } else if (c2) {
-    if constexpr (NTW <= 6) hipLaunchKernelGGL((k_decode<16, NTW, 4, true>), g, dim3(1024), 0, stream, P);
-    else hipLaunchKernelGGL((k_decode<8, NTW, 4, true>), g, dim3(512), 0, stream, P);
+    if constexpr (NTW <= 6) hipExtLaunchKernelGGL((k_decode<16, NTW, 4, true>), g, dim3(1024), 0, stream, e0, e1, 0, P);
+    else hipExtLaunchKernelGGL((k_decode<8, NTW, 4, true>), g, dim3(512), 0, stream, e0, e1, 0, P);
   } else if (P.T <= 4) {
-    hipLaunchKernelGGL((k_decode<8, NTW, 1, false>), g, dim3(512), 0, stream, P);
+    hipExtLaunchKernelGGL((k_decode<8, NTW, 1, false>), g, dim3(512), 0, stream, e0, e1, 0, P);
   } else {
-    hipLaunchKernelGGL((k_decode<8, NTW, 4, false>), g, dim3(512), 0, stream, P);
+    hipExtLaunchKernelGGL((k_decode<8, NTW, 4, false>), g, dim3(512), 0, stream, e0, e1, 0, P);
   }
 }
 
@@ -427,7 +429,6 @@ hipError_t launch_decode(const uint8_t* packed, const uint8_t* codes, const floa
   if (aux_need(ntw) > CODES_BYTES) return hipErrorInvalidValue;
   const unsigned grid = (unsigned)((ntiles + ntw - 1) / ntw);
   const bool c2 = bshift == 0 && (K / 64) % 2 == 0;
-  TraceScope ts(KID_DECODE, stream);
   switch (ntw) {
     case 1: launch_ntw<1>(P, c2, grid, stream); break;
     case 2: launch_ntw<2>(P, c2, grid, stream); break;

@@ -118,8 +118,9 @@ hipError_t launch_dropout_input(const uint16_t* X, const uint8_t* keep, float c,
   if (K % 8 != 0) return hipErrorInvalidValue;
   const int64_t n8 = T * K / 8;
   if (n8 == 0) return hipSuccess;
-  TraceScope ts(KID_DROPOUT, stream);
-  hipLaunchKernelGGL(k_dropout_input, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream, X, keep, c, n8, Xd);
+  KernelEvents ev(KID_DROPOUT);
+  hipExtLaunchKernelGGL(k_dropout_input, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream, ev.start(),
+                        ev.stop(), 0, X, keep, c, n8, Xd);
   return hipGetLastError();
 }
 
@@ -127,8 +128,9 @@ hipError_t launch_dropout_dx_add(const DropoutDxParams& P, hipStream_t stream) {
   if (P.K % DCOL != 0 || P.r < 1 || P.r > 128) return hipErrorInvalidValue;
   if (P.T == 0) return hipSuccess;
   const dim3 grid((unsigned)((P.K + 256 * DCOL - 1) / (256 * DCOL)), (unsigned)((P.T + DT - 1) / DT));
-  TraceScope ts(KID_DROPOUT, stream);
-  hipLaunchKernelGGL(k_dropout_dx_add, grid, dim3(256), (size_t)P.r * DT * 4, stream, P);
+  KernelEvents ev(KID_DROPOUT);
+  hipExtLaunchKernelGGL(k_dropout_dx_add, grid, dim3(256), (uint32_t)(P.r * DT * 4), stream, ev.start(), ev.stop(), 0,
+                        P);
   return hipGetLastError();
 }
 

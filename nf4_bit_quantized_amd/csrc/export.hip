@@ -195,14 +195,14 @@ hipError_t launch_export(const uint8_t* packed, const uint8_t* codes, const floa
   P.bshift = bshift;
   P.dq = dq;
   const dim3 grid((unsigned)((K + TC - 1) / TC), (unsigned)(N / TR));
-  TraceScope ts(KID_EXPORT, stream);
+  KernelEvents ev(KID_EXPORT);
   if (r > 0) {
     const size_t lds = (size_t)TR * LDD * 4 + (size_t)((r + 31) & ~31) * LDA * 2;
-    hipLaunchKernelGGL(k_export<true>, grid, dim3(256), lds, stream, P);
+    hipExtLaunchKernelGGL(k_export<true>, grid, dim3(256), (uint32_t)lds, stream, ev.start(), ev.stop(), 0, P);
   } else {
     const int64_t npairs = N * K / 16;
     const unsigned g = (unsigned)((npairs + 256 * DQ_PER - 1) / (256 * DQ_PER));
-    hipLaunchKernelGGL(k_dequant, dim3(g), dim3(256), 0, stream, P);
+    hipExtLaunchKernelGGL(k_dequant, dim3(g), dim3(256), 0, stream, ev.start(), ev.stop(), 0, P);
   }
   return hipGetLastError();
 }

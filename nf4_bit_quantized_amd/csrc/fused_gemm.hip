@@ -549,9 +549,9 @@ hipError_t launch_fused(FusedParams P, bool dx, hipStream_t stream, int kernel_i
   P.tab = level_table(P.table);
   const int64_t ntiles = (int64_t)P.mt * P.nt;
   const unsigned grid = (unsigned)(((ntiles + 7) / 8) * 8);
-  TraceScope ts(kernel_id, stream);
-  if (!dx) hipLaunchKernelGGL(k_qlora_fwd_gemm, dim3(grid), dim3(512), 0, stream, P);
-  else hipLaunchKernelGGL(k_qlora_dx_gemm, dim3(grid), dim3(512), 0, stream, P);
+  KernelEvents ev(kernel_id);
+  if (!dx) hipExtLaunchKernelGGL(k_qlora_fwd_gemm, dim3(grid), dim3(512), 0, stream, ev.start(), ev.stop(), 0, P);
+  else hipExtLaunchKernelGGL(k_qlora_dx_gemm, dim3(grid), dim3(512), 0, stream, ev.start(), ev.stop(), 0, P);
   return hipGetLastError();
 }
 

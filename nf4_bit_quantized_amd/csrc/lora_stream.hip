@@ -317,12 +317,13 @@ __global__ __launch_bounds__(256) void k_lora_cols(ColsBatch B) {
 }
 
 template <bool QS, int RT>
-void rows_by_jt(const RowsParams& p, int jt, dim3 grid, hipStream_t st) {
+void rows_by_jt(const RowsParams& p, int jt, dim3 grid, hipStream_t st, const KernelEvents& ev) {
+  const hipEvent_t e0 = ev.start(), e1 = ev.stop();
   switch (jt) {
-    case 1: hipLaunchKernelGGL((k_lora_rows<1, QS, RT>), grid, dim3(256), 0, st, p); break;
-    case 2: hipLaunchKernelGGL((k_lora_rows<2, QS, RT>), grid, dim3(256), 0, st, p); break;
-    case 3: hipLaunchKernelGGL((k_lora_rows<3, QS, RT>), grid, dim3(256), 0, st, p); break;
-    default: hipLaunchKernelGGL((k_lora_rows<4, QS, RT>), grid, dim3(256), 0, st, p); break;
+    case 1: hipExtLaunchKernelGGL((k_lora_rows<1, QS, RT>), grid, dim3(256), 0, st, e0, e1, 0, p); break;
+    case 2: hipExtLaunchKernelGGL((k_lora_rows<2, QS, RT>), grid, dim3(256), 0, st, e0, e1, 0, p); break;
+    case 3: hipExtLaunchKernelGGL((k_lora_rows<3, QS, RT>), grid, dim3(256), 0, st, e0, e1, 0, p); break;
+    default: hipExtLaunchKernelGGL((k_lora_rows<4, QS, RT>), grid, dim3(256), 0, st, e0, e1, 0, p); break;
   }
 }
 
@@ -342,13 +343,13 @@ hipError_t launch_lora_rows(const RowsParams& p, hipStream_t stream, int kernel_
   const int rt = lora_rows_rt(p.r);
   const int jt = (p.r + 15) / 16;
   const dim3 grid((unsigned)((p.M + rt - 1) / rt));
-  TraceScope ts(kernel_id, stream);
+  KernelEvents ev(kernel_id);
   if (p.q_strided) {
-    if (rt == 8) rows_by_jt<true, 8>(p, jt, grid, stream);
-    else rows_by_jt<true, 16>(p, jt, grid, stream);
+    if (rt == 8) rows_by_jt<true, 8>(p, jt, grid, stream, ev);
+    else rows_by_jt<true, 16>(p, jt, grid, stream, ev);
   } else {
-    if (rt == 8) rows_by_jt<false, 8>(p, jt, grid, stream);
-    else rows_by_jt<false, 16>(p, jt, grid, stream);
+    if (rt == 8) rows_by_jt<false, 8>(p, jt, grid, stream, ev);
+    else rows_by_jt<false, 16>(p, jt, grid, stream, ev);
   }
   return hipGetLastError();
 }
@@ -362,16 +363,17 @@ hipError_t launch_lora_cols(const ColsBatch& B, hipStream_t stream, int kernel_i
     slabs = std::max<int64_t>(slabs, p.D / 32);
   }
   const dim3 grid((unsigned)((slabs + 15) / 16 * 16), (unsigned)B.n);
-  TraceScope ts(kernel_id, stream);
+  KernelEvents ev(kernel_id);
+  const hipEvent_t e0 = ev.start(), e1 = ev.stop();
   switch (B.p[0].r / 8) {
-    case 1: hipLaunchKernelGGL(k_lora_cols<1>, grid, dim3(256), 0, stream, B); break;
-    case 2: hipLaunchKernelGGL(k_lora_cols<2>, grid, dim3(256), 0, stream, B); break;
-    case 3: hipLaunchKernelGGL(k_lora_cols<3>, grid, dim3(256), 0, stream, B); break;
-    case 4: hipLaunchKernelGGL(k_lora_cols<4>, grid, dim3(256), 0, stream, B); break;
-    case 5: hipLaunchKernelGGL(k_lora_cols<5>, grid, dim3(256), 0, stream, B); break;
-    case 6: hipLaunchKernelGGL(k_lora_cols<6>, grid, dim3(256), 0, stream, B); break;
-    case 7: hipLaunchKernelGGL(k_lora_cols<7>, grid, dim3(256), 0, stream, B); break;
-    default: hipLaunchKernelGGL(k_lora_cols<8>, grid, dim3(256), 0, stream, B); break;
+    case 1: hipExtLaunchKernelGGL(k_lora_cols<1>, grid, dim3(256), 0, stream, e0, e1, 0, B); break;
+    case 2: hipExtLaunchKernelGGL(k_lora_cols<2>, grid, dim3(256), 0, stream, e0, e1, 0, B); break;
+    case 3: hipExtLaunchKernelGGL(k_lora_cols<3>, grid, dim3(256), 0, stream, e0, e1, 0, B); break;
+    case 4: hipExtLaunchKernelGGL(k_lora_cols<4>, grid, dim3(256), 0, stream, e0, e1, 0, B); break;
+    case 5: hipExtLaunchKernelGGL(k_lora_cols<5>, grid, dim3(256), 0, stream, e0, e1, 0, B); break;
+    case 6: hipExtLaunchKernelGGL(k_lora_cols<6>, grid, dim3(256), 0, stream, e0, e1, 0, B); break;
+    case 7: hipExtLaunchKernelGGL(k_lora_cols<7>, grid, dim3(256), 0, stream, e0, e1, 0, B); break;
+    default: hipExtLaunchKernelGGL(k_lora_cols<8>, grid, dim3(256), 0, stream, e0, e1, 0, B); break;
   }
   return hipGetLastError();
 }

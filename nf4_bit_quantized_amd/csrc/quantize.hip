@@ -198,10 +198,11 @@ hipError_t launch_nf4_quantize(const void* W, int wformat, uint8_t* packed, uint
     return hipErrorInvalidValue;
   const int64_t nb = numel / blocksize;
   const int64_t ng = (nb + 255) / 256;
-  TraceScope ts(KID_QUANTIZE, stream);
+  KernelEvents ev(KID_QUANTIZE);
   const dim3 grid((unsigned)ng), block(256);
-#define QLORA_QUANT_LAUNCH(WFV, BSV) \
-  hipLaunchKernelGGL((k_nf4_quantize<WFV, BSV>), grid, block, 0, stream, W, packed, codes, consts, nb, lut, dq)
+#define QLORA_QUANT_LAUNCH(WFV, BSV)                                                                            \
+  hipExtLaunchKernelGGL((k_nf4_quantize<WFV, BSV>), grid, block, 0, stream, ev.start(), ev.stop(), 0, W, packed, \
+                        codes, consts, nb, lut, dq)
 #define QLORA_QUANT_BS(WFV)                \
   if (blocksize == 64) QLORA_QUANT_LAUNCH(WFV, 64);   \
   else if (blocksize == 128) QLORA_QUANT_LAUNCH(WFV, 128); \

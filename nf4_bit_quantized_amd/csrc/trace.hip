@@ -31,7 +31,9 @@ hipEvent_t take_event() {
     return e;
   }
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  // timing only: no system-scope fence (cache writeback and invalidation)
+  // when the event is recorded, which would lengthen the bracketed interval
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
   return e;
 }
 
@@ -50,6 +52,24 @@ TraceScope::~TraceScope() {
   if (!active_) return;
   std::lock_guard<std::mutex> lk(g_mu);
   if (hipEventRecord(stop_, stream_) == hipSuccess) g_pending.push_back({kid_, start_, stop_});
+}
+
+KernelEvents::KernelEvents(int kid) : kid_(kid) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (!((g_mask >> kid) & 1u)) return;
+  start_ = take_event();
+  stop_ = take_event();
+  if (!start_ || !stop_) {
+    if (start_) g_pool.push_back(start_);
+    if (stop_) g_pool.push_back(stop_);
+    start_ = stop_ = nullptr;
+  }
+}
+
+KernelEvents::~KernelEvents() {
+  if (!start_) return;
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_pending.push_back({kid_, start_, stop_});
 }
 
 }  // namespace qlora

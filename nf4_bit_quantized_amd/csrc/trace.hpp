@@ -2,6 +2,7 @@
 // bracketed by two hipEvents recorded on the launch stream.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 namespace qlora {
@@ -35,6 +36,26 @@ class TraceScope {
   hipStream_t stream_;
   hipEvent_t start_ = nullptr, stop_ = nullptr;
   bool active_ = false;
+};
+
+// Timing events attached to one kernel's own dispatch: when kernel kid is
+// traced, start() and stop() are events for hipExtLaunchKernelGGL, which
+// records them at the kernel's begin and end (no separate marker packets
+// around it, whose processing would add to the interval); otherwise both are
+// null and the launch is untimed.  The pair is queued for qlora_trace_read
+// when the object goes out of scope, after the launch.
+class KernelEvents {
+ public:
+  explicit KernelEvents(int kid);
+  ~KernelEvents();
+  KernelEvents(const KernelEvents&) = delete;
+  KernelEvents& operator=(const KernelEvents&) = delete;
+  hipEvent_t start() const { return start_; }
+  hipEvent_t stop() const { return stop_; }
+
+ private:
+  int kid_;
+  hipEvent_t start_ = nullptr, stop_ = nullptr;
 };
 
 }  // namespace qlora
