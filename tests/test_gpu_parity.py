@@ -150,6 +150,11 @@ CASES = [
     (16448, 256, 3, 8, 16.0, 16),     # 5 tiles, the last workgroup 3
     (20608, 256, 6, 16, 16.0, 18),    # 6 tiles, the last workgroup 4
     (28736, 128, 16, 64, 16.0, 17),   # 8 tiles, the last workgroup 4
+    # one token, more shapes
+    (192, 320, 1, 3, 5.0, 20),        # K/64 odd, odd rank
+    (320, 4160, 1, 128, 16.0, 21),    # long contraction, largest rank
+    (256, 256, 1, 0, 0.0, 22),        # base branch only
+    (70016, 512, 1, 16, 16.0, 23),    # 4376 row tiles: eight per workgroup, the last one short
 ]
 
 
