@@ -307,6 +307,67 @@ def dropout_section(lin, steps):
     return out
 
 
+def mlp_section(steps):
+    """The MLP set of a 7B-class layer: gate and up 4096->11008, down
+    11008->4096, 4096 tokens, r = 64, alpha = 16.  Per step: quantize of the
+    three weights, then fwd + bwd of each linear (inputs resident)."""
+    import torch
+    import nf4_bit_quantized_amd as q
+    import workloads
+
+    lins = workloads.mlp_llama7b()
+    st = []
+    for lin in lins:
+        N, K, T, r = lin.d_out, lin.d_in, lin.T, lin.r
+        inp = workloads.layer_inputs(N, K, T, r, lin.seed)
+        W = torch.from_numpy(inp["W"]).cuda()
+        X, A, B, dY = (bf16_dev(inp[k]) for k in ("X", "A", "B", "dY"))
+        pk, cd, cs = q.qlora_quantize_nf4(W)
+        st.append(dict(lin=lin, W=W, X=X, A=A, B=B, dY=dY, pk=pk, cd=cd, cs=cs,
+                       Y=torch.empty((T, N), dtype=torch.bfloat16, device="cuda"),
+                       U=torch.empty((T, r), dtype=torch.float32, device="cuda"),
+                       dX=torch.empty((T, K), dtype=torch.bfloat16, device="cuda"),
+                       dA=torch.empty((r, K), dtype=torch.float32, device="cuda"),
+                       dB=torch.empty((N, r), dtype=torch.float32, device="cuda"),
+                       ws=torch.empty(max(q.qlora_bwd_workspace_bytes(N, K, T, r),
+                                          q.qlora_fwd_workspace_bytes(N, K, T, r), 1),
+                                      dtype=torch.uint8, device="cuda")))
+
+    def run(quant, fwdbwd):
+        for e in st:
+            l = e["lin"]
+            if quant:
+                q.qlora_quantize_nf4(e["W"], e["pk"], e["cd"], e["cs"])
+            if fwdbwd:
+                q.qlora_linear_fwd(e["pk"], e["cd"], e["cs"], e["X"], e["A"], e["B"], l.alpha, Y=e["Y"], U_out=e["U"],
+                                   workspace=e["ws"])
+                q.qlora_linear_bwd(e["pk"], e["cd"], e["cs"], e["X"], e["A"], e["B"], l.alpha, e["dY"], U_in=e["U"],
+                                   dX=e["dX"], dA=e["dA"], dB=e["dB"], workspace=e["ws"])
+
+    out = {}
+    flops = sum(sum(layer_flops(e["lin"].T, e["lin"].d_in, e["lin"].d_out, e["lin"].r)) for e in st)
+    for name, quant, fb in (("fwd_bwd", False, True), ("quantize", True, False)):
+        for _ in range(2):
+            run(quant, fb)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            run(quant, fb)
+        e1.record()
+        torch.cuda.synchronize()
+        out[name + "_ms"] = round(e0.elapsed_time(e1) / steps, 4)
+    out["fwd_bwd_tflops"] = round(flops / (out["fwd_bwd_ms"] * 1e-3) / 1e12, 1)
+    out["fwd_bwd_frac_mfma"] = round(out["fwd_bwd_tflops"] / BF16_PEAK_TFLOPS, 4)
+    qbytes = sum(e["lin"].d_out * e["lin"].d_in * (4 + 0.5) + e["cd"].numel() + e["cs"].numel() * 4 for e in st)
+    out["quantize_GBps"] = round(qbytes / (out["quantize_ms"] * 1e-3) / 1e9, 1)
+    out["quantize_frac_hbm"] = round(out["quantize_GBps"] / HBM_PEAK_GBPS, 4)
+    out["config"] = "gate/up 4096->11008, down 11008->4096, 4096 tokens, r=64, alpha=16"
+    log("mlp", out)
+    del st
+    return out
+
+
 def adamw_section(steps):
     """The AdamW update over every adapter of the 65B-class stack (8 layers x
     q, k, v, o 8192x8192, gate/up 8192->22016, down 22016->8192, r = 64) laid
@@ -460,6 +521,7 @@ def main():
         result["quantize_16bit_weight"] = quantize16_section(lin, steps=max(20, args.steps))
         result["adamw_65b_adapters"] = adamw_section(steps=max(20, args.steps))
         result["lora_dropout_attn4096"] = dropout_section(lin, steps=max(20, args.steps))
+        result["mlp_llama7b"] = mlp_section(steps=10)
     if not args.no_cpu_baseline:
         log("timing the oracle on the host ...")
         result["cpu_baseline"] = cpu_baseline(inp, lin, args.cpu_seconds)
