@@ -368,6 +368,60 @@ def mlp_section(steps):
     return out
 
 
+def multi_proj_section(steps):
+    """Query, key and value projections of a 70B-class layer with grouped
+    queries (8192x8192, 1024x8192, 1024x8192; r = 64, alpha = 16) at 1 and 16
+    tokens: one forward call over the three weights against three separate
+    calls, with the weights rotated over 4 copies (173 MB of packed weight).  call_us includes the host's enqueue of each call;
+    kernel_us is the weight-streaming kernels alone."""
+    import torch
+    import nf4_bit_quantized_amd as q
+
+    K, r, alpha = 8192, 64, 16.0
+    g = torch.Generator(device="cuda").manual_seed(0)
+    sets = []
+    for _ in range(4):
+        layers = []
+        for N in (8192, 1024, 1024):
+            pk, cd, cs = q.qlora_quantize_nf4(torch.randn(N, K, device="cuda", generator=g) * 0.02)
+            A = (torch.randn(r, K, device="cuda", generator=g) / r).to(torch.bfloat16)
+            B = (torch.randn(N, r, device="cuda", generator=g) * 0.01).to(torch.bfloat16)
+            layers.append((pk, cd, cs, A, B))
+        sets.append(layers)
+    packed_bytes = sum(l[0].numel() + l[1].numel() + l[2].numel() * 4 for l in sets[0])
+    out = {"weights": "8192x8192 + 2 x 1024x8192", "packed_bytes": packed_bytes}
+    for T in (1, 16):
+        X = torch.randn(T, K, device="cuda", generator=g).to(torch.bfloat16)
+        calls = {"fused": lambda L: q.qlora_linear_fwd_multi(L, X, alpha),
+                 "separate": lambda L: [q.qlora_linear_fwd(*l[:3], X, l[3], l[4], alpha) for l in L]}
+        for name, fn in calls.items():
+            for i in range(8):
+                fn(sets[i % 4])
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(steps):
+                fn(sets[i % 4])
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / steps * 1e3
+            out[f"{name}_T{T}_call_us"] = round(us, 2)
+            # the weight-streaming kernels alone (one launch fused, three separate)
+            q.qlora_trace_read(reset=True)
+            q.qlora_trace_select({"decode"})
+            for i in range(steps):
+                fn(sets[i % 4])
+            torch.cuda.synchronize()
+            q.qlora_trace_enable(False)
+            n, ms = q.qlora_trace_read(reset=True).get("decode", (1, float("nan")))
+            kus = ms / steps * 1e3
+            out[f"{name}_T{T}_kernel_us"] = round(kus, 2)
+            out[f"{name}_T{T}_kernel_GBps"] = round(packed_bytes / (kus * 1e-6) / 1e9, 1)
+    log("multi_proj", out)
+    del sets
+    return out
+
+
 def adamw_section(steps):
     """The AdamW update over every adapter of the 65B-class stack (8 layers x
     q, k, v, o 8192x8192, gate/up 8192->22016, down 22016->8192, r = 64) laid
@@ -522,6 +576,7 @@ def main():
         result["adamw_65b_adapters"] = adamw_section(steps=max(20, args.steps))
         result["lora_dropout_attn4096"] = dropout_section(lin, steps=max(20, args.steps))
         result["mlp_llama7b"] = mlp_section(steps=10)
+        result["qkv_gqa_70b"] = multi_proj_section(steps=max(20, args.steps))
     if not args.no_cpu_baseline:
         log("timing the oracle on the host ...")
         result["cpu_baseline"] = cpu_baseline(inp, lin, args.cpu_seconds)

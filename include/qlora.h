@@ -269,6 +269,29 @@ int qlora_merge_lora(const qlora_nf4_desc* d, const uint8_t* packed, const uint8
  * Not thread-safe with respect to concurrent compute calls on other threads.
  */
 /*
+ * Forward of n (1..4) layers that share their input X -- the projections of
+ * one layer input, e.g. the query, key and value projections or the gate and
+ * up projections; "LoRA 与 QLoRA：..." §8 targets every linear module, so
+ * these arrive together.  Each layer i is the forward of qlora_linear_fwd
+ * with d[i], packed[i], codes[i], consts[i], A[i], B[i], Y[i] and U_out[i];
+ * all share X, T, r and alpha.  The layers must have the same d_in,
+ * blocksize and dq_blocksize (tables may differ).  With at most 16 tokens the
+ * rows of every weight are streamed in ONE launch (one workgroup per group of
+ * row tiles, whichever weight they belong to), so small projections do not
+ * leave the GPU idle and X is read from HBM once; otherwise the layers run
+ * one after another.  The pointer arrays are host memory holding device
+ * pointers; U_out may be NULL, or hold NULL entries.  Workspace:
+ * qlora_multi_fwd_workspace_bytes.  Errors: as qlora_linear_fwd, and SHAPE
+ * (n outside 1..4, different d_in), UNSUPPORTED (different block format).
+ */
+int qlora_multi_fwd_workspace_bytes(int32_t n, const qlora_nf4_desc* d, int64_t T, int32_t r, size_t* bytes);
+int qlora_linear_fwd_multi(int32_t n, const qlora_nf4_desc* d, const uint8_t* const* packed,
+                           const uint8_t* const* codes, const float* const* consts, int64_t T, const uint16_t* X,
+                           int32_t r, float alpha, const uint16_t* const* A, const uint16_t* const* B,
+                           uint16_t* const* Y, float* const* U_out, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
  * LoRA dropout on the adapter's input ("LoRA 与 QLoRA：..." §4.3; its §8
  * configuration uses lora_dropout 0.05).  The base branch takes X unchanged;
  * the adapter takes X_d = bf16_rne(fl32(x * c)) where kept and 0 where

@@ -44,6 +44,8 @@ EXPORTED = (
     "qlora_dropout_workspace_bytes",
     "qlora_linear_fwd_dropout",
     "qlora_linear_bwd_dropout",
+    "qlora_multi_fwd_workspace_bytes",
+    "qlora_linear_fwd_multi",
     "qlora_dequantize_nf4",
     "qlora_merge_lora",
     "qlora_adamw_step",
@@ -107,6 +109,8 @@ def lib() -> ctypes.CDLL:
     L.qlora_linear_bwd.argtypes = [dp, vp, vp, vp, i64, vp, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.qlora_linear_bwd_accumulate.argtypes = L.qlora_linear_bwd.argtypes
     L.qlora_dropout_workspace_bytes.argtypes = [dp, i64, i32, i32, ctypes.POINTER(sz)]
+    L.qlora_multi_fwd_workspace_bytes.argtypes = [i32, dp, i64, i32, ctypes.POINTER(sz)]
+    L.qlora_linear_fwd_multi.argtypes = [i32, dp, vp, vp, vp, i64, vp, i32, f32, vp, vp, vp, vp, vp, sz, vp]
     L.qlora_linear_fwd_dropout.argtypes = [dp, vp, vp, vp, i64, vp, i32, f32, vp, vp, vp, f32, vp, vp, vp, sz, vp]
     L.qlora_linear_bwd_dropout.argtypes = [dp, vp, vp, vp, i64, vp, i32, f32, vp, vp, vp, vp, vp, f32, vp, vp, vp,
                                            i32, vp, sz, vp]
@@ -328,6 +332,40 @@ def _dropout_ws(d, T: int, r: int, backward: int) -> int:
     _check(lib().qlora_dropout_workspace_bytes(ctypes.byref(d), int(T), int(r), int(backward), ctypes.byref(n)),
            "qlora_dropout_workspace_bytes")
     return n.value
+
+
+def qlora_linear_fwd_multi(layers, X, alpha: float, want_u: bool = True, workspace=None, stream=None,
+                           tables=None):
+    """Forward of up to four layers sharing X: ``layers`` is a list of
+    (packed, codes, consts, A, B) (A, B None for r = 0, the same r for all).
+    Returns a list of (Y, U) as qlora_linear_fwd does for each layer."""
+    import torch
+    n = len(layers)
+    if not 1 <= n <= 4:
+        raise ValueError("one to four layers")
+    T = X.shape[0]
+    r = 0 if layers[0][3] is None else layers[0][3].shape[0]
+    tables = tables or [TABLE_NF4] * n
+    descs = (Nf4Desc * n)()
+    outs = []
+    for i, (packed, codes, consts, A, B) in enumerate(layers):
+        _need_cuda(packed, codes, consts, A, B, name="qlora_linear_fwd_multi")
+        descs[i] = _stored_desc(packed, codes, consts, tables[i])
+        Y = torch.empty((T, packed.shape[0]), dtype=torch.bfloat16, device=X.device)
+        U = torch.empty((T, r), dtype=torch.float32, device=X.device) if want_u and r > 0 else None
+        outs.append((Y, U))
+    _need_cuda(X, name="qlora_linear_fwd_multi")
+    n_b = ctypes.c_size_t()
+    _check(lib().qlora_multi_fwd_workspace_bytes(n, descs, int(T), int(r), ctypes.byref(n_b)),
+           "qlora_multi_fwd_workspace_bytes")
+    ws = _workspace(n_b.value, X.device, workspace)
+    arr = lambda vals: (ctypes.c_void_p * n)(*vals)
+    _check(lib().qlora_linear_fwd_multi(
+        n, descs, arr([_ptr(l[0]) for l in layers]), arr([_ptr(l[1]) for l in layers]),
+        arr([_ptr(l[2]) for l in layers]), int(T), _ptr(X), int(r), float(alpha),
+        arr([_ptr(l[3]) for l in layers]), arr([_ptr(l[4]) for l in layers]), arr([_ptr(o[0]) for o in outs]),
+        arr([_ptr(o[1]) for o in outs]), _ptr(ws), n_b.value, _stream(stream)), "qlora_linear_fwd_multi")
+    return outs
 
 
 def qlora_linear_bwd(packed, codes, consts, X, A, B, alpha: float, dY, U_in=None, dX=None, dA=None, dB=None,

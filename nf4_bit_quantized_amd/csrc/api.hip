@@ -10,6 +10,7 @@
 #include <cmath>
 
 #include "adamw.hpp"
+#include "decode.hpp"
 #include "dropout.hpp"
 #include "skinny.hpp"
 #include "trace.hpp"
@@ -18,10 +19,6 @@
 namespace qlora {
 hipError_t launch_nf4_quantize(const void* W, int wformat, uint8_t* packed, uint8_t* codes, float* consts,
                                int64_t numel, int blocksize, int dq, int table, hipStream_t stream);
-bool decode_supported(int64_t N, int64_t K, int bshift);
-hipError_t launch_decode(const uint8_t* packed, const uint8_t* codes, const float* consts, const uint16_t* X,
-                         int64_t T, int64_t N, int64_t K, const uint16_t* Us, int64_t ldh, const uint16_t* B,
-                         int r, uint16_t* Y, int table, int bshift, hipStream_t stream);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
 hipError_t launch_export(const uint8_t* packed, const uint8_t* codes, const float* consts, int64_t N, int64_t K,
                          int r, float s, const uint16_t* A, const uint16_t* B, uint16_t* W, int table,
@@ -425,6 +422,93 @@ int qlora_linear_bwd_accumulate(const qlora_nf4_desc* d, const uint8_t* packed, 
                                 void* stream) {
   return linear_bwd(d, packed, codes, consts, T, X, X, nullptr, 1.0f, r, alpha, A, B, U_in, dY, dX, dA, dB, workspace,
                     workspace_bytes, stream, 1);
+}
+
+namespace {
+// Several weights that share X: validation, and each weight's workspace slice
+// (its plan_fwd bytes, rounded up to 256).
+int check_multi(int32_t n, const qlora_nf4_desc* d, int64_t T, int32_t r) {
+  if (!d) return QLORA_ERR_NULL;
+  if (n < 1 || n > kDecodeMaxWeights) return QLORA_ERR_SHAPE;
+  for (int i = 0; i < n; ++i) {
+    const int st = check_layer(&d[i], T, r);
+    if (st) return st;
+    if (d[i].d_in != d[0].d_in) return QLORA_ERR_SHAPE;
+    if (d[i].blocksize != d[0].blocksize || d[i].dq_blocksize != d[0].dq_blocksize) return QLORA_ERR_UNSUPPORTED;
+  }
+  return QLORA_OK;
+}
+
+size_t multi_slice(const qlora_nf4_desc* d, int64_t T, int32_t r) {
+  return (plan_fwd(d, T, r, nullptr).bytes + 255) & ~(size_t)255;
+}
+}  // namespace
+
+int qlora_multi_fwd_workspace_bytes(int32_t n, const qlora_nf4_desc* d, int64_t T, int32_t r, size_t* bytes) {
+  if (!bytes) return QLORA_ERR_NULL;
+  const int st = check_multi(n, d, T, r);
+  if (st) return st;
+  size_t b = 0;
+  for (int i = 0; i < n; ++i) b += multi_slice(&d[i], T, r);
+  *bytes = b;
+  return QLORA_OK;
+}
+
+int qlora_linear_fwd_multi(int32_t n, const qlora_nf4_desc* d, const uint8_t* const* packed,
+                           const uint8_t* const* codes, const float* const* consts, int64_t T, const uint16_t* X,
+                           int32_t r, float alpha, const uint16_t* const* A, const uint16_t* const* B,
+                           uint16_t* const* Y, float* const* U_out, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  int st = check_multi(n, d, T, r);
+  if (st) return st;
+  if (!packed || !codes || !consts || !Y || (r > 0 && (!A || !B))) return QLORA_ERR_NULL;
+  size_t need = 0;
+  for (int i = 0; i < n; ++i) {
+    if (!packed[i] || (!codes[i] && d[i].dq_blocksize) || !consts[i]) return QLORA_ERR_NULL;
+    if (T > 0 && !Y[i]) return QLORA_ERR_NULL;
+    if (r > 0 && (!A[i] || !B[i])) return QLORA_ERR_NULL;
+    if (!aligned16(packed[i]) || (r > 0 && (!aligned16(A[i]) || !aligned16(B[i])))) return QLORA_ERR_UNSUPPORTED;
+    need += multi_slice(&d[i], T, r);
+  }
+  if (T > 0 && !X) return QLORA_ERR_NULL;
+  if (!aligned16(X)) return QLORA_ERR_UNSUPPORTED;
+  if (need > 0 && (!workspace || workspace_bytes < need)) return QLORA_ERR_WORKSPACE;
+  if (T == 0) return QLORA_OK;
+
+  hipStream_t s_ = (hipStream_t)stream;
+  const int64_t K = d[0].d_in;
+  bool fused = T <= kDecodeMaxT && d[0].dq_blocksize != 0;
+  for (int i = 0; i < n && fused; ++i)
+    fused = decode_supported(d[i].d_out, K, block_shift(&d[i])) && aligned16(codes[i]);
+  if (!fused) {  // one forward per weight
+    size_t off = 0;
+    for (int i = 0; i < n; ++i) {
+      const size_t sl = multi_slice(&d[i], T, r);
+      st = linear_fwd(&d[i], packed[i], codes[i], consts[i], T, X, X, r, alpha, r > 0 ? A[i] : nullptr,
+                      r > 0 ? B[i] : nullptr, Y[i], U_out ? U_out[i] : nullptr, static_cast<char*>(workspace) + off,
+                      sl, stream);
+      if (st) return st;
+      off += sl;
+    }
+    return QLORA_OK;
+  }
+  // few tokens: each weight's U = X A^T, then one launch over all the weights
+  const float s = r > 0 ? alpha / (float)r : 0.0f;
+  DecodeWeight w[kDecodeMaxWeights];
+  const uint16_t* us[kDecodeMaxWeights];
+  size_t off = 0;
+  for (int i = 0; i < n; ++i) {
+    FwdWs fw = plan_fwd(&d[i], T, r, static_cast<char*>(workspace) + off);
+    off += multi_slice(&d[i], T, r);
+    if (r > 0) {
+      const int e = lora_down(X, A[i], T, K, r, s, fw.part, U_out && U_out[i] ? U_out[i] : fw.U, fw.Us, s_);
+      if (e) return e;
+    }
+    w[i] = DecodeWeight{packed[i], codes[i], consts[i], d[i].d_out, r > 0 ? B[i] : nullptr, Y[i], d[i].table};
+    us[i] = fw.Us;
+  }
+  HIP_TRY(launch_decode_multi(w, n, X, T, K, us, hilo_ld(r), r, block_shift(&d[0]), s_));
+  return QLORA_OK;
 }
 
 namespace {

@@ -40,7 +40,7 @@
 //
 // Rank-r term: added per tile after the sum, s (X A^T) B^T through the same
 // MFMA over the 2r hi/lo columns of s U (zero-padded to a multiple of 64).
-#include "common.hpp"
+#include "decode.hpp"
 #include "trace.hpp"
 
 namespace qlora {
@@ -66,6 +66,16 @@ struct DecodeParams {
   uint16_t* Y;         // [T][N]
   int bshift;          // log2(weights per absmax block / 64); K is a multiple of the block
   float level[16];
+};
+
+// Several weights that share X (the projections of one layer input) in one
+// launch: workgroups first_wg[i] .. first_wg[i+1]-1 take the row tiles of
+// weight i.  T, K and the block format are the same for all of them.
+constexpr int kMaxProj = kDecodeMaxWeights;
+struct DecodeMulti {
+  DecodeParams p[kMaxProj];
+  int first_wg[kMaxProj + 1];
+  int n;
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, int64_t bytes) {
@@ -111,7 +121,11 @@ __device__ __forceinline__ f32x4_t mfma(bf16x8_t a, bf16x8_t b, f32x4_t c) {
 // two codes are one aligned 2-byte LDS read and its two blocks (an even block
 // index and the next) never straddle a group of 256 blocks.
 template <int DW, int NTW, int XQ, bool CODES2>
-__global__ __launch_bounds__(DW * 64) void k_decode(DecodeParams P) {
+__global__ __launch_bounds__(DW * 64) void k_decode(DecodeMulti M) {
+  // this workgroup's weight (a wave-uniform choice)
+  int pi = 0;
+  for (int q = 1; q < M.n; ++q) pi += (int)blockIdx.x >= M.first_wg[q] ? 1 : 0;
+  const DecodeParams& P = M.p[pi];
   constexpr int DT = DW * 64;
   // chunks in flight per wave besides the reissued tiles (registers: 128 per
   // lane with 16 waves, 256 with 8)
@@ -133,7 +147,7 @@ __global__ __launch_bounds__(DW * 64) void k_decode(DecodeParams P) {
   // every byte offset below fits 32 bits: the packed weight is below 2 GiB
   const int T = (int)P.T, K = (int)P.K;
   const int ntiles = (int)(P.N / 16);
-  const int nt0 = (int)blockIdx.x * NTW;
+  const int nt0 = ((int)blockIdx.x - M.first_wg[pi]) * NTW;
   const int nbk = K / 64;             // 64-weight halves of chunks per row
   const int nbc = nbk >> P.bshift;    // scale codes per row
   const int nch = (K + 127) / 128;
@@ -375,17 +389,17 @@ __global__ __launch_bounds__(DW * 64) void k_decode(DecodeParams P) {
 
 // 16 waves where their 128 registers per lane hold the loop, else 8
 template <int NTW>
-void launch_ntw(const DecodeParams& P, bool c2, unsigned grid, hipStream_t stream) {
+void launch_ntw(const DecodeMulti& P, bool c2, unsigned grid, hipStream_t stream) {
   const dim3 g(grid);
   KernelEvents ev(KID_DECODE);
   const hipEvent_t e0 = ev.start(), e1 = ev.stop();
-  if (c2 && P.T <= 4) {
+  if (c2 && P.p[0].T <= 4) {
     if constexpr (NTW <= 7) hipExtLaunchKernelGGL((k_decode<16, NTW, 1, true>), g, dim3(1024), 0, stream, e0, e1, 0, P);
     else hipExtLaunchKernelGGL((k_decode<8, NTW, 1, true>), g, dim3(512), 0, stream, e0, e1, 0, P);
   } else if (c2) {
     if constexpr (NTW <= 6) hipExtLaunchKernelGGL((k_decode<16, NTW, 4, true>), g, dim3(1024), 0, stream, e0, e1, 0, P);
     else hipExtLaunchKernelGGL((k_decode<8, NTW, 4, true>), g, dim3(512), 0, stream, e0, e1, 0, P);
-  } else if (P.T <= 4) {
+  } else if (P.p[0].T <= 4) {
     hipExtLaunchKernelGGL((k_decode<8, NTW, 1, false>), g, dim3(512), 0, stream, e0, e1, 0, P);
   } else {
     hipExtLaunchKernelGGL((k_decode<8, NTW, 4, false>), g, dim3(512), 0, stream, e0, e1, 0, P);
@@ -403,22 +417,27 @@ bool decode_supported(int64_t N, int64_t K, int bshift) {
   return ((16 * rs + 15) & ~15LL) + 4 * (16 * nbc / 256 + 2) <= CODES_BYTES;
 }
 
-hipError_t launch_decode(const uint8_t* packed, const uint8_t* codes, const float* consts, const uint16_t* X,
-                         int64_t T, int64_t N, int64_t K, const uint16_t* Us, int64_t ldh, const uint16_t* B,
-                         int r, uint16_t* Y, int table, int bshift, hipStream_t stream) {
+hipError_t launch_decode_multi(const DecodeWeight* w, int n, const uint16_t* X, int64_t T, int64_t K,
+                               const uint16_t* const* Us, int64_t ldh, int r, int bshift, hipStream_t stream) {
   // byte offsets into the packed weight, codes and X are 32-bit
-  if (T < 1 || T > 16 || bshift < 0 || bshift > 2 || !decode_supported(N, K, bshift)) return hipErrorInvalidValue;
-  DecodeParams P;
-  P.packed = packed; P.codes = codes; P.consts = consts; P.X = X;
-  P.T = T; P.N = N; P.K = K;
-  P.Us = Us; P.ldh = ldh; P.B = B; P.r = r;
-  P.Y = Y;
-  P.bshift = bshift;
-  const Nf4Table& tab = level_table(table);
-  for (int i = 0; i < 16; ++i) P.level[i] = tab.level[i];
-  // tiles per workgroup: the 16-row tiles spread over the 256 CUs (at most 8 each)
-  const int64_t ntiles = N / 16;
-  int64_t ntw = (ntiles + 255) / 256;
+  if (n < 1 || n > kMaxProj || T < 1 || T > 16 || bshift < 0 || bshift > 2) return hipErrorInvalidValue;
+  DecodeMulti M{};
+  M.n = n;
+  int64_t ntiles_all = 0;
+  for (int i = 0; i < n; ++i) {
+    if (!decode_supported(w[i].N, K, bshift)) return hipErrorInvalidValue;
+    DecodeParams& P = M.p[i];
+    P.packed = w[i].packed; P.codes = w[i].codes; P.consts = w[i].consts; P.X = X;
+    P.T = T; P.N = w[i].N; P.K = K;
+    P.Us = Us[i]; P.ldh = ldh; P.B = w[i].B; P.r = r;
+    P.Y = w[i].Y;
+    P.bshift = bshift;
+    const Nf4Table& tab = level_table(w[i].table);
+    for (int j = 0; j < 16; ++j) P.level[j] = tab.level[j];
+    ntiles_all += w[i].N / 16;
+  }
+  // tiles per workgroup: all weights' 16-row tiles spread over the 256 CUs (at most 8 each)
+  int64_t ntw = (ntiles_all + 255) / 256;
   if (ntw > 8) ntw = 8;
   // the workgroup's codes and group ratios must fit their LDS region, and the
   // group count one load per thread
@@ -427,19 +446,32 @@ hipError_t launch_decode(const uint8_t* packed, const uint8_t* codes, const floa
   auto aux_need = [&](int64_t t) { return ((16 * t * rs + 15) & ~15LL) + 4 * (16 * t * nbc / 256 + 2); };
   while (ntw > 1 && aux_need(ntw) > CODES_BYTES) --ntw;
   if (aux_need(ntw) > CODES_BYTES) return hipErrorInvalidValue;
-  const unsigned grid = (unsigned)((ntiles + ntw - 1) / ntw);
+  int64_t wg = 0;
+  for (int i = 0; i < n; ++i) {
+    M.first_wg[i] = (int)wg;
+    wg += (w[i].N / 16 + ntw - 1) / ntw;
+  }
+  M.first_wg[n] = (int)wg;
+  const unsigned grid = (unsigned)wg;
   const bool c2 = bshift == 0 && (K / 64) % 2 == 0;
   switch (ntw) {
-    case 1: launch_ntw<1>(P, c2, grid, stream); break;
-    case 2: launch_ntw<2>(P, c2, grid, stream); break;
-    case 3: launch_ntw<3>(P, c2, grid, stream); break;
-    case 4: launch_ntw<4>(P, c2, grid, stream); break;
-    case 5: launch_ntw<5>(P, c2, grid, stream); break;
-    case 6: launch_ntw<6>(P, c2, grid, stream); break;
-    case 7: launch_ntw<7>(P, c2, grid, stream); break;
-    default: launch_ntw<8>(P, c2, grid, stream); break;
+    case 1: launch_ntw<1>(M, c2, grid, stream); break;
+    case 2: launch_ntw<2>(M, c2, grid, stream); break;
+    case 3: launch_ntw<3>(M, c2, grid, stream); break;
+    case 4: launch_ntw<4>(M, c2, grid, stream); break;
+    case 5: launch_ntw<5>(M, c2, grid, stream); break;
+    case 6: launch_ntw<6>(M, c2, grid, stream); break;
+    case 7: launch_ntw<7>(M, c2, grid, stream); break;
+    default: launch_ntw<8>(M, c2, grid, stream); break;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_decode(const uint8_t* packed, const uint8_t* codes, const float* consts, const uint16_t* X,
+                         int64_t T, int64_t N, int64_t K, const uint16_t* Us, int64_t ldh, const uint16_t* B,
+                         int r, uint16_t* Y, int table, int bshift, hipStream_t stream) {
+  const DecodeWeight w{packed, codes, consts, N, B, Y, table};
+  return launch_decode_multi(&w, 1, X, T, K, &Us, ldh, r, bshift, stream);
 }
 
 }  // namespace qlora

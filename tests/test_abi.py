@@ -229,6 +229,20 @@ def test_dropout_validation_happens_before_any_launch():
         q.QLORA_ERR_WORKSPACE
 
 
+def test_multi_forward_validation():
+    L = q.lib()
+    n = ctypes.c_size_t()
+    d3 = (q.Nf4Desc * 3)(q._desc(512, 512), q._desc(128, 512), q._desc(128, 512))
+    assert L.qlora_multi_fwd_workspace_bytes(3, d3, 4, 8, ctypes.byref(n)) == q.QLORA_OK and n.value > 0
+    assert L.qlora_multi_fwd_workspace_bytes(0, d3, 4, 8, ctypes.byref(n)) == q.QLORA_ERR_SHAPE
+    d5 = (q.Nf4Desc * 5)(*[q._desc(64, 64)] * 5)
+    assert L.qlora_multi_fwd_workspace_bytes(5, d5, 4, 8, ctypes.byref(n)) == q.QLORA_ERR_SHAPE
+    dk = (q.Nf4Desc * 2)(q._desc(64, 64), q._desc(64, 128))
+    assert L.qlora_multi_fwd_workspace_bytes(2, dk, 4, 8, ctypes.byref(n)) == q.QLORA_ERR_SHAPE
+    db = (q.Nf4Desc * 2)(q._desc(64, 256), q._desc(64, 256, 128))
+    assert L.qlora_multi_fwd_workspace_bytes(2, db, 4, 8, ctypes.byref(n)) == q.QLORA_ERR_UNSUPPORTED
+
+
 def test_workspace_sizes_grow_with_tokens_and_rank():
     a = q.qlora_bwd_workspace_bytes(4096, 4096, 2048, 16)
     b = q.qlora_bwd_workspace_bytes(4096, 4096, 4096, 64)

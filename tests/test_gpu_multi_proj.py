@@ -1,0 +1,101 @@
+"""GPU parity for the forward of several layers that share their input
+("LoRA 与 QLoRA：把大模型微调拆成可负担的工程" §8: LoRA on every linear module,
+so the projections of one input arrive together): each layer's Y and U
+against the oracle; with at most 16 tokens all weights stream in one launch,
+otherwise the layers run one after another and match separate calls bit for
+bit."""
+
+import numpy as np
+import pytest
+
+import workloads
+from gpu_helpers import TOL, dev_bf16, dev_f32, host_bf16_to_f64, normwise_err, say
+from oracle import lora as olora
+from oracle import nf4 as onf4
+from oracle.bf16 import bits_to_float
+
+pytestmark = pytest.mark.gpu
+
+
+def _layers(shapes, K, T, r, seed, tables=None):
+    import nf4_bit_quantized_amd as q
+    tables = tables or [0] * len(shapes)
+    X = workloads.layer_inputs(64, K, T, 1, seed, with_dy=False)["X"]
+    out = []
+    for i, N in enumerate(shapes):
+        inp = workloads.layer_inputs(N, K, T, r, seed + 1 + i, with_dy=False)
+        pk, cd, cs = q.qlora_quantize_nf4(dev_f32(inp["W"]), table=tables[i])
+        out.append(dict(inp=inp, dev=(pk, cd, cs, dev_bf16(inp["A"]) if r else None, dev_bf16(inp["B"]) if r else None),
+                        levels=None if tables[i] == 0 else onf4.uniform_levels()))
+    return X, out
+
+
+@pytest.mark.parametrize("T", [1, 4, 16])
+def test_qkv_shaped_few_tokens_match_oracle(T):
+    """Query 512 rows, key and value 128 rows each (grouped-query shapes), K = 512, r = 8."""
+    import nf4_bit_quantized_amd as q
+    import torch
+    K, r, alpha = 512, 8, 16.0
+    say(f"multi T={T}")
+    Xb, layers = _layers([512, 128, 128], K, T, r, seed=110)
+    outs = q.qlora_linear_fwd_multi([l["dev"] for l in layers], dev_bf16(Xb), alpha)
+    torch.cuda.synchronize()
+    X = bits_to_float(Xb)
+    for l, (Y, U) in zip(layers, outs):
+        W_hat = onf4.dequantize(onf4.quantize(l["inp"]["W"], levels=l["levels"]), levels=l["levels"])
+        Yo, Uo = olora.forward(W_hat, X, bits_to_float(l["inp"]["A"]), bits_to_float(l["inp"]["B"]), alpha, r)
+        ey, eu = normwise_err(host_bf16_to_f64(Y), Yo), normwise_err(U.cpu().numpy().astype(np.float64), Uo)
+        say(f"  Y {ey:.2e} U {eu:.2e}")
+        assert ey <= TOL and eu <= TOL
+
+
+def test_mixed_tables_and_rank_zero():
+    import nf4_bit_quantized_amd as q
+    import torch
+    K, T = 256, 3
+    Xb, layers = _layers([256, 64], K, T, 0, seed=120, tables=[1, 0])
+    outs = q.qlora_linear_fwd_multi([l["dev"] for l in layers], dev_bf16(Xb), 0.0, tables=[1, 0])
+    torch.cuda.synchronize()
+    X = bits_to_float(Xb)
+    for l, (Y, U) in zip(layers, outs):
+        assert U is None
+        W_hat = onf4.dequantize(onf4.quantize(l["inp"]["W"], levels=l["levels"]), levels=l["levels"])
+        assert normwise_err(host_bf16_to_f64(Y), X @ W_hat.T) <= TOL
+
+
+def test_many_tokens_run_layer_by_layer_bit_identical():
+    import nf4_bit_quantized_amd as q
+    import torch
+    K, T, r, alpha = 320, 40, 16, 8.0
+    Xb, layers = _layers([192, 64, 64], K, T, r, seed=130)
+    X = dev_bf16(Xb)
+    outs = q.qlora_linear_fwd_multi([l["dev"] for l in layers], X, alpha)
+    sep = [q.qlora_linear_fwd(*l["dev"][:3], X, l["dev"][3], l["dev"][4], alpha) for l in layers]
+    torch.cuda.synchronize()
+    for (Y, U), (Ys, Us) in zip(outs, sep):
+        assert torch.equal(Y.view(torch.int16), Ys.view(torch.int16))
+        assert torch.equal(U, Us)
+
+
+def test_gqa_70b_shapes_one_token():
+    """Query 8192x8192 with key and value 1024x8192 at one token, r = 64,
+    against separate calls (the same kernels, within the bar)."""
+    import nf4_bit_quantized_amd as q
+    import torch
+    K, T, r, alpha = 8192, 1, 64, 16.0
+    g = torch.Generator(device="cuda").manual_seed(140)
+    layers = []
+    for N in (8192, 1024, 1024):
+        pk, cd, cs = q.qlora_quantize_nf4(torch.randn(N, K, device="cuda", generator=g) * 0.02)
+        A = (torch.randn(r, K, device="cuda", generator=g) / r).to(torch.bfloat16)
+        B = (torch.randn(N, r, device="cuda", generator=g) * 0.01).to(torch.bfloat16)
+        layers.append((pk, cd, cs, A, B))
+    X = torch.randn(T, K, device="cuda", generator=g).to(torch.bfloat16)
+    outs = q.qlora_linear_fwd_multi(layers, X, alpha)
+    sep = [q.qlora_linear_fwd(*l[:3], X, l[3], l[4], alpha) for l in layers]
+    torch.cuda.synchronize()
+    for (Y, U), (Ys, Us) in zip(outs, sep):
+        e = normwise_err(Y.float().cpu().numpy().astype(np.float64), Ys.float().cpu().numpy().astype(np.float64))
+        say(f"  Y vs separate {e:.2e}")
+        assert e <= TOL
+        assert torch.equal(U, Us)
