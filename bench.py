@@ -67,6 +67,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the few-token packed-weight GB/s section")
+    ap.add_argument("--mlp", action="store_true",
+                    help="also time the MLP shapes of a 7B-class layer (fused products of other shapes; off by "
+                         "default so that the kernel trace of the default run holds only the roofline shape)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget for the oracle timing")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the JSON line, fill then copy a buffer of this many MiB (known HBM bytes "
@@ -575,8 +578,9 @@ def main():
         result["quantize_16bit_weight"] = quantize16_section(lin, steps=max(20, args.steps))
         result["adamw_65b_adapters"] = adamw_section(steps=max(20, args.steps))
         result["lora_dropout_attn4096"] = dropout_section(lin, steps=max(20, args.steps))
-        result["mlp_llama7b"] = mlp_section(steps=10)
         result["qkv_gqa_70b"] = multi_proj_section(steps=max(20, args.steps))
+    if args.mlp:
+        result["mlp_llama7b"] = mlp_section(steps=10)
     if not args.no_cpu_baseline:
         log("timing the oracle on the host ...")
         result["cpu_baseline"] = cpu_baseline(inp, lin, args.cpu_seconds)
