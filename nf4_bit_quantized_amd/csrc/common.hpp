@@ -51,7 +51,6 @@ struct QuantLut {
 
 // The table above (NF4, or that of level table `table`); ok is false if some
 // widened bucket held two thresholds.
-const QuantLut& quant_lut(bool* ok);
 const QuantLut& quant_lut(int table, bool* ok);
 
 // Workgroup barrier that orders LDS only: waits for this wave's LDS

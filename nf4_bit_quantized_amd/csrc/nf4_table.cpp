@@ -136,8 +136,6 @@ const Nf4Table& level_table(int table) {
   return table == kTableUniform ? uniform : nf4_table();
 }
 
-const QuantLut& quant_lut(bool* ok) { return quant_lut(kTableNf4, ok); }
-
 const QuantLut& quant_lut(int table, bool* ok) {
   static bool good_nf4 = false, good_uniform = false;
   static const QuantLut lut_nf4 = build_lut(nf4_table(), &good_nf4);
