@@ -39,11 +39,11 @@ BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 # on (sha256 of the files below); reported as null once those change.
 TRAFFIC_SOURCES = ("fused_gemm.hip", "fused.hpp", "restore.hpp", "common.hpp")
 TRAFFIC = {
-    "sha256": "ab51b1e57b8f2a73180fea5c408e1e9b3f124ff7f3fb301824e04ea4ccbca3db",
+    "sha256": "b41ca9f18b4951235f4cbdaf960786f190755bfa87f1ccd40cd5dcb678c92b2d",
     "fetch_scale": 262144.0 / 131088.4,
     "write_scale": 1.0,
-    "fwd_gemm": {"fetch_kib": 36003.7, "write_kib": 16384.0},
-    "dx_gemm": {"fetch_kib": 35833.9, "write_kib": 16384.0},
+    "fwd_gemm": {"fetch_kib": 36004.0, "write_kib": 16384.0},
+    "dx_gemm": {"fetch_kib": 35834.2, "write_kib": 16384.0},
 }
 
 
