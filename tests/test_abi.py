@@ -243,6 +243,25 @@ def test_multi_forward_validation():
     assert L.qlora_multi_fwd_workspace_bytes(2, db, 4, 8, ctypes.byref(n)) == q.QLORA_ERR_UNSUPPORTED
 
 
+def test_trace_api_on_the_host():
+    """The kernel-timing switches and read-out need no GPU: names of every
+    timed kernel, an empty read, selection by name."""
+    names = []
+    k = 0
+    while q.qlora_trace_kernel_name(k) is not None:
+        names.append(q.qlora_trace_kernel_name(k))
+        k += 1
+    for n in ("nf4_quantize", "fwd_gemm", "dx_gemm", "decode", "export", "adamw", "dropout"):
+        assert n in names
+    assert len(set(names)) == len(names)
+    assert q.qlora_trace_kernel_name(-1) is None
+    q.qlora_trace_enable(False)
+    assert q.qlora_trace_read(reset=True) == {}
+    q.qlora_trace_select({"fwd_gemm", "dx_gemm"})
+    q.qlora_trace_enable(False)
+    assert q.qlora_trace_read(reset=True) == {}
+
+
 def test_workspace_sizes_grow_with_tokens_and_rank():
     a = q.qlora_bwd_workspace_bytes(4096, 4096, 2048, 16)
     b = q.qlora_bwd_workspace_bytes(4096, 4096, 4096, 64)
