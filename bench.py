@@ -33,17 +33,17 @@ BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 # from two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE,
 # KiB per dispatch, averaged over the dispatches of each kernel), scaled by
 # what the same counters read for a plain 256 MiB fill and copy in the same
-# runs (--copy-calibration 256): the copy's FETCH_SIZE reads 131088.4 KiB for
-# 262144 KiB moved (scale 1.99977), the fill's WRITE_SIZE reads exactly
+# runs (--copy-calibration 256): the copy's FETCH_SIZE reads 131090.9 KiB for
+# 262144 KiB moved (scale 1.99973), the fill's WRITE_SIZE reads exactly
 # 262144 KiB (scale 1).  Valid only for the kernel sources they were taken
 # on (sha256 of the files below); reported as null once those change.
 TRAFFIC_SOURCES = ("fused_gemm.hip", "fused.hpp", "restore.hpp", "common.hpp")
 TRAFFIC = {
-    "sha256": "b41ca9f18b4951235f4cbdaf960786f190755bfa87f1ccd40cd5dcb678c92b2d",
-    "fetch_scale": 262144.0 / 131088.4,
+    "sha256": "fa541814e1aa5d9ef702c1df6eaf09ea4b58889738e205a5ea9722a9b7c99008",
+    "fetch_scale": 262144.0 / 131090.9,
     "write_scale": 1.0,
-    "fwd_gemm": {"fetch_kib": 36004.0, "write_kib": 16384.0},
-    "dx_gemm": {"fetch_kib": 35834.2, "write_kib": 16384.0},
+    "fwd_gemm": {"fetch_kib": 36005.5, "write_kib": 16384.0},
+    "dx_gemm": {"fetch_kib": 35835.9, "write_kib": 16384.0},
 }
 
 

@@ -292,6 +292,25 @@ int qlora_linear_fwd_multi(int32_t n, const qlora_nf4_desc* d, const uint8_t* co
                            void* stream);
 
 /*
+ * Backward of n (1..4) layers that share their input X (as for
+ * qlora_linear_fwd_multi): X's gradient is the sum of the layers' shares,
+ *   dX = bf16( sum_i (dY_i W_hat_i + s G_i A_i) ),
+ * formed layer after layer: the first layer's product writes dX, each later
+ * one adds its tile to what dX holds in fp32 and rounds (so dX is rounded
+ * once per layer).  dA[i] and dB[i] are each layer's own, overwritten.
+ * U_in may be NULL or hold NULL entries (U recomputed).  dX may be NULL.
+ * The layers run one after another on the stream, reusing one workspace of
+ * qlora_multi_bwd_workspace_bytes.  Errors: as qlora_linear_bwd, and SHAPE
+ * (n outside 1..4, different d_in), UNSUPPORTED (different block format).
+ */
+int qlora_multi_bwd_workspace_bytes(int32_t n, const qlora_nf4_desc* d, int64_t T, int32_t r, size_t* bytes);
+int qlora_linear_bwd_multi(int32_t n, const qlora_nf4_desc* d, const uint8_t* const* packed,
+                           const uint8_t* const* codes, const float* const* consts, int64_t T, const uint16_t* X,
+                           int32_t r, float alpha, const uint16_t* const* A, const uint16_t* const* B,
+                           const float* const* U_in, const uint16_t* const* dY, uint16_t* dX, float* const* dA,
+                           float* const* dB, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * LoRA dropout on the adapter's input ("LoRA 与 QLoRA：..." §4.3; its §8
  * configuration uses lora_dropout 0.05).  The base branch takes X unchanged;
  * the adapter takes X_d = bf16_rne(fl32(x * c)) where kept and 0 where

@@ -46,6 +46,8 @@ EXPORTED = (
     "qlora_linear_bwd_dropout",
     "qlora_multi_fwd_workspace_bytes",
     "qlora_linear_fwd_multi",
+    "qlora_multi_bwd_workspace_bytes",
+    "qlora_linear_bwd_multi",
     "qlora_dequantize_nf4",
     "qlora_merge_lora",
     "qlora_adamw_step",
@@ -111,6 +113,8 @@ def lib() -> ctypes.CDLL:
     L.qlora_dropout_workspace_bytes.argtypes = [dp, i64, i32, i32, ctypes.POINTER(sz)]
     L.qlora_multi_fwd_workspace_bytes.argtypes = [i32, dp, i64, i32, ctypes.POINTER(sz)]
     L.qlora_linear_fwd_multi.argtypes = [i32, dp, vp, vp, vp, i64, vp, i32, f32, vp, vp, vp, vp, vp, sz, vp]
+    L.qlora_multi_bwd_workspace_bytes.argtypes = [i32, dp, i64, i32, ctypes.POINTER(sz)]
+    L.qlora_linear_bwd_multi.argtypes = [i32, dp, vp, vp, vp, i64, vp, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.qlora_linear_fwd_dropout.argtypes = [dp, vp, vp, vp, i64, vp, i32, f32, vp, vp, vp, f32, vp, vp, vp, sz, vp]
     L.qlora_linear_bwd_dropout.argtypes = [dp, vp, vp, vp, i64, vp, i32, f32, vp, vp, vp, vp, vp, f32, vp, vp, vp,
                                            i32, vp, sz, vp]
@@ -366,6 +370,44 @@ def qlora_linear_fwd_multi(layers, X, alpha: float, want_u: bool = True, workspa
         arr([_ptr(l[3]) for l in layers]), arr([_ptr(l[4]) for l in layers]), arr([_ptr(o[0]) for o in outs]),
         arr([_ptr(o[1]) for o in outs]), _ptr(ws), n_b.value, _stream(stream)), "qlora_linear_fwd_multi")
     return outs
+
+
+def qlora_linear_bwd_multi(layers, X, alpha: float, dYs, U_ins=None, want_dx: bool = True, workspace=None,
+                           stream=None, tables=None):
+    """Backward of up to four layers sharing X: ``layers`` as for
+    qlora_linear_fwd_multi, ``dYs`` each layer's upstream gradient, ``U_ins``
+    each layer's saved U (or None).  Returns (dX summed over the layers,
+    [(dA, dB) per layer])."""
+    import torch
+    n = len(layers)
+    if not 1 <= n <= 4 or len(dYs) != n:
+        raise ValueError("one to four layers, one dY each")
+    T, d_in = X.shape[0], X.shape[1]
+    r = 0 if layers[0][3] is None else layers[0][3].shape[0]
+    tables = tables or [TABLE_NF4] * n
+    U_ins = U_ins or [None] * n
+    descs = (Nf4Desc * n)()
+    grads = []
+    for i, (packed, codes, consts, A, B) in enumerate(layers):
+        _need_cuda(packed, codes, consts, A, B, dYs[i], U_ins[i], name="qlora_linear_bwd_multi")
+        descs[i] = _stored_desc(packed, codes, consts, tables[i])
+        dA = torch.empty((r, d_in), dtype=torch.float32, device=X.device) if r > 0 else None
+        dB = torch.empty((packed.shape[0], r), dtype=torch.float32, device=X.device) if r > 0 else None
+        grads.append((dA, dB))
+    _need_cuda(X, name="qlora_linear_bwd_multi")
+    dX = torch.empty((T, d_in), dtype=torch.bfloat16, device=X.device) if want_dx else None
+    n_b = ctypes.c_size_t()
+    _check(lib().qlora_multi_bwd_workspace_bytes(n, descs, int(T), int(r), ctypes.byref(n_b)),
+           "qlora_multi_bwd_workspace_bytes")
+    ws = _workspace(n_b.value, X.device, workspace)
+    arr = lambda vals: (ctypes.c_void_p * n)(*vals)
+    _check(lib().qlora_linear_bwd_multi(
+        n, descs, arr([_ptr(l[0]) for l in layers]), arr([_ptr(l[1]) for l in layers]),
+        arr([_ptr(l[2]) for l in layers]), int(T), _ptr(X), int(r), float(alpha),
+        arr([_ptr(l[3]) for l in layers]), arr([_ptr(l[4]) for l in layers]), arr([_ptr(u) for u in U_ins]),
+        arr([_ptr(dy) for dy in dYs]), _ptr(dX), arr([_ptr(g[0]) for g in grads]), arr([_ptr(g[1]) for g in grads]),
+        _ptr(ws), n_b.value, _stream(stream)), "qlora_linear_bwd_multi")
+    return dX, grads
 
 
 def qlora_linear_bwd(packed, codes, consts, X, A, B, alpha: float, dY, U_in=None, dX=None, dA=None, dB=None,

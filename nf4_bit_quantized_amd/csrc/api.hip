@@ -317,7 +317,7 @@ namespace {
 int linear_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes, const float* consts, int64_t T,
                const uint16_t* X, const uint16_t* Xa, const uint8_t* keep, float c, int32_t r, float alpha,
                const uint16_t* A, const uint16_t* B, const float* U_in, const uint16_t* dY, uint16_t* dX, float* dA,
-               float* dB, void* workspace, size_t workspace_bytes, void* stream, int accumulate) {
+               float* dB, void* workspace, size_t workspace_bytes, void* stream, int accumulate, int dx_accumulate = 0) {
   const int st = check_layer(d, T, r);
   if (st) return st;
   if (!packed || (!codes && d->dq_blocksize) || !consts) return QLORA_ERR_NULL;
@@ -374,6 +374,7 @@ int linear_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* co
     fp.At = w.Gs; fp.ldat = ldh; fp.Bt = A; fp.ldbt = K;
     fp.r = keep ? 0 : r;  // with dropout the adapter's share is added after, through the mask
     fp.C = dX; fp.ldc = K;
+    fp.accumulate = dx_accumulate;
     HIP_TRY(launch_fused(fp, true, s_, KID_DX_GEMM));
     if (keep && r > 0) {
       DropoutDxParams Dp{};
@@ -451,6 +452,42 @@ int qlora_multi_fwd_workspace_bytes(int32_t n, const qlora_nf4_desc* d, int64_t 
   size_t b = 0;
   for (int i = 0; i < n; ++i) b += multi_slice(&d[i], T, r);
   *bytes = b;
+  return QLORA_OK;
+}
+
+int qlora_multi_bwd_workspace_bytes(int32_t n, const qlora_nf4_desc* d, int64_t T, int32_t r, size_t* bytes) {
+  if (!bytes) return QLORA_ERR_NULL;
+  const int st = check_multi(n, d, T, r);
+  if (st) return st;
+  size_t b = 0;
+  for (int i = 0; i < n; ++i) b = std::max(b, plan_bwd(&d[i], T, r, nullptr).bytes);
+  *bytes = b;
+  return QLORA_OK;
+}
+
+int qlora_linear_bwd_multi(int32_t n, const qlora_nf4_desc* d, const uint8_t* const* packed,
+                           const uint8_t* const* codes, const float* const* consts, int64_t T, const uint16_t* X,
+                           int32_t r, float alpha, const uint16_t* const* A, const uint16_t* const* B,
+                           const float* const* U_in, const uint16_t* const* dY, uint16_t* dX, float* const* dA,
+                           float* const* dB, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_multi(n, d, T, r);
+  if (st) return st;
+  if (!packed || !codes || !consts || !dY || (r > 0 && (!A || !B || !dA || !dB))) return QLORA_ERR_NULL;
+  size_t need = 0;
+  for (int i = 0; i < n; ++i) {
+    if (!packed[i] || (!codes[i] && d[i].dq_blocksize) || !consts[i] || (T > 0 && !dY[i])) return QLORA_ERR_NULL;
+    if (r > 0 && (!A[i] || !B[i] || !dA[i] || !dB[i])) return QLORA_ERR_NULL;
+    need = std::max(need, plan_bwd(&d[i], T, r, nullptr).bytes);
+  }
+  if (need > 0 && (!workspace || workspace_bytes < need)) return QLORA_ERR_WORKSPACE;
+  // one layer after another on the stream (the workspace is reused); from
+  // the second on, the dX product adds to the dX the earlier ones wrote
+  for (int i = 0; i < n; ++i) {
+    st = linear_bwd(&d[i], packed[i], codes[i], consts[i], T, X, X, nullptr, 1.0f, r, alpha,
+                    r > 0 ? A[i] : nullptr, r > 0 ? B[i] : nullptr, U_in ? U_in[i] : nullptr, dY[i], dX,
+                    r > 0 ? dA[i] : nullptr, r > 0 ? dB[i] : nullptr, workspace, workspace_bytes, stream, 0, i > 0);
+    if (st) return st;
+  }
   return QLORA_OK;
 }
 

@@ -25,6 +25,7 @@ struct FusedParams {
   int32_t table;           // level table (kTableNf4 / kTableUniform)
   int32_t bshift;          // log2(weights per absmax block / 64)
   int32_t dq;              // 1: 8-bit codes + group constants; 0: consts holds the fp32 block scales
+  int32_t accumulate;      // 1: C = bf16(C + tile), adding to what C holds (C's tile is rounded first)
   int32_t mt, nt, group_m; // filled by the launcher
   Nf4Table tab;            // filled by the launcher from table
 };

@@ -522,13 +522,26 @@ __device__ __forceinline__ void fused_body(const FusedParams& P) {
     lds_barrier();  // the output tile is in LDS
   }
 
-  // coalesced 16-byte stores of the bf16 tile, all eight waves
+  // coalesced 16-byte stores of the bf16 tile, all eight waves; when
+  // accumulating, each 8-element piece is added to C's in fp32 and rounded
   const uint16_t* ct = reinterpret_cast<const uint16_t*>(lds);
   for (int c = threadIdx.x; c < G::BM * (BN / 8); c += 512) {
     const int row = c / (BN / 8), cc = (c % (BN / 8)) * 8;
     const int64_t gr = m0 + row, gc = n0 + cc;
-    if (gr < P.M && gc < P.N)
-      *reinterpret_cast<uint4*>(P.C + gr * P.ldc + gc) = *reinterpret_cast<const uint4*>(ct + row * G::LDC + cc);
+    if (gr >= P.M || gc >= P.N) continue;
+    uint4 v = *reinterpret_cast<const uint4*>(ct + row * G::LDC + cc);
+    uint4* dst = reinterpret_cast<uint4*>(P.C + gr * P.ldc + gc);
+    if (P.accumulate) {
+      const uint4 o = *dst;
+      const uint32_t ow[4] = {o.x, o.y, o.z, o.w}, nw[4] = {v.x, v.y, v.z, v.w};
+      uint32_t sw[4];
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+        sw[h] = pack_bf16x2(bf16_bits_to_f32(ow[h] & 0xFFFFu) + bf16_bits_to_f32(nw[h] & 0xFFFFu),
+                            bf16_bits_to_f32(ow[h] >> 16) + bf16_bits_to_f32(nw[h] >> 16));
+      v = make_uint4(sw[0], sw[1], sw[2], sw[3]);
+    }
+    *dst = v;
   }
 }
 

@@ -241,6 +241,8 @@ def test_multi_forward_validation():
     assert L.qlora_multi_fwd_workspace_bytes(2, dk, 4, 8, ctypes.byref(n)) == q.QLORA_ERR_SHAPE
     db = (q.Nf4Desc * 2)(q._desc(64, 256), q._desc(64, 256, 128))
     assert L.qlora_multi_fwd_workspace_bytes(2, db, 4, 8, ctypes.byref(n)) == q.QLORA_ERR_UNSUPPORTED
+    assert L.qlora_multi_bwd_workspace_bytes(3, d3, 40, 8, ctypes.byref(n)) == q.QLORA_OK and n.value > 0
+    assert L.qlora_multi_bwd_workspace_bytes(2, dk, 40, 8, ctypes.byref(n)) == q.QLORA_ERR_SHAPE
 
 
 def test_trace_api_on_the_host():

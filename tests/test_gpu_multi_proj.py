@@ -99,3 +99,32 @@ def test_gqa_70b_shapes_one_token():
         say(f"  Y vs separate {e:.2e}")
         assert e <= TOL
         assert torch.equal(U, Us)
+
+
+@pytest.mark.parametrize("T", [4, 40, 600])
+def test_backward_of_layers_sharing_x(T):
+    """dX is the sum of the layers' shares; dA, dB are each layer's own."""
+    import nf4_bit_quantized_amd as q
+    import torch
+    K, r, alpha = 320, 8, 16.0
+    say(f"multi backward T={T}")
+    Xb, layers = _layers([192, 64, 64], K, T, r, seed=150)
+    X = dev_bf16(Xb)
+    dYs_b = [workloads.layer_inputs(l["dev"][0].shape[0], K, T, 1, 160 + i)["dY"] for i, l in enumerate(layers)]
+    dYs = [dev_bf16(b) for b in dYs_b]
+    outs = q.qlora_linear_fwd_multi([l["dev"] for l in layers], X, alpha)
+    dX, grads = q.qlora_linear_bwd_multi([l["dev"] for l in layers], X, alpha, dYs, U_ins=[o[1] for o in outs])
+    torch.cuda.synchronize()
+    Xf = bits_to_float(Xb)
+    want_dx = 0.0
+    for l, dyb, (dA, dB) in zip(layers, dYs_b, grads):
+        W_hat = onf4.dequantize(onf4.quantize(l["inp"]["W"]))
+        dXo, dAo, dBo = olora.backward(W_hat, Xf, bits_to_float(l["inp"]["A"]), bits_to_float(l["inp"]["B"]),
+                                       bits_to_float(dyb), alpha, r)
+        want_dx = want_dx + dXo
+        ea = normwise_err(dA.cpu().numpy().astype(np.float64), dAo)
+        eb = normwise_err(dB.cpu().numpy().astype(np.float64), dBo)
+        assert ea <= TOL and eb <= TOL, (ea, eb)
+    ex = normwise_err(host_bf16_to_f64(dX), want_dx)
+    say(f"  dX {ex:.2e}")
+    assert ex <= TOL
