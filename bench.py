@@ -464,7 +464,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the layer's multi-GPU sharding is described in DESIGN.md, not built).", file=sys.stderr)
+              "(sharding the layer over several GPUs is not part of this library).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
