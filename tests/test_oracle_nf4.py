@@ -293,3 +293,35 @@ def test_low_rank_count():
     d, r = g["d"], g["r"]
     assert d * d == g["full"] and 2 * d * r == g["lowrank"]
     assert round(100 * 2 * d * r / (d * d), 1) == g["percent_approx"]
+
+
+# --------------------------------------------------------------------------
+# Block size ([QLoRA-入门到精通] §3(1): blocks of e.g. 64 or 256 values)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bs", [128, 256])
+def test_larger_blocks_equal_64_when_subblocks_share_the_absmax(bs):
+    """If every 64-value piece of a bs-block has the same absmax, the bs-block
+    scale equals each piece's and every index is the same as with blocks of 64."""
+    rng = np.random.default_rng(7)
+    W = np.clip(rng.standard_normal((64, 512)), -3.9, 3.9).astype(np.float32)   # below the planted absmax
+    blocks = W.reshape(-1, bs)
+    M = np.float32(4.0)
+    blocks[:, ::64] = np.where(rng.random((blocks.shape[0], bs // 64)) < 0.5, M, -M)   # absmax M in each piece
+    W = blocks.reshape(64, 512)
+    Qb = nf4.quantize(W, blocksize=bs)
+    Q64 = nf4.quantize(W, blocksize=64)
+    np.testing.assert_array_equal(Qb.q, Q64.q)
+    np.testing.assert_array_equal(Qb.scales, np.full(W.size // bs, M, np.float32))
+    np.testing.assert_array_equal(Q64.scales, np.full(W.size // 64, M, np.float32))
+
+
+def test_block_128_nearest_level_brute_force():
+    rng = np.random.default_rng(8)
+    W = (rng.standard_normal((8, 256)) * np.exp(rng.uniform(-3, 3, (8, 1)))).astype(np.float32)
+    Q = nf4.quantize(W, blocksize=128)
+    T = nf4.nf4_levels().astype(np.float64)
+    x = (W.reshape(-1, 128) / Q.scales[:, None]).astype(np.float32).astype(np.float64).reshape(-1)
+    d = np.abs(x[:, None] - T[None, :])
+    best = np.argmin(d, axis=1)      # argmin takes the lower index on ties, as the layer does
+    np.testing.assert_array_equal(Q.q, best)
