@@ -18,6 +18,7 @@ host cores (cpu_baseline), and packed-weight GB/s of the few-token forward.
 """
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -375,7 +376,8 @@ def multi_proj_section(steps):
     """Query, key and value projections of a 70B-class layer with grouped
     queries (8192x8192, 1024x8192, 1024x8192; r = 64, alpha = 16) at 1 and 16
     tokens: one forward call over the three weights against three separate
-    calls, with the weights rotated over 4 copies (173 MB of packed weight).  call_us includes the host's enqueue of each call;
+    calls, with the weights rotated over 4 copies (173 MB of packed weight) and the outputs and
+    workspace allocated once.  call_us includes the host's enqueue of each call;
     kernel_us is the weight-streaming kernels alone."""
     import torch
     import nf4_bit_quantized_amd as q
@@ -395,8 +397,17 @@ def multi_proj_section(steps):
     out = {"weights": "8192x8192 + 2 x 1024x8192", "packed_bytes": packed_bytes}
     for T in (1, 16):
         X = torch.randn(T, K, device="cuda", generator=g).to(torch.bfloat16)
-        calls = {"fused": lambda L: q.qlora_linear_fwd_multi(L, X, alpha),
-                 "separate": lambda L: [q.qlora_linear_fwd(*l[:3], X, l[3], l[4], alpha) for l in L]}
+        # outputs and workspace allocated once, as a serving loop holds them
+        outs = [(torch.empty((T, N), dtype=torch.bfloat16, device="cuda"),
+                 torch.empty((T, r), dtype=torch.float32, device="cuda")) for N in (8192, 1024, 1024)]
+        n_b = ctypes.c_size_t()
+        descs = (q.Nf4Desc * 3)(*[q._stored_desc(*l[:3], q.TABLE_NF4) for l in sets[0]])
+        q._check(q.lib().qlora_multi_fwd_workspace_bytes(3, descs, T, r, ctypes.byref(n_b)), "workspace")
+        ws_bytes = max([n_b.value] + [q.qlora_fwd_workspace_bytes(N, K, T, r) for N in (8192, 1024)])
+        ws = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device="cuda")
+        calls = {"fused": lambda L: q.qlora_linear_fwd_multi(L, X, alpha, workspace=ws, outs=outs),
+                 "separate": lambda L: [q.qlora_linear_fwd(*l[:3], X, l[3], l[4], alpha, Y=o[0], U_out=o[1],
+                                                           workspace=ws) for l, o in zip(L, outs)]}
         for name, fn in calls.items():
             for i in range(8):
                 fn(sets[i % 4])

@@ -181,6 +181,14 @@ def _need_cuda(*tensors, dtype=None, name=""):
             raise ValueError(f"{name}: tensors must be contiguous")
 
 
+def _check_out(t, shape, dtype, name: str):
+    """A caller-given output: contiguous, of the shape and dtype the call writes."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)}")
+
+
 # ---------------------------------------------------------------------------
 # Host-only queries
 # ---------------------------------------------------------------------------
@@ -302,6 +310,8 @@ def qlora_linear_fwd(packed, codes, consts, X, A, B, alpha: float, Y=None, U_out
     for t, nm in ((X, "X"), (A, "A"), (B, "B")):
         if t is not None and t.dtype != torch.bfloat16:
             raise ValueError(f"{nm} must be bfloat16")
+    _check_out(Y, (T, d_out), torch.bfloat16, "Y")
+    _check_out(U_out, (T, r), torch.float32, "U_out")
     if Y is None:
         Y = torch.empty((T, d_out), dtype=torch.bfloat16, device=X.device)
     if U_out is None and want_u and r > 0:
@@ -339,9 +349,11 @@ def _dropout_ws(d, T: int, r: int, backward: int) -> int:
 
 
 def qlora_linear_fwd_multi(layers, X, alpha: float, want_u: bool = True, workspace=None, stream=None,
-                           tables=None):
+                           tables=None, outs=None):
     """Forward of up to four layers sharing X: ``layers`` is a list of
     (packed, codes, consts, A, B) (A, B None for r = 0, the same r for all).
+    ``outs`` optionally gives each layer's (Y, U) buffers (U may be None);
+    with them and ``workspace`` the call allocates nothing.
     Returns a list of (Y, U) as qlora_linear_fwd does for each layer."""
     import torch
     n = len(layers)
@@ -350,13 +362,23 @@ def qlora_linear_fwd_multi(layers, X, alpha: float, want_u: bool = True, workspa
     T = X.shape[0]
     r = 0 if layers[0][3] is None else layers[0][3].shape[0]
     tables = tables or [TABLE_NF4] * n
+    if outs is not None and len(outs) != n:
+        raise ValueError("one (Y, U) pair per layer")
+    given, outs = outs, []
     descs = (Nf4Desc * n)()
-    outs = []
     for i, (packed, codes, consts, A, B) in enumerate(layers):
         _need_cuda(packed, codes, consts, A, B, name="qlora_linear_fwd_multi")
         descs[i] = _stored_desc(packed, codes, consts, tables[i])
-        Y = torch.empty((T, packed.shape[0]), dtype=torch.bfloat16, device=X.device)
-        U = torch.empty((T, r), dtype=torch.float32, device=X.device) if want_u and r > 0 else None
+        if given is not None:
+            Y, U = given[i]
+            _check_out(Y, (T, packed.shape[0]), torch.bfloat16, f"outs[{i}] Y")
+            _check_out(U, (T, r), torch.float32, f"outs[{i}] U")
+            _need_cuda(Y, U, name="qlora_linear_fwd_multi")
+            if Y is None:
+                raise ValueError(f"outs[{i}]: Y is required")
+        else:
+            Y = torch.empty((T, packed.shape[0]), dtype=torch.bfloat16, device=X.device)
+            U = torch.empty((T, r), dtype=torch.float32, device=X.device) if want_u and r > 0 else None
         outs.append((Y, U))
     _need_cuda(X, name="qlora_linear_fwd_multi")
     n_b = ctypes.c_size_t()

@@ -245,6 +245,18 @@ def test_multi_forward_validation():
     assert L.qlora_multi_bwd_workspace_bytes(2, dk, 40, 8, ctypes.byref(n)) == q.QLORA_ERR_SHAPE
 
 
+def test_caller_outputs_are_checked_on_the_host():
+    """A caller-given output must have the shape and dtype the call writes and
+    be contiguous: the C entry points see only its pointer."""
+    import torch
+    q._check_out(None, (4, 8), torch.bfloat16, "Y")
+    q._check_out(torch.empty(4, 8, dtype=torch.bfloat16), (4, 8), torch.bfloat16, "Y")
+    for bad in (torch.empty(4, 9, dtype=torch.bfloat16), torch.empty(4, 8, dtype=torch.float32),
+                torch.empty(8, 4, dtype=torch.bfloat16).t()):
+        with pytest.raises(ValueError, match="Y must be"):
+            q._check_out(bad, (4, 8), torch.bfloat16, "Y")
+
+
 def test_trace_api_on_the_host():
     """The kernel-timing switches and read-out need no GPU: names of every
     timed kernel, an empty read, selection by name."""

@@ -101,6 +101,34 @@ def test_gqa_70b_shapes_one_token():
         assert torch.equal(U, Us)
 
 
+@pytest.mark.parametrize("T", [16, 40])
+def test_caller_buffers_match_allocated_outputs(T):
+    """Outputs and workspace given by the caller (filled with 0xFF bytes
+    first) hold what the allocating call returns, bit for bit: the one-launch
+    path at 16 tokens, layer by layer at 40."""
+    import nf4_bit_quantized_amd as q
+    import torch
+    K, r, alpha = 512, 8, 16.0
+    say(f"multi caller buffers T={T}")
+    Xb, layers = _layers([512, 128, 128], K, T, r, seed=150)
+    devs = [l["dev"] for l in layers]
+    X = dev_bf16(Xb)
+    ref = q.qlora_linear_fwd_multi(devs, X, alpha)
+    bufs = [(torch.full((T, N), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16),
+             torch.full((T, r), -1, dtype=torch.int32, device="cuda").view(torch.float32)) for N in (512, 128, 128)]
+    import ctypes
+    n_b = ctypes.c_size_t()
+    descs = (q.Nf4Desc * 3)(*[q._stored_desc(*d[:3], 0) for d in devs])
+    q._check(q.lib().qlora_multi_fwd_workspace_bytes(3, descs, T, r, ctypes.byref(n_b)), "ws")
+    ws = torch.full((max(1, n_b.value),), 0xFF, dtype=torch.uint8, device="cuda")
+    got = q.qlora_linear_fwd_multi(devs, X, alpha, workspace=ws, outs=bufs)
+    torch.cuda.synchronize()
+    for (Yr, Ur), (Yg, Ug), (Yb, Ub) in zip(ref, got, bufs):
+        assert Yg.data_ptr() == Yb.data_ptr() and Ug.data_ptr() == Ub.data_ptr()
+        assert torch.equal(Yr.view(torch.int16), Yg.view(torch.int16))
+        assert torch.equal(Ur.view(torch.int32), Ug.view(torch.int32))
+
+
 @pytest.mark.parametrize("T", [4, 40, 600])
 def test_backward_of_layers_sharing_x(T):
     """dX is the sum of the layers' shares; dA, dB are each layer's own."""
