@@ -448,6 +448,8 @@ def qlora_linear_bwd(packed, codes, consts, X, A, B, alpha: float, dY, U_in=None
     for t, nm in ((X, "X"), (A, "A"), (B, "B"), (dY, "dY")):
         if t is not None and t.dtype != torch.bfloat16:
             raise ValueError(f"{nm} must be bfloat16")
+    _check_out(dX, (T, d_in), torch.bfloat16, "dX")
+    _check_out(U_in, (T, r), torch.float32, "U_in")
     if dX is None and want_dx:
         dX = torch.empty((T, d_in), dtype=torch.bfloat16, device=X.device)
     if r > 0:
