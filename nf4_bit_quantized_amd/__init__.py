@@ -395,11 +395,12 @@ def qlora_linear_fwd_multi(layers, X, alpha: float, want_u: bool = True, workspa
 
 
 def qlora_linear_bwd_multi(layers, X, alpha: float, dYs, U_ins=None, want_dx: bool = True, workspace=None,
-                           stream=None, tables=None):
+                           stream=None, tables=None, dX=None, grads=None):
     """Backward of up to four layers sharing X: ``layers`` as for
     qlora_linear_fwd_multi, ``dYs`` each layer's upstream gradient, ``U_ins``
-    each layer's saved U (or None).  Returns (dX summed over the layers,
-    [(dA, dB) per layer])."""
+    each layer's saved U (or None).  ``dX`` and ``grads`` (one (dA, dB) per
+    layer) optionally give the output buffers; they are overwritten.
+    Returns (dX summed over the layers, [(dA, dB) per layer])."""
     import torch
     n = len(layers)
     if not 1 <= n <= 4 or len(dYs) != n:
@@ -408,16 +409,29 @@ def qlora_linear_bwd_multi(layers, X, alpha: float, dYs, U_ins=None, want_dx: bo
     r = 0 if layers[0][3] is None else layers[0][3].shape[0]
     tables = tables or [TABLE_NF4] * n
     U_ins = U_ins or [None] * n
+    if grads is not None and len(grads) != n:
+        raise ValueError("one (dA, dB) pair per layer")
+    given, grads = grads, []
     descs = (Nf4Desc * n)()
-    grads = []
     for i, (packed, codes, consts, A, B) in enumerate(layers):
         _need_cuda(packed, codes, consts, A, B, dYs[i], U_ins[i], name="qlora_linear_bwd_multi")
+        _check_out(U_ins[i], (T, r), torch.float32, f"U_ins[{i}]")
         descs[i] = _stored_desc(packed, codes, consts, tables[i])
-        dA = torch.empty((r, d_in), dtype=torch.float32, device=X.device) if r > 0 else None
-        dB = torch.empty((packed.shape[0], r), dtype=torch.float32, device=X.device) if r > 0 else None
+        if given is not None and r > 0:
+            dA, dB = given[i]
+            _check_out(dA, (r, d_in), torch.float32, f"grads[{i}] dA")
+            _check_out(dB, (packed.shape[0], r), torch.float32, f"grads[{i}] dB")
+            if dA is None or dB is None:
+                raise ValueError(f"grads[{i}]: dA and dB are required")
+            _need_cuda(dA, dB, name="qlora_linear_bwd_multi")
+        else:
+            dA = torch.empty((r, d_in), dtype=torch.float32, device=X.device) if r > 0 else None
+            dB = torch.empty((packed.shape[0], r), dtype=torch.float32, device=X.device) if r > 0 else None
         grads.append((dA, dB))
-    _need_cuda(X, name="qlora_linear_bwd_multi")
-    dX = torch.empty((T, d_in), dtype=torch.bfloat16, device=X.device) if want_dx else None
+    _need_cuda(X, dX, name="qlora_linear_bwd_multi")
+    _check_out(dX, (T, d_in), torch.bfloat16, "dX")
+    if dX is None and want_dx:
+        dX = torch.empty((T, d_in), dtype=torch.bfloat16, device=X.device)
     n_b = ctypes.c_size_t()
     _check(lib().qlora_multi_bwd_workspace_bytes(n, descs, int(T), int(r), ctypes.byref(n_b)),
            "qlora_multi_bwd_workspace_bytes")

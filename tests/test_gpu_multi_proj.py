@@ -156,3 +156,30 @@ def test_backward_of_layers_sharing_x(T):
     ex = normwise_err(host_bf16_to_f64(dX), want_dx)
     say(f"  dX {ex:.2e}")
     assert ex <= TOL
+
+
+@pytest.mark.parametrize("T", [4, 40])
+def test_backward_caller_buffers_match_allocated_outputs(T):
+    """dX, dA and dB given by the caller (filled with 0xFF bytes first) are
+    overwritten with what the allocating call returns, bit for bit."""
+    import nf4_bit_quantized_amd as q
+    import torch
+    K, r, alpha = 320, 8, 16.0
+    say(f"multi backward caller buffers T={T}")
+    Xb, layers = _layers([192, 64, 64], K, T, r, seed=170)
+    X = dev_bf16(Xb)
+    devs = [l["dev"] for l in layers]
+    dYs = [dev_bf16(workloads.layer_inputs(d[0].shape[0], K, T, 1, 180 + i)["dY"]) for i, d in enumerate(devs)]
+    Us = [o[1] for o in q.qlora_linear_fwd_multi(devs, X, alpha)]
+    dX_ref, g_ref = q.qlora_linear_bwd_multi(devs, X, alpha, dYs, U_ins=Us)
+    dX = torch.full((T, K), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    grads = [(torch.full((r, K), -1, dtype=torch.int32, device="cuda").view(torch.float32),
+              torch.full((d[0].shape[0], r), -1, dtype=torch.int32, device="cuda").view(torch.float32)) for d in devs]
+    dX_got, g_got = q.qlora_linear_bwd_multi(devs, X, alpha, dYs, U_ins=Us, dX=dX, grads=grads)
+    torch.cuda.synchronize()
+    assert dX_got.data_ptr() == dX.data_ptr()
+    assert torch.equal(dX_ref.view(torch.int16), dX.view(torch.int16))
+    for (dAr, dBr), (dAg, dBg), (dAb, dBb) in zip(g_ref, g_got, grads):
+        assert dAg.data_ptr() == dAb.data_ptr() and dBg.data_ptr() == dBb.data_ptr()
+        assert torch.equal(dAr.view(torch.int32), dAg.view(torch.int32))
+        assert torch.equal(dBr.view(torch.int32), dBg.view(torch.int32))
