@@ -501,6 +501,7 @@ def qlora_dequantize_nf4(packed, codes, consts, W_hat=None, stream=None, table: 
     import torch
     d_out, d_in = packed.shape[0], packed.shape[1] * 2
     _need_cuda(packed, codes, consts, W_hat, name="qlora_dequantize_nf4")
+    _check_out(W_hat, (d_out, d_in), torch.bfloat16, "W_hat")
     if W_hat is None:
         W_hat = torch.empty((d_out, d_in), dtype=torch.bfloat16, device=packed.device)
     d = _stored_desc(packed, codes, consts, table)
@@ -520,6 +521,7 @@ def qlora_merge_lora(packed, codes, consts, A, B, alpha: float, W_merged=None, s
     for t, nm in ((A, "A"), (B, "B")):
         if t.dtype != torch.bfloat16:
             raise ValueError(f"{nm} must be bfloat16")
+    _check_out(W_merged, (d_out, d_in), torch.bfloat16, "W_merged")
     if W_merged is None:
         W_merged = torch.empty((d_out, d_in), dtype=torch.bfloat16, device=packed.device)
     d = _stored_desc(packed, codes, consts, table)
