@@ -121,6 +121,17 @@ def _nearest_level(x: np.ndarray, levels: np.ndarray, chunk: int = 1 << 20) -> n
     return out
 
 
+def _normalize(blocks: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Step 4: x = fl32(w / s_b) for every value of a block, by IEEE float32
+    division (the normalized value X_block / scale of [QLoRA-入门到精通]
+    §3(1)); rows of ``blocks`` are blocks, ``scales`` their absmax.  A block
+    whose scale is 0 (all zero) gives x = 0."""
+    safe = np.where(scales > 0, scales, np.float32(1.0)).astype(np.float32)
+    x = (blocks / safe[:, None]).astype(np.float32)
+    x[scales == 0] = np.float32(0.0)
+    return x
+
+
 def quantize(W, levels: Optional[np.ndarray] = None, blocksize: int = 64,
              dq_blocksize: int = 256) -> Quantized:
     """Blockwise absmax quantization of a float32 weight to 4-bit level indices.
@@ -142,9 +153,7 @@ def quantize(W, levels: Optional[np.ndarray] = None, blocksize: int = 64,
     # step 3: absmax scale per block (float32, exact)
     scales = np.max(np.abs(blocks), axis=1).astype(np.float32)
     # step 4: normalize by IEEE float32 division; all-zero block -> x = 0
-    safe = np.where(scales > 0, scales, np.float32(1.0)).astype(np.float32)
-    x = (blocks / safe[:, None]).astype(np.float32)
-    x[scales == 0] = np.float32(0.0)
+    x = _normalize(blocks, scales)
     # step 5: nearest level index
     q = _nearest_level(x, levels).reshape(-1)
     # step 6: two indices per byte, element 2j in the high nibble

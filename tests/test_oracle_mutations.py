@@ -95,3 +95,20 @@ def test_transposed_operand_in_db_is_caught(monkeypatch):
 def test_dropped_lora_branch_in_forward_is_caught(monkeypatch):
     monkeypatch.setattr(lora, "forward", lambda W_hat, X, A, B, alpha, r: (np.asarray(X) @ np.asarray(W_hat).T, None))
     _fails(pins_lora.test_sales_table_rank1_and_rank2)
+
+
+def test_reciprocal_multiply_normalize_is_caught(monkeypatch):
+    def bad(blocks, scales):
+        safe = np.where(scales > 0, scales, np.float32(1.0)).astype(np.float32)
+        inv = (np.float32(1.0) / safe).astype(np.float32)
+        x = (blocks * inv[:, None]).astype(np.float32)
+        x[scales == 0] = np.float32(0.0)
+        return x
+    monkeypatch.setattr(nf4, "_normalize", bad)
+    with np.errstate(all="ignore"):
+        _fails(pins_nf4.test_normalize_is_the_exact_ieee_quotient_at_many_scales, "nf4")
+        _fails(pins_nf4.test_normalize_is_the_exact_ieee_quotient_at_many_scales, "uniform")
+        # caught by rounding alone: ordinary scales, where 1/s stays finite
+        for s in (1.52, 0.0371, 123.456):
+            monkeypatch.setattr(pins_nf4, "NORMALIZE_SCALES", (s,))
+            _fails(pins_nf4.test_normalize_is_the_exact_ieee_quotient_at_many_scales, "nf4")

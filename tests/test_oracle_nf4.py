@@ -154,6 +154,84 @@ def test_exact_tie_goes_to_lower_index():
 
 
 # --------------------------------------------------------------------------
+# Step 4: normalize, x = fl32(w / s), pinned by exact rationals
+# --------------------------------------------------------------------------
+
+def _fl32_rne(q: Fraction) -> Fraction:
+    """The float32 nearest to the rational q, ties to even (IEEE 754
+    round-to-nearest-even written out: 24-bit significands, exponents down to
+    -126, then the fixed subnormal spacing 2^-149)."""
+    if q == 0:
+        return Fraction(0)
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    elif Fraction(2) ** (e + 1) <= a:
+        e += 1
+    assert Fraction(2) ** e <= a < Fraction(2) ** (e + 1)
+    ulp = Fraction(2) ** (max(e, -126) - 23)
+    m = a / ulp
+    n = m.numerator // m.denominator
+    rem = m - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return (n * ulp) if q > 0 else -(n * ulp)
+
+
+# fp32 block scales: ordinary, between powers of two, tiny normal, subnormal, huge
+NORMALIZE_SCALES = (1.52, 0.0371, 7.77e-6, 123.456, 2.3e-38, 1.0e-40, 3.0e38)
+
+
+def normalize_walk_blocks(T):
+    """Blocks of 64 whose first value is the absmax s and whose other values
+    walk +-64 float32 steps across each threshold of T times s."""
+    rows, scales = [], []
+    for s in NORMALIZE_SCALES:
+        s32 = np.float32(s)
+        vals = []
+        for k in range(15):
+            mid = (Fraction(float(T[k])) + Fraction(float(T[k + 1]))) / 2
+            c = np.float32(float(_fl32_rne(mid * Fraction(float(s32)))))
+            lo = hi = c
+            vals.append(c)
+            for _ in range(64):
+                lo = np.nextafter(lo, np.float32(-np.inf), dtype=np.float32)
+                hi = np.nextafter(hi, np.float32(np.inf), dtype=np.float32)
+                vals.extend([lo, hi])
+        vals = [v for v in vals if abs(float(v)) <= float(s32)]
+        for i in range(0, len(vals), 63):
+            chunk = vals[i:i + 63]
+            chunk = chunk + [np.float32(0.0)] * (63 - len(chunk))
+            rows.append([s32] + chunk)
+            scales.append(s32)
+    return np.array(rows, dtype=np.float32), np.array(scales, dtype=np.float32)
+
+
+@pytest.mark.parametrize("table", ["nf4", "uniform"])
+def test_normalize_is_the_exact_ieee_quotient_at_many_scales(table):
+    """[QLoRA-入门到精通] §3(1) normalizes a block as X_block / scale.  For
+    block scales that are not powers of two (and for tiny, subnormal and huge
+    ones), values within 64 float32 steps of every threshold times s are
+    quantized; each index must be the nearest level (ties to the lower index)
+    of the correctly rounded quotient, formed here from the exact rational
+    w / s.  A reciprocal-multiply normalize, w * fl32(1 / s), moves some of
+    these values across a threshold."""
+    T = nf4.nf4_levels() if table == "nf4" else nf4.uniform_levels()
+    W, scales = normalize_walk_blocks(T)
+    Q = nf4.quantize(W, levels=T, blocksize=64, dq_blocksize=0)
+    assert np.array_equal(Q.scales, scales)
+    got = Q.q.reshape(W.shape)
+    Tq = [Fraction(float(t)) for t in T]
+    for b in range(W.shape[0]):
+        s = Fraction(float(scales[b]))
+        for e in range(64):
+            x = _fl32_rne(Fraction(float(W[b, e])) / s)
+            want = min(range(16), key=lambda i: (abs(x - Tq[i]), i))
+            assert got[b, e] == want, (table, float(scales[b]), float(W[b, e]), int(got[b, e]), want)
+
+
+# --------------------------------------------------------------------------
 # Whole quantizer: blocking, scales, packing, zero blocks
 # --------------------------------------------------------------------------
 
