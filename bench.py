@@ -1,20 +1,27 @@
 #!/usr/bin/env python3
 """Throughput of the QLoRA NF4 linear layer on one MI355X.
 
-One step = one pass of the whole hot path over one batch of synthetic input:
-NF4 quantization of the fp32 base weight (block absmax, nearest level, nibble
-packing, 8-bit double quantization of the scales), the forward (on-chip
-restore, base GEMM, fused rank-r term) and the backward (dX through the
-transposed restore, dA, dB).  Inputs are resident in HBM before timing.
+Headline workload: the share of a 65B-class model that one GPU trains, 8
+layers, each with the query, key, value and output projections (8192 x 8192)
+and the gate, up (8192 -> 22016) and down (22016 -> 8192) projections, every
+base weight blockwise NF4 (64-weight blocks, 8-bit scale codes per 256
+blocks), 4096 tokens, rank 64, alpha 16.  One step = the forward and the
+backward (dX, dA, dB; no gradient for the frozen weight) of all 56 linears,
+with the inputs already resident in HBM: per layer, one call for the three
+projections that share the attention input and one for the two that share
+the MLP input, the backward in reverse layer order.  The weights are
+quantized once, before timing (their quantization is reported on its own).
 
-Default workload: attention-projection-shaped layer, W 4096 x 4096, 2048
-tokens, r = 16, alpha = 32 (seeded N(0, 0.02) weights; no model is loaded).
-Metric: fwd+bwd algorithmic TFLOP/s = (4 T K N + 6 T r (K + N)) per step /
-step time; the quantization has no flops but its time is inside the step.
+Metric: algorithmic TFLOP/s = sum over the linears of 4 T K N + 6 T r (K + N)
+per step / step time (no flops are counted for the restore or for the dW
+product that is never formed).
 
-Prints ONE JSON line.  Extra fields: per-kernel times from the library's
-hipEvent trace, the roofline of the dominant kernel, the oracle timed on the
-host cores (cpu_baseline), and packed-weight GB/s of the few-token forward.
+Prints ONE JSON line.  Extra fields: the roofline of the dominant kernel
+(timed with hipEvents attached to its own dispatches inside the timed
+region), a per-kernel table from a second pass, the other workloads (the
+attention-shaped layer, the MLP set of a 7B-class layer, the few-token
+forward's packed-weight GB/s, exports, optimizer, dropout), and the oracle
+timed on the host cores (cpu_baseline, cpu_baselines).
 """
 
 import argparse
@@ -30,21 +37,17 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 
-# HBM bytes per launch of the two large kernels on the attention-shaped step,
-# from two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE,
-# KiB per dispatch, averaged over the dispatches of each kernel), scaled by
-# what the same counters read for a plain 256 MiB fill and copy in the same
-# runs (--copy-calibration 256): the copy's FETCH_SIZE reads 131090.9 KiB for
-# 262144 KiB moved (scale 1.99973), the fill's WRITE_SIZE reads exactly
-# 262144 KiB (scale 1).  Valid only for the kernel sources they were taken
-# on (sha256 of the files below); reported as null once those change.
+# HBM bytes per launch of the dominant kernel on the headline step, from two
+# rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, KiB per
+# dispatch, averaged over that kernel's dispatches), scaled by what the same
+# counters read for a plain fill and copy of known size in the same runs
+# (--copy-calibration).  Valid only for the kernel sources they were taken on
+# (sha256 of the files below); reported as null once those change.
 TRAFFIC_SOURCES = ("fused_gemm.hip", "fused.hpp", "restore.hpp", "common.hpp")
 TRAFFIC = {
-    "sha256": "fa541814e1aa5d9ef702c1df6eaf09ea4b58889738e205a5ea9722a9b7c99008",
-    "fetch_scale": 262144.0 / 131090.9,
+    "sha256": None,
+    "fetch_scale": 1.0,
     "write_scale": 1.0,
-    "fwd_gemm": {"fetch_kib": 36005.5, "write_kib": 16384.0},
-    "dx_gemm": {"fetch_kib": 35835.9, "write_kib": 16384.0},
 }
 
 
@@ -55,7 +58,7 @@ def traffic_bytes(kernel):
     for f in TRAFFIC_SOURCES:
         with open(os.path.join(ROOT, "nf4_bit_quantized_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
-    if h.hexdigest() != TRAFFIC["sha256"] or kernel not in TRAFFIC:
+    if TRAFFIC["sha256"] is None or h.hexdigest() != TRAFFIC["sha256"] or kernel not in TRAFFIC:
         return None
     t = TRAFFIC[kernel]
     return int(round((t["fetch_kib"] * TRAFFIC["fetch_scale"] + t["write_kib"] * TRAFFIC["write_scale"]) * 1024))
@@ -64,14 +67,13 @@ def traffic_bytes(kernel):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--layers", type=int, default=8, help="layers of the 65B-class stack (8 = the full share)")
+    ap.add_argument("--headline-only", action="store_true", help="skip the other workloads' sections")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-decode", action="store_true", help="skip the few-token packed-weight GB/s section")
-    ap.add_argument("--mlp", action="store_true",
-                    help="also time the MLP shapes of a 7B-class layer (fused products of other shapes; off by "
-                         "default so that the kernel trace of the default run holds only the roofline shape)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget for the oracle timing")
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="time the oracle on every workload's plan (minutes of host time), not the bounded set")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the JSON line, fill then copy a buffer of this many MiB (known HBM bytes "
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -94,38 +96,247 @@ def layer_flops(T, K, N, r):
     return fwd, bwd
 
 
-def cpu_baseline(inp, lin, budget_s):
-    """The oracle (numpy) on the same workload: quantize + dequant + fwd + bwd."""
-    import numpy as np
-    from threadpoolctl import threadpool_info
-    from oracle import lora as olora
-    from oracle import nf4 as onf4
-    from oracle.bf16 import bits_to_float
+def fused_flops(T, K, N, r):
+    """Algorithmic flops of the two fused products of one linear: the forward
+    (X W_hat^T plus the rank-r term U B^T) and dX (dY W_hat plus G A)."""
+    return 2 * T * K * N + 2 * T * r * N, 2 * T * N * K + 2 * T * r * K
 
-    X, A, B, dY = (bits_to_float(inp[k]) for k in ("X", "A", "B", "dY"))
-    times = []
-    t_start = time.perf_counter()
-    while True:
-        t0 = time.perf_counter()
-        Q = onf4.quantize(inp["W"])
-        W_hat = onf4.dequantize(Q).astype(np.float64)
-        olora.forward(W_hat, X, A, B, lin.alpha, lin.r)
-        olora.backward(W_hat, X, A, B, dY, lin.alpha, lin.r)
-        times.append(time.perf_counter() - t0)
-        if time.perf_counter() - t_start > budget_s or len(times) >= 20:
-            break
-    fwd, bwd = layer_flops(lin.T, lin.d_in, lin.d_out, lin.r)
-    per_step = sum(times) / len(times)
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {
-        "value": round((fwd + bwd) / per_step / 1e12, 4),
-        "unit": "TFLOP/s",
-        "cores": int(threads),
-        "kind": "oracle",
-        "sample": (f"the full {lin.name} step (quantize {lin.d_out}x{lin.d_in}, dequantize, float64 fwd+bwd "
-                   f"at T={lin.T}, r={lin.r}), {len(times)} repetitions, {per_step:.3f} s each; "
-                   f"host threads available {len(os.sched_getaffinity(0))}"),
+
+# ---------------------------------------------------------------------------
+# Headline: the 65B-class layer stack share
+# ---------------------------------------------------------------------------
+
+def stack_section(args):
+    """Forward + backward of the 65B-class stack share at 4096 tokens.
+
+    Synthetic inputs with the recipe's distributions (W ~ N(0, 0.02) fp32,
+    X and dY ~ N(0, 1), A ~ N(0, 1/r), B ~ N(0, 0.01), bf16 rounded to
+    nearest even), drawn on the GPU by torch's seeded generator (seed
+    100 * layer + projection), since drawing 6.5e9 weights on the host would
+    take minutes.  Each weight is quantized by the library, then its fp32
+    copy is freed."""
+    import torch
+    import nf4_bit_quantized_amd as q
+    import workloads
+
+    lins = workloads.stack_65b(args.layers)
+    T, r, alpha = lins[0].T, lins[0].r, lins[0].alpha
+    dev = "cuda"
+    gen = torch.Generator(device=dev)
+    torch.cuda.reset_peak_memory_stats()
+    qe0, qe1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    quant_ms = 0.0
+    quant_bytes = 0
+    layers = []
+    for li in range(args.layers):
+        projs = {}
+        for lin in lins[li * 7:(li + 1) * 7]:
+            name = lin.name.split(".")[1]
+            gen.manual_seed(lin.seed)
+            W = torch.randn(lin.d_out, lin.d_in, generator=gen, device=dev) * 0.02
+            pk, cd, cs = q.qlora_quantize_nf4(W)            # allocation + first touch (untimed)
+            torch.cuda.synchronize()
+            qe0.record()
+            q.qlora_quantize_nf4(W, pk, cd, cs)
+            qe1.record()
+            torch.cuda.synchronize()
+            quant_ms += qe0.elapsed_time(qe1)
+            quant_bytes += W.numel() * 4 + pk.numel() + cd.numel() + cs.numel() * 4
+            del W
+            A = (torch.randn(r, lin.d_in, generator=gen, device=dev) / r).to(torch.bfloat16)
+            B = (torch.randn(lin.d_out, r, generator=gen, device=dev) * 0.01).to(torch.bfloat16)
+            dY = torch.randn(T, lin.d_out, generator=gen, device=dev).to(torch.bfloat16)
+            projs[name] = dict(lin=lin, w=(pk, cd, cs, A, B), dY=dY,
+                               Y=torch.empty((T, lin.d_out), dtype=torch.bfloat16, device=dev),
+                               U=torch.empty((T, r), dtype=torch.float32, device=dev),
+                               dA=torch.empty((r, lin.d_in), dtype=torch.float32, device=dev),
+                               dB=torch.empty((lin.d_out, r), dtype=torch.float32, device=dev))
+        gen.manual_seed(100 * li + 99)
+        groups = []
+        for names, d_in in ((("q", "k", "v"), 8192), (("o",), 8192), (("gate", "up"), 8192), (("down",), 22016)):
+            groups.append(dict(names=names,
+                               X=torch.randn(T, d_in, generator=gen, device=dev).to(torch.bfloat16),
+                               dX=torch.empty((T, d_in), dtype=torch.bfloat16, device=dev)))
+        layers.append((projs, groups))
+
+    shapes = [(8192, 8192)] * 3 + [(22016, 8192)] * 2 + [(8192, 22016)]
+    ws_bytes = max(q.qlora_multi_fwd_workspace_bytes([(8192, 8192)] * 3, T, r),
+                   q.qlora_multi_bwd_workspace_bytes([(8192, 8192)] * 3, T, r),
+                   q.qlora_multi_fwd_workspace_bytes([(22016, 8192)] * 2, T, r),
+                   q.qlora_multi_bwd_workspace_bytes([(22016, 8192)] * 2, T, r),
+                   *[q.qlora_fwd_workspace_bytes(o, i, T, r) for o, i in shapes],
+                   *[q.qlora_bwd_workspace_bytes(o, i, T, r) for o, i in shapes])
+    ws = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device=dev)
+
+    def fwd_group(projs, g):
+        P = [projs[n] for n in g["names"]]
+        if len(P) == 1:
+            p = P[0]
+            q.qlora_linear_fwd(*p["w"][:3], g["X"], p["w"][3], p["w"][4], alpha, Y=p["Y"], U_out=p["U"],
+                               workspace=ws)
+        else:
+            q.qlora_linear_fwd_multi([p["w"] for p in P], g["X"], alpha, workspace=ws,
+                                     outs=[(p["Y"], p["U"]) for p in P])
+
+    def bwd_group(projs, g):
+        P = [projs[n] for n in g["names"]]
+        if len(P) == 1:
+            p = P[0]
+            q.qlora_linear_bwd(*p["w"][:3], g["X"], p["w"][3], p["w"][4], alpha, p["dY"], U_in=p["U"], dX=g["dX"],
+                               dA=p["dA"], dB=p["dB"], workspace=ws)
+        else:
+            q.qlora_linear_bwd_multi([p["w"] for p in P], g["X"], alpha, [p["dY"] for p in P],
+                                     U_ins=[p["U"] for p in P], workspace=ws, dX=g["dX"],
+                                     grads=[(p["dA"], p["dB"]) for p in P])
+
+    def step():
+        for projs, groups in layers:
+            for g in groups:
+                fwd_group(projs, g)
+        for projs, groups in reversed(layers):
+            for g in reversed(groups):
+                bwd_group(projs, g)
+
+    step_flops = sum(sum(layer_flops(l.T, l.d_in, l.d_out, l.r)) for l in lins)
+    kflops = {"fwd_gemm": 0, "dx_gemm": 0}
+    for l in lins:
+        f, d = fused_flops(l.T, l.d_in, l.d_out, l.r)
+        kflops["fwd_gemm"] += f
+        kflops["dx_gemm"] += d
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # timed region: exactly `steps` steps; the library attaches hipEvents to
+    # the dispatches of the two fused products (on the launch stream)
+    q.qlora_trace_read(reset=True)
+    q.qlora_trace_select({"fwd_gemm", "dx_gemm"})
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    q.qlora_trace_enable(False)
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    kt = q.qlora_trace_read(reset=True)
+    log(f"stack: {ms_per_step:.3f} ms per step")
+
+    # per-kernel breakdown: a second, untimed pass with every launch bracketed
+    kpass = 2
+    q.qlora_trace_enable(True)
+    for _ in range(kpass):
+        step()
+    torch.cuda.synchronize()
+    q.qlora_trace_enable(False)
+    kt_all = q.qlora_trace_read(reset=True)
+    total_k = sum(ms for (_, ms) in kt_all.values())
+    kernels = {name: {"launches_per_step": n / kpass, "avg_us": round(ms / n * 1e3, 2),
+                      "ms_per_step": round(ms / kpass, 3), "share": round(ms / total_k, 4) if total_k else None}
+               for name, (n, ms) in kt_all.items()}
+
+    fused = {}
+    for k in ("fwd_gemm", "dx_gemm"):
+        n, ms = kt.get(k, (0, float("nan")))
+        if n == 0:
+            continue
+        flops = kflops[k] * args.steps
+        fused[k] = {"launches": n, "avg_launch_us": round(ms / n * 1e3, 2),
+                    "flops_per_launch": flops // n,
+                    "achieved_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+                    "frac": round(flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    dom = max(fused, key=lambda k: kt[k][1])
+    d = fused[dom]
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": d["achieved_tflops"], "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": d["frac"], "traffic": traffic_bytes(dom),
+                "avg_launch_us": d["avg_launch_us"], "flops_per_launch": d["flops_per_launch"],
+                "launch_note": "flops_per_launch and avg_launch_us average over the kernel's launches in the "
+                               "timed region (three weight shapes); achieved = their flops / their time"}
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+    out = {
+        "ms_per_step": ms_per_step, "value": value, "step_flops": step_flops, "roofline": roofline,
+        "fused_products": fused, "kernels": kernels,
+        "kernels_note": f"from a second pass of {kpass} steps with every launch bracketed by hipEvents",
+        "quantize_stack": {"weights": sum(l.d_out * l.d_in for l in lins), "bytes": quant_bytes,
+                           "ms": round(quant_ms, 3),
+                           "GBps": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1),
+                           "frac_hbm": round(quant_bytes / (quant_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                           "note": "each weight quantized once from fp32, outside the timed step"},
+        "peak_hbm_allocated_bytes": torch.cuda.max_memory_allocated(),
+        "packed_weight_bytes": sum(p["w"][0].numel() + p["w"][1].numel() + p["w"][2].numel() * 4
+                                   for projs, _ in layers for p in projs.values()),
+        "T": T, "r": r, "alpha": alpha, "layers": args.layers,
     }
+    del layers, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+# ---------------------------------------------------------------------------
+# The attention-shaped layer (W 4096 x 4096, 2048 tokens, r = 16)
+# ---------------------------------------------------------------------------
+
+def attn_section(lin, steps):
+    """fwd + bwd of the attention-shaped layer (quantization outside the step,
+    reported beside it)."""
+    import torch
+    import nf4_bit_quantized_amd as q
+    import workloads
+
+    T, K, N, r, alpha = lin.T, lin.d_in, lin.d_out, lin.r, lin.alpha
+    inp = workloads.layer_inputs(N, K, T, r, lin.seed)
+    W = torch.from_numpy(inp["W"]).cuda()
+    X, A, B, dY = (bf16_dev(inp[k]) for k in ("X", "A", "B", "dY"))
+    packed, codes, consts = q.qlora_quantize_nf4(W)
+    Y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+    U = torch.empty((T, r), dtype=torch.float32, device="cuda")
+    dX = torch.empty((T, K), dtype=torch.bfloat16, device="cuda")
+    dA = torch.empty((r, K), dtype=torch.float32, device="cuda")
+    dB = torch.empty((N, r), dtype=torch.float32, device="cuda")
+    wsf = torch.empty(max(1, q.qlora_fwd_workspace_bytes(N, K, T, r)), dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(max(1, q.qlora_bwd_workspace_bytes(N, K, T, r)), dtype=torch.uint8, device="cuda")
+
+    def step():
+        q.qlora_linear_fwd(packed, codes, consts, X, A, B, alpha, Y=Y, U_out=U, workspace=wsf)
+        q.qlora_linear_bwd(packed, codes, consts, X, A, B, alpha, dY, U_in=U, dX=dX, dA=dA, dB=dB, workspace=wsb)
+
+    for _ in range(5):
+        step()
+        q.qlora_quantize_nf4(W, packed, codes, consts)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    q.qlora_trace_read(reset=True)
+    q.qlora_trace_enable(True)
+    for _ in range(steps):
+        step()
+        q.qlora_quantize_nf4(W, packed, codes, consts)
+    torch.cuda.synchronize()
+    q.qlora_trace_enable(False)
+    kt = q.qlora_trace_read(reset=True)
+    fwd_f, bwd_f = layer_flops(T, K, N, r)
+    out = {"d_out": N, "d_in": K, "T": T, "r": r, "alpha": alpha, "fwd_bwd_ms": round(ms, 4),
+           "tflops": round((fwd_f + bwd_f) / (ms * 1e-3) / 1e12, 1),
+           "frac_mfma": round((fwd_f + bwd_f) / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+           "kernels_us": {k: round(v[1] / v[0] * 1e3, 2) for k, v in kt.items()}}
+    fl = dict(zip(("fwd_gemm", "dx_gemm"), fused_flops(T, K, N, r)))
+    for k in fl:
+        if k in kt:
+            out[f"{k}_frac_mfma"] = round(fl[k] / (kt[k][1] / kt[k][0] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
+    qn, qms = kt.get("nf4_quantize", (1, float("nan")))
+    n_c, n_k = codes.numel(), consts.numel() * 4
+    q_bytes = N * K * 4 + N * K // 2 + n_c + n_k
+    out["quantize"] = {"avg_us": round(qms / qn * 1e3, 2), "bytes": q_bytes,
+                       "GBps": round(q_bytes / (qms / qn * 1e-3) / 1e9, 1),
+                       "frac_hbm": round(q_bytes / (qms / qn * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    log("attn", out)
+    return out
 
 
 def decode_section(steps, warmup):
@@ -471,6 +682,87 @@ def adamw_section(steps):
     return out
 
 
+
+# ---------------------------------------------------------------------------
+# The oracle on the host cores
+# ---------------------------------------------------------------------------
+
+def _threads():
+    from threadpoolctl import threadpool_info
+    return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
+
+
+def time_oracle_linear(lin, T, quantize=False, backward=True):
+    """Seconds of the oracle on one linear of the recipe: optionally its
+    quantization, then the restore of the weight and the float64 forward
+    (and backward) at T tokens."""
+    import numpy as np
+    import workloads
+    from oracle import lora as olora
+    from oracle import nf4 as onf4
+    from oracle.bf16 import bits_to_float
+
+    inp = workloads.layer_inputs(lin.d_out, lin.d_in, T, lin.r, lin.seed, with_dy=backward)
+    t0 = time.perf_counter()
+    Q = onf4.quantize(inp["W"])
+    t_quant = time.perf_counter() - t0
+    X, A, B = (bits_to_float(inp[k]) for k in ("X", "A", "B"))
+    t0 = time.perf_counter()
+    W_hat = onf4.dequantize(Q).astype(np.float64)
+    olora.forward(W_hat, X, A, B, lin.alpha, lin.r)
+    if backward:
+        olora.backward(W_hat, X, A, B, bits_to_float(inp["dY"]), lin.alpha, lin.r)
+    t_layer = time.perf_counter() - t0
+    fwd, bwd = layer_flops(T, lin.d_in, lin.d_out, lin.r)
+    flops = fwd + (bwd if backward else 0)
+    out = {"layer_s": round(t_layer, 3), "tflops": round(flops / t_layer / 1e12, 4)}
+    if quantize:
+        out["quantize_s"] = round(t_quant, 3)
+    return out
+
+
+def cpu_baseline_headline():
+    """The oracle on a bounded sample of the headline workload: the query
+    projection of layer 0 (8192 x 8192) at all 4096 tokens, restore + forward
+    + backward in float64, as TFLOP/s (the headline's unit)."""
+    import workloads
+    lin = workloads.stack_65b(1)[0]
+    t = time_oracle_linear(lin, lin.T)
+    return {
+        "value": t["tflops"], "unit": "TFLOP/s", "cores": _threads(), "kind": "oracle",
+        "sample": (f"one of the 56 linears of the stack: layer 0's query projection {lin.d_out}x{lin.d_in}, "
+                   f"{lin.T} tokens, r={lin.r}: restore of the NF4 weight + float64 forward + backward, "
+                   f"{t['layer_s']} s; the stack's step is 56 such linears (3 weight shapes); "
+                   f"host threads available {len(os.sched_getaffinity(0))}"),
+    }
+
+
+def cpu_baselines(full):
+    """The oracle timing plan per workload.  By default a bounded set (about
+    half a minute of host time); with --cpu-full every planned case,
+    including the few-token forward at each T and one layer of the stack
+    (reported x8 as the whole share, extrapolated)."""
+    import workloads
+    out = {"cores": _threads(), "host_threads_available": len(os.sched_getaffinity(0))}
+    (p,) = workloads.parity_256()
+    out["parity_256"] = time_oracle_linear(p, p.T, quantize=True)
+    (a,) = workloads.attn_4096()
+    out["attn_4096"] = time_oracle_linear(a, a.T, quantize=True)
+    mlp = workloads.mlp_llama7b()
+    out["mlp_llama7b"] = {l.name: time_oracle_linear(l, l.T, quantize=True) for l in (mlp if full else mlp[:1])}
+    if full:
+        out["decode_70b"] = {f"{l.name}": time_oracle_linear(l, T, backward=False)
+                             for T in (1, 4, 16) for l in workloads.decode_70b(T)}
+        layer = workloads.stack_65b(1)
+        per = {l.name: time_oracle_linear(l, l.T) for l in layer}
+        s = sum(v["layer_s"] for v in per.values())
+        flops = sum(sum(layer_flops(l.T, l.d_in, l.d_out, l.r)) for l in layer)
+        out["stack_65b"] = {"one_layer": per, "one_layer_s": round(s, 2),
+                            "eight_layers_s_extrapolated": round(8 * s, 2),
+                            "tflops": round(flops / s / 1e12, 4)}
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -478,123 +770,58 @@ def main():
               "(sharding the layer over several GPUs is not part of this library).", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
-    import nf4_bit_quantized_amd as q
     import workloads
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
-    (lin,) = workloads.attn_4096()
-    T, K, N, r, alpha = lin.T, lin.d_in, lin.d_out, lin.r, lin.alpha
-    log(f"workload {lin}")
-    inp = workloads.layer_inputs(N, K, T, r, lin.seed)
-
-    W = torch.from_numpy(inp["W"]).cuda()
-    X, A, B, dY = (bf16_dev(inp[k]) for k in ("X", "A", "B", "dY"))
-    n_p, n_c, n_k = q.qlora_nf4_sizes(N, K)
-    packed = torch.empty((N, K // 2), dtype=torch.uint8, device="cuda")
-    codes = torch.empty(n_c, dtype=torch.uint8, device="cuda")
-    consts = torch.empty(n_k // 4, dtype=torch.float32, device="cuda")
-    Y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
-    U = torch.empty((T, r), dtype=torch.float32, device="cuda")
-    dX = torch.empty((T, K), dtype=torch.bfloat16, device="cuda")
-    dA = torch.empty((r, K), dtype=torch.float32, device="cuda")
-    dB = torch.empty((N, r), dtype=torch.float32, device="cuda")
-    wsf = torch.empty(max(1, q.qlora_fwd_workspace_bytes(N, K, T, r)), dtype=torch.uint8, device="cuda")
-    wsb = torch.empty(max(1, q.qlora_bwd_workspace_bytes(N, K, T, r)), dtype=torch.uint8, device="cuda")
-
-    def step():
-        q.qlora_quantize_nf4(W, packed, codes, consts)
-        q.qlora_linear_fwd(packed, codes, consts, X, A, B, alpha, Y=Y, U_out=U, workspace=wsf)
-        q.qlora_linear_bwd(packed, codes, consts, X, A, B, alpha, dY, U_in=U, dX=dX, dA=dA, dB=dB, workspace=wsb)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # timed region: exactly K steps; the library brackets the two large kernels
-    # (forward and dX products) with hipEvents on the launch stream
-    q.qlora_trace_read(reset=True)
-    q.qlora_trace_select({"fwd_gemm", "dx_gemm"})
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(args.steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    q.qlora_trace_enable(False)
-    ms_per_step = e0.elapsed_time(e1) / args.steps
-    kt = q.qlora_trace_read(reset=True)
-
-    # per-kernel breakdown: a second, untimed pass of K steps with every launch bracketed
-    q.qlora_trace_enable(True)
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    q.qlora_trace_enable(False)
-    kt_all = q.qlora_trace_read(reset=True)
-
-    fwd_f, bwd_f = layer_flops(T, K, N, r)
-    value = (fwd_f + bwd_f) / (ms_per_step * 1e-3) / 1e12
-
-    kernels = {name: {"launches": n, "avg_us": round(ms / n * 1e3, 2), "share": None}
-               for name, (n, ms) in kt_all.items()}
-    total_k = sum(ms for (_, ms) in kt_all.values())
-    for name, (n, ms) in kt_all.items():
-        kernels[name]["share"] = round(ms / total_k, 4) if total_k > 0 else None
-    # algorithmic work per launch of the two big kernels
-    kernel_flops = {"fwd_gemm": 2 * T * K * N + 2 * T * r * N, "dx_gemm": 2 * T * N * K + 2 * T * r * K}
-    dom = max(kernel_flops, key=lambda k: kt.get(k, (1, 0.0))[1])
-    dn, dms = kt.get(dom, (1, float("nan")))
-    dom_avg_s = dms / dn * 1e-3
-    achieved = kernel_flops[dom] / dom_avg_s / 1e12
-    roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": traffic_bytes(dom),
-                "avg_launch_us": round(dom_avg_s * 1e6, 2), "flops_per_launch": kernel_flops[dom]}
-    qn, qms = kt_all.get("nf4_quantize", (1, float("nan")))
-    q_bytes = N * K * 4 + N * K // 2 + n_c + n_k
-    quant = {"avg_us": round(qms / qn * 1e3, 2), "bytes": q_bytes,
-             "GBps": round(q_bytes / (qms / qn * 1e-3) / 1e9, 1),
-             "frac_hbm": round(q_bytes / (qms / qn * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    log(f"stack: {args.layers} layers x 7 linears, 4096 tokens, r=64")
+    st = stack_section(args)
 
     result = {
         "metric": "QLoRA linear fwd+bwd TFLOP/s & packed-weight GB/s; % of MI355X roofline",
-        "value": round(value, 3),
+        "value": round(st["value"], 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(st["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded PCG64: W ~ N(0, 0.02) fp32, X, dY ~ N(0, 1) bf16, A ~ N(0, 1/r), B ~ N(0, 0.01))",
-        "config": {"workload": "attention-projection QLoRA linear: W 4096x4096 NF4 (block 64, 8-bit scale "
-                               "codes per 256 blocks), 2048 tokens, r=16, alpha=32; step = quantize + fwd + bwd",
-                   "d_out": N, "d_in": K, "tokens": T, "r": r, "alpha": alpha},
-        "roofline": roofline,
-        "kernels": kernels,
-        "kernels_note": "avg_us from a second pass of the same steps with every launch bracketed by hipEvents "
-                        "(bracketing all ~14 launches slows a step by about a quarter); the roofline kernel "
-                        "is timed inside the timed region itself, where only it is bracketed",
-        "quantize": quant,
-        "step_flops": fwd_f + bwd_f,
+        "data": "synthetic (seeded: W ~ N(0, 0.02) fp32 quantized to NF4, X, dY ~ N(0, 1) bf16, A ~ N(0, 1/r), "
+                "B ~ N(0, 0.01) bf16); no model weights or dataset",
+        "config": {"workload": f"65B-class layer stack share: {args.layers} layers x (q, k, v, o 8192x8192; gate, up "
+                               "8192->22016; down 22016->8192), NF4 block 64 + 8-bit scale codes per 256 blocks, "
+                               "4096 tokens, r=64, alpha=16; step = fwd + bwd (dX, dA, dB) of every linear",
+                   "layers": args.layers, "tokens": st["T"], "r": st["r"], "alpha": st["alpha"],
+                   "step_flops": st["step_flops"]},
+        "roofline": st["roofline"],
+        "fused_products": st["fused_products"],
+        "kernels": st["kernels"],
+        "kernels_note": st["kernels_note"],
+        "quantize_stack": st["quantize_stack"],
+        "peak_hbm_allocated_bytes": st["peak_hbm_allocated_bytes"],
+        "packed_weight_bytes": st["packed_weight_bytes"],
+        "context": "the pages report a 65B model fine-tuned with this method on one 48 GB GPU in 24 hours "
+                   "(no throughput figure); context only, not a target",
     }
-    if not args.no_decode:
-        result["decode_packed_weight"] = decode_section(steps=max(20, args.steps), warmup=5)
-        result["export_bf16"] = export_section(lin, steps=max(20, args.steps))
-        result["quantize_16bit_weight"] = quantize16_section(lin, steps=max(20, args.steps))
-        result["adamw_65b_adapters"] = adamw_section(steps=max(20, args.steps))
-        result["lora_dropout_attn4096"] = dropout_section(lin, steps=max(20, args.steps))
-        result["qkv_gqa_70b"] = multi_proj_section(steps=max(20, args.steps))
-    if args.mlp:
+    if not args.headline_only:
+        (lin,) = workloads.attn_4096()
+        sec_steps = max(20, args.steps)
+        result["attn_4096"] = attn_section(lin, sec_steps)
         result["mlp_llama7b"] = mlp_section(steps=10)
+        result["decode_packed_weight"] = decode_section(steps=sec_steps, warmup=5)
+        result["export_bf16"] = export_section(lin, steps=sec_steps)
+        result["quantize_16bit_weight"] = quantize16_section(lin, steps=sec_steps)
+        result["adamw_65b_adapters"] = adamw_section(steps=sec_steps)
+        result["lora_dropout_attn4096"] = dropout_section(lin, steps=sec_steps)
+        result["qkv_gqa_70b"] = multi_proj_section(steps=sec_steps)
     if not args.no_cpu_baseline:
         log("timing the oracle on the host ...")
-        result["cpu_baseline"] = cpu_baseline(inp, lin, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline_headline()
+        result["cpu_baselines"] = cpu_baselines(args.cpu_full)
     print(json.dumps(result), flush=True)
     if args.copy_calibration > 0:
         nbytes = args.copy_calibration << 20

@@ -47,11 +47,19 @@
  *   compute call only enqueues work on that stream and returns without
  *   synchronizing; outputs are valid once the stream has reached that point.
  * - Errors: functions return QLORA_OK (0) or a negative QLORA_ERR_* code.
- *   Arguments are validated on the host before anything is enqueued, so a
+ *   Arguments are validated on the host before anything is enqueued -- for
+ *   the calls on several layers, every layer before the first launch -- so a
  *   call that fails validation has no side effect.  QLORA_ERR_HIP reports a
- *   failed launch (hipGetLastError after enqueueing).
- * - W, packed, X, dY, A and B must be 16-byte aligned (QLORA_ERR_UNSUPPORTED
- *   otherwise); other pointers need only their element alignment.  A forward
+ *   failed launch (hipGetLastError after enqueueing); work enqueued before
+ *   it by the same call may then have run.
+ * - Size limit: the kernels address each dense operand with 32-bit byte
+ *   offsets, so the packed weight (N*K/2 bytes), X (T*K*2), Y and dY (T*N*2),
+ *   dX (T*K*2) and the [T][2r] rank-r pairs of the workspace must each be
+ *   below 2^31 - 16 bytes; larger calls return QLORA_ERR_SHAPE (the workspace
+ *   queries too).  Dimensions are below 2^31.
+ * - W, packed, X, dY, A, B, Y, dX, U_out, U_in, dA and dB must be 16-byte
+ *   aligned (QLORA_ERR_UNSUPPORTED otherwise); codes and consts need only
+ *   their element alignment.  A forward
  *   call with at most 16 tokens takes the weight-streaming kernel when codes
  *   is 16-byte aligned, K is a multiple of the block size and K/bs is at
  *   most about 2000, else the tiled kernel (same results within the accuracy
@@ -256,19 +264,6 @@ int qlora_merge_lora(const qlora_nf4_desc* d, const uint8_t* packed, const uint8
                      uint16_t* W_merged, void* stream);
 
 /*
- * Per-kernel timing (measurement support; not an operation of the layer).
- * qlora_trace_enable(1) makes every subsequent kernel launch of the library
- * record a hipEvent before and after it on the launch stream (event objects
- * are created on first use and reused; no device memory is allocated);
- * qlora_trace_enable(0) (the default) records nothing.
- * qlora_trace_read waits for the recorded events, adds their elapsed times to
- * per-kernel totals and writes up to max_stats entries {name, launches,
- * total_ms} (name: static string) for the kernels launched so far; *count
- * receives the number of kernels with launches.  reset != 0 clears the
- * totals afterwards.  Errors: NULL (count, or stats with max_stats > 0), HIP.
- * Not thread-safe with respect to concurrent compute calls on other threads.
- */
-/*
  * Forward of n (1..4) layers that share their input X -- the projections of
  * one layer input, e.g. the query, key and value projections or the gate and
  * up projections; "LoRA 与 QLoRA：..." §8 targets every linear module, so
@@ -376,6 +371,19 @@ typedef struct qlora_adamw_hparams {
 int qlora_adamw_step(const qlora_adamw_hparams* h, int64_t n, float* param, const float* grad, float* exp_avg,
                      float* exp_avg_sq, uint16_t* param_bf16, void* stream);
 
+/*
+ * Per-kernel timing (measurement support; not an operation of the layer).
+ * qlora_trace_enable(1) makes every subsequent kernel launch of the library
+ * record a hipEvent before and after it on the launch stream (event objects
+ * are created on first use and reused; no device memory is allocated);
+ * qlora_trace_enable(0) (the default) records nothing.
+ * qlora_trace_read waits for the recorded events, adds their elapsed times to
+ * per-kernel totals and writes up to max_stats entries {name, launches,
+ * total_ms} (name: static string) for the kernels launched so far; *count
+ * receives the number of kernels with launches.  reset != 0 clears the
+ * totals afterwards.  Errors: NULL (count, or stats with max_stats > 0), HIP.
+ * Not thread-safe with respect to concurrent compute calls on other threads.
+ */
 /*
  * qlora_trace_select: like qlora_trace_enable, but only the kernels whose bit
  * is set in kernel_mask are bracketed (bit k = the kernel named by

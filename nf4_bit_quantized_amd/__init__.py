@@ -189,6 +189,49 @@ def _check_out(t, shape, dtype, name: str):
         raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)}")
 
 
+def _check_in(t, shape, dtype, name: str):
+    """A required input: of the shape and dtype the weight's descriptor and the
+    call imply, contiguous.  The kernels size their reads from the stored
+    weight's shape, so a smaller tensor would be read past its end."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)}, "
+                         f"got {t.dtype} {tuple(t.shape)}")
+
+
+def _matrix(X, name: str = "X"):
+    """X must be a 2-D tensor (its rows are the tokens)."""
+    if X is None or X.dim() != 2:
+        raise ValueError(f"{name} must be a 2-D tensor")
+    return X
+
+
+def _check_weight(packed, codes, consts, name: str = "weight"):
+    """The stored weight: packed uint8 [d_out][d_in/2], codes uint8 and
+    consts float32 (one-dimensional, contiguous)."""
+    import torch
+    if packed is None or consts is None:
+        raise ValueError(f"{name}: packed and consts are required")
+    if packed.dtype != torch.uint8 or packed.dim() != 2 or not packed.is_contiguous():
+        raise ValueError(f"{name}: packed must be a contiguous 2-D uint8 tensor")
+    if codes is not None and (codes.dtype != torch.uint8 or codes.dim() != 1 or not codes.is_contiguous()):
+        raise ValueError(f"{name}: codes must be a contiguous 1-D uint8 tensor")
+    if consts.dtype != torch.float32 or consts.dim() != 1 or not consts.is_contiguous():
+        raise ValueError(f"{name}: consts must be a contiguous 1-D float32 tensor")
+
+
+def _check_adapter(A, B, d_out: int, d_in: int, r: int, name: str = ""):
+    """A bf16 [r][d_in] and B bf16 [d_out][r], both given or both None (r = 0)."""
+    import torch
+    if (A is None) != (B is None):
+        raise ValueError(f"{name}A and B must be given together")
+    if A is None:
+        return
+    _check_in(A, (r, d_in), torch.bfloat16, f"{name}A")
+    _check_in(B, (d_out, r), torch.bfloat16, f"{name}B")
+
+
 # ---------------------------------------------------------------------------
 # Host-only queries
 # ---------------------------------------------------------------------------
@@ -239,6 +282,27 @@ def qlora_bwd_workspace_bytes(d_out: int, d_in: int, T: int, r: int) -> int:
     _check(lib().qlora_bwd_workspace_bytes(ctypes.byref(d), int(T), int(r), ctypes.byref(n)),
            "qlora_bwd_workspace_bytes")
     return n.value
+
+
+def qlora_multi_fwd_workspace_bytes(shapes, T: int, r: int) -> int:
+    """Workspace of qlora_linear_fwd_multi for weights of the given
+    (d_out, d_in) shapes (blocks of 64, double quantization)."""
+    n = len(shapes)
+    descs = (Nf4Desc * n)(*[_desc(o, i) for o, i in shapes])
+    b = ctypes.c_size_t()
+    _check(lib().qlora_multi_fwd_workspace_bytes(n, descs, int(T), int(r), ctypes.byref(b)),
+           "qlora_multi_fwd_workspace_bytes")
+    return b.value
+
+
+def qlora_multi_bwd_workspace_bytes(shapes, T: int, r: int) -> int:
+    """Workspace of qlora_linear_bwd_multi for weights of the given shapes."""
+    n = len(shapes)
+    descs = (Nf4Desc * n)(*[_desc(o, i) for o, i in shapes])
+    b = ctypes.c_size_t()
+    _check(lib().qlora_multi_bwd_workspace_bytes(n, descs, int(T), int(r), ctypes.byref(b)),
+           "qlora_multi_bwd_workspace_bytes")
+    return b.value
 
 
 # ---------------------------------------------------------------------------
@@ -304,12 +368,13 @@ def qlora_linear_fwd(packed, codes, consts, X, A, B, alpha: float, Y=None, U_out
     """
     import torch
     d_out, d_in = packed.shape[0], packed.shape[1] * 2
+    _matrix(X)
     T = X.shape[0]
     r = 0 if A is None else A.shape[0]
+    _check_weight(packed, codes, consts)
+    _check_in(X, (T, d_in), torch.bfloat16, "X")
+    _check_adapter(A, B, d_out, d_in, r)
     _need_cuda(packed, codes, consts, X, A, B, Y, U_out, name="qlora_linear_fwd")
-    for t, nm in ((X, "X"), (A, "A"), (B, "B")):
-        if t is not None and t.dtype != torch.bfloat16:
-            raise ValueError(f"{nm} must be bfloat16")
     _check_out(Y, (T, d_out), torch.bfloat16, "Y")
     _check_out(U_out, (T, r), torch.float32, "U_out")
     if Y is None:
@@ -359,6 +424,7 @@ def qlora_linear_fwd_multi(layers, X, alpha: float, want_u: bool = True, workspa
     n = len(layers)
     if not 1 <= n <= 4:
         raise ValueError("one to four layers")
+    _matrix(X)
     T = X.shape[0]
     r = 0 if layers[0][3] is None else layers[0][3].shape[0]
     tables = tables or [TABLE_NF4] * n
@@ -366,6 +432,12 @@ def qlora_linear_fwd_multi(layers, X, alpha: float, want_u: bool = True, workspa
         raise ValueError("one (Y, U) pair per layer")
     given, outs = outs, []
     descs = (Nf4Desc * n)()
+    _check_in(X, (T, X.shape[1]), torch.bfloat16, "X")
+    for i, (packed, codes, consts, A, B) in enumerate(layers):      # every layer's shapes first
+        _check_weight(packed, codes, consts, f"layers[{i}]")
+        if packed.shape[1] * 2 != X.shape[1]:
+            raise ValueError(f"layers[{i}]: d_in {packed.shape[1] * 2} differs from X's {X.shape[1]}")
+        _check_adapter(A, B, packed.shape[0], X.shape[1], r, f"layers[{i}] ")
     for i, (packed, codes, consts, A, B) in enumerate(layers):
         _need_cuda(packed, codes, consts, A, B, name="qlora_linear_fwd_multi")
         descs[i] = _stored_desc(packed, codes, consts, tables[i])
@@ -405,6 +477,7 @@ def qlora_linear_bwd_multi(layers, X, alpha: float, dYs, U_ins=None, want_dx: bo
     n = len(layers)
     if not 1 <= n <= 4 or len(dYs) != n:
         raise ValueError("one to four layers, one dY each")
+    _matrix(X)
     T, d_in = X.shape[0], X.shape[1]
     r = 0 if layers[0][3] is None else layers[0][3].shape[0]
     tables = tables or [TABLE_NF4] * n
@@ -413,6 +486,13 @@ def qlora_linear_bwd_multi(layers, X, alpha: float, dYs, U_ins=None, want_dx: bo
         raise ValueError("one (dA, dB) pair per layer")
     given, grads = grads, []
     descs = (Nf4Desc * n)()
+    _check_in(X, (T, d_in), torch.bfloat16, "X")
+    for i, (packed, codes, consts, A, B) in enumerate(layers):      # every layer's shapes first
+        _check_weight(packed, codes, consts, f"layers[{i}]")
+        if packed.shape[1] * 2 != d_in:
+            raise ValueError(f"layers[{i}]: d_in {packed.shape[1] * 2} differs from X's {d_in}")
+        _check_adapter(A, B, packed.shape[0], d_in, r, f"layers[{i}] ")
+        _check_in(dYs[i], (T, packed.shape[0]), torch.bfloat16, f"dYs[{i}]")
     for i, (packed, codes, consts, A, B) in enumerate(layers):
         _need_cuda(packed, codes, consts, A, B, dYs[i], U_ins[i], name="qlora_linear_bwd_multi")
         _check_out(U_ins[i], (T, r), torch.float32, f"U_ins[{i}]")
@@ -456,12 +536,14 @@ def qlora_linear_bwd(packed, codes, consts, X, A, B, alpha: float, dY, U_in=None
     qlora_linear_fwd (qlora_linear_bwd_dropout; pass the forward's U)."""
     import torch
     d_out, d_in = packed.shape[0], packed.shape[1] * 2
+    _matrix(X)
     T = X.shape[0]
     r = 0 if A is None else A.shape[0]
+    _check_weight(packed, codes, consts)
+    _check_in(X, (T, d_in), torch.bfloat16, "X")
+    _check_in(dY, (T, d_out), torch.bfloat16, "dY")
+    _check_adapter(A, B, d_out, d_in, r)
     _need_cuda(packed, codes, consts, X, A, B, dY, U_in, dX, dA, dB, name="qlora_linear_bwd")
-    for t, nm in ((X, "X"), (A, "A"), (B, "B"), (dY, "dY")):
-        if t is not None and t.dtype != torch.bfloat16:
-            raise ValueError(f"{nm} must be bfloat16")
     _check_out(dX, (T, d_in), torch.bfloat16, "dX")
     _check_out(U_in, (T, r), torch.float32, "U_in")
     if dX is None and want_dx:
@@ -500,6 +582,7 @@ def qlora_dequantize_nf4(packed, codes, consts, W_hat=None, stream=None, table: 
     products restore on chip."""
     import torch
     d_out, d_in = packed.shape[0], packed.shape[1] * 2
+    _check_weight(packed, codes, consts)
     _need_cuda(packed, codes, consts, W_hat, name="qlora_dequantize_nf4")
     _check_out(W_hat, (d_out, d_in), torch.bfloat16, "W_hat")
     if W_hat is None:
@@ -517,10 +600,11 @@ def qlora_merge_lora(packed, codes, consts, A, B, alpha: float, W_merged=None, s
     import torch
     d_out, d_in = packed.shape[0], packed.shape[1] * 2
     r = A.shape[0]
+    _check_weight(packed, codes, consts)
+    if A is None or B is None:
+        raise ValueError("A and B are required")
+    _check_adapter(A, B, d_out, d_in, r)
     _need_cuda(packed, codes, consts, A, B, W_merged, name="qlora_merge_lora")
-    for t, nm in ((A, "A"), (B, "B")):
-        if t.dtype != torch.bfloat16:
-            raise ValueError(f"{nm} must be bfloat16")
     _check_out(W_merged, (d_out, d_in), torch.bfloat16, "W_merged")
     if W_merged is None:
         W_merged = torch.empty((d_out, d_in), dtype=torch.bfloat16, device=packed.device)

@@ -49,14 +49,25 @@ int check_desc(const qlora_nf4_desc* d) {
   return QLORA_OK;
 }
 
+int64_t hilo_ld(int32_t r) { return cdiv(2 * (int64_t)r, 64) * 64; }
+
+// The kernels address every dense operand with 32-bit byte offsets (buffer
+// resources capped below 2 GiB): the packed weight, X, Y, dY, dX and the
+// workspace's [T][2r] pairs must each stay below kMaxOperandBytes.
+constexpr int64_t kMaxOperandBytes = 0x7FFFFFF0LL;
+constexpr int64_t kMaxDim = (int64_t)1 << 31;
+
 int check_layer(const qlora_nf4_desc* d, int64_t T, int32_t r) {
   const int st = check_desc(d);
   if (st) return st;
   if (T < 0 || r < 0 || r > kMaxRank) return QLORA_ERR_SHAPE;
+  const int64_t N = d->d_out, K = d->d_in;
+  if (N >= kMaxDim || K >= kMaxDim || T >= kMaxDim) return QLORA_ERR_SHAPE;
+  if (N * K / 2 > kMaxOperandBytes || T * K * 2 > kMaxOperandBytes || T * N * 2 > kMaxOperandBytes ||
+      T * hilo_ld(r) * 2 > kMaxOperandBytes)
+    return QLORA_ERR_SHAPE;
   return QLORA_OK;
 }
-
-int64_t hilo_ld(int32_t r) { return cdiv(2 * (int64_t)r, 64) * 64; }
 
 // Workspace carving: a bump allocator over the caller's buffer.
 struct Carve {
@@ -262,20 +273,28 @@ int qlora_bwd_workspace_bytes(const qlora_nf4_desc* d, int64_t T, int32_t r, siz
 }
 
 namespace {
-// Xa: the adapter's input (X itself, or X with dropout applied)
-int linear_fwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes, const float* consts, int64_t T,
-               const uint16_t* X, const uint16_t* Xa, int32_t r, float alpha, const uint16_t* A, const uint16_t* B,
-               uint16_t* Y, float* U_out, void* workspace, size_t workspace_bytes, void* stream) {
+// Everything a forward call checks before it enqueues anything.
+int validate_fwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes, const float* consts, int64_t T,
+                 const uint16_t* X, int32_t r, const uint16_t* A, const uint16_t* B, const uint16_t* Y,
+                 const float* U_out, void* workspace, size_t workspace_bytes) {
   const int st = check_layer(d, T, r);
   if (st) return st;
   if (!packed || (!codes && d->dq_blocksize) || !consts) return QLORA_ERR_NULL;
   if (T > 0 && (!X || !Y)) return QLORA_ERR_NULL;
   if (r > 0 && (!A || !B)) return QLORA_ERR_NULL;
-  if (!aligned16(packed) || !aligned16(X) || !aligned16(A) || !aligned16(B)) return QLORA_ERR_UNSUPPORTED;
+  if (!aligned16(packed) || !aligned16(X) || !aligned16(A) || !aligned16(B) || !aligned16(Y) || !aligned16(U_out))
+    return QLORA_ERR_UNSUPPORTED;
   const size_t need = plan_fwd(d, T, r, nullptr).bytes;
   if (need > 0 && (!workspace || workspace_bytes < need)) return QLORA_ERR_WORKSPACE;
-  if (T == 0) return QLORA_OK;
+  return QLORA_OK;
+}
 
+// The launches of a validated forward.  Xa: the adapter's input (X itself,
+// or X with dropout applied).
+int enqueue_fwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes, const float* consts, int64_t T,
+                const uint16_t* X, const uint16_t* Xa, int32_t r, float alpha, const uint16_t* A, const uint16_t* B,
+                uint16_t* Y, float* U_out, void* workspace, void* stream) {
+  if (T == 0) return QLORA_OK;
   hipStream_t s_ = (hipStream_t)stream;
   FwdWs w = plan_fwd(d, T, r, workspace);
   const int64_t N = d->d_out, K = d->d_in;
@@ -302,32 +321,50 @@ int linear_fwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* co
   HIP_TRY(launch_fused(fp, false, s_, KID_FWD_GEMM));
   return QLORA_OK;
 }
+
+int linear_fwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes, const float* consts, int64_t T,
+               const uint16_t* X, int32_t r, float alpha, const uint16_t* A, const uint16_t* B, uint16_t* Y,
+               float* U_out, void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = validate_fwd(d, packed, codes, consts, T, X, r, A, B, Y, U_out, workspace, workspace_bytes);
+  if (st) return st;
+  return enqueue_fwd(d, packed, codes, consts, T, X, X, r, alpha, A, B, Y, U_out, workspace, stream);
+}
 }  // namespace
 
 int qlora_linear_fwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes,
                      const float* consts, int64_t T, const uint16_t* X, int32_t r, float alpha,
                      const uint16_t* A, const uint16_t* B, uint16_t* Y, float* U_out,
                      void* workspace, size_t workspace_bytes, void* stream) {
-  return linear_fwd(d, packed, codes, consts, T, X, X, r, alpha, A, B, Y, U_out, workspace, workspace_bytes, stream);
+  return linear_fwd(d, packed, codes, consts, T, X, r, alpha, A, B, Y, U_out, workspace, workspace_bytes, stream);
 }
 
 namespace {
-// Xa: the adapter's input (X, or X with dropout applied); keep (optional):
-// the dropout mask, whose factor c scales the adapter's share of dX
-int linear_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes, const float* consts, int64_t T,
-               const uint16_t* X, const uint16_t* Xa, const uint8_t* keep, float c, int32_t r, float alpha,
-               const uint16_t* A, const uint16_t* B, const float* U_in, const uint16_t* dY, uint16_t* dX, float* dA,
-               float* dB, void* workspace, size_t workspace_bytes, void* stream, int accumulate, int dx_accumulate = 0) {
+// Everything a backward call checks before it enqueues anything.
+int validate_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes, const float* consts, int64_t T,
+                 const uint16_t* X, int32_t r, const uint16_t* A, const uint16_t* B, const float* U_in,
+                 const uint16_t* dY, const uint16_t* dX, const float* dA, const float* dB, void* workspace,
+                 size_t workspace_bytes) {
   const int st = check_layer(d, T, r);
   if (st) return st;
   if (!packed || (!codes && d->dq_blocksize) || !consts) return QLORA_ERR_NULL;
   if (T > 0 && (!X || !dY)) return QLORA_ERR_NULL;
   if (r > 0 && (!A || !B || !dA || !dB)) return QLORA_ERR_NULL;
-  if (!aligned16(packed) || !aligned16(X) || !aligned16(dY) || !aligned16(A) || !aligned16(B))
+  if (!aligned16(packed) || !aligned16(X) || !aligned16(dY) || !aligned16(A) || !aligned16(B) || !aligned16(dX) ||
+      !aligned16(U_in) || !aligned16(dA) || !aligned16(dB))
     return QLORA_ERR_UNSUPPORTED;
   const size_t need = plan_bwd(d, T, r, nullptr).bytes;
   if (need > 0 && (!workspace || workspace_bytes < need)) return QLORA_ERR_WORKSPACE;
+  return QLORA_OK;
+}
 
+// The launches of a validated backward.  Xa: the adapter's input (X, or X
+// with dropout applied); keep (optional): the dropout mask, whose factor c
+// scales the adapter's share of dX; dx_accumulate: the dX product adds to
+// what dX holds.
+int enqueue_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes, const float* consts, int64_t T,
+                const uint16_t* X, const uint16_t* Xa, const uint8_t* keep, float c, int32_t r, float alpha,
+                const uint16_t* A, const uint16_t* B, const float* U_in, const uint16_t* dY, uint16_t* dX, float* dA,
+                float* dB, void* workspace, void* stream, int accumulate, int dx_accumulate) {
   hipStream_t s_ = (hipStream_t)stream;
   const int64_t N = d->d_out, K = d->d_in;
   if (T == 0) {
@@ -405,6 +442,17 @@ int linear_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* co
   }
   return QLORA_OK;
 }
+
+int linear_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes, const float* consts, int64_t T,
+               const uint16_t* X, int32_t r, float alpha, const uint16_t* A, const uint16_t* B, const float* U_in,
+               const uint16_t* dY, uint16_t* dX, float* dA, float* dB, void* workspace, size_t workspace_bytes,
+               void* stream, int accumulate) {
+  const int st = validate_bwd(d, packed, codes, consts, T, X, r, A, B, U_in, dY, dX, dA, dB, workspace,
+                              workspace_bytes);
+  if (st) return st;
+  return enqueue_bwd(d, packed, codes, consts, T, X, X, nullptr, 1.0f, r, alpha, A, B, U_in, dY, dX, dA, dB,
+                     workspace, stream, accumulate, 0);
+}
 }  // namespace
 
 int qlora_linear_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes,
@@ -412,8 +460,8 @@ int qlora_linear_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8
                      const uint16_t* A, const uint16_t* B, const float* U_in, const uint16_t* dY,
                      uint16_t* dX, float* dA, float* dB, void* workspace, size_t workspace_bytes,
                      void* stream) {
-  return linear_bwd(d, packed, codes, consts, T, X, X, nullptr, 1.0f, r, alpha, A, B, U_in, dY, dX, dA, dB, workspace,
-                    workspace_bytes, stream, 0);
+  return linear_bwd(d, packed, codes, consts, T, X, r, alpha, A, B, U_in, dY, dX, dA, dB, workspace, workspace_bytes,
+                    stream, 0);
 }
 
 int qlora_linear_bwd_accumulate(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes,
@@ -421,8 +469,8 @@ int qlora_linear_bwd_accumulate(const qlora_nf4_desc* d, const uint8_t* packed, 
                                 const uint16_t* A, const uint16_t* B, const float* U_in, const uint16_t* dY,
                                 uint16_t* dX, float* dA, float* dB, void* workspace, size_t workspace_bytes,
                                 void* stream) {
-  return linear_bwd(d, packed, codes, consts, T, X, X, nullptr, 1.0f, r, alpha, A, B, U_in, dY, dX, dA, dB, workspace,
-                    workspace_bytes, stream, 1);
+  return linear_bwd(d, packed, codes, consts, T, X, r, alpha, A, B, U_in, dY, dX, dA, dB, workspace, workspace_bytes,
+                    stream, 1);
 }
 
 namespace {
@@ -465,6 +513,10 @@ int qlora_multi_bwd_workspace_bytes(int32_t n, const qlora_nf4_desc* d, int64_t 
   return QLORA_OK;
 }
 
+namespace {
+char* ws_at(void* ws, size_t off) { return ws ? static_cast<char*>(ws) + off : nullptr; }
+}  // namespace
+
 int qlora_linear_bwd_multi(int32_t n, const qlora_nf4_desc* d, const uint8_t* const* packed,
                            const uint8_t* const* codes, const float* const* consts, int64_t T, const uint16_t* X,
                            int32_t r, float alpha, const uint16_t* const* A, const uint16_t* const* B,
@@ -473,19 +525,19 @@ int qlora_linear_bwd_multi(int32_t n, const qlora_nf4_desc* d, const uint8_t* co
   int st = check_multi(n, d, T, r);
   if (st) return st;
   if (!packed || !codes || !consts || !dY || (r > 0 && (!A || !B || !dA || !dB))) return QLORA_ERR_NULL;
-  size_t need = 0;
+  // every layer is validated before the first launch
   for (int i = 0; i < n; ++i) {
-    if (!packed[i] || (!codes[i] && d[i].dq_blocksize) || !consts[i] || (T > 0 && !dY[i])) return QLORA_ERR_NULL;
-    if (r > 0 && (!A[i] || !B[i] || !dA[i] || !dB[i])) return QLORA_ERR_NULL;
-    need = std::max(need, plan_bwd(&d[i], T, r, nullptr).bytes);
+    st = validate_bwd(&d[i], packed[i], codes[i], consts[i], T, X, r, r > 0 ? A[i] : nullptr,
+                      r > 0 ? B[i] : nullptr, U_in ? U_in[i] : nullptr, dY[i], dX, r > 0 ? dA[i] : nullptr,
+                      r > 0 ? dB[i] : nullptr, workspace, workspace_bytes);
+    if (st) return st;
   }
-  if (need > 0 && (!workspace || workspace_bytes < need)) return QLORA_ERR_WORKSPACE;
   // one layer after another on the stream (the workspace is reused); from
   // the second on, the dX product adds to the dX the earlier ones wrote
   for (int i = 0; i < n; ++i) {
-    st = linear_bwd(&d[i], packed[i], codes[i], consts[i], T, X, X, nullptr, 1.0f, r, alpha,
-                    r > 0 ? A[i] : nullptr, r > 0 ? B[i] : nullptr, U_in ? U_in[i] : nullptr, dY[i], dX,
-                    r > 0 ? dA[i] : nullptr, r > 0 ? dB[i] : nullptr, workspace, workspace_bytes, stream, 0, i > 0);
+    st = enqueue_bwd(&d[i], packed[i], codes[i], consts[i], T, X, X, nullptr, 1.0f, r, alpha, r > 0 ? A[i] : nullptr,
+                     r > 0 ? B[i] : nullptr, U_in ? U_in[i] : nullptr, dY[i], dX, r > 0 ? dA[i] : nullptr,
+                     r > 0 ? dB[i] : nullptr, workspace, stream, 0, i > 0);
     if (st) return st;
   }
   return QLORA_OK;
@@ -499,17 +551,18 @@ int qlora_linear_fwd_multi(int32_t n, const qlora_nf4_desc* d, const uint8_t* co
   int st = check_multi(n, d, T, r);
   if (st) return st;
   if (!packed || !codes || !consts || !Y || (r > 0 && (!A || !B))) return QLORA_ERR_NULL;
+  // every layer is validated, on its slice of the workspace, before the first launch
   size_t need = 0;
-  for (int i = 0; i < n; ++i) {
-    if (!packed[i] || (!codes[i] && d[i].dq_blocksize) || !consts[i]) return QLORA_ERR_NULL;
-    if (T > 0 && !Y[i]) return QLORA_ERR_NULL;
-    if (r > 0 && (!A[i] || !B[i])) return QLORA_ERR_NULL;
-    if (!aligned16(packed[i]) || (r > 0 && (!aligned16(A[i]) || !aligned16(B[i])))) return QLORA_ERR_UNSUPPORTED;
-    need += multi_slice(&d[i], T, r);
-  }
-  if (T > 0 && !X) return QLORA_ERR_NULL;
-  if (!aligned16(X)) return QLORA_ERR_UNSUPPORTED;
+  for (int i = 0; i < n; ++i) need += multi_slice(&d[i], T, r);
   if (need > 0 && (!workspace || workspace_bytes < need)) return QLORA_ERR_WORKSPACE;
+  size_t off = 0;
+  for (int i = 0; i < n; ++i) {
+    const size_t sl = multi_slice(&d[i], T, r);
+    st = validate_fwd(&d[i], packed[i], codes[i], consts[i], T, X, r, r > 0 ? A[i] : nullptr,
+                      r > 0 ? B[i] : nullptr, Y[i], U_out ? U_out[i] : nullptr, ws_at(workspace, off), sl);
+    if (st) return st;
+    off += sl;
+  }
   if (T == 0) return QLORA_OK;
 
   hipStream_t s_ = (hipStream_t)stream;
@@ -518,14 +571,12 @@ int qlora_linear_fwd_multi(int32_t n, const qlora_nf4_desc* d, const uint8_t* co
   for (int i = 0; i < n && fused; ++i)
     fused = decode_supported(d[i].d_out, K, block_shift(&d[i])) && aligned16(codes[i]);
   if (!fused) {  // one forward per weight
-    size_t off = 0;
+    off = 0;
     for (int i = 0; i < n; ++i) {
-      const size_t sl = multi_slice(&d[i], T, r);
-      st = linear_fwd(&d[i], packed[i], codes[i], consts[i], T, X, X, r, alpha, r > 0 ? A[i] : nullptr,
-                      r > 0 ? B[i] : nullptr, Y[i], U_out ? U_out[i] : nullptr, static_cast<char*>(workspace) + off,
-                      sl, stream);
+      st = enqueue_fwd(&d[i], packed[i], codes[i], consts[i], T, X, X, r, alpha, r > 0 ? A[i] : nullptr,
+                       r > 0 ? B[i] : nullptr, Y[i], U_out ? U_out[i] : nullptr, ws_at(workspace, off), stream);
       if (st) return st;
-      off += sl;
+      off += multi_slice(&d[i], T, r);
     }
     return QLORA_OK;
   }
@@ -533,9 +584,9 @@ int qlora_linear_fwd_multi(int32_t n, const qlora_nf4_desc* d, const uint8_t* co
   const float s = r > 0 ? alpha / (float)r : 0.0f;
   DecodeWeight w[kDecodeMaxWeights];
   const uint16_t* us[kDecodeMaxWeights];
-  size_t off = 0;
+  off = 0;
   for (int i = 0; i < n; ++i) {
-    FwdWs fw = plan_fwd(&d[i], T, r, static_cast<char*>(workspace) + off);
+    FwdWs fw = plan_fwd(&d[i], T, r, ws_at(workspace, off));
     off += multi_slice(&d[i], T, r);
     if (r > 0) {
       const int e = lora_down(X, A[i], T, K, r, s, fw.part, U_out && U_out[i] ? U_out[i] : fw.U, fw.Us, s_);
@@ -578,19 +629,16 @@ int qlora_linear_fwd_dropout(const qlora_nf4_desc* d, const uint8_t* packed, con
   if (st) return st;
   if ((st = check_dropout(d, T, r, keep, p))) return st;
   if (r == 0 || T == 0)
-    return linear_fwd(d, packed, codes, consts, T, X, X, r, alpha, A, B, Y, U_out, workspace, workspace_bytes,
-                      stream);
-  if (!X) return QLORA_ERR_NULL;
-  if (!aligned16(X)) return QLORA_ERR_UNSUPPORTED;
+    return linear_fwd(d, packed, codes, consts, T, X, r, alpha, A, B, Y, U_out, workspace, workspace_bytes, stream);
+  // X_d at the start of the workspace, the plain call's workspace after it;
+  // everything is validated before the first launch
   const size_t xd = dropout_xd_bytes(d, T);
-  if (!workspace || workspace_bytes < xd + plan_fwd(d, T, r, nullptr).bytes) return QLORA_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < xd) return QLORA_ERR_WORKSPACE;
+  st = validate_fwd(d, packed, codes, consts, T, X, r, A, B, Y, U_out, ws_at(workspace, xd), workspace_bytes - xd);
+  if (st) return st;
   uint16_t* Xd = static_cast<uint16_t*>(workspace);
-  // validate everything else before the first launch
-  if (!packed || (!codes && d->dq_blocksize) || !consts || !Y || !A || !B) return QLORA_ERR_NULL;
-  if (!aligned16(packed) || !aligned16(A) || !aligned16(B)) return QLORA_ERR_UNSUPPORTED;
   HIP_TRY(launch_dropout_input(X, keep, dropout_factor(p), T, d->d_in, Xd, (hipStream_t)stream));
-  return linear_fwd(d, packed, codes, consts, T, X, Xd, r, alpha, A, B, Y, U_out, static_cast<char*>(workspace) + xd,
-                    workspace_bytes - xd, stream);
+  return enqueue_fwd(d, packed, codes, consts, T, X, Xd, r, alpha, A, B, Y, U_out, ws_at(workspace, xd), stream);
 }
 
 int qlora_linear_bwd_dropout(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes,
@@ -602,19 +650,18 @@ int qlora_linear_bwd_dropout(const qlora_nf4_desc* d, const uint8_t* packed, con
   if (st) return st;
   if ((st = check_dropout(d, T, r, keep, p))) return st;
   if (r == 0 || T == 0)
-    return linear_bwd(d, packed, codes, consts, T, X, X, nullptr, 1.0f, r, alpha, A, B, U_in, dY, dX, dA, dB,
-                      workspace, workspace_bytes, stream, accumulate != 0);
-  if (!X || !dY || !A || !B || !dA || !dB || !packed || (!codes && d->dq_blocksize) || !consts)
-    return QLORA_ERR_NULL;
-  if (!aligned16(X) || !aligned16(dY) || !aligned16(A) || !aligned16(B) || !aligned16(packed))
-    return QLORA_ERR_UNSUPPORTED;
+    return linear_bwd(d, packed, codes, consts, T, X, r, alpha, A, B, U_in, dY, dX, dA, dB, workspace,
+                      workspace_bytes, stream, accumulate != 0);
   const size_t xd = dropout_xd_bytes(d, T);
-  if (!workspace || workspace_bytes < xd + plan_bwd(d, T, r, nullptr).bytes) return QLORA_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < xd) return QLORA_ERR_WORKSPACE;
+  st = validate_bwd(d, packed, codes, consts, T, X, r, A, B, U_in, dY, dX, dA, dB, ws_at(workspace, xd),
+                    workspace_bytes - xd);
+  if (st) return st;
   uint16_t* Xd = static_cast<uint16_t*>(workspace);
   const float c = dropout_factor(p);
   HIP_TRY(launch_dropout_input(X, keep, c, T, d->d_in, Xd, (hipStream_t)stream));
-  return linear_bwd(d, packed, codes, consts, T, X, Xd, keep, c, r, alpha, A, B, U_in, dY, dX, dA, dB,
-                    static_cast<char*>(workspace) + xd, workspace_bytes - xd, stream, accumulate != 0);
+  return enqueue_bwd(d, packed, codes, consts, T, X, Xd, keep, c, r, alpha, A, B, U_in, dY, dX, dA, dB,
+                     ws_at(workspace, xd), stream, accumulate != 0, 0);
 }
 
 int qlora_adamw_step(const qlora_adamw_hparams* h, int64_t n, float* param, const float* grad, float* exp_avg,

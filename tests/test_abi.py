@@ -282,3 +282,169 @@ def test_workspace_sizes_grow_with_tokens_and_rank():
     assert 0 < a < b
     assert q.qlora_fwd_workspace_bytes(4096, 4096, 2048, 0) == 0          # base-only, no decode: nothing
     assert q.qlora_bwd_workspace_bytes(4096, 4096, 0, 16) == 0
+
+
+def _no_gpu_here():
+    """The fake-pointer tests below must never reach a device: on a machine
+    with a GPU a call that passed validation would launch on them."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("fake-pointer validation tests run only where no GPU is visible")
+
+
+def test_operand_size_limits_rejected_before_any_launch():
+    """Every dense operand is addressed with 32-bit byte offsets: a packed
+    weight, X, Y, dY or dX of 2 GiB or more is a shape error on the host (the
+    query functions agree), never a launch failure."""
+    _no_gpu_here()
+    fake = 0x10000
+    L = q.lib()
+    n = ctypes.c_size_t()
+    big_w = q._desc(65536, 65536)                  # packed weight 2 GiB
+    assert L.qlora_fwd_workspace_bytes(ctypes.byref(big_w), 16, 8, ctypes.byref(n)) == q.QLORA_ERR_SHAPE
+    assert _raw_fwd(big_w, fake, fake, fake, 16, fake, 8, fake, fake, fake, fake, 1 << 30) == q.QLORA_ERR_SHAPE
+    d = q._desc(8192, 8192)
+    T = 131072                                     # X = T x 8192 bf16 = 2 GiB
+    assert L.qlora_fwd_workspace_bytes(ctypes.byref(d), T, 8, ctypes.byref(n)) == q.QLORA_ERR_SHAPE
+    assert L.qlora_bwd_workspace_bytes(ctypes.byref(d), T, 8, ctypes.byref(n)) == q.QLORA_ERR_SHAPE
+    assert _raw_fwd(d, fake, fake, fake, T, fake, 8, fake, fake, fake, fake, 1 << 30) == q.QLORA_ERR_SHAPE
+    wide = q._desc(262144, 64)                     # Y = T x 262144 bf16 = 2 GiB at T = 4096
+    assert L.qlora_fwd_workspace_bytes(ctypes.byref(wide), 4096, 8, ctypes.byref(n)) == q.QLORA_ERR_SHAPE
+    assert L.qlora_fwd_workspace_bytes(ctypes.byref(wide), 4095, 8, ctypes.byref(n)) == q.QLORA_OK
+    assert L.qlora_merge_lora(ctypes.byref(big_w), fake, fake, fake, 4, ctypes.c_float(1.0), fake, fake, fake,
+                              None) == q.QLORA_ERR_SHAPE
+
+
+def test_output_alignment_rejected_before_any_launch():
+    """Y and dX are written with 16-byte stores, U and the gradients need it
+    too: a misaligned output is UNSUPPORTED on the host."""
+    _no_gpu_here()
+    fake = 0x10000
+    d = q._desc(64, 64)
+    L = q.lib()
+    need = q.qlora_fwd_workspace_bytes(64, 64, 8, 4)
+    assert _raw_fwd(d, fake, fake, fake, 8, fake, 4, fake, fake, fake + 2, fake, need) == q.QLORA_ERR_UNSUPPORTED
+    nb = q.qlora_bwd_workspace_bytes(64, 64, 8, 4)
+    f1 = ctypes.c_float(1.0)
+    for dX, dA, dB in ((fake + 2, fake, fake), (fake, fake + 4, fake), (fake, fake, fake + 8)):
+        assert L.qlora_linear_bwd(ctypes.byref(d), fake, fake, fake, 8, fake, 4, f1, fake, fake, None, fake, dX, dA,
+                                  dB, fake, nb, None) == q.QLORA_ERR_UNSUPPORTED
+
+
+def _ptrs(*vals):
+    return (ctypes.c_void_p * len(vals))(*vals)
+
+
+def test_multi_calls_validate_every_layer_before_the_first_launch():
+    """A bad second layer makes the whole call fail on the host: the status
+    is the validation error, not a launch failure from layer 0 (which, with
+    no GPU here, is what a launch would report)."""
+    _no_gpu_here()
+    fake = 0x10000
+    L = q.lib()
+    f = ctypes.c_float(16.0)
+    T, r = 40, 8
+    d2 = (q.Nf4Desc * 2)(q._desc(128, 256), q._desc(64, 256))
+    n = ctypes.c_size_t()
+    assert L.qlora_multi_fwd_workspace_bytes(2, d2, T, r, ctypes.byref(n)) == q.QLORA_OK
+    wsf = n.value
+    assert L.qlora_multi_bwd_workspace_bytes(2, d2, T, r, ctypes.byref(n)) == q.QLORA_OK
+    wsb = n.value
+    P = _ptrs(fake, fake)
+    for bad_packed, bad_A, bad_Y in (((fake, fake + 8), (fake, fake), (fake, fake)),
+                                     ((fake, fake), (fake, fake + 2), (fake, fake)),
+                                     ((fake, fake), (fake, fake), (fake, fake + 2))):
+        st = L.qlora_linear_fwd_multi(2, d2, _ptrs(*bad_packed), P, P, T, fake, r, f, _ptrs(*bad_A), P,
+                                      _ptrs(*bad_Y), None, fake, wsf, None)
+        assert st == q.QLORA_ERR_UNSUPPORTED
+    # a NULL B in the second layer
+    st = L.qlora_linear_fwd_multi(2, d2, P, P, P, T, fake, r, f, P, _ptrs(fake, None), P, None, fake, wsf, None)
+    assert st == q.QLORA_ERR_NULL
+    # backward: misaligned A, dY or dA of the second layer; a short workspace
+    for bad_A, bad_dY, bad_dA in (((fake, fake + 2), (fake, fake), (fake, fake)),
+                                  ((fake, fake), (fake, fake + 2), (fake, fake)),
+                                  ((fake, fake), (fake, fake), (fake, fake + 4))):
+        st = L.qlora_linear_bwd_multi(2, d2, P, P, P, T, fake, r, f, _ptrs(*bad_A), P, None, _ptrs(*bad_dY), fake,
+                                      _ptrs(*bad_dA), P, fake, wsb, None)
+        assert st == q.QLORA_ERR_UNSUPPORTED
+    st = L.qlora_linear_bwd_multi(2, d2, P, P, P, T, fake, r, f, P, P, None, P, fake, P, P, fake, wsb - 1, None)
+    assert st == q.QLORA_ERR_WORKSPACE
+
+
+def test_dropout_calls_validate_before_the_dropout_launch():
+    """The dropout calls apply the mask in a launch of their own before the
+    layer: everything is validated before that first launch."""
+    _no_gpu_here()
+    fake = 0x10000
+    d = q._desc(64, 64)
+    L = q.lib()
+    f = ctypes.c_float
+    big = 1 << 30
+    # misaligned Y / misaligned dX: rejected, not a launch failure
+    assert L.qlora_linear_fwd_dropout(ctypes.byref(d), fake, fake, fake, 4, fake, 8, f(16.0), fake, fake, fake,
+                                      f(0.1), fake + 2, None, fake, big, None) == q.QLORA_ERR_UNSUPPORTED
+    assert L.qlora_linear_bwd_dropout(ctypes.byref(d), fake, fake, fake, 4, fake, 8, f(16.0), fake, fake, None, fake,
+                                      fake, f(0.1), fake + 2, fake, fake, 0, fake, big, None) == \
+        q.QLORA_ERR_UNSUPPORTED
+    # workspace that holds X_d but not the layer's own part
+    n = ctypes.c_size_t()
+    assert L.qlora_dropout_workspace_bytes(ctypes.byref(d), 4, 8, 0, ctypes.byref(n)) == q.QLORA_OK
+    assert L.qlora_linear_fwd_dropout(ctypes.byref(d), fake, fake, fake, 4, fake, 8, f(16.0), fake, fake, fake,
+                                      f(0.1), fake, None, fake, n.value - 1, None) == q.QLORA_ERR_WORKSPACE
+
+
+def test_binding_checks_inputs_against_the_stored_weight():
+    """The binding compares X, A, B and dY with the weight's shape and the
+    rank before any call: too narrow a tensor would otherwise be read past its
+    end by kernels that size their reads from the weight."""
+    import torch
+    bf = torch.bfloat16
+    packed = torch.zeros(128, 128, dtype=torch.uint8)            # d_out 128, d_in 256
+    codes = torch.zeros(128 * 256 // 64, dtype=torch.uint8)
+    consts = torch.zeros(2, dtype=torch.float32)
+    X = torch.zeros(8, 256, dtype=bf)
+    A = torch.zeros(4, 256, dtype=bf)
+    B = torch.zeros(128, 4, dtype=bf)
+    dY = torch.zeros(8, 128, dtype=bf)
+    bad_cases = [
+        ("X must be", dict(X=torch.zeros(8, 192, dtype=bf))),
+        ("X must be", dict(X=torch.zeros(8, 256, dtype=torch.float32))),
+        ("A must be", dict(A=torch.zeros(4, 192, dtype=bf))),
+        ("B must be", dict(B=torch.zeros(64, 4, dtype=bf))),
+        ("B must be", dict(B=torch.zeros(128, 8, dtype=bf))),
+        ("A and B", dict(B=None)),
+    ]
+    for msg, kw in bad_cases:
+        a = dict(X=X, A=A, B=B)
+        a.update(kw)
+        with pytest.raises(ValueError, match=msg):
+            q.qlora_linear_fwd(packed, codes, consts, a["X"], a["A"], a["B"], 16.0)
+        with pytest.raises(ValueError, match=msg):
+            q.qlora_linear_bwd(packed, codes, consts, a["X"], a["A"], a["B"], 16.0, dY)
+    with pytest.raises(ValueError, match="dY must be"):
+        q.qlora_linear_bwd(packed, codes, consts, X, A, B, 16.0, torch.zeros(8, 64, dtype=bf))
+    with pytest.raises(ValueError, match="dY must be"):
+        q.qlora_linear_bwd(packed, codes, consts, X, A, B, 16.0, torch.zeros(4, 128, dtype=bf))
+    with pytest.raises(ValueError, match="packed must be"):
+        q.qlora_linear_fwd(packed.view(torch.int8), codes, consts, X, A, B, 16.0)
+    with pytest.raises(ValueError, match="consts must be"):
+        q.qlora_linear_fwd(packed, codes, consts.double(), X, A, B, 16.0)
+    # correct shapes get as far as the device check
+    with pytest.raises(ValueError, match="on the GPU"):
+        q.qlora_linear_fwd(packed, codes, consts, X, A, B, 16.0)
+    # several layers: each layer's adapter against its own weight, one rank for all
+    small = torch.zeros(64, 128, dtype=torch.uint8)               # d_out 64
+    scodes = torch.zeros(64 * 256 // 64, dtype=torch.uint8)
+    sconsts = torch.zeros(1, dtype=torch.float32)
+    layers = [(packed, codes, consts, A, B), (small, scodes, sconsts, A, torch.zeros(128, 4, dtype=bf))]
+    with pytest.raises(ValueError, match=r"layers\[1\] B must be"):
+        q.qlora_linear_fwd_multi(layers, X, 16.0)
+    layers = [(packed, codes, consts, A, B), (small, scodes, sconsts, torch.zeros(8, 256, dtype=bf),
+                                              torch.zeros(64, 8, dtype=bf))]
+    with pytest.raises(ValueError, match=r"layers\[1\] A must be"):
+        q.qlora_linear_fwd_multi(layers, X, 16.0)
+    layers = [(packed, codes, consts, A, B), (small, scodes, sconsts, A, torch.zeros(64, 4, dtype=bf))]
+    with pytest.raises(ValueError, match=r"dYs\[1\] must be"):
+        q.qlora_linear_bwd_multi(layers, X, 16.0, [dY, dY])
+    with pytest.raises(ValueError, match="A must be"):
+        q.qlora_merge_lora(packed, codes, consts, torch.zeros(4, 128, dtype=bf), B, 16.0)
