@@ -85,7 +85,8 @@ enum {
   QLORA_ERR_SHAPE = -2,       /* a size is out of range or not a multiple it must be */
   QLORA_ERR_UNSUPPORTED = -3, /* a format parameter the library does not implement */
   QLORA_ERR_WORKSPACE = -4,   /* workspace is NULL or smaller than the size query returned */
-  QLORA_ERR_HIP = -5          /* the HIP runtime reported an error while enqueueing */
+  QLORA_ERR_HIP = -5,         /* the HIP runtime reported an error while enqueueing */
+  QLORA_ERR_SCRATCH_LIMIT = -6 /* the call needs more scratch than QLORA_STATIC_SCRATCH_BYTES */
 };
 
 /* Descriptor of the stored base weight. */
@@ -193,6 +194,28 @@ int qlora_linear_fwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8
                      const float* consts, int64_t T, const uint16_t* X, int32_t r, float alpha,
                      const uint16_t* A, const uint16_t* B, uint16_t* Y, float* U_out,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The forward above for callers that cannot allocate device memory -- code
+ * recorded into a HIP graph, serving loops, harnesses that forbid hipMalloc:
+ * the same kernels and the same results, bit for bit, as qlora_linear_fwd,
+ * with no workspace argument.  The scratch comes from a device array of
+ * QLORA_STATIC_SCRATCH_BYTES inside the library, one per GPU, kept until the
+ * process ends; the call itself allocates and frees nothing.  A call whose
+ * scratch (qlora_fwd_workspace_bytes) exceeds it returns
+ * QLORA_ERR_SCRATCH_LIMIT before anything is enqueued (at r = 64: above
+ * 32768 tokens).  All calls on one GPU share that GPU's array: two calls
+ * that may run at the same time on one GPU (other streams, other host
+ * threads) race on it and must be ordered by the caller.  The array's
+ * contents on entry are ignored.  The stream must belong to the current
+ * device (the array's address is looked up for it).  Other arguments,
+ * accuracy and errors as qlora_linear_fwd; also HIP when the array cannot be
+ * located.
+ */
+#define QLORA_STATIC_SCRATCH_BYTES (16u << 20)
+int qlora_linear_fwd_noalloc(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes,
+                             const float* consts, int64_t T, const uint16_t* X, int32_t r, float alpha,
+                             const uint16_t* A, const uint16_t* B, uint16_t* Y, float* U_out, void* stream);
 
 /*
  * Workspace (device bytes) qlora_linear_bwd needs for T tokens and rank r.

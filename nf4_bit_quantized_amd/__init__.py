@@ -22,6 +22,10 @@ QLORA_ERR_SHAPE = -2
 QLORA_ERR_UNSUPPORTED = -3
 QLORA_ERR_WORKSPACE = -4
 QLORA_ERR_HIP = -5
+QLORA_ERR_SCRATCH_LIMIT = -6
+
+# device bytes of the library's static scratch array (qlora_linear_fwd_noalloc)
+QLORA_STATIC_SCRATCH_BYTES = 16 << 20
 
 # element formats of the weight handed to quantization
 QLORA_W_F32 = 0
@@ -38,6 +42,7 @@ EXPORTED = (
     "qlora_quantize_nf4_typed",
     "qlora_fwd_workspace_bytes",
     "qlora_linear_fwd",
+    "qlora_linear_fwd_noalloc",
     "qlora_bwd_workspace_bytes",
     "qlora_linear_bwd",
     "qlora_linear_bwd_accumulate",
@@ -108,6 +113,7 @@ def lib() -> ctypes.CDLL:
     L.qlora_fwd_workspace_bytes.argtypes = [dp, i64, i32, ctypes.POINTER(sz)]
     L.qlora_bwd_workspace_bytes.argtypes = [dp, i64, i32, ctypes.POINTER(sz)]
     L.qlora_linear_fwd.argtypes = [dp, vp, vp, vp, i64, vp, i32, f32, vp, vp, vp, vp, vp, sz, vp]
+    L.qlora_linear_fwd_noalloc.argtypes = [dp, vp, vp, vp, i64, vp, i32, f32, vp, vp, vp, vp, vp]
     L.qlora_linear_bwd.argtypes = [dp, vp, vp, vp, i64, vp, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.qlora_linear_bwd_accumulate.argtypes = L.qlora_linear_bwd.argtypes
     L.qlora_dropout_workspace_bytes.argtypes = [dp, i64, i32, i32, ctypes.POINTER(sz)]
@@ -396,6 +402,32 @@ def qlora_linear_fwd(packed, codes, consts, X, A, B, alpha: float, Y=None, U_out
     _check(lib().qlora_linear_fwd(ctypes.byref(d), _ptr(packed), _ptr(codes), _ptr(consts), T, _ptr(X), r,
                                   float(alpha), _ptr(A), _ptr(B), _ptr(Y), _ptr(U_out), _ptr(ws), nbytes,
                                   _stream(stream)), "qlora_linear_fwd")
+    return Y, U_out
+
+
+def qlora_linear_fwd_noalloc(packed, codes, consts, X, A, B, alpha: float, Y, U_out=None, stream=None,
+                             table: int = TABLE_NF4):
+    """The forward through qlora_linear_fwd_noalloc: no workspace and no
+    allocation anywhere (the caller gives Y, and U_out if it wants U); the
+    library's static per-GPU scratch serves the call.  Calls that may overlap
+    on one GPU race on that scratch.  Returns (Y, U_out)."""
+    import torch
+    _matrix(X)
+    d_out, d_in = packed.shape[0], packed.shape[1] * 2
+    T = X.shape[0]
+    r = 0 if A is None else A.shape[0]
+    _check_weight(packed, codes, consts)
+    _check_in(X, (T, d_in), torch.bfloat16, "X")
+    _check_adapter(A, B, d_out, d_in, r)
+    if Y is None:
+        raise ValueError("Y is required (this call allocates nothing)")
+    _check_out(Y, (T, d_out), torch.bfloat16, "Y")
+    _check_out(U_out, (T, r), torch.float32, "U_out")
+    _need_cuda(packed, codes, consts, X, A, B, Y, U_out, name="qlora_linear_fwd_noalloc")
+    d = _stored_desc(packed, codes, consts, table)
+    _check(lib().qlora_linear_fwd_noalloc(ctypes.byref(d), _ptr(packed), _ptr(codes), _ptr(consts), T, _ptr(X), r,
+                                          float(alpha), _ptr(A), _ptr(B), _ptr(Y), _ptr(U_out), _stream(stream)),
+           "qlora_linear_fwd_noalloc")
     return Y, U_out
 
 

@@ -4,6 +4,7 @@
 // include/qlora.h.
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 
 #include "fused.hpp"
 #include "lora_stream.hpp"
@@ -190,6 +191,7 @@ const char* qlora_status_string(int status) {
     case QLORA_ERR_UNSUPPORTED: return "unsupported format parameter or pointer alignment";
     case QLORA_ERR_WORKSPACE: return "workspace missing or too small";
     case QLORA_ERR_HIP: return "HIP runtime error while enqueueing work";
+    case QLORA_ERR_SCRATCH_LIMIT: return "the call needs more scratch than the library's static buffer holds";
     default: return "unknown status";
   }
 }
@@ -276,7 +278,7 @@ namespace {
 // Everything a forward call checks before it enqueues anything.
 int validate_fwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes, const float* consts, int64_t T,
                  const uint16_t* X, int32_t r, const uint16_t* A, const uint16_t* B, const uint16_t* Y,
-                 const float* U_out, void* workspace, size_t workspace_bytes) {
+                 const float* U_out, void* workspace, size_t workspace_bytes, bool check_workspace = true) {
   const int st = check_layer(d, T, r);
   if (st) return st;
   if (!packed || (!codes && d->dq_blocksize) || !consts) return QLORA_ERR_NULL;
@@ -284,6 +286,7 @@ int validate_fwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* 
   if (r > 0 && (!A || !B)) return QLORA_ERR_NULL;
   if (!aligned16(packed) || !aligned16(X) || !aligned16(A) || !aligned16(B) || !aligned16(Y) || !aligned16(U_out))
     return QLORA_ERR_UNSUPPORTED;
+  if (!check_workspace) return QLORA_OK;
   const size_t need = plan_fwd(d, T, r, nullptr).bytes;
   if (need > 0 && (!workspace || workspace_bytes < need)) return QLORA_ERR_WORKSPACE;
   return QLORA_OK;
@@ -336,6 +339,51 @@ int qlora_linear_fwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8
                      const uint16_t* A, const uint16_t* B, uint16_t* Y, float* U_out,
                      void* workspace, size_t workspace_bytes, void* stream) {
   return linear_fwd(d, packed, codes, consts, T, X, r, alpha, A, B, Y, U_out, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The forward without a caller workspace: its scratch (U when not saved, the
+// hi/lo pairs of s*U, split-contraction partials) lives in a file-scope
+// device array.  Each GPU holds its own copy of the array; the host side
+// only ever uses the address hipGetSymbolAddress returns for the current
+// device, looked up once per device and kept.
+// ---------------------------------------------------------------------------
+
+static __device__ __align__(256) unsigned char scratch[QLORA_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The device address of the current device's copy of `scratch`.
+int static_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QLORA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return QLORA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return QLORA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int qlora_linear_fwd_noalloc(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes,
+                             const float* consts, int64_t T, const uint16_t* X, int32_t r, float alpha,
+                             const uint16_t* A, const uint16_t* B, uint16_t* Y, float* U_out, void* stream) {
+  int st = validate_fwd(d, packed, codes, consts, T, X, r, A, B, Y, U_out, nullptr, 0, false);
+  if (st) return st;
+  if (plan_fwd(d, T, r, nullptr).bytes > (size_t)QLORA_STATIC_SCRATCH_BYTES) return QLORA_ERR_SCRATCH_LIMIT;
+  void* ws = nullptr;
+  if ((st = static_scratch(&ws))) return st;
+  return enqueue_fwd(d, packed, codes, consts, T, X, X, r, alpha, A, B, Y, U_out, ws, stream);
 }
 
 namespace {

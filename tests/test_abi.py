@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         assert isinstance(q.qlora_status_string(code), str) and q.qlora_status_string(code)
     assert q.qlora_status_string(-99) == "unknown status"
 
@@ -448,3 +448,22 @@ def test_binding_checks_inputs_against_the_stored_weight():
         q.qlora_linear_bwd_multi(layers, X, 16.0, [dY, dY])
     with pytest.raises(ValueError, match="A must be"):
         q.qlora_merge_lora(packed, codes, consts, torch.zeros(4, 128, dtype=bf), B, 16.0)
+
+
+def test_noalloc_forward_validation_happens_before_any_launch():
+    """The allocation-free forward validates like the plain one and refuses a
+    call whose scratch exceeds the static array before looking it up."""
+    _no_gpu_here()
+    fake = 0x10000
+    L = q.lib()
+    f = ctypes.c_float(16.0)
+    d = q._desc(64, 64)
+    assert L.qlora_linear_fwd_noalloc(ctypes.byref(d), fake, fake, fake, 8, fake, 4, f, fake, fake, None, None,
+                                      None) == q.QLORA_ERR_NULL
+    assert L.qlora_linear_fwd_noalloc(ctypes.byref(d), fake, fake, fake, 8, fake, 4, f, fake, fake, fake + 2, None,
+                                      None) == q.QLORA_ERR_UNSUPPORTED
+    T = 40000
+    assert q.qlora_fwd_workspace_bytes(64, 64, T, 64) > q.QLORA_STATIC_SCRATCH_BYTES
+    assert L.qlora_linear_fwd_noalloc(ctypes.byref(d), fake, fake, fake, T, fake, 64, f, fake, fake, fake, None,
+                                      None) == q.QLORA_ERR_SCRATCH_LIMIT
+    assert q.qlora_fwd_workspace_bytes(64, 64, 32768, 64) <= q.QLORA_STATIC_SCRATCH_BYTES
