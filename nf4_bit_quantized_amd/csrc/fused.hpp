@@ -32,4 +32,9 @@ struct FusedParams {
 
 hipError_t launch_fused(FusedParams P, bool dx, hipStream_t stream, int kernel_id);
 
+// The forward product on 256 x 256 tiles with the restore in the multiplying
+// waves' registers (fused_wide.hip); launch_fused picks it where it applies.
+bool fused_wide_ok(const FusedParams& P, bool dx);
+hipError_t launch_fused_wide(FusedParams P, hipStream_t stream, int kernel_id);
+
 }  // namespace qlora

@@ -551,6 +551,7 @@ __global__ __launch_bounds__(512) void k_qlora_fwd_gemm(FusedParams P) { fused_b
 __global__ __launch_bounds__(512) void k_qlora_dx_gemm(FusedParams P) { fused_body<128, true>(P); }
 
 hipError_t launch_fused(FusedParams P, bool dx, hipStream_t stream, int kernel_id) {
+  if (fused_wide_ok(P, dx)) return launch_fused_wide(P, stream, kernel_id);
   constexpr int bn = 128;
   // buffer offsets are 32-bit and the ranges are capped below 2 GiB
   if (P.M * P.lda * 2 > 0x7FFFFFF0LL || (P.r > 0 && P.M * P.ldat * 2 > 0x7FFFFFF0LL) ||

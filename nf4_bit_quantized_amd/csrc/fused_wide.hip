@@ -1,0 +1,498 @@
+// The forward product of the layer on 256 x 256 output tiles, with the NF4
+// restore done in registers by the multiplying waves themselves:
+//   Y = bf16( X W_hat^T + [sU_hi | sU_lo] [B | B]^T )
+//
+// "QLoRA技术从入门到精通" §3(2) restores the 4-bit weight to a 16-bit float at
+// compute time (table value times the block's stored scale) and discards it;
+// here every restored value goes straight from the restoring lane's registers
+// into v_mfma_f32_32x32x16_bf16 as its B operand and never reaches LDS or
+// memory.
+//
+// Layout of the work (gfx950: 256 CUs of 4 SIMDs, one workgroup of four waves
+// per CU, one wave per SIMD with 512 registers): the workgroup tile is 256
+// tokens x 256 output features; wave w owns output features 64w .. 64w+63 for
+// all 256 tokens (8 x 2 tiles of 32 x 32, 256 fp32 accumulators per lane).
+// No two waves restore the same weight.
+//
+// The contraction runs in steps of 64 (one absmax block of every weight row).
+// The B operand of v_mfma_f32_32x32x16_bf16 gives lane l the 8 contraction
+// values 8*(l/32) .. +7 of its slice at column l%32; the order in which a step's
+// 64 contraction values enter the four slices is free as long as both operands
+// use it, so slice ks of lane half h takes the 8 consecutive values of chunk
+// c = 4h + ks.  A lane of half h then needs bytes 16h .. 16h+15 of its weight
+// row's 32 packed bytes of the step: one 16-byte load, whose four words are
+// its four slices' B fragments once restored (8 indices -> 8 bf16 each).
+//
+// The activation operand (X, then the hi/lo pair of s*U for the rank-r tail)
+// is copied from global memory straight into one of three LDS stages
+// (buffer_load_dwordx4 ... lds); each wave copies a quarter of the rows.  A
+// rows are 128 B; chunk c of row R sits at position c ^ (R & 7) ^ ((R>>3) & 1),
+// so the fragment reads (16 lanes: 16 consecutive rows, one chunk) hit 16
+// distinct bank groups.  One barrier per step hands the stages over.
+//
+// Pipelining per step s (per wave): the A fragments of the next slice are read
+// while the current slice's 16 MFMAs run; two of the eight copies for step s+2
+// go out per slice; the packed words, scale codes and group constants of step
+// s+2 are loaded at the start of the step; the B fragments of step s+1 are
+// restored from the words loaded during step s-1, between the MFMAs.
+//
+// The rank-r term runs as extra contraction steps over the 2r columns of the
+// hi/lo split of s*U; its B fragments (B[n][kk mod r]) are loaded from global
+// memory directly.  Output: the fp32 tile is rounded to bf16 into LDS and
+// written with coalesced 16-byte stores.  The workgroup order is XCD-aware as
+// in the 256 x 128 kernel (two tile rows per XCD group, walked column by
+// column; rotated contraction start per tile row).
+#include "fused.hpp"
+#include "restore.hpp"
+#include "trace.hpp"
+
+namespace qlora {
+namespace {
+
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int A_BYTES = BM * BK * 2;                 // one A stage: 256 rows of 128 B
+constexpr int LDC = BN + 8;                          // epilogue bf16 row
+constexpr int EPI_BYTES = BM * LDC * 2;
+constexpr int LDS_BYTES = EPI_BYTES > 3 * A_BYTES ? EPI_BYTES : 3 * A_BYTES;
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, int64_t bytes) {
+  const int32_t n = bytes > 0x7FFFFFF0LL ? 0x7FFFFFF0 : (int32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, n, 0x00020000);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Weight data of one step for one lane: for each of its two 32-column tiles,
+// the 16 packed bytes of its half of the row's step segment, the aligned
+// dword holding the row block's scale code, and the group constant (or the
+// block's fp32 scale without the second level).
+struct Fetch {
+  u32x4_t w[2];
+  uint32_t code4[2];
+  float cg[2];
+};
+
+struct WCursor {
+  __amdgpu_buffer_rsrc_t rw, rc, rk;
+  uint32_t woff[2];  // byte offset of the lane's 16 bytes at contraction step 0
+  uint32_t coff[2];  // 64-weight chunk index of the lane's row at step 0
+  uint32_t nk, rot, bshift;
+};
+
+// Steps run in a rotated order per tile row: step s reads column block rot(s).
+__device__ __forceinline__ uint32_t rotated(uint32_t step, uint32_t rot, uint32_t nk) {
+  const uint32_t kt = step + rot;
+  return kt >= nk ? kt - nk : kt;
+}
+
+// Exactly six vector-memory loads per call (the waits below count them).
+template <bool DQ>
+__device__ __forceinline__ void fetch(Fetch& f, const WCursor& c, uint32_t step) {
+  const uint32_t kt = rotated(step, c.rot, c.nk);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    f.w[j] = __builtin_amdgcn_raw_buffer_load_b128(c.rw, c.woff[j], kt * 32u, 0);
+    const uint32_t blk = (c.coff[j] + kt) >> c.bshift;
+    // the codes array holds N*K/bs bytes, a multiple of 4, so the aligned dword is in
+    // range; without the second level the code load reads zero and cg is the block's scale
+    f.code4[j] = __builtin_amdgcn_raw_buffer_load_b32(c.rc, blk & ~3u, 0, 0);
+    f.cg[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(c.rk, (DQ ? blk >> 8 : blk) * 4, 0, 0));
+  }
+}
+
+// Bit position of the step's scale code inside the loaded dword.
+__device__ __forceinline__ uint32_t code_shift(const WCursor& c, int j, uint32_t step) {
+  const uint32_t kt = rotated(step, c.rot, c.nk);
+  return (((c.coff[j] + kt) >> c.bshift) & 3u) * 8u;
+}
+
+// Keep the scheduler from moving work on fetched registers above their use
+// (an early use of a late load would wait for every load issued before it).
+__device__ __forceinline__ void pin(Fetch& f) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    asm volatile("" : "+v"(f.w[j].x), "+v"(f.w[j].y), "+v"(f.w[j].z), "+v"(f.w[j].w));
+    asm volatile("" : "+v"(f.code4[j]), "+v"(f.cg[j]));
+  }
+}
+
+struct BFrag {
+  bf16x8_t b[2][4];  // [column tile][slice]
+};
+
+template <bool DQ>
+__device__ __forceinline__ RestoreTab block_tab(const Fetch& f, int j, uint32_t shift, const Nf4Table& tab) {
+  const float sc = DQ ? restored_scale((f.code4[j] >> shift) & 0xFFu, f.cg[j]) : f.cg[j];
+  return make_tab(tab, sc);
+}
+
+__device__ __forceinline__ void restore_word(uint32_t w, const RestoreTab& t, bf16x8_t& out) {
+  uint32_t o[4];
+  restore8(w, t, o);
+  const u32x4_t v = {o[0], o[1], o[2], o[3]};
+  out = __builtin_bit_cast(bf16x8_t, v);
+}
+
+// Rank-r tail B fragments of tail step t: B[n][kk mod r], kk = 64t + 8(4h + ks) + e.
+// TV: r is a multiple of 8, so each fragment is 8 consecutive elements of B's row.
+template <bool TV>
+__device__ __forceinline__ void tail_frags(const FusedParams& P, const int64_t (&n)[2], int h, uint32_t t, BFrag& B) {
+  const uint32_t r = (uint32_t)P.r;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const uint16_t* row = P.Bt + n[j] * P.ldbt;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint32_t kk = 64u * t + 8u * (4u * h + ks);
+      if (TV) {
+        B.b[j][ks] = *reinterpret_cast<const bf16x8_t*>(row + kk % r);
+      } else {
+        uint16_t e[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) e[q] = row[(kk + q) % r];
+        const u32x4_t v = {e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16),
+                           e[4] | ((uint32_t)e[5] << 16), e[6] | ((uint32_t)e[7] << 16)};
+        B.b[j][ks] = __builtin_bit_cast(bf16x8_t, v);
+      }
+    }
+  }
+}
+
+// Instruction order inside one slice: the next slice's fragment reads and the
+// slice's copies (plus, in slice 0, the step's weight loads) first, then the
+// 16 MFMAs, each followed by up to V vector instructions of the restore.
+template <int KS, int V>
+__device__ __forceinline__ void order_slice() {
+  __builtin_amdgcn_sched_group_barrier(0x100, KS < 3 ? 8 : 0, 0);  // LDS reads
+  __builtin_amdgcn_sched_group_barrier(0x020, KS == 0 ? 8 : 2, 0);  // weight loads (slice 0) and copies
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, V, 0);  // VALU
+  }
+}
+
+}  // namespace
+
+template <bool DQ, bool TV>
+__device__ __forceinline__ void fwd_wide_body(const FusedParams& P) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
+
+  // tile order: chunks of consecutive tiles go to one XCD; inside the order,
+  // groups of two tile rows are walked column by column
+  const int64_t ntiles = (int64_t)P.mt * P.nt;
+  const int64_t chunk = (ntiles + 7) / 8;
+  const int64_t order = (int64_t)(blockIdx.x % 8) * chunk + blockIdx.x / 8;
+  if (order >= ntiles) return;
+  const int gm = P.group_m;
+  const int64_t group = order / ((int64_t)gm * P.nt);
+  const int64_t first_m = group * gm;
+  const int64_t rows_in_group = (P.mt - first_m) < gm ? (P.mt - first_m) : gm;
+  const int64_t in_group = order - group * gm * P.nt;
+  const int64_t tm = first_m + in_group % rows_in_group;
+  const int64_t tn = in_group / rows_in_group;
+  const int64_t m0 = tm * BM, n0 = tn * BN;
+
+  const int lane = threadIdx.x & 63;
+  const int cw = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int h = lane >> 5, c32 = lane & 31;
+  // step counts and the tile row's rotation are wave-uniform (scalar registers)
+  const uint32_t nk = __builtin_amdgcn_readfirstlane((uint32_t)(P.K0 / BK));
+  const uint32_t ntail = P.r > 0 ? (uint32_t)((2 * (int64_t)P.r + BK - 1) / BK) : 0;
+  const uint32_t nsteps = __builtin_amdgcn_readfirstlane(nk + ntail);
+  const uint32_t rot = __builtin_amdgcn_readfirstlane((uint32_t)((tm * 5) % nk));
+
+  // the lane's weight rows (clamped: rows beyond the output feed unstored columns)
+  int64_t nrow[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int64_t n = n0 + 64 * cw + 32 * j + c32;
+    nrow[j] = n < P.N ? n : P.N - 1;
+  }
+  WCursor wc;
+  {
+    wc.rw = rsrc(P.packed, P.N * P.Kw / 2);
+    const int64_t nblocks = (P.N * P.Kw / 64) >> P.bshift;
+    wc.rc = rsrc(P.codes, DQ ? nblocks : 0);
+    wc.rk = rsrc(P.consts, DQ ? ((nblocks + 255) / 256) * 4 : nblocks * 4);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      wc.woff[j] = (uint32_t)(nrow[j] * (P.Kw / 2) + 16 * h);
+      wc.coff[j] = (uint32_t)(nrow[j] * (P.Kw / 64));
+    }
+    wc.nk = nk;
+    wc.rot = rot;
+    wc.bshift = (uint32_t)P.bshift;
+  }
+  const Nf4Table tab = P.tab;
+
+  // fragment addresses: row 32i + c32, chunk 4h + ks at position (4h + ks) ^ x
+  const uint32_t arow = (uint32_t)(c32 * 128);
+  const int x = (c32 & 7) ^ ((c32 >> 3) & 1);
+  uint32_t apos[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) apos[ks] = (uint32_t)(((4 * h + ks) ^ x) * 16);
+
+  f32x16_t acc[8][2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  // copies: steps < nk read the rotated column block of X, step nk + t the
+  // hi/lo columns 64t .. 64t+63; steps past the last repeat the last one.
+  // Copy j of this wave covers rows 64cw + 8j .. +7 of the stage: lane l lands
+  // at byte 16l of it (row 64cw + 8j + l/8, position l%8) and so fetches
+  // chunk (l%8) ^ (l/8) ^ (j%2) of that row.  Rows beyond the output are
+  // clamped to the last row (they only feed output rows never stored).
+  uint32_t crow[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int64_t row = m0 + 64 * cw + 8 * j + (lane >> 3);
+    crow[j] = (uint32_t)(row < P.M ? row : P.M - 1);
+  }
+  const uint32_t chunk16[2] = {(uint32_t)(((lane & 7) ^ (lane >> 3)) * 16),
+                               (uint32_t)(((lane & 7) ^ (lane >> 3) ^ 1) * 16)};
+  const __amdgpu_buffer_rsrc_t rx = rsrc(P.A, P.M * P.lda * 2);
+  uint32_t xoff[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) xoff[j] = crow[j] * (uint32_t)(P.lda * 2) + chunk16[j & 1];
+  auto stage = [&](uint32_t s) { return lds + (s % 3) * A_BYTES; };
+  auto lds_dst = [&](uint32_t c, int j) { return (lds_void_t*)(stage(c) + (64 * cw + 8 * j) * 128); };
+  // copy j of a step c < nk (X)
+  auto copy_x = [&](uint32_t c, int j) {
+    const uint32_t col = __builtin_amdgcn_readfirstlane(rotated(c, rot, nk) * (BK * 2));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lds_dst(c, j), 16, xoff[j], col, 0, 0);
+  };
+  // copy j of any step c (X, or the hi/lo pairs, or a repeat of the last step)
+  auto copy = [&](uint32_t c, int j) {
+    const uint32_t cc = c < nsteps ? c : nsteps - 1;
+    if (cc < nk) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lds_dst(c, j), 16, xoff[j],
+                                               __builtin_amdgcn_readfirstlane(rotated(cc, rot, nk) * (BK * 2)), 0, 0);
+    } else {
+      const __amdgpu_buffer_rsrc_t rt = rsrc(P.At, P.M * P.ldat * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, lds_dst(c, j), 16, crow[j] * (uint32_t)(P.ldat * 2) + chunk16[j & 1],
+                                               __builtin_amdgcn_readfirstlane((cc - nk) * (BK * 2)), 0, 0);
+    }
+  };
+  auto read_a = [&](bf16x8_t (&a)[8], const uint8_t* As, int ks) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = *reinterpret_cast<const bf16x8_t*>(As + arow + i * 4096 + apos[ks]);
+  };
+  auto mma = [&](const bf16x8_t (&a)[8], const BFrag& B, int ks) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], B.b[j][ks], acc[i][j], 0, 0, 0);
+  };
+
+  // B fragments of one slice (both column tiles).
+  struct BS {
+    bf16x8_t b[2];
+  };
+  auto mma_s = [&](const bf16x8_t (&a)[8], const BS& B) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], B.b[j], acc[i][j], 0, 0, 0);
+  };
+  auto word = [](const Fetch& f, int j, int ks) {
+    return ks == 0 ? f.w[j].x : ks == 1 ? f.w[j].y : ks == 2 ? f.w[j].z : f.w[j].w;
+  };
+  auto restore_slice = [&](const Fetch& f, const RestoreTab (&t)[2], int ks, BS& out) {
+    restore_word(word(f, 0, ks), t[0], out.b[0]);
+    restore_word(word(f, 1, ks), t[1], out.b[1]);
+  };
+
+  // A weight step s: the B fragments of each slice are restored one slice
+  // ahead, between the MFMAs of the slice before.  On entry fa holds step s's
+  // weight data (its first slice already restored into b0, with tables t), fb
+  // step s+1's (loaded or in flight); step s+2's is loaded into fc in slice 0.
+  // Slices 1-3 of step s come from fa; when step s+1 is a weight step, its
+  // tables are built from fb in slices 2 and 3 and its first slice restored in
+  // slice 3 (into b0 and t for the next step).  Each step issues six weight
+  // loads and eight copies, so step s+1's copies (issued during step s-1) have
+  // landed once at most 14 vector-memory operations are in flight.
+  auto weight_step = [&](uint32_t s, const Fetch& fa, Fetch& fb, Fetch& fc, RestoreTab (&t)[2], BS& b0,
+                         bool next_weight, auto cp) {
+    const uint8_t* As = stage(s);
+    bf16x8_t a0[8], a1[8];
+    BS b1, b2, b3;
+    read_a(a0, As, 0);
+    // slice 0
+    fetch<DQ>(fc, wc, s + 2 < nk ? s + 2 : nk - 1);
+    read_a(a1, As, 1);
+    cp(s + 2, 0);
+    cp(s + 2, 1);
+    mma_s(a0, b0);
+    restore_slice(fa, t, 1, b1);
+    order_slice<0, 5>();
+    // slice 1
+    read_a(a0, As, 2);
+    cp(s + 2, 2);
+    cp(s + 2, 3);
+    mma_s(a1, b1);
+    restore_slice(fa, t, 2, b2);
+    order_slice<1, 5>();
+    // slice 2
+    read_a(a1, As, 3);
+    cp(s + 2, 4);
+    cp(s + 2, 5);
+    mma_s(a0, b2);
+    restore_slice(fa, t, 3, b3);
+    if (next_weight) {
+      pin(fb);
+      t[0] = block_tab<DQ>(fb, 0, code_shift(wc, 0, s + 1), tab);
+    }
+    order_slice<2, 7>();
+    // slice 3
+    cp(s + 2, 6);
+    cp(s + 2, 7);
+    mma_s(a1, b3);
+    if (next_weight) {
+      t[1] = block_tab<DQ>(fb, 1, code_shift(wc, 1, s + 1), tab);
+      restore_slice(fb, t, 0, b0);
+    }
+    order_slice<3, 7>();
+    wait_vm<14>();
+    lds_barrier();
+  };
+
+  // A step of the rank-r tail: all of its B fragments (B[n][kk mod r]) were
+  // loaded during the step before; the next tail step's are loaded now.  Same
+  // copies and loads per step as above.
+  auto tail_step = [&](uint32_t s, const BFrag& cur, BFrag& nxt, Fetch& fs) {
+    const uint8_t* As = stage(s);
+    fetch<DQ>(fs, wc, nk - 1);
+    if (s + 1 < nsteps) tail_frags<TV>(P, nrow, h, s + 1 - nk, nxt);
+    bf16x8_t a0[8], a1[8];
+    read_a(a0, As, 0);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (ks < 3) read_a(a1, As, ks + 1);
+      copy(s + 2, 2 * ks);
+      copy(s + 2, 2 * ks + 1);
+      mma(a0, cur, ks);
+      if (ks < 3) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a0[i] = a1[i];
+      }
+    }
+    wait_vm<14>();
+    lds_barrier();
+  };
+
+  // prologue: weight data of steps 0 and 1, copies of steps 0 and 1, the
+  // tables and the first slice of step 0
+  Fetch fA, fB, fC;
+  fetch<DQ>(fA, wc, 0);
+  fetch<DQ>(fB, wc, 1 < nk ? 1 : nk - 1);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) copy(0, j);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) copy(1, j);
+  RestoreTab t[2];
+  BS b0;
+  t[0] = block_tab<DQ>(fA, 0, code_shift(wc, 0, 0), tab);
+  t[1] = block_tab<DQ>(fA, 1, code_shift(wc, 1, 0), tab);
+  restore_slice(fA, t, 0, b0);
+  wait_vm<8>();  // step 0's copies have landed (step 1's may be in flight)
+  lds_barrier();
+
+  // weight steps, three per iteration (the weight-data registers rotate)
+  // while all copy X for step s+2; then the last ones, whose copies may
+  // reach the rank-r tail
+  uint32_t s = 0;
+  for (; s + 4 < nk; s += 3) {
+    weight_step(s, fA, fB, fC, t, b0, true, copy_x);
+    weight_step(s + 1, fB, fC, fA, t, b0, true, copy_x);
+    weight_step(s + 2, fC, fA, fB, t, b0, true, copy_x);
+  }
+  for (; s < nk; ++s) {
+    weight_step(s, fA, fB, fC, t, b0, s + 1 < nk, copy);
+    const Fetch tmp = fA;
+    fA = fB;
+    fB = fC;
+    fC = tmp;
+  }
+  // the rank-r tail
+  if (s < nsteps) {
+    BFrag bc, bn;
+    tail_frags<TV>(P, nrow, h, 0, bc);
+    for (; s < nsteps; ++s) {
+      tail_step(s, bc, bn, fA);
+      bc = bn;
+    }
+  }
+
+  // the last copies (into stages no one reads) land before the output tile
+  // goes over the A stages: every wave's own, then a barrier
+  wait_vm<0>();
+  lds_barrier();
+
+  // epilogue: bf16 tile into LDS, then coalesced 16-byte stores
+  uint16_t* ctile = reinterpret_cast<uint16_t*>(lds);
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = 64 * cw + 32 * j + c32;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+        ctile[row * LDC + col] = f32_to_bf16_bits(acc[i][j][v]);
+      }
+    }
+  lds_barrier();
+  for (int c = threadIdx.x; c < BM * (BN / 8); c += 256) {
+    const int row = c / (BN / 8), cc = (c % (BN / 8)) * 8;
+    const int64_t gr = m0 + row, gc = n0 + cc;
+    if (gr >= P.M || gc >= P.N) continue;
+    *reinterpret_cast<uint4*>(P.C + gr * P.ldc + gc) = *reinterpret_cast<const uint4*>(ctile + row * LDC + cc);
+  }
+}
+
+// DQ: 8-bit scale codes (else fp32 block scales); TV: r is a multiple of 8
+__global__ __launch_bounds__(256, 1) void k_qlora_fwd_wide(FusedParams P) { fwd_wide_body<true, true>(P); }
+__global__ __launch_bounds__(256, 1) void k_qlora_fwd_wide_r(FusedParams P) { fwd_wide_body<true, false>(P); }
+__global__ __launch_bounds__(256, 1) void k_qlora_fwd_wide_f32s(FusedParams P) { fwd_wide_body<false, true>(P); }
+__global__ __launch_bounds__(256, 1) void k_qlora_fwd_wide_f32s_r(FusedParams P) { fwd_wide_body<false, false>(P); }
+
+// 256 x 256 tiles: worth it when the tile count fills the GPU at least twice.
+bool fused_wide_ok(const FusedParams& P, bool dx) {
+  if (dx) return false;
+  const int64_t tiles = ((P.M + BM - 1) / BM) * ((P.N + BN - 1) / BN);
+  return tiles >= 512 && P.K0 % BK == 0 && !P.accumulate;
+}
+
+hipError_t launch_fused_wide(FusedParams P, hipStream_t stream, int kernel_id) {
+  P.mt = (int32_t)((P.M + BM - 1) / BM);
+  P.nt = (int32_t)((P.N + BN - 1) / BN);
+  P.group_m = 2;
+  P.tab = level_table(P.table);
+  const int64_t ntiles = (int64_t)P.mt * P.nt;
+  const unsigned grid = (unsigned)(((ntiles + 7) / 8) * 8);
+  KernelEvents ev(kernel_id);
+  const bool tv = P.r % 8 == 0;
+  if (P.dq) {
+    if (tv) hipExtLaunchKernelGGL(k_qlora_fwd_wide, dim3(grid), dim3(256), 0, stream, ev.start(), ev.stop(), 0, P);
+    else hipExtLaunchKernelGGL(k_qlora_fwd_wide_r, dim3(grid), dim3(256), 0, stream, ev.start(), ev.stop(), 0, P);
+  } else {
+    if (tv) hipExtLaunchKernelGGL(k_qlora_fwd_wide_f32s, dim3(grid), dim3(256), 0, stream, ev.start(), ev.stop(), 0, P);
+    else hipExtLaunchKernelGGL(k_qlora_fwd_wide_f32s_r, dim3(grid), dim3(256), 0, stream, ev.start(), ev.stop(), 0, P);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace qlora

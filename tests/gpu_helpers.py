@@ -43,6 +43,19 @@ def normwise_err(got, want) -> float:
     return float(np.max(np.abs(got - want)) / scale)
 
 
+def elementwise_stats(got, want, floor: float = 1e-3) -> dict:
+    """Element-by-element error beside the normwise bar: the largest
+    |got - want| / (|want| + floor * max|want|) and the share of elements
+    above 1e-2 on that scale (a local fault -- one wrong block scale, a wrong
+    tail column -- shows here even when it is small against the tensor's
+    largest entry)."""
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    den = np.abs(want) + floor * max(float(np.max(np.abs(want))), 1e-300)
+    rel = np.abs(got - want) / den
+    return {"max_rel": float(np.max(rel)), "share_above_1e-2": float(np.mean(rel > 1e-2))}
+
+
 def oracle_quantized(W):
     return onf4.quantize(W)
 
