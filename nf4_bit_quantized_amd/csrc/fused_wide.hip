@@ -53,7 +53,7 @@ constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int A_BYTES = BM * BK * 2;                 // one A stage: 256 rows of 128 B
 constexpr int LDC = BN + 8;                          // epilogue bf16 row
 constexpr int EPI_BYTES = BM * LDC * 2;
-constexpr int LDS_BYTES = EPI_BYTES > 3 * A_BYTES ? EPI_BYTES : 3 * A_BYTES;
+constexpr int LDS_BYTES = EPI_BYTES > 4 * A_BYTES ? EPI_BYTES : 4 * A_BYTES;
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -137,6 +137,73 @@ __device__ __forceinline__ void restore_word(uint32_t w, const RestoreTab& t, bf
   restore8(w, t, o);
   const u32x4_t v = {o[0], o[1], o[2], o[3]};
   out = __builtin_bit_cast(bf16x8_t, v);
+}
+
+// The restore of one packed word (restore8) and the table of one block
+// (make_tab), cut into pieces of a few vector instructions each, so that a
+// wave can place one piece between consecutive MFMAs of its own.  The pieces
+// compute exactly what restore8 / make_tab compute.
+struct WordWork {
+  uint32_t sl, s2, HE, LE, HO, LO;
+};
+
+template <int PIECE>
+__device__ __forceinline__ void word_piece(uint32_t w, const RestoreTab& t, WordWork& s, bf16x8_t& out) {
+  if (PIECE == 0) {
+    selectors_even(w, s.sl, s.s2);
+  } else if (PIECE == 1) {
+    s.HE = perm(perm(t.h[3], t.h[2], s.sl), perm(t.h[1], t.h[0], s.sl), s.s2);
+  } else if (PIECE == 2) {
+    s.LE = perm(perm(t.l[3], t.l[2], s.sl), perm(t.l[1], t.l[0], s.sl), s.s2);
+  } else if (PIECE == 3) {
+    selectors_odd(w, s.sl, s.s2);
+  } else if (PIECE == 4) {
+    lookup4(s.sl, s.s2, t, s.HO, s.LO);
+  } else if (PIECE == 5) {  // bf16 pairs (e0,e2) (e4,e6) (e1,e3) (e5,e7), kept in the same fields
+    const uint32_t e01 = perm(s.HE, s.LE, 0x05010400u), e23 = perm(s.HE, s.LE, 0x07030602u);
+    const uint32_t o01 = perm(s.HO, s.LO, 0x05010400u), o23 = perm(s.HO, s.LO, 0x07030602u);
+    s.HE = e01;
+    s.LE = e23;
+    s.HO = o01;
+    s.LO = o23;
+  } else {
+    const u32x4_t v = {perm(s.HO, s.HE, 0x05040100u), perm(s.HO, s.HE, 0x07060302u), perm(s.LO, s.LE, 0x05040100u),
+                       perm(s.LO, s.LE, 0x07060302u)};
+    out = __builtin_bit_cast(bf16x8_t, v);
+  }
+}
+
+// The table of a block shared by the two halves of the wave (lanes l and
+// l + 32 restore the same weight row, so the same block): each half forms
+// the bf16 values of eight of the sixteen levels (half h: levels 8h .. 8h+7,
+// lvh = its eight levels), and v_permlane32_swap hands each half the other's.
+// Piece 0 forms the restored scale, pieces 1 and 2 four values each, pieces
+// 3 and 4 exchange them.  The result equals make_tab's.
+struct TabWork {
+  float sc;
+  uint32_t p[4];
+};
+
+template <bool DQ, int Q>
+__device__ __forceinline__ void tab_piece(const Fetch& f, int j, uint32_t shift, const float (&lvh)[8], TabWork& s,
+                                          RestoreTab& t) {
+  if (Q == 0) {
+    s.sc = DQ ? restored_scale((f.code4[j] >> shift) & 0xFFu, f.cg[j]) : f.cg[j];
+  } else if (Q == 1 || Q == 2) {
+    const int q = Q - 1;
+    const uint32_t w0 = pack_bf16x2(lvh[4 * q] * s.sc, lvh[4 * q + 1] * s.sc);
+    const uint32_t w1 = pack_bf16x2(lvh[4 * q + 2] * s.sc, lvh[4 * q + 3] * s.sc);
+    s.p[2 * q] = perm(w1, w0, 0x07050301u);      // half 0: h[q]; half 1: h[q + 2]
+    s.p[2 * q + 1] = perm(w1, w0, 0x06040200u);  // half 0: l[q]; half 1: l[q + 2]
+  } else {
+    const int q = Q - 3;
+    const auto hx = __builtin_amdgcn_permlane32_swap(s.p[2 * q], s.p[2 * q], false, false);
+    const auto lx = __builtin_amdgcn_permlane32_swap(s.p[2 * q + 1], s.p[2 * q + 1], false, false);
+    t.h[q] = hx[0];
+    t.h[q + 2] = hx[1];
+    t.l[q] = lx[0];
+    t.l[q + 2] = lx[1];
+  }
 }
 
 // Rank-r tail B fragments of tail step t: B[n][kk mod r], kk = 64t + 8(4h + ks) + e.
@@ -231,6 +298,9 @@ __device__ __forceinline__ void fwd_wide_body(const FusedParams& P) {
     wc.bshift = (uint32_t)P.bshift;
   }
   const Nf4Table tab = P.tab;
+  float lvh[8];  // the eight levels whose restored values this half of the wave forms
+#pragma unroll
+  for (int i = 0; i < 8; ++i) lvh[i] = h ? tab.level[8 + i] : tab.level[i];
 
   // fragment addresses: row 32i + c32, chunk 4h + ks at position (4h + ks) ^ x
   const uint32_t arow = (uint32_t)(c32 * 128);
@@ -265,7 +335,7 @@ __device__ __forceinline__ void fwd_wide_body(const FusedParams& P) {
   uint32_t xoff[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) xoff[j] = crow[j] * (uint32_t)(P.lda * 2) + chunk16[j & 1];
-  auto stage = [&](uint32_t s) { return lds + (s % 3) * A_BYTES; };
+  auto stage = [&](uint32_t s) { return lds + (s & 3) * A_BYTES; };
   auto lds_dst = [&](uint32_t c, int j) { return (lds_void_t*)(stage(c) + (64 * cw + 8 * j) * 128); };
   // copy j of a step c < nk (X)
   auto copy_x = [&](uint32_t c, int j) {
@@ -324,114 +394,188 @@ __device__ __forceinline__ void fwd_wide_body(const FusedParams& P) {
   // slice 3 (into b0 and t for the next step).  Each step issues six weight
   // loads and eight copies, so step s+1's copies (issued during step s-1) have
   // landed once at most 14 vector-memory operations are in flight.
-  auto weight_step = [&](uint32_t s, const Fetch& fa, Fetch& fb, Fetch& fc, RestoreTab (&t)[2], BS& b0,
-                         bool next_weight, auto cp) {
+  //
+  // Each slice is written as 16 beats, one MFMA each, with the beat's share
+  // of the other work after it (one fragment read of the next slice in beats
+  // 0-7, a copy in beats 4 and 12, the weight loads in beat 1 of slice 0, one
+  // piece of the restore); a scheduling barrier closes every beat, so the
+  // vector work of the restore runs beside the MFMAs of the same wave.
+  auto weight_step = [&](uint32_t s, bf16x8_t (&a0)[8], const Fetch& fa, Fetch& fb, Fetch& fc, RestoreTab (&t)[2],
+                         BS& b0, auto cp) {
     const uint8_t* As = stage(s);
-    bf16x8_t a0[8], a1[8];
-    BS b1, b2, b3;
-    read_a(a0, As, 0);
-    // slice 0
-    fetch<DQ>(fc, wc, s + 2 < nk ? s + 2 : nk - 1);
-    read_a(a1, As, 1);
-    cp(s + 2, 0);
-    cp(s + 2, 1);
-    mma_s(a0, b0);
-    restore_slice(fa, t, 1, b1);
-    order_slice<0, 5>();
-    // slice 1
-    read_a(a0, As, 2);
-    cp(s + 2, 2);
-    cp(s + 2, 3);
-    mma_s(a1, b1);
-    restore_slice(fa, t, 2, b2);
-    order_slice<1, 5>();
-    // slice 2
-    read_a(a1, As, 3);
-    cp(s + 2, 4);
-    cp(s + 2, 5);
-    mma_s(a0, b2);
-    restore_slice(fa, t, 3, b3);
-    if (next_weight) {
-      pin(fb);
-      t[0] = block_tab<DQ>(fb, 0, code_shift(wc, 0, s + 1), tab);
-    }
-    order_slice<2, 7>();
-    // slice 3
-    cp(s + 2, 6);
-    cp(s + 2, 7);
-    mma_s(a1, b3);
-    if (next_weight) {
-      t[1] = block_tab<DQ>(fb, 1, code_shift(wc, 1, s + 1), tab);
-      restore_slice(fb, t, 0, b0);
-    }
-    order_slice<3, 7>();
-    wait_vm<14>();
-    lds_barrier();
-  };
-
-  // A step of the rank-r tail: all of its B fragments (B[n][kk mod r]) were
-  // loaded during the step before; the next tail step's are loaded now.  Same
-  // copies and loads per step as above.
-  auto tail_step = [&](uint32_t s, const BFrag& cur, BFrag& nxt, Fetch& fs) {
-    const uint8_t* As = stage(s);
-    fetch<DQ>(fs, wc, nk - 1);
-    if (s + 1 < nsteps) tail_frags<TV>(P, nrow, h, s + 1 - nk, nxt);
-    bf16x8_t a0[8], a1[8];
-    read_a(a0, As, 0);
+    const uint8_t* An = stage(s + 1);
+    bf16x8_t a1[8];
+    BS bs[3];
+    WordWork w0, w1;
+    TabWork tw0, tw1;
+    RestoreTab tn[2];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      if (ks < 3) read_a(a1, As, ks + 1);
-      copy(s + 2, 2 * ks);
-      copy(s + 2, 2 * ks + 1);
-      mma(a0, cur, ks);
-      if (ks < 3) {
+      const bf16x8_t(&ac)[8] = ks % 2 == 0 ? a0 : a1;
+      bf16x8_t(&an)[8] = ks % 2 == 0 ? a1 : a0;
+      const BS& bcur = ks == 0 ? b0 : bs[ks - 1];
+      if (ks == 3) {
+        // step s+1's copies (issued during step s-2) have landed: after them
+        // this wave issued step s-1's six loads and eight copies and six
+        // loads and six copies of this step
+        wait_vm<26>();
+        lds_barrier();
+      }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) a0[i] = a1[i];
+      for (int m = 0; m < 16; ++m) {
+        acc[m >> 1][m & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ac[m >> 1], bcur.b[m & 1], acc[m >> 1][m & 1], 0, 0, 0);
+        // fragments of the next slice; in slice 3, those of step s+1's first slice
+        if (m < 8) an[m] = *reinterpret_cast<const bf16x8_t*>((ks < 3 ? As : An) + arow + m * 4096 + apos[(ks + 1) & 3]);
+        if (m == 4 || m == 12) cp(s + 3, 2 * ks + (m == 12));
+        if (ks == 0 && m == 1) fetch<DQ>(fc, wc, s + 2 < nk ? s + 2 : nk - 1);
+        // restore pieces: A = tile 0's word, B = tile 1's
+        const uint32_t sh0 = code_shift(wc, 0, s + 1), sh1 = code_shift(wc, 1, s + 1);
+        if (ks < 3) {
+          // slices 0-2: restore slice ks+1 of step s (pieces of the two tiles
+          // alternating in beats 0-13), then pieces of step s+1's tables
+          BS& o = bs[ks];
+          const uint32_t wa = word(fa, 0, ks + 1), wb = word(fa, 1, ks + 1);
+          switch (m) {
+            case 0: word_piece<0>(wa, t[0], w0, o.b[0]); break;
+            case 1: word_piece<0>(wb, t[1], w1, o.b[1]); break;
+            case 2: word_piece<1>(wa, t[0], w0, o.b[0]); break;
+            case 3: word_piece<1>(wb, t[1], w1, o.b[1]); break;
+            case 4: word_piece<2>(wa, t[0], w0, o.b[0]); break;
+            case 5: word_piece<2>(wb, t[1], w1, o.b[1]); break;
+            case 6: word_piece<3>(wa, t[0], w0, o.b[0]); break;
+            case 7: word_piece<3>(wb, t[1], w1, o.b[1]); break;
+            case 8: word_piece<4>(wa, t[0], w0, o.b[0]); break;
+            case 9: word_piece<4>(wb, t[1], w1, o.b[1]); break;
+            case 10: word_piece<5>(wa, t[0], w0, o.b[0]); break;
+            case 11: word_piece<5>(wb, t[1], w1, o.b[1]); break;
+            case 12: word_piece<6>(wa, t[0], w0, o.b[0]); break;
+            case 13:
+              word_piece<6>(wb, t[1], w1, o.b[1]);
+              if (ks == 0) pin(fb);
+              break;
+            case 14:
+              if (ks == 0) tab_piece<DQ, 0>(fb, 0, sh0, lvh, tw0, tn[0]);
+              if (ks == 1) tab_piece<DQ, 2>(fb, 0, sh0, lvh, tw0, tn[0]);
+              if (ks == 2) tab_piece<DQ, 4>(fb, 0, sh0, lvh, tw0, tn[0]);
+              break;
+            case 15:
+              if (ks == 0) tab_piece<DQ, 1>(fb, 0, sh0, lvh, tw0, tn[0]);
+              if (ks == 1) tab_piece<DQ, 3>(fb, 0, sh0, lvh, tw0, tn[0]);
+              if (ks == 2) tab_piece<DQ, 0>(fb, 1, sh1, lvh, tw1, tn[1]);
+              break;
+            default: break;
+          }
+        } else {
+          // slice 3: the rest of step s+1's tile 1 table, and step s+1's first slice
+          const uint32_t wa = word(fb, 0, 0), wb = word(fb, 1, 0);
+          switch (m) {
+            case 0: tab_piece<DQ, 1>(fb, 1, sh1, lvh, tw1, tn[1]); break;
+            case 1: word_piece<0>(wa, tn[0], w0, b0.b[0]); break;
+            case 2: tab_piece<DQ, 2>(fb, 1, sh1, lvh, tw1, tn[1]); break;
+            case 3: word_piece<1>(wa, tn[0], w0, b0.b[0]); break;
+            case 4: tab_piece<DQ, 3>(fb, 1, sh1, lvh, tw1, tn[1]); break;
+            case 5: word_piece<2>(wa, tn[0], w0, b0.b[0]); break;
+            case 6: tab_piece<DQ, 4>(fb, 1, sh1, lvh, tw1, tn[1]); break;
+            case 7: word_piece<3>(wa, tn[0], w0, b0.b[0]); break;
+            case 8: word_piece<0>(wb, tn[1], w1, b0.b[1]); break;
+            case 9: word_piece<4>(wa, tn[0], w0, b0.b[0]); break;
+            case 10: word_piece<1>(wb, tn[1], w1, b0.b[1]); break;
+            case 11: word_piece<5>(wa, tn[0], w0, b0.b[0]); break;
+            case 12: word_piece<2>(wb, tn[1], w1, b0.b[1]); break;
+            case 13:
+              word_piece<6>(wa, tn[0], w0, b0.b[0]);
+              word_piece<3>(wb, tn[1], w1, b0.b[1]);
+              break;
+            case 14: word_piece<4>(wb, tn[1], w1, b0.b[1]); break;
+            case 15:
+              word_piece<5>(wb, tn[1], w1, b0.b[1]);
+              word_piece<6>(wb, tn[1], w1, b0.b[1]);
+              break;
+            default: break;
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    wait_vm<14>();
-    lds_barrier();
+    t[0] = tn[0];
+    t[1] = tn[1];
   };
 
-  // prologue: weight data of steps 0 and 1, copies of steps 0 and 1, the
-  // tables and the first slice of step 0
+  // The last weight step (its next step is the rank-r tail's, or none) and
+  // the tail steps: the same loads, copies and barrier as a weight step, with
+  // the B fragments of a tail step (B[n][kk mod r]) loaded during the step
+  // before it.  `bnext` receives the next step's fragments when there is one.
+  auto plain_step = [&](uint32_t s, bf16x8_t (&a0)[8], auto&& bslice, Fetch& fc, BFrag& bnext) {
+    const uint8_t* As = stage(s);
+    const uint8_t* An = stage(s + 1);
+    bf16x8_t a1[8];
+    fetch<DQ>(fc, wc, nk - 1);
+    if (s + 1 < nsteps) tail_frags<TV>(P, nrow, h, s + 1 - nk, bnext);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (ks == 3) {
+        wait_vm<26>();
+        lds_barrier();
+      }
+      bf16x8_t(&ac)[8] = ks % 2 == 0 ? a0 : a1;
+      bf16x8_t(&an)[8] = ks % 2 == 0 ? a1 : a0;
+      read_a(an, ks < 3 ? As : An, (ks + 1) & 3);
+      copy(s + 3, 2 * ks);
+      copy(s + 3, 2 * ks + 1);
+      const BS b = bslice(ks);
+      mma_s(ac, b);
+    }
+  };
+
+  // prologue: weight data of steps 0 and 1, copies of steps 0, 1 and 2, the
+  // tables and first slice of step 0, and that slice's A fragments
   Fetch fA, fB, fC;
   fetch<DQ>(fA, wc, 0);
   fetch<DQ>(fB, wc, 1 < nk ? 1 : nk - 1);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) copy(0, j);
+  for (int c = 0; c < 3; ++c)
 #pragma unroll
-  for (int j = 0; j < 8; ++j) copy(1, j);
+    for (int j = 0; j < 8; ++j) copy(c, j);
   RestoreTab t[2];
   BS b0;
   t[0] = block_tab<DQ>(fA, 0, code_shift(wc, 0, 0), tab);
   t[1] = block_tab<DQ>(fA, 1, code_shift(wc, 1, 0), tab);
   restore_slice(fA, t, 0, b0);
-  wait_vm<8>();  // step 0's copies have landed (step 1's may be in flight)
+  wait_vm<8>();  // steps 0 and 1 have landed (step 2 may be in flight)
   lds_barrier();
+  bf16x8_t a0[8];
+  read_a(a0, stage(0), 0);
 
   // weight steps, three per iteration (the weight-data registers rotate)
-  // while all copy X for step s+2; then the last ones, whose copies may
+  // while all copy X for step s+3; then the last ones, whose copies may
   // reach the rank-r tail
   uint32_t s = 0;
-  for (; s + 4 < nk; s += 3) {
-    weight_step(s, fA, fB, fC, t, b0, true, copy_x);
-    weight_step(s + 1, fB, fC, fA, t, b0, true, copy_x);
-    weight_step(s + 2, fC, fA, fB, t, b0, true, copy_x);
+  for (; s + 5 < nk; s += 3) {
+    weight_step(s, a0, fA, fB, fC, t, b0, copy_x);
+    weight_step(s + 1, a0, fB, fC, fA, t, b0, copy_x);
+    weight_step(s + 2, a0, fC, fA, fB, t, b0, copy_x);
   }
-  for (; s < nk; ++s) {
-    weight_step(s, fA, fB, fC, t, b0, s + 1 < nk, copy);
+  for (; s + 1 < nk; ++s) {
+    weight_step(s, a0, fA, fB, fC, t, b0, copy);
     const Fetch tmp = fA;
     fA = fB;
     fB = fC;
     fC = tmp;
   }
-  // the rank-r tail
-  if (s < nsteps) {
-    BFrag bc, bn;
-    tail_frags<TV>(P, nrow, h, 0, bc);
+  {
+    // the last weight step: slices 1-3 restored from fA as it goes
+    BFrag bn;
+    BS bl[4];
+    bl[0] = b0;
+    restore_slice(fA, t, 1, bl[1]);
+    restore_slice(fA, t, 2, bl[2]);
+    restore_slice(fA, t, 3, bl[3]);
+    plain_step(s, a0, [&](int ks) { return bl[ks]; }, fC, bn);
+    ++s;
+    // the rank-r tail
+    BFrag bc = bn;
     for (; s < nsteps; ++s) {
-      tail_step(s, bc, bn, fA);
+      plain_step(s, a0, [&](int ks) { BS b; b.b[0] = bc.b[0][ks]; b.b[1] = bc.b[1][ks]; return b; }, fC, bn);
       bc = bn;
     }
   }

@@ -36,11 +36,30 @@ __device__ __forceinline__ RestoreTab make_tab(const Nf4Table& tab, float sc) {
   return t;
 }
 
-// n holds four 4-bit indices, one per byte; returns the high and low bytes of
-// their restored bf16 values, one per byte.
-__device__ __forceinline__ void lookup4(uint32_t n, const RestoreTab& t, uint32_t& H, uint32_t& L) {
-  const uint32_t sl = n & 0x07070707u;
-  const uint32_t s2 = ((n >> 1) & 0x04040404u) | 0x03020100u;
+// Byte selectors of four 4-bit indices: sl picks, in each byte, the index's
+// entry inside the low (0-7) or high (8-15) half of a table (its low three
+// bits), s2 then picks per byte between the two halves' results (bit 3).
+// Even elements are the high nibbles of the packed word, odd ones the low
+// nibbles; the selectors are formed straight from the word.
+// (x & 0x04040404) | 0x03020100 as one v_and_or_b32: its two constants are
+// held in vector registers, since a VOP3 instruction takes neither two scalar
+// operands nor a literal here.
+__device__ __forceinline__ uint32_t half_select(uint32_t x) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(0x04040404u), "v"(0x03020100u));
+  return r;
+}
+__device__ __forceinline__ void selectors_even(uint32_t w, uint32_t& sl, uint32_t& s2) {
+  sl = (w >> 4) & 0x07070707u;
+  s2 = half_select(w >> 5);
+}
+__device__ __forceinline__ void selectors_odd(uint32_t w, uint32_t& sl, uint32_t& s2) {
+  sl = w & 0x07070707u;
+  s2 = half_select(w >> 1);
+}
+
+// The high and low bytes of the four restored values the selectors name, one per byte.
+__device__ __forceinline__ void lookup4(uint32_t sl, uint32_t s2, const RestoreTab& t, uint32_t& H, uint32_t& L) {
   H = perm(perm(t.h[3], t.h[2], sl), perm(t.h[1], t.h[0], sl), s2);
   L = perm(perm(t.l[3], t.l[2], sl), perm(t.l[1], t.l[0], sl), s2);
 }
@@ -48,9 +67,11 @@ __device__ __forceinline__ void lookup4(uint32_t n, const RestoreTab& t, uint32_
 // One packed word (8 indices, element 2j in the high nibble of byte j) ->
 // four words of bf16 pairs in element order.
 __device__ __forceinline__ void restore8(uint32_t w, const RestoreTab& t, uint32_t* out) {
-  uint32_t HE, LE, HO, LO;
-  lookup4((w >> 4) & 0x0F0F0F0Fu, t, HE, LE);
-  lookup4(w & 0x0F0F0F0Fu, t, HO, LO);
+  uint32_t HE, LE, HO, LO, sl, s2;
+  selectors_even(w, sl, s2);
+  lookup4(sl, s2, t, HE, LE);
+  selectors_odd(w, sl, s2);
+  lookup4(sl, s2, t, HO, LO);
   const uint32_t e01 = perm(HE, LE, 0x05010400u), e23 = perm(HE, LE, 0x07030602u);
   const uint32_t o01 = perm(HO, LO, 0x05010400u), o23 = perm(HO, LO, 0x07030602u);
   out[0] = perm(o01, e01, 0x05040100u);
