@@ -201,21 +201,40 @@ def unpack(packed: np.ndarray) -> np.ndarray:
     return q
 
 
-def dequantize(Q: Quantized, levels: Optional[np.ndarray] = None, to_bf16: bool = True) -> np.ndarray:
+def dequantize(Q: Quantized, levels: Optional[np.ndarray] = None, to_bf16: bool = True,
+               rows=None, cols=None) -> np.ndarray:
     """Restore the weight: T[q] * s'_b in float32, then rounded to bfloat16.
 
     Returns float32 [d_out][d_in] (bf16-valued when ``to_bf16``).  Indices are
-    read back from the packed bytes, so packing is exercised too.
+    read back from the packed bytes, so packing is exercised too.  For a 2-D
+    weight whose rows are whole blocks, ``rows`` (or ``cols``) restores only
+    those rows [len(rows)][d_in] (or columns [d_out][len(cols)]), each element
+    with the same arithmetic as the whole restore.
     """
     if levels is None:
         levels = nf4_levels()
     q = unpack(Q.packed)
     s = restored_scales(Q)
-    vals = levels[q].reshape(-1, Q.blocksize)
-    w = (vals * s[:, None]).astype(np.float32)
+    if rows is None and cols is None:
+        vals = levels[q].reshape(-1, Q.blocksize)
+        w = (vals * s[:, None]).astype(np.float32)
+        shape = Q.shape
+    else:
+        N, K = Q.shape
+        if K % Q.blocksize:
+            raise ValueError("a row/column subset needs rows made of whole blocks")
+        q2, s2 = q.reshape(N, K), s.reshape(N, K // Q.blocksize)
+        if rows is not None:
+            r = np.asarray(rows)
+            qq, ss = q2[r], s2[r][:, np.arange(K) // Q.blocksize]
+        else:
+            c = np.asarray(cols)
+            qq, ss = q2[:, c], s2[:, c // Q.blocksize]
+        w = (levels[qq] * ss).astype(np.float32)
+        shape = w.shape
     if to_bf16:
         w = round_to_bf16(w)
-    return w.reshape(Q.shape)
+    return w.reshape(shape)
 
 
 # ----------------------------------------------------------------------------

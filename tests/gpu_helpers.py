@@ -56,6 +56,20 @@ def elementwise_stats(got, want, floor: float = 1e-3) -> dict:
     return {"max_rel": float(np.max(rel)), "share_above_1e-2": float(np.mean(rel > 1e-2))}
 
 
+def oracle_sampled(Q, X, A, B, dY, alpha, r, rows, cols):
+    """The oracle's layer on sampled outputs of a full-size weight: Y and dB
+    on output rows ``rows``, dX (this layer's share) and dA on input columns
+    ``cols``.  olora.forward/backward run on the restored rows (or columns)
+    with the operands those outputs depend on, so every value is the
+    oracle's own.  X, A, B, dY: float arrays of the exact bf16 values."""
+    W_rows = onf4.dequantize(Q, rows=rows).astype(np.float64)   # [rows][K]
+    W_cols = onf4.dequantize(Q, cols=cols).astype(np.float64)   # [N][cols]
+    Y, _ = olora.forward(W_rows, X, A, B[rows], alpha, r)             # Y[:, rows]
+    _, _, dB = olora.backward(W_rows, X, A, B[rows], dY[:, rows], alpha, r)  # dB[rows]
+    dX, dA, _ = olora.backward(W_cols, X[:, cols], A[:, cols], B, dY, alpha, r)  # dX[:, cols], dA[:, cols]
+    return {"Y": Y, "dB": dB, "dX": dX, "dA": dA}
+
+
 def oracle_quantized(W):
     return onf4.quantize(W)
 

@@ -346,6 +346,24 @@ def test_dequant_is_bf16_of_float32_product():
     np.testing.assert_array_equal(nf4.dequantize(Q).reshape(-1, 64), manual)
 
 
+def test_dequant_row_and_column_subsets_are_elementwise():
+    """A subset restore is the whole restore's rows or columns, bit for bit
+    (the manual loop above pins the whole restore itself), for NF4 and the
+    uniform table, with and without double quantization."""
+    rng = np.random.default_rng(5)
+    W = (rng.standard_normal((24, 320)) * 0.03).astype(np.float32)
+    rows, cols = [0, 5, 23, 7], [0, 63, 64, 319, 128, 200]
+    for lv, dq in ((None, 256), (nf4.uniform_levels(), 256), (None, 0)):
+        Q = nf4.quantize(W, levels=lv, dq_blocksize=dq)
+        full = nf4.dequantize(Q, levels=lv)
+        np.testing.assert_array_equal(nf4.dequantize(Q, levels=lv, rows=rows), full[rows])
+        np.testing.assert_array_equal(nf4.dequantize(Q, levels=lv, cols=cols), full[:, cols])
+        np.testing.assert_array_equal(nf4.dequantize(Q, levels=lv, rows=rows, to_bf16=False),
+                                      nf4.dequantize(Q, levels=lv, to_bf16=False)[rows])
+    with pytest.raises(ValueError):
+        nf4.dequantize(nf4.quantize(np.ones((2, 96), np.float32)), rows=[0])
+
+
 # --------------------------------------------------------------------------
 # P5: storage figures
 # --------------------------------------------------------------------------
