@@ -314,20 +314,22 @@ __global__ __launch_bounds__(256) void k_skinny(SkinnyBatch SB) {
 
 // Fixed-order sum of split partials, then the same outputs as the kernel above.
 // TPO threads share one output: thread j adds splits j, j + TPO, ... in order,
-// then the TPO sums are added in order (deterministic).  With pairs of
-// columns (OUT_PAIRS / OUT_PAIRS_T) a workgroup covers whole rows.
+// then the TPO sums are added in order (deterministic).  A workgroup covers
+// S.sum_per_wg consecutive outputs (at most 256 / TPO); with pairs of columns
+// (OUT_PAIRS / OUT_PAIRS_T) that is a whole number of rows, so a row's column
+// col + r is in the same workgroup as its column col.
 __global__ __launch_bounds__(256) void k_skinny_sum(SkinnyBatch SB, int tpo) {
   const SkinnyParams& S = SB.p[blockIdx.z];
   if (S.nsplit == 1) return;
   __shared__ float part[256];
   __shared__ float tot[256];
-  const int per_wg = 256 / tpo;
+  const int per_wg = S.sum_per_wg;
   const int64_t o0 = (int64_t)blockIdx.x * per_wg;
   const int64_t nout = S.mrows * S.ocols;
   if (o0 >= nout) return;
   const int tid = threadIdx.x, o = tid / tpo, j = tid % tpo;
   float v = 0.0f;
-  if (o0 + o < nout)
+  if (o < per_wg && o0 + o < nout)
     for (int z = j; z < S.nsplit; z += tpo) v += S.Pout[(int64_t)z * nout + o0 + o];
   part[tid] = v;
   __syncthreads();
@@ -432,17 +434,22 @@ hipError_t launch_batch(SkinnyBatch B, hipStream_t stream, int kernel_id) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || outs == 0) return e;
-  // threads per output: about 4 splits each, at most 16, and whole rows per
-  // workgroup when columns are summed in pairs
+  // threads per output: about 4 splits each, at most 16, and at least one
+  // whole row per workgroup when columns are summed in pairs
   int tpo = 1;
   while (tpo < 16 && tpo * 4 < ns) tpo *= 2;
   for (int i = 0; i < B.n; ++i)
     if (B.p[i].out_mode != OUT_ROWS_HILO)
-      while (tpo > 1 && (256 / tpo) % B.p[i].ocols != 0) tpo /= 2;
-  const int64_t per_wg = 256 / tpo;
+      while (tpo > 1 && 256 / tpo < B.p[i].ocols) tpo /= 2;
+  int64_t wgs = 0;
+  for (int i = 0; i < B.n; ++i) {
+    SkinnyParams& S = B.p[i];
+    const int cap = 256 / tpo;
+    S.sum_per_wg = S.out_mode == OUT_ROWS_HILO ? cap : (cap / S.ocols) * S.ocols;
+    if (S.nsplit > 1) wgs = std::max(wgs, (S.mrows * S.ocols + S.sum_per_wg - 1) / S.sum_per_wg);
+  }
   TraceScope ts(KID_REDUCE, stream);
-  hipLaunchKernelGGL(k_skinny_sum, dim3((unsigned)((outs + per_wg - 1) / per_wg), 1, (unsigned)B.n), dim3(256), 0,
-                     stream, B, tpo);
+  hipLaunchKernelGGL(k_skinny_sum, dim3((unsigned)wgs, 1, (unsigned)B.n), dim3(256), 0, stream, B, tpo);
   return hipGetLastError();
 }
 

@@ -48,6 +48,7 @@ struct SkinnyParams {
   // of s * Uc[m][0..r) for the same rows m, zero-padded to ldh
   const float* Uc;
   uint16_t* Ucs;
+  int32_t sum_per_wg; // set by the launcher: outputs per workgroup of the split-partial sum
 };
 
 // Up to two independent products in one launch (blockIdx.z picks one).

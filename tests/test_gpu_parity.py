@@ -7,7 +7,7 @@ import pytest
 
 import workloads
 from gpu_helpers import (TOL, assert_quant_bit_exact, gpu_layer, normwise_err, oracle_layer, say,
-                         dev_bf16, dev_f32, host_bf16_to_f64, sweep_blocks)
+                         dev_bf16, dev_f32, host_bf16_to_f64, oracle_sampled, sweep_blocks)
 from oracle import nf4 as onf4
 from oracle.bf16 import bits_to_float, float_to_bits
 
@@ -144,6 +144,9 @@ CASES = [
     (192, 320, 523, 8, 16.0, 11),
     (256, 192, 600, 24, 8.0, 12),
     (320, 448, 1031, 64, 16.0, 13),
+    # many tokens with a rank the streaming kernels do not take: split-contraction adapter products
+    (192, 384, 1000, 12, 16.0, 24),
+    (320, 384, 1000, 12, 16.0, 25),
     # few-token path with several 16-row tiles per workgroup (N/16 above 256)
     (4160, 256, 2, 16, 16.0, 14),     # 2 tiles per workgroup
     (8320, 192, 9, 24, 8.0, 15),      # 3 tiles, the last workgroup 1; K/64 odd
@@ -485,21 +488,6 @@ def test_decode_full_size_sampled(d_out, d_in):
 # projections (8192 x 8192, 8192 <-> 22016), 4096 tokens, r = 64, alpha = 16
 # --------------------------------------------------------------------------
 
-def _restore_subset(Q, rows=None, cols=None):
-    """Oracle restored weight (float64) for whole rows or whole columns, with
-    the same arithmetic as oracle.nf4.dequantize: bf16(fl32(T[q] * s'))."""
-    from oracle.bf16 import round_to_bf16
-    N, K = Q.shape
-    levels = onf4.nf4_levels()
-    q = Q.q.reshape(N, K)
-    s = onf4.restored_scales(Q).reshape(N, K // 64)
-    if rows is not None:
-        qq, ss = q[rows], np.repeat(s[rows], 64, axis=1)
-    else:
-        qq, ss = q[:, cols], s[:, np.asarray(cols) // 64]
-    return round_to_bf16((levels[qq] * ss).astype(np.float32)).astype(np.float64)
-
-
 @pytest.mark.parametrize("d_out,d_in", [(11008, 4096), (4096, 11008), (8192, 8192), (22016, 8192), (8192, 22016)])
 def test_training_shapes_full_size_sampled(d_out, d_in):
     """Quantize bit-exact over the whole weight; forward and backward at the
@@ -526,17 +514,7 @@ def test_training_shapes_full_size_sampled(d_out, d_in):
     rows = np.sort(rng.choice(d_out, size=32, replace=False))
     cols = np.sort(rng.choice(d_in, size=32, replace=False))
     X, A, B, dY = (bits_to_float(inp[k]) for k in ("X", "A", "B", "dY"))
-    s = float(np.float32(alpha / r))
-    Uo = X @ A.T                                   # [T][r]
-    Go = dY @ B                                    # [T][r]
-    W_rows = _restore_subset(Q, rows=rows)         # [32][K]
-    W_cols = _restore_subset(Q, cols=cols)         # [N][32]
-    want = {
-        "Y": X @ W_rows.T + s * (Uo @ B[rows].T),          # Y[:, rows]
-        "dB": s * (dY[:, rows].T @ Uo),                     # dB[rows, :]
-        "dX": dY @ W_cols + s * (Go @ A[:, cols]),           # dX[:, cols]
-        "dA": s * (Go.T @ X[:, cols]),                       # dA[:, cols]
-    }
+    want = oracle_sampled(Q, X, A, B, dY, alpha, r, rows, cols)
     ri, ci = torch.as_tensor(rows, device="cuda"), torch.as_tensor(cols, device="cuda")
     got = {
         "Y": Y.index_select(1, ri).float().cpu().numpy().astype(np.float64),
