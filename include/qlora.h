@@ -296,8 +296,13 @@ int qlora_merge_lora(const qlora_nf4_desc* d, const uint8_t* packed, const uint8
  * blocksize and dq_blocksize (tables may differ).  With at most 16 tokens the
  * rows of every weight are streamed in ONE launch (one workgroup per group of
  * row tiles, whichever weight they belong to), so small projections do not
- * leave the GPU idle and X is read from HBM once; otherwise the layers run
- * one after another.  The pointer arrays are host memory holding device
+ * leave the GPU idle and X is read from HBM once.  With more tokens, when
+ * n > 1, every d_out is a multiple of 256, all layers use one table and the
+ * weights' 256 x 256 output tiles number 512 or more, each layer's U runs
+ * first and then ONE product covers all the weights (their output columns
+ * side by side, each tile writing into its own layer's Y); otherwise the
+ * layers run one after another.  Either way each Y element is the same
+ * fp32 sum, rounded once.  The pointer arrays are host memory holding device
  * pointers; U_out may be NULL, or hold NULL entries.  Workspace:
  * qlora_multi_fwd_workspace_bytes.  Errors: as qlora_linear_fwd, and SHAPE
  * (n outside 1..4, different d_in), UNSUPPORTED (different block format).
@@ -312,14 +317,18 @@ int qlora_linear_fwd_multi(int32_t n, const qlora_nf4_desc* d, const uint8_t* co
 /*
  * Backward of n (1..4) layers that share their input X (as for
  * qlora_linear_fwd_multi): X's gradient is the sum of the layers' shares,
- *   dX = bf16( sum_i (dY_i W_hat_i + s G_i A_i) ),
- * formed layer after layer: the first layer's product writes dX, each later
- * one adds its tile to what dX holds in fp32 and rounds (so dX is rounded
- * once per layer).  dA[i] and dB[i] are each layer's own, overwritten.
- * U_in may be NULL or hold NULL entries (U recomputed).  dX may be NULL.
- * The layers run one after another on the stream, reusing one workspace of
- * qlora_multi_bwd_workspace_bytes.  Errors: as qlora_linear_bwd, and SHAPE
- * (n outside 1..4, different d_in), UNSUPPORTED (different block format).
+ *   dX = bf16( sum_i (dY_i W_hat_i + s G_i A_i) ).
+ * When n > 1, T > 0, dX is given and all layers use one table, dX is ONE
+ * product: its contraction runs over the rows of every weight in turn (each
+ * against its layer's dY), then over every layer's rank-r term, all in one
+ * fp32 sum per element, rounded once.  Otherwise it is formed layer after
+ * layer: the first layer's product writes dX, and each later one rounds its
+ * own share to bf16, adds it to what dX holds and rounds again.  dA[i] and
+ * dB[i] are each layer's own, overwritten.  U_in may be NULL or hold NULL
+ * entries (U recomputed).  dX may be NULL.  Each layer has its own slice of
+ * the workspace (qlora_multi_bwd_workspace_bytes is the sum of the slices).
+ * Errors: as qlora_linear_bwd, and SHAPE (n outside 1..4, different d_in),
+ * UNSUPPORTED (different block format).
  */
 int qlora_multi_bwd_workspace_bytes(int32_t n, const qlora_nf4_desc* d, int64_t T, int32_t r, size_t* bytes);
 int qlora_linear_bwd_multi(int32_t n, const qlora_nf4_desc* d, const uint8_t* const* packed,

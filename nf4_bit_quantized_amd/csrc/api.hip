@@ -276,7 +276,7 @@ int qlora_bwd_workspace_bytes(const qlora_nf4_desc* d, int64_t T, int32_t r, siz
 
 namespace {
 // Everything a forward call checks before it enqueues anything.
-int validate_fwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes, const float* consts, int64_t T,
+static int validate_fwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes, const float* consts, int64_t T,
                  const uint16_t* X, int32_t r, const uint16_t* A, const uint16_t* B, const uint16_t* Y,
                  const float* U_out, void* workspace, size_t workspace_bytes, bool check_workspace = true) {
   const int st = check_layer(d, T, r);
@@ -294,7 +294,7 @@ int validate_fwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* 
 
 // The launches of a validated forward.  Xa: the adapter's input (X itself,
 // or X with dropout applied).
-int enqueue_fwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes, const float* consts, int64_t T,
+static int enqueue_fwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes, const float* consts, int64_t T,
                 const uint16_t* X, const uint16_t* Xa, int32_t r, float alpha, const uint16_t* A, const uint16_t* B,
                 uint16_t* Y, float* U_out, void* workspace, void* stream) {
   if (T == 0) return QLORA_OK;
@@ -325,7 +325,7 @@ int enqueue_fwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* c
   return QLORA_OK;
 }
 
-int linear_fwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes, const float* consts, int64_t T,
+static int linear_fwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes, const float* consts, int64_t T,
                const uint16_t* X, int32_t r, float alpha, const uint16_t* A, const uint16_t* B, uint16_t* Y,
                float* U_out, void* workspace, size_t workspace_bytes, void* stream) {
   const int st = validate_fwd(d, packed, codes, consts, T, X, r, A, B, Y, U_out, workspace, workspace_bytes);
@@ -388,7 +388,7 @@ int qlora_linear_fwd_noalloc(const qlora_nf4_desc* d, const uint8_t* packed, con
 
 namespace {
 // Everything a backward call checks before it enqueues anything.
-int validate_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes, const float* consts, int64_t T,
+static int validate_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes, const float* consts, int64_t T,
                  const uint16_t* X, int32_t r, const uint16_t* A, const uint16_t* B, const float* U_in,
                  const uint16_t* dY, const uint16_t* dX, const float* dA, const float* dB, void* workspace,
                  size_t workspace_bytes) {
@@ -409,10 +409,14 @@ int validate_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* 
 // with dropout applied); keep (optional): the dropout mask, whose factor c
 // scales the adapter's share of dX; dx_accumulate: the dX product adds to
 // what dX holds.
-int enqueue_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes, const float* consts, int64_t T,
+// Parts of a backward (enqueue_bwd's `phases`): U and G with their hi/lo
+// pairs, the dX product, the adapter gradients.
+constexpr int kBwdPre = 1, kBwdDx = 2, kBwdGrads = 4, kBwdAll = 7;
+
+static int enqueue_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes, const float* consts, int64_t T,
                 const uint16_t* X, const uint16_t* Xa, const uint8_t* keep, float c, int32_t r, float alpha,
                 const uint16_t* A, const uint16_t* B, const float* U_in, const uint16_t* dY, uint16_t* dX, float* dA,
-                float* dB, void* workspace, void* stream, int accumulate, int dx_accumulate) {
+                float* dB, void* workspace, void* stream, int accumulate, int dx_accumulate, int phases = kBwdAll) {
   hipStream_t s_ = (hipStream_t)stream;
   const int64_t N = d->d_out, K = d->d_in;
   if (T == 0) {
@@ -426,7 +430,7 @@ int enqueue_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* c
   const float s = r > 0 ? alpha / (float)r : 0.0f;
   const int64_t ldh = hilo_ld(r);
 
-  if (r > 0) {
+  if (r > 0 && (phases & kBwdPre)) {
     // U = X A^T when the forward's U is not given (its hi/lo pair feeds dB)
     if (!U_in) {
       const int e = lora_down(Xa, A, T, K, r, s, w.part, w.U, w.Us, s_);
@@ -449,7 +453,7 @@ int enqueue_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* c
       HIP_TRY(launch_skinny(S, s_, KID_LORA_G));
     }
   }
-  if (dX) {
+  if (dX && (phases & kBwdDx)) {
     // dX = dY W_hat + (s G) A: the contraction runs over d_out, the rows of W
     FusedParams fp{};
     fp.A = dY; fp.lda = N;
@@ -467,7 +471,7 @@ int enqueue_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* c
       HIP_TRY(launch_dropout_dx_add(Dp, s_));
     }
   }
-  if (r > 0) {
+  if (r > 0 && (phases & kBwdGrads)) {
     // one launch for both adapter gradients, contractions over the hi/lo columns:
     // dA = (s G)^T X -> [r][d_in]; dB = dY^T (s U) -> [d_out][r]
     if (lora_stream_ok(r)) {
@@ -491,7 +495,7 @@ int enqueue_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* c
   return QLORA_OK;
 }
 
-int linear_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes, const float* consts, int64_t T,
+static int linear_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uint8_t* codes, const float* consts, int64_t T,
                const uint16_t* X, int32_t r, float alpha, const uint16_t* A, const uint16_t* B, const float* U_in,
                const uint16_t* dY, uint16_t* dX, float* dA, float* dB, void* workspace, size_t workspace_bytes,
                void* stream, int accumulate) {
@@ -524,7 +528,7 @@ int qlora_linear_bwd_accumulate(const qlora_nf4_desc* d, const uint8_t* packed, 
 namespace {
 // Several weights that share X: validation, and each weight's workspace slice
 // (its plan_fwd bytes, rounded up to 256).
-int check_multi(int32_t n, const qlora_nf4_desc* d, int64_t T, int32_t r) {
+static int check_multi(int32_t n, const qlora_nf4_desc* d, int64_t T, int32_t r) {
   if (!d) return QLORA_ERR_NULL;
   if (n < 1 || n > kDecodeMaxWeights) return QLORA_ERR_SHAPE;
   for (int i = 0; i < n; ++i) {
@@ -536,9 +540,12 @@ int check_multi(int32_t n, const qlora_nf4_desc* d, int64_t T, int32_t r) {
   return QLORA_OK;
 }
 
-size_t multi_slice(const qlora_nf4_desc* d, int64_t T, int32_t r) {
+static size_t multi_slice(const qlora_nf4_desc* d, int64_t T, int32_t r) {
   return (plan_fwd(d, T, r, nullptr).bytes + 255) & ~(size_t)255;
 }
+
+// each layer's share of the workspace of a backward over several layers
+static size_t bwd_slice(const qlora_nf4_desc* d, int64_t T, int32_t r) { return align256(plan_bwd(d, T, r, nullptr).bytes); }
 }  // namespace
 
 int qlora_multi_fwd_workspace_bytes(int32_t n, const qlora_nf4_desc* d, int64_t T, int32_t r, size_t* bytes) {
@@ -556,13 +563,13 @@ int qlora_multi_bwd_workspace_bytes(int32_t n, const qlora_nf4_desc* d, int64_t 
   const int st = check_multi(n, d, T, r);
   if (st) return st;
   size_t b = 0;
-  for (int i = 0; i < n; ++i) b = std::max(b, plan_bwd(&d[i], T, r, nullptr).bytes);
+  for (int i = 0; i < n; ++i) b += bwd_slice(&d[i], T, r);
   *bytes = b;
   return QLORA_OK;
 }
 
 namespace {
-char* ws_at(void* ws, size_t off) { return ws ? static_cast<char*>(ws) + off : nullptr; }
+static char* ws_at(void* ws, size_t off) { return ws ? static_cast<char*>(ws) + off : nullptr; }
 }  // namespace
 
 int qlora_linear_bwd_multi(int32_t n, const qlora_nf4_desc* d, const uint8_t* const* packed,
@@ -573,21 +580,64 @@ int qlora_linear_bwd_multi(int32_t n, const qlora_nf4_desc* d, const uint8_t* co
   int st = check_multi(n, d, T, r);
   if (st) return st;
   if (!packed || !codes || !consts || !dY || (r > 0 && (!A || !B || !dA || !dB))) return QLORA_ERR_NULL;
-  // every layer is validated before the first launch
+  // every layer is validated, on its slice of the workspace, before the first launch
+  size_t need = 0;
+  for (int i = 0; i < n; ++i) need += bwd_slice(&d[i], T, r);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return QLORA_ERR_WORKSPACE;
+  size_t off = 0;
   for (int i = 0; i < n; ++i) {
+    const size_t sl = bwd_slice(&d[i], T, r);
     st = validate_bwd(&d[i], packed[i], codes[i], consts[i], T, X, r, r > 0 ? A[i] : nullptr,
                       r > 0 ? B[i] : nullptr, U_in ? U_in[i] : nullptr, dY[i], dX, r > 0 ? dA[i] : nullptr,
-                      r > 0 ? dB[i] : nullptr, workspace, workspace_bytes);
+                      r > 0 ? dB[i] : nullptr, ws_at(workspace, off), sl);
     if (st) return st;
+    off += sl;
   }
-  // one layer after another on the stream (the workspace is reused); from
-  // the second on, the dX product adds to the dX the earlier ones wrote
-  for (int i = 0; i < n; ++i) {
-    st = enqueue_bwd(&d[i], packed[i], codes[i], consts[i], T, X, X, nullptr, 1.0f, r, alpha, r > 0 ? A[i] : nullptr,
-                     r > 0 ? B[i] : nullptr, U_in ? U_in[i] : nullptr, dY[i], dX, r > 0 ? dA[i] : nullptr,
-                     r > 0 ? dB[i] : nullptr, workspace, stream, 0, i > 0);
-    if (st) return st;
+  auto layer = [&](int i, int phases, int dx_acc) {
+    size_t o = 0;
+    for (int k = 0; k < i; ++k) o += bwd_slice(&d[k], T, r);
+    return enqueue_bwd(&d[i], packed[i], codes[i], consts[i], T, X, X, nullptr, 1.0f, r, alpha,
+                       r > 0 ? A[i] : nullptr, r > 0 ? B[i] : nullptr, U_in ? U_in[i] : nullptr, dY[i], dX,
+                       r > 0 ? dA[i] : nullptr, r > 0 ? dB[i] : nullptr, ws_at(workspace, o), stream, 0, dx_acc,
+                       phases);
+  };
+  bool same_table = true;
+  for (int i = 1; i < n; ++i) same_table = same_table && d[i].table == d[0].table;
+  if (n > 1 && T > 0 && dX && same_table) {
+    // X's gradient over all the layers in ONE product: their contractions
+    // (rows of each weight, against each layer's dY) follow each other, and
+    // every layer's rank-r term is a tail of the same accumulation, so dX is
+    // summed in fp32 and rounded once
+    for (int i = 0; i < n; ++i)
+      if ((st = layer(i, kBwdPre, 0))) return st;
+    const int64_t K = d[0].d_in, ldh = hilo_ld(r);
+    FusedParams fp{};
+    off = 0;
+    for (int i = 0; i < n; ++i) {
+      const BwdWs w = plan_bwd(&d[i], T, r, ws_at(workspace, off));
+      off += bwd_slice(&d[i], T, r);
+      if (i == 0) {
+        fp.A = dY[0]; fp.lda = d[0].d_out;
+        fp.packed = packed[0]; fp.codes = codes[0]; fp.consts = consts[0]; fp.Kw = K; fp.table = d[0].table;
+        fp.bshift = block_shift(&d[0]); fp.dq = d[0].dq_blocksize != 0;
+        fp.M = T; fp.N = K; fp.K0 = d[0].d_out;
+        fp.At = w.Gs; fp.ldat = ldh; fp.Bt = r > 0 ? A[0] : nullptr; fp.ldbt = K; fp.r = r;
+        fp.C = dX; fp.ldc = K;
+      } else {
+        fp.seg[i] = FusedSeg{dY[i], d[i].d_out, packed[i], codes[i], consts[i], d[i].d_out, w.Gs, ldh,
+                             r > 0 ? A[i] : nullptr, K, dX, K};
+      }
+    }
+    fp.nseg = n;
+    HIP_TRY(launch_fused(fp, true, (hipStream_t)stream, KID_DX_GEMM));
+    for (int i = 0; i < n; ++i)
+      if ((st = layer(i, kBwdGrads, 0))) return st;
+    return QLORA_OK;
   }
+  // one layer after another on the stream; from the second on, the dX
+  // product adds to the dX the earlier ones wrote
+  for (int i = 0; i < n; ++i)
+    if ((st = layer(i, kBwdAll, i > 0))) return st;
   return QLORA_OK;
 }
 
@@ -618,6 +668,40 @@ int qlora_linear_fwd_multi(int32_t n, const qlora_nf4_desc* d, const uint8_t* co
   bool fused = T <= kDecodeMaxT && d[0].dq_blocksize != 0;
   for (int i = 0; i < n && fused; ++i)
     fused = decode_supported(d[i].d_out, K, block_shift(&d[i])) && aligned16(codes[i]);
+  if (!fused && n > 1 && T > kDecodeMaxT) {
+    // many tokens: each weight's U = X A^T, then one product over all the
+    // weights (their output columns side by side), when every weight is
+    // whole 256-column tiles and one table serves them all
+    bool same_table = true;
+    for (int i = 1; i < n; ++i) same_table = same_table && d[i].table == d[0].table;
+    FusedParams fp{};
+    fp.A = X; fp.lda = K;
+    fp.packed = packed[0]; fp.codes = codes[0]; fp.consts = consts[0]; fp.Kw = K; fp.table = d[0].table;
+    fp.bshift = block_shift(&d[0]); fp.dq = d[0].dq_blocksize != 0;
+    fp.M = T; fp.N = d[0].d_out; fp.K0 = K;
+    fp.ldat = hilo_ld(r); fp.Bt = r > 0 ? B[0] : nullptr; fp.ldbt = r; fp.r = r;
+    fp.C = Y[0]; fp.ldc = d[0].d_out;
+    fp.nseg = n;
+    for (int i = 1; i < n; ++i)
+      fp.seg[i] = FusedSeg{X, K, packed[i], codes[i], consts[i], d[i].d_out, nullptr, hilo_ld(r),
+                           r > 0 ? B[i] : nullptr, r, Y[i], d[i].d_out};
+    if (same_table && fused_wide_ok(fp, false)) {
+      const float s = r > 0 ? alpha / (float)r : 0.0f;
+      off = 0;
+      for (int i = 0; i < n; ++i) {
+        FwdWs fw = plan_fwd(&d[i], T, r, ws_at(workspace, off));
+        off += multi_slice(&d[i], T, r);
+        if (r > 0) {
+          const int e = lora_down(X, A[i], T, K, r, s, fw.part, U_out && U_out[i] ? U_out[i] : fw.U, fw.Us, s_);
+          if (e) return e;
+        }
+        if (i == 0) fp.At = fw.Us;
+        else fp.seg[i].At = fw.Us;
+      }
+      HIP_TRY(launch_fused(fp, false, s_, KID_FWD_GEMM));
+      return QLORA_OK;
+    }
+  }
   if (!fused) {  // one forward per weight
     off = 0;
     for (int i = 0; i < n; ++i) {
@@ -650,15 +734,15 @@ int qlora_linear_fwd_multi(int32_t n, const qlora_nf4_desc* d, const uint8_t* co
 namespace {
 // X with dropout applied, at the start of the workspace; the rest is the
 // plain call's workspace
-size_t dropout_xd_bytes(const qlora_nf4_desc* d, int64_t T) { return ((size_t)(T * d->d_in * 2) + 255) & ~(size_t)255; }
+static size_t dropout_xd_bytes(const qlora_nf4_desc* d, int64_t T) { return ((size_t)(T * d->d_in * 2) + 255) & ~(size_t)255; }
 
-int check_dropout(const qlora_nf4_desc* d, int64_t T, int32_t r, const uint8_t* keep, float p) {
+static int check_dropout(const qlora_nf4_desc* d, int64_t T, int32_t r, const uint8_t* keep, float p) {
   if (!(p >= 0.0f && p < 1.0f)) return QLORA_ERR_UNSUPPORTED;
   if (T > 0 && r > 0 && !keep) return QLORA_ERR_NULL;
   return QLORA_OK;
 }
 
-float dropout_factor(float p) { return 1.0f / (1.0f - p); }
+static float dropout_factor(float p) { return 1.0f / (1.0f - p); }
 }  // namespace
 
 int qlora_dropout_workspace_bytes(const qlora_nf4_desc* d, int64_t T, int32_t r, int32_t backward, size_t* bytes) {

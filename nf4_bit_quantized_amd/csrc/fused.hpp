@@ -5,6 +5,24 @@
 
 namespace qlora {
 
+constexpr int kMaxFusedSegs = 4;
+
+// One further weight of a product over several weights (see FusedParams).
+struct FusedSeg {
+  const uint16_t* A;       // dX: this weight's dY [M][lda]; forward: unused (X is shared)
+  int64_t lda;
+  const uint8_t* packed;
+  const uint8_t* codes;
+  const float* consts;
+  int64_t N;               // d_out of this weight
+  const uint16_t* At;      // its hi/lo pair of s*U (forward) or s*G (dX)
+  int64_t ldat;
+  const uint16_t* Bt;      // its B (forward) or A (dX)
+  int64_t ldbt;
+  uint16_t* C;             // forward: its Y
+  int64_t ldc;
+};
+
 // forward: C[M=T][N=d_out] = A(X)[T][K0=d_in] . W_hat^T + tail
 // dX:      C[M=T][N=d_in]  = A(dY)[T][K0=d_out] . W_hat  + tail
 struct FusedParams {
@@ -28,6 +46,14 @@ struct FusedParams {
   int32_t accumulate;      // 1: C = bf16(C + tile), adding to what C holds (C's tile is rounded first)
   int32_t mt, nt, group_m; // filled by the launcher
   Nf4Table tab;            // filled by the launcher from table
+  // A product over several weights that share the activation (the projections
+  // of one layer input): nseg > 1 and segments 1 .. nseg-1 below; segment 0
+  // is the weight above.  Forward: the segments' output columns follow each
+  // other (each weight's own Y); dX: their contraction rows follow each other
+  // (each weight's own dY), all summed into one dX.
+  int32_t nseg;
+  FusedSeg seg[kMaxFusedSegs];
+  int32_t seg_first[kMaxFusedSegs + 1];  // filled by the launcher: first tile column (forward) of each segment
 };
 
 hipError_t launch_fused(FusedParams P, bool dx, hipStream_t stream, int kernel_id);

@@ -161,6 +161,8 @@ struct Cursor {
   uint32_t rot;      // this workgroup starts its contraction at step rot (see fused_body)
   uint32_t bshift;   // 64-weight chunk index >> bshift = absmax block index
   uint32_t dq;       // 1: codes + group constants; 0: fp32 block scales in consts
+  uint32_t nseg;     // dX over several weights: their contraction steps follow each other,
+  uint32_t k0[kMaxFusedSegs + 1];  // weight i's first step k0[i] (no rotation then)
 };
 
 // Restoring-wave thread index: those are waves 4..7 of the workgroup.
@@ -217,21 +219,36 @@ __device__ __forceinline__ uint32_t rotated(uint32_t step, uint32_t rot, uint32_
 }
 
 template <int BN>
-__device__ __forceinline__ void fetch(StepRegs<BN>& f, const Cursor& c, uint32_t step) {
-  const uint32_t kt = rotated(step, c.rot, c.nk);
+__device__ __forceinline__ void fetch(StepRegs<BN>& f, const Cursor& c, uint32_t step, const FusedParams& P) {
+  uint32_t kt = rotated(step, c.rot, c.nk);
+  __amdgpu_buffer_rsrc_t rw = c.rw, rc = c.rc, rk = c.rk;
+  if (c.nseg > 1) {
+    // several weights (dX): the step's weight and its step within that weight
+    int si = 0;
+    for (int i = 1; i < (int)c.nseg; ++i)
+      if (kt >= c.k0[i]) si = i;
+    if (si > 0) {
+      const FusedSeg& g = P.seg[si];
+      rw = rsrc(g.packed, g.N * P.Kw / 2);
+      const int64_t nblocks = (g.N * P.Kw / 64) >> P.bshift;
+      rc = rsrc(g.codes, P.dq ? nblocks : 0);
+      rk = rsrc(g.consts, P.dq ? ((nblocks + 255) / 256) * 4 : nblocks * 4);
+    }
+    kt -= c.k0[si];
+  }
   const uint32_t sw = kt * c.wstep;
-  const u32x4_t w0 = __builtin_amdgcn_raw_buffer_load_b128(c.rw, c.woff, sw, 0);
+  const u32x4_t w0 = __builtin_amdgcn_raw_buffer_load_b128(rw, c.woff, sw, 0);
   f.w[0] = w0.x; f.w[1] = w0.y; f.w[2] = w0.z; f.w[3] = w0.w;
   if (BN == 256) {
-    const u32x4_t w1 = __builtin_amdgcn_raw_buffer_load_b128(c.rw, c.woff + 16, sw, 0);
+    const u32x4_t w1 = __builtin_amdgcn_raw_buffer_load_b128(rw, c.woff + 16, sw, 0);
     f.w[4] = w1.x; f.w[5] = w1.y; f.w[6] = w1.z; f.w[7] = w1.w;
   }
   const uint32_t blk = (c.coff + kt * c.cstep) >> c.bshift;
   // the codes array holds N*K/blocksize bytes, a multiple of 4, so the aligned dword is in range;
   // without the second level the code load reads zero (empty range) and cg is the block's scale
-  f.code4 = __builtin_amdgcn_raw_buffer_load_b32(c.rc, blk & ~3u, 0, 0);
+  f.code4 = __builtin_amdgcn_raw_buffer_load_b32(rc, blk & ~3u, 0, 0);
   f.code_shift = (blk & 3u) * 8u;
-  f.cg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(c.rk, (c.dq ? blk >> 8 : blk) * 4, 0, 0));
+  f.cg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rk, (c.dq ? blk >> 8 : blk) * 4, 0, 0));
 }
 
 // Keeps the scheduler from hoisting work on prefetched registers above the
@@ -372,15 +389,23 @@ __device__ __forceinline__ void fused_body(const FusedParams& P) {
   const int64_t tn = in_group / rows_in_group;
   const int64_t m0 = tm * G::BM, n0 = tn * BN;
 
-  const uint32_t nk = (uint32_t)(P.K0 / BK);
-  const uint32_t ntail = P.r > 0 ? (uint32_t)((2 * (int64_t)P.r + BK - 1) / BK) : 0;
+  // several weights (dX only): main steps of weight 0, 1, ..., then the
+  // rank-r tail steps of weight 0, 1, ...
+  const int nseg = BT && P.nseg > 1 ? P.nseg : 1;
+  uint32_t k0[kMaxFusedSegs + 1];
+  k0[0] = 0;
+  k0[1] = (uint32_t)(P.K0 / BK);
+  for (int i = 1; i < nseg; ++i) k0[i + 1] = k0[i] + (uint32_t)(P.seg[i].N / BK);
+  const uint32_t nk = k0[nseg];
+  const uint32_t ntail1 = P.r > 0 ? (uint32_t)((2 * (int64_t)P.r + BK - 1) / BK) : 0;  // per weight
+  const uint32_t ntail = ntail1 * nseg;
   const uint32_t nsteps = nk + ntail;
   // Tiles of one tile row share their A rows and walk the contraction in
   // lockstep, so those rows are read once into L2 and hit there.  Different
   // tile rows start at different steps: rows a power of two apart would
   // otherwise send the same column block of every row to few L2 channels
   // at once.  The sum order per tile is fixed, so results stay deterministic.
-  const uint32_t rot = (uint32_t)((tm * 5) % nk);
+  const uint32_t rot = nseg > 1 ? 0u : (uint32_t)((tm * 5) % nk);
   auto a_stage = [&](uint32_t s) { return lds + (s % 3) * G::A_BYTES; };
   auto b_stage = [&](uint32_t s) { return reinterpret_cast<uint16_t*>(lds + G::B_OFF + (s & 1) * G::B_BYTES); };
 
@@ -407,9 +432,36 @@ __device__ __forceinline__ void fused_body(const FusedParams& P) {
     // A copies, issued in step order: steps < nk read the rotated column block
     // of X / dY, step nk + t the hi/lo columns 64t .. 64t+63.
     ACopy cp = make_acopy(P.A, P.lda, P.M, m0, cw, lane);
-    auto col_of = [&](uint32_t c) { return c < nk ? rotated(c, rot, nk) * (BK * 2) : (c - nk) * (BK * 2); };
+    // the source of step c's copies: key i < kMaxFusedSegs is weight i's
+    // activation, kMaxFusedSegs + i its hi/lo tail columns
+    auto key_of = [&](uint32_t c) {
+      if (c < nk) {
+        int si = 0;
+        for (int i = 1; i < nseg; ++i)
+          if (c >= k0[i]) si = i;
+        return si;
+      }
+      return kMaxFusedSegs + (int)((c - nk) / ntail1);
+    };
+    int cp_key = 0;
+    auto source = [&](uint32_t c) {
+      const int key = key_of(c);
+      if (key != cp_key) {
+        cp_key = key;
+        const int si = key % kMaxFusedSegs;
+        if (key == 0) cp = make_acopy(P.A, P.lda, P.M, m0, cw, lane);
+        else if (key < kMaxFusedSegs) cp = make_acopy(P.seg[si].A, P.seg[si].lda, P.M, m0, cw, lane);
+        else if (si == 0) cp = make_acopy(P.At, P.ldat, P.M, m0, cw, lane);
+        else cp = make_acopy(P.seg[si].At, P.seg[si].ldat, P.M, m0, cw, lane);
+      }
+    };
+    auto col_of = [&](uint32_t c) {
+      if (c < nk) return (nseg > 1 ? c - k0[key_of(c)] : rotated(c, rot, nk)) * (BK * 2);
+      return ((c - nk) % ntail1) * (BK * 2);
+    };
     for (uint32_t c = 0; c < 2 && c < nsteps; ++c) {
-      if (c == nk) cp = make_acopy(P.At, P.ldat, P.M, m0, cw, lane);
+      if (nseg > 1) source(c);
+      else if (c == nk) cp = make_acopy(P.At, P.ldat, P.M, m0, cw, lane);
 #pragma unroll
       for (int j = 0; j < 8; ++j) a_copy(cp, col_of(c), a_stage(c), cw, j);
     }
@@ -441,7 +493,11 @@ __device__ __forceinline__ void fused_body(const FusedParams& P) {
     load_frags<BN, BT>(cur, a_stage(0), b_stage(0), arow, apos[0], 0);
     for (uint32_t s = 0; s < nsteps; ++s) {
       const uint32_t c = s + 2;
-      if (c == nk && c < nsteps) cp = make_acopy(P.At, P.ldat, P.M, m0, cw, lane);
+      if (nseg > 1) {
+        if (c < nsteps) source(c);
+      } else if (c == nk && c < nsteps) {
+        cp = make_acopy(P.At, P.ldat, P.M, m0, cw, lane);
+      }
       const uint32_t col = c < nsteps ? col_of(c) : last_col;
       uint8_t* dst = a_stage(c);
       const uint8_t* As = a_stage(s);
@@ -487,20 +543,27 @@ __device__ __forceinline__ void fused_body(const FusedParams& P) {
     Cursor cur = make_cursor<BN, BT>(P, n0);
     cur.nk = nk;
     cur.rot = rot;
-    auto tail_b = [&](uint32_t s) { tail_b_store<BN, BT>(P.Bt, P.ldbt, P.r, P.N, n0, s - nk, b_stage(s)); };
+    cur.nseg = (uint32_t)nseg;
+    for (int i = 0; i <= kMaxFusedSegs; ++i) cur.k0[i] = i <= nseg ? k0[i] : nk;
+    auto tail_b = [&](uint32_t s) {
+      const uint32_t t = s - nk;
+      const int si = (int)(t / ntail1);
+      tail_b_store<BN, BT>(si == 0 ? P.Bt : P.seg[si].Bt, si == 0 ? P.ldbt : P.seg[si].ldbt, P.r, P.N, n0, t % ntail1,
+                           b_stage(s));
+    };
     // three register sets: set i%3 holds step i; in the period of step h the
     // restoring waves issue the loads of step h+3 into the set freed by step
     // h, then restore step h+1 into B stage (h+1)%2, so every load has two
     // steps in flight.
     StepRegs<BN> f0, f1, f2;
     const uint32_t last = nk - 1;
-    fetch<BN>(f0, cur, 0);
-    fetch<BN>(f1, cur, 1 < nk ? 1 : last);
-    fetch<BN>(f2, cur, 2 < nk ? 2 : last);
+    fetch<BN>(f0, cur, 0, P);
+    fetch<BN>(f1, cur, 1 < nk ? 1 : last, P);
+    fetch<BN>(f2, cur, 2 < nk ? 2 : last, P);
     restore_step<BN, BT>(f0, P.tab, P.dq, b_stage(0));
     lds_barrier();
     auto period = [&](StepRegs<BN>& into, StepRegs<BN>& from, uint32_t h) {
-      fetch<BN>(into, cur, h + 3 < nk ? h + 3 : last);
+      fetch<BN>(into, cur, h + 3 < nk ? h + 3 : last, P);
       restore_step<BN, BT>(from, P.tab, P.dq, b_stage(h + 1));
       lds_barrier();
     };
@@ -552,6 +615,7 @@ __global__ __launch_bounds__(512) void k_qlora_dx_gemm(FusedParams P) { fused_bo
 
 hipError_t launch_fused(FusedParams P, bool dx, hipStream_t stream, int kernel_id) {
   if (fused_wide_ok(P, dx)) return launch_fused_wide(P, stream, kernel_id);
+  if (!dx && P.nseg > 1) return hipErrorInvalidValue;  // several weights: forward only on 256 x 256 tiles
   constexpr int bn = 128;
   // buffer offsets are 32-bit and the ranges are capped below 2 GiB
   if (P.M * P.lda * 2 > 0x7FFFFFF0LL || (P.r > 0 && P.M * P.ldat * 2 > 0x7FFFFFF0LL) ||

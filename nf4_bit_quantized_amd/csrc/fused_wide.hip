@@ -209,11 +209,12 @@ __device__ __forceinline__ void tab_piece(const Fetch& f, int j, uint32_t shift,
 // Rank-r tail B fragments of tail step t: B[n][kk mod r], kk = 64t + 8(4h + ks) + e.
 // TV: r is a multiple of 8, so each fragment is 8 consecutive elements of B's row.
 template <bool TV>
-__device__ __forceinline__ void tail_frags(const FusedParams& P, const int64_t (&n)[2], int h, uint32_t t, BFrag& B) {
-  const uint32_t r = (uint32_t)P.r;
+__device__ __forceinline__ void tail_frags(const uint16_t* Bt, int64_t ldbt, int32_t rank, const int64_t (&n)[2], int h,
+                                           uint32_t t, BFrag& B) {
+  const uint32_t r = (uint32_t)rank;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const uint16_t* row = P.Bt + n[j] * P.ldbt;
+    const uint16_t* row = Bt + n[j] * ldbt;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const uint32_t kk = 64u * t + 8u * (4u * h + ks);
@@ -263,7 +264,36 @@ __device__ __forceinline__ void fwd_wide_body(const FusedParams& P) {
   const int64_t rows_in_group = (P.mt - first_m) < gm ? (P.mt - first_m) : gm;
   const int64_t in_group = order - group * gm * P.nt;
   const int64_t tm = first_m + in_group % rows_in_group;
-  const int64_t tn = in_group / rows_in_group;
+  int64_t tn = in_group / rows_in_group;
+  // the weight this tile column belongs to (several weights: their columns follow each other)
+  const uint8_t* packed = P.packed;
+  const uint8_t* codes = P.codes;
+  const float* consts = P.consts;
+  int64_t N = P.N;
+  const uint16_t* At = P.At;
+  int64_t ldat = P.ldat;
+  const uint16_t* Bt = P.Bt;
+  int64_t ldbt = P.ldbt;
+  uint16_t* C = P.C;
+  int64_t ldc = P.ldc;
+  int64_t first_col = 0;
+  for (int i = 1; i < P.nseg; ++i) {
+    if (tn >= P.seg_first[i]) {
+      const FusedSeg& g = P.seg[i];
+      first_col = P.seg_first[i];
+      packed = g.packed;
+      codes = g.codes;
+      consts = g.consts;
+      N = g.N;
+      At = g.At;
+      ldat = g.ldat;
+      Bt = g.Bt;
+      ldbt = g.ldbt;
+      C = g.C;
+      ldc = g.ldc;
+    }
+  }
+  tn -= first_col;
   const int64_t m0 = tm * BM, n0 = tn * BN;
 
   const int lane = threadIdx.x & 63;
@@ -280,14 +310,14 @@ __device__ __forceinline__ void fwd_wide_body(const FusedParams& P) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int64_t n = n0 + 64 * cw + 32 * j + c32;
-    nrow[j] = n < P.N ? n : P.N - 1;
+    nrow[j] = n < N ? n : N - 1;
   }
   WCursor wc;
   {
-    wc.rw = rsrc(P.packed, P.N * P.Kw / 2);
-    const int64_t nblocks = (P.N * P.Kw / 64) >> P.bshift;
-    wc.rc = rsrc(P.codes, DQ ? nblocks : 0);
-    wc.rk = rsrc(P.consts, DQ ? ((nblocks + 255) / 256) * 4 : nblocks * 4);
+    wc.rw = rsrc(packed, N * P.Kw / 2);
+    const int64_t nblocks = (N * P.Kw / 64) >> P.bshift;
+    wc.rc = rsrc(codes, DQ ? nblocks : 0);
+    wc.rk = rsrc(consts, DQ ? ((nblocks + 255) / 256) * 4 : nblocks * 4);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       wc.woff[j] = (uint32_t)(nrow[j] * (P.Kw / 2) + 16 * h);
@@ -349,8 +379,8 @@ __device__ __forceinline__ void fwd_wide_body(const FusedParams& P) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lds_dst(c, j), 16, xoff[j],
                                                __builtin_amdgcn_readfirstlane(rotated(cc, rot, nk) * (BK * 2)), 0, 0);
     } else {
-      const __amdgpu_buffer_rsrc_t rt = rsrc(P.At, P.M * P.ldat * 2);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, lds_dst(c, j), 16, crow[j] * (uint32_t)(P.ldat * 2) + chunk16[j & 1],
+      const __amdgpu_buffer_rsrc_t rt = rsrc(At, P.M * ldat * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, lds_dst(c, j), 16, crow[j] * (uint32_t)(ldat * 2) + chunk16[j & 1],
                                                __builtin_amdgcn_readfirstlane((cc - nk) * (BK * 2)), 0, 0);
     }
   };
@@ -510,7 +540,7 @@ __device__ __forceinline__ void fwd_wide_body(const FusedParams& P) {
     const uint8_t* An = stage(s + 1);
     bf16x8_t a1[8];
     fetch<DQ>(fc, wc, nk - 1);
-    if (s + 1 < nsteps) tail_frags<TV>(P, nrow, h, s + 1 - nk, bnext);
+    if (s + 1 < nsteps) tail_frags<TV>(Bt, ldbt, P.r, nrow, h, s + 1 - nk, bnext);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       if (ks == 3) {
@@ -602,8 +632,8 @@ __device__ __forceinline__ void fwd_wide_body(const FusedParams& P) {
   for (int c = threadIdx.x; c < BM * (BN / 8); c += 256) {
     const int row = c / (BN / 8), cc = (c % (BN / 8)) * 8;
     const int64_t gr = m0 + row, gc = n0 + cc;
-    if (gr >= P.M || gc >= P.N) continue;
-    *reinterpret_cast<uint4*>(P.C + gr * P.ldc + gc) = *reinterpret_cast<const uint4*>(ctile + row * LDC + cc);
+    if (gr >= P.M || gc >= N) continue;
+    *reinterpret_cast<uint4*>(C + gr * ldc + gc) = *reinterpret_cast<const uint4*>(ctile + row * LDC + cc);
   }
 }
 
@@ -614,15 +644,31 @@ __global__ __launch_bounds__(256, 1) void k_qlora_fwd_wide_f32s(FusedParams P) {
 __global__ __launch_bounds__(256, 1) void k_qlora_fwd_wide_f32s_r(FusedParams P) { fwd_wide_body<false, false>(P); }
 
 // 256 x 256 tiles: worth it when the tile count fills the GPU at least twice.
+// Over several weights every weight's columns must be whole tiles.
 bool fused_wide_ok(const FusedParams& P, bool dx) {
-  if (dx) return false;
-  const int64_t tiles = ((P.M + BM - 1) / BM) * ((P.N + BN - 1) / BN);
-  return tiles >= 512 && P.K0 % BK == 0 && !P.accumulate;
+  if (dx || P.accumulate || P.K0 % BK != 0) return false;
+  const int64_t mt = (P.M + BM - 1) / BM;
+  int64_t nt = (P.N + BN - 1) / BN;
+  if (P.nseg > 1) {
+    if (P.N % BN != 0) return false;
+    for (int i = 1; i < P.nseg; ++i) {
+      if (P.seg[i].N % BN != 0) return false;
+      nt += P.seg[i].N / BN;
+    }
+  }
+  return mt * nt >= 512;
 }
 
 hipError_t launch_fused_wide(FusedParams P, hipStream_t stream, int kernel_id) {
   P.mt = (int32_t)((P.M + BM - 1) / BM);
   P.nt = (int32_t)((P.N + BN - 1) / BN);
+  if (P.nseg < 1) P.nseg = 1;
+  P.seg_first[0] = 0;
+  for (int i = 1; i < P.nseg; ++i) {
+    P.seg_first[i] = P.nt;
+    P.nt += (int32_t)(P.seg[i].N / BN);
+  }
+  P.seg_first[P.nseg] = P.nt;
   P.group_m = 2;
   P.tab = level_table(P.table);
   const int64_t ntiles = (int64_t)P.mt * P.nt;
