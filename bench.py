@@ -43,7 +43,7 @@ BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 # counters read for a plain fill and copy of known size in the same runs
 # (--copy-calibration).  Valid only for the kernel sources they were taken on
 # (sha256 of the files below); reported as null once those change.
-TRAFFIC_SOURCES = ("fused_gemm.hip", "fused.hpp", "restore.hpp", "common.hpp")
+TRAFFIC_SOURCES = ("fused_gemm.hip", "fused_wide.hip", "fused.hpp", "restore.hpp", "common.hpp")
 TRAFFIC = {
     "sha256": None,
     "fetch_scale": 1.0,
@@ -252,7 +252,9 @@ def stack_section(args):
                 "unit": "TFLOP/s", "frac": d["frac"], "traffic": traffic_bytes(dom),
                 "avg_launch_us": d["avg_launch_us"], "flops_per_launch": d["flops_per_launch"],
                 "launch_note": "flops_per_launch and avg_launch_us average over the kernel's launches in the "
-                               "timed region (three weight shapes); achieved = their flops / their time"}
+                               "timed region (per layer: one product over the query/key/value weights, "
+                               "the output projection, one over gate/up, down); achieved = their flops / "
+                               "their time"}
     value = step_flops / (ms_per_step * 1e-3) / 1e12
     out = {
         "ms_per_step": ms_per_step, "value": value, "step_flops": step_flops, "roofline": roofline,

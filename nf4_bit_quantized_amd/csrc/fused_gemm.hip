@@ -162,8 +162,19 @@ struct Cursor {
   uint32_t bshift;   // 64-weight chunk index >> bshift = absmax block index
   uint32_t dq;       // 1: codes + group constants; 0: fp32 block scales in consts
   uint32_t nseg;     // dX over several weights: their contraction steps follow each other,
-  uint32_t k0[kMaxFusedSegs + 1];  // weight i's first step k0[i] (no rotation then)
+  uint32_t k0[kMaxFusedSegs + 1];  // weight i's first (unrotated) step k0[i]
+  uint32_t lo, hi;   // several weights: rw, rc, rk are those of the weight with steps [lo, hi)
 };
+
+// Buffer resources of one stored weight of `rows` rows: packed words, scale
+// codes, group constants (or fp32 block scales).
+__device__ __forceinline__ void weight_rsrcs(const FusedParams& P, const uint8_t* packed, const uint8_t* codes,
+                                             const float* consts, int64_t rows, Cursor& c) {
+  c.rw = rsrc(packed, rows * P.Kw / 2);
+  const int64_t nblocks = (rows * P.Kw / 64) >> P.bshift;
+  c.rc = rsrc(codes, P.dq ? nblocks : 0);
+  c.rk = rsrc(consts, P.dq ? ((nblocks + 255) / 256) * 4 : nblocks * 4);
+}
 
 // Restoring-wave thread index: those are waves 4..7 of the workgroup.
 __device__ __forceinline__ int ptid() { return (int)threadIdx.x - 256; }
@@ -185,11 +196,7 @@ __device__ __forceinline__ void w_coords(int& lrow, int& lcol) {
 template <int BN, bool BT>
 __device__ __forceinline__ Cursor make_cursor(const FusedParams& P, int64_t n0) {
   Cursor c;
-  const int64_t Nw = BT ? P.K0 : P.N;  // rows of the stored weight
-  c.rw = rsrc(P.packed, Nw * P.Kw / 2);
-  const int64_t nblocks = (Nw * P.Kw / 64) >> P.bshift;
-  c.rc = rsrc(P.codes, P.dq ? nblocks : 0);
-  c.rk = rsrc(P.consts, P.dq ? ((nblocks + 255) / 256) * 4 : nblocks * 4);
+  weight_rsrcs(P, P.packed, P.codes, P.consts, BT ? P.K0 : P.N, c);
   c.bshift = (uint32_t)P.bshift;
   c.dq = (uint32_t)P.dq;
   int lrow, lcol;
@@ -218,24 +225,55 @@ __device__ __forceinline__ uint32_t rotated(uint32_t step, uint32_t rot, uint32_
   return kt >= nk ? kt - nk : kt;
 }
 
+// Several weights: lookups by segment index go through fixed-bound unrolled
+// selects on a wave-uniform index, so the parameter block and the k0 table
+// stay in scalar registers (an index known only at run time would copy them
+// to scratch memory).
+__device__ __forceinline__ int seg_of(uint32_t kt, const uint32_t (&k0)[kMaxFusedSegs + 1], int nseg) {
+  int si = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxFusedSegs; ++i) si = (i < nseg && kt >= k0[i]) ? i : si;
+  return __builtin_amdgcn_readfirstlane(si);
+}
+
+__device__ __forceinline__ uint32_t k0_of(const uint32_t (&k0)[kMaxFusedSegs + 1], int si) {
+  uint32_t v = 0;
+#pragma unroll
+  for (int i = 1; i <= kMaxFusedSegs; ++i) v = si == i ? k0[i] : v;
+  return v;
+}
+
+// The kernels' one argument, read in place from the kernel-argument segment
+// (it starts there, at offset 0).  A field of segment si, si known only at
+// run time but the same for the whole wave, is then one scalar load at a
+// computed offset; indexing the by-value parameter itself at a run-time
+// index would copy all of it to scratch memory first.
+typedef const __attribute__((address_space(4))) FusedParams* KernargParams;
+
+__device__ __forceinline__ KernargParams kernarg_params() {
+  return (KernargParams)__builtin_amdgcn_kernarg_segment_ptr();
+}
+
 template <int BN>
-__device__ __forceinline__ void fetch(StepRegs<BN>& f, const Cursor& c, uint32_t step, const FusedParams& P) {
+__device__ __forceinline__ void fetch(StepRegs<BN>& f, Cursor& c, uint32_t step, const FusedParams& P) {
   uint32_t kt = rotated(step, c.rot, c.nk);
-  __amdgpu_buffer_rsrc_t rw = c.rw, rc = c.rc, rk = c.rk;
   if (c.nseg > 1) {
-    // several weights (dX): the step's weight and its step within that weight
-    int si = 0;
-    for (int i = 1; i < (int)c.nseg; ++i)
-      if (kt >= c.k0[i]) si = i;
-    if (si > 0) {
-      const FusedSeg& g = P.seg[si];
-      rw = rsrc(g.packed, g.N * P.Kw / 2);
-      const int64_t nblocks = (g.N * P.Kw / 64) >> P.bshift;
-      rc = rsrc(g.codes, P.dq ? nblocks : 0);
-      rk = rsrc(g.consts, P.dq ? ((nblocks + 255) / 256) * 4 : nblocks * 4);
+    // several weights (dX): the step's weight and its step within that weight;
+    // the resources change only when the step enters another weight
+    if (kt < c.lo || kt >= c.hi) {
+      const int si = seg_of(kt, c.k0, (int)c.nseg);
+      c.lo = k0_of(c.k0, si);
+      c.hi = k0_of(c.k0, si + 1);
+      if (si == 0) {
+        weight_rsrcs(P, P.packed, P.codes, P.consts, P.K0, c);
+      } else {
+        const KernargParams K = kernarg_params();
+        weight_rsrcs(P, K->seg[si].packed, K->seg[si].codes, K->seg[si].consts, K->seg[si].N, c);
+      }
     }
-    kt -= c.k0[si];
+    kt -= c.lo;
   }
+  const __amdgpu_buffer_rsrc_t rw = c.rw, rc = c.rc, rk = c.rk;
   const uint32_t sw = kt * c.wstep;
   const u32x4_t w0 = __builtin_amdgcn_raw_buffer_load_b128(rw, c.woff, sw, 0);
   f.w[0] = w0.x; f.w[1] = w0.y; f.w[2] = w0.z; f.w[3] = w0.w;
@@ -368,7 +406,9 @@ __device__ __forceinline__ void mma_frags(const Frags<BN>& f, f32x16_t (&acc)[4]
 // The kernel body
 // ---------------------------------------------------------------------------
 
-template <int BN, bool BT>
+// MULTI: dX over several weights (P.nseg of them); a kernel of its own, so
+// the single-weight kernels carry none of the segment code.
+template <int BN, bool BT, bool MULTI = false>
 __device__ __forceinline__ void fused_body(const FusedParams& P) {
   using G = Geometry<BN, BT>;
   constexpr int TM = G::TM, TN = G::TN;
@@ -391,12 +431,13 @@ __device__ __forceinline__ void fused_body(const FusedParams& P) {
 
   // several weights (dX only): main steps of weight 0, 1, ..., then the
   // rank-r tail steps of weight 0, 1, ...
-  const int nseg = BT && P.nseg > 1 ? P.nseg : 1;
-  uint32_t k0[kMaxFusedSegs + 1];
+  const int nseg = MULTI ? P.nseg : 1;
+  uint32_t k0[kMaxFusedSegs + 1];  // past the last weight every entry is nk
   k0[0] = 0;
   k0[1] = (uint32_t)(P.K0 / BK);
-  for (int i = 1; i < nseg; ++i) k0[i + 1] = k0[i] + (uint32_t)(P.seg[i].N / BK);
-  const uint32_t nk = k0[nseg];
+#pragma unroll
+  for (int i = 1; i < kMaxFusedSegs; ++i) k0[i + 1] = k0[i] + (i < nseg ? (uint32_t)(P.seg[i].N / BK) : 0u);
+  const uint32_t nk = k0[kMaxFusedSegs];
   const uint32_t ntail1 = P.r > 0 ? (uint32_t)((2 * (int64_t)P.r + BK - 1) / BK) : 0;  // per weight
   const uint32_t ntail = ntail1 * nseg;
   const uint32_t nsteps = nk + ntail;
@@ -405,7 +446,7 @@ __device__ __forceinline__ void fused_body(const FusedParams& P) {
   // tile rows start at different steps: rows a power of two apart would
   // otherwise send the same column block of every row to few L2 channels
   // at once.  The sum order per tile is fixed, so results stay deterministic.
-  const uint32_t rot = nseg > 1 ? 0u : (uint32_t)((tm * 5) % nk);
+  const uint32_t rot = (uint32_t)((tm * 5) % nk);
   auto a_stage = [&](uint32_t s) { return lds + (s % 3) * G::A_BYTES; };
   auto b_stage = [&](uint32_t s) { return reinterpret_cast<uint16_t*>(lds + G::B_OFF + (s & 1) * G::B_BYTES); };
 
@@ -435,13 +476,8 @@ __device__ __forceinline__ void fused_body(const FusedParams& P) {
     // the source of step c's copies: key i < kMaxFusedSegs is weight i's
     // activation, kMaxFusedSegs + i its hi/lo tail columns
     auto key_of = [&](uint32_t c) {
-      if (c < nk) {
-        int si = 0;
-        for (int i = 1; i < nseg; ++i)
-          if (c >= k0[i]) si = i;
-        return si;
-      }
-      return kMaxFusedSegs + (int)((c - nk) / ntail1);
+      if (c < nk) return seg_of(rotated(c, rot, nk), k0, nseg);
+      return __builtin_amdgcn_readfirstlane(kMaxFusedSegs + (int)((c - nk) / ntail1));
     };
     int cp_key = 0;
     auto source = [&](uint32_t c) {
@@ -449,15 +485,23 @@ __device__ __forceinline__ void fused_body(const FusedParams& P) {
       if (key != cp_key) {
         cp_key = key;
         const int si = key % kMaxFusedSegs;
-        if (key == 0) cp = make_acopy(P.A, P.lda, P.M, m0, cw, lane);
-        else if (key < kMaxFusedSegs) cp = make_acopy(P.seg[si].A, P.seg[si].lda, P.M, m0, cw, lane);
-        else if (si == 0) cp = make_acopy(P.At, P.ldat, P.M, m0, cw, lane);
-        else cp = make_acopy(P.seg[si].At, P.seg[si].ldat, P.M, m0, cw, lane);
+        if (key == 0) {
+          cp = make_acopy(P.A, P.lda, P.M, m0, cw, lane);
+        } else if (key < kMaxFusedSegs) {
+          const KernargParams K = kernarg_params();
+          cp = make_acopy(K->seg[si].A, K->seg[si].lda, P.M, m0, cw, lane);
+        } else if (si == 0) {
+          cp = make_acopy(P.At, P.ldat, P.M, m0, cw, lane);
+        } else {
+          const KernargParams K = kernarg_params();
+          cp = make_acopy(K->seg[si].At, K->seg[si].ldat, P.M, m0, cw, lane);
+        }
       }
     };
     auto col_of = [&](uint32_t c) {
-      if (c < nk) return (nseg > 1 ? c - k0[key_of(c)] : rotated(c, rot, nk)) * (BK * 2);
-      return ((c - nk) % ntail1) * (BK * 2);
+      const uint32_t col = c < nk ? (rotated(c, rot, nk) - (nseg > 1 ? k0_of(k0, key_of(c)) : 0u)) * (BK * 2)
+                                  : ((c - nk) % ntail1) * (BK * 2);
+      return (uint32_t)__builtin_amdgcn_readfirstlane((int)col);
     };
     for (uint32_t c = 0; c < 2 && c < nsteps; ++c) {
       if (nseg > 1) source(c);
@@ -544,12 +588,17 @@ __device__ __forceinline__ void fused_body(const FusedParams& P) {
     cur.nk = nk;
     cur.rot = rot;
     cur.nseg = (uint32_t)nseg;
-    for (int i = 0; i <= kMaxFusedSegs; ++i) cur.k0[i] = i <= nseg ? k0[i] : nk;
+#pragma unroll
+    for (int i = 0; i <= kMaxFusedSegs; ++i) cur.k0[i] = k0[i];
+    cur.lo = 0;
+    cur.hi = k0[1];
     auto tail_b = [&](uint32_t s) {
       const uint32_t t = s - nk;
-      const int si = (int)(t / ntail1);
-      tail_b_store<BN, BT>(si == 0 ? P.Bt : P.seg[si].Bt, si == 0 ? P.ldbt : P.seg[si].ldbt, P.r, P.N, n0, t % ntail1,
-                           b_stage(s));
+      const int si = __builtin_amdgcn_readfirstlane((int)(t / ntail1));
+      const KernargParams K = kernarg_params();
+      const uint16_t* bt = si == 0 ? P.Bt : K->seg[si].Bt;
+      const int64_t ldbt = si == 0 ? P.ldbt : K->seg[si].ldbt;
+      tail_b_store<BN, BT>(bt, ldbt, P.r, P.N, n0, t % ntail1, b_stage(s));
     };
     // three register sets: set i%3 holds step i; in the period of step h the
     // restoring waves issue the loads of step h+3 into the set freed by step
@@ -612,6 +661,7 @@ __device__ __forceinline__ void fused_body(const FusedParams& P) {
 
 __global__ __launch_bounds__(512) void k_qlora_fwd_gemm(FusedParams P) { fused_body<128, false>(P); }
 __global__ __launch_bounds__(512) void k_qlora_dx_gemm(FusedParams P) { fused_body<128, true>(P); }
+__global__ __launch_bounds__(512) void k_qlora_dx_gemm_multi(FusedParams P) { fused_body<128, true, true>(P); }
 
 hipError_t launch_fused(FusedParams P, bool dx, hipStream_t stream, int kernel_id) {
   if (fused_wide_ok(P, dx)) return launch_fused_wide(P, stream, kernel_id);
@@ -629,6 +679,8 @@ hipError_t launch_fused(FusedParams P, bool dx, hipStream_t stream, int kernel_i
   const unsigned grid = (unsigned)(((ntiles + 7) / 8) * 8);
   KernelEvents ev(kernel_id);
   if (!dx) hipExtLaunchKernelGGL(k_qlora_fwd_gemm, dim3(grid), dim3(512), 0, stream, ev.start(), ev.stop(), 0, P);
+  else if (P.nseg > 1)
+    hipExtLaunchKernelGGL(k_qlora_dx_gemm_multi, dim3(grid), dim3(512), 0, stream, ev.start(), ev.stop(), 0, P);
   else hipExtLaunchKernelGGL(k_qlora_dx_gemm, dim3(grid), dim3(512), 0, stream, ev.start(), ev.stop(), 0, P);
   return hipGetLastError();
 }
