@@ -75,8 +75,9 @@ struct Geometry {
   static constexpr int TM = 4;              // 32-row MFMA tiles per wave (wave rows 128)
   static constexpr int TN = BN / 64;        // 32-col MFMA tiles per wave
   static constexpr int A_BYTES = BM * BK * 2;  // one A stage: 256 rows of 128 B
-  // B tile: [BN][LDK] (contraction-contiguous) or [64][BN + 16] (column-contiguous)
-  static constexpr int LDB_T = BN + 16;
+  // B tile: [BN][LDK] (contraction-contiguous) or [64][BN] (column-contiguous,
+  // swizzled: see bt_col)
+  static constexpr int LDB_T = BN;
   static constexpr int B_ELEMS = BT ? BK * LDB_T : BN * LDK;
   static constexpr int B_BYTES = B_ELEMS * 2;
   static constexpr int B_OFF = 3 * A_BYTES;    // the two B stages follow the three A stages
@@ -84,6 +85,19 @@ struct Geometry {
   static constexpr int MAIN_BYTES = B_OFF + 2 * B_BYTES;
   static constexpr int LDS_BYTES = MAIN_BYTES > BM * LDC * 2 ? MAIN_BYTES : BM * LDC * 2;
 };
+
+// Column-contiguous B tile (dX): element (row, col) sits in row `row` at
+// column bt_col(row, col).  Columns move in units of four (8 bytes, what one
+// lane of a transposed fragment read takes); unit u of row r goes to unit
+// u ^ 10 (r mod 4).  With 64 four-byte banks and a 256-byte row, a fragment
+// read (32 lanes at a time: four consecutive rows from a multiple of four,
+// eight consecutive units from a multiple of eight) and a restore store (16
+// lanes at a time: four consecutive rows, 16-byte pieces at units 8q + 2i)
+// then each touch every bank once.  Units 2i and 2i + 1 stay adjacent, so a
+// 16-byte store stays one store.
+__device__ __forceinline__ int bt_col(int row, int col) {
+  return (((col >> 2) ^ (10 * (row & 3))) << 2) | (col & 3);
+}
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -306,14 +320,17 @@ __device__ __forceinline__ void restore_step(StepRegs<BN>& f, const Nf4Table& ta
   int lrow, lcol;
   w_coords<BN, BT>(lrow, lcol);
   const RestoreTab t = make_tab(tab, dq ? restored_scale((f.code4 >> f.code_shift) & 0xFFu, f.cg) : f.cg);
-  uint16_t* dst = BT ? Bs + lrow * Geometry<BN, BT>::LDB_T + lcol : Bs + lrow * LDK + lcol;
+  static_assert(!BT || BN == 128, "the dX tile swizzle covers 128 columns");
 #pragma unroll
   for (int i = 0; i < BN / 32; i += 2) {
     uint32_t o[8];
     restore8(f.w[i], t, o);
     restore8(f.w[i + 1], t, o + 4);
-    *reinterpret_cast<uint4*>(dst + i * 8) = make_uint4(o[0], o[1], o[2], o[3]);
-    *reinterpret_cast<uint4*>(dst + i * 8 + 8) = make_uint4(o[4], o[5], o[6], o[7]);
+    uint16_t* d0 = BT ? Bs + lrow * Geometry<BN, BT>::LDB_T + bt_col(lrow, lcol + i * 8) : Bs + lrow * LDK + lcol + i * 8;
+    uint16_t* d1 = BT ? Bs + lrow * Geometry<BN, BT>::LDB_T + bt_col(lrow, lcol + i * 8 + 8)
+                      : Bs + lrow * LDK + lcol + i * 8 + 8;
+    *reinterpret_cast<uint4*>(d0) = make_uint4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<uint4*>(d1) = make_uint4(o[4], o[5], o[6], o[7]);
   }
 }
 
@@ -347,7 +364,7 @@ __device__ __forceinline__ void tail_b_store(const uint16_t* __restrict__ Bt, in
       const int64_t kk = kt * BK + lrow;
       int64_t col = n0 + lc;
       col = col < cols ? col : 0;
-      *reinterpret_cast<uint4*>(Bs + lrow * LDB_T + lc) =
+      *reinterpret_cast<uint4*>(Bs + lrow * LDB_T + bt_col(lrow, lc)) =
           *reinterpret_cast<const uint4*>(Bt + (int64_t)((uint32_t)kk % (uint32_t)r) * ldbt + col);
     }
   }
@@ -382,10 +399,12 @@ __device__ __forceinline__ void load_frags(Frags<BN>& f, const uint8_t* __restri
       const int row = kofs + (s >> 2);
       typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
       const lds_u16_t* base = (const lds_u16_t*)Bs;
+      // rows row and row + 4 share row & 3, so both reads take the same swizzled column
+      const int scol = bt_col(row, col);
       const u16x4_t lo = __builtin_bit_cast(
-          u16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(base + row * LDB_T + col)));
+          u16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(base + row * LDB_T + scol)));
       const u16x4_t hi = __builtin_bit_cast(
-          u16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(base + (row + 4) * LDB_T + col)));
+          u16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(base + (row + 4) * LDB_T + scol)));
       typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
       const u16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       f.b[j] = __builtin_bit_cast(bf16x8_t, v);
