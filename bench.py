@@ -40,14 +40,19 @@ BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 # HBM bytes per launch of the dominant kernel on the headline step, from two
 # rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, KiB per
 # dispatch, averaged over that kernel's dispatches), scaled by what the same
-# counters read for a plain fill and copy of known size in the same runs
-# (--copy-calibration).  Valid only for the kernel sources they were taken on
+# counters read for a plain device-to-device copy of known size in the same
+# runs (--copy-calibration).  Valid only for the kernel sources they were taken on
 # (sha256 of the files below); reported as null once those change.
 TRAFFIC_SOURCES = ("fused_gemm.hip", "fused_wide.hip", "fused.hpp", "restore.hpp", "common.hpp")
 TRAFFIC = {
-    "sha256": None,
-    "fetch_scale": 1.0,
+    "sha256": "2f7173a661b5cd3d567a432ebda7f74059391bd7ef952d4e885c8e22fd453435",
+    # a 256 MiB device-to-device copy read 131084.5 KiB of FETCH_SIZE and wrote
+    # 262144 KiB of WRITE_SIZE in the same runs
+    "fetch_scale": 262144.0 / 131084.5,
     "write_scale": 1.0,
+    # per dispatch, averaged over one 65B-class layer's launches (3 steps)
+    "dx_gemm": {"fetch_kib": 1042278.1, "write_kib": 93184.0},
+    "fwd_gemm": {"fetch_kib": 708104.6, "write_kib": 211152.0},
 }
 
 
@@ -351,49 +356,51 @@ def decode_section(steps, warmup):
 
     out = {}
     copies = 5
-    for T in (1, 4, 16):
-        for lin in workloads.decode_70b(T):
-            inp = workloads.layer_inputs(lin.d_out, lin.d_in, T, lin.r, lin.seed, with_dy=False)
-            W = torch.from_numpy(inp["W"]).cuda()
-            pk, cd, cs = q.qlora_quantize_nf4(W)
-            del W
-            reps = [(pk.clone(), cd.clone(), cs.clone()) for _ in range(copies)]
-            X, A, B = (bf16_dev(inp[k]) for k in ("X", "A", "B"))
-            Y = torch.empty((T, lin.d_out), dtype=torch.bfloat16, device="cuda")
-            U = torch.empty((T, lin.r), dtype=torch.float32, device="cuda")
-            ws = torch.empty(max(1, q.qlora_fwd_workspace_bytes(lin.d_out, lin.d_in, T, lin.r)),
-                             dtype=torch.uint8, device="cuda")
-            for i in range(warmup):
-                p = reps[i % copies]
-                q.qlora_linear_fwd(p[0], p[1], p[2], X, A, B, lin.alpha, Y=Y, U_out=U, workspace=ws)
-            torch.cuda.synchronize()
-            q.qlora_trace_read(reset=True)
-            q.qlora_trace_select({"decode"})
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for i in range(steps):
-                p = reps[i % copies]
-                q.qlora_linear_fwd(p[0], p[1], p[2], X, A, B, lin.alpha, Y=Y, U_out=U, workspace=ws)
-            e1.record()
-            torch.cuda.synchronize()
-            q.qlora_trace_enable(False)
-            kt = q.qlora_trace_read(reset=True)
-            call_ms = e0.elapsed_time(e1) / steps
-            packed_bytes = pk.numel() + cd.numel() + cs.numel() * 4
-            dec_n, dec_ms = kt.get("decode", (1, float("nan")))
-            dec_avg = dec_ms / max(dec_n, 1)
-            out[lin.name] = {
-                "T": T, "d_out": lin.d_out, "d_in": lin.d_in,
-                "packed_weight_bytes": packed_bytes,
-                "call_us": round(call_ms * 1e3, 2),
-                "packed_GBps_call": round(packed_bytes / (call_ms * 1e-3) / 1e9, 1),
-                "decode_kernel_us": round(dec_avg * 1e3, 2),
-                "packed_GBps_kernel": round(packed_bytes / (dec_avg * 1e-3) / 1e9, 1),
-                "frac_hbm_kernel": round(packed_bytes / (dec_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-            }
-            log("decode", lin.name, out[lin.name])
-            del reps, pk, cd, cs
-            torch.cuda.empty_cache()
+    for dq, tag in ((True, ""), (False, "_fp32_scales")):
+        for T in (1, 4, 16):
+            for lin in workloads.decode_70b(T):
+                inp = workloads.layer_inputs(lin.d_out, lin.d_in, T, lin.r, lin.seed, with_dy=False)
+                W = torch.from_numpy(inp["W"]).cuda()
+                pk, cd, cs = q.qlora_quantize_nf4(W, double_quant=dq)
+                del W
+                reps = [(pk.clone(), cd.clone(), cs.clone()) for _ in range(copies)]
+                X, A, B = (bf16_dev(inp[k]) for k in ("X", "A", "B"))
+                Y = torch.empty((T, lin.d_out), dtype=torch.bfloat16, device="cuda")
+                U = torch.empty((T, lin.r), dtype=torch.float32, device="cuda")
+                ws = torch.empty(max(1, q.qlora_fwd_workspace_bytes(lin.d_out, lin.d_in, T, lin.r)),
+                                 dtype=torch.uint8, device="cuda")
+                for i in range(warmup):
+                    p = reps[i % copies]
+                    q.qlora_linear_fwd(p[0], p[1], p[2], X, A, B, lin.alpha, Y=Y, U_out=U, workspace=ws)
+                torch.cuda.synchronize()
+                q.qlora_trace_read(reset=True)
+                q.qlora_trace_select({"decode"})
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for i in range(steps):
+                    p = reps[i % copies]
+                    q.qlora_linear_fwd(p[0], p[1], p[2], X, A, B, lin.alpha, Y=Y, U_out=U, workspace=ws)
+                e1.record()
+                torch.cuda.synchronize()
+                q.qlora_trace_enable(False)
+                kt = q.qlora_trace_read(reset=True)
+                call_ms = e0.elapsed_time(e1) / steps
+                packed_bytes = pk.numel() + cd.numel() + cs.numel() * 4
+                dec_n, dec_ms = kt.get("decode", (1, float("nan")))
+                dec_avg = dec_ms / max(dec_n, 1)
+                out[lin.name + tag] = {
+                    "T": T, "d_out": lin.d_out, "d_in": lin.d_in,
+                    "scales": "8-bit codes + fp32 group constants" if dq else "fp32 per block (no second level)",
+                    "packed_weight_bytes": packed_bytes,
+                    "call_us": round(call_ms * 1e3, 2),
+                    "packed_GBps_call": round(packed_bytes / (call_ms * 1e-3) / 1e9, 1),
+                    "decode_kernel_us": round(dec_avg * 1e3, 2),
+                    "packed_GBps_kernel": round(packed_bytes / (dec_avg * 1e-3) / 1e9, 1),
+                    "frac_hbm_kernel": round(packed_bytes / (dec_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                }
+                log("decode", lin.name + tag, out[lin.name + tag])
+                del reps, pk, cd, cs
+                torch.cuda.empty_cache()
     return out
 
 
@@ -582,6 +589,69 @@ def mlp_section(steps):
     out["config"] = "gate/up 4096->11008, down 11008->4096, 4096 tokens, r=64, alpha=16"
     log("mlp", out)
     del st
+    return out
+
+
+def multi_proj_train_section(steps):
+    """The projection groups of one 65B-class layer at 4096 tokens (r = 64,
+    alpha = 16): query/key/value (three 8192 x 8192 weights) and gate/up (two
+    8192 -> 22016), forward and backward, as one group call (one forward
+    product over the group's weights, one dX product over their rows) against
+    one call per weight.  Times in ms per group, fwd + bwd."""
+    import torch
+    import nf4_bit_quantized_amd as q
+
+    K, T, r, alpha = 8192, 4096, 64, 16.0
+    g = torch.Generator(device="cuda").manual_seed(1)
+    out = {"tokens": T, "r": r}
+    for name, shapes in (("qkv", (8192, 8192, 8192)), ("gate_up", (22016, 22016))):
+        layers, dYs, outs, grads = [], [], [], []
+        for N in shapes:
+            pk, cd, cs = q.qlora_quantize_nf4(torch.randn(N, K, device="cuda", generator=g) * 0.02)
+            layers.append((pk, cd, cs, (torch.randn(r, K, device="cuda", generator=g) / r).to(torch.bfloat16),
+                           (torch.randn(N, r, device="cuda", generator=g) * 0.01).to(torch.bfloat16)))
+            dYs.append(torch.randn(T, N, device="cuda", generator=g).to(torch.bfloat16))
+            outs.append((torch.empty((T, N), dtype=torch.bfloat16, device="cuda"),
+                         torch.empty((T, r), dtype=torch.float32, device="cuda")))
+            grads.append((torch.empty((r, K), dtype=torch.float32, device="cuda"),
+                          torch.empty((N, r), dtype=torch.float32, device="cuda")))
+        X = torch.randn(T, K, device="cuda", generator=g).to(torch.bfloat16)
+        dX = torch.empty((T, K), dtype=torch.bfloat16, device="cuda")
+        ws_bytes = max(q.qlora_multi_fwd_workspace_bytes([(N, K) for N in shapes], T, r),
+                       q.qlora_multi_bwd_workspace_bytes([(N, K) for N in shapes], T, r))
+        ws = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device="cuda")
+
+        def fused():
+            q.qlora_linear_fwd_multi(layers, X, alpha, workspace=ws, outs=outs)
+            q.qlora_linear_bwd_multi(layers, X, alpha, dYs, U_ins=[o[1] for o in outs], workspace=ws, dX=dX,
+                                     grads=grads)
+
+        def separate():
+            for l, o in zip(layers, outs):
+                q.qlora_linear_fwd(*l[:3], X, l[3], l[4], alpha, Y=o[0], U_out=o[1], workspace=ws)
+            for i, (l, o, dy, gr) in enumerate(zip(layers, outs, dYs, grads)):
+                # one bf16 dX per weight; the caller would add them (not timed)
+                q.qlora_linear_bwd(*l[:3], X, l[3], l[4], alpha, dy, U_in=o[1], dX=dX, dA=gr[0], dB=gr[1],
+                                   workspace=ws)
+
+        flops = sum(sum(layer_flops(T, K, N, r)) for N in shapes)
+        for label, fn in (("group_call", fused), ("per_weight_calls", separate)):
+            for _ in range(2):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / steps
+            out[f"{name}_{label}_ms"] = round(ms, 3)
+            out[f"{name}_{label}_tflops"] = round(flops / (ms * 1e-3) / 1e12, 1)
+        del layers, dYs, outs, grads, X, dX, ws
+    out["note"] = ("per-weight calls leave X's gradient as one bf16 tensor per weight (their sum is not "
+                   "timed); the group call sums the shares in fp32 and rounds once")
+    log("multi_proj_train", out)
     return out
 
 
@@ -820,6 +890,7 @@ def main():
         result["adamw_65b_adapters"] = adamw_section(steps=sec_steps)
         result["lora_dropout_attn4096"] = dropout_section(lin, steps=sec_steps)
         result["qkv_gqa_70b"] = multi_proj_section(steps=sec_steps)
+        result["projection_groups_65b"] = multi_proj_train_section(steps=10)
     if not args.no_cpu_baseline:
         log("timing the oracle on the host ...")
         result["cpu_baseline"] = cpu_baseline_headline()
