@@ -40,6 +40,13 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 // log2(blocksize / 64): 64-weight chunk index -> block index
 int block_shift(const qlora_nf4_desc* d) { return d->blocksize == 256 ? 2 : (d->blocksize == 128 ? 1 : 0); }
 
+// The few-token kernel takes this weight (8-bit codes are staged from a
+// 16-byte aligned run; fp32 block scales are read per chunk).
+bool decode_ok(const qlora_nf4_desc* d, const uint8_t* codes) {
+  const bool f32s = d->dq_blocksize == 0;
+  return decode_supported(d->d_out, d->d_in, block_shift(d), f32s) && (f32s || aligned16(codes));
+}
+
 int check_desc(const qlora_nf4_desc* d) {
   if (!d) return QLORA_ERR_NULL;
   if ((d->blocksize != 64 && d->blocksize != 128 && d->blocksize != 256) ||
@@ -308,10 +315,11 @@ static int enqueue_fwd(const qlora_nf4_desc* d, const uint8_t* packed, const uin
     const int e = lora_down(Xa, A, T, K, r, s, w.part, U, w.Us, s_);
     if (e) return e;
   }
-  // the few-token kernel stages 8-bit codes; fp32 block scales take the tiled kernel
-  if (T <= kDecodeMaxT && d->dq_blocksize != 0 && decode_supported(N, K, block_shift(d)) && aligned16(codes)) {
+  // few tokens: the weight-streaming kernel (it stages 8-bit codes in LDS, so
+  // those must be 16-byte aligned; fp32 block scales are loaded per chunk)
+  if (T <= kDecodeMaxT && decode_ok(d, codes)) {
     HIP_TRY(launch_decode(packed, codes, consts, X, T, N, K, w.Us, hilo_ld(r), B, r, Y, d->table, block_shift(d),
-                          s_));
+                          d->dq_blocksize == 0, s_));
     return QLORA_OK;
   }
   FusedParams fp{};
@@ -665,9 +673,8 @@ int qlora_linear_fwd_multi(int32_t n, const qlora_nf4_desc* d, const uint8_t* co
 
   hipStream_t s_ = (hipStream_t)stream;
   const int64_t K = d[0].d_in;
-  bool fused = T <= kDecodeMaxT && d[0].dq_blocksize != 0;
-  for (int i = 0; i < n && fused; ++i)
-    fused = decode_supported(d[i].d_out, K, block_shift(&d[i])) && aligned16(codes[i]);
+  bool fused = T <= kDecodeMaxT;
+  for (int i = 0; i < n && fused; ++i) fused = decode_ok(&d[i], codes[i]);
   if (!fused && n > 1 && T > kDecodeMaxT) {
     // many tokens: each weight's U = X A^T, then one product over all the
     // weights (their output columns side by side), when every weight is
@@ -727,7 +734,7 @@ int qlora_linear_fwd_multi(int32_t n, const qlora_nf4_desc* d, const uint8_t* co
     w[i] = DecodeWeight{packed[i], codes[i], consts[i], d[i].d_out, r > 0 ? B[i] : nullptr, Y[i], d[i].table};
     us[i] = fw.Us;
   }
-  HIP_TRY(launch_decode_multi(w, n, X, T, K, us, hilo_ld(r), r, block_shift(&d[0]), s_));
+  HIP_TRY(launch_decode_multi(w, n, X, T, K, us, hilo_ld(r), r, block_shift(&d[0]), d[0].dq_blocksize == 0, s_));
   return QLORA_OK;
 }
 

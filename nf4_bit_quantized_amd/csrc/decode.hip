@@ -40,6 +40,11 @@
 //
 // Rank-r term: added per tile after the sum, s (X A^T) B^T through the same
 // MFMA over the 2r hi/lo columns of s U (zero-padded to a multiple of 64).
+//
+// Without the second level (fp32 block scales, "7、QLoRA 量化微调" §7.1) the
+// scales are 4 bytes per block, too many to stage per workgroup (57 KB at the
+// 8192 <-> 28672 shapes); each lane instead loads its row's two block scales
+// of a chunk together with that chunk's packed bytes, into registers.
 #include "decode.hpp"
 #include "trace.hpp"
 
@@ -89,6 +94,7 @@ template <int NTW, int XQ>
 struct ChunkRegs {
   u32x4_t x[XQ];
   u32x4_t w[NTW];
+  float s[NTW][2];  // fp32 block scales of the chunk's two halves (fp32-scale format only)
 };
 
 // Four table lookups of the bytes of packed dword d -> 8 restored bf16 in element order.
@@ -119,8 +125,9 @@ __device__ __forceinline__ f32x4_t mfma(bf16x8_t a, bf16x8_t b, f32x4_t c) {
 // DW: waves per workgroup (8 or 16).  NTW: 16-row tiles per workgroup.  XQ: X
 // loads per chunk (1 for T <= 4, else 4).  CODES2: K/64 is even, so a chunk's
 // two codes are one aligned 2-byte LDS read and its two blocks (an even block
-// index and the next) never straddle a group of 256 blocks.
-template <int DW, int NTW, int XQ, bool CODES2>
+// index and the next) never straddle a group of 256 blocks.  F32S: fp32 block
+// scales in consts (no codes).
+template <int DW, int NTW, int XQ, bool CODES2, bool F32S = false>
 __global__ __launch_bounds__(DW * 64) void k_decode(DecodeMulti M) {
   // this workgroup's weight (a wave-uniform choice)
   int pi = 0;
@@ -156,8 +163,8 @@ __global__ __launch_bounds__(DW * 64) void k_decode(DecodeMulti M) {
 
   const __amdgpu_buffer_rsrc_t rw = rsrc(P.packed, P.N * P.K / 2);
   const __amdgpu_buffer_rsrc_t rx = rsrc(P.X, P.T * P.K * 2);
-  const __amdgpu_buffer_rsrc_t rc = rsrc(P.codes, P.N * nbc);
-  const __amdgpu_buffer_rsrc_t rk = rsrc(P.consts, ((P.N * nbc + 255) / 256) * 4);
+  const __amdgpu_buffer_rsrc_t rc = rsrc(P.codes, F32S ? 0 : P.N * nbc);
+  const __amdgpu_buffer_rsrc_t rk = rsrc(P.consts, F32S ? P.N * nbc * 4 : ((P.N * nbc + 255) / 256) * 4);
 
   // the workgroup's codes: rows nt0*16 .. are one contiguous, 16-byte aligned
   // run of 16*NTW*nbc bytes in memory (rows past N read zero); in LDS each row
@@ -165,10 +172,10 @@ __global__ __launch_bounds__(DW * 64) void k_decode(DecodeMulti M) {
   // read at one column fall in distinct banks.  Then the ratios c_g / 255 of
   // the groups of 256 blocks the run spans.
   const uint32_t cfirst = (uint32_t)nt0 * 16u * (uint32_t)nbc;
-  const uint32_t cbytes = 16u * NTW * (uint32_t)nbc;
+  const uint32_t cbytes = F32S ? 0u : 16u * NTW * (uint32_t)nbc;
   const uint32_t rs = 4u * (((uint32_t)(nbc + 3) >> 2) | 1u);
   const uint32_t g_lo = cfirst >> 8;
-  const uint32_t ngr = ((cfirst + cbytes - 1u) >> 8) - g_lo + 1u;
+  const uint32_t ngr = F32S ? 0u : ((cfirst + cbytes - 1u) >> 8) - g_lo + 1u;
   float* ratio = reinterpret_cast<float*>(aux + ((16u * NTW * rs + 15u) & ~15u));
   constexpr int CQ = CODES_BYTES / 16 / DT;
   u32x4_t cv[CQ];
@@ -208,6 +215,16 @@ __global__ __launch_bounds__(DW * 64) void k_decode(DecodeMulti M) {
     const bool in = ch < nch && ch * 64 + 16 * g < K / 2 && nt0 + i < ntiles;
     R.w[i] = __builtin_amdgcn_raw_buffer_load_b128(
         rw, in ? wbase + (uint32_t)i * wtile + (uint32_t)ch * 64u : kOob, 0, 0);
+    if (F32S) {
+      // this lane's row's scales of the chunk's two 64-weight halves (the same
+      // block for blocks of 128 or 256; zero for a half past the row's end)
+      const bool rin = ch < nch && nt0 + i < ntiles;
+      const uint32_t rb = (n0 + 16u * (uint32_t)i) * (uint32_t)nbc;
+      const uint32_t b0 = (uint32_t)(2 * ch) >> P.bshift, b1 = (uint32_t)(2 * ch + 1) >> P.bshift;
+      R.s[i][0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rk, rin ? (rb + b0) * 4u : kOob, 0, 0));
+      R.s[i][1] = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(rk, rin && 2 * ch + 1 < nbk ? (rb + b1) * 4u : kOob, 0, 0));
+    }
   };
 
   // the first chunks' loads go out before the table is built
@@ -280,7 +297,10 @@ __global__ __launch_bounds__(DW * 64) void k_decode(DecodeMulti M) {
         // lane's row (zero for a chunk past the row's end, whose weights read zero)
         const uint32_t row = (uint32_t)(16 * i + i16);
         float s0, s1;
-        if (CODES2) {  // 64-weight blocks, an even count per row
+        if (F32S) {
+          s0 = R[sp].s[i][0];
+          s1 = R[sp].s[i][1];
+        } else if (CODES2) {  // 64-weight blocks, an even count per row
           const uint32_t cl = row * rs + (uint32_t)(2 * chc);                     // code byte in LDS
           const uint32_t gb = cfirst + row * (uint32_t)nbc + (uint32_t)(2 * chc);  // its block index
           const uint32_t c2 = *reinterpret_cast<const uint16_t*>(aux + cl);
@@ -389,11 +409,19 @@ __global__ __launch_bounds__(DW * 64) void k_decode(DecodeMulti M) {
 
 // 16 waves where their 128 registers per lane hold the loop, else 8
 template <int NTW>
-void launch_ntw(const DecodeMulti& P, bool c2, unsigned grid, hipStream_t stream) {
+void launch_ntw(const DecodeMulti& P, bool c2, bool f32s, unsigned grid, hipStream_t stream) {
   const dim3 g(grid);
   KernelEvents ev(KID_DECODE);
   const hipEvent_t e0 = ev.start(), e1 = ev.stop();
-  if (c2 && P.p[0].T <= 4) {
+  if (f32s) {
+    if (P.p[0].T <= 4) {
+      if constexpr (NTW <= 6)
+        hipExtLaunchKernelGGL((k_decode<16, NTW, 1, false, true>), g, dim3(1024), 0, stream, e0, e1, 0, P);
+      else hipExtLaunchKernelGGL((k_decode<8, NTW, 1, false, true>), g, dim3(512), 0, stream, e0, e1, 0, P);
+    } else {
+      hipExtLaunchKernelGGL((k_decode<8, NTW, 4, false, true>), g, dim3(512), 0, stream, e0, e1, 0, P);
+    }
+  } else if (c2 && P.p[0].T <= 4) {
     if constexpr (NTW <= 7) hipExtLaunchKernelGGL((k_decode<16, NTW, 1, true>), g, dim3(1024), 0, stream, e0, e1, 0, P);
     else hipExtLaunchKernelGGL((k_decode<8, NTW, 1, true>), g, dim3(512), 0, stream, e0, e1, 0, P);
   } else if (c2) {
@@ -408,24 +436,26 @@ void launch_ntw(const DecodeMulti& P, bool c2, unsigned grid, hipStream_t stream
 
 }  // namespace
 
-// Rows hold whole blocks, and the workgroup's codes must fit their LDS region
-// with at least one 16-row tile.
-bool decode_supported(int64_t N, int64_t K, int bshift) {
+// Rows hold whole blocks, and (with 8-bit scale codes) the workgroup's codes
+// must fit their LDS region with at least one 16-row tile.
+bool decode_supported(int64_t N, int64_t K, int bshift, bool f32s) {
   if (N % 16 != 0 || K % (64 << bshift) != 0 || N * K / 2 > 0x7FFFFFF0LL) return false;
+  if (f32s) return N * ((K / 64) >> bshift) * 4 <= 0x7FFFFFF0LL;
   const int64_t nbc = (K / 64) >> bshift;
   const int64_t rs = 4 * (((nbc + 3) / 4) | 1);
   return ((16 * rs + 15) & ~15LL) + 4 * (16 * nbc / 256 + 2) <= CODES_BYTES;
 }
 
 hipError_t launch_decode_multi(const DecodeWeight* w, int n, const uint16_t* X, int64_t T, int64_t K,
-                               const uint16_t* const* Us, int64_t ldh, int r, int bshift, hipStream_t stream) {
+                               const uint16_t* const* Us, int64_t ldh, int r, int bshift, bool f32s,
+                               hipStream_t stream) {
   // byte offsets into the packed weight, codes and X are 32-bit
   if (n < 1 || n > kMaxProj || T < 1 || T > 16 || bshift < 0 || bshift > 2) return hipErrorInvalidValue;
   DecodeMulti M{};
   M.n = n;
   int64_t ntiles_all = 0;
   for (int i = 0; i < n; ++i) {
-    if (!decode_supported(w[i].N, K, bshift)) return hipErrorInvalidValue;
+    if (!decode_supported(w[i].N, K, bshift, f32s)) return hipErrorInvalidValue;
     DecodeParams& P = M.p[i];
     P.packed = w[i].packed; P.codes = w[i].codes; P.consts = w[i].consts; P.X = X;
     P.T = T; P.N = w[i].N; P.K = K;
@@ -444,8 +474,8 @@ hipError_t launch_decode_multi(const DecodeWeight* w, int n, const uint16_t* X, 
   const int64_t nbc = (K / 64) >> bshift;             // scale codes per row
   const int64_t rs = 4 * (((nbc + 3) / 4) | 1);      // LDS row stride of the codes
   auto aux_need = [&](int64_t t) { return ((16 * t * rs + 15) & ~15LL) + 4 * (16 * t * nbc / 256 + 2); };
-  while (ntw > 1 && aux_need(ntw) > CODES_BYTES) --ntw;
-  if (aux_need(ntw) > CODES_BYTES) return hipErrorInvalidValue;
+  while (!f32s && ntw > 1 && aux_need(ntw) > CODES_BYTES) --ntw;
+  if (!f32s && aux_need(ntw) > CODES_BYTES) return hipErrorInvalidValue;
   int64_t wg = 0;
   for (int i = 0; i < n; ++i) {
     M.first_wg[i] = (int)wg;
@@ -455,23 +485,23 @@ hipError_t launch_decode_multi(const DecodeWeight* w, int n, const uint16_t* X, 
   const unsigned grid = (unsigned)wg;
   const bool c2 = bshift == 0 && (K / 64) % 2 == 0;
   switch (ntw) {
-    case 1: launch_ntw<1>(M, c2, grid, stream); break;
-    case 2: launch_ntw<2>(M, c2, grid, stream); break;
-    case 3: launch_ntw<3>(M, c2, grid, stream); break;
-    case 4: launch_ntw<4>(M, c2, grid, stream); break;
-    case 5: launch_ntw<5>(M, c2, grid, stream); break;
-    case 6: launch_ntw<6>(M, c2, grid, stream); break;
-    case 7: launch_ntw<7>(M, c2, grid, stream); break;
-    default: launch_ntw<8>(M, c2, grid, stream); break;
+    case 1: launch_ntw<1>(M, c2, f32s, grid, stream); break;
+    case 2: launch_ntw<2>(M, c2, f32s, grid, stream); break;
+    case 3: launch_ntw<3>(M, c2, f32s, grid, stream); break;
+    case 4: launch_ntw<4>(M, c2, f32s, grid, stream); break;
+    case 5: launch_ntw<5>(M, c2, f32s, grid, stream); break;
+    case 6: launch_ntw<6>(M, c2, f32s, grid, stream); break;
+    case 7: launch_ntw<7>(M, c2, f32s, grid, stream); break;
+    default: launch_ntw<8>(M, c2, f32s, grid, stream); break;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_decode(const uint8_t* packed, const uint8_t* codes, const float* consts, const uint16_t* X,
                          int64_t T, int64_t N, int64_t K, const uint16_t* Us, int64_t ldh, const uint16_t* B,
-                         int r, uint16_t* Y, int table, int bshift, hipStream_t stream) {
+                         int r, uint16_t* Y, int table, int bshift, bool f32s, hipStream_t stream) {
   const DecodeWeight w{packed, codes, consts, N, B, Y, table};
-  return launch_decode_multi(&w, 1, X, T, K, &Us, ldh, r, bshift, stream);
+  return launch_decode_multi(&w, 1, X, T, K, &Us, ldh, r, bshift, f32s, stream);
 }
 
 }  // namespace qlora

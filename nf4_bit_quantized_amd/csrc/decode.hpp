@@ -18,13 +18,15 @@ struct DecodeWeight {
 
 constexpr int kDecodeMaxWeights = 4;
 
-bool decode_supported(int64_t N, int64_t K, int bshift);
+// f32s: fp32 block scales in consts (no second level, no codes)
+bool decode_supported(int64_t N, int64_t K, int bshift, bool f32s);
 hipError_t launch_decode(const uint8_t* packed, const uint8_t* codes, const float* consts, const uint16_t* X,
                          int64_t T, int64_t N, int64_t K, const uint16_t* Us, int64_t ldh, const uint16_t* B,
-                         int r, uint16_t* Y, int table, int bshift, hipStream_t stream);
+                         int r, uint16_t* Y, int table, int bshift, bool f32s, hipStream_t stream);
 // Up to kDecodeMaxWeights weights sharing X (and T, K, r, the block format) in
 // one launch; Us[i] is weight i's hi/lo pair of s*U.
 hipError_t launch_decode_multi(const DecodeWeight* w, int n, const uint16_t* X, int64_t T, int64_t K,
-                               const uint16_t* const* Us, int64_t ldh, int r, int bshift, hipStream_t stream);
+                               const uint16_t* const* Us, int64_t ldh, int r, int bshift, bool f32s,
+                               hipStream_t stream);
 
 }  // namespace qlora

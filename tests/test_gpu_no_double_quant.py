@@ -92,3 +92,59 @@ def test_exports(bs):
     W2 = q.qlora_dequantize_nf4(p2, c2, k2)
     torch.cuda.synchronize()
     assert not torch.equal(W2.view(torch.int16), Wh.view(torch.int16))
+
+
+@pytest.mark.parametrize("d_out,d_in", [(28672, 8192), (8192, 28672)])
+def test_decode_shapes_full_size_sampled(d_out, d_in):
+    """The few-token forward in this format at the decode shapes, T = 1, 4
+    and 16, r = 64, alpha = 16, on the weight-streaming kernel (one `decode`
+    launch per call): Y on 48 sampled output columns against the oracle
+    (normwise, and per element within the kernel's rounding bound), the
+    sampled rows' packed bytes and fp32 scales bit-exact.  Without the second level every 64-weight block of a
+    row is quantized on its own, so the oracle quantizes just those rows."""
+    import nf4_bit_quantized_amd as q
+    import torch
+    from gpu_helpers import elementwise_stats
+    from oracle import lora as olora
+    r, alpha = 64, 16.0
+    say(f"fp32 scales decode shape {d_out}x{d_in}: drawing inputs")
+    inp = workloads.layer_inputs(d_out, d_in, 16, r, seed=6, with_dy=False)
+    rng = np.random.default_rng(d_out + 3 * d_in)
+    rows = np.sort(rng.choice(d_out, size=48, replace=False))
+    Q = onf4.quantize(inp["W"][rows], dq_blocksize=0)
+    packed, codes, consts = q.qlora_quantize_nf4(dev_f32(inp["W"]), double_quant=False)
+    assert codes.numel() == 0
+    nb = d_in // 64
+    np.testing.assert_array_equal(packed[torch.as_tensor(rows, device="cuda")].cpu().numpy(),
+                                  Q.packed.reshape(len(rows), d_in // 2))
+    np.testing.assert_array_equal(consts.view(d_out, nb)[torch.as_tensor(rows, device="cuda")].cpu().numpy()
+                                  .view(np.uint32), Q.scales.reshape(len(rows), nb).view(np.uint32))
+    say("  sampled rows bit-exact")
+    W_rows = onf4.dequantize(Q).astype(np.float64)
+    X = bits_to_float(inp["X"])
+    A, B = bits_to_float(inp["A"]), bits_to_float(inp["B"])
+    Ag, Bg = dev_bf16(inp["A"]), dev_bf16(inp["B"])
+    ri = torch.as_tensor(rows, device="cuda")
+    for T in (1, 4, 16):
+        Xg = dev_bf16(inp["X"][:T])
+        q.qlora_trace_select({"decode"})
+        q.qlora_trace_read(reset=True)
+        try:
+            Y, _ = q.qlora_linear_fwd(packed, codes, consts, Xg, Ag, Bg, alpha)
+            torch.cuda.synchronize()
+            assert q.qlora_trace_read(reset=True).get("decode", (0, 0.0))[0] == 1
+        finally:
+            q.qlora_trace_enable(False)
+        got = host_bf16_to_f64(Y.index_select(1, ri))
+        want, _ = olora.forward(W_rows, X[:T], A, B[rows], alpha, r)
+        # per element: this kernel scales each block's products by s' in fp32
+        # instead of rounding T[q] * s' to bf16 first, one bf16 rounding (2^-8)
+        # per weight; with the output's own rounding the error stays within
+        # 2^-8 |Y| + 2^-7 (sum of the terms' magnitudes), which the oracle gives
+        # on absolute values
+        mag, _ = olora.forward(np.abs(W_rows), np.abs(X[:T]), np.abs(A), np.abs(B[rows]), alpha, r)
+        worst = float(np.max(np.abs(got - want) / (2.0 ** -8 * np.abs(want) + 2.0 ** -7 * mag)))
+        err, st = normwise_err(got, want), elementwise_stats(got, want)
+        say(f"  T={T}: normwise {err:.2e}, elementwise {st}, rounding-bound ratio {worst:.3f}")
+        assert err <= TOL
+        assert worst <= 1.0
