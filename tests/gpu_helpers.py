@@ -56,6 +56,37 @@ def elementwise_stats(got, want, floor: float = 1e-3) -> dict:
     return {"max_rel": float(np.max(rel)), "share_above_1e-2": float(np.mean(rel > 1e-2))}
 
 
+def rounding_bound_ratio(got, want, mag, c: float) -> float:
+    """Largest |got - want| / (2^-8 |want| + c * mag) over the elements: mag is
+    the oracle's result on absolute values (a bound on the sum of the terms'
+    magnitudes).  2^-8 |want| covers the output's own bf16 rounding; c * mag
+    covers accumulation and the bf16 steps inside the kernel.  At or below 1
+    means every element is within that bound; a local fault (one wrong block
+    scale, a wrong tail column) exceeds it."""
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    den = 2.0 ** -8 * np.abs(want) + c * np.asarray(mag, np.float64) + 1e-30
+    return float(np.max(np.abs(got - want) / den))
+
+
+def oracle_magnitudes(inp, r, alpha, Q=None, levels=None, do_bwd=True):
+    """oracle_layer on absolute values: |X| |W_hat|^T + s (|X| |A|^T) |B|^T and
+    the backward's counterparts, bounds on each output's sum of term
+    magnitudes."""
+    if Q is None:
+        Q = onf4.quantize(inp["W"], levels=levels)
+    W = np.abs(onf4.dequantize(Q, levels=levels).astype(np.float64))
+    X = np.abs(bits_to_float(inp["X"]))
+    A = np.abs(bits_to_float(inp["A"])) if r > 0 else None
+    B = np.abs(bits_to_float(inp["B"])) if r > 0 else None
+    Y, U = olora.forward(W, X, A, B, alpha, r)
+    out = {"Y": Y, "U": U}
+    if do_bwd:
+        dX, dA, dB = olora.backward(W, X, A, B, np.abs(bits_to_float(inp["dY"])), alpha, r)
+        out.update(dX=dX, dA=dA, dB=dB)
+    return out
+
+
 def oracle_sampled(Q, X, A, B, dY, alpha, r, rows, cols):
     """The oracle's layer on sampled outputs of a full-size weight: Y and dB
     on output rows ``rows``, dX (this layer's share) and dA on input columns
