@@ -7,6 +7,10 @@ workspace with torch, and calls the entry point through ctypes.  Every step of
 the layer runs in the library's HIP kernels.  If the library is not built, or
 no GPU is present when a compute call is made, an error is raised: there is no
 fallback implementation.
+
+The library loaded is ``libqlora_nf4.so`` next to this file, or the file that
+the environment variable ``QLORA_NF4_LIBRARY`` names (for example a build of
+the same sources with host-side sanitizers).
 """
 
 import ctypes
@@ -14,7 +18,7 @@ import os
 from typing import Optional, Tuple
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libqlora_nf4.so")
+LIB_PATH = os.environ.get("QLORA_NF4_LIBRARY") or os.path.join(HERE, "libqlora_nf4.so")
 
 QLORA_OK = 0
 QLORA_ERR_NULL = -1
