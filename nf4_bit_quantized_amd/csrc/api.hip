@@ -118,6 +118,7 @@ FwdWs plan_fwd(const qlora_nf4_desc* d, int64_t T, int32_t r, void* ws) {
 struct BwdWs {
   float* part = nullptr;   // shared by the rank-r products that run one after another
   float* part2 = nullptr;  // dB's partials (it runs in the same launch as dA)
+  size_t part_bytes = 0;
   float* U = nullptr;
   uint16_t* Us = nullptr;
   uint16_t* Gs = nullptr;
@@ -136,7 +137,12 @@ BwdWs plan_bwd(const qlora_nf4_desc* d, int64_t T, int32_t r, void* ws) {
     if (!lora_stream_ok(r)) {
       part = std::max(part, skinny_part_bytes(K, T, 2 * (int64_t)r));
       part2 = skinny_part_bytes(N, T, 2 * (int64_t)r);
+    } else {
+      // the streaming dA/dB kernel's token-range partials (it runs after G is done with part)
+      const int64_t Ds[2] = {K, N};
+      part = std::max(part, lora_cols_part_bytes(T, Ds, 2, r));
     }
+    w.part_bytes = part;
     w.part = static_cast<float*>(c.take(part));
     w.part2 = static_cast<float*>(c.take(part2));
     w.U = static_cast<float*>(c.take((size_t)T * r * 4));
@@ -487,7 +493,7 @@ static int enqueue_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uin
       C.p[0] = ColsParams{Xa, K, K, w.Gs, ldh, T, r, 1, dA, accumulate};
       C.p[1] = ColsParams{dY, N, N, w.Us, ldh, T, r, 0, dB, accumulate};
       C.n = 2;
-      HIP_TRY(launch_lora_cols(C, s_, KID_LORA_DA));
+      HIP_TRY(launch_lora_cols(C, w.part, w.part_bytes, s_, KID_LORA_DA));
     } else {
       SkinnyParams Sa = skinny(Xa, K, false, K, T, r, s, 2 * r, OUT_PAIRS_T, w.part);
       skinny_q(Sa, w.Gs, ldh, 2 * (int64_t)r, Q_STRIDED);

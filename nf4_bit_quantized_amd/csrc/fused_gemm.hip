@@ -321,14 +321,24 @@ __device__ __forceinline__ void restore_step(StepRegs<BN>& f, const Nf4Table& ta
   w_coords<BN, BT>(lrow, lcol);
   const RestoreTab t = make_tab(tab, dq ? restored_scale((f.code4 >> f.code_shift) & 0xFFu, f.cg) : f.cg);
   static_assert(!BT || BN == 128, "the dX tile swizzle covers 128 columns");
+  // dX: the four threads of a row store their 16-byte pieces (8 columns each)
+  // in two orders: threads 2 and 3 start with their third piece.  A 16-byte
+  // store is done 8 lanes (two rows) at a time on 32 banks, where threads 0
+  // and 2 of a row, 64 columns apart, would otherwise share banks; with the
+  // tile swizzle (bt_col) every store then touches each bank once.
+  const bool rot = BT && (ptid() & 2) != 0;
+  const uint32_t w0 = rot ? f.w[2] : f.w[0], w1 = rot ? f.w[3] : f.w[1];
+  const uint32_t w2 = rot ? f.w[0] : f.w[2], w3 = rot ? f.w[1] : f.w[3];
+  const uint32_t ww[4] = {w0, w1, w2, w3};
 #pragma unroll
   for (int i = 0; i < BN / 32; i += 2) {
     uint32_t o[8];
-    restore8(f.w[i], t, o);
-    restore8(f.w[i + 1], t, o + 4);
-    uint16_t* d0 = BT ? Bs + lrow * Geometry<BN, BT>::LDB_T + bt_col(lrow, lcol + i * 8) : Bs + lrow * LDK + lcol + i * 8;
-    uint16_t* d1 = BT ? Bs + lrow * Geometry<BN, BT>::LDB_T + bt_col(lrow, lcol + i * 8 + 8)
-                      : Bs + lrow * LDK + lcol + i * 8 + 8;
+    restore8(BT ? ww[i] : f.w[i], t, o);
+    restore8(BT ? ww[i + 1] : f.w[i + 1], t, o + 4);
+    const int c0 = BT ? lcol + (((i + (rot ? 2 : 0)) & 3) * 8) : lcol + i * 8;
+    const int c1 = BT ? lcol + (((i + 1 + (rot ? 2 : 0)) & 3) * 8) : lcol + i * 8 + 8;
+    uint16_t* d0 = BT ? Bs + lrow * Geometry<BN, BT>::LDB_T + bt_col(lrow, c0) : Bs + lrow * LDK + c0;
+    uint16_t* d1 = BT ? Bs + lrow * Geometry<BN, BT>::LDB_T + bt_col(lrow, c1) : Bs + lrow * LDK + c1;
     *reinterpret_cast<uint4*>(d0) = make_uint4(o[0], o[1], o[2], o[3]);
     *reinterpret_cast<uint4*>(d1) = make_uint4(o[4], o[5], o[6], o[7]);
   }

@@ -57,6 +57,36 @@ __device__ __forceinline__ bf16x8_t tr_frag(const uint16_t* tile, int ld, int kb
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
+// Row-major tiles read with transposing reads: the 16-byte piece p of row R
+// is stored at piece p ^ tr_swz(R, pieces per row).  A transposing read (16
+// lanes: four rows from a multiple of four, two adjacent pieces; the lanes of
+// a 32-lane half take rows 8 further on) then touches each LDS bank at most
+// once per 32 lanes (64 banks) and per 16 lanes (32 banks); with an
+// unswizzled row of 64 bytes or more those rows fall on the same banks.  Row
+// bit 2 is left out, so rows R and R + 4 (the two halves of a fragment) share
+// the swizzle.  Widths of other piece counts keep the plain layout.
+__device__ __forceinline__ int tr_swz(int row, int ppr) {
+  const int b0 = row & 1, b1 = (row >> 1) & 1, b3 = (row >> 3) & 1;
+  if (ppr == 4) return 2 * (b1 ^ b3);
+  if (ppr == 8) return (2 * b0) ^ (4 * b1) ^ (2 * b3);
+  if (ppr == 16 || ppr == 32 || ppr == 64) return (2 * b0) ^ (4 * b1) ^ (8 * b3);
+  return 0;
+}
+
+// tr_frag from a tile stored with tr_swz (ld elements per row, a multiple of 8)
+__device__ __forceinline__ bf16x8_t tr_frag_swz(const uint16_t* tile, int ld, int kb, int c0) {
+  const int s = threadIdx.x & 15;
+  const lds_u16_t* base = (const lds_u16_t*)tile;
+  const int col = c0 + 4 * (s & 3);
+  const int row = kb + (s >> 2);
+  const int pcol = (((col >> 3) ^ tr_swz(row, ld >> 3)) << 3) | (col & 7);
+  const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(base + row * ld + pcol));
+  const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(base + (row + 4) * ld + pcol));
+  const u16x8_t v = {(uint16_t)lo[0], (uint16_t)lo[1], (uint16_t)lo[2], (uint16_t)lo[3],
+                     (uint16_t)hi[0], (uint16_t)hi[1], (uint16_t)hi[2], (uint16_t)hi[3]};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
 __device__ __forceinline__ f32x4_t mfma(bf16x8_t a, bf16x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -205,115 +235,202 @@ __global__ __launch_bounds__(256) void k_lora_rows(RowsParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// cols: out[m][j] = sum_t P[t][m] Q[t][j], m in 32 columns per workgroup,
-// j < 2r (hi/lo columns of s*G or s*U), then the pair sums.
+// cols: out[m][j] = sum_t P[t][m] (Q[t][j] + Q[t][j + r]): dA and dB over the
+// hi/lo columns of s*G or s*U.
 //
-// Contraction chunks of 32 tokens; wave w takes chunks w, w+4, ...  A chunk is
-// copied into LDS as two row-major tiles, P [32 t][32 m] and Q [32 t][2r], and
-// both MFMA operands are read with transposing LDS reads (their contraction
-// runs down the rows).  Workgroups b and b+8 run on the same XCD and take the
-// two 64-byte halves of the same 128-byte lines of P.
+// A workgroup of sixteen waves owns 512 output columns m (wave w: columns
+// 32w .. 32w+31) for one range of tokens.  The token ranges of a column slab
+// are split over workgroups so that every CU has one; their fp32 partial sums
+// are added in a fixed order by k_lora_cols_sum (a single range: the kernel
+// writes the result itself).  The waves share each 32-token chunk:
+// - its P tile [32 t][512 m]: one contiguous kilobyte of each token row, from
+//   HBM; pieces of 1 KB per row stream at 5-6 TB/s where pieces of 512 B
+//   reached 3.3 TB/s;
+// - its Q tile [32 t][128 j]: from L2 (the hi/lo columns are small and every
+//   workgroup reads them), staged once per 512 columns of P.
+// Four 40 KB stages fill the LDS; one barrier per chunk tells the waves that
+// every copy of the chunk has landed and that every wave is done with the
+// stage the next copies refill.  Both MFMA operands are read with transposing
+// LDS reads (their contraction runs down the rows); the tiles are stored with
+// tr_swz, the global piece each lane copies being chosen so that it lands at
+// its swizzled place.  The Q tile always holds 128 columns (columns past 2r,
+// and tokens past T, only meet outputs that are never stored).  The pair sums
+// j + (j + r) are formed in registers: the C fragment of
+// v_mfma_f32_16x16x32_bf16 gives lane l column 16 jt + l % 16, so column
+// j + r is in the same lane when 16 divides r, else in lane l ^ 8.
 // ---------------------------------------------------------------------------
 
-template <int J2T>
-__global__ __launch_bounds__(256) void k_lora_cols(ColsBatch B) {
-  constexpr int J2 = 16 * J2T;
-  constexpr int PD = J2T <= 2 ? 6 : (J2T <= 4 ? 4 : 3);  // chunks in flight per wave
-  constexpr int NQ = J2T;                                 // Q copies per chunk: 32 x J2 bf16 / 1 KB
-  constexpr int STAGE = 32 * 32 + 32 * J2;                // bf16 elements per stage
-  constexpr int MAIN = 4 * PD * STAGE * 2;
-  constexpr int RED = 4 * 32 * J2 * 4;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[MAIN > RED ? MAIN : RED];
+constexpr int kColsWaves = 16;
+constexpr int kColsM = 32 * kColsWaves;        // output columns per workgroup
+constexpr int kColsJ = 128;                    // staged Q columns (2r <= 128)
+constexpr int kColsPD = 4;                     // stages
+constexpr int kColsPBytes = 32 * kColsM * 2;   // 32 KB
+constexpr int kColsQBytes = 32 * kColsJ * 2;   // 8 KB
+constexpr int kColsStage = kColsPBytes + kColsQBytes;
+constexpr int kColsCopies = 3;                 // per wave and chunk: two P rows, half a KB of Q
 
-  const ColsParams& p = B.p[blockIdx.y];
-  const int b = blockIdx.x;
-  const int slab = 2 * ((b / 16) * 8 + b % 8) + ((b / 8) & 1);
-  const int64_t m0 = (int64_t)slab * 32;
-  if (m0 >= p.D) return;
+struct ColsLaunch {
+  ColsBatch B;
+  float* part;            // [split] x (the output's layout) fp32 partial sums of product p at part + part_off[p]
+  int64_t part_off[2];
+  int32_t nsplit;         // token ranges per column slab
+  int32_t chunks_per_split;
+  int32_t first_wg[3];    // product p: workgroups first_wg[p] .. first_wg[p+1]-1
+};
+
+typedef const __attribute__((address_space(4))) ColsLaunch* ColsLaunchK;
+
+// R: the rank (8 .. 64, a multiple of 8)
+template <int R>
+__global__ __launch_bounds__(kColsWaves * 64) void k_lora_cols(ColsLaunch L) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kColsPD * kColsStage];
+  // the product is a wave-uniform choice; its fields are read in place from the
+  // kernel-argument segment (indexing the parameter copy at a run-time index
+  // would move it to scratch)
+  const ColsLaunchK LK = (ColsLaunchK)__builtin_amdgcn_kernarg_segment_ptr();
+  const int pi = (int)blockIdx.x >= L.first_wg[1] && L.B.n > 1 ? 1 : 0;
+  const uint16_t* Pp = LK->B.p[pi].P;
+  const int64_t ldp = LK->B.p[pi].ldp, D = LK->B.p[pi].D, T = LK->B.p[pi].T;
+  const uint16_t* Qp = LK->B.p[pi].Q;
+  const int64_t ldq = LK->B.p[pi].ldq;
+  const int local = (int)blockIdx.x - (pi ? L.first_wg[1] : 0);
+  const int slab = local / L.nsplit, split = local - slab * L.nsplit;
+  const int64_t m0 = (int64_t)slab * kColsM;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int g = lane >> 4;
-  const int64_t nch = (p.T + 31) / 32;
-  const int nmine = nch > wave ? (int)((nch - wave + 3) / 4) : 0;
-  const int iters = (nmine + PD - 1) / PD * PD;
+  const int g = lane >> 4, i16 = lane & 15;
+  const int64_t nch_all = (T + 31) / 32;
+  const int64_t c_begin = (int64_t)split * L.chunks_per_split;
+  const int64_t c_end = c_begin + L.chunks_per_split < nch_all ? c_begin + L.chunks_per_split : nch_all;
+  const int nch = (int)(c_end - c_begin);
 
-  const v4i_t rp = rsrc(p.P, p.T * p.ldp * 2);
-  const v4i_t rq = rsrc(p.Q, p.T * p.ldq * 2);
-  uint16_t* stage0 = reinterpret_cast<uint16_t*>(lds) + wave * PD * STAGE;
-  const uint32_t lstage0 = LDS_ADDR(lds) + (uint32_t)(wave * PD * STAGE * 2);
-  // per-lane offsets inside a chunk: P copy q covers tokens 16q + l/4, columns m0 + 8(l%4)
-  const uint32_t poff = (uint32_t)((lane >> 2) * p.ldp * 2 + (m0 + 8 * (lane & 3)) * 2);
-  auto issue = [&](int sp, int k) {
-    const int64_t t0 = (wave + 4 * (int64_t)k) * 32;
-    const uint32_t st = lstage0 + (uint32_t)(sp * STAGE * 2);
+  const v4i_t rp = rsrc(Pp, T * ldp * 2);
+  const v4i_t rq = rsrc(Qp, T * ldq * 2);
+  const uint32_t lds0 = LDS_ADDR(lds);
+  // this wave's copies of a chunk: P tile rows wave and wave + 16 (lane l:
+  // the row's piece l at its swizzled place), and half a kilobyte of the Q
+  // tile, its rows 2 wave and 2 wave + 1 (lanes 0..31)
+  uint32_t pv[2];
+  bool pin[2];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int64_t t = t0 + 16 * q + (lane >> 2);
-      copy16(rp, t < p.T ? (uint32_t)(t0 * p.ldp * 2 + 16 * q * p.ldp * 2) + poff : kOob, st + q * 1024);
-    }
+  for (int c = 0; c < 2; ++c) {
+    const int row = wave + kColsWaves * c;
+    const int piece = lane ^ tr_swz(row, 64);
+    const int64_t col = m0 + 8 * piece;
+    pin[c] = col < D;
+    pv[c] = (uint32_t)((int64_t)row * ldp * 2 + col * 2);
+  }
+  const int qrow = 2 * wave + (lane >> 4);
+  const uint32_t qv = (uint32_t)((int64_t)qrow * ldq * 2 + (((lane & 15) ^ tr_swz(qrow, 16)) * 16));
+  auto issue = [&](int k) {
+    const int64_t ch = c_begin + k;
+    const bool in = k < nch;
+    const uint32_t st = lds0 + (uint32_t)((k % kColsPD) * kColsStage);
+    const uint32_t pbase = (uint32_t)(ch * 32 * ldp * 2), qbase = (uint32_t)(ch * 32 * ldq * 2);
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      const int f = q * 1024 + lane * 16;  // byte of the [32][J2] tile
-      const int64_t t = t0 + f / (J2 * 2);
-      const uint32_t voff = t < p.T ? (uint32_t)(t * p.ldq * 2 + f % (J2 * 2)) : kOob;
-      copy16(rq, voff, st + 2048 + q * 1024);
+    for (int c = 0; c < 2; ++c) {
+      const int row = wave + kColsWaves * c;
+      copy16(rp, in && pin[c] && ch * 32 + row < T ? pbase + pv[c] : kOob, st + (uint32_t)(row * 1024));
     }
+    if (lane < 32) copy16(rq, in && ch * 32 + qrow < T ? qbase + qv : kOob, st + kColsPBytes + (uint32_t)(wave * 512));
   };
 
-  f32x4_t acc[2][J2T];
+  f32x4_t acc[2][8];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int jt = 0; jt < J2T; ++jt) acc[a][jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int jt = 0; jt < 8; ++jt) acc[a][jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
-  for (int sp = 0; sp < PD; ++sp) issue(sp, sp);
-  for (int k = 0; k < iters; k += PD) {
+  for (int k = 0; k < kColsPD - 1; ++k) issue(k);
+  for (int k = 0; k < nch; ++k) {
+    // chunk k's copies (this wave's) have landed: the later ones in flight are
+    // those of chunks k+1 .. k+PD-2
+    wait_vm<(kColsPD - 2) * kColsCopies>();
+    __syncthreads();  // every wave's copies of chunk k have landed; every wave is done with chunk k-1
+    issue(k + kColsPD - 1);  // into the stage of chunk k-1
+    const uint16_t* st = reinterpret_cast<const uint16_t*>(lds + (k % kColsPD) * kColsStage);
+    bf16x8_t pa[2];
 #pragma unroll
-    for (int sp = 0; sp < PD; ++sp) {
-      wait_vm<(PD - 1) * (2 + NQ)>();  // this chunk's copies have landed
-      const uint16_t* st = stage0 + sp * STAGE;
-      bf16x8_t pa[2];
+    for (int a = 0; a < 2; ++a) pa[a] = tr_frag_swz(st, kColsM, 8 * g, 32 * wave + 16 * a);
 #pragma unroll
-      for (int a = 0; a < 2; ++a) pa[a] = tr_frag(st, 32, 8 * g, 16 * a);
+    for (int jt = 0; jt < 8; ++jt) {
+      const bf16x8_t qb = tr_frag_swz(st + kColsPBytes / 2, kColsJ, 8 * g, 16 * jt);
 #pragma unroll
-      for (int jt = 0; jt < J2T; ++jt) {
-        const bf16x8_t qb = tr_frag(st + 1024, J2, 8 * g, 16 * jt);
-#pragma unroll
-        for (int a = 0; a < 2; ++a) acc[a][jt] = mfma(pa[a], qb, acc[a][jt]);
-      }
-      wait_lds();  // the stage is read before it is refilled
-      issue(sp, k + sp + PD);
+      for (int a = 0; a < 2; ++a) acc[a][jt] = mfma(pa[a], qb, acc[a][jt]);
     }
   }
   wait_vm<0>();
-  __syncthreads();  // every wave is done with its stages; the space becomes the reduction tile
 
-  float* red = reinterpret_cast<float*>(lds);  // [4][32][J2]
+  // lane l holds C[m][j] for m = 32 wave + 16 a + 4 g + v, j = 16 jt + l % 16
+  const bool tr = LK->B.p[pi].transposed_out != 0;
+  const bool accum = L.nsplit == 1 && LK->B.p[pi].accumulate != 0;
+  float* out = L.nsplit > 1 ? L.part + (pi ? L.part_off[1] : L.part_off[0]) + (int64_t)split * D * R
+                            : LK->B.p[pi].Fout;
+  constexpr int Q16 = R / 16;  // j + r = 16 (jt + Q16) + l % 16 (+ 8 when 16 does not divide R)
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < 2; ++a) {
+    const int64_t mb = m0 + 32 * wave + 16 * a + 4 * g;  // m of v = 0
 #pragma unroll
-    for (int jt = 0; jt < J2T; ++jt)
+    for (int jt = 0; jt < (R + 15) / 16; ++jt) {
+      const int j = 16 * jt + i16;
+      float t[4];
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
-        red[(wave * 32 + 16 * a + 4 * g + v) * J2 + 16 * jt + (lane & 15)] = acc[a][jt][v];
-  __syncthreads();
-  const int r = p.r;
-  for (int e = threadIdx.x; e < 32 * r; e += 256) {
-    // dA (transposed output) walks m fastest so its stores are contiguous
-    const int mm = p.transposed_out ? e % 32 : e / r;
-    const int j = p.transposed_out ? e / 32 : e % r;
-    const int64_t m = m0 + mm;
-    if (m >= p.D) continue;
-    auto col = [&](int jj) {
-      return ((red[(0 * 32 + mm) * J2 + jj] + red[(1 * 32 + mm) * J2 + jj]) + red[(2 * 32 + mm) * J2 + jj]) +
-             red[(3 * 32 + mm) * J2 + jj];
-    };
-    const float t = col(j) + col(j + r);
-    float* dst = p.transposed_out ? p.Fout + (int64_t)j * p.D + m : p.Fout + m * r + j;
-    *dst = p.accumulate ? *dst + t : t;
+      for (int v = 0; v < 4; ++v) {
+        float pair;
+        if (R % 16 == 0) {
+          pair = acc[a][jt + Q16][v];
+        } else {
+          // column j + r sits in lane l ^ 8: of tile jt + Q16 for l % 16 < 8, of the next one otherwise
+          const float send = i16 >= 8 ? acc[a][jt + Q16][v] : acc[a][(jt + Q16 + 1) & 7][v];
+          pair = __shfl_xor(send, 8, 16);
+        }
+        t[v] = acc[a][jt][v] + pair;
+      }
+      if (j >= R || mb >= D) continue;
+      if (tr) {
+        // out[j][m .. m+3]: four consecutive m in one 16-byte store
+        float4* dst = reinterpret_cast<float4*>(out + (int64_t)j * D + mb);
+        float4 o = make_float4(t[0], t[1], t[2], t[3]);
+        if (accum) {
+          const float4 w = *dst;
+          o = make_float4(w.x + o.x, w.y + o.y, w.z + o.z, w.w + o.w);
+        }
+        *dst = o;
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          float* dst = out + (mb + v) * R + j;
+          *dst = accum ? *dst + t[v] : t[v];
+        }
+      }
+    }
   }
+}
+
+// out = sum over the token ranges, in order, of the partials (+ old out);
+// the partials are laid out as the output, so this is a plain stream of
+// four-element pieces (D * r is a multiple of 8)
+__global__ __launch_bounds__(256) void k_lora_cols_sum(ColsLaunch L) {
+  const ColsLaunchK LK = (ColsLaunchK)__builtin_amdgcn_kernarg_segment_ptr();
+  const int pi = (int)blockIdx.y;
+  if (pi >= L.B.n) return;
+  const int64_t n = LK->B.p[pi].D * L.B.p[0].r;
+  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e >= n) return;
+  const float* part = L.part + (pi ? L.part_off[1] : L.part_off[0]);
+  float4 t = *reinterpret_cast<const float4*>(part + e);
+  for (int s = 1; s < L.nsplit; ++s) {
+    const float4 v = *reinterpret_cast<const float4*>(part + (int64_t)s * n + e);
+    t.x += v.x; t.y += v.y; t.z += v.z; t.w += v.w;
+  }
+  float4* dst = reinterpret_cast<float4*>(LK->B.p[pi].Fout + e);
+  if (LK->B.p[pi].accumulate) {
+    const float4 o = *dst;
+    t.x = o.x + t.x; t.y = o.y + t.y; t.z = o.z + t.z; t.w = o.w + t.w;
+  }
+  *dst = t;
 }
 
 template <bool QS, int RT>
@@ -354,27 +471,76 @@ hipError_t launch_lora_rows(const RowsParams& p, hipStream_t stream, int kernel_
   return hipGetLastError();
 }
 
-hipError_t launch_lora_cols(const ColsBatch& B, hipStream_t stream, int kernel_id) {
-  int64_t slabs = 0;
+namespace {
+// token ranges per column slab: as many workgroups as fit on the 256 CUs in
+// one round (one workgroup fills a CU's LDS), each range at least eight chunks
+int cols_splits(int64_t T, int64_t slabs) {
+  const int64_t nch = (T + 31) / 32;
+  int64_t s = 256 / slabs;
+  const int64_t cap = nch / 8 > 1 ? nch / 8 : 1;
+  if (s > cap) s = cap;
+  if (s > 16) s = 16;
+  return (int)(s < 1 ? 1 : s);
+}
+int64_t cols_slabs(int64_t D) { return (D + kColsM - 1) / kColsM; }
+}  // namespace
+
+size_t lora_cols_part_bytes(int64_t T, const int64_t* D, int n, int r) {
+  int64_t slabs = 0, elems = 0;
+  for (int k = 0; k < n; ++k) slabs += cols_slabs(D[k]);
+  const int s = cols_splits(T, slabs);
+  if (s <= 1) return 0;
+  for (int k = 0; k < n; ++k) elems += (int64_t)s * D[k] * r;
+  return (size_t)elems * 4;
+}
+
+hipError_t launch_lora_cols(const ColsBatch& B, float* part, size_t part_bytes, hipStream_t stream, int kernel_id) {
+  if (B.n < 1 || B.n > 2) return hipErrorInvalidValue;
+  int64_t slabs = 0, D[2] = {0, 0};
   for (int k = 0; k < B.n; ++k) {
     const ColsParams& p = B.p[k];
-    if (p.r != B.p[0].r || !lora_stream_ok(p.r) || p.D % 32 != 0 || p.ldq < 2 * p.r) return hipErrorInvalidValue;
+    if (p.r != B.p[0].r || p.T != B.p[0].T || !lora_stream_ok(p.r) || p.D % 8 != 0 || p.ldq < 2 * p.r ||
+        p.ldp % 8 != 0 || p.ldq % 8 != 0)
+      return hipErrorInvalidValue;
     if (p.T * p.ldp * 2 > 0x7FFFFFF0LL || p.T * p.ldq * 2 > 0x7FFFFFF0LL) return hipErrorInvalidValue;
-    slabs = std::max<int64_t>(slabs, p.D / 32);
+    D[k] = p.D;
+    slabs += cols_slabs(p.D);
   }
-  const dim3 grid((unsigned)((slabs + 15) / 16 * 16), (unsigned)B.n);
-  KernelEvents ev(kernel_id);
-  const hipEvent_t e0 = ev.start(), e1 = ev.stop();
-  switch (B.p[0].r / 8) {
-    case 1: hipExtLaunchKernelGGL(k_lora_cols<1>, grid, dim3(256), 0, stream, e0, e1, 0, B); break;
-    case 2: hipExtLaunchKernelGGL(k_lora_cols<2>, grid, dim3(256), 0, stream, e0, e1, 0, B); break;
-    case 3: hipExtLaunchKernelGGL(k_lora_cols<3>, grid, dim3(256), 0, stream, e0, e1, 0, B); break;
-    case 4: hipExtLaunchKernelGGL(k_lora_cols<4>, grid, dim3(256), 0, stream, e0, e1, 0, B); break;
-    case 5: hipExtLaunchKernelGGL(k_lora_cols<5>, grid, dim3(256), 0, stream, e0, e1, 0, B); break;
-    case 6: hipExtLaunchKernelGGL(k_lora_cols<6>, grid, dim3(256), 0, stream, e0, e1, 0, B); break;
-    case 7: hipExtLaunchKernelGGL(k_lora_cols<7>, grid, dim3(256), 0, stream, e0, e1, 0, B); break;
-    default: hipExtLaunchKernelGGL(k_lora_cols<8>, grid, dim3(256), 0, stream, e0, e1, 0, B); break;
+  ColsLaunch L{};
+  L.B = B;
+  L.nsplit = cols_splits(B.p[0].T, slabs);
+  const int64_t nch = (B.p[0].T + 31) / 32;
+  L.chunks_per_split = (int32_t)((nch + L.nsplit - 1) / L.nsplit);
+  if (L.nsplit > 1) {
+    if (!part || part_bytes < lora_cols_part_bytes(B.p[0].T, D, B.n, B.p[0].r)) return hipErrorInvalidValue;
+    L.part = part;
+    L.part_off[0] = 0;
+    L.part_off[1] = (int64_t)L.nsplit * D[0] * B.p[0].r;
   }
+  L.first_wg[0] = 0;
+  for (int k = 0; k < B.n; ++k) L.first_wg[k + 1] = L.first_wg[k] + (int32_t)(cols_slabs(D[k]) * L.nsplit);
+  for (int k = B.n; k < 2; ++k) L.first_wg[k + 1] = L.first_wg[k];
+  {
+    KernelEvents ev(kernel_id);
+    const dim3 grid((unsigned)L.first_wg[B.n]), block(kColsWaves * 64);
+    const hipEvent_t e0 = ev.start(), e1 = ev.stop();
+    switch (B.p[0].r) {
+      case 8: hipExtLaunchKernelGGL(k_lora_cols<8>, grid, block, 0, stream, e0, e1, 0, L); break;
+      case 16: hipExtLaunchKernelGGL(k_lora_cols<16>, grid, block, 0, stream, e0, e1, 0, L); break;
+      case 24: hipExtLaunchKernelGGL(k_lora_cols<24>, grid, block, 0, stream, e0, e1, 0, L); break;
+      case 32: hipExtLaunchKernelGGL(k_lora_cols<32>, grid, block, 0, stream, e0, e1, 0, L); break;
+      case 40: hipExtLaunchKernelGGL(k_lora_cols<40>, grid, block, 0, stream, e0, e1, 0, L); break;
+      case 48: hipExtLaunchKernelGGL(k_lora_cols<48>, grid, block, 0, stream, e0, e1, 0, L); break;
+      case 56: hipExtLaunchKernelGGL(k_lora_cols<56>, grid, block, 0, stream, e0, e1, 0, L); break;
+      default: hipExtLaunchKernelGGL(k_lora_cols<64>, grid, block, 0, stream, e0, e1, 0, L); break;
+    }
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || L.nsplit <= 1) return e;
+  const int64_t dr = std::max(D[0], D[1]) * B.p[0].r;
+  KernelEvents ev(KID_REDUCE);
+  hipExtLaunchKernelGGL(k_lora_cols_sum, dim3((unsigned)((dr / 4 + 255) / 256), (unsigned)B.n), dim3(256), 0, stream,
+                        ev.start(), ev.stop(), 0, L);
   return hipGetLastError();
 }
 

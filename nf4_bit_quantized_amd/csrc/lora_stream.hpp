@@ -29,7 +29,7 @@ struct RowsParams {
 struct ColsParams {
   const uint16_t* P;  // bf16 [T][ldp], 16-byte aligned, ldp % 8 == 0
   int64_t ldp;
-  int64_t D;          // a multiple of 32
+  int64_t D;          // a multiple of 8
   const uint16_t* Q;  // bf16 [T][ldq] (hi columns 0..r-1, lo columns r..2r-1), 16-byte aligned
   int64_t ldq;
   int64_t T;
@@ -47,6 +47,9 @@ struct ColsBatch {
 bool lora_stream_ok(int r);
 bool lora_rows_ok(int64_t M, int r);
 hipError_t launch_lora_rows(const RowsParams& p, hipStream_t stream, int kernel_id);
-hipError_t launch_lora_cols(const ColsBatch& B, hipStream_t stream, int kernel_id);
+// dA and dB: part is workspace for the partial sums of the token ranges,
+// lora_cols_part_bytes(T, {D of each product}, n, r) bytes (0: none needed).
+size_t lora_cols_part_bytes(int64_t T, const int64_t* D, int n, int r);
+hipError_t launch_lora_cols(const ColsBatch& B, float* part, size_t part_bytes, hipStream_t stream, int kernel_id);
 
 }  // namespace qlora
