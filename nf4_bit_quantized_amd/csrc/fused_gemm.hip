@@ -330,11 +330,19 @@ __device__ __forceinline__ void restore_step(StepRegs<BN>& f, const Nf4Table& ta
   const uint32_t w0 = rot ? f.w[2] : f.w[0], w1 = rot ? f.w[3] : f.w[1];
   const uint32_t w2 = rot ? f.w[0] : f.w[2], w3 = rot ? f.w[1] : f.w[3];
   const uint32_t ww[4] = {w0, w1, w2, w3};
+  // dX: the restored columns stay in the order 0, 2, 4, 6, 1, 3, 5, 7 inside
+  // each group of eight (restore8_evenodd); the rank-r tail's rows are stored
+  // in the same order, and the epilogue puts the output columns back
 #pragma unroll
   for (int i = 0; i < BN / 32; i += 2) {
     uint32_t o[8];
-    restore8(BT ? ww[i] : f.w[i], t, o);
-    restore8(BT ? ww[i + 1] : f.w[i + 1], t, o + 4);
+    if (BT) {
+      restore8_evenodd(ww[i], t, o);
+      restore8_evenodd(ww[i + 1], t, o + 4);
+    } else {
+      restore8(f.w[i], t, o);
+      restore8(f.w[i + 1], t, o + 4);
+    }
     const int c0 = BT ? lcol + (((i + (rot ? 2 : 0)) & 3) * 8) : lcol + i * 8;
     const int c1 = BT ? lcol + (((i + 1 + (rot ? 2 : 0)) & 3) * 8) : lcol + i * 8 + 8;
     uint16_t* d0 = BT ? Bs + lrow * Geometry<BN, BT>::LDB_T + bt_col(lrow, c0) : Bs + lrow * LDK + c0;
@@ -374,8 +382,11 @@ __device__ __forceinline__ void tail_b_store(const uint16_t* __restrict__ Bt, in
       const int64_t kk = kt * BK + lrow;
       int64_t col = n0 + lc;
       col = col < cols ? col : 0;
+      // the eight columns in the restore's order 0, 2, 4, 6, 1, 3, 5, 7
+      const uint4 v = *reinterpret_cast<const uint4*>(Bt + (int64_t)((uint32_t)kk % (uint32_t)r) * ldbt + col);
       *reinterpret_cast<uint4*>(Bs + lrow * LDB_T + bt_col(lrow, lc)) =
-          *reinterpret_cast<const uint4*>(Bt + (int64_t)((uint32_t)kk % (uint32_t)r) * ldbt + col);
+          make_uint4(perm(v.y, v.x, 0x05040100u), perm(v.w, v.z, 0x05040100u), perm(v.y, v.x, 0x07060302u),
+                     perm(v.w, v.z, 0x07060302u));
     }
   }
 }
@@ -604,7 +615,10 @@ __device__ __forceinline__ void fused_body(const FusedParams& P) {
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int col = (wn * TN + j) * 32 + (lane & 31);
+        // dX: tile column c holds output column 8 (c / 8) + pi(c % 8), the
+        // restore's order 0, 2, 4, 6, 1, 3, 5, 7
+        const int c = (wn * TN + j) * 32 + (lane & 31);
+        const int col = BT ? (c & ~7) | ((c & 3) << 1) | ((c >> 2) & 1) : c;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int row = (wm * TM + i) * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);

@@ -80,4 +80,20 @@ __device__ __forceinline__ void restore8(uint32_t w, const RestoreTab& t, uint32
   out[3] = perm(o23, e23, 0x07060302u);
 }
 
+// restore8 without the final interleave: the words hold the bf16 pairs
+// (e0, e2), (e4, e6), (e1, e3), (e5, e7) -- elements in the order
+// 0, 2, 4, 6, 1, 3, 5, 7.  A product that takes its operand in this order on
+// both sides (or undoes it on its output) saves four v_perm per word.
+__device__ __forceinline__ void restore8_evenodd(uint32_t w, const RestoreTab& t, uint32_t* out) {
+  uint32_t HE, LE, HO, LO, sl, s2;
+  selectors_even(w, sl, s2);
+  lookup4(sl, s2, t, HE, LE);
+  selectors_odd(w, sl, s2);
+  lookup4(sl, s2, t, HO, LO);
+  out[0] = perm(HE, LE, 0x05010400u);
+  out[1] = perm(HE, LE, 0x07030602u);
+  out[2] = perm(HO, LO, 0x05010400u);
+  out[3] = perm(HO, LO, 0x07030602u);
+}
+
 }  // namespace qlora
