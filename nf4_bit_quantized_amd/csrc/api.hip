@@ -177,6 +177,11 @@ void skinny_q(SkinnyParams& S, const uint16_t* Q, int64_t ldq, int64_t qrows, in
 // U = X A^T (fp32 into U), and the hi/lo bf16 pair of s*U into Us.
 int lora_down(const uint16_t* X, const uint16_t* A, int64_t T, int64_t K, int32_t r, float s, float* part,
               float* U, uint16_t* Us, hipStream_t st) {
+  if (lora_down_small_ok(T, K, r)) {  // few tokens: one launch, no partial sums
+    const SmallDownParams P{X, A, T, K, r, s, U, Us, hilo_ld(r)};
+    HIP_TRY(launch_lora_down_small(P, st, KID_LORA_DOWN));
+    return QLORA_OK;
+  }
   if (lora_rows_ok(T, r)) {
     RowsParams R{};
     R.P = X; R.ldp = K; R.M = T; R.D = K;

@@ -433,6 +433,61 @@ __global__ __launch_bounds__(256) void k_lora_cols_sum(ColsLaunch L) {
   *dst = t;
 }
 
+// ---------------------------------------------------------------------------
+// U = X A^T for a few tokens (T <= 16), in one launch: workgroup j owns column
+// j of U for every token.  Its 256 threads walk the contraction in pieces of
+// eight (thread t: pieces t, t + 256, ...), each piece one 16-byte load of A's
+// row j and of every token's X row, with fp32 products; the threads' sums are
+// added in a fixed order (wave shuffles, then the four waves in LDS).  The
+// workgroup then writes U[t][j], the hi/lo pair of s*U[t][j] into Us (columns
+// j and r + j), and its share of Us's zero padding.
+// ---------------------------------------------------------------------------
+
+template <int TT>
+__global__ __launch_bounds__(256) void k_lora_down_small(SmallDownParams p) {
+  __shared__ float red[4][TT];
+  const int j = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int T = (int)p.T;
+  float acc[TT];
+#pragma unroll
+  for (int t = 0; t < TT; ++t) acc[t] = 0.0f;
+  const uint16_t* arow = p.A + (int64_t)j * p.K;
+  for (int64_t k = (int64_t)tid * 8; k < p.K; k += 256 * 8) {
+    const uint4 a = *reinterpret_cast<const uint4*>(arow + k);
+    const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+      if (t < T) {
+        const uint4 x = *reinterpret_cast<const uint4*>(p.X + (int64_t)t * p.K + k);
+        const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[t] = fmaf(bf16_bits_to_f32(aw[q] & 0xFFFFu), bf16_bits_to_f32(xw[q] & 0xFFFFu), acc[t]);
+          acc[t] = fmaf(bf16_bits_to_f32(aw[q] >> 16), bf16_bits_to_f32(xw[q] >> 16), acc[t]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < TT; ++t) {
+    float v = acc[t];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    if (lane == 0) red[wave][t] = v;
+  }
+  __syncthreads();
+  if (tid < T) {
+    const float u = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+    if (p.U) p.U[(int64_t)tid * p.r + j] = u;
+    uint16_t hi, lo;
+    split_bf16(p.s * u, hi, lo);
+    p.Us[(int64_t)tid * p.ldh + j] = hi;
+    p.Us[(int64_t)tid * p.ldh + p.r + j] = lo;
+    for (int64_t c = 2 * p.r + j; c < p.ldh; c += p.r) p.Us[(int64_t)tid * p.ldh + c] = 0;
+  }
+}
+
 template <bool QS, int RT>
 void rows_by_jt(const RowsParams& p, int jt, dim3 grid, hipStream_t st, const KernelEvents& ev) {
   const hipEvent_t e0 = ev.start(), e1 = ev.stop();
@@ -445,6 +500,19 @@ void rows_by_jt(const RowsParams& p, int jt, dim3 grid, hipStream_t st, const Ke
 }
 
 }  // namespace
+
+bool lora_down_small_ok(int64_t T, int64_t K, int r) { return T >= 1 && T <= 16 && r >= 1 && K % 8 == 0; }
+
+hipError_t launch_lora_down_small(const SmallDownParams& p, hipStream_t stream, int kernel_id) {
+  if (!lora_down_small_ok(p.T, p.K, p.r) || p.ldh < 2 * p.r) return hipErrorInvalidValue;
+  if (p.T * p.K * 2 > 0x7FFFFFF0LL || (int64_t)p.r * p.K * 2 > 0x7FFFFFF0LL) return hipErrorInvalidValue;
+  KernelEvents ev(kernel_id);
+  const hipEvent_t e0 = ev.start(), e1 = ev.stop();
+  const dim3 grid((unsigned)p.r);
+  if (p.T <= 4) hipExtLaunchKernelGGL(k_lora_down_small<4>, grid, dim3(256), 0, stream, e0, e1, 0, p);
+  else hipExtLaunchKernelGGL(k_lora_down_small<16>, grid, dim3(256), 0, stream, e0, e1, 0, p);
+  return hipGetLastError();
+}
 
 int lora_rows_rt(int r) { return r <= 32 ? 8 : 16; }
 

@@ -44,6 +44,23 @@ struct ColsBatch {
   int n;
 };
 
+// U = X A^T for at most 16 tokens, in one launch: U [T][r] fp32 (optional),
+// Us [T][ldh] the hi/lo pair of s*U, zero-padded.  X [T][K], A [r][K] bf16,
+// 16-byte aligned, K a multiple of 8.
+struct SmallDownParams {
+  const uint16_t* X;
+  const uint16_t* A;
+  int64_t T, K;
+  int32_t r;
+  float s;
+  float* U;
+  uint16_t* Us;
+  int64_t ldh;
+};
+
+bool lora_down_small_ok(int64_t T, int64_t K, int r);
+hipError_t launch_lora_down_small(const SmallDownParams& p, hipStream_t stream, int kernel_id);
+
 bool lora_stream_ok(int r);
 bool lora_rows_ok(int64_t M, int r);
 hipError_t launch_lora_rows(const RowsParams& p, hipStream_t stream, int kernel_id);
