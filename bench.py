@@ -373,8 +373,7 @@ def decode_section(steps, warmup):
                     p = reps[i % copies]
                     q.qlora_linear_fwd(p[0], p[1], p[2], X, A, B, lin.alpha, Y=Y, U_out=U, workspace=ws)
                 torch.cuda.synchronize()
-                q.qlora_trace_read(reset=True)
-                q.qlora_trace_select({"decode"})
+                # the call rate untraced, then the kernels' own times in a traced pass
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record()
                 for i in range(steps):
@@ -382,18 +381,26 @@ def decode_section(steps, warmup):
                     q.qlora_linear_fwd(p[0], p[1], p[2], X, A, B, lin.alpha, Y=Y, U_out=U, workspace=ws)
                 e1.record()
                 torch.cuda.synchronize()
+                call_ms = e0.elapsed_time(e1) / steps
+                q.qlora_trace_read(reset=True)
+                q.qlora_trace_select({"decode", "lora_down_gemm"})
+                for i in range(steps):
+                    p = reps[i % copies]
+                    q.qlora_linear_fwd(p[0], p[1], p[2], X, A, B, lin.alpha, Y=Y, U_out=U, workspace=ws)
+                torch.cuda.synchronize()
                 q.qlora_trace_enable(False)
                 kt = q.qlora_trace_read(reset=True)
-                call_ms = e0.elapsed_time(e1) / steps
                 packed_bytes = pk.numel() + cd.numel() + cs.numel() * 4
                 dec_n, dec_ms = kt.get("decode", (1, float("nan")))
                 dec_avg = dec_ms / max(dec_n, 1)
+                u_n, u_ms = kt.get("lora_down_gemm", (1, float("nan")))
                 out[lin.name + tag] = {
                     "T": T, "d_out": lin.d_out, "d_in": lin.d_in,
                     "scales": "8-bit codes + fp32 group constants" if dq else "fp32 per block (no second level)",
                     "packed_weight_bytes": packed_bytes,
                     "call_us": round(call_ms * 1e3, 2),
                     "packed_GBps_call": round(packed_bytes / (call_ms * 1e-3) / 1e9, 1),
+                    "u_kernel_us": round(u_ms / max(u_n, 1) * 1e3, 2),
                     "decode_kernel_us": round(dec_avg * 1e3, 2),
                     "packed_GBps_kernel": round(packed_bytes / (dec_avg * 1e-3) / 1e9, 1),
                     "frac_hbm_kernel": round(packed_bytes / (dec_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
@@ -404,10 +411,16 @@ def decode_section(steps, warmup):
     return out
 
 
+def mall_copies(nbytes):
+    """Copies of a call's operands to rotate so that together they hold more
+    than twice the 256 MB MALL (2 to 8)."""
+    return max(2, min(8, -(-(512 << 20) // max(nbytes, 1))))
+
+
 def export_section(lin, steps):
-    """HBM GB/s of the restored-weight export and of the merge, on the step's
-    weight (rotating 8 copies of the packed weight and of the output, 336 MB,
-    so the 256 MB MALL cannot hold them)."""
+    """HBM GB/s of the restored-weight export and of the merge on one weight,
+    rotating copies of the packed weight and of the output (more than twice
+    the 256 MB MALL together)."""
     import torch
     import nf4_bit_quantized_amd as q
     import workloads
@@ -417,7 +430,7 @@ def export_section(lin, steps):
     W = torch.from_numpy(inp["W"]).cuda()
     pk, cd, cs = q.qlora_quantize_nf4(W)
     del W
-    copies = 8
+    copies = mall_copies(N * K * 2 + pk.numel())
     reps = [(pk.clone(), cd.clone(), cs.clone()) for _ in range(copies)]
     outs = [torch.empty((N, K), dtype=torch.bfloat16, device="cuda") for _ in range(copies)]
     A, B = bf16_dev(inp["A"]), bf16_dev(inp["B"])
@@ -443,20 +456,22 @@ def export_section(lin, steps):
                      "kernel_us": round(avg * 1e3, 2), "GBps": round(nbytes / (avg * 1e-3) / 1e9, 1),
                      "frac_hbm": round(nbytes / (avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
         log("export", name, out[name])
+    del reps, outs
+    torch.cuda.empty_cache()
     return out
 
 
 def quantize16_section(lin, steps):
-    """Quantization of the attention-shaped weight handed over as bf16 and as
-    fp16 (2 bytes in per weight instead of 4), rotating 8 copies of the
-    weight (268 MB) so the 256 MB MALL cannot hold them."""
+    """Quantization of one weight handed over as bf16 and as fp16 (2 bytes in
+    per weight instead of 4), rotating copies of the weight (more than twice
+    the 256 MB MALL together)."""
     import torch
     import nf4_bit_quantized_amd as q
     import workloads
 
     N, K = lin.d_out, lin.d_in
     W = workloads.layer_inputs(N, K, 1, 1, lin.seed, with_dy=False)["W"]
-    copies = 8
+    copies = mall_copies(N * K * 2)
     out = {}
     for name, dt in (("bf16", torch.bfloat16), ("fp16", torch.float16)):
         w16 = torch.from_numpy(W).cuda().to(dt)
@@ -479,6 +494,7 @@ def quantize16_section(lin, steps):
                      "frac_hbm": round(nbytes / (avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
         log("quantize16", name, out[name])
         del reps, bufs
+        torch.cuda.empty_cache()
     return out
 
 
@@ -885,8 +901,11 @@ def main():
         result["attn_4096"] = attn_section(lin, sec_steps)
         result["mlp_llama7b"] = mlp_section(steps=10)
         result["decode_packed_weight"] = decode_section(steps=sec_steps, warmup=5)
+        gate = workloads.stack_65b(1)[4]  # 22016 x 8192: a size where the kernel's streaming rate shows
         result["export_bf16"] = export_section(lin, steps=sec_steps)
+        result["export_bf16_22016x8192"] = export_section(gate, steps=sec_steps)
         result["quantize_16bit_weight"] = quantize16_section(lin, steps=sec_steps)
+        result["quantize_16bit_weight_22016x8192"] = quantize16_section(gate, steps=sec_steps)
         result["adamw_65b_adapters"] = adamw_section(steps=sec_steps)
         result["lora_dropout_attn4096"] = dropout_section(lin, steps=sec_steps)
         result["qkv_gqa_70b"] = multi_proj_section(steps=sec_steps)

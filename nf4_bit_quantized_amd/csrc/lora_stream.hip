@@ -435,17 +435,22 @@ __global__ __launch_bounds__(256) void k_lora_cols_sum(ColsLaunch L) {
 
 // ---------------------------------------------------------------------------
 // U = X A^T for a few tokens (T <= 16), in one launch: workgroup j owns column
-// j of U for every token.  Its 256 threads walk the contraction in pieces of
-// eight (thread t: pieces t, t + 256, ...), each piece one 16-byte load of A's
-// row j and of every token's X row, with fp32 products; the threads' sums are
-// added in a fixed order (wave shuffles, then the four waves in LDS).  The
+// j of U for every token.  Its 1024 threads walk the contraction in pieces of
+// eight (thread t: pieces t, t + 1024, ...), each piece one 16-byte load of
+// A's row j and of every token's X row, with fp32 products; the threads' sums
+// are added in a fixed order (wave shuffles, then the 16 waves in LDS).  The
 // workgroup then writes U[t][j], the hi/lo pair of s*U[t][j] into Us (columns
-// j and r + j), and its share of Us's zero padding.
+// j and r + j), and its share of Us's zero padding.  Only r workgroups run, so
+// each keeps a whole piece per thread and token in flight: up to 17 loads of
+// 16 bytes per thread, 278 KB per workgroup at 16 tokens.
 // ---------------------------------------------------------------------------
 
+constexpr int kSmallDownThreads = 1024;
+
 template <int TT>
-__global__ __launch_bounds__(256) void k_lora_down_small(SmallDownParams p) {
-  __shared__ float red[4][TT];
+__global__ __launch_bounds__(kSmallDownThreads) void k_lora_down_small(SmallDownParams p) {
+  constexpr int NW = kSmallDownThreads / 64;
+  __shared__ float red[NW][TT];
   const int j = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T = (int)p.T;
@@ -453,19 +458,21 @@ __global__ __launch_bounds__(256) void k_lora_down_small(SmallDownParams p) {
 #pragma unroll
   for (int t = 0; t < TT; ++t) acc[t] = 0.0f;
   const uint16_t* arow = p.A + (int64_t)j * p.K;
-  for (int64_t k = (int64_t)tid * 8; k < p.K; k += 256 * 8) {
+  for (int64_t k = (int64_t)tid * 8; k < p.K; k += kSmallDownThreads * 8) {
+    // every load of the piece goes out before the first product: token rows
+    // t >= T read row T - 1 again, and their sums are never stored
     const uint4 a = *reinterpret_cast<const uint4*>(arow + k);
+    uint4 x[TT];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) x[t] = *reinterpret_cast<const uint4*>(p.X + (int64_t)(t < T ? t : T - 1) * p.K + k);
     const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
-      if (t < T) {
-        const uint4 x = *reinterpret_cast<const uint4*>(p.X + (int64_t)t * p.K + k);
-        const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+      const uint32_t xw[4] = {x[t].x, x[t].y, x[t].z, x[t].w};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[t] = fmaf(bf16_bits_to_f32(aw[q] & 0xFFFFu), bf16_bits_to_f32(xw[q] & 0xFFFFu), acc[t]);
-          acc[t] = fmaf(bf16_bits_to_f32(aw[q] >> 16), bf16_bits_to_f32(xw[q] >> 16), acc[t]);
-        }
+      for (int q = 0; q < 4; ++q) {
+        acc[t] = fmaf(bf16_bits_to_f32(aw[q] & 0xFFFFu), bf16_bits_to_f32(xw[q] & 0xFFFFu), acc[t]);
+        acc[t] = fmaf(bf16_bits_to_f32(aw[q] >> 16), bf16_bits_to_f32(xw[q] >> 16), acc[t]);
       }
     }
   }
@@ -478,7 +485,9 @@ __global__ __launch_bounds__(256) void k_lora_down_small(SmallDownParams p) {
   }
   __syncthreads();
   if (tid < T) {
-    const float u = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+    float u = red[0][tid];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) u += red[w][tid];
     if (p.U) p.U[(int64_t)tid * p.r + j] = u;
     uint16_t hi, lo;
     split_bf16(p.s * u, hi, lo);
@@ -509,8 +518,10 @@ hipError_t launch_lora_down_small(const SmallDownParams& p, hipStream_t stream, 
   KernelEvents ev(kernel_id);
   const hipEvent_t e0 = ev.start(), e1 = ev.stop();
   const dim3 grid((unsigned)p.r);
-  if (p.T <= 4) hipExtLaunchKernelGGL(k_lora_down_small<4>, grid, dim3(256), 0, stream, e0, e1, 0, p);
-  else hipExtLaunchKernelGGL(k_lora_down_small<16>, grid, dim3(256), 0, stream, e0, e1, 0, p);
+  const dim3 block(kSmallDownThreads);
+  if (p.T <= 4) hipExtLaunchKernelGGL(k_lora_down_small<4>, grid, block, 0, stream, e0, e1, 0, p);
+  else if (p.T <= 8) hipExtLaunchKernelGGL(k_lora_down_small<8>, grid, block, 0, stream, e0, e1, 0, p);
+  else hipExtLaunchKernelGGL(k_lora_down_small<16>, grid, block, 0, stream, e0, e1, 0, p);
   return hipGetLastError();
 }
 
