@@ -42,9 +42,9 @@ int block_shift(const qlora_nf4_desc* d) { return d->blocksize == 256 ? 2 : (d->
 
 // The few-token kernel takes this weight (8-bit codes are staged from a
 // 16-byte aligned run; fp32 block scales are read per chunk).
-bool decode_ok(const qlora_nf4_desc* d, const uint8_t* codes) {
+bool decode_ok(const qlora_nf4_desc* d, const uint8_t* codes, const float* consts) {
   const bool f32s = d->dq_blocksize == 0;
-  return decode_supported(d->d_out, d->d_in, block_shift(d), f32s) && (f32s || aligned16(codes));
+  return decode_supported(d->d_out, d->d_in, block_shift(d), f32s) && (f32s ? aligned16(consts) : aligned16(codes));
 }
 
 int check_desc(const qlora_nf4_desc* d) {
@@ -328,7 +328,7 @@ static int enqueue_fwd(const qlora_nf4_desc* d, const uint8_t* packed, const uin
   }
   // few tokens: the weight-streaming kernel (it stages 8-bit codes in LDS, so
   // those must be 16-byte aligned; fp32 block scales are loaded per chunk)
-  if (T <= kDecodeMaxT && decode_ok(d, codes)) {
+  if (T <= kDecodeMaxT && decode_ok(d, codes, consts)) {
     HIP_TRY(launch_decode(packed, codes, consts, X, T, N, K, w.Us, hilo_ld(r), B, r, Y, d->table, block_shift(d),
                           d->dq_blocksize == 0, s_));
     return QLORA_OK;
@@ -685,7 +685,7 @@ int qlora_linear_fwd_multi(int32_t n, const qlora_nf4_desc* d, const uint8_t* co
   hipStream_t s_ = (hipStream_t)stream;
   const int64_t K = d[0].d_in;
   bool fused = T <= kDecodeMaxT;
-  for (int i = 0; i < n && fused; ++i) fused = decode_ok(&d[i], codes[i]);
+  for (int i = 0; i < n && fused; ++i) fused = decode_ok(&d[i], codes[i], consts[i]);
   if (!fused && n > 1 && T > kDecodeMaxT) {
     // many tokens: each weight's U = X A^T, then one product over all the
     // weights (their output columns side by side), when every weight is

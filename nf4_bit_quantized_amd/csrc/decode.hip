@@ -42,10 +42,13 @@
 // MFMA over the 2r hi/lo columns of s U (zero-padded to a multiple of 64).
 //
 // Without the second level (fp32 block scales, "7、QLoRA 量化微调" §7.1) the
-// scales are 4 bytes per block, too many to stage per workgroup (57 KB at the
-// 8192 <-> 28672 shapes); each lane instead loads its row's two block scales
-// of a chunk together with that chunk's packed bytes, into registers.
+// workgroup's block scales (one contiguous run, 57 KB at the 8192 <-> 28672
+// shapes) are copied straight to LDS (buffer loads into LDS, no registers) in
+// place of the codes, each row at a stride of sst floats, an odd multiple of
+// four, so that 16 rows read at one column (8 bytes each) fall in distinct
+// banks; the loop reads a chunk's two scales with one LDS read.
 #include "decode.hpp"
+#include "dma.hpp"
 #include "trace.hpp"
 
 namespace qlora {
@@ -54,6 +57,7 @@ namespace {
 
 constexpr int LUT_DWORDS = 256 * 64;      // 64 KB
 constexpr int CODES_BYTES = 32 * 1024;    // the workgroup's scale codes and group ratios
+constexpr int SCALES_BYTES = 64 * 1024;   // or, without the second level, its fp32 block scales
 constexpr uint32_t kOob = 0x80000000u;    // buffer offset past every range used here: loads read zero
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -94,7 +98,6 @@ template <int NTW, int XQ>
 struct ChunkRegs {
   u32x4_t x[XQ];
   u32x4_t w[NTW];
-  float s[NTW][2];  // fp32 block scales of the chunk's two halves (fp32-scale format only)
 };
 
 // Four table lookups of the bytes of packed dword d -> 8 restored bf16 in element order.
@@ -139,7 +142,8 @@ __global__ __launch_bounds__(DW * 64) void k_decode(DecodeMulti M) {
   constexpr int PD = DW == 16 ? (NTW <= 2 ? 2 : 1) : (NTW <= 2 ? 3 : (NTW <= 5 ? 2 : 1));
   constexpr int XSW = XQ * 1024;          // a wave's X slot: 4 XQ token rows x 256 bytes
   constexpr int RED = 8 * NTW * 1024;     // eight waves' partial tiles, after the loop
-  constexpr int REGION = CODES_BYTES + DW * XSW > RED ? CODES_BYTES + DW * XSW : RED;
+  constexpr int AUXB = F32S ? SCALES_BYTES : CODES_BYTES;  // the staged scales
+  constexpr int REGION = AUXB + DW * XSW > RED ? AUXB + DW * XSW : RED;
   // the table must sit at LDS offset 0 (its addresses are formed without a base):
   // this is the kernel's only LDS variable
   __shared__ __attribute__((aligned(16))) uint32_t lds[LUT_DWORDS + REGION / 4];
@@ -156,7 +160,8 @@ __global__ __launch_bounds__(DW * 64) void k_decode(DecodeMulti M) {
   const int ntiles = (int)(P.N / 16);
   const int nt0 = ((int)blockIdx.x - M.first_wg[pi]) * NTW;
   const int nbk = K / 64;             // 64-weight halves of chunks per row
-  const int nbc = nbk >> P.bshift;    // scale codes per row
+  const int nbc = nbk >> P.bshift;    // scale codes (or fp32 scales) per row
+  const int sst = 4 * (((nbc + 3) >> 2) | 1);  // LDS row stride of the fp32 scales, in floats
   const int nch = (K + 127) / 128;
   const int nmine = nch > wave ? (nch - wave + DW - 1) / DW : 0;
   const int iters = (nmine + PD - 1) / PD * PD;
@@ -170,22 +175,43 @@ __global__ __launch_bounds__(DW * 64) void k_decode(DecodeMulti M) {
   // run of 16*NTW*nbc bytes in memory (rows past N read zero); in LDS each row
   // starts at a multiple of rs bytes, rs/4 odd, so that 16 consecutive rows
   // read at one column fall in distinct banks.  Then the ratios c_g / 255 of
-  // the groups of 256 blocks the run spans.
+  // the groups of 256 blocks the run spans.  Without the second level the run
+  // is the rows' fp32 scales, 64*NTW*nbc bytes, and there are no ratios.
   const uint32_t cfirst = (uint32_t)nt0 * 16u * (uint32_t)nbc;
-  const uint32_t cbytes = F32S ? 0u : 16u * NTW * (uint32_t)nbc;
+  const uint32_t cbytes = (F32S ? 64u : 16u) * NTW * (uint32_t)nbc;
   const uint32_t rs = 4u * (((uint32_t)(nbc + 3) >> 2) | 1u);
   const uint32_t g_lo = cfirst >> 8;
   const uint32_t ngr = F32S ? 0u : ((cfirst + cbytes - 1u) >> 8) - g_lo + 1u;
   float* ratio = reinterpret_cast<float*>(aux + ((16u * NTW * rs + 15u) & ~15u));
-  constexpr int CQ = CODES_BYTES / 16 / DT;
-  u32x4_t cv[CQ];
+  constexpr int CQ = F32S ? 0 : AUXB / 16 / DT;
+  u32x4_t cv[CQ > 0 ? CQ : 1];
 #pragma unroll
   for (int q = 0; q < CQ; ++q) {
     const uint32_t o = (uint32_t)(tid + q * DT) * 16u;
     cv[q] = __builtin_amdgcn_raw_buffer_load_b128(rc, o < cbytes ? cfirst + o : kOob, 0, 0);
   }
-  const float cg = __builtin_bit_cast(
-      float, __builtin_amdgcn_raw_buffer_load_b32(rk, (uint32_t)tid < ngr ? (g_lo + (uint32_t)tid) * 4u : kOob, 0, 0));
+  if (F32S) {
+    // the scales' LDS image in 16-byte slots: row j's slot p holds its scales
+    // 4p .. 4p+3 (slots past the row's scales read zero, or the next row's
+    // first scales, never used); copy c of the workgroup fills slots
+    // 64c .. 64c+63, wave w issuing copies w, w + DW, ...
+    const dma::v4i_t rd = dma::rsrc(P.consts, P.N * nbc * 4);
+    const uint32_t spr = (uint32_t)sst / 4u, nslots = 16u * NTW * spr, pieces = ((uint32_t)nbc + 3u) / 4u;
+#pragma unroll
+    for (int c = 0; c < 64 / DW; ++c) {
+      const uint32_t cc = (uint32_t)(wave + DW * c);
+      if (64u * cc < nslots) {
+        const uint32_t slot = 64u * cc + (uint32_t)lane, row = slot / spr, p = slot - row * spr;
+        const uint32_t src = (cfirst + row * (uint32_t)nbc + 4u * p) * 4u;
+        dma::copy16(rd, slot < nslots && p < pieces ? src : kOob, LDS_ADDR(aux) + 1024u * cc);
+      }
+    }
+  }
+  // (no load at all without the second level, so that exactly the chunk loads
+  // below follow the scale copies)
+  const float cg = F32S ? 0.f
+                        : __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                        rk, (uint32_t)tid < ngr ? (g_lo + (uint32_t)tid) * 4u : kOob, 0, 0));
 
   // this lane's row of tile i is n0 + 16 i
   const uint32_t n0 = (uint32_t)nt0 * 16u + (uint32_t)i16;
@@ -197,7 +223,7 @@ __global__ __launch_bounds__(DW * 64) void k_decode(DecodeMulti M) {
   // X slot: piece p of token row t at piece position p ^ t (conflict-free reads);
   // with one load per chunk only rows 0..3 exist, and lanes of rows >= 4 read
   // row i16 % 4 (MFMA rows are independent and token rows >= T are never stored)
-  uint8_t* xs = aux + CODES_BYTES + wave * XSW;
+  uint8_t* xs = aux + AUXB + wave * XSW;
   const int xrow = XQ == 1 ? (i16 & 3) : i16;
 
   auto issue_x = [&](ChunkRegs<NTW, XQ>& R, int k) {
@@ -215,16 +241,6 @@ __global__ __launch_bounds__(DW * 64) void k_decode(DecodeMulti M) {
     const bool in = ch < nch && ch * 64 + 16 * g < K / 2 && nt0 + i < ntiles;
     R.w[i] = __builtin_amdgcn_raw_buffer_load_b128(
         rw, in ? wbase + (uint32_t)i * wtile + (uint32_t)ch * 64u : kOob, 0, 0);
-    if (F32S) {
-      // this lane's row's scales of the chunk's two 64-weight halves (the same
-      // block for blocks of 128 or 256; zero for a half past the row's end)
-      const bool rin = ch < nch && nt0 + i < ntiles;
-      const uint32_t rb = (n0 + 16u * (uint32_t)i) * (uint32_t)nbc;
-      const uint32_t b0 = (uint32_t)(2 * ch) >> P.bshift, b1 = (uint32_t)(2 * ch + 1) >> P.bshift;
-      R.s[i][0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rk, rin ? (rb + b0) * 4u : kOob, 0, 0));
-      R.s[i][1] = __builtin_bit_cast(
-          float, __builtin_amdgcn_raw_buffer_load_b32(rk, rin && 2 * ch + 1 < nbk ? (rb + b1) * 4u : kOob, 0, 0));
-    }
   };
 
   // the first chunks' loads go out before the table is built
@@ -246,8 +262,8 @@ __global__ __launch_bounds__(DW * 64) void k_decode(DecodeMulti M) {
   for (int q = 0; q < CQ; ++q) {
     const uint32_t o = (uint32_t)(tid + q * DT) * 16u;
     if (o < cbytes) {
-      uint32_t row = o / (uint32_t)nbc, col = o - row * (uint32_t)nbc;
       const uint32_t w4[4] = {cv[q].x, cv[q].y, cv[q].z, cv[q].w};
+      uint32_t row = o / (uint32_t)nbc, col = o - row * (uint32_t)nbc;
       if ((nbc & 3) == 0) {  // dwords never straddle rows
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
@@ -269,7 +285,10 @@ __global__ __launch_bounds__(DW * 64) void k_decode(DecodeMulti M) {
   f32x4_t acc[NTW];
 #pragma unroll
   for (int i = 0; i < NTW; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  __syncthreads();  // the table, codes and ratios are in place
+  // this wave's scale copies have landed: only the first chunks' loads (XQ + NTW
+  // per chunk), issued after them, may still be in flight
+  if (F32S) dma::wait_vm<PD * (XQ + NTW)>();
+  __syncthreads();  // the table, codes and ratios (or scales) are in place
 
   for (int k = 0; k < iters; k += PD) {
 #pragma unroll
@@ -298,8 +317,14 @@ __global__ __launch_bounds__(DW * 64) void k_decode(DecodeMulti M) {
         const uint32_t row = (uint32_t)(16 * i + i16);
         float s0, s1;
         if (F32S) {
-          s0 = R[sp].s[i][0];
-          s1 = R[sp].s[i][1];
+          // the chunk's two halves' scales: blocks 2ch and 2ch + 1 (64 weights),
+          // or one block for both (blocks of 128 or 256); one aligned 8-byte read
+          const uint32_t b0 = (uint32_t)(2 * chc) >> P.bshift;
+          const float2 v = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(aux) +
+                                                            row * (uint32_t)sst + (b0 & ~1u));
+          const float lo = (b0 & 1u) ? v.y : v.x;
+          s0 = lo;
+          s1 = 2 * chc + 1 < nbk ? (P.bshift == 0 ? v.y : lo) : 0.f;
         } else if (CODES2) {  // 64-weight blocks, an even count per row
           const uint32_t cl = row * rs + (uint32_t)(2 * chc);                     // code byte in LDS
           const uint32_t gb = cfirst + row * (uint32_t)nbc + (uint32_t)(2 * chc);  // its block index
@@ -413,9 +438,9 @@ void launch_ntw(const DecodeMulti& P, bool c2, bool f32s, unsigned grid, hipStre
   const dim3 g(grid);
   KernelEvents ev(KID_DECODE);
   const hipEvent_t e0 = ev.start(), e1 = ev.stop();
-  if (f32s) {
+  if (f32s) {  // 16 waves' X slots for 16 tokens and the staged scales would overflow LDS
     if (P.p[0].T <= 4) {
-      if constexpr (NTW <= 6)
+      if constexpr (NTW <= 7)
         hipExtLaunchKernelGGL((k_decode<16, NTW, 1, false, true>), g, dim3(1024), 0, stream, e0, e1, 0, P);
       else hipExtLaunchKernelGGL((k_decode<8, NTW, 1, false, true>), g, dim3(512), 0, stream, e0, e1, 0, P);
     } else {
@@ -436,11 +461,17 @@ void launch_ntw(const DecodeMulti& P, bool c2, bool f32s, unsigned grid, hipStre
 
 }  // namespace
 
-// Rows hold whole blocks, and (with 8-bit scale codes) the workgroup's codes
-// must fit their LDS region with at least one 16-row tile.
+// LDS bytes of the fp32 scales of t 16-row tiles (rows at stride sst floats).
+static int64_t f32_scales_bytes(int64_t K, int bshift, int64_t t) {
+  const int64_t nbc = (K / 64) >> bshift;
+  return 64 * t * 4 * (((nbc + 3) / 4) | 1);
+}
+
+// Rows hold whole blocks, and the workgroup's codes (or fp32 scales) must fit
+// their LDS region with at least one 16-row tile.
 bool decode_supported(int64_t N, int64_t K, int bshift, bool f32s) {
   if (N % 16 != 0 || K % (64 << bshift) != 0 || N * K / 2 > 0x7FFFFFF0LL) return false;
-  if (f32s) return N * ((K / 64) >> bshift) * 4 <= 0x7FFFFFF0LL;
+  if (f32s) return N * ((K / 64) >> bshift) * 4 <= 0x7FFFFFF0LL && f32_scales_bytes(K, bshift, 1) <= SCALES_BYTES;
   const int64_t nbc = (K / 64) >> bshift;
   const int64_t rs = 4 * (((nbc + 3) / 4) | 1);
   return ((16 * rs + 15) & ~15LL) + 4 * (16 * nbc / 256 + 2) <= CODES_BYTES;
@@ -476,6 +507,8 @@ hipError_t launch_decode_multi(const DecodeWeight* w, int n, const uint16_t* X, 
   auto aux_need = [&](int64_t t) { return ((16 * t * rs + 15) & ~15LL) + 4 * (16 * t * nbc / 256 + 2); };
   while (!f32s && ntw > 1 && aux_need(ntw) > CODES_BYTES) --ntw;
   if (!f32s && aux_need(ntw) > CODES_BYTES) return hipErrorInvalidValue;
+  while (f32s && ntw > 1 && f32_scales_bytes(K, bshift, ntw) > SCALES_BYTES) --ntw;
+  if (f32s && f32_scales_bytes(K, bshift, ntw) > SCALES_BYTES) return hipErrorInvalidValue;
   int64_t wg = 0;
   for (int i = 0; i < n; ++i) {
     M.first_wg[i] = (int)wg;

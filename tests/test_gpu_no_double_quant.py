@@ -39,9 +39,13 @@ def test_quantize_bit_exact(bs, d_out, d_in):
 
 
 CASES = [
-    # (d_out, d_in, T, r, alpha, seed, bs): few tokens take the tiled kernel in this format
+    # (d_out, d_in, T, r, alpha, seed, bs): at most 16 tokens take the few-token
+    # kernel when rows hold whole blocks (the scales staged in LDS), else the tiles
     (256, 512, 4, 8, 16.0, 91, 64),
-    (192, 320, 1, 16, 16.0, 92, 128),
+    (192, 320, 1, 16, 16.0, 92, 128),   # rows of 2.5 blocks: the tiles
+    (192, 384, 1, 16, 16.0, 95, 128),   # 3 scales per row (odd), blocks of 128
+    (128, 192, 2, 8, 16.0, 96, 64),     # 3 scales per row: a half chunk at the row's end
+    (256, 1024, 16, 8, 16.0, 97, 256),  # 16 tokens, blocks of 256
     (256, 256, 100, 16, 32.0, 93, 64),
     (320, 448, 600, 24, 8.0, 94, 256),
 ]
@@ -57,7 +61,16 @@ def test_fwd_bwd_parity(d_out, d_in, T, r, alpha, seed, bs):
     o = oracle_layer(inp, r, alpha, Q=Q)
     packed, codes, consts = q.qlora_quantize_nf4(dev_f32(inp["W"]), blocksize=bs, double_quant=False)
     X, A, B, dY = (dev_bf16(inp[k]) for k in ("X", "A", "B", "dY"))
-    Y, U = q.qlora_linear_fwd(packed, codes, consts, X, A, B, alpha)
+    q.qlora_trace_select({"decode"})
+    q.qlora_trace_read(reset=True)
+    try:
+        Y, U = q.qlora_linear_fwd(packed, codes, consts, X, A, B, alpha)
+        torch.cuda.synchronize()
+        decode_launches = q.qlora_trace_read(reset=True).get("decode", (0, 0.0))[0]
+    finally:
+        q.qlora_trace_enable(False)
+    # the few-token kernel takes the call exactly when rows hold whole blocks
+    assert decode_launches == (1 if T <= 16 and d_in % bs == 0 else 0), decode_launches
     dX, dA, dB = q.qlora_linear_bwd(packed, codes, consts, X, A, B, alpha, dY, U_in=U)
     torch.cuda.synchronize()
     _check_quant(packed, codes, consts, Q)
