@@ -107,7 +107,8 @@ FwdWs plan_fwd(const qlora_nf4_desc* d, int64_t T, int32_t r, void* ws) {
   Carve c(ws);
   const int64_t N = d->d_out, K = d->d_in;
   if (r > 0 && T > 0) {
-    if (!lora_rows_ok(T, r)) w.part = static_cast<float*>(c.take(skinny_part_bytes(T, K, r)));
+    w.part = static_cast<float*>(
+        c.take(lora_rows_ok(T, r) ? lora_rows_part_bytes(T, K, r) : skinny_part_bytes(T, K, r)));
     w.U = static_cast<float*>(c.take((size_t)T * r * 4));
     w.Us = static_cast<uint16_t*>(c.take((size_t)T * hilo_ld(r) * 2));
   }
@@ -133,7 +134,9 @@ BwdWs plan_bwd(const qlora_nf4_desc* d, int64_t T, int32_t r, void* ws) {
     const int64_t ldh = hilo_ld(r);
     // split-contraction partials, only for the products the streaming kernels do not take
     size_t part = 0, part2 = 0;
+    // (U's and G's: the streaming kernel's contraction-range partials, or the skinny kernel's)
     if (!lora_rows_ok(T, r)) part = std::max(skinny_part_bytes(T, K, r), skinny_part_bytes(T, N, r));
+    else part = std::max(lora_rows_part_bytes(T, K, r), lora_rows_part_bytes(T, N, r));
     if (!lora_stream_ok(r)) {
       part = std::max(part, skinny_part_bytes(K, T, 2 * (int64_t)r));
       part2 = skinny_part_bytes(N, T, 2 * (int64_t)r);
@@ -187,7 +190,7 @@ int lora_down(const uint16_t* X, const uint16_t* A, int64_t T, int64_t K, int32_
     R.P = X; R.ldp = K; R.M = T; R.D = K;
     R.Q = A; R.ldq = K; R.q_strided = 0; R.r = r; R.s = s;
     R.Vout = U; R.Hout = Us; R.ldh = hilo_ld(r);
-    HIP_TRY(launch_lora_rows(R, st, KID_LORA_DOWN));
+    HIP_TRY(launch_lora_rows(R, part, lora_rows_part_bytes(T, K, r), st, KID_LORA_DOWN));
     return QLORA_OK;
   }
   SkinnyParams S = skinny(X, K, true, T, K, r, s, r, OUT_ROWS_HILO, part);
@@ -463,7 +466,7 @@ static int enqueue_bwd(const qlora_nf4_desc* d, const uint8_t* packed, const uin
       R.Q = B; R.ldq = r; R.q_strided = 1; R.r = r; R.s = s;
       R.Hout = w.Gs; R.ldh = ldh;
       if (U_in) { R.Uc = U_in; R.Ucs = w.Us; }
-      HIP_TRY(launch_lora_rows(R, s_, KID_LORA_G));
+      HIP_TRY(launch_lora_rows(R, w.part, w.part_bytes, s_, KID_LORA_G));
     } else {
       SkinnyParams S = skinny(dY, N, true, T, N, r, s, r, OUT_ROWS_HILO, w.part);
       skinny_q(S, B, r, r, Q_STRIDED);

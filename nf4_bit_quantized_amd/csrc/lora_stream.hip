@@ -92,18 +92,27 @@ __device__ __forceinline__ f32x4_t mfma(bf16x8_t a, bf16x8_t b, f32x4_t c) {
 }
 
 // ---------------------------------------------------------------------------
-// rows: C[m][j] = sum_c P[m][c] Qop[j][c], m in RT rows per workgroup, j < r
+// rows: C[m][j] = sum_c P[m][c] Qop[j][c], m < M, j < r
 //
-// Contraction chunks of 64 (D is a multiple of 64); wave w takes chunks w,
-// w+4, ...  Each chunk of P (RT rows x 128 B) and of Q is copied into LDS.
-// Contraction-contiguous tiles (P, and Q = A) keep whole 128-byte rows; the
-// sixteen-byte piece p of row R sits at slot p ^ (R & 7) ^ ((R >> 3) & 1), so
-// a fragment read (16 lanes: 16 rows, one piece) touches 16 distinct bank
-// groups.  Q = B ([D][r], contraction strided) is copied as its contiguous
-// [64][r] block and read with transposing LDS reads.
+// A workgroup owns 64 rows m for one range of the contraction; the ranges of a
+// row tile are split over workgroups so that the row tiles times the ranges
+// fill the CUs, and their fp32 partial sums are added in a fixed order by
+// k_lora_rows_sum (a single range: the kernel writes the result itself).  Its
+// four waves take the range's 64-wide contraction chunks in turn (wave w:
+// chunks w, w+4, ...), two in flight each, and add their tiles in LDS in a
+// fixed order at the end.  Each chunk's P tile (64 rows x 128 B, from HBM) and
+// Q tile (r rows of A x 128 B, or B's contiguous [64][r] block, from L2) are
+// copied into the wave's LDS stage: as many bytes of Q as of P, where a tile
+// of 16 rows had read four times more of Q than of P.  Contraction-contiguous
+// tiles keep whole 128-byte rows; the sixteen-byte piece p of row R sits at
+// slot p ^ (R & 7) ^ ((R >> 3) & 1), so a fragment read (16 lanes: 16 rows, one
+// piece) touches 16 distinct bank groups.  B's block is read with transposing
+// LDS reads.
 // ---------------------------------------------------------------------------
 
 constexpr int kRowsChunk = 64;
+constexpr int kRowsRT = 64;  // rows per workgroup
+constexpr int kRowsPD = 2;   // chunks in flight per wave
 
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
@@ -121,21 +130,61 @@ __device__ __forceinline__ void copy_rows(v4i_t rs, uint32_t base, int64_t ld, i
   }
 }
 
-template <int JT, bool QS, int RT>
-__global__ __launch_bounds__(256) void k_lora_rows(RowsParams p) {
+struct RowsLaunch {
+  RowsParams p;
+  float* part;               // nsplit > 1: [nsplit][M][r] fp32 partial sums
+  int32_t nsplit;            // contraction ranges per row tile
+  int32_t chunks_per_split;  // 64-wide chunks per range
+};
+
+// The final values of row m, column c < ldh of the hi/lo output (and of U
+// and the hi/lo pair of the given U), from the row's sum v(j) over j < r.
+template <typename SumJ>
+__device__ __forceinline__ void rows_out(const RowsParams& p, int64_t m, int c, SumJ v_of) {
+  const int r = p.r;
+  const int64_t ldh = p.ldh;
+  uint16_t h = 0;
+  if (c < 2 * r) {
+    const int j = c < r ? c : c - r;
+    const float v = v_of(j);
+    if (p.Vout && c < r) p.Vout[m * r + j] = v;
+    uint16_t hi, lo;
+    split_bf16(p.s * v, hi, lo);
+    h = c < r ? hi : lo;
+  }
+  p.Hout[m * ldh + c] = h;
+  if (p.Ucs) {
+    uint16_t u = 0;
+    if (c < 2 * r) {
+      uint16_t hi, lo;
+      split_bf16(p.s * p.Uc[m * r + (c < r ? c : c - r)], hi, lo);
+      u = c < r ? hi : lo;
+    }
+    p.Ucs[m * ldh + c] = u;
+  }
+}
+
+template <int JT, bool QS>
+__global__ __launch_bounds__(256) void k_lora_rows(RowsLaunch L) {
+  constexpr int RT = kRowsRT, PD = kRowsPD;
   constexpr int QROWS = 16 * JT;                            // Q tile rows (A) or 64 rows x r (B)
   constexpr int STAGE = RT * 64 + QROWS * 64 + 64;          // bf16 elements (+ slack for transposed reads)
-  constexpr int PD0 = (120 * 1024) / (4 * STAGE * 2);
-  constexpr int PD = PD0 > 8 ? 8 : PD0;                     // chunks in flight per wave
+  constexpr int LDR = 16 * JT + 4;                          // row of a wave's tile in the sum, in floats
   __shared__ __attribute__((aligned(16))) uint16_t lds[4 * PD * STAGE];
-  __shared__ float red[4][16][16 * JT];
+  static_assert(4 * RT * LDR * 4 <= 4 * PD * STAGE * 2, "the waves' tiles fit over the stages");
+  float* red = reinterpret_cast<float*>(lds);               // [wave][RT][LDR], after the loop
+  const RowsParams& p = L.p;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int i = lane & 15, g = lane >> 4;
-  const int64_t m0 = (int64_t)blockIdx.x * RT;
+  const int tile = (int)blockIdx.x / L.nsplit, split = (int)blockIdx.x - tile * L.nsplit;
+  const int64_t m0 = (int64_t)tile * RT;
   const int64_t nch = p.D / kRowsChunk;
-  const int nmine = nch > wave ? (int)((nch - wave + 3) / 4) : 0;
+  const int64_t cbeg = (int64_t)split * L.chunks_per_split;
+  const int64_t cend = cbeg + L.chunks_per_split < nch ? cbeg + L.chunks_per_split : nch;
+  const int64_t mine = cend - cbeg;
+  const int nmine = mine > wave ? (int)((mine - wave + 3) / 4) : 0;
   const int iters = (nmine + PD - 1) / PD * PD;
   const int r = p.r;
   // copies per chunk: RT/8 for P, 2JT for Q (copies past r read zeros)
@@ -149,8 +198,8 @@ __global__ __launch_bounds__(256) void k_lora_rows(RowsParams p) {
   const uint32_t lstage0 = LDS_ADDR(lds) + (uint32_t)(wave * PD * STAGE * 2);
 
   auto issue = [&](int sp, int k) {
-    const int64_t ch = wave + 4 * (int64_t)k;
-    const bool in = ch < nch;
+    const int64_t ch = cbeg + wave + 4 * (int64_t)k;
+    const bool in = ch < cend;
     const int64_t c0 = ch * kRowsChunk;
     const uint32_t st = lstage0 + (uint32_t)(sp * STAGE * 2);
     copy_rows<RT>(rp, in ? pbase + (uint32_t)(c0 * 2) : kOob, p.ldp, prows, st);
@@ -165,11 +214,11 @@ __global__ __launch_bounds__(256) void k_lora_rows(RowsParams p) {
     }
   };
 
-  // fragment read offsets: row i (P) / Q row j = 16jt + i, pieces 4ks + g
-  const int prow_l = i & (RT - 1);
-  f32x4_t acc[JT];
+  f32x4_t acc[RT / 16][JT];
 #pragma unroll
-  for (int jt = 0; jt < JT; ++jt) acc[jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int rt = 0; rt < RT / 16; ++rt)
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt) acc[rt][jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
   for (int sp = 0; sp < PD; ++sp) issue(sp, sp);
@@ -181,8 +230,12 @@ __global__ __launch_bounds__(256) void k_lora_rows(RowsParams p) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const int piece = 4 * ks + g;
-        const bf16x8_t a =
-            *reinterpret_cast<const bf16x8_t*>(st + prow_l * 64 + ((piece ^ swz(prow_l)) * 8));
+        bf16x8_t a[RT / 16];
+#pragma unroll
+        for (int rt = 0; rt < RT / 16; ++rt) {
+          const int prow = 16 * rt + i;
+          a[rt] = *reinterpret_cast<const bf16x8_t*>(st + prow * 64 + ((piece ^ swz(prow)) * 8));
+        }
 #pragma unroll
         for (int jt = 0; jt < JT; ++jt) {
           bf16x8_t b;
@@ -192,7 +245,8 @@ __global__ __launch_bounds__(256) void k_lora_rows(RowsParams p) {
             const int j = 16 * jt + i < r ? 16 * jt + i : r - 1;
             b = *reinterpret_cast<const bf16x8_t*>(st + RT * 64 + j * 64 + ((piece ^ swz(j)) * 8));
           }
-          acc[jt] = mfma(a, b, acc[jt]);
+#pragma unroll
+          for (int rt = 0; rt < RT / 16; ++rt) acc[rt][jt] = mfma(a[rt], b, acc[rt][jt]);
         }
       }
       wait_lds();  // the stage is read before it is refilled
@@ -200,38 +254,77 @@ __global__ __launch_bounds__(256) void k_lora_rows(RowsParams p) {
     }
   }
   wait_vm<0>();
+  __syncthreads();  // every wave is done with the stages the tiles go over
 
-  // fixed-order sum of the four waves' tiles
+  // fixed-order sum of the four waves' tiles: lane l, value v holds row
+  // 16 rt + 4(l/16) + v, column 16 jt + l % 16
 #pragma unroll
-  for (int jt = 0; jt < JT; ++jt)
+  for (int rt = 0; rt < RT / 16; ++rt)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) red[wave][4 * g + v][16 * jt + i] = acc[jt][v];
+    for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[(wave * RT + 16 * rt + 4 * g + v) * LDR + 16 * jt + i] = acc[rt][jt][v];
   __syncthreads();
-  const int ldh = (int)p.ldh;
-  for (int e = threadIdx.x; e < RT * ldh; e += 256) {
-    const int rr = e / ldh, c = e % ldh;
-    const int64_t m = m0 + rr;
-    if (m >= p.M) continue;
-    uint16_t h = 0;
-    if (c < 2 * r) {
-      const int j = c < r ? c : c - r;
-      const float v = ((red[0][rr][j] + red[1][rr][j]) + red[2][rr][j]) + red[3][rr][j];
-      if (p.Vout && c < r) p.Vout[m * r + j] = v;
-      uint16_t hi, lo;
-      split_bf16(p.s * v, hi, lo);
-      h = c < r ? hi : lo;
+  auto sum = [&](int rr, int j) {
+    return ((red[(0 * RT + rr) * LDR + j] + red[(1 * RT + rr) * LDR + j]) + red[(2 * RT + rr) * LDR + j]) +
+           red[(3 * RT + rr) * LDR + j];
+  };
+  if (L.nsplit == 1) {
+    const int ldh = (int)p.ldh;
+    for (int e = threadIdx.x; e < RT * ldh; e += 256) {
+      const int rr = e / ldh, c = e % ldh;
+      const int64_t m = m0 + rr;
+      if (m < p.M) rows_out(p, m, c, [&](int j) { return sum(rr, j); });
     }
-    p.Hout[m * ldh + c] = h;
-    if (p.Ucs) {
-      uint16_t u = 0;
-      if (c < 2 * r) {
-        uint16_t hi, lo;
-        split_bf16(p.s * p.Uc[m * r + (c < r ? c : c - r)], hi, lo);
-        u = c < r ? hi : lo;
-      }
-      p.Ucs[m * ldh + c] = u;
+  } else {
+    float* part = L.part + (int64_t)split * p.M * r;
+    for (int e = threadIdx.x; e < RT * r; e += 256) {
+      const int rr = e / r, j = e % r;
+      const int64_t m = m0 + rr;
+      if (m < p.M) part[m * r + j] = sum(rr, j);
     }
   }
+}
+
+// The ranges' partial sums, added in range order, then the same outputs as a
+// single range writes; thread e takes row e / (r/4 + z), four consecutive
+// columns j (16-byte loads of the partials and of U), or one of the z threads
+// that clear four padding columns of the hi/lo rows past 2r.
+__global__ __launch_bounds__(256) void k_lora_rows_sum(RowsLaunch L) {
+  const RowsParams& p = L.p;
+  const int r = p.r;
+  const int64_t ldh = p.ldh;
+  const int q4 = r / 4, z = (int)((ldh - 2 * r) / 4), per = q4 + z;
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= p.M * per) return;
+  const int64_t m = e / per;
+  const int t = (int)(e - m * per);
+  if (t >= q4) {  // padding columns 2r + 4(t - q4) .. +3
+    const int64_t c = 2 * r + 4 * (t - q4);
+    *reinterpret_cast<uint2*>(p.Hout + m * ldh + c) = make_uint2(0u, 0u);
+    if (p.Ucs) *reinterpret_cast<uint2*>(p.Ucs + m * ldh + c) = make_uint2(0u, 0u);
+    return;
+  }
+  const int j = 4 * t;
+  float4 v = *reinterpret_cast<const float4*>(L.part + m * r + j);
+  for (int q = 1; q < L.nsplit; ++q) {
+    const float4 w = *reinterpret_cast<const float4*>(L.part + ((int64_t)q * p.M + m) * r + j);
+    v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+  }
+  if (p.Vout) *reinterpret_cast<float4*>(p.Vout + m * r + j) = v;
+  auto pair = [&](float4 a, uint16_t* dst) {
+    uint16_t h[4], l[4];
+    split_bf16(p.s * a.x, h[0], l[0]);
+    split_bf16(p.s * a.y, h[1], l[1]);
+    split_bf16(p.s * a.z, h[2], l[2]);
+    split_bf16(p.s * a.w, h[3], l[3]);
+    *reinterpret_cast<uint2*>(dst + m * ldh + j) =
+        make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
+    *reinterpret_cast<uint2*>(dst + m * ldh + r + j) =
+        make_uint2(l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16));
+  };
+  pair(v, p.Hout);
+  if (p.Ucs) pair(*reinterpret_cast<const float4*>(p.Uc + m * r + j), p.Ucs);
 }
 
 // ---------------------------------------------------------------------------
@@ -497,15 +590,25 @@ __global__ __launch_bounds__(kSmallDownThreads) void k_lora_down_small(SmallDown
   }
 }
 
-template <bool QS, int RT>
-void rows_by_jt(const RowsParams& p, int jt, dim3 grid, hipStream_t st, const KernelEvents& ev) {
+template <bool QS>
+void rows_by_jt(const RowsLaunch& L, int jt, dim3 grid, hipStream_t st, const KernelEvents& ev) {
   const hipEvent_t e0 = ev.start(), e1 = ev.stop();
   switch (jt) {
-    case 1: hipExtLaunchKernelGGL((k_lora_rows<1, QS, RT>), grid, dim3(256), 0, st, e0, e1, 0, p); break;
-    case 2: hipExtLaunchKernelGGL((k_lora_rows<2, QS, RT>), grid, dim3(256), 0, st, e0, e1, 0, p); break;
-    case 3: hipExtLaunchKernelGGL((k_lora_rows<3, QS, RT>), grid, dim3(256), 0, st, e0, e1, 0, p); break;
-    default: hipExtLaunchKernelGGL((k_lora_rows<4, QS, RT>), grid, dim3(256), 0, st, e0, e1, 0, p); break;
+    case 1: hipExtLaunchKernelGGL((k_lora_rows<1, QS>), grid, dim3(256), 0, st, e0, e1, 0, L); break;
+    case 2: hipExtLaunchKernelGGL((k_lora_rows<2, QS>), grid, dim3(256), 0, st, e0, e1, 0, L); break;
+    case 3: hipExtLaunchKernelGGL((k_lora_rows<3, QS>), grid, dim3(256), 0, st, e0, e1, 0, L); break;
+    default: hipExtLaunchKernelGGL((k_lora_rows<4, QS>), grid, dim3(256), 0, st, e0, e1, 0, L); break;
   }
+}
+
+// contraction ranges per row tile: as many workgroups as fill the 256 CUs
+// once, each range at least 32 chunks (eight per wave)
+int rows_splits(int64_t M, int64_t D) {
+  const int64_t tiles = (M + kRowsRT - 1) / kRowsRT;
+  int64_t s = 256 / tiles;
+  const int64_t cap = D / kRowsChunk / 32;
+  if (s > cap) s = cap;
+  return (int)(s < 1 ? 1 : s);
 }
 
 }  // namespace
@@ -531,21 +634,33 @@ bool lora_stream_ok(int r) { return r > 0 && r <= 64 && r % 8 == 0; }
 
 bool lora_rows_ok(int64_t M, int r) { return lora_stream_ok(r) && M / lora_rows_rt(r) >= 64; }
 
-hipError_t launch_lora_rows(const RowsParams& p, hipStream_t stream, int kernel_id) {
+size_t lora_rows_part_bytes(int64_t M, int64_t D, int r) {
+  const int s = rows_splits(M, D);
+  return s > 1 ? (size_t)s * M * r * 4 : 0;
+}
+
+hipError_t launch_lora_rows(const RowsParams& p, float* part, size_t part_bytes, hipStream_t stream, int kernel_id) {
   if (!lora_rows_ok(p.M, p.r) || p.D % 64 != 0 || p.ldh < 2 * p.r || (p.q_strided && p.ldq != p.r))
     return hipErrorInvalidValue;
   if (p.M * p.ldp * 2 > 0x7FFFFFF0LL || (p.q_strided ? p.D * p.r * 2 : p.r * p.ldq * 2) > 0x7FFFFFF0LL)
     return hipErrorInvalidValue;
-  const int rt = lora_rows_rt(p.r);
+  RowsLaunch L;
+  L.p = p;
+  L.nsplit = rows_splits(p.M, p.D);
+  if (L.nsplit > 1 && (part == nullptr || part_bytes < lora_rows_part_bytes(p.M, p.D, p.r))) return hipErrorInvalidValue;
+  L.part = part;
+  const int64_t nch = p.D / kRowsChunk;
+  L.chunks_per_split = (int32_t)((nch + L.nsplit - 1) / L.nsplit);
   const int jt = (p.r + 15) / 16;
-  const dim3 grid((unsigned)((p.M + rt - 1) / rt));
+  const dim3 grid((unsigned)(((p.M + kRowsRT - 1) / kRowsRT) * L.nsplit));
   KernelEvents ev(kernel_id);
-  if (p.q_strided) {
-    if (rt == 8) rows_by_jt<true, 8>(p, jt, grid, stream, ev);
-    else rows_by_jt<true, 16>(p, jt, grid, stream, ev);
-  } else {
-    if (rt == 8) rows_by_jt<false, 8>(p, jt, grid, stream, ev);
-    else rows_by_jt<false, 16>(p, jt, grid, stream, ev);
+  if (p.q_strided) rows_by_jt<true>(L, jt, grid, stream, ev);
+  else rows_by_jt<false>(L, jt, grid, stream, ev);
+  if (L.nsplit > 1) {
+    KernelEvents es(KID_REDUCE);
+    const int64_t per = p.r / 4 + (p.ldh - 2 * p.r) / 4;
+    const dim3 sg((unsigned)((p.M * per + 255) / 256));
+    hipExtLaunchKernelGGL(k_lora_rows_sum, sg, dim3(256), 0, stream, es.start(), es.stop(), 0, L);
   }
   return hipGetLastError();
 }

@@ -63,7 +63,10 @@ hipError_t launch_lora_down_small(const SmallDownParams& p, hipStream_t stream, 
 
 bool lora_stream_ok(int r);
 bool lora_rows_ok(int64_t M, int r);
-hipError_t launch_lora_rows(const RowsParams& p, hipStream_t stream, int kernel_id);
+// part is workspace for the partial sums of the contraction ranges,
+// lora_rows_part_bytes(M, D, r) bytes (0: none needed).
+size_t lora_rows_part_bytes(int64_t M, int64_t D, int r);
+hipError_t launch_lora_rows(const RowsParams& p, float* part, size_t part_bytes, hipStream_t stream, int kernel_id);
 // dA and dB: part is workspace for the partial sums of the token ranges,
 // lora_cols_part_bytes(T, {D of each product}, n, r) bytes (0: none needed).
 size_t lora_cols_part_bytes(int64_t T, const int64_t* D, int n, int r);
