@@ -60,10 +60,11 @@
  * - W, packed, X, dY, A, B, Y, dX, U_out, U_in, dA and dB must be 16-byte
  *   aligned (QLORA_ERR_UNSUPPORTED otherwise); codes and consts need only
  *   their element alignment.  A forward
- *   call with at most 16 tokens takes the weight-streaming kernel when codes
- *   is 16-byte aligned, K is a multiple of the block size and K/bs is at
- *   most about 2000, else the tiled kernel (same results within the accuracy
- *   stated below).
+ *   call with at most 16 tokens takes the weight-streaming kernel when K is
+ *   a multiple of the block size and either codes is 16-byte aligned and
+ *   K/bs is at most about 2000 (8-bit codes), or consts is 16-byte aligned
+ *   and K/bs is at most about 1000 (fp32 block scales, dq_blocksize 0); else
+ *   the tiled kernel (same results within the accuracy stated below).
  * - Inputs must be finite; results for NaN/Inf inputs are unspecified.
  * - Hot-path preconditions: blocksize 64 (also 128 or 256), dq_blocksize 256 (also 0),
  *   d_in % 64 == 0, d_out % 64 == 0, 0 <= r <= 128, T >= 0 (T == 0 is a
