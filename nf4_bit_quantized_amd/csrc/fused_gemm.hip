@@ -520,8 +520,7 @@ __device__ __forceinline__ void fused_body(const FusedParams& P) {
       return __builtin_amdgcn_readfirstlane(kMaxFusedSegs + (int)((c - nk) / ntail1));
     };
     int cp_key = 0;
-    auto source = [&](uint32_t c) {
-      const int key = key_of(c);
+    auto source_key = [&](int key) {
       if (key != cp_key) {
         cp_key = key;
         const int si = key % kMaxFusedSegs;
@@ -537,6 +536,26 @@ __device__ __forceinline__ void fused_body(const FusedParams& P) {
           cp = make_acopy(K->seg[si].At, K->seg[si].ldat, P.M, m0, cw, lane);
         }
       }
+    };
+    auto source = [&](uint32_t c) { source_key(key_of(c)); };
+    // the source and column of step c < nsteps in one pass, with scalar
+    // selects only (several weights; run every step, so no division)
+    auto key_col = [&](uint32_t c, int& key, uint32_t& col) {
+      const bool tail = c >= nk;
+      uint32_t x = tail ? c - nk : rotated(c, rot, nk);
+      // (formed in vector registers: the scalar file is full in this loop)
+      asm volatile("" : "+v"(x));
+      int si = 0;
+      uint32_t base = 0;
+#pragma unroll
+      for (int i = 1; i < kMaxFusedSegs; ++i) {
+        const uint32_t start = tail ? (uint32_t)i * ntail1 : k0[i];
+        const bool in = i < nseg && x >= start;
+        si = in ? i : si;
+        base = in ? start : base;
+      }
+      key = __builtin_amdgcn_readfirstlane((tail ? kMaxFusedSegs : 0) + si);
+      col = (uint32_t)__builtin_amdgcn_readfirstlane((int)((x - base) * (BK * 2)));
     };
     auto col_of = [&](uint32_t c) {
       const uint32_t col = c < nk ? (rotated(c, rot, nk) - (nseg > 1 ? k0_of(k0, key_of(c)) : 0u)) * (BK * 2)
@@ -577,12 +596,17 @@ __device__ __forceinline__ void fused_body(const FusedParams& P) {
     load_frags<BN, BT>(cur, a_stage(0), b_stage(0), arow, apos[0], 0);
     for (uint32_t s = 0; s < nsteps; ++s) {
       const uint32_t c = s + 2;
-      if (nseg > 1) {
-        if (c < nsteps) source(c);
-      } else if (c == nk && c < nsteps) {
-        cp = make_acopy(P.At, P.ldat, P.M, m0, cw, lane);
+      uint32_t col = last_col;
+      if (MULTI) {
+        if (c < nsteps) {
+          int key;
+          key_col(c, key, col);
+          source_key(key);
+        }
+      } else {
+        if (c == nk && c < nsteps) cp = make_acopy(P.At, P.ldat, P.M, m0, cw, lane);
+        if (c < nsteps) col = col_of(c);
       }
-      const uint32_t col = c < nsteps ? col_of(c) : last_col;
       uint8_t* dst = a_stage(c);
       const uint8_t* As = a_stage(s);
       const uint16_t* Bs = b_stage(s);
