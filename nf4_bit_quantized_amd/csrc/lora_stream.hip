@@ -6,12 +6,12 @@
 // branch is B (A x) scaled by alpha / r; only A and B receive gradients.)
 //
 // Each product reads one large bf16 matrix (X or dY, T x d) exactly once and is
-// bound by HBM.  Unlike the split-contraction kernel in skinny.hip, every
-// workgroup here owns whole outputs: its four waves split the contraction and
-// add their tiles in LDS in a fixed order, so there are no partial sums in
-// memory and no second launch, and results are deterministic.  What keeps HBM
-// busy is the number of bytes in flight per CU: each wave keeps several
-// contraction chunks loading (registers or LDS copies) while it multiplies an
+// bound by HBM.  A workgroup owns a block of outputs for one range of the
+// contraction (rows) or of the tokens (cols); where a block's range is split
+// over several workgroups so that they fill the CUs, the fp32 partial sums go
+// to workspace and a second launch adds them in a fixed order, so results are
+// deterministic.  What keeps HBM busy is the number of bytes in flight per CU:
+// each wave keeps several chunks loading (LDS copies) while it multiplies an
 // earlier one.  Rows or contraction positions past the end are read through
 // buffer resources with an offset beyond the range, which returns zeros (also
 // for copies into LDS).
@@ -628,11 +628,10 @@ hipError_t launch_lora_down_small(const SmallDownParams& p, hipStream_t stream, 
   return hipGetLastError();
 }
 
-int lora_rows_rt(int r) { return r <= 32 ? 8 : 16; }
-
 bool lora_stream_ok(int r) { return r > 0 && r <= 64 && r % 8 == 0; }
 
-bool lora_rows_ok(int64_t M, int r) { return lora_stream_ok(r) && M / lora_rows_rt(r) >= 64; }
+// many tokens: at least 512 (r <= 32) or 1024 rows; fewer take the skinny kernel
+bool lora_rows_ok(int64_t M, int r) { return lora_stream_ok(r) && M >= (r <= 32 ? 512 : 1024); }
 
 size_t lora_rows_part_bytes(int64_t M, int64_t D, int r) {
   const int s = rows_splits(M, D);
