@@ -145,6 +145,10 @@ CASES = [
     (192, 320, 523, 8, 16.0, 11),
     (256, 192, 600, 24, 8.0, 12),
     (320, 448, 1031, 64, 16.0, 13),
+    # U and G over contraction ranges (partials added by a second launch): ranges
+    # of unequal length, a short last row tile, ranks 24 and 64
+    (4096, 4160, 1000, 24, 8.0, 26),
+    (1024, 8192, 1100, 64, 16.0, 27),
     # many tokens with a rank the streaming kernels do not take: split-contraction adapter products
     (192, 384, 1000, 12, 16.0, 24),
     (320, 384, 1000, 12, 16.0, 25),
