@@ -298,7 +298,10 @@ def test_dequantize_export_bit_exact(d_out, d_in):
 
 
 @pytest.mark.parametrize("d_out,d_in,r,alpha", [(128, 128, 8, 16.0), (192, 320, 3, 5.0), (256, 4160, 64, 16.0),
-                                                (512, 256, 128, 32.0)])
+                                                (512, 256, 128, 32.0),
+                                                # 512 column blocks: each workgroup walks 4 row tiles
+                                                # (next tile's loads in flight), the last block 64 wide
+                                                (256, 65472, 24, 8.0)])
 def test_merge_export_matches_oracle(d_out, d_in, r, alpha):
     """bf16(W_hat + s B A) ([工程] §3; [X长文] QLoRA section: merged into the
     restored 16-bit weight): every element within one bf16 step of the
