@@ -144,31 +144,28 @@ __device__ __forceinline__ void restore_word(uint32_t w, const RestoreTab& t, bf
 // wave can place one piece between consecutive MFMAs of its own.  The pieces
 // compute exactly what restore8 / make_tab compute.
 struct WordWork {
-  uint32_t sl, s2, HE, LE, HO, LO;
+  uint32_t w4, sl, s2, HA, LA, HB, LB;
 };
 
 template <int PIECE>
 __device__ __forceinline__ void word_piece(uint32_t w, const RestoreTab& t, WordWork& s, bf16x8_t& out) {
-  if (PIECE == 0) {
-    selectors_even(w, s.sl, s.s2);
+  if (PIECE == 0) {  // selectors of elements 0-3
+    s.w4 = w >> 4;
+    selectors(gather4(w, s.w4, 0), s.sl, s.s2);
   } else if (PIECE == 1) {
-    s.HE = perm(perm(t.h[3], t.h[2], s.sl), perm(t.h[1], t.h[0], s.sl), s.s2);
+    s.HA = perm(perm(t.h[3], t.h[2], s.sl), perm(t.h[1], t.h[0], s.sl), s.s2);
   } else if (PIECE == 2) {
-    s.LE = perm(perm(t.l[3], t.l[2], s.sl), perm(t.l[1], t.l[0], s.sl), s.s2);
-  } else if (PIECE == 3) {
-    selectors_odd(w, s.sl, s.s2);
+    s.LA = perm(perm(t.l[3], t.l[2], s.sl), perm(t.l[1], t.l[0], s.sl), s.s2);
+  } else if (PIECE == 3) {  // selectors of elements 4-7
+    selectors(gather4(w, s.w4, 1), s.sl, s.s2);
   } else if (PIECE == 4) {
-    lookup4(s.sl, s.s2, t, s.HO, s.LO);
-  } else if (PIECE == 5) {  // bf16 pairs (e0,e2) (e4,e6) (e1,e3) (e5,e7), kept in the same fields
-    const uint32_t e01 = perm(s.HE, s.LE, 0x05010400u), e23 = perm(s.HE, s.LE, 0x07030602u);
-    const uint32_t o01 = perm(s.HO, s.LO, 0x05010400u), o23 = perm(s.HO, s.LO, 0x07030602u);
-    s.HE = e01;
-    s.LE = e23;
-    s.HO = o01;
-    s.LO = o23;
+    lookup4(s.sl, s.s2, t, s.HB, s.LB);
+  } else if (PIECE == 5) {  // bf16 pairs (e0,e1) (e2,e3), kept in the same fields
+    const uint32_t e01 = perm(s.HA, s.LA, 0x05010400u), e23 = perm(s.HA, s.LA, 0x07030602u);
+    s.HA = e01;
+    s.LA = e23;
   } else {
-    const u32x4_t v = {perm(s.HO, s.HE, 0x05040100u), perm(s.HO, s.HE, 0x07060302u), perm(s.LO, s.LE, 0x05040100u),
-                       perm(s.LO, s.LE, 0x07060302u)};
+    const u32x4_t v = {s.HA, s.LA, perm(s.HB, s.LB, 0x05010400u), perm(s.HB, s.LB, 0x07030602u)};
     out = __builtin_bit_cast(bf16x8_t, v);
   }
 }
