@@ -20,8 +20,10 @@ Prints ONE JSON line.  Extra fields: the roofline of the dominant kernel
 (timed with hipEvents attached to its own dispatches inside the timed
 region), a per-kernel table from a second pass, the other workloads (the
 attention-shaped layer, the MLP set of a 7B-class layer, the few-token
-forward's packed-weight GB/s, exports, optimizer, dropout), and the oracle
-timed on the host cores (cpu_baseline, cpu_baselines).
+forward's packed-weight GB/s, exports, optimizer, dropout, the fused products
+against restoring each weight to bf16 once and multiplying with the ROCm BLAS
+library), and the oracle timed on the host cores (cpu_baseline,
+cpu_baselines).
 """
 
 import argparse
@@ -775,6 +777,90 @@ def adamw_section(steps):
 # The oracle on the host cores
 # ---------------------------------------------------------------------------
 
+def dequant_matmul_section(steps):
+    """The fused products against restoring the weight once and multiplying
+    in bf16: for each weight shape of the 65B-class layer at 4096 tokens
+    (r = 64, alpha = 16), the fused forward and dX kernels against this
+    library's dequantize kernel (W_hat bf16 written to HBM) followed by
+    torch's bf16 products X W_hat^T (F.linear) and dY W_hat on that W_hat
+    (the ROCm BLAS library).  The second route keeps a 16-bit copy of every
+    weight in HBM (2 bytes per weight instead of 0.52) and leaves out the
+    rank-r term, which the fused kernels include.  Kernel times in us."""
+    import torch
+    import torch.nn.functional as F
+    import nf4_bit_quantized_amd as q
+
+    T, r, alpha = 4096, 64, 16.0
+    g = torch.Generator(device="cuda").manual_seed(2)
+    out = {"tokens": T, "r": r}
+    for N, K in ((8192, 8192), (22016, 8192), (8192, 22016)):
+        pk, cd, cs = q.qlora_quantize_nf4(torch.randn(N, K, device="cuda", generator=g) * 0.02)
+        A = (torch.randn(r, K, device="cuda", generator=g) / r).to(torch.bfloat16)
+        B = (torch.randn(N, r, device="cuda", generator=g) * 0.01).to(torch.bfloat16)
+        X = torch.randn(T, K, device="cuda", generator=g).to(torch.bfloat16)
+        dY = torch.randn(T, N, device="cuda", generator=g).to(torch.bfloat16)
+        Y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+        U = torch.empty((T, r), dtype=torch.float32, device="cuda")
+        dX = torch.empty((T, K), dtype=torch.bfloat16, device="cuda")
+        dA = torch.empty((r, K), dtype=torch.float32, device="cuda")
+        dB = torch.empty((N, r), dtype=torch.float32, device="cuda")
+        W_hat = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
+        ws_bytes = max(q.qlora_fwd_workspace_bytes(N, K, T, r), q.qlora_bwd_workspace_bytes(N, K, T, r))
+        ws = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device="cuda")
+
+        def fused():
+            q.qlora_linear_fwd(pk, cd, cs, X, A, B, alpha, Y=Y, U_out=U, workspace=ws)
+            q.qlora_linear_bwd(pk, cd, cs, X, A, B, alpha, dY, U_in=U, dX=dX, dA=dA, dB=dB, workspace=ws)
+
+        for _ in range(2):
+            fused()
+            q.qlora_dequantize_nf4(pk, cd, cs, W_hat=W_hat)
+        torch.cuda.synchronize()
+        q.qlora_trace_read(reset=True)
+        q.qlora_trace_select({"fwd_gemm", "dx_gemm", "export"})
+        for _ in range(steps):
+            fused()
+            q.qlora_dequantize_nf4(pk, cd, cs, W_hat=W_hat)
+        torch.cuda.synchronize()
+        q.qlora_trace_enable(False)
+        kt = q.qlora_trace_read(reset=True)
+        us = {k: kt[k][1] / kt[k][0] * 1e3 for k in ("fwd_gemm", "dx_gemm", "export")}
+
+        def bf16_time(fn):
+            for _ in range(2):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / steps * 1e3
+
+        mm_fwd = bf16_time(lambda: F.linear(X, W_hat))
+        mm_dx = bf16_time(lambda: torch.mm(dY, W_hat))
+        base = 2.0 * T * K * N
+        fwd_fl, dx_fl = fused_flops(T, K, N, r)
+        fused_us = us["fwd_gemm"] + us["dx_gemm"]
+        route_us = us["export"] + mm_fwd + mm_dx
+        out[f"{N}x{K}"] = {
+            "fused_fwd_us": round(us["fwd_gemm"], 1), "fused_fwd_tflops": round(fwd_fl / us["fwd_gemm"] / 1e6, 1),
+            "fused_dx_us": round(us["dx_gemm"], 1), "fused_dx_tflops": round(dx_fl / us["dx_gemm"] / 1e6, 1),
+            "dequantize_us": round(us["export"], 1),
+            "bf16_fwd_us": round(mm_fwd, 1), "bf16_fwd_tflops": round(base / mm_fwd / 1e6, 1),
+            "bf16_dx_us": round(mm_dx, 1), "bf16_dx_tflops": round(base / mm_dx / 1e6, 1),
+            "fused_fwd_dx_us": round(fused_us, 1), "dequantize_then_bf16_us": round(route_us, 1),
+            "fused_over_route": round(fused_us / route_us, 3),
+        }
+        del pk, cd, cs, A, B, X, dY, Y, U, dX, dA, dB, W_hat, ws
+        torch.cuda.empty_cache()
+    out["note"] = ("dequantize_then_bf16 = one dequantize per weight and step, then X W_hat^T and dY W_hat in "
+                   "bf16 without the rank-r term; fused_over_route < 1 means the fused products are faster")
+    log("dequant_matmul", out)
+    return out
+
+
 def _threads():
     from threadpoolctl import threadpool_info
     return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
@@ -910,6 +996,7 @@ def main():
         result["lora_dropout_attn4096"] = dropout_section(lin, steps=sec_steps)
         result["qkv_gqa_70b"] = multi_proj_section(steps=sec_steps)
         result["projection_groups_65b"] = multi_proj_train_section(steps=10)
+        result["dequant_then_bf16_65b"] = dequant_matmul_section(steps=10)
     if not args.no_cpu_baseline:
         log("timing the oracle on the host ...")
         result["cpu_baseline"] = cpu_baseline_headline()
