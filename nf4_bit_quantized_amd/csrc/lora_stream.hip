@@ -527,15 +527,17 @@ __global__ __launch_bounds__(256) void k_lora_cols_sum(ColsLaunch L) {
 }
 
 // ---------------------------------------------------------------------------
-// U = X A^T for a few tokens (T <= 16), in one launch: workgroup j owns column
-// j of U for every token.  Its 1024 threads walk the contraction in pieces of
-// eight (thread t: pieces t, t + 1024, ...), each piece one 16-byte load of
-// A's row j and of every token's X row, with fp32 products; the threads' sums
-// are added in a fixed order (wave shuffles, then the 16 waves in LDS).  The
-// workgroup then writes U[t][j], the hi/lo pair of s*U[t][j] into Us (columns
-// j and r + j), and its share of Us's zero padding.  Only r workgroups run, so
-// each keeps a whole piece per thread and token in flight: up to 17 loads of
-// 16 bytes per thread, 278 KB per workgroup at 16 tokens.
+// U = X A^T for a few tokens (T <= 16), in one launch: workgroup (j, g) owns
+// column j of U for the tokens TT*g .. TT*g + TT - 1.  Its 1024 threads walk
+// the contraction in pieces of eight (thread t: pieces t, t + 1024, ...), each
+// piece one 16-byte load of A's row j and of each of its tokens' X rows, with
+// fp32 products; the threads' sums are added in a fixed order (wave shuffles,
+// then the 16 waves in LDS).  The workgroup then writes U[t][j], the hi/lo
+// pair of s*U[t][j] into Us (columns j and r + j), and its share of Us's zero
+// padding.  The tokens per workgroup (TT) are the fewest that keep the grid
+// within one workgroup per CU, so that each CU reads A's row and as few X
+// rows as the grid allows: with r = 64, one token per workgroup up to four
+// tokens, four at sixteen (each workgroup reads 5 rows of K instead of 17).
 // ---------------------------------------------------------------------------
 
 constexpr int kSmallDownThreads = 1024;
@@ -546,7 +548,9 @@ __global__ __launch_bounds__(kSmallDownThreads) void k_lora_down_small(SmallDown
   __shared__ float red[NW][TT];
   const int j = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int T = (int)p.T;
+  const int t0 = (int)blockIdx.y * TT;
+  const int T = (int)p.T - t0 < TT ? (int)p.T - t0 : TT;  // this workgroup's tokens, at least one
+  const uint16_t* X = p.X + (int64_t)t0 * p.K;
   float acc[TT];
 #pragma unroll
   for (int t = 0; t < TT; ++t) acc[t] = 0.0f;
@@ -557,7 +561,7 @@ __global__ __launch_bounds__(kSmallDownThreads) void k_lora_down_small(SmallDown
     const uint4 a = *reinterpret_cast<const uint4*>(arow + k);
     uint4 x[TT];
 #pragma unroll
-    for (int t = 0; t < TT; ++t) x[t] = *reinterpret_cast<const uint4*>(p.X + (int64_t)(t < T ? t : T - 1) * p.K + k);
+    for (int t = 0; t < TT; ++t) x[t] = *reinterpret_cast<const uint4*>(X + (int64_t)(t < T ? t : T - 1) * p.K + k);
     const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
@@ -581,12 +585,13 @@ __global__ __launch_bounds__(kSmallDownThreads) void k_lora_down_small(SmallDown
     float u = red[0][tid];
 #pragma unroll
     for (int w = 1; w < NW; ++w) u += red[w][tid];
-    if (p.U) p.U[(int64_t)tid * p.r + j] = u;
+    const int64_t t = t0 + tid;
+    if (p.U) p.U[t * p.r + j] = u;
     uint16_t hi, lo;
     split_bf16(p.s * u, hi, lo);
-    p.Us[(int64_t)tid * p.ldh + j] = hi;
-    p.Us[(int64_t)tid * p.ldh + p.r + j] = lo;
-    for (int64_t c = 2 * p.r + j; c < p.ldh; c += p.r) p.Us[(int64_t)tid * p.ldh + c] = 0;
+    p.Us[t * p.ldh + j] = hi;
+    p.Us[t * p.ldh + p.r + j] = lo;
+    for (int64_t c = 2 * p.r + j; c < p.ldh; c += p.r) p.Us[t * p.ldh + c] = 0;
   }
 }
 
@@ -620,11 +625,19 @@ hipError_t launch_lora_down_small(const SmallDownParams& p, hipStream_t stream, 
   if (p.T * p.K * 2 > 0x7FFFFFF0LL || (int64_t)p.r * p.K * 2 > 0x7FFFFFF0LL) return hipErrorInvalidValue;
   KernelEvents ev(kernel_id);
   const hipEvent_t e0 = ev.start(), e1 = ev.stop();
-  const dim3 grid((unsigned)p.r);
+  // tokens per workgroup: the fewest that keep r * ceil(T / tt) within 256
+  // workgroups, and no more than T rounded up to a power of two
+  int tt = 1;
+  while (tt < p.T && (int64_t)p.r * ((p.T + tt - 1) / tt) > 256) tt *= 2;
+  const dim3 grid((unsigned)p.r, (unsigned)((p.T + tt - 1) / tt));
   const dim3 block(kSmallDownThreads);
-  if (p.T <= 4) hipExtLaunchKernelGGL(k_lora_down_small<4>, grid, block, 0, stream, e0, e1, 0, p);
-  else if (p.T <= 8) hipExtLaunchKernelGGL(k_lora_down_small<8>, grid, block, 0, stream, e0, e1, 0, p);
-  else hipExtLaunchKernelGGL(k_lora_down_small<16>, grid, block, 0, stream, e0, e1, 0, p);
+  switch (tt) {
+    case 1: hipExtLaunchKernelGGL(k_lora_down_small<1>, grid, block, 0, stream, e0, e1, 0, p); break;
+    case 2: hipExtLaunchKernelGGL(k_lora_down_small<2>, grid, block, 0, stream, e0, e1, 0, p); break;
+    case 4: hipExtLaunchKernelGGL(k_lora_down_small<4>, grid, block, 0, stream, e0, e1, 0, p); break;
+    case 8: hipExtLaunchKernelGGL(k_lora_down_small<8>, grid, block, 0, stream, e0, e1, 0, p); break;
+    default: hipExtLaunchKernelGGL(k_lora_down_small<16>, grid, block, 0, stream, e0, e1, 0, p); break;
+  }
   return hipGetLastError();
 }
 

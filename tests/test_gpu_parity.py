@@ -140,6 +140,10 @@ CASES = [
     (256, 512, 7, 16, 32.0, 8),       # few-token path, 5..8 tokens
     (128, 448, 12, 8, 16.0, 9),       # few-token path, code runs not 4-byte aligned (K/64 = 7)
     (192, 1024, 16, 64, 16.0, 10),    # few-token path, two stages per contraction slice
+    # few-token U split over token groups: four tokens per workgroup with the last
+    # group holding one (T = 13, r = 64), two per workgroup with the last holding one
+    (256, 512, 13, 64, 16.0, 28),
+    (192, 1024, 7, 64, 16.0, 29),
     # streaming adapter products (many tokens): ragged token counts, contractions
     # ending in half a 128-chunk, ranks 8 / 24 / 64
     (192, 320, 523, 8, 16.0, 11),
