@@ -47,14 +47,14 @@ BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 # (sha256 of the files below); reported as null once those change.
 TRAFFIC_SOURCES = ("fused_gemm.hip", "fused_wide.hip", "fused.hpp", "restore.hpp", "common.hpp")
 TRAFFIC = {
-    "sha256": "daa5b02b20752a2135958c046215e254f41fc58b47c3b8af0441abb07e1d57f4",
+    "sha256": "f62ae23cbaecd172a7e6a426af85b6adc04f6285569f711a72cfc3e56eb418c6",
     # a 256 MiB device-to-device copy read 131084.5 KiB of FETCH_SIZE and wrote
     # 262144 KiB of WRITE_SIZE in the same runs
     "fetch_scale": 262144.0 / 131084.5,
     "write_scale": 1.0,
     # per dispatch, averaged over one 65B-class layer's launches (3 steps)
-    "dx_gemm": {"fetch_kib": 918048.0, "write_kib": 93184.0},
-    "fwd_gemm": {"fetch_kib": 709768.1, "write_kib": 211152.0},
+    "dx_gemm": {"fetch_kib": 932632.7, "write_kib": 93184.0},
+    "fwd_gemm": {"fetch_kib": 690559.1, "write_kib": 211152.0},
 }
 
 
