@@ -385,7 +385,7 @@ def decode_section(steps, warmup):
                 torch.cuda.synchronize()
                 call_ms = e0.elapsed_time(e1) / steps
                 q.qlora_trace_read(reset=True)
-                q.qlora_trace_select({"decode", "lora_down_gemm"})
+                q.qlora_trace_select({"decode", "decode_sum", "lora_down_gemm"})
                 for i in range(steps):
                     p = reps[i % copies]
                     q.qlora_linear_fwd(p[0], p[1], p[2], X, A, B, lin.alpha, Y=Y, U_out=U, workspace=ws)
@@ -394,7 +394,10 @@ def decode_section(steps, warmup):
                 kt = q.qlora_trace_read(reset=True)
                 packed_bytes = pk.numel() + cd.numel() + cs.numel() * 4
                 dec_n, dec_ms = kt.get("decode", (1, float("nan")))
-                dec_avg = dec_ms / max(dec_n, 1)
+                # a split contraction adds its ranges in a second kernel: counted with the stream
+                sum_n, sum_ms = kt.get("decode_sum", (0, 0.0))
+                sum_avg = sum_ms / max(dec_n, 1)
+                dec_avg = dec_ms / max(dec_n, 1) + sum_avg
                 u_n, u_ms = kt.get("lora_down_gemm", (1, float("nan")))
                 out[lin.name + tag] = {
                     "T": T, "d_out": lin.d_out, "d_in": lin.d_in,
@@ -404,6 +407,7 @@ def decode_section(steps, warmup):
                     "packed_GBps_call": round(packed_bytes / (call_ms * 1e-3) / 1e9, 1),
                     "u_kernel_us": round(u_ms / max(u_n, 1) * 1e3, 2),
                     "decode_kernel_us": round(dec_avg * 1e3, 2),
+                    "decode_sum_kernel_us": round(sum_avg * 1e3, 2) if sum_n else None,
                     "packed_GBps_kernel": round(packed_bytes / (dec_avg * 1e-3) / 1e9, 1),
                     "frac_hbm_kernel": round(packed_bytes / (dec_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                 }

@@ -99,6 +99,8 @@ struct FwdWs {
   float* part = nullptr;
   float* U = nullptr;
   uint16_t* Us = nullptr;
+  float* dpart = nullptr;  // the few-token kernel's contraction-split sums
+  size_t dpart_bytes = 0;
   size_t bytes = 0;
 };
 
@@ -111,6 +113,10 @@ FwdWs plan_fwd(const qlora_nf4_desc* d, int64_t T, int32_t r, void* ws) {
         c.take(lora_rows_ok(T, r) ? lora_rows_part_bytes(T, K, r) : skinny_part_bytes(T, K, r)));
     w.U = static_cast<float*>(c.take((size_t)T * r * 4));
     w.Us = static_cast<uint16_t*>(c.take((size_t)T * hilo_ld(r) * 2));
+  }
+  if (T > 0 && T <= kDecodeMaxT) {
+    w.dpart_bytes = decode_part_bytes(T, N, K, block_shift(d), d->dq_blocksize == 0);
+    w.dpart = static_cast<float*>(c.take(w.dpart_bytes));
   }
   w.bytes = c.off;
   return w;
@@ -333,7 +339,7 @@ static int enqueue_fwd(const qlora_nf4_desc* d, const uint8_t* packed, const uin
   // those must be 16-byte aligned; fp32 block scales are loaded per chunk)
   if (T <= kDecodeMaxT && decode_ok(d, codes, consts)) {
     HIP_TRY(launch_decode(packed, codes, consts, X, T, N, K, w.Us, hilo_ld(r), B, r, Y, d->table, block_shift(d),
-                          d->dq_blocksize == 0, s_));
+                          d->dq_blocksize == 0, w.dpart, w.dpart_bytes, s_));
     return QLORA_OK;
   }
   FusedParams fp{};

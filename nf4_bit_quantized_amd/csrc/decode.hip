@@ -75,6 +75,12 @@ struct DecodeParams {
   uint16_t* Y;         // [T][N]
   int bshift;          // log2(weights per absmax block / 64); K is a multiple of the block
   float level[16];
+  // contraction split: with nsplit > 1 the workgroups of a run of tiles take
+  // nsplit consecutive ranges of the chunks and store their sums to
+  // part[split][T][N] (the first range's with the rank-r term); k_decode_sum
+  // adds them and rounds Y
+  int nsplit;
+  float* part;
 };
 
 // Several weights that share X (the projections of one layer input) in one
@@ -158,11 +164,18 @@ __global__ __launch_bounds__(DW * 64) void k_decode(DecodeMulti M) {
   // every byte offset below fits 32 bits: the packed weight is below 2 GiB
   const int T = (int)P.T, K = (int)P.K;
   const int ntiles = (int)(P.N / 16);
-  const int nt0 = ((int)blockIdx.x - M.first_wg[pi]) * NTW;
+  const int local = (int)blockIdx.x - M.first_wg[pi];
+  const int split = local % P.nsplit;
+  const int nt0 = local / P.nsplit * NTW;
   const int nbk = K / 64;             // 64-weight halves of chunks per row
   const int nbc = nbk >> P.bshift;    // scale codes (or fp32 scales) per row
   const int sst = 4 * (((nbc + 3) >> 2) | 1);  // LDS row stride of the fp32 scales, in floats
-  const int nch = (K + 127) / 128;
+  // this workgroup's chunks c_lo .. c_hi - 1 (all of them without a split)
+  const int nch_all = (K + 127) / 128;
+  const int cps = (nch_all + P.nsplit - 1) / P.nsplit;
+  const int c_lo = split * cps;
+  const int c_hi = c_lo + cps < nch_all ? c_lo + cps : nch_all;
+  const int nch = c_hi - c_lo;
   const int nmine = nch > wave ? (nch - wave + DW - 1) / DW : 0;
   const int iters = (nmine + PD - 1) / PD * PD;
 
@@ -227,8 +240,8 @@ __global__ __launch_bounds__(DW * 64) void k_decode(DecodeMulti M) {
   const int xrow = XQ == 1 ? (i16 & 3) : i16;
 
   auto issue_x = [&](ChunkRegs<NTW, XQ>& R, int k) {
-    const int ch = wave + DW * k;
-    const bool in = ch < nch && ch * 128 + 8 * xp < K;
+    const int ch = c_lo + wave + DW * k;
+    const bool in = ch < c_hi && ch * 128 + 8 * xp < K;
 #pragma unroll
     for (int q = 0; q < XQ; ++q) {
       const bool tin = in && 4 * q + g < T;
@@ -237,8 +250,8 @@ __global__ __launch_bounds__(DW * 64) void k_decode(DecodeMulti M) {
     }
   };
   auto issue_w = [&](ChunkRegs<NTW, XQ>& R, int i, int k) {
-    const int ch = wave + DW * k;
-    const bool in = ch < nch && ch * 64 + 16 * g < K / 2 && nt0 + i < ntiles;
+    const int ch = c_lo + wave + DW * k;
+    const bool in = ch < c_hi && ch * 64 + 16 * g < K / 2 && nt0 + i < ntiles;
     R.w[i] = __builtin_amdgcn_raw_buffer_load_b128(
         rw, in ? wbase + (uint32_t)i * wtile + (uint32_t)ch * 64u : kOob, 0, 0);
   };
@@ -293,8 +306,8 @@ __global__ __launch_bounds__(DW * 64) void k_decode(DecodeMulti M) {
   for (int k = 0; k < iters; k += PD) {
 #pragma unroll
     for (int sp = 0; sp < PD; ++sp) {
-      const int ch = wave + DW * (k + sp);
-      const bool chin = ch < nch;
+      const int ch = c_lo + wave + DW * (k + sp);
+      const bool chin = ch < c_hi;
       const int chc = chin ? ch : 0;
       // X through the wave's slot into the MFMA layout; the slot's reads of the
       // previous chunk precede these writes in the wave's LDS order
@@ -366,7 +379,8 @@ __global__ __launch_bounds__(DW * 64) void k_decode(DecodeMulti M) {
   const int64_t n = (int64_t)n0 + 16 * wave;
   const bool tok = i16 < T;
   constexpr int MJ = 4;
-  const bool pre = P.r > 0 && (P.r & 7) == 0 && P.ldh <= 32 * MJ;
+  const bool tail = split == 0;  // the first range carries the rank-r term
+  const bool pre = tail && P.r > 0 && (P.r & 7) == 0 && P.ldh <= 32 * MJ;
   const __amdgpu_buffer_rsrc_t ru = rsrc(P.Us, P.T * P.ldh * 2);
   u32x4_t ua[MJ], ub[MJ];
   if (fin && pre) {
@@ -413,7 +427,7 @@ __global__ __launch_bounds__(DW * 64) void k_decode(DecodeMulti M) {
 #pragma unroll
     for (int q = 0; q < MJ; ++q)
       if (32 * q < P.ldh) c = mfma(__builtin_bit_cast(bf16x8_t, ua[q]), __builtin_bit_cast(bf16x8_t, ub[q]), c);
-  } else if (P.r > 0) {
+  } else if (tail && P.r > 0) {
     for (int64_t jj = 0; jj < P.ldh; jj += 32) {
       const uint32_t uo = tok ? (uint32_t)((i16 * P.ldh + jj + 8 * g) * 2) : kOob;
       const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(ru, uo, 0, 0);
@@ -425,11 +439,35 @@ __global__ __launch_bounds__(DW * 64) void k_decode(DecodeMulti M) {
       c = mfma(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c);
     }
   }
+  if (P.nsplit > 1) {  // this range's sum; k_decode_sum adds the ranges and rounds
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int t = 4 * g + v;
+      if (t < T) P.part[((int64_t)split * T + t) * P.N + n] = c[v];
+    }
+    return;
+  }
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const int t = 4 * g + v;
     if (t < T) P.Y[t * P.N + n] = f32_to_bf16_bits(c[v]);
   }
+}
+
+// Y = bf16(part[0] + part[1] + ...) after a split launch, the ranges added in
+// range order; four consecutive outputs per thread (N is a multiple of 16).
+__global__ __launch_bounds__(256) void k_decode_sum(DecodeParams P) {
+  const int64_t tn = P.T * P.N;
+  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;  // t * N + n
+  if (e >= tn) return;
+  float4 v = *reinterpret_cast<const float4*>(P.part + e);
+  for (int q = 1; q < P.nsplit; ++q) {
+    const float4 w = *reinterpret_cast<const float4*>(P.part + q * tn + e);
+    v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+  }
+  const uint2 y = {(uint32_t)f32_to_bf16_bits(v.x) | ((uint32_t)f32_to_bf16_bits(v.y) << 16),
+                   (uint32_t)f32_to_bf16_bits(v.z) | ((uint32_t)f32_to_bf16_bits(v.w) << 16)};
+  *reinterpret_cast<uint2*>(P.Y + e) = y;
 }
 
 // 16 waves where their 128 registers per lane hold the loop, else 8
@@ -477,11 +515,47 @@ bool decode_supported(int64_t N, int64_t K, int bshift, bool f32s) {
   return ((16 * rs + 15) & ~15LL) + 4 * (16 * nbc / 256 + 2) <= CODES_BYTES;
 }
 
-hipError_t launch_decode_multi(const DecodeWeight* w, int n, const uint16_t* X, int64_t T, int64_t K,
-                               const uint16_t* const* Us, int64_t ldh, int r, int bshift, bool f32s,
-                               hipStream_t stream) {
+// Tiles per workgroup for weights of ntiles_all 16-row tiles in all: spread
+// over the 256 CUs (at most 8 each), then cut until the workgroup's codes and
+// group ratios (or fp32 scales) fit their LDS region.  0: nothing fits.
+static int64_t decode_ntw(int64_t ntiles_all, int64_t K, int bshift, bool f32s) {
+  int64_t ntw = (ntiles_all + 255) / 256;
+  if (ntw > 8) ntw = 8;
+  const int64_t nbc = (K / 64) >> bshift;             // scale codes per row
+  const int64_t rs = 4 * (((nbc + 3) / 4) | 1);      // LDS row stride of the codes
+  auto aux_need = [&](int64_t t) { return ((16 * t * rs + 15) & ~15LL) + 4 * (16 * t * nbc / 256 + 2); };
+  while (!f32s && ntw > 1 && aux_need(ntw) > CODES_BYTES) --ntw;
+  if (!f32s && aux_need(ntw) > CODES_BYTES) return 0;
+  while (f32s && ntw > 1 && f32_scales_bytes(K, bshift, ntw) > SCALES_BYTES) --ntw;
+  if (f32s && f32_scales_bytes(K, bshift, ntw) > SCALES_BYTES) return 0;
+  return ntw;
+}
+
+// More than four tokens on a weight of at most 512 tiles: X (T rows of 256
+// bytes per chunk) outweighs the workgroup's one or two tiles of packed bytes
+// (1 KB each per chunk).  Two workgroups per run of twice the tiles, each over
+// half the contraction, halve the X each reads; their sums go through
+// part[2][T][N] and k_decode_sum.  Codes only (the fp32 scales of twice the
+// tiles would overflow LDS), and at least 64 chunks so that each of the 16
+// waves keeps two.
+int decode_split(int64_t T, int64_t N, int64_t K, int bshift, bool f32s) {
+  if (f32s || T <= 4 || T > 16 || !decode_supported(N, K, bshift, f32s) || (K + 127) / 128 < 64) return 1;
+  const int64_t ntw = decode_ntw(N / 16, K, bshift, f32s);
+  if (ntw < 1 || ntw > 2) return 1;
+  return decode_ntw(2 * ntw * 256, K, bshift, f32s) == 2 * ntw ? 2 : 1;
+}
+
+size_t decode_part_bytes(int64_t T, int64_t N, int64_t K, int bshift, bool f32s) {
+  const int sp = decode_split(T, N, K, bshift, f32s);
+  return sp > 1 ? (size_t)sp * T * N * 4 : 0;
+}
+
+static hipError_t decode_launch(const DecodeWeight* w, int n, const uint16_t* X, int64_t T, int64_t K,
+                                const uint16_t* const* Us, int64_t ldh, int r, int bshift, bool f32s, int nsplit,
+                                float* part, hipStream_t stream) {
   // byte offsets into the packed weight, codes and X are 32-bit
   if (n < 1 || n > kMaxProj || T < 1 || T > 16 || bshift < 0 || bshift > 2) return hipErrorInvalidValue;
+  if (nsplit > 1 && (n != 1 || !part)) return hipErrorInvalidValue;
   DecodeMulti M{};
   M.n = n;
   int64_t ntiles_all = 0;
@@ -495,24 +569,17 @@ hipError_t launch_decode_multi(const DecodeWeight* w, int n, const uint16_t* X, 
     P.bshift = bshift;
     const Nf4Table& tab = level_table(w[i].table);
     for (int j = 0; j < 16; ++j) P.level[j] = tab.level[j];
+    P.nsplit = nsplit;
+    P.part = part;
     ntiles_all += w[i].N / 16;
   }
-  // tiles per workgroup: all weights' 16-row tiles spread over the 256 CUs (at most 8 each)
-  int64_t ntw = (ntiles_all + 255) / 256;
-  if (ntw > 8) ntw = 8;
-  // the workgroup's codes and group ratios must fit their LDS region, and the
-  // group count one load per thread
-  const int64_t nbc = (K / 64) >> bshift;             // scale codes per row
-  const int64_t rs = 4 * (((nbc + 3) / 4) | 1);      // LDS row stride of the codes
-  auto aux_need = [&](int64_t t) { return ((16 * t * rs + 15) & ~15LL) + 4 * (16 * t * nbc / 256 + 2); };
-  while (!f32s && ntw > 1 && aux_need(ntw) > CODES_BYTES) --ntw;
-  if (!f32s && aux_need(ntw) > CODES_BYTES) return hipErrorInvalidValue;
-  while (f32s && ntw > 1 && f32_scales_bytes(K, bshift, ntw) > SCALES_BYTES) --ntw;
-  if (f32s && f32_scales_bytes(K, bshift, ntw) > SCALES_BYTES) return hipErrorInvalidValue;
+  // with a split, each run of tiles is twice as long and has nsplit workgroups
+  const int64_t ntw = decode_ntw(nsplit * ntiles_all, K, bshift, f32s);
+  if (ntw < 1) return hipErrorInvalidValue;
   int64_t wg = 0;
   for (int i = 0; i < n; ++i) {
     M.first_wg[i] = (int)wg;
-    wg += (w[i].N / 16 + ntw - 1) / ntw;
+    wg += (w[i].N / 16 + ntw - 1) / ntw * nsplit;
   }
   M.first_wg[n] = (int)wg;
   const unsigned grid = (unsigned)wg;
@@ -527,14 +594,28 @@ hipError_t launch_decode_multi(const DecodeWeight* w, int n, const uint16_t* X, 
     case 7: launch_ntw<7>(M, c2, f32s, grid, stream); break;
     default: launch_ntw<8>(M, c2, f32s, grid, stream); break;
   }
+  if (nsplit > 1) {
+    KernelEvents ev(KID_DECODE_SUM);
+    hipExtLaunchKernelGGL(k_decode_sum, dim3((unsigned)((T * w[0].N / 4 + 255) / 256)), dim3(256), 0, stream,
+                          ev.start(), ev.stop(), 0, M.p[0]);
+  }
   return hipGetLastError();
+}
+
+hipError_t launch_decode_multi(const DecodeWeight* w, int n, const uint16_t* X, int64_t T, int64_t K,
+                               const uint16_t* const* Us, int64_t ldh, int r, int bshift, bool f32s,
+                               hipStream_t stream) {
+  return decode_launch(w, n, X, T, K, Us, ldh, r, bshift, f32s, 1, nullptr, stream);
 }
 
 hipError_t launch_decode(const uint8_t* packed, const uint8_t* codes, const float* consts, const uint16_t* X,
                          int64_t T, int64_t N, int64_t K, const uint16_t* Us, int64_t ldh, const uint16_t* B,
-                         int r, uint16_t* Y, int table, int bshift, bool f32s, hipStream_t stream) {
+                         int r, uint16_t* Y, int table, int bshift, bool f32s, float* part, size_t part_bytes,
+                         hipStream_t stream) {
   const DecodeWeight w{packed, codes, consts, N, B, Y, table};
-  return launch_decode_multi(&w, 1, X, T, K, &Us, ldh, r, bshift, f32s, stream);
+  int sp = decode_split(T, N, K, bshift, f32s);
+  if (sp > 1 && (!part || part_bytes < (size_t)sp * T * N * 4)) sp = 1;
+  return decode_launch(&w, 1, X, T, K, &Us, ldh, r, bshift, f32s, sp, part, stream);
 }
 
 }  // namespace qlora

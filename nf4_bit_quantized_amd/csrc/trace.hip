@@ -10,7 +10,7 @@ namespace {
 
 const char* const kNames[KID_COUNT] = {
     "nf4_quantize", "fwd_gemm", "dx_gemm", "lora_down_gemm", "lora_g_gemm", "lora_grad_gemm",
-    "lora_db_gemm", "decode", "reduce", "fill_zero", "export", "adamw", "dropout"};
+    "lora_db_gemm", "decode", "reduce", "fill_zero", "export", "adamw", "dropout", "decode_sum"};
 
 struct Pending {
   int kid;

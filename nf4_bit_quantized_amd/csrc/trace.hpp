@@ -21,6 +21,7 @@ enum KernelId : int {
   KID_EXPORT,
   KID_ADAMW,
   KID_DROPOUT,
+  KID_DECODE_SUM,
   KID_COUNT
 };
 

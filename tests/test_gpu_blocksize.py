@@ -69,6 +69,7 @@ BS_CASES = [
     (256, 512, 4, 8, 16.0, 73, 256),
     (192, 1024, 16, 64, 16.0, 74, 128),   # few-token kernel, four token rows per load
     (4160, 256, 2, 16, 16.0, 75, 256),    # few-token kernel, two 16-row tiles per workgroup
+    (256, 8192, 9, 16, 16.0, 80, 128),    # few-token kernel, contraction split over two workgroups
     (128, 320, 3, 8, 16.0, 76, 128),      # rows not whole blocks: tiled kernel for few tokens
     (256, 256, 100, 16, 32.0, 77, 256),   # tiled kernels
     (192, 320, 150, 64, 16.0, 78, 128),   # tiled kernels, blocks spanning rows

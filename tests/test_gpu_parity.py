@@ -144,6 +144,14 @@ CASES = [
     # group holding one (T = 13, r = 64), two per workgroup with the last holding one
     (256, 512, 13, 64, 16.0, 28),
     (192, 1024, 7, 64, 16.0, 29),
+    # few-token kernel with the contraction split over two workgroups (more than
+    # four tokens, at most two tiles per workgroup, at least 64 chunks of 128):
+    # one tile per run, 65 chunks (ranges of 33 and 32), three tiles per run
+    # with the last run two and an odd rank, no rank-r term
+    (256, 8192, 16, 64, 16.0, 30),
+    (384, 8320, 13, 24, 8.0, 31),
+    (4160, 8192, 7, 12, 16.0, 32),
+    (512, 8192, 16, 0, 0.0, 33),
     # streaming adapter products (many tokens): ragged token counts, contractions
     # ending in half a 128-chunk, ranks 8 / 24 / 64
     (192, 320, 523, 8, 16.0, 11),
@@ -392,6 +400,39 @@ def test_few_tokens_with_unaligned_codes():
             e = normwise_err(host_bf16_to_f64(Y), o["Y"])
             say(f"  T={T} codes offset {c.data_ptr() % 16}: Y err {e:.2e}")
             assert e <= TOL, (T, e)
+
+
+@pytest.mark.parametrize("d_out,d_in,T,split", [
+    (256, 8192, 16, True),     # one tile per workgroup, 64 chunks
+    (384, 8320, 13, True),     # 65 chunks
+    (8192, 8192, 5, True),     # two tiles per workgroup unsplit
+    (256, 8192, 4, False),     # four tokens or fewer: one launch
+    (256, 4096, 16, False),    # fewer than 64 chunks
+    (8320, 8192, 16, False),   # three tiles per workgroup
+])
+def test_few_token_contraction_split_launches(d_out, d_in, T, split):
+    """The few-token forward splits the contraction over two workgroups (and
+    adds the ranges in a second launch) exactly for more than four tokens, at
+    most two tiles per workgroup and at least 64 chunks of 128 weights; the
+    parity cases above check the values of both forms against the oracle."""
+    import nf4_bit_quantized_amd as q
+    import torch
+    say(f"decode split d_out={d_out} d_in={d_in} T={T} expect split={split}")
+    g = torch.Generator(device="cuda").manual_seed(5)
+    packed, codes, consts = q.qlora_quantize_nf4(torch.randn(d_out, d_in, device="cuda", generator=g) * 0.02)
+    X = torch.randn(T, d_in, device="cuda", generator=g).to(torch.bfloat16)
+    A = (torch.randn(16, d_in, device="cuda", generator=g) / 16).to(torch.bfloat16)
+    B = (torch.randn(d_out, 16, device="cuda", generator=g) * 0.01).to(torch.bfloat16)
+    q.qlora_trace_select({"decode", "decode_sum"})
+    q.qlora_trace_read(reset=True)
+    try:
+        q.qlora_linear_fwd(packed, codes, consts, X, A, B, 32.0)
+        torch.cuda.synchronize()
+        t = q.qlora_trace_read(reset=True)
+    finally:
+        q.qlora_trace_enable(False)
+    assert t.get("decode", (0, 0.0))[0] == 1, t
+    assert t.get("decode_sum", (0, 0.0))[0] == (1 if split else 0), t
 
 
 def test_zero_tokens_is_a_no_op():
