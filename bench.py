@@ -45,7 +45,7 @@ BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 # counters read for a plain device-to-device copy of known size in the same
 # runs (--copy-calibration).  Valid only for the kernel sources they were taken on
 # (sha256 of the files below); reported as null once those change.
-TRAFFIC_SOURCES = ("fused_gemm.hip", "fused_wide.hip", "fused.hpp", "restore.hpp", "common.hpp")
+TRAFFIC_SOURCES = ("fused_gemm.hip", "fused_wide.hip", "fused_dx_wide.hip", "fused.hpp", "restore.hpp", "common.hpp")
 TRAFFIC = {
     "sha256": "f62ae23cbaecd172a7e6a426af85b6adc04f6285569f711a72cfc3e56eb418c6",
     # a 256 MiB device-to-device copy read 131084.5 KiB of FETCH_SIZE and wrote

@@ -63,4 +63,9 @@ hipError_t launch_fused(FusedParams P, bool dx, hipStream_t stream, int kernel_i
 bool fused_wide_ok(const FusedParams& P, bool dx);
 hipError_t launch_fused_wide(FusedParams P, hipStream_t stream, int kernel_id);
 
+// dX on 256 x 256 tiles with the restore done by the multiplying waves
+// (fused_dx_wide.hip); launch_fused picks it where it applies.
+bool fused_dx_wide_ok(const FusedParams& P);
+hipError_t launch_fused_dx_wide(FusedParams P, hipStream_t stream, int kernel_id);
+
 }  // namespace qlora

@@ -54,6 +54,8 @@
 // coalesced 16-byte writes.  Workgroups are ordered so that the tiles a single
 // XCD (round-robin by workgroup id) works on form a compact block (two tile
 // rows), keeping the operands they share in that XCD's L2.
+#include <cstdlib>
+
 #include "fused.hpp"
 #include "restore.hpp"
 #include "trace.hpp"
@@ -738,6 +740,12 @@ hipError_t launch_fused(FusedParams P, bool dx, hipStream_t stream, int kernel_i
   if (P.M * P.lda * 2 > 0x7FFFFFF0LL || (P.r > 0 && P.M * P.ldat * 2 > 0x7FFFFFF0LL) ||
       (dx ? P.K0 : P.N) * P.Kw / 2 > 0x7FFFFFF0LL)
     return hipErrorInvalidValue;
+  // QLORA_DX_NARROW=1 keeps dX on the 256 x 128 kernel (to compare the two on one GPU)
+  static const bool dx_narrow = [] {
+    const char* e = getenv("QLORA_DX_NARROW");
+    return e && e[0] == '1';
+  }();
+  if (dx && !dx_narrow && fused_dx_wide_ok(P)) return launch_fused_dx_wide(P, stream, kernel_id);
   P.mt = (int32_t)((P.M + 255) / 256);
   P.nt = (int32_t)((P.N + bn - 1) / bn);
   P.group_m = 2;
