@@ -10,7 +10,10 @@ oracle (normwise bar and elementwise statistics), dA and dB too; through
 one-hot rows of dY every output must be one restored weight, bit for bit;
 the product over several weights (their rows one contraction) and its
 layer-by-layer form (dX rounded after each layer and accumulated) are
-compared with the oracle's sum."""
+compared with the oracle's sum; a shape whose last round of wide tiles
+would be nearly empty runs whole rounds wide and its last columns on the
+256 x 128 kernel (through that kernel's weight-column offset), checked the
+same ways."""
 
 import numpy as np
 import pytest
@@ -184,3 +187,77 @@ def test_wide_and_tiled_dx_agree_on_a_training_shape():
     err = normwise_err(got, o["dX"])
     say(f"  sampled columns normwise {err:.2e}, elementwise {elementwise_stats(got, o['dX'])}")
     assert err <= TOL
+
+
+# d_in = 33216 at 1024 tokens: 4 x 130 tiles of 256 x 256, two full rounds of
+# the GPU plus 8 tiles; the wide launch keeps the 128 tile columns of the two
+# rounds and the 256 x 128 kernel takes the last 448 columns (the weight's
+# columns 32768 .. 33215, through its column offset).
+SPLIT_K = 33216
+
+
+@pytest.mark.parametrize("d_out,T,r,alpha,seed", [(128, 1024, 8, 16.0, 70), (192, 1000, 12, 24.0, 71)])
+def test_wide_dx_with_a_narrow_last_round_matches_oracle(d_out, T, r, alpha, seed):
+    import torch
+    import nf4_bit_quantized_amd as q
+    say(f"wide dX + narrow tail d_out={d_out} d_in={SPLIT_K} T={T} r={r}")
+    inp = workloads.layer_inputs(d_out, SPLIT_K, T, r, seed)
+    W_hat = onf4.dequantize(onf4.quantize(inp["W"])).astype(np.float64)
+    dXo, dAo, dBo = olora.backward(W_hat, bits_to_float(inp["X"]), bits_to_float(inp["A"]),
+                                   bits_to_float(inp["B"]), bits_to_float(inp["dY"]), alpha, r)
+    packed, codes, consts = q.qlora_quantize_nf4(dev_f32(inp["W"]))
+    dX, dA, dB = q.qlora_linear_bwd(packed, codes, consts, dev_bf16(inp["X"]), dev_bf16(inp["A"]),
+                                    dev_bf16(inp["B"]), alpha, dev_bf16(inp["dY"]))
+    torch.cuda.synchronize()
+    got = host_bf16_to_f64(dX)
+    err = normwise_err(got, dXo)
+    st = elementwise_stats(got, dXo)
+    tail = elementwise_stats(got[:, 32768:], dXo[:, 32768:])
+    say(f"  dX normwise {err:.2e}, elementwise {st}, last 448 columns {tail}")
+    assert err <= TOL
+    assert st["share_above_1e-2"] < 1e-3 and tail["share_above_1e-2"] < 1e-3
+    assert normwise_err(dA.cpu().numpy(), dAo) <= TOL
+    assert normwise_err(dB.cpu().numpy(), dBo) <= TOL
+
+
+def test_wide_dx_with_a_narrow_last_round_bit_exact_through_one_hot_rows():
+    """As test_wide_dx_restore_bit_exact_through_one_hot_rows, at the split
+    shape: every column of both launches, the narrow one's included, holds
+    the restored weight of its own column."""
+    import torch
+    import nf4_bit_quantized_amd as q
+    d_out, T = 128, 1024
+    say(f"wide dX + narrow tail one-hot d_out={d_out} d_in={SPLIT_K} T={T}")
+    inp = workloads.layer_inputs(d_out, SPLIT_K, 1, 1, seed=72, with_dy=False)
+    W_hat = onf4.dequantize(onf4.quantize(inp["W"]))
+    packed, codes, consts = q.qlora_quantize_nf4(dev_f32(inp["W"]))
+    rows = np.arange(T) % d_out
+    dY = torch.zeros((T, d_out), dtype=torch.bfloat16, device="cuda")
+    dY[torch.arange(T, device="cuda"), torch.from_numpy(rows).cuda()] = 1.0
+    X = torch.zeros((T, SPLIT_K), dtype=torch.bfloat16, device="cuda")
+    dX, _, _ = q.qlora_linear_bwd(packed, codes, consts, X, None, None, 0.0, dY)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(dX.float().cpu().numpy(), W_hat[rows])
+
+
+def test_wide_dx_with_a_narrow_last_round_over_several_weights():
+    import torch
+    import nf4_bit_quantized_amd as q
+    shapes, r, T, alpha = (128, 64), 8, 1024, 16.0
+    say(f"wide dX + narrow tail several weights shapes={shapes} d_in={SPLIT_K}")
+    Xb, layers = _layers(shapes, SPLIT_K, T, r, 180, [0, 0])
+    dX, grads = q.qlora_linear_bwd_multi([l["dev"] for l in layers], dev_bf16(Xb), alpha,
+                                         [dev_bf16(l["inp"]["dY"]) for l in layers])
+    torch.cuda.synchronize()
+    Xf = bits_to_float(Xb)
+    want = 0.0
+    for l in layers:
+        W_hat = onf4.dequantize(onf4.quantize(l["inp"]["W"]))
+        want = want + olora.backward(W_hat, Xf, bits_to_float(l["inp"]["A"]), bits_to_float(l["inp"]["B"]),
+                                     bits_to_float(l["inp"]["dY"]), alpha, r)[0]
+    got = host_bf16_to_f64(dX)
+    err = normwise_err(got, want)
+    st = elementwise_stats(got, want)
+    say(f"  dX normwise {err:.2e}, elementwise {st}")
+    assert err <= TOL
+    assert st["share_above_1e-2"] < 1e-3
