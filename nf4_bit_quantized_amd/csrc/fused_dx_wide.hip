@@ -318,7 +318,7 @@ __device__ __forceinline__ void read_b(Frag& f, const uint8_t* __restrict__ Bs, 
 
 }  // namespace
 
-template <bool DQ>
+template <bool DQ, bool SAMELD>
 __device__ __forceinline__ void dx_wide_body(const FusedParams& P) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
 
@@ -429,6 +429,21 @@ __device__ __forceinline__ void dx_wide_body(const FusedParams& P) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) xoff[j] = crow[j] * (uint32_t)(ld * 2) + chunk16[j & 1];
   };
+  // a main step's source inside the loop: with one row stride for every
+  // weight's dY (SAMELD) only the scalar resource changes, so the lanes'
+  // offsets stay in place from step to step
+  auto copy_source_main = [&](int si) {
+    if (!SAMELD) {
+      copy_source(si);
+      return;
+    }
+    if (si == ckey) return;
+    ckey = si;
+    const uint16_t* src;
+    if (si == 0) src = P.A;
+    else { const KernargParams K = kernarg_params(); src = K->seg[si].A; }
+    rx = rsrc(src, P.M * P.lda * 2);
+  };
   auto stage_a = [&](uint32_t s) { return lds + (s % 3) * A_BYTES; };
   auto stage_b = [&](uint32_t s) { return lds + B_OFF + (s & 1) * B_BYTES; };
   auto copy = [&](uint32_t c, uint32_t col, int j) {
@@ -458,9 +473,10 @@ __device__ __forceinline__ void dx_wide_body(const FusedParams& P) {
   // memory operations after them, and every wave has stored step s+1's B
   // tile; the last eight MFMAs of the step run while step s+1's first
   // fragments are read.
-  auto step = [&](uint32_t s, Frag& f0, auto main_tag, auto par_tag, Fetch& fcur, Fetch& fnext) {
+  auto step = [&](uint32_t s, Frag& f0, auto main_tag, auto par_tag, auto next_tag, Fetch& fcur, Fetch& fnext) {
     constexpr bool MAIN = decltype(main_tag)::value;
     constexpr int PAR = decltype(par_tag)::value;
+    constexpr bool NEXT_MAIN = decltype(next_tag)::value;  // step s+2 is known to be a main step
     uint8_t* const Bc = PAR < 0 ? stage_b(s) : lds + B_OFF + PAR * B_BYTES;
     uint8_t* const Bn = PAR < 0 ? stage_b(s + 1) : lds + B_OFF + (1 - PAR) * B_BYTES;
     const uint8_t* const Ac = stage_a(s);
@@ -471,7 +487,9 @@ __device__ __forceinline__ void dx_wide_body(const FusedParams& P) {
     int fsi = run.si;
     uint32_t floc = run.x - run.base;
     uint32_t col = floc * (uint32_t)(BK * 2);
-    if (s + 2 < nk) {
+    if (NEXT_MAIN) {
+      copy_source_main(run.si);
+    } else if (s + 2 < nk) {
       copy_source(run.si);
     } else {
       int si2;
@@ -579,16 +597,22 @@ __device__ __forceinline__ void dx_wide_body(const FusedParams& P) {
 
   // main steps in pairs (s even, so the B stages' parity is known), then the
   // last main step and the steps whose next step is a tail step (or none)
+  // (in the pairs, step s+2 of both steps is a main step; the last main
+  // steps may copy a tail step's columns)
   uint32_t s = 0;
-  for (; s + 2 < nk; s += 2) {
-    step(s, f0, Main{}, Par<0>{}, F1, F0);
-    step(s + 1, f0, Main{}, Par<1>{}, F0, F1);
+  for (; s + 3 < nk; s += 2) {
+    step(s, f0, Main{}, Par<0>{}, Main{}, F1, F0);
+    step(s + 1, f0, Main{}, Par<1>{}, Main{}, F0, F1);
   }
   if (s + 1 < nk) {
-    step(s, f0, Main{}, Par<0>{}, F1, F0);
+    step(s, f0, Main{}, Par<0>{}, Other{}, F1, F0);
     ++s;
+    if (s + 1 < nk) {
+      step(s, f0, Main{}, Par<1>{}, Other{}, F0, F1);
+      ++s;
+    }
   }
-  for (; s < nsteps; ++s) step(s, f0, Other{}, Par<-1>{}, F1, F0);
+  for (; s < nsteps; ++s) step(s, f0, Other{}, Par<-1>{}, Other{}, F1, F0);
 
   // the last copies (into stages no one reads) land before the output tile
   // goes over the stages: every wave's own, then a barrier
@@ -632,9 +656,12 @@ __device__ __forceinline__ void dx_wide_body(const FusedParams& P) {
   }
 }
 
-// DQ: 8-bit scale codes (else fp32 block scales)
-__global__ __launch_bounds__(256, 1) void k_qlora_dx_wide(FusedParams P) { dx_wide_body<true>(P); }
-__global__ __launch_bounds__(256, 1) void k_qlora_dx_wide_f32s(FusedParams P) { dx_wide_body<false>(P); }
+// DQ: 8-bit scale codes (else fp32 block scales); _ld: the weights' dY have
+// different row strides (several weights of different d_out)
+__global__ __launch_bounds__(256, 1) void k_qlora_dx_wide(FusedParams P) { dx_wide_body<true, true>(P); }
+__global__ __launch_bounds__(256, 1) void k_qlora_dx_wide_f32s(FusedParams P) { dx_wide_body<false, true>(P); }
+__global__ __launch_bounds__(256, 1) void k_qlora_dx_wide_ld(FusedParams P) { dx_wide_body<true, false>(P); }
+__global__ __launch_bounds__(256, 1) void k_qlora_dx_wide_f32s_ld(FusedParams P) { dx_wide_body<false, false>(P); }
 
 // 256 x 256 tiles: worth it when the tile count fills the GPU at least twice.
 // Every weight's rows must be whole contraction steps and the output whole
@@ -656,9 +683,11 @@ hipError_t launch_fused_dx_wide(FusedParams P, hipStream_t stream, int kernel_id
   P.tab = level_table(P.table);
   const int64_t ntiles = (int64_t)P.mt * P.nt;
   const unsigned grid = (unsigned)(((ntiles + 7) / 8) * 8);
+  bool same_ld = true;
+  for (int i = 1; i < P.nseg; ++i) same_ld = same_ld && P.seg[i].lda == P.lda;
   KernelEvents ev(kernel_id);
-  if (P.dq) hipExtLaunchKernelGGL(k_qlora_dx_wide, dim3(grid), dim3(256), 0, stream, ev.start(), ev.stop(), 0, P);
-  else hipExtLaunchKernelGGL(k_qlora_dx_wide_f32s, dim3(grid), dim3(256), 0, stream, ev.start(), ev.stop(), 0, P);
+  auto k = P.dq ? (same_ld ? k_qlora_dx_wide : k_qlora_dx_wide_ld) : (same_ld ? k_qlora_dx_wide_f32s : k_qlora_dx_wide_f32s_ld);
+  hipExtLaunchKernelGGL(k, dim3(grid), dim3(256), 0, stream, ev.start(), ev.stop(), 0, P);
   return hipGetLastError();
 }
 
