@@ -47,14 +47,15 @@ BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 # (sha256 of the files below); reported as null once those change.
 TRAFFIC_SOURCES = ("fused_gemm.hip", "fused_wide.hip", "fused_dx_wide.hip", "fused.hpp", "restore.hpp", "common.hpp")
 TRAFFIC = {
-    "sha256": "f6cc98e3255c144987d3e4f236429a3ad8b67550169af5957d53301d950a4dca",
-    # a 256 MiB device-to-device copy read 131084.9 KiB of FETCH_SIZE and wrote
+    "sha256": "573f89714a5511f9605bfd08bbf79aef47b419ca273342daa94d409d31d6b597",
+    # a 256 MiB device-to-device copy read 131084.5 KiB of FETCH_SIZE and wrote
     # 262144 KiB of WRITE_SIZE in the same runs
-    "fetch_scale": 262144.0 / 131084.9,
+    "fetch_scale": 262144.0 / 131084.5,
     "write_scale": 1.0,
-    # per dispatch, averaged over one 65B-class layer's launches (3 steps)
-    "dx_gemm": {"fetch_kib": 660690.4, "write_kib": 93184.0},
-    "fwd_gemm": {"fetch_kib": 690997.6, "write_kib": 211152.0},
+    # per dispatch, averaged over one 65B-class layer's launches (3 steps; dX:
+    # five per layer, down's dX being two)
+    "dx_gemm": {"fetch_kib": 535457.8, "write_kib": 74547.2},
+    "fwd_gemm": {"fetch_kib": 691156.9, "write_kib": 211152.0},
 }
 
 
