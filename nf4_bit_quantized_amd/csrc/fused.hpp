@@ -60,6 +60,15 @@ struct FusedParams {
 
 hipError_t launch_fused(FusedParams P, bool dx, hipStream_t stream, int kernel_id);
 
+// Choosing between the 256 x 256 kernels and the 256 x 128 one: `tiles`
+// workgroups take ceil(tiles / 256) rounds of the GPU (one per CU), and a
+// round of 256 x 256 tiles costs about 1.9 rounds of 256 x 128 ones (twice
+// the work, done a few per cent faster per flop).  Costs in tenths of a
+// 256 x 128 round.
+inline int64_t gpu_rounds(int64_t tiles) { return (tiles + 255) / 256; }
+inline int64_t wide_cost(int64_t tiles) { return 19 * gpu_rounds(tiles); }
+inline int64_t narrow_cost(int64_t tiles) { return 10 * gpu_rounds(tiles); }
+
 // The forward product on 256 x 256 tiles with the restore in the multiplying
 // waves' registers (fused_wide.hip); launch_fused picks it where it applies.
 bool fused_wide_ok(const FusedParams& P, bool dx);

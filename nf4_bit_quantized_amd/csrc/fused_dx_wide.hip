@@ -663,16 +663,17 @@ __global__ __launch_bounds__(256, 1) void k_qlora_dx_wide_f32s(FusedParams P) { 
 __global__ __launch_bounds__(256, 1) void k_qlora_dx_wide_ld(FusedParams P) { dx_wide_body<true, false>(P); }
 __global__ __launch_bounds__(256, 1) void k_qlora_dx_wide_f32s_ld(FusedParams P) { dx_wide_body<false, false>(P); }
 
-// 256 x 256 tiles: worth it when the tile count fills the GPU at least twice.
-// Every weight's rows must be whole contraction steps and the output whole
-// 64-column blocks, starting at the weight's first column (N may stop short
-// of d_in: the 256 x 128 kernel then takes the remaining columns).
+// 256 x 256 tiles can serve this dX (at least one full round of them; the
+// launcher weighs them against the 256 x 128 kernel).  Every weight's rows
+// must be whole contraction steps and the output whole 64-column blocks,
+// starting at the weight's first column (N may stop short of d_in: the
+// 256 x 128 kernel then takes the remaining columns).
 bool fused_dx_wide_ok(const FusedParams& P) {
   if (P.K0 % BK != 0 || P.N % 64 != 0 || P.N > P.Kw || P.col0 != 0) return false;
   for (int i = 1; i < P.nseg; ++i)
     if (P.seg[i].N % BK != 0) return false;
   const int64_t mt = (P.M + BM - 1) / BM, nt = (P.N + BN - 1) / BN;
-  return mt * nt >= 512;
+  return mt * nt >= 256;
 }
 
 hipError_t launch_fused_dx_wide(FusedParams P, hipStream_t stream, int kernel_id) {

@@ -746,25 +746,28 @@ hipError_t launch_fused(FusedParams P, bool dx, hipStream_t stream, int kernel_i
     return e && e[0] == '1';
   }();
   if (dx && !dx_narrow && P.col0 == 0 && fused_dx_wide_ok(P)) {
-    // A last round of 256 x 256 tiles that would leave most CUs idle goes to
-    // this kernel instead when its 256 x 128 tiles take at most one round:
-    // the wide launch keeps whole rounds, the rest of dX's columns follow.
+    // the cheapest of: every tile 256 x 256; whole rounds of those and the
+    // rest of dX's columns on this kernel; every tile 256 x 128
     const int64_t mt = (P.M + 255) / 256, nt = (P.N + 255) / 256;
-    const int64_t rounds = mt * nt / 256, rest = mt * nt % 256;
+    const int64_t rounds = mt * nt / 256;
     const int64_t ntw = rounds * 256 / mt;
     const int64_t tail_cols = P.N - ntw * 256;
-    if (rest == 0 || ntw < 1 || tail_cols <= 0 || mt * ((tail_cols + bn - 1) / bn) > 256)
-      return launch_fused_dx_wide(P, stream, kernel_id);
-    FusedParams W = P;
-    W.N = ntw * 256;
-    const hipError_t e = launch_fused_dx_wide(W, stream, kernel_id);
-    if (e != hipSuccess) return e;
-    P.col0 = ntw * 256;
-    P.N = tail_cols;
-    P.C += P.col0;
-    if (P.r > 0) {
-      P.Bt += P.col0;
-      for (int i = 1; i < P.nseg; ++i) P.seg[i].Bt += P.col0;
+    const int64_t all_wide = wide_cost(mt * nt), all_narrow = narrow_cost(mt * ((P.N + bn - 1) / bn));
+    const bool can_split = ntw >= 1 && tail_cols > 0 && mt * nt % 256 != 0;
+    const int64_t split = can_split ? 19 * rounds + narrow_cost(mt * ((tail_cols + bn - 1) / bn)) : all_wide + 1;
+    if (all_wide <= split && all_wide <= all_narrow) return launch_fused_dx_wide(P, stream, kernel_id);
+    if (split < all_narrow) {
+      FusedParams W = P;
+      W.N = ntw * 256;
+      const hipError_t e = launch_fused_dx_wide(W, stream, kernel_id);
+      if (e != hipSuccess) return e;
+      P.col0 = ntw * 256;
+      P.N = tail_cols;
+      P.C += P.col0;
+      if (P.r > 0) {
+        P.Bt += P.col0;
+        for (int i = 1; i < P.nseg; ++i) P.seg[i].Bt += P.col0;
+      }
     }
   }
   P.mt = (int32_t)((P.M + 255) / 256);

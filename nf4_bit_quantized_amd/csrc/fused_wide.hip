@@ -640,20 +640,25 @@ __global__ __launch_bounds__(256, 1) void k_qlora_fwd_wide_r(FusedParams P) { fw
 __global__ __launch_bounds__(256, 1) void k_qlora_fwd_wide_f32s(FusedParams P) { fwd_wide_body<false, true>(P); }
 __global__ __launch_bounds__(256, 1) void k_qlora_fwd_wide_f32s_r(FusedParams P) { fwd_wide_body<false, false>(P); }
 
-// 256 x 256 tiles: worth it when the tile count fills the GPU at least twice.
-// Over several weights every weight's columns must be whole tiles.
+// 256 x 256 tiles where their rounds of the GPU cost no more than those of the
+// 256 x 128 kernel's tiles (wide_cost / narrow_cost), or over several weights
+// (whose columns must each be whole tiles).
 bool fused_wide_ok(const FusedParams& P, bool dx) {
   if (dx || P.accumulate || P.K0 % BK != 0) return false;
   const int64_t mt = (P.M + BM - 1) / BM;
-  int64_t nt = (P.N + BN - 1) / BN;
+  int64_t nt = (P.N + BN - 1) / BN, nt128 = (P.N + 127) / 128;
   if (P.nseg > 1) {
     if (P.N % BN != 0) return false;
     for (int i = 1; i < P.nseg; ++i) {
       if (P.seg[i].N % BN != 0) return false;
       nt += P.seg[i].N / BN;
+      nt128 += P.seg[i].N / 128;
     }
   }
-  return mt * nt >= 512;
+  // several weights: one launch reads X once per tile row (the alternative is
+  // a launch per weight), so any full round of tiles takes it
+  if (P.nseg > 1) return mt * nt >= 256;
+  return mt * nt >= 256 && wide_cost(mt * nt) <= narrow_cost(mt * nt128);
 }
 
 hipError_t launch_fused_wide(FusedParams P, hipStream_t stream, int kernel_id) {
