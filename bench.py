@@ -47,15 +47,15 @@ BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 # (sha256 of the files below); reported as null once those change.
 TRAFFIC_SOURCES = ("fused_gemm.hip", "fused_wide.hip", "fused_dx_wide.hip", "fused.hpp", "restore.hpp", "common.hpp")
 TRAFFIC = {
-    "sha256": "573f89714a5511f9605bfd08bbf79aef47b419ca273342daa94d409d31d6b597",
+    "sha256": "8ce5a3633c0507f169469aefcacd0f69547121beb3776976f7042d7c063d716b",
     # a 256 MiB device-to-device copy read 131084.5 KiB of FETCH_SIZE and wrote
     # 262144 KiB of WRITE_SIZE in the same runs
     "fetch_scale": 262144.0 / 131084.5,
     "write_scale": 1.0,
     # per dispatch, averaged over one 65B-class layer's launches (3 steps; dX:
     # five per layer, down's dX being two)
-    "dx_gemm": {"fetch_kib": 535457.8, "write_kib": 74547.2},
-    "fwd_gemm": {"fetch_kib": 691156.9, "write_kib": 211152.0},
+    "dx_gemm": {"fetch_kib": 534185.1, "write_kib": 74547.2},
+    "fwd_gemm": {"fetch_kib": 692580.8, "write_kib": 211152.0},
 }
 
 
