@@ -47,7 +47,7 @@ BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 # (sha256 of the files below); reported as null once those change.
 TRAFFIC_SOURCES = ("fused_gemm.hip", "fused_wide.hip", "fused_dx_wide.hip", "fused.hpp", "restore.hpp", "common.hpp")
 TRAFFIC = {
-    "sha256": "8ce5a3633c0507f169469aefcacd0f69547121beb3776976f7042d7c063d716b",
+    "sha256": "de6260cf45260719f5ed6e873792ae49a1d35d1db4ff099d749d29b38641c07e",
     # a 256 MiB device-to-device copy read 131084.5 KiB of FETCH_SIZE and wrote
     # 262144 KiB of WRITE_SIZE in the same runs
     "fetch_scale": 262144.0 / 131084.5,

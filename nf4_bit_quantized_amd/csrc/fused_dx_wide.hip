@@ -39,16 +39,18 @@
 // goes from global memory straight into one of three LDS A stages
 // (buffer_load_dwordx4 ... lds), two steps ahead, two copies per slice; A rows
 // are 128 B with chunk c of row R at c ^ (R & 7) ^ ((R >> 3) & 1).  One
-// barrier per step, at the start of its last slice: by then every wave has
+// barrier per step, in the middle of its last slice: by then every wave has
 // stored the next step's B tile and the next step's copies have landed, and
-// the last slice's MFMAs run while the next step's first fragments are read.
+// the last eight MFMAs of the step run while the next step's first fragments
+// are read.
 //
-// Per step s and wave: slice 0 issues the weight loads of step s+2; slices 0-2
-// restore step s+1 (loaded during step s-1), one piece of a few vector
-// instructions after each MFMA; 16 MFMAs per slice, each followed by one
-// fragment read of the next slice.  Several weights (the projections that
-// share one input): their contraction rows follow each other, each against
-// its own dY, then every weight's rank-r tail; dX is one fp32 sum.
+// Per step s and wave: slice 0 issues the weight loads of step s+2; the
+// restore of step s+1 (loaded during step s-1) runs in 39 pieces of a few
+// vector instructions, one after each of the 56 MFMAs before the barrier; the
+// MFMAs of slices 0-2 are each followed by one fragment read of the next
+// slice.  Several weights (the projections that share one input): their
+// contraction rows follow each other, each against its own dY, then every
+// weight's rank-r tail; dX is one fp32 sum.
 #include "fused.hpp"
 #include "restore.hpp"
 #include "trace.hpp"
