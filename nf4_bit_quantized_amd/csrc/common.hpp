@@ -87,12 +87,14 @@ __device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) 
 // q + r * fl32(1/255) rounds to the correctly rounded quotient for every
 // finite c_g >= 0 (checked over all such floats).  c_g = inf or NaN leaves r
 // NaN; q is then the IEEE quotient itself.
-__device__ __forceinline__ float restored_scale(uint32_t code, float c_g) {
+__device__ __forceinline__ float scale_step(float c_g) {
   constexpr float inv = 1.0f / 255.0f;
   const float q = c_g * inv;
   const float r = __builtin_fmaf(-q, 255.0f, c_g);
-  const float step = r == r ? __builtin_fmaf(r, inv, q) : q;
-  return (float)code * step;
+  return r == r ? __builtin_fmaf(r, inv, q) : q;
+}
+__device__ __forceinline__ float restored_scale(uint32_t code, float c_g) {
+  return (float)code * scale_step(c_g);
 }
 
 }  // namespace qlora

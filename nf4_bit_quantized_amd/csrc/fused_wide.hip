@@ -126,10 +126,20 @@ struct BFrag {
   bf16x8_t b[2][4];  // [column tile][slice]
 };
 
-template <bool DQ>
-__device__ __forceinline__ RestoreTab block_tab(const Fetch& f, int j, uint32_t shift, const Nf4Table& tab) {
-  const float sc = DQ ? restored_scale((f.code4[j] >> shift) & 0xFFu, f.cg[j]) : f.cg[j];
-  return make_tab(tab, sc);
+// The restored scale of the fetched block of column tile j.  CG: every block of
+// the lane's row lies in one group of 256, whose step fl32(c_g / 255) the lane
+// computed once (step[j]); the result is the same as restored_scale's.
+template <bool DQ, bool CG>
+__device__ __forceinline__ float fetched_scale(const Fetch& f, int j, uint32_t shift, const float (&step)[2]) {
+  if (!DQ) return f.cg[j];
+  const uint32_t code = (f.code4[j] >> shift) & 0xFFu;
+  return CG ? (float)code * step[j] : restored_scale(code, f.cg[j]);
+}
+
+template <bool DQ, bool CG>
+__device__ __forceinline__ RestoreTab block_tab(const Fetch& f, int j, uint32_t shift, const Nf4Table& tab,
+                                               const float (&step)[2]) {
+  return make_tab(tab, fetched_scale<DQ, CG>(f, j, shift, step));
 }
 
 __device__ __forceinline__ void restore_word(uint32_t w, const RestoreTab& t, bf16x8_t& out) {
@@ -181,11 +191,11 @@ struct TabWork {
   uint32_t p[4];
 };
 
-template <bool DQ, int Q>
+template <bool DQ, bool CG, int Q>
 __device__ __forceinline__ void tab_piece(const Fetch& f, int j, uint32_t shift, const float (&lvh)[8], TabWork& s,
-                                          RestoreTab& t) {
+                                          RestoreTab& t, const float (&step)[2]) {
   if (Q == 0) {
-    s.sc = DQ ? restored_scale((f.code4[j] >> shift) & 0xFFu, f.cg[j]) : f.cg[j];
+    s.sc = fetched_scale<DQ, CG>(f, j, shift, step);
   } else if (Q == 1 || Q == 2) {
     const int q = Q - 1;
     const uint32_t w0 = pack_bf16x2(lvh[4 * q] * s.sc, lvh[4 * q + 1] * s.sc);
@@ -245,7 +255,7 @@ __device__ __forceinline__ void order_slice() {
 
 }  // namespace
 
-template <bool DQ, bool TV>
+template <bool DQ, bool TV, bool CG>
 __device__ __forceinline__ void fwd_wide_body(const FusedParams& P) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
 
@@ -323,6 +333,14 @@ __device__ __forceinline__ void fwd_wide_body(const FusedParams& P) {
     wc.nk = nk;
     wc.rot = rot;
     wc.bshift = (uint32_t)P.bshift;
+  }
+  // CG: the step fl32(c_g / 255) of each of the lane's two rows' group
+  float step[2] = {0.0f, 0.0f};
+  if (CG) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      step[j] = scale_step(__builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(wc.rk, ((wc.coff[j] >> wc.bshift) >> 8) * 4, 0, 0)));
   }
   const Nf4Table tab = P.tab;
   float lvh[8];  // the eight levels whose restored values this half of the wave forms
@@ -481,14 +499,14 @@ __device__ __forceinline__ void fwd_wide_body(const FusedParams& P) {
               if (ks == 0) pin(fb);
               break;
             case 14:
-              if (ks == 0) tab_piece<DQ, 0>(fb, 0, sh0, lvh, tw0, tn[0]);
-              if (ks == 1) tab_piece<DQ, 2>(fb, 0, sh0, lvh, tw0, tn[0]);
-              if (ks == 2) tab_piece<DQ, 4>(fb, 0, sh0, lvh, tw0, tn[0]);
+              if (ks == 0) tab_piece<DQ, CG, 0>(fb, 0, sh0, lvh, tw0, tn[0], step);
+              if (ks == 1) tab_piece<DQ, CG, 2>(fb, 0, sh0, lvh, tw0, tn[0], step);
+              if (ks == 2) tab_piece<DQ, CG, 4>(fb, 0, sh0, lvh, tw0, tn[0], step);
               break;
             case 15:
-              if (ks == 0) tab_piece<DQ, 1>(fb, 0, sh0, lvh, tw0, tn[0]);
-              if (ks == 1) tab_piece<DQ, 3>(fb, 0, sh0, lvh, tw0, tn[0]);
-              if (ks == 2) tab_piece<DQ, 0>(fb, 1, sh1, lvh, tw1, tn[1]);
+              if (ks == 0) tab_piece<DQ, CG, 1>(fb, 0, sh0, lvh, tw0, tn[0], step);
+              if (ks == 1) tab_piece<DQ, CG, 3>(fb, 0, sh0, lvh, tw0, tn[0], step);
+              if (ks == 2) tab_piece<DQ, CG, 0>(fb, 1, sh1, lvh, tw1, tn[1], step);
               break;
             default: break;
           }
@@ -496,13 +514,13 @@ __device__ __forceinline__ void fwd_wide_body(const FusedParams& P) {
           // slice 3: the rest of step s+1's tile 1 table, and step s+1's first slice
           const uint32_t wa = word(fb, 0, 0), wb = word(fb, 1, 0);
           switch (m) {
-            case 0: tab_piece<DQ, 1>(fb, 1, sh1, lvh, tw1, tn[1]); break;
+            case 0: tab_piece<DQ, CG, 1>(fb, 1, sh1, lvh, tw1, tn[1], step); break;
             case 1: word_piece<0>(wa, tn[0], w0, b0.b[0]); break;
-            case 2: tab_piece<DQ, 2>(fb, 1, sh1, lvh, tw1, tn[1]); break;
+            case 2: tab_piece<DQ, CG, 2>(fb, 1, sh1, lvh, tw1, tn[1], step); break;
             case 3: word_piece<1>(wa, tn[0], w0, b0.b[0]); break;
-            case 4: tab_piece<DQ, 3>(fb, 1, sh1, lvh, tw1, tn[1]); break;
+            case 4: tab_piece<DQ, CG, 3>(fb, 1, sh1, lvh, tw1, tn[1], step); break;
             case 5: word_piece<2>(wa, tn[0], w0, b0.b[0]); break;
-            case 6: tab_piece<DQ, 4>(fb, 1, sh1, lvh, tw1, tn[1]); break;
+            case 6: tab_piece<DQ, CG, 4>(fb, 1, sh1, lvh, tw1, tn[1], step); break;
             case 7: word_piece<3>(wa, tn[0], w0, b0.b[0]); break;
             case 8: word_piece<0>(wb, tn[1], w1, b0.b[1]); break;
             case 9: word_piece<4>(wa, tn[0], w0, b0.b[0]); break;
@@ -565,8 +583,8 @@ __device__ __forceinline__ void fwd_wide_body(const FusedParams& P) {
     for (int j = 0; j < 8; ++j) copy(c, j);
   RestoreTab t[2];
   BS b0;
-  t[0] = block_tab<DQ>(fA, 0, code_shift(wc, 0, 0), tab);
-  t[1] = block_tab<DQ>(fA, 1, code_shift(wc, 1, 0), tab);
+  t[0] = block_tab<DQ, CG>(fA, 0, code_shift(wc, 0, 0), tab, step);
+  t[1] = block_tab<DQ, CG>(fA, 1, code_shift(wc, 1, 0), tab, step);
   restore_slice(fA, t, 0, b0);
   wait_vm<8>();  // steps 0 and 1 have landed (step 2 may be in flight)
   lds_barrier();
@@ -634,11 +652,14 @@ __device__ __forceinline__ void fwd_wide_body(const FusedParams& P) {
   }
 }
 
-// DQ: 8-bit scale codes (else fp32 block scales); TV: r is a multiple of 8
-__global__ __launch_bounds__(256, 1) void k_qlora_fwd_wide(FusedParams P) { fwd_wide_body<true, true>(P); }
-__global__ __launch_bounds__(256, 1) void k_qlora_fwd_wide_r(FusedParams P) { fwd_wide_body<true, false>(P); }
-__global__ __launch_bounds__(256, 1) void k_qlora_fwd_wide_f32s(FusedParams P) { fwd_wide_body<false, true>(P); }
-__global__ __launch_bounds__(256, 1) void k_qlora_fwd_wide_f32s_r(FusedParams P) { fwd_wide_body<false, false>(P); }
+// DQ: 8-bit scale codes (else fp32 block scales); TV: r is a multiple of 8;
+// _cg: each weight row's blocks lie in one group of 256 blocks
+__global__ __launch_bounds__(256, 1) void k_qlora_fwd_wide(FusedParams P) { fwd_wide_body<true, true, false>(P); }
+__global__ __launch_bounds__(256, 1) void k_qlora_fwd_wide_r(FusedParams P) { fwd_wide_body<true, false, false>(P); }
+__global__ __launch_bounds__(256, 1) void k_qlora_fwd_wide_cg(FusedParams P) { fwd_wide_body<true, true, true>(P); }
+__global__ __launch_bounds__(256, 1) void k_qlora_fwd_wide_r_cg(FusedParams P) { fwd_wide_body<true, false, true>(P); }
+__global__ __launch_bounds__(256, 1) void k_qlora_fwd_wide_f32s(FusedParams P) { fwd_wide_body<false, true, false>(P); }
+__global__ __launch_bounds__(256, 1) void k_qlora_fwd_wide_f32s_r(FusedParams P) { fwd_wide_body<false, false, false>(P); }
 
 // 256 x 256 tiles where their rounds of the GPU cost no more than those of the
 // 256 x 128 kernel's tiles (wide_cost / narrow_cost), or over several weights
@@ -677,9 +698,12 @@ hipError_t launch_fused_wide(FusedParams P, hipStream_t stream, int kernel_id) {
   const unsigned grid = (unsigned)(((ntiles + 7) / 8) * 8);
   KernelEvents ev(kernel_id);
   const bool tv = P.r % 8 == 0;
+  // blocks per weight row; a row lies in one group of 256 blocks when they divide 256
+  const int64_t nbpr = (P.Kw / 64) >> P.bshift;
+  const bool cg = nbpr > 0 && 256 % nbpr == 0;
   if (P.dq) {
-    if (tv) hipExtLaunchKernelGGL(k_qlora_fwd_wide, dim3(grid), dim3(256), 0, stream, ev.start(), ev.stop(), 0, P);
-    else hipExtLaunchKernelGGL(k_qlora_fwd_wide_r, dim3(grid), dim3(256), 0, stream, ev.start(), ev.stop(), 0, P);
+    auto k = tv ? (cg ? k_qlora_fwd_wide_cg : k_qlora_fwd_wide) : (cg ? k_qlora_fwd_wide_r_cg : k_qlora_fwd_wide_r);
+    hipExtLaunchKernelGGL(k, dim3(grid), dim3(256), 0, stream, ev.start(), ev.stop(), 0, P);
   } else {
     if (tv) hipExtLaunchKernelGGL(k_qlora_fwd_wide_f32s, dim3(grid), dim3(256), 0, stream, ev.start(), ev.stop(), 0, P);
     else hipExtLaunchKernelGGL(k_qlora_fwd_wide_f32s_r, dim3(grid), dim3(256), 0, stream, ev.start(), ev.stop(), 0, P);
