@@ -829,7 +829,9 @@ def dequant_matmul_section(steps):
         torch.cuda.synchronize()
         q.qlora_trace_enable(False)
         kt = q.qlora_trace_read(reset=True)
-        us = {k: kt[k][1] / kt[k][0] * 1e3 for k in ("fwd_gemm", "dx_gemm", "export")}
+        # per call (a dX call can be two launches: whole rounds of 256x256
+        # tiles, then the last columns on 256x128 tiles)
+        us = {k: kt[k][1] / steps * 1e3 for k in ("fwd_gemm", "dx_gemm", "export")}
 
         def bf16_time(fn):
             for _ in range(2):
