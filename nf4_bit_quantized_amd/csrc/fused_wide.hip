@@ -91,8 +91,9 @@ __device__ __forceinline__ uint32_t rotated(uint32_t step, uint32_t rot, uint32_
   return kt >= nk ? kt - nk : kt;
 }
 
-// Exactly six vector-memory loads per call (the waits below count them).
-template <bool DQ>
+// Exactly six vector-memory loads per call, four with CG (no group constants;
+// the waits below count them).
+template <bool DQ, bool CG>
 __device__ __forceinline__ void fetch(Fetch& f, const WCursor& c, uint32_t step) {
   const uint32_t kt = rotated(step, c.rot, c.nk);
 #pragma unroll
@@ -102,7 +103,8 @@ __device__ __forceinline__ void fetch(Fetch& f, const WCursor& c, uint32_t step)
     // the codes array holds N*K/bs bytes, a multiple of 4, so the aligned dword is in
     // range; without the second level the code load reads zero and cg is the block's scale
     f.code4[j] = __builtin_amdgcn_raw_buffer_load_b32(c.rc, blk & ~3u, 0, 0);
-    f.cg[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(c.rk, (DQ ? blk >> 8 : blk) * 4, 0, 0));
+    f.cg[j] = CG ? 0.0f
+                 : __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(c.rk, (DQ ? blk >> 8 : blk) * 4, 0, 0));
   }
 }
 
@@ -461,9 +463,9 @@ __device__ __forceinline__ void fwd_wide_body(const FusedParams& P) {
       const BS& bcur = ks == 0 ? b0 : bs[ks - 1];
       if (ks == 3) {
         // step s+1's copies (issued during step s-2) have landed: after them
-        // this wave issued step s-1's six loads and eight copies and six
-        // loads and six copies of this step
-        wait_vm<26>();
+        // this wave issued step s-1's six loads (four with CG) and eight
+        // copies and six loads (four) and six copies of this step
+        wait_vm<CG ? 22 : 26>();
         lds_barrier();
       }
 #pragma unroll
@@ -472,7 +474,7 @@ __device__ __forceinline__ void fwd_wide_body(const FusedParams& P) {
         // fragments of the next slice; in slice 3, those of step s+1's first slice
         if (m < 8) an[m] = *reinterpret_cast<const bf16x8_t*>((ks < 3 ? As : An) + arow + m * 4096 + apos[(ks + 1) & 3]);
         if (m == 4 || m == 12) cp(s + 3, 2 * ks + (m == 12));
-        if (ks == 0 && m == 1) fetch<DQ>(fc, wc, s + 2 < nk ? s + 2 : nk - 1);
+        if (ks == 0 && m == 1) fetch<DQ, CG>(fc, wc, s + 2 < nk ? s + 2 : nk - 1);
         // restore pieces: A = tile 0's word, B = tile 1's
         const uint32_t sh0 = code_shift(wc, 0, s + 1), sh1 = code_shift(wc, 1, s + 1);
         if (ks < 3) {
@@ -554,12 +556,12 @@ __device__ __forceinline__ void fwd_wide_body(const FusedParams& P) {
     const uint8_t* As = stage(s);
     const uint8_t* An = stage(s + 1);
     bf16x8_t a1[8];
-    fetch<DQ>(fc, wc, nk - 1);
+    fetch<DQ, CG>(fc, wc, nk - 1);
     if (s + 1 < nsteps) tail_frags<TV>(Bt, ldbt, P.r, nrow, h, s + 1 - nk, bnext);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       if (ks == 3) {
-        wait_vm<26>();
+        wait_vm<CG ? 22 : 26>();
         lds_barrier();
       }
       bf16x8_t(&ac)[8] = ks % 2 == 0 ? a0 : a1;
@@ -575,8 +577,8 @@ __device__ __forceinline__ void fwd_wide_body(const FusedParams& P) {
   // prologue: weight data of steps 0 and 1, copies of steps 0, 1 and 2, the
   // tables and first slice of step 0, and that slice's A fragments
   Fetch fA, fB, fC;
-  fetch<DQ>(fA, wc, 0);
-  fetch<DQ>(fB, wc, 1 < nk ? 1 : nk - 1);
+  fetch<DQ, CG>(fA, wc, 0);
+  fetch<DQ, CG>(fB, wc, 1 < nk ? 1 : nk - 1);
 #pragma unroll
   for (int c = 0; c < 3; ++c)
 #pragma unroll
