@@ -47,15 +47,15 @@ BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 # (sha256 of the files below); reported as null once those change.
 TRAFFIC_SOURCES = ("fused_gemm.hip", "fused_wide.hip", "fused_dx_wide.hip", "fused.hpp", "restore.hpp", "common.hpp")
 TRAFFIC = {
-    "sha256": "48dfe674b0f1c2a6b3c350bad1dfede3ebc9f4eaaf84d462ce8982b7cbc62bc3",
+    "sha256": "6812984a85af55c939c99dcfb7a2574d245f4a5fe691ccf8f856102a1ba2c4b9",
     # a 256 MiB device-to-device copy read 131084.5 KiB of FETCH_SIZE and wrote
     # 262144 KiB of WRITE_SIZE in the same runs
     "fetch_scale": 262144.0 / 131084.5,
     "write_scale": 1.0,
     # per dispatch, averaged over one 65B-class layer's launches (3 steps; dX:
     # five per layer, down's dX being two)
-    "dx_gemm": {"fetch_kib": 541122.7, "write_kib": 74547.2},
-    "fwd_gemm": {"fetch_kib": 688163.1, "write_kib": 211152.0},
+    "dx_gemm": {"fetch_kib": 538340.8, "write_kib": 74547.2},
+    "fwd_gemm": {"fetch_kib": 705016.6, "write_kib": 211152.0},
 }
 
 
